@@ -1,0 +1,350 @@
+"""Plain CPU oracle for the KVarN tile quantizer and the paged decode-attention read path.
+
+THIS IS TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT. Only the test suite, the smoke
+check and the benchmark's CPU-baseline leg may import it. The HIP library never calls it
+and shares no code, table or constant generator with it.
+
+Everything here is float64 NumPy. The only roundings are the explicit float16 ones that
+the stored format requires (normalizers, scales and zeros are float16 values in a page).
+
+Sources (page titles; the pages hold no code, no worked example and no kernel):
+  [README]  "huawei-csl/KVarN" README (Chinese translation on bittide.aicompass.dev),
+            sections "Quick start" and "How KVarN works" (four stages).
+  [README-ko] Korean translation of the same README (molayo1419.me), same sections.
+  [hypho]   "KV-cache quantization finally production-ready? KVarN ..." (blog.hypho.cn),
+            section "four-step pipeline".
+  [icwork]  "Huawei open-sources KVarN" (ic.work), the preset description (4-bit keys,
+            2-bit values, group/block size 128).
+
+Readings taken where the pages are silent (all listed with reasons in the design notes):
+  * tile = 128 channels (rows) x 128 tokens (columns);
+  * H = natural-order Sylvester Hadamard / sqrt(128), no random signs;
+  * one Sinkhorn iteration = a column (per-token) step then a row (per-channel) step;
+  * "std" = population standard deviation (ddof=0), centred;
+  * log-scales start at 0, accumulate additively, exp'd once at the end;
+  * a zero / non-finite std skips that update;
+  * normalizers rounded to float16 (clipped to [2^-14, 65504]) and the tile is quantized
+    against the stored float16 values;
+  * asymmetric RTN: zero = group min, scale = (max - min) / (2^b - 1), both stored float16,
+    code = round-half-even((y - zero) / scale) clipped to [0, 2^b - 1]; scale 0 => code 0.
+
+Parity status: every function below is pinned by tests that do not re-type its formula
+(closed forms, invariants, library routines, brute force, hand-derived byte patterns).
+The exact normalizer values for general inputs are not printed on the pages; they are
+fixed only by the readings above plus those pins.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+TILE_TOKENS = 128
+HEAD_DIM = 128
+K_BITS = 4
+V_BITS = 2
+FP16_MIN_NORMAL = 2.0 ** -14
+FP16_MAX = 65504.0
+
+KIND_K = 0
+KIND_V = 1
+
+# ----------------------------------------------------------------------------- helpers
+
+
+def to_fp16(x) -> np.ndarray:
+    """Round float64 values to float16, nearest-even (NumPy converts directly from double)."""
+    return np.asarray(x, dtype=np.float64).astype(np.float16)
+
+
+def hadamard(n: int = HEAD_DIM) -> np.ndarray:
+    """Normalized natural-order Sylvester Hadamard matrix, float64, n a power of two.
+
+    [README] "How KVarN works", stage 2: the rotation along channels is a Hadamard rotation
+    and is orthonormal. Built by the doubling recursion [[A, A], [A, -A]], then / sqrt(n).
+    """
+    if n < 1 or n & (n - 1):
+        raise ValueError("n must be a power of two")
+    h = np.ones((1, 1), dtype=np.float64)
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h / np.sqrt(n)
+
+
+# ----------------------------------------------------------------------------- quantizer
+
+
+def rotate(x: np.ndarray) -> np.ndarray:
+    """Stage 2 ([README] "How KVarN works", stage 2): Xr = H @ X along the channel axis.
+
+    x: [..., 128 channels, 128 tokens] float64.
+    """
+    return hadamard(x.shape[-2]) @ x
+
+
+def _log_std_update(sigma: np.ndarray) -> np.ndarray:
+    ok = np.isfinite(sigma) & (sigma > 0)
+    return np.where(ok, np.log(np.where(ok, sigma, 1.0)), 0.0)
+
+
+def sinkhorn_log(xr: np.ndarray, n_iters: int, history: list | None = None):
+    """Stage 3 ([README] "How KVarN works", stage 3; [README-ko] same stage; [hypho] step 3).
+
+    Iterative variance normalization in log space, alternating a column (per-token) std
+    normalization and a row (per-channel) std normalization.
+
+    xr: [..., C, T] rotated tile. Returns (la [..., C], lb [..., T]) with r = exp(la) the
+    per-channel normalizer and s = exp(lb) the per-token normalizer, so that the normalized
+    tile is Y = xr / (r[:, None] * s[None, :]).
+
+    If `history` is a list, the max |log column std| measured at the start of every column
+    step is appended (a convergence diagnostic).
+    """
+    shape = xr.shape
+    la = np.zeros(shape[:-1], dtype=np.float64)                 # log r, per channel
+    lb = np.zeros(shape[:-2] + (shape[-1],), dtype=np.float64)  # log s, per token
+    for _ in range(n_iters):
+        # column step: every token column gets unit std over the channels
+        y = xr * np.exp(-la)[..., :, None] * np.exp(-lb)[..., None, :]
+        sig_t = y.std(axis=-2)
+        if history is not None:
+            history.append(float(np.max(np.abs(_log_std_update(sig_t)))))
+        lb = lb + _log_std_update(sig_t)
+        # row step: every channel row gets unit std over the tokens
+        y = xr * np.exp(-la)[..., :, None] * np.exp(-lb)[..., None, :]
+        sig_c = y.std(axis=-1)
+        la = la + _log_std_update(sig_c)
+    return la, lb
+
+
+def store_normalizer(log_v: np.ndarray) -> np.ndarray:
+    """exp of a log-normalizer, clipped to the float16 normal range and rounded to float16."""
+    return to_fp16(np.clip(np.exp(log_v), FP16_MIN_NORMAL, FP16_MAX))
+
+
+def rtn_asym(y: np.ndarray, bits: int, axis: int):
+    """Stage 4 ([README] "How KVarN works", stage 4): asymmetric round-to-nearest.
+
+    Groups run along `axis` (the group is every element sharing the other index).
+    Returns (codes uint8, scale16, zero16, u) where u is the unrounded code value in float64
+    (kept for the analysis of rounding ties).
+    """
+    qmax = (1 << bits) - 1
+    mn = y.min(axis=axis, keepdims=True)
+    mx = y.max(axis=axis, keepdims=True)
+    scale16 = to_fp16((mx - mn) / qmax)
+    zero16 = to_fp16(mn)
+    sc = scale16.astype(np.float64)
+    zr = zero16.astype(np.float64)
+    live = sc > 0
+    u = np.where(live, (y - zr) / np.where(live, sc, 1.0), 0.0)
+    codes = np.clip(np.rint(u), 0, qmax).astype(np.uint8)
+    codes = np.where(live, codes, 0).astype(np.uint8)
+    return codes, np.squeeze(scale16, axis), np.squeeze(zero16, axis), u
+
+
+def quantize_tiles(x16: np.ndarray, kind: int, n_iters: int = 8, lossless: bool = False):
+    """Quantize tiles end to end (stages 1-4 of [README] "How KVarN works").
+
+    x16: [..., 128 channels, 128 tokens] float16 (stage 1: the raw tile, channels x tokens).
+    kind: KIND_K (4-bit, one group per channel row) or KIND_V (2-bit, one group per token
+    column) -- [README] stage 4 (keys per channel, values per token) and the preset
+    kvarn_k4v2_g128 ([README] "Quick start"; [icwork] preset table: group size 128).
+
+    Returns a dict with float16 r [...,128], s [...,128], scale [...,128], zero [...,128],
+    uint8 codes [..., 128 c, 128 t], plus float64 'xr' (rotated tile), 'y' (normalized tile
+    against the stored normalizers) and 'u' (unrounded codes).
+
+    lossless=True stops after stage 3 and returns no codes (used to pin the bookkeeping).
+    """
+    x = np.asarray(x16, dtype=np.float16).astype(np.float64)
+    if x.shape[-2:] != (HEAD_DIM, TILE_TOKENS):
+        raise ValueError("tile must be 128 channels x 128 tokens")
+    xr = rotate(x)
+    la, lb = sinkhorn_log(xr, n_iters)
+    r16 = store_normalizer(la)
+    s16 = store_normalizer(lb)
+    y = xr / (r16.astype(np.float64)[..., :, None] * s16.astype(np.float64)[..., None, :])
+    out = dict(r=r16, s=s16, xr=xr, y=y)
+    if lossless:
+        return out
+    if kind == KIND_K:
+        codes, scale16, zero16, u = rtn_asym(y, K_BITS, axis=-1)
+    elif kind == KIND_V:
+        codes, scale16, zero16, u = rtn_asym(y, V_BITS, axis=-2)
+    else:
+        raise ValueError("kind must be KIND_K or KIND_V")
+    out.update(codes=codes, scale=scale16, zero=zero16, u=u)
+    return out
+
+
+def dequantize_tiles(codes, r16, s16, scale16, zero16, kind: int) -> np.ndarray:
+    """Inverse of quantize_tiles up to rounding: X_hat = H (r s^T * (zero + scale * code)).
+
+    The scales are re-applied per channel for keys and per token for values
+    ([README] "How KVarN works", stage 4); H is symmetric and its own inverse.
+    Returns float64 [..., 128 c, 128 t].
+    """
+    codes = np.asarray(codes, dtype=np.float64)
+    sc = np.asarray(scale16, dtype=np.float64)
+    zr = np.asarray(zero16, dtype=np.float64)
+    if kind == KIND_K:
+        yhat = zr[..., :, None] + sc[..., :, None] * codes
+    else:
+        yhat = zr[..., None, :] + sc[..., None, :] * codes
+    r = np.asarray(r16, dtype=np.float64)
+    s = np.asarray(s16, dtype=np.float64)
+    xr_hat = r[..., :, None] * s[..., None, :] * yhat
+    return hadamard(HEAD_DIM) @ xr_hat
+
+
+# ----------------------------------------------------------------------------- page format
+# Format v1 of one page record (one 128-token tile of one KV head). Written here from the
+# format specification, independently of the HIP packer.
+#   K record, 9216 bytes: 8192 B of 4-bit codes, token-major: token t owns bytes
+#     [64 t, 64 t + 64) as 16 little-endian 32-bit words; word j holds channels 8j..8j+7,
+#     nibble p (bits 4p..4p+3) holding channel 8j + K_NIBBLE_CHANNEL[p].
+#   V record, 5120 bytes: 4096 B of 2-bit codes, channel-major: channel c owns 8 words at
+#     word index 8c + 2g + d (g in 0..3, d in 0..1); crumb p (bits 2p..2p+1) of that word
+#     holds token v_crumb_token(g, d, p).
+#   Then four float16[128] vectors: r (per channel), s (per token), scale, zero
+#     (per channel for K, per token for V).
+
+K_RECORD_BYTES = 9216
+V_RECORD_BYTES = 5120
+K_NIBBLE_CHANNEL = (0, 2, 4, 6, 1, 3, 5, 7)
+
+
+def v_crumb_token(g: int, d: int, p: int) -> int:
+    """Token held by crumb p of word (g, d) of a channel in a V record."""
+    i, half = (p, 0) if p < 8 else (p - 8, 1)
+    step = 2 * d + i // 4
+    slot = 2 * (i % 4) + half
+    within = 4 * g + slot if slot < 4 else 12 + 4 * g + slot
+    return 32 * step + within
+
+
+def _meta_bytes(r16, s16, scale16, zero16) -> bytes:
+    parts = [np.asarray(v, dtype="<f2").reshape(128) for v in (r16, s16, scale16, zero16)]
+    return b"".join(p.tobytes() for p in parts)
+
+
+def pack_k_record(codes, r16, s16, scale16, zero16) -> bytes:
+    codes = np.asarray(codes)
+    assert codes.shape == (128, 128) and codes.max(initial=0) <= 15
+    words = np.zeros((128, 16), dtype=np.uint32)
+    for t in range(128):
+        for j in range(16):
+            w = 0
+            for p in range(8):
+                w |= int(codes[8 * j + K_NIBBLE_CHANNEL[p], t]) << (4 * p)
+            words[t, j] = w
+    return words.astype("<u4").tobytes() + _meta_bytes(r16, s16, scale16, zero16)
+
+
+def pack_v_record(codes, r16, s16, scale16, zero16) -> bytes:
+    codes = np.asarray(codes)
+    assert codes.shape == (128, 128) and codes.max(initial=0) <= 3
+    words = np.zeros(128 * 8, dtype=np.uint32)
+    for c in range(128):
+        for g in range(4):
+            for d in range(2):
+                w = 0
+                for p in range(16):
+                    w |= int(codes[c, v_crumb_token(g, d, p)]) << (2 * p)
+                words[8 * c + 2 * g + d] = w
+    return words.astype("<u4").tobytes() + _meta_bytes(r16, s16, scale16, zero16)
+
+
+def _unpack_meta(buf: np.ndarray, off: int):
+    m = buf[off:off + 1024].view("<f2").reshape(4, 128)
+    return m[0].copy(), m[1].copy(), m[2].copy(), m[3].copy()
+
+
+def unpack_k_record(rec) -> dict:
+    buf = np.frombuffer(bytes(rec), dtype=np.uint8)
+    assert buf.size == K_RECORD_BYTES
+    words = buf[:8192].view("<u4").reshape(128, 16)
+    codes = np.zeros((128, 128), dtype=np.uint8)
+    for p in range(8):
+        nib = (words >> np.uint32(4 * p)) & np.uint32(0xF)        # [t, j]
+        for j in range(16):
+            codes[8 * j + K_NIBBLE_CHANNEL[p], :] = nib[:, j]
+    r, s, sc, zr = _unpack_meta(buf, 8192)
+    return dict(codes=codes, r=r, s=s, scale=sc, zero=zr)
+
+
+def unpack_v_record(rec) -> dict:
+    buf = np.frombuffer(bytes(rec), dtype=np.uint8)
+    assert buf.size == V_RECORD_BYTES
+    words = buf[:4096].view("<u4").reshape(128, 4, 2)
+    codes = np.zeros((128, 128), dtype=np.uint8)
+    for g in range(4):
+        for d in range(2):
+            for p in range(16):
+                codes[:, v_crumb_token(g, d, p)] = (words[:, g, d] >> np.uint32(2 * p)) & np.uint32(3)
+    r, s, sc, zr = _unpack_meta(buf, 4096)
+    return dict(codes=codes, r=r, s=s, scale=sc, zero=zr)
+
+
+# ----------------------------------------------------------------------------- attention
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, softmax_scale: float) -> np.ndarray:
+    """Single-query softmax attention in float64, written out from its definition.
+
+    q: [128], k: [n, 128], v: [n, 128]. Returns o = sum_t p_t v_t with
+    p = softmax(softmax_scale * k @ q).
+    """
+    z = softmax_scale * (np.asarray(k, np.float64) @ np.asarray(q, np.float64))
+    z = z - z.max()
+    p = np.exp(z)
+    return (p / p.sum()) @ np.asarray(v, np.float64)
+
+
+def dequantize_k_record(rec) -> np.ndarray:
+    """Unpack one K page record and return the dequantized keys [128 tokens, 128 channels]."""
+    d = unpack_k_record(rec)
+    return dequantize_tiles(d["codes"], d["r"], d["s"], d["scale"], d["zero"], KIND_K).T
+
+
+def dequantize_v_record(rec) -> np.ndarray:
+    d = unpack_v_record(rec)
+    return dequantize_tiles(d["codes"], d["r"], d["s"], d["scale"], d["zero"], KIND_V).T
+
+
+def decode_attention_row(q_row, k_pages, v_pages, k_tail=None, v_tail=None,
+                         softmax_scale: float = 1.0 / np.sqrt(HEAD_DIM)) -> np.ndarray:
+    """Decode attention of one query row over one KV head's cache.
+
+    k_pages / v_pages: lists of page records (bytes) of that KV head, in block-table order
+    (the cache is read from quantized tiles, [README] intro: a native attention backend;
+    scales re-applied on read, "How KVarN works" stage 4).
+    k_tail / v_tail: [n_tail, 128] float16 tokens past the last full page (raw, exact).
+    Returns float64 [128].
+    """
+    ks = [dequantize_k_record(p) for p in k_pages]
+    vs = [dequantize_v_record(p) for p in v_pages]
+    if k_tail is not None and len(k_tail):
+        ks.append(np.asarray(k_tail, np.float16).astype(np.float64))
+        vs.append(np.asarray(v_tail, np.float16).astype(np.float64))
+    k = np.concatenate(ks, axis=0)
+    v = np.concatenate(vs, axis=0)
+    return attention(np.asarray(q_row, np.float16).astype(np.float64), k, v, softmax_scale)
+
+
+def merge_partials(m: np.ndarray, l: np.ndarray, acc: np.ndarray) -> np.ndarray:
+    """Combine partial softmax results of disjoint token ranges.
+
+    Each part i holds its max score m_i, its sum l_i = sum exp(z - m_i) and its unnormalized
+    output acc_i = sum exp(z - m_i) v. The result equals attention over the union.
+    """
+    m = np.asarray(m, np.float64)
+    w = np.exp(m - m.max())
+    return (w[:, None] * np.asarray(acc, np.float64)).sum(0) / (w * np.asarray(l, np.float64)).sum()
+
+
+def partial_attention(q, k, v, softmax_scale):
+    """(m, l, acc) of one token range, for merge_partials."""
+    z = softmax_scale * (np.asarray(k, np.float64) @ np.asarray(q, np.float64))
+    m = z.max()
+    p = np.exp(z - m)
+    return m, p.sum(), p @ np.asarray(v, np.float64)

@@ -1,0 +1,387 @@
+"""Pins of the CPU oracle to things other than itself (closed forms, invariants, library
+routines, brute force, hand-derived byte patterns). CPU only."""
+import json
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+import torch
+
+from oracle import kvarn_oracle as O
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+RNG = np.random.default_rng(1234)
+
+
+def _balanced_signs(rng, n=128):
+    v = np.array([1.0] * (n // 2) + [-1.0] * (n // 2))
+    rng.shuffle(v)
+    return v
+
+
+# ----------------------------------------------------------------------------- Hadamard
+
+
+def test_hadamard_matches_library():
+    assert np.array_equal(O.hadamard(128), scipy.linalg.hadamard(128) / np.sqrt(128))
+    for n in (1, 2, 4, 16, 64):
+        assert np.allclose(O.hadamard(n), scipy.linalg.hadamard(n) / np.sqrt(n), atol=0, rtol=0)
+
+
+def test_hadamard_orthonormal_symmetric():
+    h = O.hadamard(128)
+    assert np.abs(h @ h.T - np.eye(128)).max() < 1e-12
+    assert np.array_equal(h, h.T)
+
+
+def test_rotation_preserves_scores():
+    # README "How KVarN works" stage 2: the rotation is orthonormal so q.k is preserved.
+    q, k = RNG.standard_normal(128), RNG.standard_normal((128, 50))
+    h = O.hadamard(128)
+    assert np.allclose((h @ q) @ (h @ k), q @ k, rtol=1e-12, atol=1e-12)
+    x = RNG.standard_normal((3, 128, 128))
+    assert np.allclose(O.rotate(x), np.einsum("ij,bjt->bit", scipy.linalg.hadamard(128) / np.sqrt(128), x))
+
+
+# ----------------------------------------------------------------------------- Sinkhorn
+
+
+@pytest.mark.parametrize("n_iters", [1, 2, 8])
+def test_sinkhorn_closed_form_rank_one(n_iters):
+    """X = diag(a) u w^T diag(b), u and w balanced +-1: after one column step s = sigma_a b,
+    after one row step r = a / sigma_a with sigma_a = population std of a*u; later
+    iterations change nothing (the normalized tile u w^T already has unit stds)."""
+    rng = np.random.default_rng(7)
+    a = rng.uniform(0.2, 5.0, 128)
+    b = rng.uniform(0.2, 5.0, 128)
+    u, w = _balanced_signs(rng), _balanced_signs(rng)
+    xr = a[:, None] * np.outer(u, w) * b[None, :]
+    sig_a = np.sqrt(np.mean((a * u) ** 2) - np.mean(a * u) ** 2)
+    la, lb = O.sinkhorn_log(xr, n_iters)
+    assert np.allclose(np.exp(lb), sig_a * b, rtol=1e-12)
+    assert np.allclose(np.exp(la), a / sig_a, rtol=1e-12)
+
+
+def test_sinkhorn_fixed_point_is_identity():
+    rng = np.random.default_rng(8)
+    y = np.outer(_balanced_signs(rng), _balanced_signs(rng))
+    la, lb = O.sinkhorn_log(y, 8)
+    assert np.array_equal(la, np.zeros(128)) and np.array_equal(lb, np.zeros(128))
+
+
+@pytest.mark.parametrize("n_iters", [1, 3, 8])
+def test_sinkhorn_last_row_step_gives_unit_row_std(n_iters):
+    xr = O.rotate(RNG.standard_normal((4, 128, 128)) * RNG.lognormal(0, 1.5, (4, 128, 1)))
+    la, lb = O.sinkhorn_log(xr, n_iters)
+    y = xr * np.exp(-la)[..., :, None] * np.exp(-lb)[..., None, :]
+    assert np.allclose(y.std(axis=-1), 1.0, rtol=1e-10)
+
+
+def test_sinkhorn_converges_on_average():
+    first, last = [], []
+    for seed in range(6):
+        rng = np.random.default_rng(100 + seed)
+        x = rng.standard_t(3, (128, 128)) * rng.lognormal(0, 1.0, (128, 1)) * rng.lognormal(0, 1.0, (1, 128))
+        hist = []
+        O.sinkhorn_log(O.rotate(x), 8, history=hist)
+        first.append(hist[1])
+        last.append(hist[-1])
+    assert np.mean(last) < np.mean(first)
+
+
+def test_sinkhorn_zero_tile_is_skipped():
+    la, lb = O.sinkhorn_log(np.zeros((128, 128)), 8)
+    assert not la.any() and not lb.any()
+
+
+def test_scale_by_power_of_two_moves_only_token_normalizer():
+    x = RNG.standard_normal((128, 128)).astype(np.float16)
+    a = O.quantize_tiles(x, O.KIND_K, 8)
+    b = O.quantize_tiles((x.astype(np.float64) * 4.0).astype(np.float16), O.KIND_K, 8)
+    assert np.array_equal(a["r"], b["r"])
+    assert np.array_equal(a["s"].astype(np.float64) * 4.0, b["s"].astype(np.float64))
+    assert np.array_equal(a["codes"], b["codes"])
+    assert np.array_equal(a["scale"], b["scale"]) and np.array_equal(a["zero"], b["zero"])
+
+
+def test_token_permutation_equivariance():
+    x = RNG.standard_normal((128, 128)).astype(np.float16)
+    perm = RNG.permutation(128)
+    for kind in (O.KIND_K, O.KIND_V):
+        a = O.quantize_tiles(x, kind, 4)
+        b = O.quantize_tiles(x[:, perm], kind, 4)
+        assert np.array_equal(a["s"][perm], b["s"])
+        assert np.array_equal(a["codes"][:, perm], b["codes"])
+        assert np.allclose(a["r"].astype(float), b["r"].astype(float), rtol=2e-3)
+
+
+def test_zero_iterations_is_plain_rotated_rtn():
+    x = RNG.standard_normal((128, 128)).astype(np.float16)
+    out = O.quantize_tiles(x, O.KIND_K, 0)
+    assert np.all(out["r"] == 1) and np.all(out["s"] == 1)
+    xr = scipy.linalg.hadamard(128) @ x.astype(np.float64) / np.sqrt(128)
+    # per-channel min / max of the rotated tile are the zero point and range
+    assert np.array_equal(out["zero"], xr.min(axis=1).astype(np.float16))
+    assert np.array_equal(out["scale"], ((xr.max(axis=1) - xr.min(axis=1)) / 15).astype(np.float16))
+
+
+# ----------------------------------------------------------------------------- RTN
+
+
+@pytest.mark.parametrize("kind,bits", [(O.KIND_K, 4), (O.KIND_V, 2)])
+def test_rtn_code_range_and_extremes(kind, bits):
+    qmax = (1 << bits) - 1
+    x = (RNG.standard_t(3, (6, 128, 128)) * 3).astype(np.float16)
+    out = O.quantize_tiles(x, kind, 8)
+    codes = out["codes"]
+    assert codes.min() >= 0 and codes.max() <= qmax
+    axis = -1 if kind == O.KIND_K else -2
+    assert np.all(codes.min(axis=axis) == 0)
+    assert np.all(codes.max(axis=axis) == qmax)
+
+
+@pytest.mark.parametrize("kind,bits", [(O.KIND_K, 4), (O.KIND_V, 2)])
+def test_rtn_error_bound(kind, bits):
+    qmax = (1 << bits) - 1
+    y = RNG.standard_normal((128, 128)) * RNG.lognormal(0, 1, (128, 1))
+    axis = -1 if kind == O.KIND_K else -2
+    codes, sc16, zr16, _ = O.rtn_asym(y, bits, axis)
+    mn, mx = y.min(axis=axis), y.max(axis=axis)
+    sc, zr = sc16.astype(np.float64), zr16.astype(np.float64)
+    exp_ = (lambda v: v[:, None]) if kind == O.KIND_K else (lambda v: v[None, :])
+    yhat = exp_(zr) + exp_(sc) * codes
+    bound = exp_(sc) / 2 + np.abs(exp_(mn) - exp_(zr)) + qmax * np.abs(exp_((mx - mn) / qmax) - exp_(sc))
+    assert np.all(np.abs(y - yhat) <= bound * (1 + 1e-12))
+
+
+def test_rtn_groups_follow_kind():
+    """K groups are channel rows, V groups are token columns (README stage 4)."""
+    y = np.add.outer(np.arange(128.0), np.zeros(128)) + RNG.uniform(0, 1, (128, 128))
+    _, sk, zk, _ = O.rtn_asym(y, 4, axis=-1)
+    assert np.array_equal(zk, y.min(axis=1).astype(np.float16))
+    _, sv, zv, _ = O.rtn_asym(y, 2, axis=-2)
+    assert np.array_equal(zv, y.min(axis=0).astype(np.float16))
+
+
+def test_rtn_exact_on_grid_and_constant_group():
+    z, s = np.float16(-1.25), np.float16(0.125)
+    k = RNG.integers(0, 16, (128, 128))
+    k[:, 0], k[:, 1] = 0, 15
+    y = float(z) + float(s) * k
+    codes, sc, zr, _ = O.rtn_asym(y, 4, axis=-1)
+    assert np.all(sc == s) and np.all(zr == z) and np.array_equal(codes, k)
+    codes, sc, zr, _ = O.rtn_asym(np.full((128, 128), 3.0), 4, axis=-1)
+    assert np.all(sc == 0) and np.all(codes == 0) and np.all(zr == 3.0)
+
+
+def test_constant_and_zero_tiles():
+    """A zero tile skips every normalizer update and codes to 0. A constant tile rotates
+    into a single non-zero channel (row 0 of H X); it reconstructs to float16 accuracy."""
+    for val in (0.0, 2.5):
+        x = np.full((128, 128), val, dtype=np.float16)
+        for kind in (O.KIND_K, O.KIND_V):
+            out = O.quantize_tiles(x, kind, 8)
+            if val == 0.0:
+                assert np.all(out["codes"] == 0) and np.all(out["r"] == 1) and np.all(out["s"] == 1)
+            else:
+                assert np.all(out["codes"][1:] == 0)
+            xh = O.dequantize_tiles(out["codes"], out["r"], out["s"], out["scale"], out["zero"], kind)
+            assert np.allclose(xh, x.astype(np.float64), atol=3e-3 * max(val, 1))
+
+
+def test_lossless_bookkeeping_reconstructs_input():
+    """Without RTN, H (r s^T * Y) reproduces X exactly: pins the rotation and normalizers."""
+    x = (RNG.standard_normal((128, 128)) * RNG.lognormal(0, 1, (128, 1))).astype(np.float16)
+    out = O.quantize_tiles(x, O.KIND_K, 8, lossless=True)
+    r, s = out["r"].astype(np.float64), out["s"].astype(np.float64)
+    xh = O.hadamard() @ (r[:, None] * s[None, :] * out["y"])
+    assert np.allclose(xh, x.astype(np.float64), rtol=0, atol=1e-12 * float(np.abs(x).max()))
+
+
+def test_quantization_error_improves_over_plain_rtn():
+    """Rotation + normalization lower the reconstruction error vs. RTN on the raw tile with
+    outlier channels (README intro and stage 2/3: outliers spread, variance equalized)."""
+    x = RNG.standard_normal((128, 128))
+    x[RNG.choice(128, 4, replace=False), :] *= 20
+    x16 = x.astype(np.float16)
+    out = O.quantize_tiles(x16, O.KIND_K, 8)
+    xh = O.dequantize_tiles(out["codes"], out["r"], out["s"], out["scale"], out["zero"], O.KIND_K)
+    codes, sc, zr, _ = O.rtn_asym(x16.astype(np.float64), 4, axis=-1)
+    plain = zr.astype(float)[:, None] + sc.astype(float)[:, None] * codes
+    e_kvarn = np.linalg.norm(xh - x16)
+    e_plain = np.linalg.norm(plain - x16)
+    assert e_kvarn < e_plain
+
+
+# ----------------------------------------------------------------------------- format
+
+
+def _gold():
+    with open(os.path.join(GOLD, "format_patterns.json")) as f:
+        return json.load(f)
+
+
+def _meta():
+    return (np.full(128, 1.0, np.float16), np.full(128, 2.0, np.float16),
+            np.full(128, 0.5, np.float16), np.full(128, -1.0, np.float16))
+
+
+def _words(rec, n):
+    return np.frombuffer(rec[:n], dtype="<u4")
+
+
+def test_k_format_golden_patterns():
+    g = _gold()
+    c, t = np.meshgrid(np.arange(128), np.arange(128), indexing="ij")
+    w = _words(O.pack_k_record(c % 16, *_meta()), 8192).reshape(128, 16)
+    assert np.all(w[:, 0::2] == int(g["k_codes_c_mod_16"]["word_even"], 16))
+    assert np.all(w[:, 1::2] == int(g["k_codes_c_mod_16"]["word_odd"], 16))
+    w = _words(O.pack_k_record(t % 16, *_meta()), 8192).reshape(128, 16)
+    assert np.all(w == (np.arange(128)[:, None] % 16) * 0x11111111)
+    rec = O.pack_k_record(t % 16, *_meta())
+    m = g["metadata"]
+    for i, key in enumerate(("r_bytes", "s_bytes", "scale_bytes", "zero_bytes")):
+        seg = rec[8192 + 256 * i: 8192 + 256 * (i + 1)]
+        assert seg == bytes.fromhex(m[key]) * 128
+
+
+def test_v_format_golden_patterns():
+    g = _gold()
+    c, t = np.meshgrid(np.arange(128), np.arange(128), indexing="ij")
+    w = _words(O.pack_v_record(c % 4, *_meta()), 4096).reshape(128, 4, 2)
+    assert np.all(w == (np.arange(128)[:, None, None] % 4) * 0x55555555)
+    w = _words(O.pack_v_record(t // 32, *_meta()), 4096).reshape(128, 4, 2)
+    assert np.all(w[:, :, 0] == int(g["v_codes_t_div_32"]["word_d0"], 16))
+    assert np.all(w[:, :, 1] == int(g["v_codes_t_div_32"]["word_d1"], 16))
+    w = _words(O.pack_v_record((t // 4) % 4, *_meta()), 4096).reshape(128, 4, 2)
+    assert np.all(w == np.arange(4)[None, :, None] * 0x55555555)
+    w = _words(O.pack_v_record(t % 4, *_meta()), 4096)
+    assert np.all(w == int(g["v_codes_t_mod_4"]["word"], 16))
+    rec = O.pack_v_record(t % 4, *_meta())
+    assert rec[4096:4096 + 256] == bytes.fromhex(g["metadata"]["r_bytes"]) * 128
+    assert rec[4096 + 768:] == bytes.fromhex(g["metadata"]["zero_bytes"]) * 128
+
+
+def test_pack_unpack_roundtrip():
+    for bits, pack, unpack, size in ((4, O.pack_k_record, O.unpack_k_record, 9216),
+                                     (2, O.pack_v_record, O.unpack_v_record, 5120)):
+        codes = RNG.integers(0, 1 << bits, (128, 128)).astype(np.uint8)
+        meta = [RNG.standard_normal(128).astype(np.float16) for _ in range(4)]
+        rec = pack(codes, *meta)
+        assert len(rec) == size
+        d = unpack(rec)
+        assert np.array_equal(d["codes"], codes)
+        for key, m in zip(("r", "s", "scale", "zero"), meta):
+            assert np.array_equal(d[key], m)
+
+
+def test_v_crumb_map_is_a_permutation():
+    toks = sorted(O.v_crumb_token(g, d, p) for g in range(4) for d in range(2) for p in range(16))
+    assert toks == list(range(128))
+
+
+def test_capacity_within_claimed_range():
+    # README intro: 3-5x KV capacity vs FP16; format v1 stores K+V in 14336 B per 128 tokens.
+    ratio = 2 * 128 * 128 * 2 / (O.K_RECORD_BYTES + O.V_RECORD_BYTES)
+    assert 3.0 <= ratio <= 5.0
+
+
+# ----------------------------------------------------------------------------- attention
+
+
+def test_attention_matches_sdpa():
+    q = RNG.standard_normal(128)
+    k = RNG.standard_normal((300, 128))
+    v = RNG.standard_normal((300, 128))
+    sm = 1 / np.sqrt(128)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.tensor(q)[None, None, None], torch.tensor(k)[None, None], torch.tensor(v)[None, None],
+        scale=sm)[0, 0, 0].numpy()
+    assert np.allclose(O.attention(q, k, v, sm), ref, rtol=1e-12, atol=1e-13)
+
+
+def test_split_merge_equals_single_pass():
+    q = RNG.standard_normal(128)
+    k = RNG.standard_normal((1000, 128)) * 3
+    v = RNG.standard_normal((1000, 128))
+    sm = 1 / np.sqrt(128)
+    cuts = [0, 1, 128, 129, 500, 999, 1000]
+    parts = [O.partial_attention(q, k[a:b], v[a:b], sm) for a, b in zip(cuts[:-1], cuts[1:])]
+    m, l, acc = (np.array([p[i] for p in parts]) for i in range(3))
+    assert np.allclose(O.merge_partials(m, l, acc), O.attention(q, k, v, sm), rtol=1e-12, atol=1e-13)
+
+
+def _quantize_pages(xk, xv, n_iters=8):
+    """xk, xv [n_pages, 128 tok, 128 ch] float16 -> lists of records."""
+    kp, vp = [], []
+    for i in range(xk.shape[0]):
+        a = O.quantize_tiles(xk[i].T, O.KIND_K, n_iters)
+        kp.append(O.pack_k_record(a["codes"], a["r"], a["s"], a["scale"], a["zero"]))
+        b = O.quantize_tiles(xv[i].T, O.KIND_V, n_iters)
+        vp.append(O.pack_v_record(b["codes"], b["r"], b["s"], b["scale"], b["zero"]))
+    return kp, vp
+
+
+def test_decode_row_equals_sdpa_on_dequantized_cache_with_gqa():
+    """One sequence, 2 KV heads, 8 query heads (GQA 4): the oracle decode equals SDPA with
+    repeat_interleave on the dequantized keys/values (+ raw fp16 tail)."""
+    hkv, hq, pages, tail = 2, 8, 2, 37
+    xk = RNG.standard_normal((hkv, pages, 128, 128)).astype(np.float16)
+    xv = RNG.standard_normal((hkv, pages, 128, 128)).astype(np.float16)
+    tk = RNG.standard_normal((hkv, tail, 128)).astype(np.float16)
+    tv = RNG.standard_normal((hkv, tail, 128)).astype(np.float16)
+    q = RNG.standard_normal((hq, 128)).astype(np.float16)
+    recs = [_quantize_pages(xk[h], xv[h]) for h in range(hkv)]
+    kfull = np.stack([np.concatenate([O.dequantize_k_record(r) for r in recs[h][0]] + [tk[h].astype(float)]) for h in range(hkv)])
+    vfull = np.stack([np.concatenate([O.dequantize_v_record(r) for r in recs[h][1]] + [tv[h].astype(float)]) for h in range(hkv)])
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.tensor(q.astype(float))[None, :, None],
+        torch.tensor(kfull).repeat_interleave(hq // hkv, 0)[None],
+        torch.tensor(vfull).repeat_interleave(hq // hkv, 0)[None], scale=1 / np.sqrt(128))[0, :, 0].numpy()
+    for h in range(hq):
+        g = h // (hq // hkv)
+        o = O.decode_attention_row(q[h], recs[g][0], recs[g][1], tk[g], tv[g])
+        assert np.allclose(o, ref[h], rtol=1e-11, atol=1e-12)
+
+
+def test_rotated_space_decode_identity():
+    """The read path's algebra: with q_rot = H q, per tile q'' = q_rot*r*scale (keys), the
+    score is s_t (q''.code_t + q_rot.(r*zero)); values accumulate r * (sum_t p_t s_t
+    (scale_t code_t + zero_t)); the output is H^T acc / l. Equal to dequantize-then-attend."""
+    xk = RNG.standard_normal((3, 128, 128)).astype(np.float16)
+    xv = RNG.standard_normal((3, 128, 128)).astype(np.float16)
+    kp, vp = _quantize_pages(xk, xv)
+    q = RNG.standard_normal(128).astype(np.float16).astype(np.float64)
+    sm = 1 / np.sqrt(128)
+    h = O.hadamard()
+    q_rot = h @ q
+    scores, contrib = [], []
+    for kr, vr in zip(kp, vp):
+        dk, dv = O.unpack_k_record(kr), O.unpack_v_record(vr)
+        r, s, sc, zr = (dk[k_].astype(np.float64) for k_ in ("r", "s", "scale", "zero"))
+        qpp = q_rot * r * sc
+        scores.append(sm * s * (qpp @ dk["codes"] + q_rot @ (r * zr)))
+        contrib.append(dv)
+    z = np.concatenate(scores)
+    p = np.exp(z - z.max())
+    acc = np.zeros(128)
+    for i, dv in enumerate(contrib):
+        pt = p[128 * i: 128 * (i + 1)]
+        r, s, sc, zr = (dv[k_].astype(np.float64) for k_ in ("r", "s", "scale", "zero"))
+        acc += r * (dv["codes"] @ (pt * s * sc) + np.sum(pt * s * zr))
+    o = h.T @ acc / p.sum()
+    ref = O.decode_attention_row(q.astype(np.float16), kp, vp)
+    assert np.allclose(o, ref, rtol=1e-11, atol=1e-12)
+
+
+def test_quantized_attention_close_to_fp16_attention():
+    """End-to-end sanity on a single tile: attention over the quantized cache stays close to
+    exact attention (the method's accuracy claim, README intro; loose bound)."""
+    xk = RNG.standard_normal((1, 128, 128)).astype(np.float16)
+    xv = RNG.standard_normal((1, 128, 128)).astype(np.float16)
+    kp, vp = _quantize_pages(xk, xv)
+    q = RNG.standard_normal(128).astype(np.float16)
+    exact = O.attention(q.astype(float), xk[0].astype(float), xv[0].astype(float), 1 / np.sqrt(128))
+    approx = O.decode_attention_row(q, kp, vp)
+    assert np.linalg.norm(approx - exact) < 0.5 * np.linalg.norm(exact) + 0.1

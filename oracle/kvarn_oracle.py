@@ -85,6 +85,13 @@ def _log_std_update(sigma: np.ndarray) -> np.ndarray:
     return np.where(ok, np.log(np.where(ok, sigma, 1.0)), 0.0)
 
 
+def population_std(y: np.ndarray, axis: int) -> np.ndarray:
+    """Centred population standard deviation along `axis`; exactly 0 for a group of
+    identical values (whatever the summation order of the library mean)."""
+    sd = y.std(axis=axis)
+    return np.where(y.max(axis=axis) == y.min(axis=axis), 0.0, sd)
+
+
 def sinkhorn_log(xr: np.ndarray, n_iters: int, history: list | None = None):
     """Stage 3 ([README] "How KVarN works", stage 3; [README-ko] same stage; [hypho] step 3).
 
@@ -104,13 +111,13 @@ def sinkhorn_log(xr: np.ndarray, n_iters: int, history: list | None = None):
     for _ in range(n_iters):
         # column step: every token column gets unit std over the channels
         y = xr * np.exp(-la)[..., :, None] * np.exp(-lb)[..., None, :]
-        sig_t = y.std(axis=-2)
+        sig_t = population_std(y, axis=-2)
         if history is not None:
             history.append(float(np.max(np.abs(_log_std_update(sig_t)))))
         lb = lb + _log_std_update(sig_t)
         # row step: every channel row gets unit std over the tokens
         y = xr * np.exp(-la)[..., :, None] * np.exp(-lb)[..., None, :]
-        sig_c = y.std(axis=-1)
+        sig_c = population_std(y, axis=-1)
         la = la + _log_std_update(sig_c)
     return la, lb
 

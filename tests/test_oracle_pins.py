@@ -385,3 +385,13 @@ def test_quantized_attention_close_to_fp16_attention():
     exact = O.attention(q.astype(float), xk[0].astype(float), xv[0].astype(float), 1 / np.sqrt(128))
     approx = O.decode_attention_row(q, kp, vp)
     assert np.linalg.norm(approx - exact) < 0.5 * np.linalg.norm(exact) + 0.1
+
+
+def test_population_std_is_exactly_zero_for_identical_values():
+    """The std of identical values is 0 by definition, whatever the library's summation
+    order; 0.1 (inexact in binary) repeated along either axis is the hard case."""
+    y = np.full((128, 128), 0.1) * RNG.uniform(0.5, 2.0, (128, 1))
+    assert np.all(O.population_std(y, axis=-1) == 0.0)
+    assert np.all(O.population_std(y.T, axis=-2) == 0.0)
+    z = RNG.standard_normal((128, 128))
+    assert np.allclose(O.population_std(z, axis=-1), np.sqrt(np.mean((z - z.mean(-1, keepdims=True)) ** 2, -1)), rtol=1e-13)

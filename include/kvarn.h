@@ -1,0 +1,190 @@
+/*
+ * kvarn.h -- C ABI of the KVarN tile quantizer and paged decode attention for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (KVarN README, "How KVarN works", four stages): a KV cache is cut into
+ * 128-token tiles (channels x tokens); each tile is rotated along channels by an
+ * orthonormal Hadamard matrix, normalized by an iterative log-space Sinkhorn-style
+ * alternation of column-std and row-std normalization, then quantized by asymmetric
+ * round-to-nearest, keys 4-bit with scales per channel, values 2-bit with scales per token
+ * (preset "kvarn_k4v2_g128", README "Quick start"; 128 = tile / page size).
+ * The read path is decode attention that dequantizes the tiles on the fly: the query is
+ * rotated by H for QK and the accumulated values are rotated back by H^T.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named *_dev are DEVICE pointers owned by the caller; the library never
+ *     frees or retains them. Host pointers are named *_host or are plain structs.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). All GPU work
+ *     is enqueued on it; calls return once the work is queued.
+ *   - The library allocates no memory and keeps no global state. It is re-entrant.
+ *   - Arguments are validated on the host before anything is enqueued. On any error
+ *     nothing is enqueued and outputs are untouched.
+ *   - Device-resident indices (page ids, token offsets, sequence lengths) cannot be checked
+ *     on the host; the kernels bound-check them and skip out-of-range entries instead of
+ *     faulting (documented per call).
+ *   - float16 is IEEE binary16, little-endian. Rounding to float16 is nearest-even.
+ */
+#ifndef KVARN_H
+#define KVARN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Entry points keep default visibility even when the library is built with hidden
+ * visibility. */
+#if defined(__GNUC__) || defined(__clang__)
+#define KVARN_API __attribute__((visibility("default")))
+#else
+#define KVARN_API
+#endif
+
+#define KVARN_ABI_VERSION 1
+#define KVARN_FORMAT_VERSION 1
+
+typedef enum {
+    KVARN_OK = 0,
+    KVARN_ERR_INVALID_ARG = 1, /* NULL pointer, bad size, misalignment, bad enum      */
+    KVARN_ERR_UNSUPPORTED = 2, /* a valid request outside what this build implements */
+    KVARN_ERR_WORKSPACE = 3,   /* workspace smaller than kvarn_decode_workspace_bytes */
+    KVARN_ERR_HIP = 4          /* the HIP runtime refused a launch                    */
+} kvarn_status;
+
+typedef enum { KVARN_K = 0, KVARN_V = 1 } kvarn_kind;
+
+/* Quantizer parameters. Only head_dim = tile_tokens = group = 128, k_bits = 4,
+ * v_bits = 2 are implemented (README "Quick start": other page sizes are not yet
+ * supported). sinkhorn_iters is the number of (column step, row step) pairs of the
+ * normalization (README "How KVarN works", stage 3); 0..64 accepted. */
+typedef struct {
+    int32_t head_dim;
+    int32_t tile_tokens;
+    int32_t k_bits;
+    int32_t v_bits;
+    int32_t group;
+    int32_t sinkhorn_iters;
+} kvarn_params;
+
+/* Library ABI version (KVARN_ABI_VERSION) and page-format version. */
+KVARN_API int32_t kvarn_abi_version(void);
+KVARN_API int32_t kvarn_format_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+KVARN_API const char* kvarn_status_str(kvarn_status status);
+
+/* Parse a kv-cache dtype string of the form "kvarn_k<kb>v<vb>_g<group>" (README "Quick
+ * start": kv_cache_dtype="kvarn_k4v2_g128") into params, with the given iteration count.
+ * Returns INVALID_ARG for a malformed string or NULL pointer, UNSUPPORTED for a well-formed
+ * preset other than k4v2_g128. `out_host` is written only on success. */
+KVARN_API kvarn_status kvarn_params_from_dtype(const char* kv_cache_dtype, int32_t sinkhorn_iters,
+                                     kvarn_params* out_host);
+
+/* Check a params struct: OK, INVALID_ARG (NULL / out of range) or UNSUPPORTED. */
+KVARN_API kvarn_status kvarn_params_check(const kvarn_params* params);
+
+/* Bytes of one page record (one 128-token tile of one KV head) of the given kind:
+ * 9216 for keys, 5120 for values; 0 if params are invalid or unsupported.
+ *
+ * Page format v1 (little-endian):
+ *   K record: bytes [0, 8192) are 4-bit codes, token-major: token t owns bytes
+ *     [64t, 64t+64) as 16 32-bit words; word j holds channels 8j..8j+7 with nibble p
+ *     (bits 4p..4p+3) holding channel 8j + {0,2,4,6,1,3,5,7}[p].
+ *   V record: bytes [0, 4096) are 2-bit codes, channel-major: channel c owns the 8 words
+ *     8c + 2g + d (g = 0..3, d = 0..1); crumb p (bits 2p..2p+1) of word (c, g, d) holds
+ *     token 32 s + (j < 4 ? 4g + j : 12 + 4g + j) where i = p mod 8, s = 2d + i / 4,
+ *     j = 2 (i mod 4) + p / 8.
+ *   Both then hold four float16[128] vectors: r (per-channel normalizer), s (per-token
+ *   normalizer), scale and zero (per channel for K, per token for V).
+ *   A tile X (channels x tokens, rotated Xr = H X) is recovered as
+ *     Xr[c][t] = r[c] * s[t] * (zero[g] + scale[g] * code[c][t]),  X = H Xr,
+ *   with g = c for K and g = t for V, H the normalized natural-order Sylvester
+ *   Hadamard matrix (symmetric, its own inverse). */
+KVARN_API size_t kvarn_page_bytes(const kvarn_params* params, kvarn_kind kind);
+
+/* Quantize tiles into a page pool (README "How KVarN works", stages 1-4).
+ *
+ * For every tile i in [0, n_tiles) and KV head h in [0, num_kv_heads): the tile is
+ * tokens [tile_src_token[i], tile_src_token[i] + 128) of head h of `src_dev`, element
+ * (token, head, channel) at src_dev[token * src_token_stride + head * src_head_stride +
+ * channel] (float16, strides in elements, channel stride 1). Its record is written to
+ * pool_dev + (tile_dst_page[i] * num_kv_heads + h) * kvarn_page_bytes(params, kind).
+ *
+ * Arguments:
+ *   src_dev: float16, 16-byte aligned; strides multiples of 8, non-negative.
+ *   src_num_tokens: number of valid source tokens; tiles whose token range is not inside
+ *     [0, src_num_tokens) are skipped (left unwritten).
+ *   tile_src_token_dev: int64[n_tiles], tile_dst_page_dev: int32[n_tiles] (device).
+ *   pool_dev: 16-byte aligned, pool_num_pages pages of num_kv_heads records; tiles whose
+ *     page is outside [0, pool_num_pages) are skipped.
+ *   n_tiles == 0 is a no-op returning OK.
+ * Tiles must write distinct pages; overlapping destinations give an undefined record. */
+KVARN_API kvarn_status kvarn_quantize_tiles(const kvarn_params* params, kvarn_kind kind,
+                                  const void* src_dev, int64_t src_token_stride,
+                                  int64_t src_head_stride, int64_t src_num_tokens,
+                                  const int64_t* tile_src_token_dev,
+                                  const int32_t* tile_dst_page_dev, int32_t n_tiles,
+                                  int32_t num_kv_heads, void* pool_dev,
+                                  int64_t pool_num_pages, void* stream);
+
+/* Append one decode token per sequence into the float16 staging tiles, and quantize every
+ * staging tile that this append fills (the 128th token) into its page.
+ *
+ * For sequence b with L = seq_lens_dev[b] tokens BEFORE the append (0 <= L), the new
+ * token k_new_dev[b][h][:] / v_new_dev[b][h][:] ([B, Hkv, 128] float16) is written to
+ * row L mod 128 of k_tail_dev[b][h] / v_tail_dev[b][h] ([B, Hkv, 128, 128] float16,
+ * [b][h][token][channel]). If L mod 128 == 127 the staging tiles of b are then quantized
+ * (both kinds, all heads) into page block_table_dev[b * block_table_stride + L / 128] of
+ * k_pool_dev / v_pool_dev. Pages outside [0, pool_num_pages) are skipped. The caller
+ * increments seq_lens afterwards. Staging is plain float16 so the decode reads it exactly
+ * (tiles are fixed-size, README "How KVarN works"; a partial tile is never quantized). */
+KVARN_API kvarn_status kvarn_append_tokens(const kvarn_params* params, const void* k_new_dev,
+                                 const void* v_new_dev, int32_t batch, int32_t num_kv_heads,
+                                 const int32_t* seq_lens_dev, void* k_tail_dev,
+                                 void* v_tail_dev, const int32_t* block_table_dev,
+                                 int32_t block_table_stride, void* k_pool_dev,
+                                 void* v_pool_dev, int64_t pool_num_pages, void* stream);
+
+/* Workspace bytes kvarn_decode_attention needs for this shape (0 if invalid). */
+KVARN_API size_t kvarn_decode_workspace_bytes(const kvarn_params* params, int32_t batch,
+                                    int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t max_seq_len);
+
+/* Number of key splits the decode uses for this shape (0 if invalid); informative. */
+KVARN_API int32_t kvarn_decode_num_splits(const kvarn_params* params, int32_t batch,
+                                int32_t num_kv_heads, int32_t max_seq_len);
+
+/* Paged decode attention over quantized pages plus a float16 tail (README intro: a native
+ * attention backend reading the quantized cache; "How KVarN works" stage 4: scales are
+ * re-applied on read).
+ *
+ * For sequence b, query head hq, KV head g = hq / (num_q_heads / num_kv_heads):
+ *   L = min(seq_lens_dev[b], max_seq_len); pages p < L / 128 are
+ *   block_table_dev[b * block_table_stride + p] of k_pool_dev / v_pool_dev; the last
+ *   L mod 128 tokens are rows 0.. of k_tail_dev[b][g] / v_tail_dev[b][g].
+ *   out[b][hq] = sum_t softmax_t(softmax_scale * q[b][hq] . k_t) v_t  (float16, RNE),
+ *   k_t, v_t the dequantized (or staged) keys and values.
+ * Arguments:
+ *   q_dev, out_dev: [batch, num_q_heads, 128] float16, contiguous, 16-byte aligned.
+ *   num_q_heads % num_kv_heads == 0 and num_q_heads / num_kv_heads <= 8.
+ *   k_tail_dev / v_tail_dev may be NULL: then tail tokens are ignored.
+ *   Pages outside [0, pool_num_pages) are skipped. A sequence with L = 0 gets out = 0.
+ *   workspace_dev: >= kvarn_decode_workspace_bytes(...) bytes, 16-byte aligned; it holds
+ *   per-split partial softmax state and must not be shared by concurrent calls. */
+KVARN_API kvarn_status kvarn_decode_attention(const kvarn_params* params, const void* q_dev,
+                                    int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                    const void* k_pool_dev, const void* v_pool_dev,
+                                    int64_t pool_num_pages, const int32_t* block_table_dev,
+                                    int32_t block_table_stride, const int32_t* seq_lens_dev,
+                                    int32_t max_seq_len, const void* k_tail_dev,
+                                    const void* v_tail_dev, float softmax_scale,
+                                    void* workspace_dev, size_t workspace_bytes,
+                                    void* out_dev, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVARN_H */

@@ -1,0 +1,190 @@
+// C ABI of the KVarN library: host-side validation, then kernel launches.
+// Every check runs before anything is enqueued; see include/kvarn.h for the contract.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/kvarn.h"
+#include "kvarn_launch.h"
+
+namespace {
+
+constexpr int32_t kMaxIters = 64;
+constexpr int32_t kMaxGroup = 8;  // query heads per KV head handled by one decode wave
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+kvarn_status launch_status(hipError_t e) { return e == hipSuccess ? KVARN_OK : KVARN_ERR_HIP; }
+
+// Parse a non-negative decimal integer at *p (advancing it); -1 if none or too large.
+int parse_uint(const char** p) {
+  const char* s = *p;
+  if (*s < '0' || *s > '9') return -1;
+  long v = 0;
+  while (*s >= '0' && *s <= '9') {
+    v = v * 10 + (*s - '0');
+    if (v > 1000000) return -1;
+    ++s;
+  }
+  *p = s;
+  return int(v);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kvarn_abi_version(void) { return KVARN_ABI_VERSION; }
+int32_t kvarn_format_version(void) { return KVARN_FORMAT_VERSION; }
+
+const char* kvarn_status_str(kvarn_status status) {
+  switch (status) {
+    case KVARN_OK: return "ok";
+    case KVARN_ERR_INVALID_ARG: return "invalid argument";
+    case KVARN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KVARN_ERR_WORKSPACE: return "workspace too small";
+    case KVARN_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+kvarn_status kvarn_params_check(const kvarn_params* p) {
+  if (!p) return KVARN_ERR_INVALID_ARG;
+  if (p->head_dim <= 0 || p->tile_tokens <= 0 || p->group <= 0 || p->k_bits <= 0 ||
+      p->v_bits <= 0 || p->sinkhorn_iters < 0 || p->sinkhorn_iters > kMaxIters)
+    return KVARN_ERR_INVALID_ARG;
+  if (p->head_dim != 128 || p->tile_tokens != 128 || p->group != 128 || p->k_bits != 4 ||
+      p->v_bits != 2)
+    return KVARN_ERR_UNSUPPORTED;
+  return KVARN_OK;
+}
+
+kvarn_status kvarn_params_from_dtype(const char* dtype, int32_t sinkhorn_iters, kvarn_params* out) {
+  if (!dtype || !out) return KVARN_ERR_INVALID_ARG;
+  const char* s = dtype;
+  if (strncmp(s, "kvarn_k", 7) != 0) return KVARN_ERR_INVALID_ARG;
+  s += 7;
+  const int kb = parse_uint(&s);
+  if (kb < 0 || *s != 'v') return KVARN_ERR_INVALID_ARG;
+  ++s;
+  const int vb = parse_uint(&s);
+  if (vb < 0 || strncmp(s, "_g", 2) != 0) return KVARN_ERR_INVALID_ARG;
+  s += 2;
+  const int grp = parse_uint(&s);
+  if (grp < 0 || *s != '\0') return KVARN_ERR_INVALID_ARG;
+  kvarn_params p;
+  p.head_dim = 128;
+  p.tile_tokens = 128;
+  p.k_bits = kb;
+  p.v_bits = vb;
+  p.group = grp;
+  p.sinkhorn_iters = sinkhorn_iters;
+  if (kb == 0 || vb == 0 || grp == 0) return KVARN_ERR_INVALID_ARG;
+  const kvarn_status st = kvarn_params_check(&p);
+  if (st != KVARN_OK) return st;
+  *out = p;
+  return KVARN_OK;
+}
+
+size_t kvarn_page_bytes(const kvarn_params* p, kvarn_kind kind) {
+  if (kvarn_params_check(p) != KVARN_OK) return 0;
+  if (kind == KVARN_K) return 9216;
+  if (kind == KVARN_V) return 5120;
+  return 0;
+}
+
+kvarn_status kvarn_quantize_tiles(const kvarn_params* params, kvarn_kind kind, const void* src,
+                                  int64_t src_token_stride, int64_t src_head_stride,
+                                  int64_t src_num_tokens, const int64_t* tile_src_token,
+                                  const int32_t* tile_dst_page, int32_t n_tiles,
+                                  int32_t num_kv_heads, void* pool, int64_t pool_num_pages,
+                                  void* stream) {
+  const kvarn_status st = kvarn_params_check(params);
+  if (st != KVARN_OK) return st;
+  if (kind != KVARN_K && kind != KVARN_V) return KVARN_ERR_INVALID_ARG;
+  if (n_tiles < 0 || num_kv_heads <= 0 || num_kv_heads > 65535 || src_num_tokens < 0 ||
+      pool_num_pages < 0 || src_token_stride < 0 || src_head_stride < 0)
+    return KVARN_ERR_INVALID_ARG;
+  if (n_tiles == 0) return KVARN_OK;
+  if (!src || !tile_src_token || !tile_dst_page || !pool) return KVARN_ERR_INVALID_ARG;
+  if (!aligned16(src) || !aligned16(pool) || (src_token_stride % 8) != 0 ||
+      (src_head_stride % 8) != 0)
+    return KVARN_ERR_INVALID_ARG;
+  return launch_status(kvarn::launch_quantize_tiles(
+      int(kind), src, src_token_stride, src_head_stride, src_num_tokens, tile_src_token,
+      tile_dst_page, n_tiles, num_kv_heads, pool, pool_num_pages, params->sinkhorn_iters,
+      static_cast<hipStream_t>(stream)));
+}
+
+kvarn_status kvarn_append_tokens(const kvarn_params* params, const void* k_new, const void* v_new,
+                                 int32_t batch, int32_t num_kv_heads, const int32_t* seq_lens,
+                                 void* k_tail, void* v_tail, const int32_t* block_table,
+                                 int32_t block_table_stride, void* k_pool, void* v_pool,
+                                 int64_t pool_num_pages, void* stream) {
+  const kvarn_status st = kvarn_params_check(params);
+  if (st != KVARN_OK) return st;
+  if (batch < 0 || num_kv_heads <= 0 || num_kv_heads > 65535 || block_table_stride <= 0 ||
+      pool_num_pages < 0)
+    return KVARN_ERR_INVALID_ARG;
+  if (batch == 0) return KVARN_OK;
+  if (!k_new || !v_new || !seq_lens || !k_tail || !v_tail || !block_table || !k_pool || !v_pool)
+    return KVARN_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_tail) || !aligned16(v_tail) ||
+      !aligned16(k_pool) || !aligned16(v_pool))
+    return KVARN_ERR_INVALID_ARG;
+  return launch_status(kvarn::launch_append_tokens(
+      k_new, v_new, batch, num_kv_heads, seq_lens, k_tail, v_tail, block_table,
+      block_table_stride, k_pool, v_pool, pool_num_pages, params->sinkhorn_iters,
+      static_cast<hipStream_t>(stream)));
+}
+
+size_t kvarn_decode_workspace_bytes(const kvarn_params* params, int32_t batch, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t max_seq_len) {
+  if (kvarn_params_check(params) != KVARN_OK) return 0;
+  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_seq_len < 0 ||
+      num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > kMaxGroup)
+    return 0;
+  return kvarn::decode_workspace_bytes(batch, num_q_heads, num_kv_heads, max_seq_len);
+}
+
+int32_t kvarn_decode_num_splits(const kvarn_params* params, int32_t batch, int32_t num_kv_heads,
+                                int32_t max_seq_len) {
+  if (kvarn_params_check(params) != KVARN_OK) return 0;
+  if (batch <= 0 || num_kv_heads <= 0 || max_seq_len < 0) return 0;
+  return kvarn::decode_num_splits(batch, num_kv_heads, max_seq_len);
+}
+
+kvarn_status kvarn_decode_attention(const kvarn_params* params, const void* q, int32_t batch,
+                                    int32_t num_q_heads, int32_t num_kv_heads, const void* k_pool,
+                                    const void* v_pool, int64_t pool_num_pages,
+                                    const int32_t* block_table, int32_t block_table_stride,
+                                    const int32_t* seq_lens, int32_t max_seq_len,
+                                    const void* k_tail, const void* v_tail, float softmax_scale,
+                                    void* workspace, size_t workspace_bytes, void* out,
+                                    void* stream) {
+  const kvarn_status st = kvarn_params_check(params);
+  if (st != KVARN_OK) return st;
+  if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_seq_len < 0 ||
+      pool_num_pages < 0 || block_table_stride < 0 || num_q_heads > 65535 || num_kv_heads > 65535)
+    return KVARN_ERR_INVALID_ARG;
+  if (num_q_heads % num_kv_heads != 0) return KVARN_ERR_INVALID_ARG;
+  if (num_q_heads / num_kv_heads > kMaxGroup) return KVARN_ERR_UNSUPPORTED;
+  if (!isfinite(softmax_scale)) return KVARN_ERR_INVALID_ARG;
+  if (batch == 0) return KVARN_OK;
+  if (!q || !seq_lens || !out || !workspace) return KVARN_ERR_INVALID_ARG;
+  if ((k_tail == nullptr) != (v_tail == nullptr)) return KVARN_ERR_INVALID_ARG;
+  if (max_seq_len >= 128) {
+    if (!k_pool || !v_pool || !block_table) return KVARN_ERR_INVALID_ARG;
+    if (block_table_stride < max_seq_len / 128) return KVARN_ERR_INVALID_ARG;
+    if (!aligned16(k_pool) || !aligned16(v_pool)) return KVARN_ERR_INVALID_ARG;
+  }
+  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return KVARN_ERR_INVALID_ARG;
+  if (k_tail && (!aligned16(k_tail) || !aligned16(v_tail))) return KVARN_ERR_INVALID_ARG;
+  if (workspace_bytes < kvarn::decode_workspace_bytes(batch, num_q_heads, num_kv_heads, max_seq_len))
+    return KVARN_ERR_WORKSPACE;
+  return launch_status(kvarn::launch_decode(
+      q, batch, num_q_heads, num_kv_heads, k_pool, v_pool, pool_num_pages, block_table,
+      block_table_stride, seq_lens, max_seq_len, k_tail, v_tail, softmax_scale, workspace, out,
+      static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

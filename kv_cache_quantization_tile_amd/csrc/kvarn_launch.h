@@ -1,0 +1,33 @@
+// Internal launchers of the KVarN HIP kernels (called by the C ABI after validation).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvarn {
+
+hipError_t launch_quantize_tiles(int kind, const void* src, int64_t token_stride,
+                                 int64_t head_stride, int64_t src_num_tokens,
+                                 const int64_t* tile_src_token, const int32_t* tile_dst_page,
+                                 int32_t n_tiles, int32_t num_kv_heads, void* pool,
+                                 int64_t pool_num_pages, int n_iters, hipStream_t stream);
+
+hipError_t launch_append_tokens(const void* k_new, const void* v_new, int32_t batch,
+                                int32_t num_kv_heads, const int32_t* seq_lens, void* k_tail,
+                                void* v_tail, const int32_t* block_table, int32_t bt_stride,
+                                void* k_pool, void* v_pool, int64_t pool_num_pages, int n_iters,
+                                hipStream_t stream);
+
+int32_t decode_tiles_per_wave(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len);
+int32_t decode_num_splits(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len);
+size_t decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t max_seq_len);
+
+hipError_t launch_decode(const void* q, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                         const void* k_pool, const void* v_pool, int64_t pool_num_pages,
+                         const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                         int32_t max_seq_len, const void* k_tail, const void* v_tail,
+                         float softmax_scale, void* workspace, void* out, hipStream_t stream);
+
+}  // namespace kvarn

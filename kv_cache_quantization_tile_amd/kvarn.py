@@ -1,0 +1,206 @@
+"""ctypes binding of libkvarn.so (the C ABI in include/kvarn.h).
+
+Argument marshalling only: every step of the quantize and decode paths runs in the HIP
+kernels of the library. PyTorch supplies device memory and the current stream. Importing
+this module fails loudly if the library has not been built; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvarn.so")
+
+KIND_K = 0
+KIND_V = 1
+K_PAGE_BYTES = 9216
+V_PAGE_BYTES = 5120
+
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
+          3: "workspace too small", 4: "HIP launch failed"}
+
+
+class KvarnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {STATUS.get(status, status)} (status {status})")
+        self.status = status
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("head_dim", ctypes.c_int32), ("tile_tokens", ctypes.c_int32),
+                ("k_bits", ctypes.c_int32), ("v_bits", ctypes.c_int32),
+                ("group", ctypes.c_int32), ("sinkhorn_iters", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with "
+                          "`python -m kv_cache_quantization_tile_amd.build` (needs hipcc)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.POINTER(Params)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "kvarn_abi_version": (i32, []),
+        "kvarn_format_version": (i32, []),
+        "kvarn_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+        "kvarn_params_from_dtype": (ctypes.c_int, [ctypes.c_char_p, i32, P]),
+        "kvarn_params_check": (ctypes.c_int, [P]),
+        "kvarn_page_bytes": (sz, [P, ctypes.c_int]),
+        "kvarn_quantize_tiles": (ctypes.c_int, [P, ctypes.c_int, vp, i64, i64, i64, vp, vp, i32,
+                                                i32, vp, i64, vp]),
+        "kvarn_append_tokens": (ctypes.c_int, [P, vp, vp, i32, i32, vp, vp, vp, vp, i32, vp, vp,
+                                               i64, vp]),
+        "kvarn_decode_workspace_bytes": (sz, [P, i32, i32, i32, i32]),
+        "kvarn_decode_num_splits": (i32, [P, i32, i32, i32]),
+        "kvarn_decode_attention": (ctypes.c_int, [P, vp, i32, i32, i32, vp, vp, i64, vp, i32, vp,
+                                                  i32, vp, vp, ctypes.c_float, vp, sz, vp, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+EXPORTED = ("kvarn_abi_version", "kvarn_format_version", "kvarn_status_str",
+            "kvarn_params_from_dtype", "kvarn_params_check", "kvarn_page_bytes",
+            "kvarn_quantize_tiles", "kvarn_append_tokens", "kvarn_decode_workspace_bytes",
+            "kvarn_decode_num_splits", "kvarn_decode_attention")
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise KvarnError(status, what)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, name, dtype, device=True):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
+# ----------------------------------------------------------------------------- params
+
+
+def params_from_dtype(kv_cache_dtype: str = "kvarn_k4v2_g128", sinkhorn_iters: int = 8) -> Params:
+    p = Params()
+    _check(lib.kvarn_params_from_dtype(kv_cache_dtype.encode(), sinkhorn_iters, ctypes.byref(p)),
+           f"kv_cache_dtype {kv_cache_dtype!r}")
+    return p
+
+
+def page_bytes(params: Params, kind: int) -> int:
+    return int(lib.kvarn_page_bytes(ctypes.byref(params), kind))
+
+
+def new_pool(num_pages: int, num_kv_heads: int, kind: int, device="cuda") -> torch.Tensor:
+    """A zeroed page pool [num_pages, num_kv_heads, record bytes] of uint8."""
+    nb = K_PAGE_BYTES if kind == KIND_K else V_PAGE_BYTES
+    return torch.zeros((num_pages, num_kv_heads, nb), dtype=torch.uint8, device=device)
+
+
+# ----------------------------------------------------------------------------- quantize
+
+
+def quantize_tiles(params: Params, kind: int, src: torch.Tensor, tile_src_token: torch.Tensor,
+                   tile_dst_page: torch.Tensor, pool: torch.Tensor, stream=None) -> torch.Tensor:
+    """Quantize tiles of src ([tokens, Hkv, 128] float16, channel stride 1) into pool."""
+    _need(src, "src", torch.float16)
+    _need(tile_src_token, "tile_src_token", torch.int64)
+    _need(tile_dst_page, "tile_dst_page", torch.int32)
+    _need(pool, "pool", torch.uint8)
+    if src.dim() != 3 or src.shape[2] != 128 or src.stride(2) != 1:
+        raise ValueError("src must be [tokens, Hkv, 128] with unit channel stride")
+    hkv = src.shape[1]
+    nb = page_bytes(params, kind)
+    if pool.dim() != 3 or pool.shape[1] != hkv or pool.shape[2] != nb or not pool.is_contiguous():
+        raise ValueError(f"pool must be contiguous [pages, {hkv}, {nb}]")
+    n = tile_src_token.numel()
+    if tile_dst_page.numel() != n:
+        raise ValueError("tile_src_token and tile_dst_page differ in length")
+    _check(lib.kvarn_quantize_tiles(ctypes.byref(params), kind, _ptr(src), src.stride(0),
+                                    src.stride(1), src.shape[0], _ptr(tile_src_token),
+                                    _ptr(tile_dst_page), n, hkv, _ptr(pool), pool.shape[0],
+                                    _stream(stream)), "kvarn_quantize_tiles")
+    return pool
+
+
+def append_tokens(params: Params, k_new, v_new, seq_lens, k_tail, v_tail, block_table,
+                  k_pool, v_pool, stream=None):
+    """Write one token per sequence into staging; quantize staging tiles that fill."""
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new"), (k_tail, "k_tail"), (v_tail, "v_tail")):
+        _need(t, nm, torch.float16)
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    _need(seq_lens, "seq_lens", torch.int32)
+    _need(block_table, "block_table", torch.int32)
+    B, hkv = k_new.shape[0], k_new.shape[1]
+    if tuple(k_tail.shape) != (B, hkv, 128, 128) or tuple(v_tail.shape) != (B, hkv, 128, 128):
+        raise ValueError("staging must be [B, Hkv, 128, 128]")
+    if block_table.dim() != 2 or block_table.shape[0] != B or not block_table.is_contiguous():
+        raise ValueError("block_table must be contiguous [B, width]")
+    _check(lib.kvarn_append_tokens(ctypes.byref(params), _ptr(k_new), _ptr(v_new), B, hkv,
+                                   _ptr(seq_lens), _ptr(k_tail), _ptr(v_tail), _ptr(block_table),
+                                   block_table.shape[1], _ptr(k_pool), _ptr(v_pool),
+                                   k_pool.shape[0], _stream(stream)), "kvarn_append_tokens")
+
+
+# ----------------------------------------------------------------------------- decode
+
+
+def decode_workspace_bytes(params: Params, batch: int, num_q_heads: int, num_kv_heads: int,
+                           max_seq_len: int) -> int:
+    return int(lib.kvarn_decode_workspace_bytes(ctypes.byref(params), batch, num_q_heads,
+                                                num_kv_heads, max_seq_len))
+
+
+def decode_num_splits(params: Params, batch: int, num_kv_heads: int, max_seq_len: int) -> int:
+    return int(lib.kvarn_decode_num_splits(ctypes.byref(params), batch, num_kv_heads, max_seq_len))
+
+
+def new_workspace(params: Params, batch, num_q_heads, num_kv_heads, max_seq_len, device="cuda"):
+    nbytes = decode_workspace_bytes(params, batch, num_q_heads, num_kv_heads, max_seq_len)
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
+def decode_attention(params: Params, q, k_pool, v_pool, block_table, seq_lens, max_seq_len: int,
+                     k_tail=None, v_tail=None, softmax_scale: float | None = None,
+                     workspace=None, out=None, stream=None) -> torch.Tensor:
+    """Paged decode attention; q [B, Hq, 128] float16 -> out [B, Hq, 128] float16."""
+    _need(q, "q", torch.float16)
+    _need(seq_lens, "seq_lens", torch.int32)
+    _need(block_table, "block_table", torch.int32)
+    if q.dim() != 3 or q.shape[2] != 128 or not q.is_contiguous():
+        raise ValueError("q must be contiguous [B, Hq, 128]")
+    B, hq = q.shape[0], q.shape[1]
+    hkv = k_pool.shape[1]
+    if block_table.dim() != 2 or block_table.shape[0] != B or not block_table.is_contiguous():
+        raise ValueError("block_table must be contiguous [B, width]")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(128)
+    if workspace is None:
+        workspace = new_workspace(params, B, hq, hkv, max_seq_len, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib.kvarn_decode_attention(ctypes.byref(params), _ptr(q), B, hq, hkv, _ptr(k_pool),
+                                      _ptr(v_pool), k_pool.shape[0], _ptr(block_table),
+                                      block_table.shape[1], _ptr(seq_lens), max_seq_len,
+                                      _ptr(k_tail), _ptr(v_tail), float(softmax_scale),
+                                      _ptr(workspace), workspace.numel(), _ptr(out),
+                                      _stream(stream)), "kvarn_decode_attention")
+    return out

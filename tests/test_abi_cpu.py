@@ -1,0 +1,118 @@
+"""The C ABI on the CPU: the library loads, exports every function include/kvarn.h declares,
+and rejects bad arguments on the host before anything is enqueued (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from kv_cache_quantization_tile_amd import kvarn as K
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "kvarn.h")
+OK, INVALID, UNSUP, WS = 0, 1, 2, 3
+FAKE = ctypes.c_void_p(0x10000)      # aligned, never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    return sorted(set(re.findall(r"\b(kvarn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(K.lib, n), n
+    assert set(names) == set(K.EXPORTED)
+
+
+def test_versions_and_status_strings():
+    assert K.lib.kvarn_abi_version() == 1
+    assert K.lib.kvarn_format_version() == 1
+    for s in range(5):
+        assert K.lib.kvarn_status_str(s).decode() == K.STATUS[s]
+    assert K.lib.kvarn_status_str(99) == b"unknown status"
+
+
+def test_params_from_dtype():
+    p = K.params_from_dtype("kvarn_k4v2_g128", 8)
+    assert (p.head_dim, p.tile_tokens, p.k_bits, p.v_bits, p.group, p.sinkhorn_iters) == (128, 128, 4, 2, 128, 8)
+    out = K.Params()
+    for bad in ("", "fp8", "kvarn_k4v2", "kvarn_k4v2_g", "kvarn_kv2_g128", "kvarn_k4v2_g128x", "kvarn_k0v2_g128"):
+        assert K.lib.kvarn_params_from_dtype(bad.encode(), 8, ctypes.byref(out)) == INVALID, bad
+    for unsup in ("kvarn_k4v4_g128", "kvarn_k2v2_g128", "kvarn_k4v2_g64"):
+        assert K.lib.kvarn_params_from_dtype(unsup.encode(), 8, ctypes.byref(out)) == UNSUP, unsup
+    assert K.lib.kvarn_params_from_dtype(b"kvarn_k4v2_g128", -1, ctypes.byref(out)) == INVALID
+    assert K.lib.kvarn_params_from_dtype(b"kvarn_k4v2_g128", 65, ctypes.byref(out)) == INVALID
+    assert K.lib.kvarn_params_from_dtype(None, 8, ctypes.byref(out)) == INVALID
+    with pytest.raises(K.KvarnError):
+        K.params_from_dtype("kvarn_k8v8_g128")
+
+
+def test_page_bytes():
+    p = K.params_from_dtype()
+    assert K.page_bytes(p, K.KIND_K) == 9216 and K.page_bytes(p, K.KIND_V) == 5120
+    assert K.page_bytes(p, 7) == 0
+    bad = K.Params(128, 64, 4, 2, 128, 8)
+    assert K.lib.kvarn_params_check(ctypes.byref(bad)) == UNSUP
+    assert K.page_bytes(bad, K.KIND_K) == 0
+
+
+def _quant(p, **kw):
+    a = dict(kind=0, src=FAKE, ts=1024, hs=128, ntok=4096, tok=FAKE, page=FAKE, n=1, hkv=8,
+             pool=FAKE, npages=10)
+    a.update(kw)
+    return K.lib.kvarn_quantize_tiles(ctypes.byref(p), a["kind"], a["src"], a["ts"], a["hs"],
+                                      a["ntok"], a["tok"], a["page"], a["n"], a["hkv"],
+                                      a["pool"], a["npages"], None)
+
+
+def test_quantize_validation():
+    p = K.params_from_dtype()
+    assert _quant(p, n=0) == OK                       # no-op, nothing enqueued
+    assert _quant(p, src=None) == INVALID
+    assert _quant(p, pool=None) == INVALID
+    assert _quant(p, tok=None) == INVALID
+    assert _quant(p, kind=2) == INVALID
+    assert _quant(p, n=-1) == INVALID
+    assert _quant(p, hkv=0) == INVALID
+    assert _quant(p, ts=1023) == INVALID              # stride not a multiple of 8
+    assert _quant(p, src=ctypes.c_void_p(0x10008)) == INVALID   # misaligned
+    assert _quant(p, ntok=-1) == INVALID
+    bad = K.Params(128, 128, 4, 4, 128, 8)
+    assert _quant(bad) == UNSUP
+    assert K.lib.kvarn_quantize_tiles(None, 0, FAKE, 8, 8, 1, FAKE, FAKE, 1, 1, FAKE, 1, None) == INVALID
+
+
+def _decode(p, **kw):
+    a = dict(q=FAKE, B=2, hq=64, hkv=8, kp=FAKE, vp=FAKE, npages=100, bt=FAKE, bts=200, sl=FAKE,
+             mx=16384, kt=None, vt=None, scale=0.088, ws=FAKE, wsb=1 << 30, out=FAKE)
+    a.update(kw)
+    return K.lib.kvarn_decode_attention(ctypes.byref(p), a["q"], a["B"], a["hq"], a["hkv"], a["kp"],
+                                        a["vp"], a["npages"], a["bt"], a["bts"], a["sl"], a["mx"],
+                                        a["kt"], a["vt"], a["scale"], a["ws"], a["wsb"], a["out"], None)
+
+
+def test_decode_validation():
+    p = K.params_from_dtype()
+    assert _decode(p, B=0) == OK
+    assert _decode(p, hq=63) == INVALID               # not a multiple of hkv
+    assert _decode(p, hq=128) == UNSUP                # 16 query heads per KV head
+    assert _decode(p, q=None) == INVALID
+    assert _decode(p, kt=FAKE) == INVALID             # one tail without the other
+    assert _decode(p, bts=10) == INVALID              # block table narrower than max pages
+    assert _decode(p, scale=float("nan")) == INVALID
+    assert _decode(p, out=ctypes.c_void_p(0x10002)) == INVALID
+    assert _decode(p, wsb=16) == WS
+    need = K.decode_workspace_bytes(p, 2, 64, 8, 16384)
+    assert _decode(p, wsb=need - 1) == WS
+
+
+def test_decode_workspace_formula():
+    p = K.params_from_dtype()
+    for B, hq, hkv, mx in ((1, 64, 8, 16384), (32, 64, 8, 32768), (1, 64, 8, 131072), (64, 64, 8, 16384), (3, 8, 8, 100)):
+        ns = K.decode_num_splits(p, B, hkv, mx)
+        assert ns >= 1
+        assert K.decode_workspace_bytes(p, B, hq, hkv, mx) == B * hq * (ns + 1) * 132 * 4
+    assert K.decode_workspace_bytes(p, 1, 64, 8, -1) == 0
+    assert K.decode_workspace_bytes(p, 1, 128, 8, 1024) == 0

@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of the KVarN hot path on one MI355X: tile quantization + paged decode attention.
+
+Workload (one decoder layer of a Qwen3-32B-like model, the pages' measurement shape): batch 1,
+64 query / 8 KV heads, head_dim 128, 16384 tokens of float16 K/V (channel magnitudes
+lognormal(0,1), 3 outlier channels x10, times N(0,1)); one step = quantize all 2048 K and V
+tiles (k4v2_g128, 8 Sinkhorn iterations) into pages, then one decode-attention step of all
+64 query heads over those pages. Synthetic data; inputs resident in HBM before timing.
+
+Distinct layer copies (64 by default, as in a 64-layer model) are cycled step by step, so
+each step's ~82 MB of inputs and pages are not resident in the 256 MB Infinity Cache.
+
+Prints one JSON line. Numbers:
+  value / ms_per_step: whole step (quantize + decode), algorithmic bytes / step time.
+  decode_kv_gbps, quantize_tiles_per_s: the two halves, from HIP events around each launch.
+  roofline: the dominant kernel (by time) against its bound; roofline_other: the other one.
+  cpu_baseline: the float64 CPU oracle on a bounded sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# Algorithmic work units (what the method must move / compute, not what the kernels do)
+Q_READ = 128 * 128 * 2                 # float16 tile in
+K_REC, V_REC = 9216, 5120              # page records out
+HBM_PEAK_GBPS = 8000.0                 # MI355X HBM3E
+# fp32 FMA on the vector ALUs without packed-FP32 forms: 256 CU x 4 SIMD x 16 lanes x 2 x 2.4 GHz
+ALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+
+
+def quant_flop_per_tile(n_iters: int) -> int:
+    """FWHT-128 (7 x 16384 add/sub) + per iteration two moment passes in each direction
+    (4 x 16384 FMA = 131072 FLOP) + RTN (~131072: min/max, scale, round)."""
+    return 7 * 16384 + n_iters * 131072 + 131072
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "kv_cache_quantization_tile_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, src_hash: str):
+    """HBM bytes per launch measured by rocprofv3 counters (profiles/traffic.json), or None
+    when absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != src_hash or kernel not in t.get("kernels", {}):
+        return None
+    return t["kernels"][kernel].get("bytes_per_launch")
+
+
+def cpu_baseline(w, n_iters: int, budget_s: float):
+    """The float64 oracle on a bounded sample of one step, scaled to the whole step."""
+    import numpy as np
+    from oracle import kvarn_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    k = w.k_src.cpu().numpy()
+    v = w.v_src.cpu().numpy()
+    q = w.step_inputs(0, device="cpu")[0].numpy()
+    T = k.shape[0]
+    n_tiles_step = 2 * (T // 128) * w.hkv
+    # quantize: a batch of tiles of KV head 0, both kinds
+    nq = 16
+    tiles_k = np.stack([k[128 * i:128 * (i + 1), 0, :].T for i in range(nq)])
+    tiles_v = np.stack([v[128 * i:128 * (i + 1), 0, :].T for i in range(nq)])
+    t0 = time.perf_counter()
+    rk = O.quantize_tiles(tiles_k, O.KIND_K, n_iters)
+    rv = O.quantize_tiles(tiles_v, O.KIND_V, n_iters)
+    tq = (time.perf_counter() - t0) / (2 * nq)               # seconds per tile
+    # decode: all query heads of KV head 0 over as many pages as fit the budget
+    pages = max(1, min(T // 128, int(budget_s / max(tq, 1e-3) / 4)))
+    t0 = time.perf_counter()
+    kd = np.concatenate([O.dequantize_tiles(rk["codes"][i % nq], rk["r"][i % nq], rk["s"][i % nq],
+                                            rk["scale"][i % nq], rk["zero"][i % nq], O.KIND_K).T
+                         for i in range(pages)])
+    vd = np.concatenate([O.dequantize_tiles(rv["codes"][i % nq], rv["r"][i % nq], rv["s"][i % nq],
+                                            rv["scale"][i % nq], rv["zero"][i % nq], O.KIND_V).T
+                         for i in range(pages)])
+    G = w.hq // w.hkv
+    for h in range(G):
+        O.attention(q[0, h].astype(np.float64), kd, vd, 1 / math.sqrt(128))
+    td = (time.perf_counter() - t0) * (T // 128) / pages * w.hkv   # whole decode step
+    t_step = tq * n_tiles_step + td
+    return t_step, blas_threads, (f"{2 * nq} tiles quantized (K and V, KV head 0) and decode of "
+                                  f"{G} query heads over {pages} pages of KV head 0, scaled to "
+                                  f"{n_tiles_step} tiles and {w.hkv} KV heads x {T // 128} pages")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--layers", type=int, default=64,
+                    help="distinct layer copies cycled across steps (defeats the 256 MB MALL)")
+    ap.add_argument("--sinkhorn-iters", type=int, default=8)
+    ap.add_argument("--context", type=int, default=16384)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--calibration-copy-mb", type=int, default=0,
+                    help="also run one device copy of this size (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the hot path needs no cross-GPU exchange; see the sharding notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    from kv_cache_quantization_tile_amd import kvarn as K
+    from kv_cache_quantization_tile_amd import synth
+
+    dev = torch.device("cuda:0")
+    n_iters = args.sinkhorn_iters
+    params = K.params_from_dtype("kvarn_k4v2_g128", n_iters)
+    L = max(1, args.layers)
+    print(f"[bench] generating {L} layer copies of one_layer_16k (context {args.context})",
+          file=sys.stderr, flush=True)
+    layers = []
+    for i in range(L):
+        w = synth.one_layer(device=dev, seed=1 + i, context=args.context)
+        q = w.step_inputs(0)[0]
+        n_pages = w.num_pages
+        kp = K.new_pool(n_pages, w.hkv, K.KIND_K)
+        vp = K.new_pool(n_pages, w.hkv, K.KIND_V)
+        layers.append((w, q, kp, vp))
+    w0 = layers[0][0]
+    B, hq, hkv, T = w0.batch, w0.hq, w0.hkv, args.context
+    seq_lens = torch.tensor(w0.prompt_lens, dtype=torch.int32, device=dev)
+    ws = K.new_workspace(params, B, hq, hkv, T)
+    out = torch.empty((B, hq, 128), dtype=torch.float16, device=dev)
+    calls = []
+    for (w, q, kp, vp) in layers:
+        qk = K.prepare_quantize(params, K.KIND_K, w.k_src, w.tile_src_token, w.tile_dst_page, kp)
+        qv = K.prepare_quantize(params, K.KIND_V, w.v_src, w.tile_src_token, w.tile_dst_page, vp)
+        dc = K.prepare_decode(params, q, kp, vp, w.block_table, seq_lens, T, ws, out)
+        calls.append((qk, qv, dc))
+    n_tiles = w0.tile_src_token.numel() * hkv          # per kind
+    torch.cuda.synchronize()
+
+    if args.calibration_copy_mb:
+        a = torch.empty(args.calibration_copy_mb << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    # warmup
+    for s in range(args.warmup):
+        qk, qv, dc = calls[s % L]
+        qk(); qv(); dc()
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps; events bracket every launch group
+    marks = [(ev(), ev(), ev()) for _ in range(args.steps)]
+    start, stop = ev(), ev()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for s in range(args.steps):
+        qk, qv, dc = calls[(args.warmup + s) % L]
+        e0, e1, e2 = marks[s]
+        e0.record(); qk(); qv(); e1.record(); dc(); e2.record()
+    stop.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(stop)
+    q_ms = sum(m[0].elapsed_time(m[1]) for m in marks) / args.steps      # 2 quantize launches
+    d_ms = sum(m[1].elapsed_time(m[2]) for m in marks) / args.steps      # decode launches
+    ms_step = total_ms / args.steps
+
+    # algorithmic bytes
+    q_bytes = n_tiles * (Q_READ + K_REC) + n_tiles * (Q_READ + V_REC)
+    full_pages = T // 128
+    d_bytes = B * hkv * full_pages * (K_REC + V_REC) + 2 * B * hq * 128 * 2
+    step_bytes = q_bytes + d_bytes
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    tiles_per_s = 2 * n_tiles / (q_ms * 1e-3)
+    decode_gbps = d_bytes / (d_ms * 1e-3) / 1e9
+
+    src_hash = source_hash()
+    flop_tile = quant_flop_per_tile(n_iters)
+    q_launch_ms = q_ms / 2
+    q_achieved = n_tiles * flop_tile / (q_launch_ms * 1e-3) / 1e12
+    quant_roof = {"kernel": "quantize_tiles_kernel", "bound": "alu",
+                  "achieved": round(q_achieved, 2), "peak": round(ALU_PEAK_TFLOPS, 1),
+                  "unit": "TFLOP/s", "frac": round(q_achieved / ALU_PEAK_TFLOPS, 4),
+                  "traffic": load_traffic("quantize_tiles_kernel", src_hash),
+                  "hbm_gbps": round(n_tiles * (Q_READ + (K_REC + V_REC) / 2) / (q_launch_ms * 1e-3) / 1e9, 1),
+                  "per_launch": f"{n_tiles} tiles x {flop_tile} FLOP", "launch_ms": round(q_launch_ms, 5)}
+    dec_roof = {"kernel": "decode (pages + merge)", "bound": "hbm",
+                "achieved": round(decode_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(decode_gbps / HBM_PEAK_GBPS, 4),
+                "traffic": load_traffic("decode_pages_kernel", src_hash),
+                "per_launch": f"{B * hkv * full_pages} K+V page pairs x {K_REC + V_REC} B + q/out",
+                "launch_ms": round(d_ms, 5)}
+    dominant, other = (quant_roof, dec_roof) if q_ms >= d_ms else (dec_roof, quant_roof)
+
+    res = {
+        "metric": "decode-attn KV GB/s (% HBM roofline) + tiles quantized/s, k4v2_g128",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16 in/out, f32 compute",
+        "data": "synthetic",
+        "config": {"workload": "one_layer_16k: quantize 2048 K+V tiles + 1 decode step",
+                   "batch": B, "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": 128,
+                   "context": T, "kv_cache_dtype": "kvarn_k4v2_g128", "sinkhorn_iters": n_iters,
+                   "layer_copies_cycled": L, "parallelism": "single GPU"},
+        "value_definition": "algorithmic bytes of one step (quantize: tile in + record out; "
+                            "decode: K+V records + q + out) / step time",
+        "decode_kv_gbps": round(decode_gbps, 1),
+        "decode_hbm_frac": round(decode_gbps / HBM_PEAK_GBPS, 4),
+        "decode_ms": round(d_ms, 5),
+        "quantize_tiles_per_s": round(tiles_per_s, 1),
+        "quantize_ms": round(q_ms, 5),
+        "roofline": dominant,
+        "roofline_other": other,
+        "wall_s_timed": round(t_wall, 4),
+        "source_hash": src_hash,
+    }
+    if not args.no_cpu_baseline:
+        t_step, cores, sample = cpu_baseline(w0, n_iters, args.cpu_budget)
+        res["cpu_baseline"] = {"value": round(step_bytes / t_step / 1e9, 5), "unit": "GB/s",
+                               "cores": cores, "kind": "oracle", "sample": sample,
+                               "seconds_per_step": round(t_step, 3)}
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -204,3 +204,48 @@ def decode_attention(params: Params, q, k_pool, v_pool, block_table, seq_lens, m
                                       _ptr(workspace), workspace.numel(), _ptr(out),
                                       _stream(stream)), "kvarn_decode_attention")
     return out
+
+
+# ----------------------------------------------------------------------------- prepared calls
+
+
+class Prepared:
+    """A C-ABI call with every argument marshalled once; calling it re-issues the same launch
+    (same buffers, same stream) with no per-call Python checks. For benchmark loops and graph
+    capture, where a few microseconds of host work per launch would dominate."""
+
+    def __init__(self, fn, args, what):
+        self._fn, self._args, self._what = fn, args, what
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != 0:
+            raise KvarnError(st, self._what)
+
+
+def prepare_quantize(params: Params, kind: int, src, tile_src_token, tile_dst_page, pool,
+                     stream=None) -> Prepared:
+    _need(src, "src", torch.float16)
+    _need(tile_src_token, "tile_src_token", torch.int64)
+    _need(tile_dst_page, "tile_dst_page", torch.int32)
+    _need(pool, "pool", torch.uint8)
+    hkv = src.shape[1]
+    args = (ctypes.byref(params), kind, _ptr(src), src.stride(0), src.stride(1), src.shape[0],
+            _ptr(tile_src_token), _ptr(tile_dst_page), tile_src_token.numel(), hkv, _ptr(pool),
+            pool.shape[0], _stream(stream))
+    return Prepared(lib.kvarn_quantize_tiles, args, "kvarn_quantize_tiles")
+
+
+def prepare_decode(params: Params, q, k_pool, v_pool, block_table, seq_lens, max_seq_len: int,
+                   workspace, out, k_tail=None, v_tail=None, softmax_scale=None,
+                   stream=None) -> Prepared:
+    _need(q, "q", torch.float16)
+    B, hq = q.shape[0], q.shape[1]
+    hkv = k_pool.shape[1]
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(128)
+    args = (ctypes.byref(params), _ptr(q), B, hq, hkv, _ptr(k_pool), _ptr(v_pool), k_pool.shape[0],
+            _ptr(block_table), block_table.shape[1], _ptr(seq_lens), max_seq_len, _ptr(k_tail),
+            _ptr(v_tail), float(softmax_scale), _ptr(workspace), workspace.numel(), _ptr(out),
+            _stream(stream))
+    return Prepared(lib.kvarn_decode_attention, args, "kvarn_decode_attention")

@@ -8,7 +8,7 @@
 //      normalizer s_t to the std over channels of Xr[:, t] / r, then every channel's r_c to
 //      the std over tokens of Xr[c, :] / s (population std, centred; a zero std leaves the
 //      normalizer unchanged). Accumulating log-std's as the pages describe telescopes to
-//      exactly this assignment, so the kernel keeps r, s directly;
+//      exactly this assignment, so the kernel keeps 1/r, 1/s (rsqrt of the variances);
 //   4. r, s rounded to float16; Y = Xr / (r s^T) against the stored values; asymmetric
 //      round-to-nearest: keys 4-bit, one (scale, zero) per channel; values 2-bit, one per
 //      token; codes packed in the page format of include/kvarn.h.
@@ -29,35 +29,58 @@ namespace {
 constexpr int kThreads = 256;
 
 struct QuantSmem {
-  float red[4][16][16];        // per-wave partials for token-direction reductions
+  float red[2][4][16][8];      // per-wave partials of token-direction reductions (2 buffers)
   uint8_t codes[kTile * kDim]; // K: [token][channel]; V: [channel][token]
   uint16_t meta[4][kDim];      // r, s, scale, zero as float16 bits
 };
 
 // Sum (or min / max) of 8 per-thread values over the 16 token blocks of the tile; every
-// thread receives the totals for its own 8 channels. op: 0 sum, 1 min, 2 max.
+// thread receives the totals for its own 8 channels. op: 0 sum, 1 min, 2 max. `buf`
+// alternates between calls so one barrier per call suffices (a buffer is rewritten only
+// after the other buffer's barrier).
 template <int OP>
-__device__ __forceinline__ void reduce_over_tokens(float (&v)[8], QuantSmem& sm, int w, int l) {
+__device__ __forceinline__ void reduce_over_tokens(float (&v)[8], QuantSmem& sm, int w, int l, int buf) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    if constexpr (OP == 0) v[i] = rows4_sum(v[i]);
-    else if constexpr (OP == 1) v[i] = rows4_min(v[i]);
-    else v[i] = rows4_max(v[i]);
+    const float o = swz_xor_f<16>(v[i]);
+    if constexpr (OP == 0) v[i] += o;
+    else if constexpr (OP == 1) v[i] = fminf(v[i], o);
+    else v[i] = fmaxf(v[i], o);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float o = shfl_xor32_f(v[i]);
+    if constexpr (OP == 0) v[i] += o;
+    else if constexpr (OP == 1) v[i] = fminf(v[i], o);
+    else v[i] = fmaxf(v[i], o);
   }
   const int cb = l & 15;
   if (l < 16) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sm.red[w][cb][i] = v[i];
+    for (int i = 0; i < 8; ++i) sm.red[buf][w][cb][i] = v[i];
   }
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    float a = sm.red[0][cb][i], b = sm.red[1][cb][i], c = sm.red[2][cb][i], d = sm.red[3][cb][i];
+    const float a = sm.red[buf][0][cb][i], b = sm.red[buf][1][cb][i];
+    const float c = sm.red[buf][2][cb][i], d = sm.red[buf][3][cb][i];
     if constexpr (OP == 0) v[i] = (a + b) + (c + d);
     else if constexpr (OP == 1) v[i] = fminf(fminf(a, b), fminf(c, d));
     else v[i] = fmaxf(fmaxf(a, b), fmaxf(c, d));
   }
-  __syncthreads();
+}
+
+// Sum of each of 8 values over the 16 lanes of a row, all values stage by stage so the DPP
+// reads never wait on the instruction just before them.
+__device__ __forceinline__ void row16_sum8(float (&v)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] += dpp_f<kDppQuadXor1>(v[i]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] += dpp_f<kDppQuadXor2>(v[i]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] += dpp_f<kDppHalfMirror>(v[i]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] += dpp_f<kDppRowRor8>(v[i]);
 }
 
 // FWHT of length 128 along channels for each of the thread's 8 tokens, then * 1/sqrt(128).
@@ -98,11 +121,7 @@ __device__ __forceinline__ void fwht_channels(float (&x)[8][8], int cb) {
     for (int i = 0; i < 8; ++i) x[j][i] *= kInvSqrt128;
 }
 
-__device__ __forceinline__ float tree8_sum(const float (&y)[8]) {
-  return ((y[0] + y[1]) + (y[2] + y[3])) + ((y[4] + y[5]) + (y[6] + y[7]));
-}
 
-__device__ __forceinline__ bool usable_std(float var) { return var > 0.f && var < 3.0e38f; }
 
 // The tile quantizer proper. row_ptr(t) gives the 16-byte aligned address of token t's
 // 128 channels. Writes one record at `rec`.
@@ -130,68 +149,87 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
   fwht_channels(x, cb);
 
   // ---- 3. normalize -----------------------------------------------------------------
-  float r[8], s[8];  // r for my channels, s for my tokens
+  // Two passes per step (mean, then centred sum of squares), float32 FMAs. The next step's
+  // weights are 1/std = rsqrt(var). A group whose variance is below 1e-12 mean^2 is constant
+  // up to float32 rounding (a non-constant group of float16-derived values has a relative
+  // spread of at least ~1e-5): its update is skipped, as for an exactly zero std.
+  float ir[8], is[8];      // 1/r for my channels, 1/s for my tokens
+  float vr[8], vs[8];      // last accepted variances (r = sqrt(vr), s = sqrt(vs)); 1 = never
 #pragma unroll
-  for (int i = 0; i < 8; ++i) { r[i] = 1.f; s[i] = 1.f; }
+  for (int i = 0; i < 8; ++i) { ir[i] = 1.f; is[i] = 1.f; vr[i] = 1.f; vs[i] = 1.f; }
+  int buf = 0;
   for (int it = 0; it < n_iters; ++it) {
-    // Products are rounded before they are summed, and sums are balanced trees, so a group
-    // of identical values has a mean equal to that value and a variance of exactly zero.
-    // column step: per token, over the 128 channels (16 lanes of the row x 8 in-thread)
-    float ir[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ir[i] = 1.f / r[i];
+    // column step: per token, over the 128 channels (8 in-thread x 16 lanes of the row)
+    float m[8], q[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      float y[8];
+      float a = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) y[i] = x[j][i] * ir[i];
-      const float mean = row16_sum(tree8_sum(y)) * (1.f / kDim);
+      for (int i = 0; i < 8; ++i) a = fmaf(x[j][i], ir[i], a);
+      m[j] = a;
+    }
+    row16_sum8(m);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      m[j] *= (1.f / kDim);
       float a = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float d = y[i] - mean;
+        const float d = fmaf(x[j][i], ir[i], -m[j]);
         a = fmaf(d, d, a);
       }
-      const float var = row16_sum(a) * (1.f / kDim);
-      if (usable_std(var)) s[j] = sqrtf(var);
+      q[j] = a;
+    }
+    row16_sum8(q);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float var = q[j] * (1.f / kDim);
+      if (var > 1e-12f * m[j] * m[j] && var < 3.0e38f) {
+        vs[j] = var;
+        is[j] = __builtin_amdgcn_rsqf(var);
+      }
     }
     // row step: per channel, over the 128 tokens (8 in-thread x 16 token blocks)
-    float is[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) is[j] = 1.f / s[j];
-    float acc[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float y[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) y[j] = x[j][i] * is[j];
-      acc[i] = tree8_sum(y);
-    }
-    reduce_over_tokens<0>(acc, sm, w, l);
-    float cmean[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) cmean[i] = acc[i] * (1.f / kTile);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       float a = 0.f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float d = x[j][i] * is[j] - cmean[i];
-        a = fmaf(d, d, a);
-      }
-      acc[i] = a;
+      for (int j = 0; j < 8; ++j) a = fmaf(x[j][i], is[j], a);
+      m[i] = a;
     }
-    reduce_over_tokens<0>(acc, sm, w, l);
+    reduce_over_tokens<0>(m, sm, w, l, buf);
+    buf ^= 1;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float var = acc[i] * (1.f / kTile);
-      if (usable_std(var)) r[i] = sqrtf(var);
+      m[i] *= (1.f / kTile);
+      float a = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float d = fmaf(x[j][i], is[j], -m[i]);
+        a = fmaf(d, d, a);
+      }
+      q[i] = a;
     }
+    reduce_over_tokens<0>(q, sm, w, l, buf);
+    buf ^= 1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float var = q[i] * (1.f / kTile);
+      if (var > 1e-12f * m[i] * m[i] && var < 3.0e38f) {
+        vr[i] = var;
+        ir[i] = __builtin_amdgcn_rsqf(var);
+      }
+    }
+  }
+  float r[8], s[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    r[i] = __builtin_amdgcn_sqrtf(vr[i]);
+    s[i] = __builtin_amdgcn_sqrtf(vs[i]);
   }
 
   // ---- 4a. stored normalizers and the normalized tile --------------------------------
   uint16_t r16[8], s16[8];
-  float ir[8], is[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     r16[i] = f2h_rn(fminf(fmaxf(r[i], 6.103515625e-05f), 65504.f));
@@ -215,8 +253,8 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
 #pragma unroll
       for (int j = 1; j < 8; ++j) { mn[i] = fminf(mn[i], x[j][i]); mx[i] = fmaxf(mx[i], x[j][i]); }
     }
-    reduce_over_tokens<1>(mn, sm, w, l);
-    reduce_over_tokens<2>(mx, sm, w, l);
+    reduce_over_tokens<1>(mn, sm, w, l, 0);
+    reduce_over_tokens<2>(mx, sm, w, l, 1);
     uint16_t sc16[8], zr16[8];
     float zr[8], inv[8];
 #pragma unroll

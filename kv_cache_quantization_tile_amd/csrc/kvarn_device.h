@@ -22,9 +22,11 @@ constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;   // lane i <-> 7-i inside each 8-lane half row
 constexpr int kDppRowRor8 = 0x128;      // rotate right by 8 inside a 16-lane row (= xor 8)
 
+// Every control used here reads a lane inside the same 16-lane row, so no lane ever falls
+// back to the bound value; bound_ctrl lets the compiler fold the move into the consumer.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
 // ds_swizzle in bit mode: lane l reads lane ((l & 0x1F) ^ XOR) within its 32-lane half.

@@ -84,6 +84,11 @@ __device__ __forceinline__ void row16_sum8(float (&v)[8]) {
 }
 
 // FWHT of length 128 along channels for each of the thread's 8 tokens, then * 1/sqrt(128).
+// Channel bits 0..2 are in-thread; bits 3..6 are lane bits 0..3. A cross-lane butterfly
+// stage on lane bit m is one fused multiply-add per value: y += c * y(lane ^ m) with c = +1
+// on lanes whose bit m is 0 and -1 on the others. Lanes with the bit set then hold the
+// negated difference; the accumulated sign, (-1)^popcount(lane bits 0..3), is removed by the
+// final scaling.
 __device__ __forceinline__ void fwht_channels(float (&x)[8][8], int cb) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -99,29 +104,26 @@ __device__ __forceinline__ void fwht_channels(float (&x)[8][8], int cb) {
       }
     }
   }
-  // channel bits 3..6 live in lane bits 0..3
-#define KVARN_XSTAGE(M)                                                   \
-  {                                                                       \
-    const bool hi = (cb & (M)) != 0;                                      \
-    _Pragma("unroll") for (int j = 0; j < 8; ++j) {                       \
-      _Pragma("unroll") for (int i = 0; i < 8; ++i) {                     \
-        float p = xor_lane16<M>(x[j][i]);                                 \
-        x[j][i] = hi ? (p - x[j][i]) : (x[j][i] + p);                     \
-      }                                                                   \
-    }                                                                     \
+  const float c1 = (cb & 1) ? -1.f : 1.f, c2 = (cb & 2) ? -1.f : 1.f;
+  const float c4 = (cb & 4) ? -1.f : 1.f, c8 = (cb & 8) ? -1.f : 1.f;
+  // partners of one token's 8 values are fetched before any of them is updated
+#define KVARN_XSTAGE(FETCH, C)                                              \
+  _Pragma("unroll") for (int j = 0; j < 8; ++j) {                           \
+    float p[8];                                                             \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) p[i] = FETCH(x[j][i]);    \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) x[j][i] = fmaf(p[i], C, x[j][i]); \
   }
-  KVARN_XSTAGE(1)
-  KVARN_XSTAGE(2)
-  KVARN_XSTAGE(4)
-  KVARN_XSTAGE(8)
+  KVARN_XSTAGE(dpp_f<kDppQuadXor1>, c1)
+  KVARN_XSTAGE(dpp_f<kDppQuadXor2>, c2)
+  KVARN_XSTAGE(swz_xor_f<4>, c4)
+  KVARN_XSTAGE(dpp_f<kDppRowRor8>, c8)
 #undef KVARN_XSTAGE
+  const float fin = (__builtin_popcount(cb) & 1) ? -kInvSqrt128 : kInvSqrt128;
 #pragma unroll
   for (int j = 0; j < 8; ++j)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[j][i] *= kInvSqrt128;
+    for (int i = 0; i < 8; ++i) x[j][i] *= fin;
 }
-
-
 
 // The tile quantizer proper. row_ptr(t) gives the 16-byte aligned address of token t's
 // 128 channels. Writes one record at `rec`.
@@ -171,11 +173,11 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
     row16_sum8(m);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      m[j] *= (1.f / kDim);
+      m[j] *= -(1.f / kDim);                 // minus the mean
       float a = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float d = fmaf(x[j][i], ir[i], -m[j]);
+        const float d = fmaf(x[j][i], ir[i], m[j]);
         a = fmaf(d, d, a);
       }
       q[j] = a;
@@ -184,10 +186,8 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float var = q[j] * (1.f / kDim);
-      if (var > 1e-12f * m[j] * m[j] && var < 3.0e38f) {
-        vs[j] = var;
-        is[j] = __builtin_amdgcn_rsqf(var);
-      }
+      vs[j] = var > 1e-12f * m[j] * m[j] ? var : vs[j];
+      is[j] = __builtin_amdgcn_rsqf(vs[j]);
     }
     // row step: per channel, over the 128 tokens (8 in-thread x 16 token blocks)
 #pragma unroll
@@ -201,11 +201,11 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
     buf ^= 1;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      m[i] *= (1.f / kTile);
+      m[i] *= -(1.f / kTile);
       float a = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float d = fmaf(x[j][i], is[j], -m[i]);
+        const float d = fmaf(x[j][i], is[j], m[i]);
         a = fmaf(d, d, a);
       }
       q[i] = a;
@@ -215,10 +215,8 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float var = q[i] * (1.f / kTile);
-      if (var > 1e-12f * m[i] * m[i] && var < 3.0e38f) {
-        vr[i] = var;
-        ir[i] = __builtin_amdgcn_rsqf(var);
-      }
+      vr[i] = var > 1e-12f * m[i] * m[i] ? var : vr[i];
+      ir[i] = __builtin_amdgcn_rsqf(vr[i]);
     }
   }
   float r[8], s[8];
@@ -233,14 +231,14 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     r16[i] = f2h_rn(fminf(fmaxf(r[i], 6.103515625e-05f), 65504.f));
-    ir[i] = 1.f / h2f(r16[i]);
+    ir[i] = __builtin_amdgcn_rcpf(h2f(r16[i]));
     s16[i] = f2h_rn(fminf(fmaxf(s[i], 6.103515625e-05f), 65504.f));
-    is[i] = 1.f / h2f(s16[i]);
+    is[i] = __builtin_amdgcn_rcpf(h2f(s16[i]));
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[j][i] = x[j][i] * ir[i] * is[j];
+    for (int i = 0; i < 8; ++i) x[j][i] = (x[j][i] * is[j]) * ir[i];
 
   // ---- 4b. asymmetric RTN -----------------------------------------------------------
   if constexpr (KIND == 0) {
@@ -256,24 +254,24 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
     reduce_over_tokens<1>(mn, sm, w, l, 0);
     reduce_over_tokens<2>(mx, sm, w, l, 1);
     uint16_t sc16[8], zr16[8];
-    float zr[8], inv[8];
+    float inv[8], off[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       sc16[i] = f2h_rn((mx[i] - mn[i]) * (1.f / 15.f));
       zr16[i] = f2h_rn(mn[i]);
-      zr[i] = h2f(zr16[i]);
       const float sc = h2f(sc16[i]);
-      inv[i] = sc > 0.f ? 1.f / sc : 0.f;
+      inv[i] = sc > 0.f ? __builtin_amdgcn_rcpf(sc) : 0.f;
+      off[i] = -h2f(zr16[i]) * inv[i];
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       uint32_t lo = 0, hi = 0;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        float u = __builtin_rintf((x[j][i] - zr[i]) * inv[i]);
-        u = fminf(fmaxf(u, 0.f), 15.f);
-        const uint32_t c = uint32_t(u);
-        if (i < 4) lo |= c << (8 * i); else hi |= c << (8 * (i - 4));
+        // code = clamp(rne((y - zero) / scale), 0, 15), packed one byte per code
+        const float u = __builtin_amdgcn_fmed3f(__builtin_rintf(fmaf(x[j][i], inv[i], off[i])), 0.f, 15.f);
+        if (i < 4) lo = __builtin_amdgcn_cvt_pk_u8_f32(u, i, lo);
+        else hi = __builtin_amdgcn_cvt_pk_u8_f32(u, i - 4, hi);
       }
       *reinterpret_cast<uint2*>(&sm.codes[(8 * tb + j) * kDim + 8 * cb]) = make_uint2(lo, hi);
     }
@@ -301,24 +299,23 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
       mx[j] = row16_max(b);
     }
     uint16_t sc16[8], zr16[8];
-    float zr[8], inv[8];
+    float inv[8], off[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       sc16[j] = f2h_rn((mx[j] - mn[j]) * (1.f / 3.f));
       zr16[j] = f2h_rn(mn[j]);
-      zr[j] = h2f(zr16[j]);
       const float sc = h2f(sc16[j]);
-      inv[j] = sc > 0.f ? 1.f / sc : 0.f;
+      inv[j] = sc > 0.f ? __builtin_amdgcn_rcpf(sc) : 0.f;
+      off[j] = -h2f(zr16[j]) * inv[j];
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       uint32_t lo = 0, hi = 0;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        float u = __builtin_rintf((x[j][i] - zr[j]) * inv[j]);
-        u = fminf(fmaxf(u, 0.f), 3.f);
-        const uint32_t c = uint32_t(u);
-        if (j < 4) lo |= c << (8 * j); else hi |= c << (8 * (j - 4));
+        const float u = __builtin_amdgcn_fmed3f(__builtin_rintf(fmaf(x[j][i], inv[j], off[j])), 0.f, 3.f);
+        if (j < 4) lo = __builtin_amdgcn_cvt_pk_u8_f32(u, j, lo);
+        else hi = __builtin_amdgcn_cvt_pk_u8_f32(u, j - 4, hi);
       }
       *reinterpret_cast<uint2*>(&sm.codes[(8 * cb + i) * kTile + 8 * tb]) = make_uint2(lo, hi);
     }

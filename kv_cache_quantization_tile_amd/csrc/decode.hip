@@ -34,6 +34,7 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kPartStride = 132;  // floats per partial: m, l, pad, pad, acc[128]
+constexpr int kMaxMergeSplits = 4096;  // splits one merge workgroup can weight (LDS)
 
 __device__ __forceinline__ float4v mfma16x16x32(const half8& a, const half8& b, const float4v& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -55,18 +56,27 @@ __device__ __forceinline__ float split16(float x, bool hi) {
   return hi ? h : h2f(f2h_rn(x - h));
 }
 
+// (t & mask) | magic in one 3-input bit operation (truth table 0xEA: S0 & S1 | S2)
+__device__ __forceinline__ uint32_t and_or(uint32_t t, uint32_t mask, uint32_t magic) {
+  return __builtin_amdgcn_bitop3_b32(t, mask, magic, 0xEA);
+}
+
 // key codes of word w, nibble pair v (nibbles v and 4 + v), as float16x2 1 + code / 16
 __device__ __forceinline__ uint32_t k_pair(uint32_t w, int v) {
   const uint32_t t = v == 0 ? (w << 6) : v == 1 ? (w << 2) : v == 2 ? (w >> 2) : (w >> 6);
-  return (t & 0x03C003C0u) | 0x3C003C00u;
+  return and_or(t, 0x03C003C0u, 0x3C003C00u);
 }
 
 // value codes of word w, crumb pair i (crumbs i and 8 + i), as float16x2 1 + code / 4
 __device__ __forceinline__ uint32_t v_pair(uint32_t w, int i) {
   const int sh = 8 - 2 * i;
   const uint32_t t = sh >= 0 ? (w << sh) : (w >> -sh);
-  return (t & 0x03000300u) | 0x3C003C00u;
+  return and_or(t, 0x03000300u, 0x3C003C00u);
 }
+
+// 2^x on the transcendental unit (results below 2^-126 flush to 0, which softmax weights
+// of that size may)
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ void load_h4(const uint8_t* p, float (&o)[4]) {
   const uint2 v = *reinterpret_cast<const uint2*>(p);
@@ -188,8 +198,11 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
         }
       }
       bias = rows4_sum(bpart);
-      bsum = rows4_sum(bs);  // column sum of this lane's B operand over the 128 channels
+      bsum = rows4_sum(bs);                     // column sum of my B operand, 128 channels
+      bsum += dpp_f<kDppRowRor8>(bsum);         // high + low columns
     }
+    // score = s_t * (16 (C_hi + C_lo) - 16 (sum B_hi + sum B_lo) + bias)
+    const float bias16 = fmaf(-16.f, bsum, bias);
 
     // ---- QK ---------------------------------------------------------------------------
     float sc_[8][4];
@@ -213,9 +226,8 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
         load_h4(krec + kKCodeBytes + 256 + (16 * tb + 4 * gq) * 2, st);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float part = fmaf(c[i], 16.f, -16.f * bsum);  // sum_c B_c code_c of my column
-          const float full = part + dpp_f<kDppRowRor8>(part);  // high + low columns
-          sc_[tb][i] = st[i] * (full + bias);
+          const float full = c[i] + dpp_f<kDppRowRor8>(c[i]);  // high + low columns
+          sc_[tb][i] = st[i] * fmaf(full, 16.f, bias16);
         }
       }
     }
@@ -228,7 +240,7 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
       for (int i = 0; i < 4; ++i) mt = fmaxf(mt, sc_[tb][i]);
     mt = rows4_max(mt);
     const float m_new = fmaxf(m_run, mt);
-    const float alpha = exp2f(m_run - m_new);
+    const float alpha = exp2_fast(m_run - m_new);
     float psum = 0.f, bz = 0.f, bsum_p = 0.f;
     H8 bp[4];
     {
@@ -241,7 +253,7 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
         load_h4(vrec + kVCodeBytes + 768 + (16 * tb + 4 * gq) * 2, vz);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = exp2f(sc_[tb][i] - m_new);
+          const float p = exp2_fast(sc_[tb][i] - m_new);
           psum += p;
           const float ps = p * vs[i];
           bz = fmaf(ps, vz[i], bz);
@@ -411,42 +423,70 @@ decode_tail_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t nu
 }
 
 // Merge the splits of one (sequence, query head): log-sum-exp weights, H^T on the page
-// part (rotated space), plus the raw-space tail; float16 output.
-__global__ void __launch_bounds__(64)
+// part (rotated space), plus the raw-space tail; float16 output. One 128-thread workgroup
+// per (query head, sequence): thread c owns channel c; split weights are computed once in
+// LDS, then every thread streams its channel of all partials (independent loads).
+__global__ void __launch_bounds__(128)
 decode_merge_kernel(int32_t num_q_heads, const int32_t* __restrict__ seq_lens, int32_t max_seq_len,
                     int32_t tiles_per_split, int32_t n_splits, int32_t has_tail,
                     const float* __restrict__ ws, __half* __restrict__ out) {
+  __shared__ float wsh[kMaxMergeSplits + 1];
+  __shared__ float red[2][2];
+  __shared__ float xs[kDim];
   const int hq = blockIdx.x, b = blockIdx.y;
-  const int l = threadIdx.x;
+  const int c = threadIdx.x, lane = c & 63, wv = c >> 6;
   int32_t L = seq_lens[b];
   L = L < 0 ? 0 : (L > max_seq_len ? max_seq_len : L);
   const int n_full = L / kTile;
   const int used = (n_full + tiles_per_split - 1) / tiles_per_split;
   const bool tail = has_tail && (L % kTile) != 0;
   const float* base = ws + (int64_t(b) * num_q_heads + hq) * (n_splits + 1) * kPartStride;
+  // 1. global max over the used splits (and the tail)
   float M = -INFINITY;
-  for (int s = 0; s < used; ++s) M = fmaxf(M, base[s * kPartStride]);
-  if (tail) M = fmaxf(M, base[n_splits * kPartStride]);
-  float lt = 0.f, a0 = 0.f, a1 = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < used; ++s) {
-      const float* p = base + s * kPartStride;
-      const float e = exp2f(p[0] - M);
-      lt = fmaf(e, p[1], lt);
-      const float2 v = *reinterpret_cast<const float2*>(p + 4 + 2 * l);
-      a0 = fmaf(e, v.x, a0);
-      a1 = fmaf(e, v.y, a1);
-    }
+  for (int s = c; s < used; s += 128) M = fmaxf(M, base[s * kPartStride]);
+  if (tail && c == 0) M = fmaxf(M, base[n_splits * kPartStride]);
+  for (int off = 32; off >= 1; off >>= 1)
+    M = fmaxf(M, __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ off) << 2, __float_as_int(M))));
+  if (lane == 0) red[0][wv] = M;
+  __syncthreads();
+  M = fmaxf(red[0][0], red[0][1]);
+  // 2. split weights exp2(m_s - M) and the total l
+  float lsum = 0.f;
+  for (int s = c; s < used; s += 128) {
+    const float e = M == -INFINITY ? 0.f : exp2f(base[s * kPartStride] - M);
+    wsh[s] = e;
+    lsum = fmaf(e, base[s * kPartStride + 1], lsum);
   }
-  // H^T (= H) on the rotated accumulator: channel 2l + bit; channel bits 1..6 = lane bits
+  if (c == 0) {
+    const float e = (tail && M != -INFINITY) ? exp2f(base[n_splits * kPartStride] - M) : 0.f;
+    wsh[kMaxMergeSplits] = e;
+    if (tail) lsum = fmaf(e, base[n_splits * kPartStride + 1], lsum);
+  }
+  for (int off = 32; off >= 1; off >>= 1)
+    lsum += __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ off) << 2, __float_as_int(lsum)));
+  if (lane == 0) red[1][wv] = lsum;
+  __syncthreads();
+  lsum = red[1][0] + red[1][1];
+  // 3. weighted sum of the rotated accumulators, channel c
+  float a = 0.f;
+  int s = 0;
+  for (; s + 4 <= used; s += 4) {
+    const float v0 = base[(s + 0) * kPartStride + 4 + c];
+    const float v1 = base[(s + 1) * kPartStride + 4 + c];
+    const float v2 = base[(s + 2) * kPartStride + 4 + c];
+    const float v3 = base[(s + 3) * kPartStride + 4 + c];
+    a = fmaf(wsh[s], v0, a);
+    a = fmaf(wsh[s + 1], v1, a);
+    a = fmaf(wsh[s + 2], v2, a);
+    a = fmaf(wsh[s + 3], v3, a);
+  }
+  for (; s < used; ++s) a = fmaf(wsh[s], base[s * kPartStride + 4 + c], a);
+  // 4. H^T = H over the 128 channels: bits 0..5 across the lanes of a wave, bit 6 via LDS
   {
-    float x0 = a0 + a1, x1 = a0 - a1;
-#define KVARN_MSTAGE(M_, FN)                                 \
-    {                                                        \
-      const bool up = (l & (M_)) != 0;                       \
-      const float p0 = FN(x0), p1 = FN(x1);                  \
-      x0 = up ? (p0 - x0) : (x0 + p0);                       \
-      x1 = up ? (p1 - x1) : (x1 + p1);                       \
+#define KVARN_MSTAGE(M_, FN)                          \
+    {                                                 \
+      const float p = FN(a);                          \
+      a = (lane & (M_)) ? (p - a) : (a + p);          \
     }
     KVARN_MSTAGE(1, dpp_f<kDppQuadXor1>)
     KVARN_MSTAGE(2, dpp_f<kDppQuadXor2>)
@@ -455,20 +495,15 @@ decode_merge_kernel(int32_t num_q_heads, const int32_t* __restrict__ seq_lens, i
     KVARN_MSTAGE(16, swz_xor_f<16>)
     KVARN_MSTAGE(32, shfl_xor32_f)
 #undef KVARN_MSTAGE
-    a0 = x0 * kInvSqrt128;
-    a1 = x1 * kInvSqrt128;
+    xs[c] = a;
+    __syncthreads();
+    const float p = xs[c ^ 64];
+    a = (c & 64) ? (p - a) : (a + p);
+    a *= kInvSqrt128;
   }
-  if (tail) {
-    const float* p = base + n_splits * kPartStride;
-    const float e = exp2f(p[0] - M);
-    lt = fmaf(e, p[1], lt);
-    const float2 v = *reinterpret_cast<const float2*>(p + 4 + 2 * l);
-    a0 = fmaf(e, v.x, a0);
-    a1 = fmaf(e, v.y, a1);
-  }
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  __half* o = out + (int64_t(b) * num_q_heads + hq) * kDim + 2 * l;
-  *reinterpret_cast<uint32_t*>(o) = uint32_t(f2h_rn(a0 * inv)) | (uint32_t(f2h_rn(a1 * inv)) << 16);
+  if (tail) a = fmaf(wsh[kMaxMergeSplits], base[n_splits * kPartStride + 4 + c], a);
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  out[(int64_t(b) * num_q_heads + hq) * kDim + c] = __float2half_rn(a * inv);
 }
 
 }  // namespace
@@ -476,9 +511,12 @@ decode_merge_kernel(int32_t num_q_heads, const int32_t* __restrict__ seq_lens, i
 int32_t decode_tiles_per_wave(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len) {
   const int64_t max_full = max_seq_len / kTile;
   const int64_t work = int64_t(batch) * num_kv_heads * max_full;
-  int64_t tpw = (work + 4095) / 4096;
+  int64_t tpw = (work + 4095) / 4096;       // aim at ~4096 page-waves of work per wave slot
   if (tpw < 1) tpw = 1;
   if (tpw > 64) tpw = 64;
+  // the merge weighs at most kMaxMergeSplits splits of 4 * tpw pages each
+  const int64_t need = (max_full + 4LL * kMaxMergeSplits - 1) / (4LL * kMaxMergeSplits);
+  if (tpw < need) tpw = need;
   return int32_t(tpw);
 }
 
@@ -522,7 +560,7 @@ hipError_t launch_decode(const void* q, int32_t batch, int32_t num_q_heads, int3
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(num_q_heads, batch), dim3(64), 0, stream,
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(num_q_heads, batch), dim3(128), 0, stream,
                      num_q_heads, seq_lens, max_seq_len, 4 * tpw, ns, has_tail ? 1 : 0,
                      static_cast<const float*>(ws), static_cast<__half*>(out));
   return hipGetLastError();

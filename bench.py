@@ -116,6 +116,9 @@ def main():
                     help="distinct layer copies cycled across steps (defeats the 256 MB MALL)")
     ap.add_argument("--sinkhorn-iters", type=int, default=8)
     ap.add_argument("--context", type=int, default=16384)
+    ap.add_argument("--workload", choices=["one_layer_16k", "prefill_burst"], default="one_layer_16k",
+                    help="one_layer_16k: batch 1 one decoder layer (default, the headline line); "
+                         "prefill_burst: 64 sequences x 16384 tokens (131072 tiles) + one batched decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
@@ -136,12 +139,15 @@ def main():
     dev = torch.device("cuda:0")
     n_iters = args.sinkhorn_iters
     params = K.params_from_dtype("kvarn_k4v2_g128", n_iters)
-    L = max(1, args.layers)
-    print(f"[bench] generating {L} layer copies of one_layer_16k (context {args.context})",
+    L = max(1, args.layers) if args.workload == "one_layer_16k" else 1
+    print(f"[bench] generating {L} copies of {args.workload} (context {args.context})",
           file=sys.stderr, flush=True)
     layers = []
     for i in range(L):
-        w = synth.one_layer(device=dev, seed=1 + i, context=args.context)
+        if args.workload == "one_layer_16k":
+            w = synth.one_layer(device=dev, seed=1 + i, context=args.context)
+        else:
+            w = synth.prefill_burst(device=dev, seed=4 + i, context=args.context, n_iters=n_iters)
         q = w.step_inputs(0)[0]
         n_pages = w.num_pages
         kp = K.new_pool(n_pages, w.hkv, K.KIND_K)
@@ -226,7 +232,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f16 in/out, f32 compute",
         "data": "synthetic",
-        "config": {"workload": "one_layer_16k: quantize 2048 K+V tiles + 1 decode step",
+        "config": {"workload": f"{args.workload}: quantize {2 * n_tiles} K+V tiles + 1 decode step",
                    "batch": B, "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": 128,
                    "context": T, "kv_cache_dtype": "kvarn_k4v2_g128", "sinkhorn_iters": n_iters,
                    "layer_copies_cycled": L, "parallelism": "single GPU"},

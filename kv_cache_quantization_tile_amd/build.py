@@ -22,6 +22,8 @@ FLAGS = [
     # packed-FP32 VALU forms stay out of the generated code (hipcc emits them from plain
     # float code otherwise)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results straight into VGPRs (no accumulation-register copies)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-result", "-fvisibility=hidden",
 ]
 

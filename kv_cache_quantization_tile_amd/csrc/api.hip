@@ -174,6 +174,8 @@ kvarn_status kvarn_decode_attention(const kvarn_params* params, const void* q, i
   if ((k_tail == nullptr) != (v_tail == nullptr)) return KVARN_ERR_INVALID_ARG;
   if (max_seq_len >= 128) {
     if (!k_pool || !v_pool || !block_table) return KVARN_ERR_INVALID_ARG;
+    // page records are addressed by a 32-bit index page * num_kv_heads + head
+    if (pool_num_pages * int64_t(num_kv_heads) > (int64_t(1) << 32)) return KVARN_ERR_UNSUPPORTED;
     if (block_table_stride < max_seq_len / 128) return KVARN_ERR_INVALID_ARG;
     if (!aligned16(k_pool) || !aligned16(v_pool)) return KVARN_ERR_INVALID_ARG;
   }

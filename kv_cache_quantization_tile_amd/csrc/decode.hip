@@ -16,12 +16,20 @@
 //   PV: A = value codes (rows = 16 channels, k = 32 tokens), B = p s scale (high / low),
 //       C = partial outputs. The k-order of the tokens in a PV step is the order in which
 //       the QK C-fragments hold them, which is the value record's crumb order.
-// Codes enter the MFMA as normal float16 numbers 1 + code/16 (keys: the nibble is moved into
-// mantissa bits 6..9 under the exponent of 1.0) and 1 + code/4 (values: the crumb into bits
-// 8..9). The MFMA then returns sum_k B_k + sum_k B_k code_k / 16 (or / 4); the kernel subtracts
-// the column sum of its own B operand, a cancellation of about 3x. Subnormal operands are
-// avoided on purpose: the matrix core accumulates products of subnormal inputs with visibly
-// less than float32 precision.
+// Codes enter the MFMA as normal float16 numbers 1 + code * 2^(b - 10): the code bits are
+// masked into mantissa bits b.. under the exponent of 1.0, with b chosen per code position so
+// that few shifts are needed (keys b = 2 or 6, values b = 6 or 8); the B operand carries the
+// factor 2^(10 - b). The MFMA then returns sum_k B_k + sum_k B'_k code_k, and the column sum
+// sum_k B_k is removed through the accumulator's initial value together with the zero-point
+// term. Subnormal operands are avoided on purpose: the matrix core accumulates products of
+// subnormal inputs with visibly less than float32 precision.
+//
+// Per page, each wave first derives the float32 factors it needs (2 channels and 2 tokens per
+// lane) into its own LDS slot; every other lane then reads them with vector LDS loads. The two
+// lanes of a high / low column pair split the work of building the B operands and of the
+// softmax (rows 0,1 of each C fragment on the high lane, rows 2,3 on the low lane) and swap
+// halves with bank-masked DPP moves. B operands are scaled by a power of two per page so that
+// their largest float16 high part is near 2^14 (no overflow, full low-part precision).
 #include "kvarn_device.h"
 #include "kvarn_launch.h"
 
@@ -61,17 +69,21 @@ __device__ __forceinline__ uint32_t and_or(uint32_t t, uint32_t mask, uint32_t m
   return __builtin_amdgcn_bitop3_b32(t, mask, magic, 0xEA);
 }
 
-// key codes of word w, nibble pair v (nibbles v and 4 + v), as float16x2 1 + code / 16
+// Key codes of word w, nibble pair v (nibbles v and 4 + v = channels 2v and 2v + 1 of the
+// word's 8), as float16x2 1 + code * 2^(b - 10): the nibbles go to mantissa bits b..b+3 with
+// b = 2 for even v and b = 6 for odd v, so two shifted copies of the word serve all four pairs.
+// The operand on the other side carries the matching factor 2^(10 - b) (256 or 16).
 __device__ __forceinline__ uint32_t k_pair(uint32_t w, int v) {
-  const uint32_t t = v == 0 ? (w << 6) : v == 1 ? (w << 2) : v == 2 ? (w >> 2) : (w >> 6);
-  return and_or(t, 0x03C003C0u, 0x3C003C00u);
+  const uint32_t t = v < 2 ? (w << 2) : (w >> 6);
+  return and_or(t, (v & 1) ? 0x03C003C0u : 0x003C003Cu, 0x3C003C00u);
 }
 
-// value codes of word w, crumb pair i (crumbs i and 8 + i), as float16x2 1 + code / 4
+// Value codes of word w, crumb pair i (crumbs i and 8 + i), as float16x2 1 + code * 2^(b - 10):
+// b = 8 for even i, 6 for odd i (factor 4 or 16 on the other side); four shifted copies.
 __device__ __forceinline__ uint32_t v_pair(uint32_t w, int i) {
-  const int sh = 8 - 2 * i;
+  const int sh = i == 0 ? 8 : i <= 2 ? 4 : i <= 4 ? 0 : i <= 6 ? -4 : -8;
   const uint32_t t = sh >= 0 ? (w << sh) : (w >> -sh);
-  return and_or(t, 0x03000300u, 0x3C003C00u);
+  return and_or(t, (i & 1) ? 0x00C000C0u : 0x03000300u, 0x3C003C00u);
 }
 
 // 2^x on the transcendental unit (results below 2^-126 flush to 0, which softmax weights
@@ -96,11 +108,108 @@ __device__ __forceinline__ void load_h8(const uint8_t* p, float* o) {
   }
 }
 
+// Per wave: the float32 factors of the page being processed.
+//   ka[c] = r_c scale_c 2^(10-b_c) ks      kb[c] = ks r_c zero_c - ka[c]     kt[t] = s_t / ks
+//   vp[t] = s_t scale_t 2^(10-b_t) vs      vz[t] = vs s_t zero_t - vp[t]     vr[c] = r_c / vs
+// (ks, vs: the page's powers of two for the B operands.)
+struct WaveMeta {
+  float4 ka[kDim / 4], kb[kDim / 4];   // read 4 channels at a time
+  float2 kt[kTile / 2], vp[kTile / 2], vz[kTile / 2];   // read 2 tokens at a time
+  float4 vr[kDim / 4];
+};
+
 struct DecodeSmem {
   float m[4][8];
   float l[4][8];
   float acc[4][8][kDim];
+  WaveMeta meta[4];
 };
+
+// Raw loads of one page: key codes (16 B per 16-token block), value codes (8 B per
+// 16-channel block), and entries 2l, 2l+1 of the 4 float16 metadata arrays of each record.
+struct PageRegs {
+  uint4 kc[8];
+  uint2 vc[8];
+  uint32_t km[4], vm[4];
+};
+
+// Global-memory byte pointer (address space 1): loads through it use a scalar base plus a
+// 32-bit per-lane offset.
+typedef const uint8_t __attribute__((address_space(1)))* gbytes;
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T>
+__device__ __forceinline__ T gload(gbytes base, uint32_t off) {
+  return *reinterpret_cast<const T __attribute__((address_space(1)))*>(base + off);
+}
+__device__ __forceinline__ uint4 gload4(gbytes base, uint32_t off) {
+  const u32x4 v = gload<u32x4>(base, off);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 gload2(gbytes base, uint32_t off) {
+  const u32x2 v = gload<u32x2>(base, off);
+  return make_uint2(v.x, v.y);
+}
+
+__device__ __forceinline__ void load_meta(PageRegs& t, gbytes krec, gbytes vrec, int l) {
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    t.km[a] = gload<uint32_t>(krec, uint32_t(kKCodeBytes + 256 * a + 4 * l));
+    t.vm[a] = gload<uint32_t>(vrec, uint32_t(kVCodeBytes + 256 * a + 4 * l));
+  }
+}
+__device__ __forceinline__ void load_kcodes(PageRegs& t, gbytes krec, int n, int gq) {
+#pragma unroll
+  for (int tb = 0; tb < 8; ++tb) t.kc[tb] = gload4(krec, uint32_t((16 * tb + n) * 64 + 16 * gq));
+}
+__device__ __forceinline__ void load_vcodes(PageRegs& t, gbytes vrec, int n, int gq) {
+#pragma unroll
+  for (int bb = 0; bb < 8; ++bb) t.vc[bb] = gload2(vrec, uint32_t((16 * bb + n) * 32 + 8 * gq));
+}
+
+__device__ __forceinline__ float lo_h(uint32_t w) { return h2f(uint16_t(w & 0xFFFF)); }
+__device__ __forceinline__ float hi_h(uint32_t w) { return h2f(uint16_t(w >> 16)); }
+
+__device__ __forceinline__ float wave_max(float v) { return rows4_max(row16_max(v)); }
+
+// Exponent k = 14 - e for x = m 2^e, m in [0.5, 1): x 2^k lies in [2^13, 2^14). 0 when x is
+// zero or not finite; clamped to +-100.
+__device__ __forceinline__ int pow2_norm_exp(float x) {
+  if (!(x > 0.f) || !(x <= 3.4e38f)) return 0;
+  const int k = 14 - __builtin_amdgcn_frexp_expf(x);
+  return k < -100 ? -100 : (k > 100 ? 100 : k);
+}
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// float16x2 high parts of (a, b) and low parts f16(a - f16(a)), f16(b - f16(b)): one packed
+// conversion and two mixed-precision FMAs that read the float16 high parts back in place
+__device__ __forceinline__ void split_pk(float a, float b, uint32_t& hi, uint32_t& lo) {
+  uint32_t h, r;
+  asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(h) : "v"(a), "v"(b));
+  asm("v_fma_mixlo_f16 %0, %1, 1.0, -%2 op_sel_hi:[0,0,1]" : "=v"(r) : "v"(a), "v"(h));
+  asm("v_fma_mixhi_f16 %0, %1, 1.0, -%2 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "+v"(r) : "v"(b), "v"(h));
+  hi = h;
+  lo = r;
+}
+
+// Per-lane choice between two values by an all-ones / all-zero mask (one 3-input bit
+// operation, truth table 0xCA: S0 ? S1 : S2 bitwise)
+__device__ __forceinline__ float pick(uint32_t mask, float if_set, float if_clear) {
+  return __uint_as_float(__builtin_amdgcn_bitop3_b32(mask, __float_as_uint(if_set),
+                                                     __float_as_uint(if_clear), 0xCA));
+}
+
+// DPP row_ror:8 move that only writes the lanes of the given banks (bank k = lanes 4k..4k+3
+// of each 16-lane row); the other lanes keep `old`.
+template <int BANKS>
+__device__ __forceinline__ uint32_t swap8_into(uint32_t old, uint32_t src) {
+  return uint32_t(__builtin_amdgcn_update_dpp(int(old), int(src), kDppRowRor8, 0xF, BANKS, false));
+}
+constexpr int kHiBanks = 0x3;   // lanes 0..7 of a row: high-part columns
+constexpr int kLoBanks = 0xC;   // lanes 8..15: low-part columns
 
 // One workgroup: (split, KV head g, sequence b). Wave w handles page slots
 // split * 4 * tpw + w + 4 k, k < tpw. Writes one partial (m, l, acc) per query head.
@@ -123,11 +232,20 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
   const int n = l & 15, gq = l >> 4;
   const int h = n & 7;
   const bool hi = n < 8;
+  const int side = hi ? 0 : 2;          // first C row this lane finishes (rows side, side+1)
   const bool head_ok = h < G;
+  // all ones on low-part lanes; opaque to the optimizer so that selections by it stay
+  // single bit-selects instead of becoming variable vector indices
+  uint32_t lo_mask = uint32_t(int32_t(uint32_t(l) << 28) >> 31);
+  asm volatile("" : "+v"(lo_mask));
 
-  // ---- q_rot = H q * softmax_scale * log2(e): lane holds channels 32 gq + j ----------
-  float qr[32];
+  // ---- q_rot = H q * softmax_scale * log2(e): channels 32 gq + j ---------------------
+  // Each lane keeps the 16 channels whose B-operand entries it builds:
+  // qo[4 s + j] = channel 32 gq + 8 s + 2 side + j.
+  float qo[16];
+  float maxq;
   {
+    float qr[32];
     const __half* qrow = q + (int64_t(b) * num_q_heads + int64_t(g) * G + (head_ok ? h : 0)) * kDim + 32 * gq;
 #pragma unroll
     for (int k = 0; k < 4; ++k) load_h8(reinterpret_cast<const uint8_t*>(qrow + 8 * k), &qr[8 * k]);
@@ -157,63 +275,125 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
       const float p = shfl_xor32_f(qr[j]);
       qr[j] = up32 ? (p - qr[j]) : (qr[j] + p);
     }
+    float mq = 0.f;
 #pragma unroll
-    for (int j = 0; j < 32; ++j) qr[j] *= qscale;  // includes 1/sqrt(128) of H
+    for (int j = 0; j < 32; ++j) {
+      qr[j] *= qscale;  // includes 1/sqrt(128) of H
+      mq = fmaxf(mq, fabsf(qr[j]));
+    }
+    maxq = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max(mq))));
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) qo[4 * s + j] = hi ? qr[8 * s + j] : qr[8 * s + 4 + j];
   }
 
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY, l_part = 0.f;
   float acc[8][4];
 #pragma unroll
   for (int bb = 0; bb < 8; ++bb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[bb][i] = 0.f;
 
-  for (int k = 0; k < tpw; ++k) {
-    const int slot = slot0 + w + 4 * k;
-    if (slot >= n_full) break;
-    const int64_t page = block_table[int64_t(b) * bt_stride + slot];
-    if (page < 0 || page >= pool_num_pages) continue;
-    const uint8_t* krec = k_pool + (page * num_kv_heads + g) * int64_t(kKRecord);
-    const uint8_t* vrec = v_pool + (page * num_kv_heads + g) * int64_t(kVRecord);
+  WaveMeta& wm = sm.meta[w];
+  // key channel 2l + j: nibble pair v = l % 4 -> b = 2 (even v) or 6; value token 2l + j:
+  // C row (2l + j) % 4 -> crumb pair parity -> b = 8 (rows 0,1) or 6 (rows 2,3)
+  const float fk = (l & 1) ? 16.f : 256.f;
+  const float fv = (l & 1) ? 16.f : 4.f;
 
-    // ---- B operand of QK: q'' for my 32 channels; bias q_rot . (r * zero) ------------
-    H8 bq[4];
-    float bias, bsum;
+  const int32_t* bt_row = block_table + int64_t(b) * bt_stride;
+  auto page_of = [&](int slot) -> int64_t {
+    if (slot >= n_full) return -1;
+    const int32_t page = __builtin_amdgcn_readfirstlane(bt_row[slot]);
+    return (page < 0 || page >= pool_num_pages) ? -1 : int64_t(page);
+  };
+  // record addresses are wave-uniform: keep them in scalar registers so that the loads use
+  // a scalar base plus a 32-bit lane offset
+  auto uniform_ptr = [](const uint8_t* p) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo32 = __builtin_amdgcn_readfirstlane(uint32_t(a));
+    const uint32_t hi32 = __builtin_amdgcn_readfirstlane(uint32_t(a >> 32));
+    return reinterpret_cast<gbytes>((uint64_t(hi32) << 32) | lo32);
+  };
+  // record index page * num_kv_heads + g fits 32 bits (the pool's record count is checked
+  // on the host); byte offsets are 32 x 32 -> 64-bit products
+  auto krec_of = [&](int64_t page) {
+    const uint32_t r = uint32_t(page) * uint32_t(num_kv_heads) + uint32_t(g);
+    return uniform_ptr(k_pool + uint64_t(r) * uint32_t(kKRecord));
+  };
+  auto vrec_of = [&](int64_t page) {
+    const uint32_t r = uint32_t(page) * uint32_t(num_kv_heads) + uint32_t(g);
+    return uniform_ptr(v_pool + uint64_t(r) * uint32_t(kVRecord));
+  };
+  // Processes the page held in t; each part of t is reloaded with page `next` as soon as
+  // this page has consumed it, so the loads overlap the rest of the page's work.
+  auto process = [&](PageRegs& t, int64_t next) {
+    // ---- page factors into the wave's LDS slot ------------------------------------------
     {
-      float bpart = 0.f, bs = 0.f;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {  // channels 32 gq + 8 s + (0..7) = k-step s
-        float rr[8], sc8[8], zr8[8];
-        load_h8(krec + kKCodeBytes + 0 * 256 + (32 * gq + 8 * s) * 2, rr);
-        load_h8(krec + kKCodeBytes + 2 * 256 + (32 * gq + 8 * s) * 2, sc8);
-        load_h8(krec + kKCodeBytes + 3 * 256 + (32 * gq + 8 * s) * 2, zr8);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) bpart = fmaf(qr[8 * s + j] * rr[j], zr8[j], bpart);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float b0 = split16(qr[8 * s + 2 * v] * rr[2 * v] * sc8[2 * v], hi);
-          const float b1 = split16(qr[8 * s + 2 * v + 1] * rr[2 * v + 1] * sc8[2 * v + 1], hi);
-          bs += b0 + b1;
-          bq[s].u[v] = pack_h2(b0, b1);
-        }
-      }
-      bias = rows4_sum(bpart);
-      bsum = rows4_sum(bs);                     // column sum of my B operand, 128 channels
-      bsum += dpp_f<kDppRowRor8>(bsum);         // high + low columns
+      const float rk0 = lo_h(t.km[0]), rk1 = hi_h(t.km[0]);
+      const float ka0 = rk0 * lo_h(t.km[2]) * fk, ka1 = rk1 * hi_h(t.km[2]) * fk;
+      const float sv0 = lo_h(t.vm[1]), sv1 = hi_h(t.vm[1]);
+      const float vp0 = sv0 * lo_h(t.vm[2]) * fv, vp1 = sv1 * hi_h(t.vm[2]) * fv;
+      const float mka = wave_max(fmaxf(ka0, ka1));
+      const float mvp = wave_max(fmaxf(vp0, vp1));
+      const int eks = pow2_norm_exp(maxq * __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mka))));
+      const int evs = pow2_norm_exp(__int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mvp))));
+      const float ks = __builtin_ldexpf(1.f, eks), iks = __builtin_ldexpf(1.f, -eks);
+      const float vs = __builtin_ldexpf(1.f, evs), ivs = __builtin_ldexpf(1.f, -evs);
+      const float a0 = ka0 * ks, a1 = ka1 * ks;
+      reinterpret_cast<float2*>(wm.ka)[l] = make_float2(a0, a1);
+      reinterpret_cast<float2*>(wm.kb)[l] =
+          make_float2(fmaf(ks * rk0, lo_h(t.km[3]), -a0), fmaf(ks * rk1, hi_h(t.km[3]), -a1));
+      wm.kt[l] = make_float2(lo_h(t.km[1]) * iks, hi_h(t.km[1]) * iks);
+      const float p0 = vp0 * vs, p1 = vp1 * vs;
+      wm.vp[l] = make_float2(p0, p1);
+      wm.vz[l] =
+          make_float2(fmaf(vs * sv0, lo_h(t.vm[3]), -p0), fmaf(vs * sv1, hi_h(t.vm[3]), -p1));
+      reinterpret_cast<float2*>(wm.vr)[l] = make_float2(lo_h(t.vm[0]) * ivs, hi_h(t.vm[0]) * ivs);
     }
-    // score = s_t * (16 (C_hi + C_lo) - 16 (sum B_hi + sum B_lo) + bias)
-    const float bias16 = fmaf(-16.f, bsum, bias);
+    if (next >= 0) load_meta(t, krec_of(next), vrec_of(next), l);
+    // LDS operations of one wave complete in order: the writes above land before the reads
+    // below, and after the previous page's reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // ---- QK ---------------------------------------------------------------------------
-    float sc_[8][4];
+    // ---- B operand of QK (q'' high / low), bias + column-sum correction ---------------
+    H8 bq[4];
+    float bias;
     {
-      uint4 kc[8];
+      float bpart = 0.f;
 #pragma unroll
-      for (int tb = 0; tb < 8; ++tb)
-        kc[tb] = *reinterpret_cast<const uint4*>(krec + (16 * tb + n) * 64 + 16 * gq);
+      for (int s = 0; s < 4; ++s) {
+        const int c4 = 8 * gq + 2 * s + (side >> 1);   // channels 4 c4 .. 4 c4 + 3
+        const float4 ka = wm.ka[c4];
+        const float4 kb = wm.kb[c4];
+        const float* q4 = &qo[4 * s];
+        bpart = fmaf(q4[0], kb.x, bpart);
+        bpart = fmaf(q4[1], kb.y, bpart);
+        bpart = fmaf(q4[2], kb.z, bpart);
+        bpart = fmaf(q4[3], kb.w, bpart);
+        uint32_t h01, l01, h23, l23;
+        split_pk(q4[0] * ka.x, q4[1] * ka.y, h01, l01);
+        split_pk(q4[2] * ka.z, q4[3] * ka.w, h23, l23);
+        // dwords 0,1 = channels 0..3 of the 8 (built by the high lane), 2,3 = channels 4..7
+        bq[s].u[0] = swap8_into<kLoBanks>(h01, l01);
+        bq[s].u[1] = swap8_into<kLoBanks>(h23, l23);
+        bq[s].u[2] = swap8_into<kHiBanks>(l01, h01);
+        bq[s].u[3] = swap8_into<kHiBanks>(l23, h23);
+      }
+      bpart += dpp_f<kDppRowRor8>(bpart);
+      bias = pick(lo_mask, 0.f, rows4_sum(bpart));   // added once: on the high columns
+    }
+
+    // ---- QK: this lane finishes rows side, side+1 of each fragment -------------------------
+    float sc[8][2];
+    {
+      const float4v binit = {bias, bias, bias, bias};
+      const uint4* kc = t.kc;
 #pragma unroll
       for (int tb = 0; tb < 8; ++tb) {
-        float4v c = {0.f, 0.f, 0.f, 0.f};
+        float4v c = binit;
         const uint32_t dw[4] = {kc[tb].x, kc[tb].y, kc[tb].z, kc[tb].w};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -222,65 +402,69 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
           for (int v = 0; v < 4; ++v) a.u[v] = k_pair(dw[s], v);
           c = mfma16x16x32(a.v, bq[s].v, c);
         }
-        float st[4];
-        load_h4(krec + kKCodeBytes + 256 + (16 * tb + 4 * gq) * 2, st);
+        const float2 st = wm.kt[8 * tb + 2 * gq + (side >> 1)];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float full = c[i] + dpp_f<kDppRowRor8>(c[i]);  // high + low columns
-          sc_[tb][i] = st[i] * fmaf(full, 16.f, bias16);
+        for (int j = 0; j < 2; ++j) {
+          // high lane: own c[j] + partner c[j]; low lane: own c[2+j] + partner c[2+j]
+          const float mine = pick(lo_mask, c[2 + j], c[j]);
+          const float send = pick(lo_mask, c[j], c[2 + j]);
+          sc[tb][j] = (mine + dpp_f<kDppRowRor8>(send)) * (j ? st.y : st.x);
         }
       }
     }
+    if (next >= 0) load_kcodes(t, krec_of(next), n, gq);
 
     // ---- online softmax ------------------------------------------------------------------
-    float mt = sc_[0][0];
+    float mt = fmaxf(sc[0][0], sc[0][1]);
 #pragma unroll
-    for (int tb = 0; tb < 8; ++tb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mt = fmaxf(mt, sc_[tb][i]);
+    for (int tb = 1; tb < 8; ++tb) mt = fmaxf(mt, fmaxf(sc[tb][0], sc[tb][1]));
+    mt = fmaxf(mt, dpp_f<kDppRowRor8>(mt));
     mt = rows4_max(mt);
     const float m_new = fmaxf(m_run, mt);
     const float alpha = exp2_fast(m_run - m_new);
-    float psum = 0.f, bz = 0.f, bsum_p = 0.f;
     H8 bp[4];
+    float vcorr;
     {
-      float pw[8][4];
-#pragma unroll
-      for (int tb = 0; tb < 8; ++tb) {
-        float vs[4], vsc[4], vz[4];
-        load_h4(vrec + kVCodeBytes + 256 + (16 * tb + 4 * gq) * 2, vs);
-        load_h4(vrec + kVCodeBytes + 512 + (16 * tb + 4 * gq) * 2, vsc);
-        load_h4(vrec + kVCodeBytes + 768 + (16 * tb + 4 * gq) * 2, vz);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = exp2_fast(sc_[tb][i] - m_new);
-          psum += p;
-          const float ps = p * vs[i];
-          bz = fmaf(ps, vz[i], bz);
-          pw[tb][i] = split16(ps * vsc[i], hi);
-          bsum_p += pw[tb][i];
-        }
-      }
+      float psum = 0.f, zpart = 0.f;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        bp[s].u[0] = pack_h2(pw[2 * s][0], pw[2 * s][1]);
-        bp[s].u[1] = pack_h2(pw[2 * s][2], pw[2 * s][3]);
-        bp[s].u[2] = pack_h2(pw[2 * s + 1][0], pw[2 * s + 1][1]);
-        bp[s].u[3] = pack_h2(pw[2 * s + 1][2], pw[2 * s + 1][3]);
+        uint32_t hh[2], ll[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int tb = 2 * s + e;
+          const int t2 = 8 * tb + 2 * gq + (side >> 1);   // tokens 2 t2, 2 t2 + 1
+          const float2 vp = wm.vp[t2];
+          const float2 vz = wm.vz[t2];
+          const float p0 = exp2_fast(sc[tb][0] - m_new), p1 = exp2_fast(sc[tb][1] - m_new);
+          psum += p0 + p1;
+          zpart = fmaf(p0, vz.x, fmaf(p1, vz.y, zpart));
+          split_pk(p0 * vp.x, p1 * vp.y, hh[e], ll[e]);
+        }
+        // dword 0 = rows 0,1 of fragment 2s (high lane built them), 1 = rows 2,3 (low lane),
+        // 2, 3 the same for fragment 2s + 1
+        bp[s].u[0] = swap8_into<kLoBanks>(hh[0], ll[0]);
+        bp[s].u[1] = swap8_into<kHiBanks>(ll[0], hh[0]);
+        bp[s].u[2] = swap8_into<kLoBanks>(hh[1], ll[1]);
+        bp[s].u[3] = swap8_into<kHiBanks>(ll[1], hh[1]);
       }
+      zpart += dpp_f<kDppRowRor8>(zpart);
+      vcorr = pick(lo_mask, 0.f, rows4_sum(zpart));  // added once: on the high columns
+      l_part = fmaf(l_part, alpha, psum);
     }
-    psum = rows4_sum(psum);
-    bz = rows4_sum(bz);
-    // the MFMA returns sum_t B_t (1 + code_t / 4); remove the 1s, add the zero-point term
-    const float corr = fmaf(-4.f, rows4_sum(bsum_p), hi ? bz : 0.f);
-    l_run = fmaf(l_run, alpha, psum);
     m_run = m_new;
 
     // ---- PV ---------------------------------------------------------------------------
+    if (!__all(alpha == 1.f)) {   // some head's running maximum moved: rescale in place
+#pragma unroll
+      for (int bb = 0; bb < 8; ++bb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[bb][i] *= alpha;
+    }
+    const float4v vinit = {vcorr, vcorr, vcorr, vcorr};
 #pragma unroll
     for (int bb = 0; bb < 8; ++bb) {
-      const uint2 vc = *reinterpret_cast<const uint2*>(vrec + (16 * bb + n) * 32 + 8 * gq);
-      float4v c = {0.f, 0.f, 0.f, 0.f};
+      const uint2 vc = t.vc[bb];
+      float4v c = vinit;
 #pragma unroll
       for (int d = 0; d < 2; ++d) {
         const uint32_t word = d ? vc.y : vc.x;
@@ -292,14 +476,34 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
           c = mfma16x16x32(a.v, bp[2 * d + hs].v, c);
         }
       }
-      float rv[4];
-      load_h4(vrec + kVCodeBytes + (16 * bb + 4 * gq) * 2, rv);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float o = fmaf(c[i], 4.f, corr);
-        acc[bb][i] = fmaf(acc[bb][i], alpha, rv[i] * o);
-      }
+      const float4 rv = wm.vr[4 * bb + gq];
+      acc[bb][0] = fmaf(rv.x, c[0], acc[bb][0]);
+      acc[bb][1] = fmaf(rv.y, c[1], acc[bb][1]);
+      acc[bb][2] = fmaf(rv.z, c[2], acc[bb][2]);
+      acc[bb][3] = fmaf(rv.w, c[3], acc[bb][3]);
     }
+    if (next >= 0) load_vcodes(t, vrec_of(next), n, gq);
+  };
+
+  PageRegs t;
+  int64_t cur = page_of(slot0 + w);
+  if (cur >= 0) {
+    load_meta(t, krec_of(cur), vrec_of(cur), l);
+    load_kcodes(t, krec_of(cur), n, gq);
+    load_vcodes(t, vrec_of(cur), n, gq);
+  }
+  for (int k = 0; k < tpw; ++k) {
+    const int slot = slot0 + w + 4 * k;
+    if (slot >= n_full) break;
+    const int64_t next = k + 1 < tpw ? page_of(slot + 4) : -1;
+    if (cur >= 0) {
+      process(t, next);
+    } else if (next >= 0) {
+      load_meta(t, krec_of(next), vrec_of(next), l);
+      load_kcodes(t, krec_of(next), n, gq);
+      load_vcodes(t, vrec_of(next), n, gq);
+    }
+    cur = next;
   }
 
   // ---- combine the high / low columns, then the 4 waves --------------------------------
@@ -307,6 +511,8 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
   for (int bb = 0; bb < 8; ++bb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[bb][i] += dpp_f<kDppRowRor8>(acc[bb][i]);
+  l_part += dpp_f<kDppRowRor8>(l_part);
+  const float l_run = rows4_sum(l_part);
   if (hi) {
     if (gq == 0) {
       sm.m[w][h] = m_run;

@@ -235,6 +235,15 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
     s16[i] = f2h_rn(fminf(fmaxf(s[i], 6.103515625e-05f), 65504.f));
     is[i] = __builtin_amdgcn_rcpf(h2f(s16[i]));
   }
+  // lanes of wave 0, row 0 hold every channel's r; the lanes of column 0 every token's s
+  if (tb == 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sm.meta[0][8 * cb + i] = r16[i];
+  }
+  if (cb == 0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sm.meta[1][8 * tb + j] = s16[j];
+  }
 #pragma unroll
   for (int j = 0; j < 8; ++j)
 #pragma unroll
@@ -263,6 +272,13 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
       inv[i] = sc > 0.f ? __builtin_amdgcn_rcpf(sc) : 0.f;
       off[i] = -h2f(zr16[i]) * inv[i];
     }
+    if (tb == 0) {  // every channel's group statistics
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        sm.meta[2][8 * cb + i] = sc16[i];
+        sm.meta[3][8 * cb + i] = zr16[i];
+      }
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       uint32_t lo = 0, hi = 0;
@@ -274,18 +290,6 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
         else hi = __builtin_amdgcn_cvt_pk_u8_f32(u, i - 4, hi);
       }
       *reinterpret_cast<uint2*>(&sm.codes[(8 * tb + j) * kDim + 8 * cb]) = make_uint2(lo, hi);
-    }
-    if (tb == 0) {  // lanes of wave 0, row 0 hold every channel's group statistics
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        sm.meta[0][8 * cb + i] = r16[i];
-        sm.meta[2][8 * cb + i] = sc16[i];
-        sm.meta[3][8 * cb + i] = zr16[i];
-      }
-    }
-    if (cb == 0) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sm.meta[1][8 * tb + j] = s16[j];
     }
   } else {
     // values: one group per token, over the 128 channels
@@ -319,14 +323,9 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
       }
       *reinterpret_cast<uint2*>(&sm.codes[(8 * cb + i) * kTile + 8 * tb]) = make_uint2(lo, hi);
     }
-    if (tb == 0) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sm.meta[0][8 * cb + i] = r16[i];
-    }
     if (cb == 0) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        sm.meta[1][8 * tb + j] = s16[j];
         sm.meta[2][8 * tb + j] = sc16[j];
         sm.meta[3][8 * tb + j] = zr16[j];
       }
@@ -388,8 +387,9 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
   }
 }
 
+// Four workgroups per CU (16 waves) keep a whole layer's tiles resident in one round.
 template <int KIND>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 quantize_tiles_kernel(const __half* __restrict__ src, int64_t token_stride, int64_t head_stride,
                       int64_t src_num_tokens, const int64_t* __restrict__ tile_src_token,
                       const int32_t* __restrict__ tile_dst_page, int32_t num_kv_heads,

@@ -129,6 +129,19 @@ KVARN_API kvarn_status kvarn_quantize_tiles(const kvarn_params* params, kvarn_ki
                                   int32_t num_kv_heads, void* pool_dev,
                                   int64_t pool_num_pages, void* stream);
 
+/* Keys and values of the same tiles in one launch: exactly kvarn_quantize_tiles(KVARN_K) on
+ * k_src_dev into k_pool_dev plus kvarn_quantize_tiles(KVARN_V) on v_src_dev into v_pool_dev
+ * (same tile list), with every argument as described there. The two sources share strides
+ * and token count; both pools have pool_num_pages pages of num_kv_heads records. A cache
+ * write produces keys and values together; one launch keeps the GPU busy across both. */
+KVARN_API kvarn_status kvarn_quantize_kv_tiles(const kvarn_params* params, const void* k_src_dev,
+                                     const void* v_src_dev, int64_t src_token_stride,
+                                     int64_t src_head_stride, int64_t src_num_tokens,
+                                     const int64_t* tile_src_token_dev,
+                                     const int32_t* tile_dst_page_dev, int32_t n_tiles,
+                                     int32_t num_kv_heads, void* k_pool_dev, void* v_pool_dev,
+                                     int64_t pool_num_pages, void* stream);
+
 /* Append one decode token per sequence into the float16 staging tiles, and quantize every
  * staging tile that this append fills (the 128th token) into its page.
  *

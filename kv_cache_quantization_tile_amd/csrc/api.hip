@@ -115,6 +115,29 @@ kvarn_status kvarn_quantize_tiles(const kvarn_params* params, kvarn_kind kind, c
       static_cast<hipStream_t>(stream)));
 }
 
+kvarn_status kvarn_quantize_kv_tiles(const kvarn_params* params, const void* k_src,
+                                     const void* v_src, int64_t src_token_stride,
+                                     int64_t src_head_stride, int64_t src_num_tokens,
+                                     const int64_t* tile_src_token, const int32_t* tile_dst_page,
+                                     int32_t n_tiles, int32_t num_kv_heads, void* k_pool,
+                                     void* v_pool, int64_t pool_num_pages, void* stream) {
+  const kvarn_status st = kvarn_params_check(params);
+  if (st != KVARN_OK) return st;
+  if (n_tiles < 0 || num_kv_heads <= 0 || num_kv_heads > 65535 || src_num_tokens < 0 ||
+      pool_num_pages < 0 || src_token_stride < 0 || src_head_stride < 0)
+    return KVARN_ERR_INVALID_ARG;
+  if (n_tiles == 0) return KVARN_OK;
+  if (!k_src || !v_src || !tile_src_token || !tile_dst_page || !k_pool || !v_pool)
+    return KVARN_ERR_INVALID_ARG;
+  if (!aligned16(k_src) || !aligned16(v_src) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      (src_token_stride % 8) != 0 || (src_head_stride % 8) != 0)
+    return KVARN_ERR_INVALID_ARG;
+  return launch_status(kvarn::launch_quantize_kv(
+      k_src, v_src, src_token_stride, src_head_stride, src_num_tokens, tile_src_token,
+      tile_dst_page, n_tiles, num_kv_heads, k_pool, v_pool, pool_num_pages,
+      params->sinkhorn_iters, static_cast<hipStream_t>(stream)));
+}
+
 kvarn_status kvarn_append_tokens(const kvarn_params* params, const void* k_new, const void* v_new,
                                  int32_t batch, int32_t num_kv_heads, const int32_t* seq_lens,
                                  void* k_tail, void* v_tail, const int32_t* block_table,

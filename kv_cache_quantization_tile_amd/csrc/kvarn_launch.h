@@ -13,6 +13,12 @@ hipError_t launch_quantize_tiles(int kind, const void* src, int64_t token_stride
                                  int32_t n_tiles, int32_t num_kv_heads, void* pool,
                                  int64_t pool_num_pages, int n_iters, hipStream_t stream);
 
+hipError_t launch_quantize_kv(const void* k_src, const void* v_src, int64_t token_stride,
+                              int64_t head_stride, int64_t src_num_tokens,
+                              const int64_t* tile_src_token, const int32_t* tile_dst_page,
+                              int32_t n_tiles, int32_t num_kv_heads, void* k_pool, void* v_pool,
+                              int64_t pool_num_pages, int n_iters, hipStream_t stream);
+
 hipError_t launch_append_tokens(const void* k_new, const void* v_new, int32_t batch,
                                 int32_t num_kv_heads, const int32_t* seq_lens, void* k_tail,
                                 void* v_tail, const int32_t* block_table, int32_t bt_stride,

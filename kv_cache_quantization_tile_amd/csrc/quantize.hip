@@ -407,6 +407,29 @@ quantize_tiles_kernel(const __half* __restrict__ src, int64_t token_stride, int6
   quantize_tile<KIND>(row_ptr, rec, n_iters, sm);
 }
 
+// Keys and values of the same tiles in one launch: grid (n_tiles, num_kv_heads, 2), z = kind.
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+quantize_kv_kernel(const __half* __restrict__ k_src, const __half* __restrict__ v_src,
+                   int64_t token_stride, int64_t head_stride, int64_t src_num_tokens,
+                   const int64_t* __restrict__ tile_src_token,
+                   const int32_t* __restrict__ tile_dst_page, int32_t num_kv_heads,
+                   uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
+                   int64_t pool_num_pages, int n_iters) {
+  __shared__ QuantSmem sm;
+  const int tile = blockIdx.x;
+  const int h = blockIdx.y;
+  const bool is_k = blockIdx.z == 0;
+  const int64_t t0 = tile_src_token[tile];
+  const int64_t page = tile_dst_page[tile];
+  if (t0 < 0 || t0 > src_num_tokens - kTile || page < 0 || page >= pool_num_pages) return;
+  const __half* base = (is_k ? k_src : v_src) + t0 * token_stride + int64_t(h) * head_stride;
+  auto row_ptr = [=](int t) { return base + int64_t(t) * token_stride; };
+  if (is_k)
+    quantize_tile<0>(row_ptr, k_pool + (page * num_kv_heads + h) * int64_t(kKRecord), n_iters, sm);
+  else
+    quantize_tile<1>(row_ptr, v_pool + (page * num_kv_heads + h) * int64_t(kVRecord), n_iters, sm);
+}
+
 // Append one token per (sequence, head) into staging; quantize the staging tile it fills.
 // grid: (batch, num_kv_heads, 2 kinds)
 __global__ void __launch_bounds__(kThreads)
@@ -459,6 +482,20 @@ hipError_t launch_quantize_tiles(int kind, const void* src, int64_t token_stride
                        tile_src_token, tile_dst_page, num_kv_heads, static_cast<uint8_t*>(pool),
                        pool_num_pages, n_iters);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_kv(const void* k_src, const void* v_src, int64_t token_stride,
+                              int64_t head_stride, int64_t src_num_tokens,
+                              const int64_t* tile_src_token, const int32_t* tile_dst_page,
+                              int32_t n_tiles, int32_t num_kv_heads, void* k_pool, void* v_pool,
+                              int64_t pool_num_pages, int n_iters, hipStream_t stream) {
+  dim3 grid(n_tiles, num_kv_heads, 2), block(kThreads);
+  hipLaunchKernelGGL(quantize_kv_kernel, grid, block, 0, stream,
+                     static_cast<const __half*>(k_src), static_cast<const __half*>(v_src),
+                     token_stride, head_stride, src_num_tokens, tile_src_token, tile_dst_page,
+                     num_kv_heads, static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool),
+                     pool_num_pages, n_iters);
   return hipGetLastError();
 }
 

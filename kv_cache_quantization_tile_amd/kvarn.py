@@ -51,6 +51,8 @@ def _load():
         "kvarn_page_bytes": (sz, [P, ctypes.c_int]),
         "kvarn_quantize_tiles": (ctypes.c_int, [P, ctypes.c_int, vp, i64, i64, i64, vp, vp, i32,
                                                 i32, vp, i64, vp]),
+        "kvarn_quantize_kv_tiles": (ctypes.c_int, [P, vp, vp, i64, i64, i64, vp, vp, i32, i32,
+                                                   vp, vp, i64, vp]),
         "kvarn_append_tokens": (ctypes.c_int, [P, vp, vp, i32, i32, vp, vp, vp, vp, i32, vp, vp,
                                                i64, vp]),
         "kvarn_decode_workspace_bytes": (sz, [P, i32, i32, i32, i32]),
@@ -68,7 +70,7 @@ def _load():
 lib = _load()
 EXPORTED = ("kvarn_abi_version", "kvarn_format_version", "kvarn_status_str",
             "kvarn_params_from_dtype", "kvarn_params_check", "kvarn_page_bytes",
-            "kvarn_quantize_tiles", "kvarn_append_tokens", "kvarn_decode_workspace_bytes",
+            "kvarn_quantize_tiles", "kvarn_quantize_kv_tiles", "kvarn_append_tokens", "kvarn_decode_workspace_bytes",
             "kvarn_decode_num_splits", "kvarn_decode_attention")
 
 
@@ -138,6 +140,40 @@ def quantize_tiles(params: Params, kind: int, src: torch.Tensor, tile_src_token:
                                     _ptr(tile_dst_page), n, hkv, _ptr(pool), pool.shape[0],
                                     _stream(stream)), "kvarn_quantize_tiles")
     return pool
+
+
+def _kv_quant_args(params, k_src, v_src, tile_src_token, tile_dst_page, k_pool, v_pool, stream):
+    for t, nm in ((k_src, "k_src"), (v_src, "v_src")):
+        _need(t, nm, torch.float16)
+        if t.dim() != 3 or t.shape[2] != 128 or t.stride(2) != 1:
+            raise ValueError(f"{nm} must be [tokens, Hkv, 128] with unit channel stride")
+    if k_src.shape != v_src.shape or k_src.stride() != v_src.stride():
+        raise ValueError("k_src and v_src must have the same shape and strides")
+    _need(tile_src_token, "tile_src_token", torch.int64)
+    _need(tile_dst_page, "tile_dst_page", torch.int32)
+    hkv = k_src.shape[1]
+    for t, nm, kind in ((k_pool, "k_pool", KIND_K), (v_pool, "v_pool", KIND_V)):
+        _need(t, nm, torch.uint8)
+        nb = page_bytes(params, kind)
+        if t.dim() != 3 or t.shape[1] != hkv or t.shape[2] != nb or not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous [pages, {hkv}, {nb}]")
+    if k_pool.shape[0] != v_pool.shape[0]:
+        raise ValueError("k_pool and v_pool must have the same number of pages")
+    n = tile_src_token.numel()
+    if tile_dst_page.numel() != n:
+        raise ValueError("tile_src_token and tile_dst_page differ in length")
+    return (ctypes.byref(params), _ptr(k_src), _ptr(v_src), k_src.stride(0), k_src.stride(1),
+            k_src.shape[0], _ptr(tile_src_token), _ptr(tile_dst_page), n, hkv, _ptr(k_pool),
+            _ptr(v_pool), k_pool.shape[0], _stream(stream))
+
+
+def quantize_kv_tiles(params: Params, k_src, v_src, tile_src_token, tile_dst_page, k_pool,
+                      v_pool, stream=None):
+    """Quantize the same tiles of keys and values ([tokens, Hkv, 128] float16) in one launch."""
+    _check(lib.kvarn_quantize_kv_tiles(*_kv_quant_args(params, k_src, v_src, tile_src_token,
+                                                       tile_dst_page, k_pool, v_pool, stream)),
+           "kvarn_quantize_kv_tiles")
+    return k_pool, v_pool
 
 
 def append_tokens(params: Params, k_new, v_new, seq_lens, k_tail, v_tail, block_table,
@@ -234,6 +270,13 @@ def prepare_quantize(params: Params, kind: int, src, tile_src_token, tile_dst_pa
             _ptr(tile_src_token), _ptr(tile_dst_page), tile_src_token.numel(), hkv, _ptr(pool),
             pool.shape[0], _stream(stream))
     return Prepared(lib.kvarn_quantize_tiles, args, "kvarn_quantize_tiles")
+
+
+def prepare_quantize_kv(params: Params, k_src, v_src, tile_src_token, tile_dst_page, k_pool,
+                        v_pool, stream=None) -> Prepared:
+    args = _kv_quant_args(params, k_src, v_src, tile_src_token, tile_dst_page, k_pool, v_pool,
+                          stream)
+    return Prepared(lib.kvarn_quantize_kv_tiles, args, "kvarn_quantize_kv_tiles")
 
 
 def prepare_decode(params: Params, q, k_pool, v_pool, block_table, seq_lens, max_seq_len: int,

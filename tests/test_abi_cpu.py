@@ -84,6 +84,31 @@ def test_quantize_validation():
     assert K.lib.kvarn_quantize_tiles(None, 0, FAKE, 8, 8, 1, FAKE, FAKE, 1, 1, FAKE, 1, None) == INVALID
 
 
+def _quant_kv(p, **kw):
+    a = dict(ksrc=FAKE, vsrc=FAKE, ts=1024, hs=128, ntok=4096, tok=FAKE, page=FAKE, n=1, hkv=8,
+             kpool=FAKE, vpool=FAKE, npages=10)
+    a.update(kw)
+    return K.lib.kvarn_quantize_kv_tiles(ctypes.byref(p), a["ksrc"], a["vsrc"], a["ts"], a["hs"],
+                                         a["ntok"], a["tok"], a["page"], a["n"], a["hkv"],
+                                         a["kpool"], a["vpool"], a["npages"], None)
+
+
+def test_quantize_kv_validation():
+    p = K.params_from_dtype()
+    assert _quant_kv(p, n=0) == OK
+    assert _quant_kv(p, ksrc=None) == INVALID
+    assert _quant_kv(p, vsrc=None) == INVALID
+    assert _quant_kv(p, vpool=None) == INVALID
+    assert _quant_kv(p, page=None) == INVALID
+    assert _quant_kv(p, n=-1) == INVALID
+    assert _quant_kv(p, hkv=0) == INVALID
+    assert _quant_kv(p, hs=100) == INVALID            # stride not a multiple of 8
+    assert _quant_kv(p, vsrc=ctypes.c_void_p(0x10004)) == INVALID
+    assert _quant_kv(p, kpool=ctypes.c_void_p(0x10008)) == INVALID
+    assert _quant_kv(p, npages=-1) == INVALID
+    assert _quant_kv(K.Params(128, 128, 4, 4, 128, 8)) == UNSUP
+
+
 def _decode(p, **kw):
     a = dict(q=FAKE, B=2, hq=64, hkv=8, kp=FAKE, vp=FAKE, npages=100, bt=FAKE, bts=200, sl=FAKE,
              mx=16384, kt=None, vt=None, scale=0.088, ws=FAKE, wsb=1 << 30, out=FAKE)

@@ -134,6 +134,35 @@ def test_quantize_deterministic(K):
         assert torch.equal(a, b)
 
 
+def test_quantize_kv_matches_separate_launches(K):
+    """The one-launch K+V entry point writes exactly the records of the two per-kind calls
+    (same kernels), on mixed tiles over 2 heads with permuted pages; the oracle then checks
+    the records of the combined call."""
+    n, hkv = 10, 2
+    tk, kinds = synth.tile_batch(n * hkv, "cpu", seed=31, return_kinds=True)
+    tv = synth.tile_batch(n * hkv, "cpu", seed=32)
+    mk = lambda t: t.view(n, hkv, 128, 128).permute(0, 2, 1, 3).reshape(n * 128, hkv, 128).contiguous()
+    ksrc, vsrc = mk(tk), mk(tv)
+    g = torch.Generator().manual_seed(6)
+    order = torch.randperm(n, generator=g)
+    tok = (order * 128).to(torch.int64)
+    pages = torch.randperm(n + 3, generator=g)[:n].to(torch.int32)
+    params = K.params_from_dtype("kvarn_k4v2_g128", 8)
+    say(f"quantize_kv_tiles n={n} hkv={hkv}")
+    kp, vp = K.new_pool(n + 3, hkv, O.KIND_K), K.new_pool(n + 3, hkv, O.KIND_V)
+    K.quantize_kv_tiles(params, ksrc.cuda(), vsrc.cuda(), tok.cuda(), pages.cuda(), kp, vp)
+    kref = _quantize(K, params, O.KIND_K, ksrc.cuda(), tok.cuda(), pages.cuda(), n + 3)
+    vref = _quantize(K, params, O.KIND_V, vsrc.cuda(), tok.cuda(), pages.cuda(), n + 3)
+    assert torch.equal(kp, kref) and torch.equal(vp, vref)
+    st = T.QuantStats()
+    for h in range(hkv):
+        ill = [i for i, o in enumerate(order.tolist()) if kinds[o * hkv + h] == synth.OFFSET_TILE_KIND]
+        T.check_quantized_tiles(_tiles_from_src(ksrc, tok.tolist(), h),
+                                T.records_of(kp, pages.tolist(), h), O.KIND_K, 8, st, ill_conditioned=ill)
+    say(st)
+    T.assert_rate(st)
+
+
 # ----------------------------------------------------------------------------- decode
 
 

@@ -15,8 +15,11 @@
 //
 // Thread layout: thread (wave w, lane l) owns the 8x8 block channels 8cb..8cb+7 x tokens
 // 8tb..8tb+7 with cb = l % 16 and tb = 4w + l / 16. Reductions over channels stay inside a
-// 16-lane row (DPP); reductions over tokens combine the 4 rows of a wave (swizzle /
-// bpermute) and the 4 waves through LDS. The tile stays in registers (64 fp32 / thread).
+// 16-lane row (DPP); reductions over tokens combine the 4 rows of a wave (row-pair swaps)
+// and the 4 waves through LDS. Both are reduce-scatters: each group's statistic lands on one
+// owner lane, which computes the group's weight once and broadcasts it back through LDS.
+// The tile stays in registers (64 fp32 / thread). Key codes are packed in registers (a
+// thread's 8 channels of one token are one record word); value codes go through LDS.
 #include "kvarn_device.h"
 #include "kvarn_launch.h"
 
@@ -29,58 +32,85 @@ namespace {
 constexpr int kThreads = 256;
 
 struct QuantSmem {
-  float red[2][4][16][8];      // per-wave partials of token-direction reductions (2 buffers)
-  uint8_t codes[kTile * kDim]; // K: [token][channel]; V: [channel][token]
+  float red[2][4][kDim];       // per-wave partial sums over tokens, per channel (2 buffers)
+  float gr[4][2][kDim];        // per-wave broadcast of per-channel values
+  float gc[4][4][2][8];        // per-wave, per-row broadcast of per-token values
+  uint8_t codes[kTile * kDim]; // value codes, [channel][token]
   uint16_t meta[4][kDim];      // r, s, scale, zero as float16 bits
 };
 
-// Sum (or min / max) of 8 per-thread values over the 16 token blocks of the tile; every
-// thread receives the totals for its own 8 channels. op: 0 sum, 1 min, 2 max. `buf`
-// alternates between calls so one barrier per call suffices (a buffer is rewritten only
-// after the other buffer's barrier).
+constexpr int kDppRowRor4 = 0x124;  // rotate right by 4 inside a 16-lane row
+
+template <int OP>  // 0 sum, 1 min, 2 max
+__device__ __forceinline__ float combine(float a, float b) {
+  if constexpr (OP == 0) return a + b;
+  else if constexpr (OP == 1) return fminf(a, b);
+  else return fmaxf(a, b);
+}
+
+// Reduce-scatter over the 16 lanes of a row: every lane holds v[0..7] (one value per token
+// of its token block); lane l returns the row-wide reduction of v[l & 7] (lanes l and l ^ 8
+// agree). Each stage keeps the half of the values whose index bit matches the lane bit and
+// adds the partner's copy of that half: bits 0 and 1 with quad permutes, bit 2 with a
+// rotation by 4 (any partner with the other bit 2 works, since bit 3 is summed last).
 template <int OP>
-__device__ __forceinline__ void reduce_over_tokens(float (&v)[8], QuantSmem& sm, int w, int l, int buf) {
+__device__ __forceinline__ float row16_scatter8(const float (&v)[8], int l) {
+  const bool b0 = (l & 1) != 0, b1 = (l & 2) != 0, b2 = (l & 4) != 0;
+  float a[4], c[2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float o = swz_xor_f<16>(v[i]);
-    if constexpr (OP == 0) v[i] += o;
-    else if constexpr (OP == 1) v[i] = fminf(v[i], o);
-    else v[i] = fmaxf(v[i], o);
+  for (int k = 0; k < 4; ++k) {
+    const float send = b0 ? v[2 * k] : v[2 * k + 1];
+    const float keep = b0 ? v[2 * k + 1] : v[2 * k];
+    a[k] = combine<OP>(keep, dpp_f<kDppQuadXor1>(send));
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float o = shfl_xor32_f(v[i]);
-    if constexpr (OP == 0) v[i] += o;
-    else if constexpr (OP == 1) v[i] = fminf(v[i], o);
-    else v[i] = fmaxf(v[i], o);
+  for (int k = 0; k < 2; ++k) {
+    const float send = b1 ? a[2 * k] : a[2 * k + 1];
+    const float keep = b1 ? a[2 * k + 1] : a[2 * k];
+    c[k] = combine<OP>(keep, dpp_f<kDppQuadXor2>(send));
   }
-  const int cb = l & 15;
-  if (l < 16) {
+  const float send = b2 ? c[0] : c[1];
+  const float keep = b2 ? c[1] : c[0];
+  const float e = combine<OP>(keep, dpp_f<kDppRowRor4>(send));
+  return combine<OP>(e, dpp_f<kDppRowRor8>(e));
+}
+
+// Reduce-scatter over the 4 rows of a wave with the row-pair swaps of gfx950: every lane
+// holds v[0..7] (one value per channel of its channel block); a lane of row r returns the
+// reduction over the 4 rows of v[k + off(r)], k = 0, 1, off(r) = 4 (r & 1) + 2 (r >> 1).
+template <int OP>
+__device__ __forceinline__ void rows4_scatter8(const float (&v)[8], float (&o)[2]) {
+  float u[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sm.red[buf][w][cb][i] = v[i];
+  for (int i = 0; i < 4; ++i) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + 4]),
+                                                    false, false);
+    u[i] = combine<OP>(__uint_as_float(p[0]), __uint_as_float(p[1]));
   }
-  __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float a = sm.red[buf][0][cb][i], b = sm.red[buf][1][cb][i];
-    const float c = sm.red[buf][2][cb][i], d = sm.red[buf][3][cb][i];
-    if constexpr (OP == 0) v[i] = (a + b) + (c + d);
-    else if constexpr (OP == 1) v[i] = fminf(fminf(a, b), fminf(c, d));
-    else v[i] = fmaxf(fmaxf(a, b), fmaxf(c, d));
+  for (int i = 0; i < 2; ++i) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(u[i]), __float_as_uint(u[i + 2]),
+                                                    false, false);
+    o[i] = combine<OP>(__uint_as_float(p[0]), __uint_as_float(p[1]));
   }
 }
 
-// Sum of each of 8 values over the 16 lanes of a row, all values stage by stage so the DPP
-// reads never wait on the instruction just before them.
-__device__ __forceinline__ void row16_sum8(float (&v)[8]) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] += dpp_f<kDppQuadXor1>(v[i]);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] += dpp_f<kDppQuadXor2>(v[i]);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] += dpp_f<kDppHalfMirror>(v[i]);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] += dpp_f<kDppRowRor8>(v[i]);
+__device__ __forceinline__ void lds_read8(const float* p, float (&v)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+// float16 bits of a normalizer: clipped to [2^-14, 65504] first
+__device__ __forceinline__ uint16_t normalizer16(float v) {
+  return f2h_rn(fminf(fmaxf(v, 6.103515625e-05f), 65504.f));
+}
+
+// 4 key codes (bytes, each <= 15) -> 4 nibbles in the low 16 bits, byte k -> nibble k
+__device__ __forceinline__ uint32_t bytes_to_nibbles(uint32_t e) {
+  const uint32_t x = (e | (e >> 4)) & 0x00FF00FFu;
+  return (x | (x >> 8)) & 0x0000FFFFu;
 }
 
 // FWHT of length 128 along channels for each of the thread's 8 tokens, then * 1/sqrt(128).
@@ -151,29 +181,57 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
   fwht_channels(x, cb);
 
   // ---- 3. normalize -----------------------------------------------------------------
-  // Two passes per step (mean, then centred sum of squares), float32 FMAs. The next step's
-  // weights are 1/std = rsqrt(var). A group whose variance is below 1e-12 mean^2 is constant
-  // up to float32 rounding (a non-constant group of float16-derived values has a relative
-  // spread of at least ~1e-5): its update is skipped, as for an exactly zero std.
+  // Two passes per step (mean, then centred sum of squares), float32 FMAs. A group's
+  // statistics are reduce-scattered to one owner lane: token 8 tb + (l & 7) for the column
+  // step (over channels), channels 8 cb + off + {0, 1} for the row step (over tokens; the
+  // 4 waves add their partials through LDS); the owner computes the group's weight and LDS
+  // broadcasts it back inside the wave. The next step's weights are 1/std = rsqrt(var). A
+  // group whose variance is below 1e-12 mean^2 is constant up to float32 rounding (a
+  // non-constant group of float16-derived values has a relative spread of at least ~1e-5):
+  // its update is skipped, as for an exactly zero std.
+  const int r = l >> 4;
+  const int tok_own = l & 7;
+  const int ch_off = 4 * (r & 1) + 2 * (r >> 1);
+  const int ch_own = 8 * cb + ch_off;
+  float* gc0 = &sm.gc[w][r][0][0];
+  float* gc1 = &sm.gc[w][r][1][0];
+  float* gr0 = &sm.gr[w][0][0];
+  float* gr1 = &sm.gr[w][1][0];
   float ir[8], is[8];      // 1/r for my channels, 1/s for my tokens
-  float vr[8], vs[8];      // last accepted variances (r = sqrt(vr), s = sqrt(vs)); 1 = never
 #pragma unroll
-  for (int i = 0; i < 8; ++i) { ir[i] = 1.f; is[i] = 1.f; vr[i] = 1.f; vs[i] = 1.f; }
+  for (int i = 0; i < 8; ++i) { ir[i] = 1.f; is[i] = 1.f; }
+  float vs_own = 1.f;                  // last accepted variance of my token (1 = never)
+  float vr_own[2] = {1.f, 1.f};        // ... of my two channels
   int buf = 0;
+  auto cross_wave_sum = [&](const float (&o)[2], float (&t)[2]) {
+    *reinterpret_cast<float2*>(&sm.red[buf][w][ch_own]) = make_float2(o[0], o[1]);
+    __syncthreads();
+    float2 a = *reinterpret_cast<const float2*>(&sm.red[buf][0][ch_own]);
+#pragma unroll
+    for (int ww = 1; ww < 4; ++ww) {
+      const float2 b = *reinterpret_cast<const float2*>(&sm.red[buf][ww][ch_own]);
+      a.x += b.x;
+      a.y += b.y;
+    }
+    t[0] = a.x;
+    t[1] = a.y;
+    buf ^= 1;
+  };
   for (int it = 0; it < n_iters; ++it) {
-    // column step: per token, over the 128 channels (8 in-thread x 16 lanes of the row)
+    // column step: per token, over the 128 channels
     float m[8], q[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      float a = 0.f;
+      float a = x[j][0] * ir[0];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) a = fmaf(x[j][i], ir[i], a);
+      for (int i = 1; i < 8; ++i) a = fmaf(x[j][i], ir[i], a);
       m[j] = a;
     }
-    row16_sum8(m);
+    const float mean_t = row16_scatter8<0>(m, l) * (1.f / kDim);
+    gc0[tok_own] = -mean_t;
+    lds_read8(gc0, m);                       // minus the means of my 8 tokens
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      m[j] *= -(1.f / kDim);                 // minus the mean
       float a = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -182,26 +240,29 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
       }
       q[j] = a;
     }
-    row16_sum8(q);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float var = q[j] * (1.f / kDim);
-      vs[j] = var > 1e-12f * m[j] * m[j] ? var : vs[j];
-      is[j] = __builtin_amdgcn_rsqf(vs[j]);
+    {
+      const float var = row16_scatter8<0>(q, l) * (1.f / kDim);
+      vs_own = var > 1e-12f * mean_t * mean_t ? var : vs_own;
+      gc0[tok_own] = __builtin_amdgcn_rsqf(vs_own);
+      lds_read8(gc0, is);
     }
-    // row step: per channel, over the 128 tokens (8 in-thread x 16 token blocks)
+    // row step: per channel, over the 128 tokens
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      float a = 0.f;
+      float a = x[0][i] * is[0];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) a = fmaf(x[j][i], is[j], a);
+      for (int j = 1; j < 8; ++j) a = fmaf(x[j][i], is[j], a);
       m[i] = a;
     }
-    reduce_over_tokens<0>(m, sm, w, l, buf);
-    buf ^= 1;
+    float o[2], mean_c[2];
+    rows4_scatter8<0>(m, o);
+    cross_wave_sum(o, mean_c);
+    mean_c[0] *= 1.f / kTile;
+    mean_c[1] *= 1.f / kTile;
+    *reinterpret_cast<float2*>(&gr0[ch_own]) = make_float2(-mean_c[0], -mean_c[1]);
+    lds_read8(&gr0[8 * cb], m);             // minus the means of my 8 channels
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      m[i] *= -(1.f / kTile);
       float a = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -210,49 +271,47 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
       }
       q[i] = a;
     }
-    reduce_over_tokens<0>(q, sm, w, l, buf);
-    buf ^= 1;
+    float var_c[2];
+    rows4_scatter8<0>(q, o);
+    cross_wave_sum(o, var_c);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float var = q[i] * (1.f / kTile);
-      vr[i] = var > 1e-12f * m[i] * m[i] ? var : vr[i];
-      ir[i] = __builtin_amdgcn_rsqf(vr[i]);
+    for (int k = 0; k < 2; ++k) {
+      const float var = var_c[k] * (1.f / kTile);
+      vr_own[k] = var > 1e-12f * mean_c[k] * mean_c[k] ? var : vr_own[k];
     }
-  }
-  float r[8], s[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    r[i] = __builtin_amdgcn_sqrtf(vr[i]);
-    s[i] = __builtin_amdgcn_sqrtf(vs[i]);
+    *reinterpret_cast<float2*>(&gr0[ch_own]) =
+        make_float2(__builtin_amdgcn_rsqf(vr_own[0]), __builtin_amdgcn_rsqf(vr_own[1]));
+    lds_read8(&gr0[8 * cb], ir);
   }
 
-  // ---- 4a. stored normalizers and the normalized tile --------------------------------
-  uint16_t r16[8], s16[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    r16[i] = f2h_rn(fminf(fmaxf(r[i], 6.103515625e-05f), 65504.f));
-    ir[i] = __builtin_amdgcn_rcpf(h2f(r16[i]));
-    s16[i] = f2h_rn(fminf(fmaxf(s[i], 6.103515625e-05f), 65504.f));
-    is[i] = __builtin_amdgcn_rcpf(h2f(s16[i]));
+  // ---- 4a. stored normalizers (float16) and their inverses on every lane ----------------
+  const uint16_t s16 = normalizer16(__builtin_amdgcn_sqrtf(vs_own));
+  const uint16_t r16a = normalizer16(__builtin_amdgcn_sqrtf(vr_own[0]));
+  const uint16_t r16b = normalizer16(__builtin_amdgcn_sqrtf(vr_own[1]));
+  const float is_own = __builtin_amdgcn_rcpf(h2f(s16));
+  const float ir_own[2] = {__builtin_amdgcn_rcpf(h2f(r16a)), __builtin_amdgcn_rcpf(h2f(r16b))};
+  if (w == 0) {            // every channel once
+    sm.meta[0][ch_own] = r16a;
+    sm.meta[0][ch_own + 1] = r16b;
   }
-  // lanes of wave 0, row 0 hold every channel's r; the lanes of column 0 every token's s
-  if (tb == 0) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) sm.meta[0][8 * cb + i] = r16[i];
-  }
-  if (cb == 0) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) sm.meta[1][8 * tb + j] = s16[j];
-  }
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[j][i] = (x[j][i] * is[j]) * ir[i];
+  if ((l & 8) == 0) sm.meta[1][8 * tb + tok_own] = s16;   // every token once
+  gc0[tok_own] = is_own;
+  lds_read8(gc0, is);
+  *reinterpret_cast<float2*>(&gr0[ch_own]) = make_float2(ir_own[0], ir_own[1]);
+  lds_read8(&gr0[8 * cb], ir);
 
-  // ---- 4b. asymmetric RTN -----------------------------------------------------------
+  // ---- 4b. asymmetric RTN --------------------------------------------------------------
+  // code = clamp(rne((y - zero) / scale), 0, top) with y = x / (r s): computed as
+  // fma(z, A, B), z the element times one of its two inverse normalizers and A, B per group;
+  // cvt_pk_u8 rounds to nearest even and clamps below at 0, the min clamps above.
+  uint32_t* out = reinterpret_cast<uint32_t*>(rec);
   if constexpr (KIND == 0) {
-    // keys: one group per channel, over the 128 tokens
+    // keys: one group per channel, over the 128 tokens; z = x / s
     float mn[8], mx[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[j][i] *= is[j];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       mn[i] = x[0][i];
@@ -260,98 +319,100 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
 #pragma unroll
       for (int j = 1; j < 8; ++j) { mn[i] = fminf(mn[i], x[j][i]); mx[i] = fmaxf(mx[i], x[j][i]); }
     }
-    reduce_over_tokens<1>(mn, sm, w, l, 0);
-    reduce_over_tokens<2>(mx, sm, w, l, 1);
-    uint16_t sc16[8], zr16[8];
-    float inv[8], off[8];
+    float omn[2], omx[2];
+    rows4_scatter8<1>(mn, omn);
+    rows4_scatter8<2>(mx, omx);
+    // the 4 waves' partials through the (free) broadcast area; both red buffers are free
+    // once every thread is past this barrier
+    *reinterpret_cast<float2*>(&sm.gr[w][0][ch_own]) = make_float2(omn[0], omn[1]);
+    *reinterpret_cast<float2*>(&sm.gr[w][1][ch_own]) = make_float2(omx[0], omx[1]);
+    __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      sc16[i] = f2h_rn((mx[i] - mn[i]) * (1.f / 15.f));
-      zr16[i] = f2h_rn(mn[i]);
-      const float sc = h2f(sc16[i]);
-      inv[i] = sc > 0.f ? __builtin_amdgcn_rcpf(sc) : 0.f;
-      off[i] = -h2f(zr16[i]) * inv[i];
+    for (int ww = 0; ww < 4; ++ww) {
+      const float2 a = *reinterpret_cast<const float2*>(&sm.gr[ww][0][ch_own]);
+      const float2 b = *reinterpret_cast<const float2*>(&sm.gr[ww][1][ch_own]);
+      omn[0] = fminf(omn[0], a.x); omn[1] = fminf(omn[1], a.y);
+      omx[0] = fmaxf(omx[0], b.x); omx[1] = fmaxf(omx[1], b.y);
     }
-    if (tb == 0) {  // every channel's group statistics
+    float A2[2], B2[2];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        sm.meta[2][8 * cb + i] = sc16[i];
-        sm.meta[3][8 * cb + i] = zr16[i];
+    for (int k = 0; k < 2; ++k) {
+      const float lo = omn[k] * ir_own[k], hi_ = omx[k] * ir_own[k];   // y = z / r, r > 0
+      const uint16_t sc16 = f2h_rn((hi_ - lo) * (1.f / 15.f));
+      const uint16_t zr16 = f2h_rn(lo);
+      const float sc = h2f(sc16);
+      const float inv = sc > 0.f ? __builtin_amdgcn_rcpf(sc) : 0.f;
+      A2[k] = ir_own[k] * inv;
+      B2[k] = -h2f(zr16) * inv;
+      if (w == 0) {
+        sm.meta[2][ch_own + k] = sc16;
+        sm.meta[3][ch_own + k] = zr16;
       }
     }
+    float* ga = &sm.red[0][w][0];
+    float* gb = &sm.red[1][w][0];
+    *reinterpret_cast<float2*>(&ga[ch_own]) = make_float2(A2[0], A2[1]);
+    *reinterpret_cast<float2*>(&gb[ch_own]) = make_float2(B2[0], B2[1]);
+    float A[8], B[8];
+    lds_read8(&ga[8 * cb], A);
+    lds_read8(&gb[8 * cb], B);
+    // word (t, cb) = channels 8cb..8cb+7 of token t; nibble p <- channel {0,2,4,6,1,3,5,7}[p]
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      uint32_t lo = 0, hi = 0;
+      uint32_t e = 0, o = 0;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        // code = clamp(rne((y - zero) / scale), 0, 15), packed one byte per code
-        const float u = __builtin_amdgcn_fmed3f(__builtin_rintf(fmaf(x[j][i], inv[i], off[i])), 0.f, 15.f);
-        if (i < 4) lo = __builtin_amdgcn_cvt_pk_u8_f32(u, i, lo);
-        else hi = __builtin_amdgcn_cvt_pk_u8_f32(u, i - 4, hi);
+        const float u = fminf(fmaf(x[j][i], A[i], B[i]), 15.f);
+        if (i & 1) o = __builtin_amdgcn_cvt_pk_u8_f32(u, i >> 1, o);
+        else e = __builtin_amdgcn_cvt_pk_u8_f32(u, i >> 1, e);
       }
-      *reinterpret_cast<uint2*>(&sm.codes[(8 * tb + j) * kDim + 8 * cb]) = make_uint2(lo, hi);
+      out[(8 * tb + j) * 16 + cb] = bytes_to_nibbles(e) | (bytes_to_nibbles(o) << 16);
     }
   } else {
-    // values: one group per token, over the 128 channels
+    // values: one group per token, over the 128 channels; z = x / r
     float mn[8], mx[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float a = x[j][0], b = x[j][0];
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int i = 1; i < 8; ++i) { a = fminf(a, x[j][i]); b = fmaxf(b, x[j][i]); }
-      mn[j] = row16_min(a);
-      mx[j] = row16_max(b);
-    }
-    uint16_t sc16[8], zr16[8];
-    float inv[8], off[8];
+      for (int i = 0; i < 8; ++i) x[j][i] *= ir[i];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      sc16[j] = f2h_rn((mx[j] - mn[j]) * (1.f / 3.f));
-      zr16[j] = f2h_rn(mn[j]);
-      const float sc = h2f(sc16[j]);
-      inv[j] = sc > 0.f ? __builtin_amdgcn_rcpf(sc) : 0.f;
-      off[j] = -h2f(zr16[j]) * inv[j];
+      mn[j] = x[j][0];
+      mx[j] = x[j][0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) { mn[j] = fminf(mn[j], x[j][i]); mx[j] = fmaxf(mx[j], x[j][i]); }
     }
+    const float lo = row16_scatter8<1>(mn, l) * is_own;   // y = z / s, s > 0
+    const float hi_ = row16_scatter8<2>(mx, l) * is_own;
+    const uint16_t sc16 = f2h_rn((hi_ - lo) * (1.f / 3.f));
+    const uint16_t zr16 = f2h_rn(lo);
+    const float sc = h2f(sc16);
+    const float inv = sc > 0.f ? __builtin_amdgcn_rcpf(sc) : 0.f;
+    if ((l & 8) == 0) {
+      sm.meta[2][8 * tb + tok_own] = sc16;
+      sm.meta[3][8 * tb + tok_own] = zr16;
+    }
+    gc0[tok_own] = is_own * inv;
+    gc1[tok_own] = -h2f(zr16) * inv;
+    float A[8], B[8];
+    lds_read8(gc0, A);
+    lds_read8(gc1, B);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      uint32_t lo = 0, hi = 0;
+      uint32_t lo4 = 0, hi4 = 0;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float u = __builtin_amdgcn_fmed3f(__builtin_rintf(fmaf(x[j][i], inv[j], off[j])), 0.f, 3.f);
-        if (j < 4) lo = __builtin_amdgcn_cvt_pk_u8_f32(u, j, lo);
-        else hi = __builtin_amdgcn_cvt_pk_u8_f32(u, j - 4, hi);
+        const float u = fminf(fmaf(x[j][i], A[j], B[j]), 3.f);
+        if (j < 4) lo4 = __builtin_amdgcn_cvt_pk_u8_f32(u, j, lo4);
+        else hi4 = __builtin_amdgcn_cvt_pk_u8_f32(u, j - 4, hi4);
       }
-      *reinterpret_cast<uint2*>(&sm.codes[(8 * cb + i) * kTile + 8 * tb]) = make_uint2(lo, hi);
-    }
-    if (cb == 0) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        sm.meta[2][8 * tb + j] = sc16[j];
-        sm.meta[3][8 * tb + j] = zr16[j];
-      }
+      *reinterpret_cast<uint2*>(&sm.codes[(8 * cb + i) * kTile + 8 * tb]) = make_uint2(lo4, hi4);
     }
   }
   __syncthreads();
 
-  // ---- 4c. pack codes into the record layout and store -------------------------------
-  uint32_t* out = reinterpret_cast<uint32_t*>(rec);
-  if constexpr (KIND == 0) {
-    // 2048 words: word (t, j) = channels 8j..8j+7 of token t, nibble p <- channel
-    // 8j + {0,2,4,6,1,3,5,7}[p]
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int wi = tid + kThreads * k;
-      const int t = wi >> 4, j = wi & 15;
-      const uint2 c8 = *reinterpret_cast<const uint2*>(&sm.codes[t * kDim + 8 * j]);
-      // byte q of c8 = code of channel 8j+q; even channels to nibbles 0..3, odd to 4..7
-      const uint32_t e = (c8.x & 0xFF) | ((c8.x >> 8) & 0xFF00) | ((c8.y & 0xFF) << 16) | ((c8.y & 0xFF0000) << 8);
-      const uint32_t o = ((c8.x >> 8) & 0xFF) | ((c8.x >> 16) & 0xFF00) | (((c8.y >> 8) & 0xFF) << 16) | ((c8.y >> 24) << 24);
-      // e, o hold 4 codes as bytes; compress bytes to nibbles
-      const uint32_t en = (e & 0xF) | ((e >> 4) & 0xF0) | ((e >> 8) & 0xF00) | ((e >> 12) & 0xF000);
-      const uint32_t on = (o & 0xF) | ((o >> 4) & 0xF0) | ((o >> 8) & 0xF00) | ((o >> 12) & 0xF000);
-      out[wi] = en | (on << 16);
-    }
-  } else {
+  // ---- 4c. value codes into the record layout; metadata ---------------------------------
+  if constexpr (KIND == 1) {
     // 1024 words: word (c, g, d); crumb p <- token 32s + (j < 4 ? 4g + j : 12 + 4g + j),
     // i = p % 8, s = 2d + i / 4, j = 2 (i % 4) + p / 8
 #pragma unroll
@@ -362,9 +423,9 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
       uint32_t word = 0;
 #pragma unroll
       for (int sl = 0; sl < 2; ++sl) {  // the two 32-token steps of this word
-        const int s = 2 * d + sl;
-        const uint32_t a = *reinterpret_cast<const uint32_t*>(row + 32 * s + 4 * g);       // slots 0..3
-        const uint32_t b = *reinterpret_cast<const uint32_t*>(row + 32 * s + 16 + 4 * g);  // slots 4..7
+        const int s_ = 2 * d + sl;
+        const uint32_t a = *reinterpret_cast<const uint32_t*>(row + 32 * s_ + 4 * g);       // slots 0..3
+        const uint32_t b = *reinterpret_cast<const uint32_t*>(row + 32 * s_ + 16 + 4 * g);  // slots 4..7
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           // slot 2v -> low-half crumb i = 4 sl + v, slot 2v+1 -> high-half crumb 8 + i
@@ -382,8 +443,8 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
   // metadata: 4 x 128 float16 = 256 words, one per thread
   {
     const int codes_words = (KIND == 0 ? kKCodeBytes : kVCodeBytes) / 4;
-    const uint16_t* m = &sm.meta[0][0];
-    out[codes_words + tid] = uint32_t(m[2 * tid]) | (uint32_t(m[2 * tid + 1]) << 16);
+    const uint16_t* mm = &sm.meta[0][0];
+    out[codes_words + tid] = uint32_t(mm[2 * tid]) | (uint32_t(mm[2 * tid + 1]) << 16);
   }
 }
 

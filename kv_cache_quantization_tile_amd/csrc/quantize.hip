@@ -113,17 +113,46 @@ __device__ __forceinline__ uint32_t bytes_to_nibbles(uint32_t e) {
   return (x | (x >> 8)) & 0x0000FFFFu;
 }
 
-// FWHT of length 128 along channels for each of the thread's 8 tokens, then * 1/sqrt(128).
-// Channel bits 0..2 are in-thread; bits 3..6 are lane bits 0..3. A cross-lane butterfly
-// stage on lane bit m is one fused multiply-add per value: y += c * y(lane ^ m) with c = +1
-// on lanes whose bit m is 0 and -1 on the others. Lanes with the bit set then hold the
-// negated difference; the accumulated sign, (-1)^popcount(lane bits 0..3), is removed by the
-// final scaling.
-__device__ __forceinline__ void fwht_channels(float (&x)[8][8], int cb) {
+// x += c * x(lane under DPP control CTRL) for 8 values, one v_fmac_f32_dpp each. The DPP
+// source is read from the register the instruction writes (all lanes read before any
+// writes). A DPP read of a VGPR needs 2 wait states after the VALU write of that VGPR: the
+// block starts with them (s_nop 1), and no instruction of the block reads a value written
+// inside it. bound_ctrl is irrelevant: every control used reads inside the 16-lane row.
+#define KVARN_FMAC_DPP8(CTRL, C, X)                                                         \
+  asm volatile("s_nop 1\n"                                                                   \
+               "v_fmac_f32_dpp %0, %0, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n" \
+               "v_fmac_f32_dpp %1, %1, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n" \
+               "v_fmac_f32_dpp %2, %2, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n" \
+               "v_fmac_f32_dpp %3, %3, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n" \
+               "v_fmac_f32_dpp %4, %4, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n" \
+               "v_fmac_f32_dpp %5, %5, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n" \
+               "v_fmac_f32_dpp %6, %6, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n" \
+               "v_fmac_f32_dpp %7, %7, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1"     \
+               : "+v"(X[0]), "+v"(X[1]), "+v"(X[2]), "+v"(X[3]), "+v"(X[4]), "+v"(X[5]),   \
+                 "+v"(X[6]), "+v"(X[7])                                                     \
+               : "v"(C))
+
+// FWHT of length 128 along channels for each of the thread's 8 tokens, then * 1/sqrt(128),
+// from the raw float16 words (channels 2k, 2k+1 in word k). Channel bits 0..2 are
+// in-thread; bits 3..6 are lane bits 0..3. The first stage adds / subtracts the two halves
+// of a word with mixed-precision FMAs that read float16 directly. A cross-lane stage on
+// lane bit m is one fused multiply-add per value: y += c * y(lane ^ m) with c = +1 on lanes
+// whose bit m is 0 and -1 on the others. Lanes with the bit set then hold the negated
+// difference; the accumulated sign, (-1)^popcount(lane bits 0..3), is removed by the final
+// scaling.
+__device__ __forceinline__ void fwht_channels(const uint32_t (&raw)[8][4], float (&x)[8][8], int cb) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
 #pragma unroll
-    for (int h = 1; h < 8; h <<= 1) {
+    for (int k = 0; k < 4; ++k) {
+      // f32(lo) + f32(hi), f32(lo) - f32(hi): each one rounding, as the float32 add would
+      asm("v_fma_mix_f32 %0, %1, 1.0, %1 op_sel:[0,0,1] op_sel_hi:[1,0,1]"
+          : "=v"(x[j][2 * k]) : "v"(raw[j][k]));
+      asm("v_fma_mix_f32 %0, %1, 1.0, -%1 op_sel:[0,0,1] op_sel_hi:[1,0,1]"
+          : "=v"(x[j][2 * k + 1]) : "v"(raw[j][k]));
+    }
+#pragma unroll
+    for (int h = 2; h < 8; h <<= 1) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         if ((i & h) == 0) {
@@ -136,24 +165,29 @@ __device__ __forceinline__ void fwht_channels(float (&x)[8][8], int cb) {
   }
   const float c1 = (cb & 1) ? -1.f : 1.f, c2 = (cb & 2) ? -1.f : 1.f;
   const float c4 = (cb & 4) ? -1.f : 1.f, c8 = (cb & 8) ? -1.f : 1.f;
-  // partners of one token's 8 values are fetched before any of them is updated
-#define KVARN_XSTAGE(FETCH, C)                                              \
-  _Pragma("unroll") for (int j = 0; j < 8; ++j) {                           \
-    float p[8];                                                             \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i) p[i] = FETCH(x[j][i]);    \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i) x[j][i] = fmaf(p[i], C, x[j][i]); \
+#pragma unroll
+  for (int j = 0; j < 8; ++j) KVARN_FMAC_DPP8("quad_perm:[1,0,3,2]", c1, x[j]);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) KVARN_FMAC_DPP8("quad_perm:[2,3,0,1]", c2, x[j]);
+  // lane bit 2: ds_swizzle (xor 4 is not a DPP row pattern); partners of one token's 8
+  // values are fetched before any of them is updated
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = swz_xor_f<4>(x[j][i]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[j][i] = fmaf(p[i], c4, x[j][i]);
   }
-  KVARN_XSTAGE(dpp_f<kDppQuadXor1>, c1)
-  KVARN_XSTAGE(dpp_f<kDppQuadXor2>, c2)
-  KVARN_XSTAGE(swz_xor_f<4>, c4)
-  KVARN_XSTAGE(dpp_f<kDppRowRor8>, c8)
-#undef KVARN_XSTAGE
+#pragma unroll
+  for (int j = 0; j < 8; ++j) KVARN_FMAC_DPP8("row_ror:8", c8, x[j]);
   const float fin = (__builtin_popcount(cb) & 1) ? -kInvSqrt128 : kInvSqrt128;
 #pragma unroll
   for (int j = 0; j < 8; ++j)
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[j][i] *= fin;
 }
+#undef KVARN_FMAC_DPP8
 
 // The tile quantizer proper. row_ptr(t) gives the 16-byte aligned address of token t's
 // 128 channels. Writes one record at `rec`.
@@ -166,19 +200,16 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
 
   // ---- 1. gather: token 8tb+j, channels 8cb..8cb+7 (16 bytes) --------------------------
   float x[8][8];
+  {
+    uint32_t raw[8][4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(row_ptr(8 * tb + j) + 8 * cb);
-    const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      x[j][2 * k] = h2f(uint16_t(wds[k] & 0xFFFF));
-      x[j][2 * k + 1] = h2f(uint16_t(wds[k] >> 16));
+    for (int j = 0; j < 8; ++j) {
+      const uint4 v = *reinterpret_cast<const uint4*>(row_ptr(8 * tb + j) + 8 * cb);
+      raw[j][0] = v.x; raw[j][1] = v.y; raw[j][2] = v.z; raw[j][3] = v.w;
     }
+    // ---- 2. rotate ------------------------------------------------------------------
+    fwht_channels(raw, x, cb);
   }
-
-  // ---- 2. rotate --------------------------------------------------------------------
-  fwht_channels(x, cb);
 
   // ---- 3. normalize -----------------------------------------------------------------
   // Two passes per step (mean, then centred sum of squares), float32 FMAs. A group's

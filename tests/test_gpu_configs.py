@@ -1,0 +1,189 @@
+"""GPU parity at the full sizes of the synthetic workloads, in the launch configuration the
+benchmark times (keys and values of a layer in one quantize launch, one decode launch per
+step), on sampled tiles and sampled (sequence, KV head) rows that the oracle recomputes:
+
+  one layer      64 q / 8 KV heads, 16384 tokens, 2048 tiles, one decode step;
+  batched paged  32 sequences of U[4096, 32768] tokens (rounded to 128) in permuted pages,
+                 16 decode steps that append one token each; a variant with lengths
+                 120 mod 128 whose staging tiles fill (and are quantized) at step 8;
+  long context   131072 tokens, 64 decode steps with appends;
+  prefill burst  64 x 16384 tokens (131072 tiles) for 2, 4 and 8 iterations, then one
+                 batched decode step.
+
+Inputs are drawn on the GPU by the seeded generators; the sampled tiles and rows are copied
+to the host for the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import kvarn_oracle as O
+from kv_cache_quantization_tile_amd import synth
+from tests import kvarn_testlib as T
+
+pytestmark = pytest.mark.gpu
+
+N_TILES = 256          # sampled tiles per kind
+N_KV_ROWS = 8          # sampled (sequence, KV head) rows per check: 8 x 8 query heads
+
+
+@pytest.fixture(scope="module")
+def K():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need an MI355X; torch.cuda.is_available() is False")
+    from kv_cache_quantization_tile_amd import kvarn
+    return kvarn
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def _quantize_layer(K, params, w):
+    kp = K.new_pool(w.num_pages, w.hkv, K.KIND_K)
+    vp = K.new_pool(w.num_pages, w.hkv, K.KIND_V)
+    K.quantize_kv_tiles(params, w.k_src, w.v_src, w.tile_src_token, w.tile_dst_page, kp, vp)
+    torch.cuda.synchronize()
+    return kp, vp
+
+
+def _check_sampled_tiles(w, kp, vp, n_iters, seed, n=N_TILES):
+    """Oracle check of n random (tile, head) pairs per kind."""
+    rng = np.random.default_rng(seed)
+    n_t = w.tile_src_token.numel()
+    tok = w.tile_src_token.cpu().numpy()
+    page = w.tile_dst_page.cpu().numpy()
+    for kind, src, pool in ((O.KIND_K, w.k_src, kp), (O.KIND_V, w.v_src, vp)):
+        pick = rng.choice(n_t * w.hkv, size=min(n, n_t * w.hkv), replace=False)
+        ti, hh = pick // w.hkv, pick % w.hkv
+        tiles = torch.stack([src[int(tok[i]):int(tok[i]) + 128, int(h), :]
+                             for i, h in zip(ti, hh)]).cpu().numpy()
+        sel = pool[torch.as_tensor(page[ti], dtype=torch.long, device=pool.device),
+                   torch.as_tensor(hh, dtype=torch.long, device=pool.device)].cpu().numpy()
+        recs = [sel[k].tobytes() for k in range(sel.shape[0])]
+        st = T.check_quantized_tiles(tiles, recs, kind, n_iters)
+        say(f"  kind={kind} {st}")
+        T.assert_rate(st)
+
+
+def _rows(rng, batch, hkv, n=N_KV_ROWS):
+    pick = rng.choice(batch * hkv, size=min(n, batch * hkv), replace=False)
+    return [(int(k // hkv), int(k % hkv)) for k in pick]
+
+
+def test_one_layer_16k(K):
+    w = synth.one_layer(device="cuda")
+    params = K.params_from_dtype("kvarn_k4v2_g128", w.n_iters)
+    say(f"one layer: {w.tile_src_token.numel() * w.hkv * 2} tiles, context {w.prompt_lens[0]}")
+    kp, vp = _quantize_layer(K, params, w)
+    _check_sampled_tiles(w, kp, vp, w.n_iters, seed=101)
+    q = w.step_inputs(0)[0]
+    sl = torch.tensor(w.prompt_lens, dtype=torch.int32, device="cuda")
+    out = K.decode_attention(params, q, kp, vp, w.block_table, sl, w.prompt_lens[0])
+    torch.cuda.synchronize()
+    err = T.check_decode(q, out, kp, vp, w.block_table, sl, w.hq // w.hkv,
+                         rows=[(0, g) for g in range(w.hkv)])
+    say(f"  decode: 64 rows, max rel err {err:.2e}")
+
+
+def _staging_from_prompt(w, kt, vt):
+    """Put each sequence's partial last prompt tile (L mod 128 tokens) into staging."""
+    for b, L in enumerate(w.prompt_lens):
+        rem = L % 128
+        if rem:
+            s = w.seq_start[b] + (L - rem)
+            kt[b, :, :rem, :] = w.k_src[s:s + rem].permute(1, 0, 2)
+            vt[b, :, :rem, :] = w.v_src[s:s + rem].permute(1, 0, 2)
+
+
+def _decode_steps(K, params, w, steps, check_at, seed):
+    """Append + decode for `steps` steps (the bench's step order: append the new token,
+    then attend with it); oracle checks of sampled rows at the steps in check_at."""
+    kp, vp = _quantize_layer(K, params, w)
+    _check_sampled_tiles(w, kp, vp, w.n_iters, seed=seed)
+    B, hkv, G = w.batch, w.hkv, w.hq // w.hkv
+    kt = torch.zeros((B, hkv, 128, 128), dtype=torch.float16, device="cuda")
+    vt = torch.zeros_like(kt)
+    _staging_from_prompt(w, kt, vt)
+    bt = w.block_table.clone()
+    fills = []
+    for b, L in enumerate(w.prompt_lens):      # the page each sequence would fill next
+        bt[b, L // 128] = int(w.free_pages[b])
+        if (L % 128) + steps >= 128:
+            fills.append(b)
+    sl = torch.tensor(w.prompt_lens, dtype=torch.int32, device="cuda")
+    max_len = max(w.prompt_lens) + steps
+    ws = K.new_workspace(params, B, w.hq, hkv, max_len)
+    rng = np.random.default_rng(seed + 1)
+    for s in range(steps):
+        q, kn, vn = w.step_inputs(s)
+        pre = (kt.clone(), vt.clone()) if s in check_at else None
+        K.append_tokens(params, kn, vn, sl, kt, vt, bt, kp, vp)
+        filled = [b for b in fills if (w.prompt_lens[b] + s) % 128 == 127]
+        sl = sl + 1
+        out = K.decode_attention(params, q, kp, vp, bt, sl, max_len, kt, vt, workspace=ws)
+        if s not in check_at:
+            continue
+        torch.cuda.synchronize()
+        for b in filled[:4]:     # a filled page equals the quantizer's record of its tile
+            page = int(bt[b, (w.prompt_lens[b] + s) // 128])
+            for kind, pool, stage, new in ((O.KIND_K, kp, pre[0], kn), (O.KIND_V, vp, pre[1], vn)):
+                tile = stage[b].clone()
+                tile[:, 127] = new[b]
+                ref = K.new_pool(1, hkv, kind)
+                K.quantize_tiles(params, kind, tile.permute(1, 0, 2).contiguous(),
+                                 torch.zeros(1, dtype=torch.int64, device="cuda"),
+                                 torch.zeros(1, dtype=torch.int32, device="cuda"), ref)
+                torch.cuda.synchronize()
+                assert torch.equal(pool[page], ref[0]), f"filled page b={b} kind={kind}"
+        rows = _rows(rng, B, hkv)
+        err = T.check_decode(q, out, kp, vp, bt, sl, G, rows=rows, k_tail=kt, v_tail=vt)
+        say(f"  step {s}: {len(rows) * G} rows, {len(filled)} pages filled, max rel err {err:.2e}")
+    return sl
+
+
+@pytest.mark.parametrize("fill", [False, True])
+def test_batched_paged(K, fill):
+    if fill:
+        # lengths 120 mod 128: every staging tile fills at step 8 and is quantized
+        g = torch.Generator().manual_seed(21)
+        u = torch.rand(32, generator=g, dtype=torch.float64)
+        lens = [synth.round_to_tile(4096 + (32768 - 4096) * float(x)) - 8 for x in u]
+        w = synth.batched_paged(device="cuda", seed=22, lens=lens)
+    else:
+        w = synth.batched_paged(device="cuda")
+    params = K.params_from_dtype("kvarn_k4v2_g128", w.n_iters)
+    say(f"batched paged fill={fill}: B={w.batch}, tokens {sum(w.prompt_lens)}, "
+        f"{w.tile_src_token.numel() * w.hkv * 2} prompt tiles")
+    sl = _decode_steps(K, params, w, steps=16, check_at={0, 7, 8, 15}, seed=201 + int(fill))
+    assert sl.tolist() == [L + 16 for L in w.prompt_lens]
+
+
+def test_long_context_128k(K):
+    w = synth.long_context(device="cuda")
+    params = K.params_from_dtype("kvarn_k4v2_g128", w.n_iters)
+    say(f"long context: {w.prompt_lens[0]} tokens, {w.decode_steps} steps")
+    _decode_steps(K, params, w, steps=w.decode_steps, check_at={0, 31, 63}, seed=301)
+
+
+@pytest.fixture(scope="module")
+def burst():
+    return synth.prefill_burst(device="cuda")
+
+
+@pytest.mark.parametrize("n_iters", [2, 4, 8])
+def test_prefill_burst(K, burst, n_iters):
+    w = burst
+    params = K.params_from_dtype("kvarn_k4v2_g128", n_iters)
+    say(f"prefill burst N={n_iters}: {w.tile_src_token.numel() * w.hkv * 2} tiles")
+    kp, vp = _quantize_layer(K, params, w)
+    _check_sampled_tiles(w, kp, vp, n_iters, seed=400 + n_iters)
+    if n_iters != 8:
+        return
+    q = w.step_inputs(0)[0]
+    sl = torch.tensor(w.prompt_lens, dtype=torch.int32, device="cuda")
+    out = K.decode_attention(params, q, kp, vp, w.block_table, sl, max(w.prompt_lens))
+    torch.cuda.synchronize()
+    rows = _rows(np.random.default_rng(409), w.batch, w.hkv)
+    err = T.check_decode(q, out, kp, vp, w.block_table, sl, w.hq // w.hkv, rows=rows)
+    say(f"  decode: {len(rows) * 8} rows, max rel err {err:.2e}")

@@ -211,19 +211,96 @@ __device__ __forceinline__ uint32_t swap8_into(uint32_t old, uint32_t src) {
 constexpr int kHiBanks = 0x3;   // lanes 0..7 of a row: high-part columns
 constexpr int kLoBanks = 0xC;   // lanes 8..15: low-part columns
 
+// Exact attention over the float16 tail (tokens past the last full page) of (sequence b,
+// KV head g), raw space, written as split n_splits of each query head's partials. Run by the
+// extra split of decode_pages_kernel; wave w handles heads 2w, 2w+1 of the group; p_sm is
+// 8 x 128 floats of LDS.
+__device__ void tail_partial(const __half* __restrict__ q, int32_t num_q_heads,
+                             int32_t num_kv_heads, const __half* __restrict__ k_tail,
+                             const __half* __restrict__ v_tail, int b, int g, int L, float qscale,
+                             int32_t n_splits, float* __restrict__ ws, float (*p_sm)[kTile]) {
+  const int G = num_q_heads / num_kv_heads;
+  const int T = L % kTile;
+  if (T == 0) return;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const __half* kt = k_tail + (int64_t(b) * num_kv_heads + g) * kTile * kDim;
+  const __half* vt = v_tail + (int64_t(b) * num_kv_heads + g) * kTile * kDim;
+  for (int hh = 2 * w; hh < 2 * w + 2; ++hh) {
+    if (hh >= G) break;
+    const int hq = g * G + hh;
+    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(q + (int64_t(b) * num_q_heads + hq) * kDim);
+    float sc[2];
+#pragma unroll
+    for (int half_ = 0; half_ < 2; ++half_) {
+      const int t = l + 64 * half_;
+      float a = -INFINITY;
+      if (t < T) {
+        a = 0.f;
+        const uint8_t* krow = reinterpret_cast<const uint8_t*>(kt + int64_t(t) * kDim);
+        for (int c8 = 0; c8 < 16; ++c8) {
+          float qv[8], kv[8];
+          load_h8(qrow + 16 * c8, qv);
+          load_h8(krow + 16 * c8, kv);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) a = fmaf(qv[i], kv[i], a);
+        }
+        a *= qscale;
+      }
+      sc[half_] = a;
+    }
+    float mx = fmaxf(sc[0], sc[1]);
+    for (int off = 1; off < 64; off <<= 1)
+      mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(((l ^ off) << 2), __float_as_int(mx))));
+    float ps = 0.f;
+#pragma unroll
+    for (int half_ = 0; half_ < 2; ++half_) {
+      const int t = l + 64 * half_;
+      const float p = t < T ? exp2f(sc[half_] - mx) : 0.f;
+      p_sm[hh][t] = p;
+      ps += p;
+    }
+    for (int off = 1; off < 64; off <<= 1)
+      ps += __int_as_float(__builtin_amdgcn_ds_bpermute(((l ^ off) << 2), __float_as_int(ps)));
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    float o0 = 0.f, o1 = 0.f;
+    for (int t = 0; t < T; ++t) {
+      const uint32_t vv = *reinterpret_cast<const uint32_t*>(vt + int64_t(t) * kDim + 2 * l);
+      const float p = p_sm[hh][t];
+      o0 = fmaf(p, h2f(uint16_t(vv & 0xFFFF)), o0);
+      o1 = fmaf(p, h2f(uint16_t(vv >> 16)), o1);
+    }
+    float* part = ws + ((int64_t(b) * num_q_heads + hq) * (n_splits + 1) + n_splits) * kPartStride;
+    *reinterpret_cast<float2*>(part + 4 + 2 * l) = make_float2(o0, o1);
+    if (l == 0) {
+      part[0] = mx;
+      part[1] = ps;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 // One workgroup: (split, KV head g, sequence b). Wave w handles page slots
-// split * 4 * tpw + w + 4 k, k < tpw. Writes one partial (m, l, acc) per query head.
+// split * 4 * tpw + w + 4 k, k < tpw. Writes one partial (m, l, acc) per query head. With
+// tail buffers the grid has one more split, n_splits, which computes the tail partial.
 __global__ void __launch_bounds__(kThreads)
 decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t num_kv_heads,
                     const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
                     int64_t pool_num_pages, const int32_t* __restrict__ block_table,
                     int32_t bt_stride, const int32_t* __restrict__ seq_lens, int32_t max_seq_len,
-                    float qscale, int32_t tpw, int32_t n_splits, float* __restrict__ ws) {
+                    float qscale, int32_t tpw, int32_t n_splits, int32_t split_base,
+                    const __half* __restrict__ k_tail, const __half* __restrict__ v_tail,
+                    float tail_qscale, float* __restrict__ ws) {
   __shared__ DecodeSmem sm;
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int split = split_base + blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = num_q_heads / num_kv_heads;
   int32_t L = seq_lens[b];
   L = L < 0 ? 0 : (L > max_seq_len ? max_seq_len : L);
+  if (split == n_splits) {   // the extra split (launched only with tail buffers): the tail
+    tail_partial(q, num_q_heads, num_kv_heads, k_tail, v_tail, b, g, L, tail_qscale, n_splits,
+                 ws, reinterpret_cast<float (*)[kTile]>(&sm.acc[0][0][0]));
+    return;
+  }
   const int n_full = L / kTile;
   const int slot0 = split * 4 * tpw;
   if (slot0 >= n_full) return;
@@ -556,78 +633,6 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
   }
 }
 
-// Exact attention over the float16 tail (tokens past the last full page), raw space.
-// One workgroup per (KV head g, sequence b); wave w handles heads 2w, 2w+1 of the group.
-__global__ void __launch_bounds__(kThreads)
-decode_tail_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t num_kv_heads,
-                   const __half* __restrict__ k_tail, const __half* __restrict__ v_tail,
-                   const int32_t* __restrict__ seq_lens, int32_t max_seq_len, float qscale,
-                   int32_t n_splits, float* __restrict__ ws) {
-  __shared__ float p_sm[8][kTile];
-  const int g = blockIdx.x, b = blockIdx.y;
-  const int G = num_q_heads / num_kv_heads;
-  int32_t L = seq_lens[b];
-  L = L < 0 ? 0 : (L > max_seq_len ? max_seq_len : L);
-  const int T = L % kTile;
-  if (T == 0) return;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const __half* kt = k_tail + (int64_t(b) * num_kv_heads + g) * kTile * kDim;
-  const __half* vt = v_tail + (int64_t(b) * num_kv_heads + g) * kTile * kDim;
-  for (int hh = 2 * w; hh < 2 * w + 2; ++hh) {
-    if (hh >= G) break;
-    const int hq = g * G + hh;
-    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(q + (int64_t(b) * num_q_heads + hq) * kDim);
-    float sc[2];
-#pragma unroll
-    for (int half_ = 0; half_ < 2; ++half_) {
-      const int t = l + 64 * half_;
-      float a = -INFINITY;
-      if (t < T) {
-        a = 0.f;
-        const uint8_t* krow = reinterpret_cast<const uint8_t*>(kt + int64_t(t) * kDim);
-        for (int c8 = 0; c8 < 16; ++c8) {
-          float qv[8], kv[8];
-          load_h8(qrow + 16 * c8, qv);
-          load_h8(krow + 16 * c8, kv);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) a = fmaf(qv[i], kv[i], a);
-        }
-        a *= qscale;
-      }
-      sc[half_] = a;
-    }
-    float mx = fmaxf(sc[0], sc[1]);
-    for (int off = 1; off < 64; off <<= 1)
-      mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(((l ^ off) << 2), __float_as_int(mx))));
-    float ps = 0.f;
-#pragma unroll
-    for (int half_ = 0; half_ < 2; ++half_) {
-      const int t = l + 64 * half_;
-      const float p = t < T ? exp2f(sc[half_] - mx) : 0.f;
-      p_sm[hh][t] = p;
-      ps += p;
-    }
-    for (int off = 1; off < 64; off <<= 1)
-      ps += __int_as_float(__builtin_amdgcn_ds_bpermute(((l ^ off) << 2), __float_as_int(ps)));
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_wave_barrier();
-    float o0 = 0.f, o1 = 0.f;
-    for (int t = 0; t < T; ++t) {
-      const uint32_t vv = *reinterpret_cast<const uint32_t*>(vt + int64_t(t) * kDim + 2 * l);
-      const float p = p_sm[hh][t];
-      o0 = fmaf(p, h2f(uint16_t(vv & 0xFFFF)), o0);
-      o1 = fmaf(p, h2f(uint16_t(vv >> 16)), o1);
-    }
-    float* part = ws + ((int64_t(b) * num_q_heads + hq) * (n_splits + 1) + n_splits) * kPartStride;
-    *reinterpret_cast<float2*>(part + 4 + 2 * l) = make_float2(o0, o1);
-    if (l == 0) {
-      part[0] = mx;
-      part[1] = ps;
-    }
-    __builtin_amdgcn_wave_barrier();
-  }
-}
-
 // Merge the splits of one (sequence, query head): log-sum-exp weights, H^T on the page
 // part (rotated space), plus the raw-space tail; float16 output. One 128-thread workgroup
 // per (query head, sequence): thread c owns channel c; split weights are computed once in
@@ -748,21 +753,18 @@ hipError_t launch_decode(const void* q, int32_t batch, int32_t num_q_heads, int3
   const int32_t ns = decode_num_splits(batch, num_kv_heads, max_seq_len);
   const float qscale = softmax_scale * kLog2e;
   float* ws = static_cast<float*>(workspace);
-  if (max_seq_len >= kTile) {
-    hipLaunchKernelGGL(decode_pages_kernel, dim3(ns, num_kv_heads, batch), dim3(kThreads), 0, stream,
-                       static_cast<const __half*>(q), num_q_heads, num_kv_heads,
+  const bool has_tail = k_tail != nullptr && v_tail != nullptr;
+  // page splits (only if a full page can exist) plus, with tail buffers, one tail split
+  const int32_t grid_x = (max_seq_len >= kTile ? ns : 0) + (has_tail ? 1 : 0);
+  if (grid_x > 0) {
+    // without pages the only split launched is the tail, which must land on index ns
+    const int32_t first = max_seq_len >= kTile ? 0 : ns;
+    hipLaunchKernelGGL(decode_pages_kernel, dim3(grid_x, num_kv_heads, batch), dim3(kThreads), 0,
+                       stream, static_cast<const __half*>(q), num_q_heads, num_kv_heads,
                        static_cast<const uint8_t*>(k_pool), static_cast<const uint8_t*>(v_pool),
                        pool_num_pages, block_table, bt_stride, seq_lens, max_seq_len,
-                       qscale * kInvSqrt128, tpw, ns, ws);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  const bool has_tail = k_tail != nullptr && v_tail != nullptr;
-  if (has_tail) {
-    hipLaunchKernelGGL(decode_tail_kernel, dim3(num_kv_heads, batch), dim3(kThreads), 0, stream,
-                       static_cast<const __half*>(q), num_q_heads, num_kv_heads,
-                       static_cast<const __half*>(k_tail), static_cast<const __half*>(v_tail),
-                       seq_lens, max_seq_len, qscale, ns, ws);
+                       qscale * kInvSqrt128, tpw, ns, first, static_cast<const __half*>(k_tail),
+                       static_cast<const __half*>(v_tail), qscale, ws);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -160,6 +160,19 @@ KVARN_API kvarn_status kvarn_append_tokens(const kvarn_params* params, const voi
                                  int32_t block_table_stride, void* k_pool_dev,
                                  void* v_pool_dev, int64_t pool_num_pages, void* stream);
 
+/* Test and inspection only, off the hot path: page records back to float16 tiles (the read
+ * side of README "How KVarN works" stage 4, then the inverse rotation; H is its own
+ * inverse). For i < n_tiles and head h < num_kv_heads, the record (pages_dev[i], h) of
+ * pool_dev (pool_num_pages pages of num_kv_heads records of kind `kind`) becomes
+ *   dst_dev[i][h][t][c] = f16_rne( (H Xr)[c][t] ),  Xr[c][t] = r[c] s[t] (zero[g] + scale[g] code[c][t])
+ * (g = c for keys, t for values; evaluated in float32). dst_dev: float16
+ * [n_tiles, num_kv_heads, 128, 128], 16-byte aligned; pool_dev 16-byte aligned. Pages
+ * outside [0, pool_num_pages) leave their dst tile untouched. n_tiles == 0 is a no-op. */
+KVARN_API kvarn_status kvarn_dequantize_tiles(const kvarn_params* params, kvarn_kind kind,
+                                    const void* pool_dev, int64_t pool_num_pages,
+                                    const int32_t* pages_dev, int32_t n_tiles,
+                                    int32_t num_kv_heads, void* dst_dev, void* stream);
+
 /* Workspace bytes kvarn_decode_attention needs for this shape (0 if invalid). */
 KVARN_API size_t kvarn_decode_workspace_bytes(const kvarn_params* params, int32_t batch,
                                     int32_t num_q_heads, int32_t num_kv_heads,

@@ -138,6 +138,22 @@ kvarn_status kvarn_quantize_kv_tiles(const kvarn_params* params, const void* k_s
       params->sinkhorn_iters, static_cast<hipStream_t>(stream)));
 }
 
+kvarn_status kvarn_dequantize_tiles(const kvarn_params* params, kvarn_kind kind, const void* pool,
+                                    int64_t pool_num_pages, const int32_t* pages, int32_t n_tiles,
+                                    int32_t num_kv_heads, void* dst, void* stream) {
+  const kvarn_status st = kvarn_params_check(params);
+  if (st != KVARN_OK) return st;
+  if (kind != KVARN_K && kind != KVARN_V) return KVARN_ERR_INVALID_ARG;
+  if (n_tiles < 0 || num_kv_heads <= 0 || num_kv_heads > 65535 || pool_num_pages < 0)
+    return KVARN_ERR_INVALID_ARG;
+  if (n_tiles == 0) return KVARN_OK;
+  if (!pool || !pages || !dst) return KVARN_ERR_INVALID_ARG;
+  if (!aligned16(pool) || !aligned16(dst)) return KVARN_ERR_INVALID_ARG;
+  return launch_status(kvarn::launch_dequantize_tiles(int(kind), pool, pool_num_pages, pages,
+                                                      n_tiles, num_kv_heads, dst,
+                                                      static_cast<hipStream_t>(stream)));
+}
+
 kvarn_status kvarn_append_tokens(const kvarn_params* params, const void* k_new, const void* v_new,
                                  int32_t batch, int32_t num_kv_heads, const int32_t* seq_lens,
                                  void* k_tail, void* v_tail, const int32_t* block_table,

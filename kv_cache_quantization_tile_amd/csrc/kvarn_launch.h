@@ -19,6 +19,10 @@ hipError_t launch_quantize_kv(const void* k_src, const void* v_src, int64_t toke
                               int32_t n_tiles, int32_t num_kv_heads, void* k_pool, void* v_pool,
                               int64_t pool_num_pages, int n_iters, hipStream_t stream);
 
+hipError_t launch_dequantize_tiles(int kind, const void* pool, int64_t pool_num_pages,
+                                   const int32_t* pages, int32_t n_tiles, int32_t num_kv_heads,
+                                   void* dst, hipStream_t stream);
+
 hipError_t launch_append_tokens(const void* k_new, const void* v_new, int32_t batch,
                                 int32_t num_kv_heads, const int32_t* seq_lens, void* k_tail,
                                 void* v_tail, const int32_t* block_table, int32_t bt_stride,

@@ -132,25 +132,14 @@ __device__ __forceinline__ uint32_t bytes_to_nibbles(uint32_t e) {
                  "+v"(X[6]), "+v"(X[7])                                                     \
                : "v"(C))
 
-// FWHT of length 128 along channels for each of the thread's 8 tokens, then * 1/sqrt(128),
-// from the raw float16 words (channels 2k, 2k+1 in word k). Channel bits 0..2 are
-// in-thread; bits 3..6 are lane bits 0..3. The first stage adds / subtracts the two halves
-// of a word with mixed-precision FMAs that read float16 directly. A cross-lane stage on
-// lane bit m is one fused multiply-add per value: y += c * y(lane ^ m) with c = +1 on lanes
-// whose bit m is 0 and -1 on the others. Lanes with the bit set then hold the negated
-// difference; the accumulated sign, (-1)^popcount(lane bits 0..3), is removed by the final
-// scaling.
-__device__ __forceinline__ void fwht_channels(const uint32_t (&raw)[8][4], float (&x)[8][8], int cb) {
+// FWHT stages after the first (channel bit 0): bits 1, 2 in-thread, bits 3..6 = lane bits
+// 0..3, then * 1/sqrt(128). A cross-lane stage on lane bit m is one fused multiply-add per
+// value: y += c * y(lane ^ m) with c = +1 on lanes whose bit m is 0 and -1 on the others.
+// Lanes with the bit set then hold the negated difference; the accumulated sign,
+// (-1)^popcount(lane bits 0..3), is removed by the final scaling.
+__device__ __forceinline__ void fwht_after_first(float (&x)[8][8], int cb) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      // f32(lo) + f32(hi), f32(lo) - f32(hi): each one rounding, as the float32 add would
-      asm("v_fma_mix_f32 %0, %1, 1.0, %1 op_sel:[0,0,1] op_sel_hi:[1,0,1]"
-          : "=v"(x[j][2 * k]) : "v"(raw[j][k]));
-      asm("v_fma_mix_f32 %0, %1, 1.0, -%1 op_sel:[0,0,1] op_sel_hi:[1,0,1]"
-          : "=v"(x[j][2 * k + 1]) : "v"(raw[j][k]));
-    }
 #pragma unroll
     for (int h = 2; h < 8; h <<= 1) {
 #pragma unroll
@@ -186,6 +175,38 @@ __device__ __forceinline__ void fwht_channels(const uint32_t (&raw)[8][4], float
   for (int j = 0; j < 8; ++j)
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[j][i] *= fin;
+}
+
+// FWHT of length 128 along channels for each of the thread's 8 tokens, then * 1/sqrt(128),
+// from the raw float16 words (channels 2k, 2k+1 in word k): the first stage adds /
+// subtracts the two halves of a word with mixed-precision FMAs that read float16 directly.
+__device__ __forceinline__ void fwht_channels(const uint32_t (&raw)[8][4], float (&x)[8][8], int cb) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      // f32(lo) + f32(hi), f32(lo) - f32(hi): each one rounding, as the float32 add would
+      asm("v_fma_mix_f32 %0, %1, 1.0, %1 op_sel:[0,0,1] op_sel_hi:[1,0,1]"
+          : "=v"(x[j][2 * k]) : "v"(raw[j][k]));
+      asm("v_fma_mix_f32 %0, %1, 1.0, -%1 op_sel:[0,0,1] op_sel_hi:[1,0,1]"
+          : "=v"(x[j][2 * k + 1]) : "v"(raw[j][k]));
+    }
+  }
+  fwht_after_first(x, cb);
+}
+
+// The same transform on float32 values.
+__device__ __forceinline__ void fwht_channels_f32(float (&x)[8][8], int cb) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float a = x[j][2 * k], b = x[j][2 * k + 1];
+      x[j][2 * k] = a + b;
+      x[j][2 * k + 1] = a - b;
+    }
+  }
+  fwht_after_first(x, cb);
 }
 #undef KVARN_FMAC_DPP8
 
@@ -555,7 +576,85 @@ append_tokens_kernel(const __half* __restrict__ k_new, const __half* __restrict_
   }
 }
 
+// Page records back to float16 tiles (read side, then the inverse rotation H^-1 = H):
+// grid (n_tiles, num_kv_heads), one workgroup per record, the thread layout of the
+// quantizer (channels 8cb..+7 x tokens 8tb..+7). dst: [n_tiles][num_kv_heads][token][channel].
+template <int KIND>
+__global__ void __launch_bounds__(kThreads)
+dequantize_tiles_kernel(const uint8_t* __restrict__ pool, int64_t pool_num_pages,
+                        const int32_t* __restrict__ pages, int32_t num_kv_heads,
+                        __half* __restrict__ dst) {
+  constexpr int kRec = KIND == 0 ? kKRecord : kVRecord;
+  __shared__ uint4 rec_sm[kRec / 16];
+  const int tile = blockIdx.x, h = blockIdx.y;
+  const int64_t page = pages[tile];
+  if (page < 0 || page >= pool_num_pages) return;
+  const uint4* rec = reinterpret_cast<const uint4*>(pool + (page * num_kv_heads + h) * int64_t(kRec));
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kRec / 16; i += kThreads) rec_sm[i] = rec[i];
+  __syncthreads();
+  const uint32_t* words = reinterpret_cast<const uint32_t*>(rec_sm);
+  const uint16_t* meta = reinterpret_cast<const uint16_t*>(
+      reinterpret_cast<const uint8_t*>(rec_sm) + (KIND == 0 ? kKCodeBytes : kVCodeBytes));
+  const int w = tid >> 6, l = tid & 63, cb = l & 15, tb = 4 * w + (l >> 4);
+  float x[8][8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int t = 8 * tb + j;
+    const float st = h2f(meta[kTile + t]);
+    uint32_t kw = 0;
+    if constexpr (KIND == 0) kw = words[t * 16 + cb];   // channels 8cb..8cb+7 of token t
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = 8 * cb + i;
+      uint32_t code;
+      float sc, zr;
+      if constexpr (KIND == 0) {
+        code = (kw >> (4 * ((i & 1) ? 4 + (i >> 1) : (i >> 1)))) & 15u;   // nibble of channel i
+        sc = h2f(meta[2 * kDim + c]);
+        zr = h2f(meta[3 * kDim + c]);
+      } else {
+        // token t of channel c: word 8c + 2g + d, crumb p (the record's crumb order)
+        const int s_ = t >> 5, rem = t & 31;
+        const int g = rem < 16 ? rem >> 2 : (rem - 16) >> 2;
+        const int jj = rem < 16 ? rem & 3 : 4 + (rem & 3);
+        const int p = 4 * (s_ & 1) + (jj >> 1) + 8 * (jj & 1);
+        code = (words[8 * c + 2 * g + (s_ >> 1)] >> (2 * p)) & 3u;
+        sc = h2f(meta[2 * kDim + t]);
+        zr = h2f(meta[3 * kDim + t]);
+      }
+      x[j][i] = h2f(meta[c]) * st * fmaf(sc, float(code), zr);
+    }
+  }
+  fwht_channels_f32(x, cb);
+  __half* out = dst + (int64_t(tile) * num_kv_heads + h) * kTile * kDim;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint4 v;
+    v.x = uint32_t(f2h_rn(x[j][0])) | (uint32_t(f2h_rn(x[j][1])) << 16);
+    v.y = uint32_t(f2h_rn(x[j][2])) | (uint32_t(f2h_rn(x[j][3])) << 16);
+    v.z = uint32_t(f2h_rn(x[j][4])) | (uint32_t(f2h_rn(x[j][5])) << 16);
+    v.w = uint32_t(f2h_rn(x[j][6])) | (uint32_t(f2h_rn(x[j][7])) << 16);
+    *reinterpret_cast<uint4*>(out + (8 * tb + j) * kDim + 8 * cb) = v;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_dequantize_tiles(int kind, const void* pool, int64_t pool_num_pages,
+                                   const int32_t* pages, int32_t n_tiles, int32_t num_kv_heads,
+                                   void* dst, hipStream_t stream) {
+  dim3 grid(n_tiles, num_kv_heads), block(kThreads);
+  if (kind == 0)
+    hipLaunchKernelGGL(dequantize_tiles_kernel<0>, grid, block, 0, stream,
+                       static_cast<const uint8_t*>(pool), pool_num_pages, pages, num_kv_heads,
+                       static_cast<__half*>(dst));
+  else
+    hipLaunchKernelGGL(dequantize_tiles_kernel<1>, grid, block, 0, stream,
+                       static_cast<const uint8_t*>(pool), pool_num_pages, pages, num_kv_heads,
+                       static_cast<__half*>(dst));
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_tiles(int kind, const void* src, int64_t token_stride,
                                  int64_t head_stride, int64_t src_num_tokens,

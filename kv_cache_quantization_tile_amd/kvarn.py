@@ -55,6 +55,7 @@ def _load():
                                                    vp, vp, i64, vp]),
         "kvarn_append_tokens": (ctypes.c_int, [P, vp, vp, i32, i32, vp, vp, vp, vp, i32, vp, vp,
                                                i64, vp]),
+        "kvarn_dequantize_tiles": (ctypes.c_int, [P, ctypes.c_int, vp, i64, vp, i32, i32, vp, vp]),
         "kvarn_decode_workspace_bytes": (sz, [P, i32, i32, i32, i32]),
         "kvarn_decode_num_splits": (i32, [P, i32, i32, i32]),
         "kvarn_decode_attention": (ctypes.c_int, [P, vp, i32, i32, i32, vp, vp, i64, vp, i32, vp,
@@ -70,7 +71,8 @@ def _load():
 lib = _load()
 EXPORTED = ("kvarn_abi_version", "kvarn_format_version", "kvarn_status_str",
             "kvarn_params_from_dtype", "kvarn_params_check", "kvarn_page_bytes",
-            "kvarn_quantize_tiles", "kvarn_quantize_kv_tiles", "kvarn_append_tokens", "kvarn_decode_workspace_bytes",
+            "kvarn_quantize_tiles", "kvarn_quantize_kv_tiles", "kvarn_append_tokens",
+            "kvarn_dequantize_tiles", "kvarn_decode_workspace_bytes",
             "kvarn_decode_num_splits", "kvarn_decode_attention")
 
 
@@ -174,6 +176,26 @@ def quantize_kv_tiles(params: Params, k_src, v_src, tile_src_token, tile_dst_pag
                                                        tile_dst_page, k_pool, v_pool, stream)),
            "kvarn_quantize_kv_tiles")
     return k_pool, v_pool
+
+
+def dequantize_tiles(params: Params, kind: int, pool, pages, out=None, stream=None):
+    """Records (pages[i], h) of pool back to float16 tiles [n, Hkv, 128 tokens, 128 channels]
+    (test and inspection only)."""
+    _need(pool, "pool", torch.uint8)
+    _need(pages, "pages", torch.int32)
+    hkv = pool.shape[1]
+    n = pages.numel()
+    if pool.dim() != 3 or pool.shape[2] != page_bytes(params, kind) or not pool.is_contiguous():
+        raise ValueError("pool must be a contiguous page pool of this kind")
+    if out is None:
+        out = torch.empty((n, hkv, 128, 128), dtype=torch.float16, device=pool.device)
+    _need(out, "out", torch.float16)
+    if tuple(out.shape) != (n, hkv, 128, 128) or not out.is_contiguous():
+        raise ValueError(f"out must be contiguous [{n}, {hkv}, 128, 128]")
+    _check(lib.kvarn_dequantize_tiles(ctypes.byref(params), kind, _ptr(pool), pool.shape[0],
+                                      _ptr(pages), n, hkv, _ptr(out), _stream(stream)),
+           "kvarn_dequantize_tiles")
+    return out
 
 
 def append_tokens(params: Params, k_new, v_new, seq_lens, k_tail, v_tail, block_table,

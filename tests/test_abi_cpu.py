@@ -109,6 +109,26 @@ def test_quantize_kv_validation():
     assert _quant_kv(K.Params(128, 128, 4, 4, 128, 8)) == UNSUP
 
 
+def _dequant(p, **kw):
+    a = dict(kind=0, pool=FAKE, npages=10, pages=FAKE, n=1, hkv=8, dst=FAKE)
+    a.update(kw)
+    return K.lib.kvarn_dequantize_tiles(ctypes.byref(p), a["kind"], a["pool"], a["npages"],
+                                        a["pages"], a["n"], a["hkv"], a["dst"], None)
+
+
+def test_dequantize_validation():
+    p = K.params_from_dtype()
+    assert _dequant(p, n=0) == OK
+    assert _dequant(p, kind=3) == INVALID
+    assert _dequant(p, pool=None) == INVALID
+    assert _dequant(p, pages=None) == INVALID
+    assert _dequant(p, dst=None) == INVALID
+    assert _dequant(p, hkv=0) == INVALID
+    assert _dequant(p, npages=-2) == INVALID
+    assert _dequant(p, dst=ctypes.c_void_p(0x10002)) == INVALID
+    assert _dequant(K.Params(128, 128, 4, 4, 128, 8)) == UNSUP
+
+
 def _decode(p, **kw):
     a = dict(q=FAKE, B=2, hq=64, hkv=8, kp=FAKE, vp=FAKE, npages=100, bt=FAKE, bts=200, sl=FAKE,
              mx=16384, kt=None, vt=None, scale=0.088, ws=FAKE, wsb=1 << 30, out=FAKE)

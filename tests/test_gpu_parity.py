@@ -163,6 +163,40 @@ def test_quantize_kv_matches_separate_launches(K):
     T.assert_rate(st)
 
 
+@pytest.mark.parametrize("kind", [O.KIND_K, O.KIND_V])
+def test_dequantize_tiles_matches_oracle(K, kind):
+    """GPU records read back by kvarn_dequantize_tiles against the oracle's dequantization of
+    the same records: each element within half a float16 ulp of the float64 value (the final
+    rounding) plus 1e-5 of the tile's largest magnitude (float32 evaluation). Pages outside
+    the pool leave their output tile untouched."""
+    n, hkv = 8, 2
+    tiles = synth.tile_batch(n * hkv, "cpu", seed=41)
+    src = tiles.view(n, hkv, 128, 128).permute(0, 2, 1, 3).reshape(n * 128, hkv, 128).contiguous()
+    tok = (torch.arange(n, dtype=torch.int64) * 128)
+    pages = torch.randperm(n + 2, generator=torch.Generator().manual_seed(7))[:n].to(torch.int32)
+    params = K.params_from_dtype("kvarn_k4v2_g128", 8)
+    say(f"dequantize kind={kind}")
+    pool = _quantize(K, params, kind, src.cuda(), tok.cuda(), pages.cuda(), n + 2)
+    read = torch.cat([pages, torch.tensor([n + 5, -1], dtype=torch.int32)])   # 2 outside
+    out = torch.full((n + 2, hkv, 128, 128), 7.0, dtype=torch.float16, device="cuda")
+    K.dequantize_tiles(params, kind, pool, read.cuda(), out=out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.all(got[n:] == 7.0)
+    unpack = O.unpack_k_record if kind == O.KIND_K else O.unpack_v_record
+    worst = 0.0
+    for h in range(hkv):
+        for i, rec in enumerate(T.records_of(pool, pages.tolist(), h)):
+            d = unpack(rec)
+            ref = O.dequantize_tiles(d["codes"], d["r"], d["s"], d["scale"], d["zero"], kind).T
+            ulp = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64)
+            bound = 0.5 * ulp + 1e-5 * np.abs(ref).max()
+            err = np.abs(got[i, h] - ref)
+            assert np.all(err <= bound), (h, i, float((err / bound).max()))
+            worst = max(worst, float((err / bound).max()))
+    say(f"  worst error / bound {worst:.3f}")
+
+
 # ----------------------------------------------------------------------------- decode
 
 

@@ -196,7 +196,8 @@ KVARN_API int32_t kvarn_decode_num_splits(const kvarn_params* params, int32_t ba
  *   q_dev, out_dev: [batch, num_q_heads, 128] float16, contiguous, 16-byte aligned.
  *   num_q_heads % num_kv_heads == 0 and num_q_heads / num_kv_heads <= 8.
  *   k_tail_dev / v_tail_dev may be NULL: then tail tokens are ignored.
- *   Pages outside [0, pool_num_pages) are skipped. A sequence with L = 0 gets out = 0.
+ *   Pages outside [0, pool_num_pages) are skipped. A sequence with L = 0, or with every
+ *   page skipped and no tail, gets out = 0.
  *   workspace_dev: >= kvarn_decode_workspace_bytes(...) bytes, 16-byte aligned; it holds
  *   per-split partial softmax state and must not be shared by concurrent calls. */
 KVARN_API kvarn_status kvarn_decode_attention(const kvarn_params* params, const void* q_dev,

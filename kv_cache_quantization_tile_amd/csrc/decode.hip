@@ -133,40 +133,42 @@ struct PageRegs {
   uint32_t km[4], vm[4];
 };
 
-// Global-memory byte pointer (address space 1): loads through it use a scalar base plus a
-// 32-bit per-lane offset.
-typedef const uint8_t __attribute__((address_space(1)))* gbytes;
-
+// Page loads through buffer descriptors: one scalar descriptor per record (base, size), a
+// 32-bit per-lane offset fixed for the kernel and a scalar offset per load, so no per-load
+// address arithmetic runs on the vector ALU (and reads past the record return 0).
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kBufferFlags = 0x00020000;   // raw (untyped) 32-bit data
 
-template <typename T>
-__device__ __forceinline__ T gload(gbytes base, uint32_t off) {
-  return *reinterpret_cast<const T __attribute__((address_space(1)))*>(base + off);
-}
-__device__ __forceinline__ uint4 gload4(gbytes base, uint32_t off) {
-  const u32x4 v = gload<u32x4>(base, off);
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ uint2 gload2(gbytes base, uint32_t off) {
-  const u32x2 v = gload<u32x2>(base, off);
-  return make_uint2(v.x, v.y);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t record_rsrc(const uint8_t* rec, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(rec), (short)0, bytes, kBufferFlags);
 }
 
-__device__ __forceinline__ void load_meta(PageRegs& t, gbytes krec, gbytes vrec, int l) {
+struct LaneOffsets {
+  uint32_t k, v, m;   // key codes, value codes, metadata
+};
+
+__device__ __forceinline__ void load_meta(PageRegs& t, __amdgpu_buffer_rsrc_t kr,
+                                          __amdgpu_buffer_rsrc_t vr, const LaneOffsets& o) {
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
-    t.km[a] = gload<uint32_t>(krec, uint32_t(kKCodeBytes + 256 * a + 4 * l));
-    t.vm[a] = gload<uint32_t>(vrec, uint32_t(kVCodeBytes + 256 * a + 4 * l));
+    t.km[a] = __builtin_amdgcn_raw_buffer_load_b32(kr, o.m, kKCodeBytes + 256 * a, 0);
+    t.vm[a] = __builtin_amdgcn_raw_buffer_load_b32(vr, o.m, kVCodeBytes + 256 * a, 0);
   }
 }
-__device__ __forceinline__ void load_kcodes(PageRegs& t, gbytes krec, int n, int gq) {
+__device__ __forceinline__ void load_kcodes(PageRegs& t, __amdgpu_buffer_rsrc_t kr, const LaneOffsets& o) {
 #pragma unroll
-  for (int tb = 0; tb < 8; ++tb) t.kc[tb] = gload4(krec, uint32_t((16 * tb + n) * 64 + 16 * gq));
+  for (int tb = 0; tb < 8; ++tb) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(kr, o.k, 1024 * tb, 0);
+    t.kc[tb] = make_uint4(v.x, v.y, v.z, v.w);
+  }
 }
-__device__ __forceinline__ void load_vcodes(PageRegs& t, gbytes vrec, int n, int gq) {
+__device__ __forceinline__ void load_vcodes(PageRegs& t, __amdgpu_buffer_rsrc_t vr, const LaneOffsets& o) {
 #pragma unroll
-  for (int bb = 0; bb < 8; ++bb) t.vc[bb] = gload2(vrec, uint32_t((16 * bb + n) * 32 + 8 * gq));
+  for (int bb = 0; bb < 8; ++bb) {
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(vr, o.v, 512 * bb, 0);
+    t.vc[bb] = make_uint2(v.x, v.y);
+  }
 }
 
 __device__ __forceinline__ float lo_h(uint32_t w) { return h2f(uint16_t(w & 0xFFFF)); }
@@ -384,27 +386,36 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
     const int32_t page = __builtin_amdgcn_readfirstlane(bt_row[slot]);
     return (page < 0 || page >= pool_num_pages) ? -1 : int64_t(page);
   };
-  // record addresses are wave-uniform: keep them in scalar registers so that the loads use
-  // a scalar base plus a 32-bit lane offset
+  // record addresses are wave-uniform: their descriptors live in scalar registers
   auto uniform_ptr = [](const uint8_t* p) {
     const uint64_t a = reinterpret_cast<uint64_t>(p);
     const uint32_t lo32 = __builtin_amdgcn_readfirstlane(uint32_t(a));
     const uint32_t hi32 = __builtin_amdgcn_readfirstlane(uint32_t(a >> 32));
-    return reinterpret_cast<gbytes>((uint64_t(hi32) << 32) | lo32);
+    return reinterpret_cast<const uint8_t*>((uint64_t(hi32) << 32) | lo32);
   };
+  const LaneOffsets lo{uint32_t(n * 64 + 16 * gq), uint32_t(n * 32 + 8 * gq), uint32_t(4 * l)};
   // record index page * num_kv_heads + g fits 32 bits (the pool's record count is checked
   // on the host); byte offsets are 32 x 32 -> 64-bit products
+  // (the page id is re-read as a scalar here so that the offset arithmetic stays scalar)
+  // A page id below 0 (no page) gives an empty descriptor: its loads return zeros without
+  // touching memory, so the prefetches below need no branch.
   auto krec_of = [&](int64_t page) {
-    const uint32_t r = uint32_t(page) * uint32_t(num_kv_heads) + uint32_t(g);
-    return uniform_ptr(k_pool + uint64_t(r) * uint32_t(kKRecord));
+    const uint32_t ps = __builtin_amdgcn_readfirstlane(uint32_t(page < 0 ? 0 : page));
+    const uint32_t r = ps * uint32_t(num_kv_heads) + uint32_t(g);
+    return record_rsrc(uniform_ptr(k_pool + uint64_t(r) * uint32_t(kKRecord)),
+                       page < 0 ? 0 : kKRecord);
   };
   auto vrec_of = [&](int64_t page) {
-    const uint32_t r = uint32_t(page) * uint32_t(num_kv_heads) + uint32_t(g);
-    return uniform_ptr(v_pool + uint64_t(r) * uint32_t(kVRecord));
+    const uint32_t ps = __builtin_amdgcn_readfirstlane(uint32_t(page < 0 ? 0 : page));
+    const uint32_t r = ps * uint32_t(num_kv_heads) + uint32_t(g);
+    return record_rsrc(uniform_ptr(v_pool + uint64_t(r) * uint32_t(kVRecord)),
+                       page < 0 ? 0 : kVRecord);
   };
   // Processes the page held in t; each part of t is reloaded with page `next` as soon as
-  // this page has consumed it, so the loads overlap the rest of the page's work.
-  auto process = [&](PageRegs& t, int64_t next) {
+  // this page has consumed it, so the loads overlap the rest of the page's work. A page
+  // that is not `valid` (its id is out of range) runs the same code and adds nothing: its
+  // maximum stays -inf and its weights exp2(s - inf) are 0.
+  auto process = [&](PageRegs& t, int64_t next, bool valid) {
     // ---- page factors into the wave's LDS slot ------------------------------------------
     {
       const float rk0 = lo_h(t.km[0]), rk1 = hi_h(t.km[0]);
@@ -428,7 +439,7 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
           make_float2(fmaf(vs * sv0, lo_h(t.vm[3]), -p0), fmaf(vs * sv1, hi_h(t.vm[3]), -p1));
       reinterpret_cast<float2*>(wm.vr)[l] = make_float2(lo_h(t.vm[0]) * ivs, hi_h(t.vm[0]) * ivs);
     }
-    if (next >= 0) load_meta(t, krec_of(next), vrec_of(next), l);
+    load_meta(t, krec_of(next), vrec_of(next), lo);
     // LDS operations of one wave complete in order: the writes above land before the reads
     // below, and after the previous page's reads
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -489,7 +500,7 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
         }
       }
     }
-    if (next >= 0) load_kcodes(t, krec_of(next), n, gq);
+    load_kcodes(t, krec_of(next), lo);
 
     // ---- online softmax ------------------------------------------------------------------
     float mt = fmaxf(sc[0][0], sc[0][1]);
@@ -497,8 +508,9 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
     for (int tb = 1; tb < 8; ++tb) mt = fmaxf(mt, fmaxf(sc[tb][0], sc[tb][1]));
     mt = fmaxf(mt, dpp_f<kDppRowRor8>(mt));
     mt = rows4_max(mt);
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = exp2_fast(m_run - m_new);
+    const float m_new = fmaxf(m_run, valid ? mt : -INFINITY);
+    const float alpha = valid ? exp2_fast(m_run - m_new) : 1.f;
+    const float m_sub = valid ? m_new : INFINITY;
     H8 bp[4];
     float vcorr;
     {
@@ -512,7 +524,7 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
           const int t2 = 8 * tb + 2 * gq + (side >> 1);   // tokens 2 t2, 2 t2 + 1
           const float2 vp = wm.vp[t2];
           const float2 vz = wm.vz[t2];
-          const float p0 = exp2_fast(sc[tb][0] - m_new), p1 = exp2_fast(sc[tb][1] - m_new);
+          const float p0 = exp2_fast(sc[tb][0] - m_sub), p1 = exp2_fast(sc[tb][1] - m_sub);
           psum += p0 + p1;
           zpart = fmaf(p0, vz.x, fmaf(p1, vz.y, zpart));
           split_pk(p0 * vp.x, p1 * vp.y, hh[e], ll[e]);
@@ -559,27 +571,21 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
       acc[bb][2] = fmaf(rv.z, c[2], acc[bb][2]);
       acc[bb][3] = fmaf(rv.w, c[3], acc[bb][3]);
     }
-    if (next >= 0) load_vcodes(t, vrec_of(next), n, gq);
+    load_vcodes(t, vrec_of(next), lo);
   };
 
   PageRegs t;
-  int64_t cur = page_of(slot0 + w);
-  if (cur >= 0) {
-    load_meta(t, krec_of(cur), vrec_of(cur), l);
-    load_kcodes(t, krec_of(cur), n, gq);
-    load_vcodes(t, vrec_of(cur), n, gq);
-  }
-  for (int k = 0; k < tpw; ++k) {
-    const int slot = slot0 + w + 4 * k;
-    if (slot >= n_full) break;
-    const int64_t next = k + 1 < tpw ? page_of(slot + 4) : -1;
-    if (cur >= 0) {
-      process(t, next);
-    } else if (next >= 0) {
-      load_meta(t, krec_of(next), vrec_of(next), l);
-      load_kcodes(t, krec_of(next), n, gq);
-      load_vcodes(t, vrec_of(next), n, gq);
-    }
+  const int wslot = __builtin_amdgcn_readfirstlane(slot0 + w);   // this wave's first slot
+  int64_t cur = page_of(wslot);
+  load_meta(t, krec_of(cur), vrec_of(cur), lo);
+  load_kcodes(t, krec_of(cur), lo);
+  load_vcodes(t, vrec_of(cur), lo);
+  // pages of this wave: slots wslot, wslot + 4, ... below n_full, at most tpw of them
+  // (a loop with one exit keeps the running state in place across iterations)
+  const int n_here = wslot < n_full ? min(tpw, (n_full - wslot + 3) >> 2) : 0;
+  for (int k = 0; k < n_here; ++k) {
+    const int64_t next = k + 1 < n_here ? page_of(wslot + 4 * (k + 1)) : -1;
+    process(t, next, cur >= 0);
     cur = next;
   }
 

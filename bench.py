@@ -52,18 +52,19 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel: str, src_hash: str):
-    """HBM bytes per launch measured by rocprofv3 counters (profiles/traffic.json), or None
-    when absent or taken on a different kernel source."""
+def load_traffic(kernel: str, src_hash: str, workload: str):
+    """HBM bytes per launch of `kernel` in `workload` measured by rocprofv3 counters
+    (profiles/traffic.json), or None when absent or taken on a different kernel source."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_hash") != src_hash or kernel not in t.get("kernels", {}):
+    kernels = t.get("workloads", {}).get(workload, {}).get("kernels", {})
+    if t.get("source_hash") != src_hash or kernel not in kernels:
         return None
-    return t["kernels"][kernel].get("bytes_per_launch")
+    return kernels[kernel].get("bytes_per_launch")
 
 
 def cpu_baseline(w, n_iters: int, budget_s: float):
@@ -215,14 +216,14 @@ def main():
     quant_roof = {"kernel": "quantize_kv_kernel", "bound": "alu",
                   "achieved": round(q_achieved, 2), "peak": round(ALU_PEAK_TFLOPS, 1),
                   "unit": "TFLOP/s", "frac": round(q_achieved / ALU_PEAK_TFLOPS, 4),
-                  "traffic": load_traffic("quantize_kv_kernel", src_hash),
+                  "traffic": load_traffic("quantize_kv_kernel", src_hash, args.workload),
                   "hbm_gbps": round(q_bytes / (q_launch_ms * 1e-3) / 1e9, 1),
                   "per_launch": f"{2 * n_tiles} K+V tiles x {flop_tile} FLOP",
                   "launch_ms": round(q_launch_ms, 5)}
     dec_roof = {"kernel": "decode (pages + merge)", "bound": "hbm",
                 "achieved": round(decode_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(decode_gbps / HBM_PEAK_GBPS, 4),
-                "traffic": load_traffic("decode_pages_kernel", src_hash),
+                "traffic": load_traffic("decode_pages_kernel", src_hash, args.workload),
                 "per_launch": f"{B * hkv * full_pages} K+V page pairs x {K_REC + V_REC} B + q/out",
                 "launch_ms": round(d_ms, 5)}
     dominant, other = (quant_roof, dec_roof) if q_ms >= d_ms else (dec_roof, quant_roof)

@@ -216,8 +216,9 @@ __host__ __device__ constexpr uint32_t walsh8_dword(int c, int d) {
   return w;
 }
 
-// Rotation X -> X H (natural-order Sylvester H, entries +-1, then * 1/sqrt(128)) of the
-// wave's 32 tokens on the matrix cores. MFMA block (token block tb2, input channels
+// Rotation X -> X H of the wave's 32 tokens on the matrix cores, H the natural-order
+// Sylvester matrix with entries +-1: the result is sqrt(128) times the orthonormal rotation
+// (the factor is carried by the channel weights of the normalization, see quantize_tile). MFMA block (token block tb2, input channels
 // 32 kb .. 32 kb + 31) x (those channels, output column block cc): A lane l = token
 // 32w + 16 tb2 + l % 16, input channels 32 kb + 8 (l / 16) + i (one 16-byte load); B lane
 // l = the same input channels, output channel 8 (l % 16) + cc. The sign of H at (input a,
@@ -267,8 +268,8 @@ __device__ __forceinline__ void rotate_tile_mfma(RowPtr row_ptr, int w, int l, f
   for (int cc = 0; cc < 8; ++cc)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      x[r][cc] = acc[0][cc][r] * kInvSqrt128;
-      x[4 + r][cc] = acc[1][cc][r] * kInvSqrt128;
+      x[r][cc] = acc[0][cc][r];
+      x[4 + r][cc] = acc[1][cc][r];
     }
 }
 
@@ -282,13 +283,16 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
   // token of slot j (the rotation's accumulator layout)
   auto tok = [&](int j) { return 32 * w + 16 * (j >> 2) + 4 * (l >> 4) + (j & 3); };
 
-  // ---- 1-2. gather and rotate: x[j][i] = (H X)[8cb + i, token of slot j] ------------------
+  // ---- 1-2. gather and rotate: x[j][i] = sqrt(128) (H X)[8cb + i, token of slot j] ---------
+  // x is kept unnormalized: the channel weights below start at 1/sqrt(128) instead of 1, so
+  // every channel variance (and r) is computed 128 (sqrt(128)) times too large, which the
+  // stored r and the code factors undo exactly (a power of two) or once per group.
   float x[8][8];
   rotate_tile_mfma(row_ptr, w, l, x);
 
   // ---- 3. normalize -----------------------------------------------------------------
   // Two passes per step (mean, then centred sum of squares), float32 FMAs. A group's
-  // statistics are reduce-scattered to one owner lane: token 8 tb + (l & 7) for the column
+  // statistics are reduce-scattered to one owner lane: token slot l & 7 for the column
   // step (over channels), channels 8 cb + off + {0, 1} for the row step (over tokens; the
   // 4 waves add their partials through LDS); the owner computes the group's weight and LDS
   // broadcasts it back inside the wave. The next step's weights are 1/std = rsqrt(var). A
@@ -305,9 +309,9 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
   float* gr1 = &sm.gr[w][1][0];
   float ir[8], is[8];      // 1/r for my channels, 1/s for my tokens
 #pragma unroll
-  for (int i = 0; i < 8; ++i) { ir[i] = 1.f; is[i] = 1.f; }
+  for (int i = 0; i < 8; ++i) { ir[i] = kInvSqrt128; is[i] = 1.f; }
   float vs_own = 1.f;                  // last accepted variance of my token (1 = never)
-  float vr_own[2] = {1.f, 1.f};        // ... of my two channels
+  float vr_own[2] = {128.f, 128.f};    // ... of my two channels, in units of x (128 = never)
   int buf = 0;
   auto cross_wave_sum = [&](const float (&o)[2], float (&t)[2]) {
     *reinterpret_cast<float2*>(&sm.red[buf][w][ch_own]) = make_float2(o[0], o[1]);
@@ -392,10 +396,12 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
 
   // ---- 4a. stored normalizers (float16) and their inverses on every lane ----------------
   const uint16_t s16 = normalizer16(__builtin_amdgcn_sqrtf(vs_own));
-  const uint16_t r16a = normalizer16(__builtin_amdgcn_sqrtf(vr_own[0]));
-  const uint16_t r16b = normalizer16(__builtin_amdgcn_sqrtf(vr_own[1]));
+  const uint16_t r16a = normalizer16(__builtin_amdgcn_sqrtf(vr_own[0] * (1.f / 128.f)));
+  const uint16_t r16b = normalizer16(__builtin_amdgcn_sqrtf(vr_own[1] * (1.f / 128.f)));
   const float is_own = __builtin_amdgcn_rcpf(h2f(s16));
-  const float ir_own[2] = {__builtin_amdgcn_rcpf(h2f(r16a)), __builtin_amdgcn_rcpf(h2f(r16b))};
+  // 1 / (sqrt(128) r): divides x (unnormalized) by the stored r
+  const float ir_own[2] = {__builtin_amdgcn_rcpf(h2f(r16a)) * kInvSqrt128,
+                           __builtin_amdgcn_rcpf(h2f(r16b)) * kInvSqrt128};
   if (w == 0) {            // every channel once
     sm.meta[0][ch_own] = r16a;
     sm.meta[0][ch_own + 1] = r16b;

@@ -181,6 +181,21 @@ def one_layer(device="cpu", seed: int = 1, context: int = 16384) -> Workload:
                   n_iters=8, decode_steps=1, seed=seed)
 
 
+def uneven_tokens(device="cpu", seed: int = 5, context: int = 4096, hkv: int = 8,
+                  sigma: float = 1.0) -> Workload:
+    """Channel structure of `one_layer` (lognormal(0,1) channel magnitudes, 3 outlier channels
+    x10) times per-token magnitudes lognormal(0, sigma): a cache whose token scales are
+    uneven. 8 query heads per KV head, batch 1, contiguous pages, one decode step."""
+    g = _gen(seed, device)
+    k = _magnitude_channels(context, hkv, g, device, 1.0, 3, 10.0)
+    v = _magnitude_channels(context, hkv, g, device, 1.0, 3, 10.0)
+    for dst in (k, v):
+        tok = _lognormal(context * hkv, sigma, g, device).view(context, hkv, 1)
+        dst.copy_((dst.float() * tok).to(torch.float16))
+    return _paged("uneven_tokens", 8 * hkv, hkv, k, v, [context], g, device, False, 0,
+                  n_iters=8, decode_steps=1, seed=seed)
+
+
 def batched_paged(device="cpu", seed: int = 2, batch: int = 32, lo: int = 4096,
                   hi: int = 32768, steps: int = 16, lens=None) -> Workload:
     """Batched paged decode: context lengths uniform in [lo, hi] rounded to 128, pages

@@ -148,7 +148,8 @@ def rtn_asym(y: np.ndarray, bits: int, axis: int):
     return codes, np.squeeze(scale16, axis), np.squeeze(zero16, axis), u
 
 
-def quantize_tiles(x16: np.ndarray, kind: int, n_iters: int = 8, lossless: bool = False):
+def quantize_tiles(x16: np.ndarray, kind: int, n_iters: int = 8, lossless: bool = False,
+                   rotate_channels: bool = True):
     """Quantize tiles end to end (stages 1-4 of [README] "How KVarN works").
 
     x16: [..., 128 channels, 128 tokens] float16 (stage 1: the raw tile, channels x tokens).
@@ -161,11 +162,12 @@ def quantize_tiles(x16: np.ndarray, kind: int, n_iters: int = 8, lossless: bool 
     against the stored normalizers) and 'u' (unrounded codes).
 
     lossless=True stops after stage 3 and returns no codes (used to pin the bookkeeping).
+    rotate_channels=False skips stage 2 (Xr = X): an ablation of the method, not the method.
     """
     x = np.asarray(x16, dtype=np.float16).astype(np.float64)
     if x.shape[-2:] != (HEAD_DIM, TILE_TOKENS):
         raise ValueError("tile must be 128 channels x 128 tokens")
-    xr = rotate(x)
+    xr = rotate(x) if rotate_channels else x
     la, lb = sinkhorn_log(xr, n_iters)
     r16 = store_normalizer(la)
     s16 = store_normalizer(lb)
@@ -183,12 +185,14 @@ def quantize_tiles(x16: np.ndarray, kind: int, n_iters: int = 8, lossless: bool 
     return out
 
 
-def dequantize_tiles(codes, r16, s16, scale16, zero16, kind: int) -> np.ndarray:
+def dequantize_tiles(codes, r16, s16, scale16, zero16, kind: int,
+                     rotate_channels: bool = True) -> np.ndarray:
     """Inverse of quantize_tiles up to rounding: X_hat = H (r s^T * (zero + scale * code)).
 
     The scales are re-applied per channel for keys and per token for values
     ([README] "How KVarN works", stage 4); H is symmetric and its own inverse.
-    Returns float64 [..., 128 c, 128 t].
+    Returns float64 [..., 128 c, 128 t]. rotate_channels=False inverts a tile quantized
+    without stage 2 (the ablation of quantize_tiles).
     """
     codes = np.asarray(codes, dtype=np.float64)
     sc = np.asarray(scale16, dtype=np.float64)
@@ -200,7 +204,7 @@ def dequantize_tiles(codes, r16, s16, scale16, zero16, kind: int) -> np.ndarray:
     r = np.asarray(r16, dtype=np.float64)
     s = np.asarray(s16, dtype=np.float64)
     xr_hat = r[..., :, None] * s[..., None, :] * yhat
-    return hadamard(HEAD_DIM) @ xr_hat
+    return hadamard(HEAD_DIM) @ xr_hat if rotate_channels else xr_hat
 
 
 # ----------------------------------------------------------------------------- page format

@@ -160,6 +160,36 @@ KVARN_API kvarn_status kvarn_append_tokens(const kvarn_params* params, const voi
                                  int32_t block_table_stride, void* k_pool_dev,
                                  void* v_pool_dev, int64_t pool_num_pages, void* stream);
 
+/* Write a chunk of new tokens per sequence into the cache: the prefill write path, with the
+ * staging append fused in (README "Quick start": one page = one 128-token tile; "How KVarN
+ * works": tiles are quantized whole, stages 1-4).
+ *
+ * Sequence b holds L = seq_lens_dev[b] tokens before the call (L >= 0; L < 0 skips b) and
+ * receives n = cu_new_dev[b + 1] - cu_new_dev[b] tokens (clamped to [0, max_new_tokens]),
+ * rows cu_new_dev[b] .. cu_new_dev[b] + n - 1 of k_new_dev / v_new_dev (float16
+ * [total_new_tokens, num_kv_heads, 128], token-major, contiguous: the projection output), at
+ * positions L .. L + n - 1. cu_new_dev: int32 [batch + 1], non-decreasing; a sequence whose
+ * rows fall outside [0, total_new_tokens) is skipped. The host bound max_new_tokens >= every
+ * n sizes the grid.
+ *   - Every tile t completed by the chunk (L < 128 t + 128 <= L + n) is quantized, both kinds
+ *     and all heads, into page block_table_dev[b * block_table_stride + t] of k_pool_dev /
+ *     v_pool_dev. Rows of that tile below L are read from the staging tiles (the tile that
+ *     was partial before the chunk), the others straight from k_new_dev / v_new_dev.
+ *   - The chunk's tokens in the partial last tile (positions >= 128 floor((L+n)/128)) are
+ *     written to rows (position mod 128) of k_tail_dev / v_tail_dev ([B, Hkv, 128, 128]
+ *     float16); other staging rows are left as they are.
+ * Tiles with t >= block_table_stride or a page outside [0, pool_num_pages) are skipped. The
+ * caller advances seq_lens by n afterwards. With n = 1 this equals kvarn_append_tokens.
+ * Two launches on `stream` (tiles, then staging); all pointers 16-byte aligned. */
+KVARN_API kvarn_status kvarn_write_tokens(const kvarn_params* params, const void* k_new_dev,
+                                const void* v_new_dev, int32_t total_new_tokens,
+                                const int32_t* cu_new_dev, int32_t max_new_tokens,
+                                int32_t batch, int32_t num_kv_heads,
+                                const int32_t* seq_lens_dev, void* k_tail_dev, void* v_tail_dev,
+                                const int32_t* block_table_dev, int32_t block_table_stride,
+                                void* k_pool_dev, void* v_pool_dev, int64_t pool_num_pages,
+                                void* stream);
+
 /* Test and inspection only, off the hot path: page records back to float16 tiles (the read
  * side of README "How KVarN works" stage 4, then the inverse rotation; H is its own
  * inverse). For i < n_tiles and head h < num_kv_heads, the record (pages_dev[i], h) of

@@ -176,6 +176,32 @@ kvarn_status kvarn_append_tokens(const kvarn_params* params, const void* k_new, 
       static_cast<hipStream_t>(stream)));
 }
 
+kvarn_status kvarn_write_tokens(const kvarn_params* params, const void* k_new, const void* v_new,
+                                int32_t total_new_tokens, const int32_t* cu_new,
+                                int32_t max_new_tokens, int32_t batch,
+                                int32_t num_kv_heads, const int32_t* seq_lens, void* k_tail,
+                                void* v_tail, const int32_t* block_table,
+                                int32_t block_table_stride, void* k_pool, void* v_pool,
+                                int64_t pool_num_pages, void* stream) {
+  const kvarn_status st = kvarn_params_check(params);
+  if (st != KVARN_OK) return st;
+  if (batch < 0 || batch > 65535 || num_kv_heads <= 0 || num_kv_heads > 32767 ||
+      block_table_stride <= 0 || pool_num_pages < 0 || max_new_tokens < 0 ||
+      total_new_tokens < 0)
+    return KVARN_ERR_INVALID_ARG;
+  if (batch == 0 || max_new_tokens == 0 || total_new_tokens == 0) return KVARN_OK;
+  if (!k_new || !v_new || !cu_new || !seq_lens || !k_tail || !v_tail || !block_table || !k_pool ||
+      !v_pool)
+    return KVARN_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_tail) || !aligned16(v_tail) ||
+      !aligned16(k_pool) || !aligned16(v_pool))
+    return KVARN_ERR_INVALID_ARG;
+  return launch_status(kvarn::launch_write_tokens(
+      k_new, v_new, total_new_tokens, cu_new, max_new_tokens, batch, num_kv_heads, seq_lens, k_tail, v_tail,
+      block_table, block_table_stride, k_pool, v_pool, pool_num_pages, params->sinkhorn_iters,
+      static_cast<hipStream_t>(stream)));
+}
+
 size_t kvarn_decode_workspace_bytes(const kvarn_params* params, int32_t batch, int32_t num_q_heads,
                                     int32_t num_kv_heads, int32_t max_seq_len) {
   if (kvarn_params_check(params) != KVARN_OK) return 0;

@@ -23,6 +23,14 @@ hipError_t launch_dequantize_tiles(int kind, const void* pool, int64_t pool_num_
                                    const int32_t* pages, int32_t n_tiles, int32_t num_kv_heads,
                                    void* dst, hipStream_t stream);
 
+hipError_t launch_write_tokens(const void* k_new, const void* v_new, int32_t total_new,
+                               const int32_t* cu_new, int32_t max_new, int32_t batch,
+                               int32_t num_kv_heads,
+                               const int32_t* seq_lens, void* k_tail, void* v_tail,
+                               const int32_t* block_table, int32_t bt_stride, void* k_pool,
+                               void* v_pool, int64_t pool_num_pages, int n_iters,
+                               hipStream_t stream);
+
 hipError_t launch_append_tokens(const void* k_new, const void* v_new, int32_t batch,
                                 int32_t num_kv_heads, const int32_t* seq_lens, void* k_tail,
                                 void* v_tail, const int32_t* block_table, int32_t bt_stride,

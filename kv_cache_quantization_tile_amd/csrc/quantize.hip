@@ -638,6 +638,76 @@ append_tokens_kernel(const __half* __restrict__ k_new, const __half* __restrict_
   }
 }
 
+// Chunk write, part 1: every tile that the chunk completes is quantized into its page.
+// Sequence b holds L = seq_lens[b] tokens before the chunk and receives n tokens, rows
+// cu_new[b] .. cu_new[b] + n - 1 of the token-major new-token buffers, at positions L .. L+n-1.
+// grid: (tile slots, batch, num_kv_heads * 2); slot j is tile t = L / 128 + j, quantized when
+// complete (128 t + 128 <= L + n). Its rows below L come from staging (only the tile that was
+// partial before the chunk has such rows), the others straight from the new-token buffer.
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+write_tiles_kernel(const __half* __restrict__ k_new, const __half* __restrict__ v_new,
+                   int32_t total_new, const int32_t* __restrict__ cu_new, int32_t max_new,
+                   int32_t num_kv_heads,
+                   const int32_t* __restrict__ seq_lens, const __half* __restrict__ k_tail,
+                   const __half* __restrict__ v_tail, const int32_t* __restrict__ block_table,
+                   int32_t bt_stride, uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
+                   int64_t pool_num_pages, int n_iters) {
+  __shared__ QuantSmem sm;
+  const int b = blockIdx.y;
+  const int h = blockIdx.z >> 1, kind = blockIdx.z & 1;
+  const int32_t L = seq_lens[b];
+  const int32_t c0 = cu_new[b];
+  int32_t n = cu_new[b + 1] - c0;
+  n = n < 0 ? 0 : (n > max_new ? max_new : n);
+  if (L < 0 || c0 < 0 || int64_t(c0) + n > total_new) return;   // rows outside the buffers
+  const int64_t t = int64_t(L / kTile) + blockIdx.x;
+  const int64_t end = int64_t(L) + n;
+  if (t * kTile + kTile > end || t >= bt_stride) return;     // not completed by this chunk
+  const int64_t page = block_table[int64_t(b) * bt_stride + t];
+  if (page < 0 || page >= pool_num_pages) return;
+  const int64_t row_stride = int64_t(num_kv_heads) * kDim;
+  const __half* src = (kind == 0 ? k_new : v_new) + int64_t(c0) * row_stride + int64_t(h) * kDim;
+  const __half* stage = (kind == 0 ? k_tail : v_tail) + (int64_t(b) * num_kv_heads + h) * kTile * kDim;
+  const int64_t t0 = t * kTile;
+  auto row_ptr = [=](int r) {
+    const int64_t a = t0 + r;
+    return a < L ? stage + int64_t(r) * kDim : src + (a - L) * row_stride;
+  };
+  if (kind == 0)
+    quantize_tile<0>(row_ptr, k_pool + (page * num_kv_heads + h) * int64_t(kKRecord), n_iters, sm);
+  else
+    quantize_tile<1>(row_ptr, v_pool + (page * num_kv_heads + h) * int64_t(kVRecord), n_iters, sm);
+}
+
+// Chunk write, part 2 (after part 1, which reads the staging rows this overwrites): the new
+// tokens of the partial last tile, positions max(L, 128 floor((L+n)/128)) .. L+n-1, go to
+// staging rows position mod 128. grid: (batch, num_kv_heads, 2 kinds); 16 bytes per thread.
+__global__ void __launch_bounds__(kThreads)
+write_staging_kernel(const __half* __restrict__ k_new, const __half* __restrict__ v_new,
+                     int32_t total_new, const int32_t* __restrict__ cu_new, int32_t max_new,
+                     int32_t num_kv_heads,
+                     const int32_t* __restrict__ seq_lens, __half* __restrict__ k_tail,
+                     __half* __restrict__ v_tail) {
+  const int b = blockIdx.x, h = blockIdx.y, kind = blockIdx.z;
+  const int32_t L = seq_lens[b];
+  const int32_t c0 = cu_new[b];
+  int32_t n = cu_new[b + 1] - c0;
+  n = n < 0 ? 0 : (n > max_new ? max_new : n);
+  if (L < 0 || n == 0 || c0 < 0 || int64_t(c0) + n > total_new) return;
+  const int64_t end = int64_t(L) + n;
+  const int64_t first = end / kTile * kTile > L ? end / kTile * kTile : L;   // first staged position
+  const int rows = int(end - first);                                          // 0 .. 127
+  const int64_t row_stride = int64_t(num_kv_heads) * kDim;
+  const __half* src = (kind == 0 ? k_new : v_new) + int64_t(c0) * row_stride + int64_t(h) * kDim;
+  __half* stage = (kind == 0 ? k_tail : v_tail) + (int64_t(b) * num_kv_heads + h) * kTile * kDim;
+  for (int i = threadIdx.x; i < rows * 16; i += kThreads) {
+    const int r = i >> 4, c = (i & 15) * 8;
+    const int64_t a = first + r;
+    *reinterpret_cast<uint4*>(stage + (a % kTile) * kDim + c) =
+        *reinterpret_cast<const uint4*>(src + (a - L) * row_stride + c);
+  }
+}
+
 // Page records back to float16 tiles (read side, then the inverse rotation H^-1 = H):
 // grid (n_tiles, num_kv_heads), one workgroup per record, the thread layout of the
 // quantizer (channels 8cb..+7 x tokens 8tb..+7). dst: [n_tiles][num_kv_heads][token][channel].
@@ -749,6 +819,32 @@ hipError_t launch_quantize_kv(const void* k_src, const void* v_src, int64_t toke
                      token_stride, head_stride, src_num_tokens, tile_src_token, tile_dst_page,
                      num_kv_heads, static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool),
                      pool_num_pages, n_iters);
+  return hipGetLastError();
+}
+
+hipError_t launch_write_tokens(const void* k_new, const void* v_new, int32_t total_new,
+                               const int32_t* cu_new, int32_t max_new, int32_t batch,
+                               int32_t num_kv_heads,
+                               const int32_t* seq_lens, void* k_tail, void* v_tail,
+                               const int32_t* block_table, int32_t bt_stride, void* k_pool,
+                               void* v_pool, int64_t pool_num_pages, int n_iters,
+                               hipStream_t stream) {
+  // tiles completed by n tokens: at most n / 128 + 1
+  dim3 grid1(max_new / kTile + 1, batch, num_kv_heads * 2), block(kThreads);
+  hipLaunchKernelGGL(write_tiles_kernel, grid1, block, 0, stream,
+                     static_cast<const __half*>(k_new), static_cast<const __half*>(v_new),
+                     total_new, cu_new, max_new, num_kv_heads, seq_lens,
+                     static_cast<const __half*>(k_tail),
+                     static_cast<const __half*>(v_tail), block_table, bt_stride,
+                     static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), pool_num_pages,
+                     n_iters);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 grid2(batch, num_kv_heads, 2);
+  hipLaunchKernelGGL(write_staging_kernel, grid2, block, 0, stream,
+                     static_cast<const __half*>(k_new), static_cast<const __half*>(v_new),
+                     total_new, cu_new, max_new, num_kv_heads, seq_lens, static_cast<__half*>(k_tail),
+                     static_cast<__half*>(v_tail));
   return hipGetLastError();
 }
 

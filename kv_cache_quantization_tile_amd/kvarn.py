@@ -55,6 +55,8 @@ def _load():
                                                    vp, vp, i64, vp]),
         "kvarn_append_tokens": (ctypes.c_int, [P, vp, vp, i32, i32, vp, vp, vp, vp, i32, vp, vp,
                                                i64, vp]),
+        "kvarn_write_tokens": (ctypes.c_int, [P, vp, vp, i32, vp, i32, i32, i32, vp, vp, vp, vp,
+                                              i32, vp, vp, i64, vp]),
         "kvarn_dequantize_tiles": (ctypes.c_int, [P, ctypes.c_int, vp, i64, vp, i32, i32, vp, vp]),
         "kvarn_decode_workspace_bytes": (sz, [P, i32, i32, i32, i32]),
         "kvarn_decode_num_splits": (i32, [P, i32, i32, i32]),
@@ -72,7 +74,7 @@ lib = _load()
 EXPORTED = ("kvarn_abi_version", "kvarn_format_version", "kvarn_status_str",
             "kvarn_params_from_dtype", "kvarn_params_check", "kvarn_page_bytes",
             "kvarn_quantize_tiles", "kvarn_quantize_kv_tiles", "kvarn_append_tokens",
-            "kvarn_dequantize_tiles", "kvarn_decode_workspace_bytes",
+            "kvarn_write_tokens", "kvarn_dequantize_tiles", "kvarn_decode_workspace_bytes",
             "kvarn_decode_num_splits", "kvarn_decode_attention")
 
 
@@ -216,6 +218,38 @@ def append_tokens(params: Params, k_new, v_new, seq_lens, k_tail, v_tail, block_
                                    _ptr(seq_lens), _ptr(k_tail), _ptr(v_tail), _ptr(block_table),
                                    block_table.shape[1], _ptr(k_pool), _ptr(v_pool),
                                    k_pool.shape[0], _stream(stream)), "kvarn_append_tokens")
+
+
+def write_tokens(params: Params, k_new, v_new, cu_new, seq_lens, k_tail, v_tail, block_table,
+                 k_pool, v_pool, max_new_tokens: int | None = None, stream=None):
+    """Write a chunk of tokens per sequence (rows cu_new[b] .. cu_new[b+1]-1 of the token-major
+    k_new / v_new [total, Hkv, 128]) at positions seq_lens[b] ..: completed tiles are quantized
+    into their pages, the partial last tile goes to staging. max_new_tokens bounds every
+    chunk (computed from cu_new on the host when omitted, which synchronizes)."""
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new"), (k_tail, "k_tail"), (v_tail, "v_tail")):
+        _need(t, nm, torch.float16)
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    _need(cu_new, "cu_new", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32)
+    _need(block_table, "block_table", torch.int32)
+    B = seq_lens.shape[0]
+    total, hkv = k_new.shape[0], k_new.shape[1]
+    if tuple(v_new.shape) != tuple(k_new.shape) or k_new.dim() != 3 or k_new.shape[2] != 128:
+        raise ValueError("k_new / v_new must be [total, Hkv, 128]")
+    if cu_new.shape != (B + 1,):
+        raise ValueError("cu_new must be [batch + 1]")
+    if tuple(k_tail.shape) != (B, hkv, 128, 128) or tuple(v_tail.shape) != (B, hkv, 128, 128):
+        raise ValueError("staging must be [B, Hkv, 128, 128]")
+    if block_table.dim() != 2 or block_table.shape[0] != B or not block_table.is_contiguous():
+        raise ValueError("block_table must be contiguous [B, width]")
+    if max_new_tokens is None:
+        max_new_tokens = int((cu_new[1:] - cu_new[:-1]).max().item()) if B else 0
+    _check(lib.kvarn_write_tokens(ctypes.byref(params), _ptr(k_new), _ptr(v_new), total,
+                                  _ptr(cu_new), max(int(max_new_tokens), 0), B, hkv,
+                                  _ptr(seq_lens), _ptr(k_tail), _ptr(v_tail), _ptr(block_table),
+                                  block_table.shape[1], _ptr(k_pool), _ptr(v_pool),
+                                  k_pool.shape[0], _stream(stream)), "kvarn_write_tokens")
 
 
 # ----------------------------------------------------------------------------- decode

@@ -129,6 +129,34 @@ def test_dequantize_validation():
     assert _dequant(K.Params(128, 128, 4, 4, 128, 8)) == UNSUP
 
 
+def _write(p, **kw):
+    a = dict(kn=FAKE, vn=FAKE, total=1000, cu=FAKE, mx=512, B=4, hkv=8, sl=FAKE, kt=FAKE, vt=FAKE,
+             bt=FAKE, bts=64, kp=FAKE, vp=FAKE, npages=100)
+    a.update(kw)
+    return K.lib.kvarn_write_tokens(ctypes.byref(p), a["kn"], a["vn"], a["total"], a["cu"], a["mx"],
+                                    a["B"], a["hkv"], a["sl"], a["kt"], a["vt"], a["bt"], a["bts"],
+                                    a["kp"], a["vp"], a["npages"], None)
+
+
+def test_write_tokens_validation():
+    p = K.params_from_dtype()
+    assert _write(p, B=0) == OK
+    assert _write(p, mx=0) == OK
+    assert _write(p, total=0) == OK
+    assert _write(p, B=-1) == INVALID
+    assert _write(p, mx=-1) == INVALID
+    assert _write(p, total=-5) == INVALID
+    assert _write(p, hkv=0) == INVALID
+    assert _write(p, hkv=40000) == INVALID            # grid z = 2 * Hkv
+    assert _write(p, bts=0) == INVALID
+    assert _write(p, cu=None) == INVALID
+    assert _write(p, vt=None) == INVALID
+    assert _write(p, kn=ctypes.c_void_p(0x10004)) == INVALID
+    assert _write(p, vp=ctypes.c_void_p(0x10008)) == INVALID
+    assert _write(p, npages=-1) == INVALID
+    assert _write(K.Params(128, 128, 4, 4, 128, 8)) == UNSUP
+
+
 def _decode(p, **kw):
     a = dict(q=FAKE, B=2, hq=64, hkv=8, kp=FAKE, vp=FAKE, npages=100, bt=FAKE, bts=200, sl=FAKE,
              mx=16384, kt=None, vt=None, scale=0.088, ws=FAKE, wsb=1 << 30, out=FAKE)

@@ -190,6 +190,35 @@ KVARN_API kvarn_status kvarn_write_tokens(const kvarn_params* params, const void
                                 void* k_pool_dev, void* v_pool_dev, int64_t pool_num_pages,
                                 void* stream);
 
+/* Attention of several query positions per sequence over the quantized cache: the read path
+ * of a prefill chunk (or of draft tokens to verify), causal, same arithmetic as
+ * kvarn_decode_attention per query position (README intro: attention reads the quantized
+ * cache; "How KVarN works" stage 4: scales re-applied on read).
+ *
+ * The cache of sequence b holds C = seq_lens_dev[b] tokens (clamped to [0, max_seq_len]), the
+ * chunk already written into it (kvarn_write_tokens). Its query rows are
+ * cu_q_dev[b] .. cu_q_dev[b + 1] - 1 of q_dev (float16 [total_q, num_q_heads, 128]): row
+ * cu_q_dev[b] + i is position C - n + i, n = cu_q_dev[b + 1] - cu_q_dev[b], and attends to
+ * positions 0 .. C - n + i (rows at positions below 0 get zeros). Positions in completed
+ * tiles are read from the pages (a tile cut by the causal limit is read with a mask), those
+ * of the partial last tile from the staging tiles (ignored when k_tail_dev / v_tail_dev are
+ * NULL). out_dev: float16 [total_q, num_q_heads, 128]. cu_q_dev: int32 [batch + 1],
+ * non-decreasing, cu_q_dev[0] = 0, cu_q_dev[batch] = total_q.
+ * Limits and other arguments as kvarn_decode_attention with total_q in place of batch
+ * (workspace from kvarn_decode_workspace_bytes(params, total_q, ...)); total_q <= 65535
+ * (UNSUPPORTED above). Each query row costs one decode row: pages shared by the rows of a
+ * sequence are re-read, mostly from the caches. */
+KVARN_API kvarn_status kvarn_chunk_attention(const kvarn_params* params, const void* q_dev,
+                                   int32_t total_q, const int32_t* cu_q_dev, int32_t batch,
+                                   int32_t num_q_heads, int32_t num_kv_heads,
+                                   const void* k_pool_dev, const void* v_pool_dev,
+                                   int64_t pool_num_pages, const int32_t* block_table_dev,
+                                   int32_t block_table_stride, const int32_t* seq_lens_dev,
+                                   int32_t max_seq_len, const void* k_tail_dev,
+                                   const void* v_tail_dev, float softmax_scale,
+                                   void* workspace_dev, size_t workspace_bytes, void* out_dev,
+                                   void* stream);
+
 /* Test and inspection only, off the hot path: page records back to float16 tiles (the read
  * side of README "How KVarN works" stage 4, then the inverse rotation; H is its own
  * inverse). For i < n_tiles and head h < num_kv_heads, the record (pages_dev[i], h) of

@@ -250,8 +250,45 @@ kvarn_status kvarn_decode_attention(const kvarn_params* params, const void* q, i
     return KVARN_ERR_WORKSPACE;
   return launch_status(kvarn::launch_decode(
       q, batch, num_q_heads, num_kv_heads, k_pool, v_pool, pool_num_pages, block_table,
-      block_table_stride, seq_lens, max_seq_len, k_tail, v_tail, softmax_scale, workspace, out,
-      static_cast<hipStream_t>(stream)));
+      block_table_stride, seq_lens, max_seq_len, nullptr, batch, k_tail, v_tail, softmax_scale,
+      workspace, out, static_cast<hipStream_t>(stream)));
+}
+
+kvarn_status kvarn_chunk_attention(const kvarn_params* params, const void* q, int32_t total_q,
+                                   const int32_t* cu_q, int32_t batch, int32_t num_q_heads,
+                                   int32_t num_kv_heads, const void* k_pool, const void* v_pool,
+                                   int64_t pool_num_pages, const int32_t* block_table,
+                                   int32_t block_table_stride, const int32_t* seq_lens,
+                                   int32_t max_seq_len, const void* k_tail, const void* v_tail,
+                                   float softmax_scale, void* workspace, size_t workspace_bytes,
+                                   void* out, void* stream) {
+  const kvarn_status st = kvarn_params_check(params);
+  if (st != KVARN_OK) return st;
+  if (total_q < 0 || batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_seq_len < 0 ||
+      pool_num_pages < 0 || block_table_stride < 0 || num_q_heads > 65535 || num_kv_heads > 65535)
+    return KVARN_ERR_INVALID_ARG;
+  if (num_q_heads % num_kv_heads != 0) return KVARN_ERR_INVALID_ARG;
+  if (num_q_heads / num_kv_heads > kMaxGroup) return KVARN_ERR_UNSUPPORTED;
+  if (total_q > 65535) return KVARN_ERR_UNSUPPORTED;      // one grid dimension per query row
+  if (!isfinite(softmax_scale)) return KVARN_ERR_INVALID_ARG;
+  if (total_q == 0) return KVARN_OK;
+  if (batch == 0) return KVARN_ERR_INVALID_ARG;            // query rows without a sequence
+  if (!q || !cu_q || !seq_lens || !out || !workspace) return KVARN_ERR_INVALID_ARG;
+  if ((k_tail == nullptr) != (v_tail == nullptr)) return KVARN_ERR_INVALID_ARG;
+  if (max_seq_len >= 128) {
+    if (!k_pool || !v_pool || !block_table) return KVARN_ERR_INVALID_ARG;
+    if (pool_num_pages * int64_t(num_kv_heads) > (int64_t(1) << 32)) return KVARN_ERR_UNSUPPORTED;
+    if (block_table_stride < max_seq_len / 128) return KVARN_ERR_INVALID_ARG;
+    if (!aligned16(k_pool) || !aligned16(v_pool)) return KVARN_ERR_INVALID_ARG;
+  }
+  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return KVARN_ERR_INVALID_ARG;
+  if (k_tail && (!aligned16(k_tail) || !aligned16(v_tail))) return KVARN_ERR_INVALID_ARG;
+  if (workspace_bytes < kvarn::decode_workspace_bytes(total_q, num_q_heads, num_kv_heads, max_seq_len))
+    return KVARN_ERR_WORKSPACE;
+  return launch_status(kvarn::launch_decode(
+      q, total_q, num_q_heads, num_kv_heads, k_pool, v_pool, pool_num_pages, block_table,
+      block_table_stride, seq_lens, max_seq_len, cu_q, batch, k_tail, v_tail, softmax_scale,
+      workspace, out, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

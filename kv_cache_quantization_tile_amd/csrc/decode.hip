@@ -216,24 +216,74 @@ __device__ __forceinline__ uint32_t swap8_into(uint32_t old, uint32_t src) {
 constexpr int kHiBanks = 0x3;   // lanes 0..7 of a row: high-part columns
 constexpr int kLoBanks = 0xC;   // lanes 8..15: low-part columns
 
-// Exact attention over the float16 tail (tokens past the last full page) of (sequence b,
-// KV head g), raw space, written as split n_splits of each query head's partials. Run by the
+// What one output row attends to. Decode (cu_q == nullptr): row b is sequence b, attending
+// to its L = seq_lens[b] tokens: the full pages, then the L mod 128 staged tokens. Several
+// queries per sequence (cu_q != nullptr): rows cu_q[b] .. cu_q[b+1]-1 are the last
+// n = cu_q[b+1] - cu_q[b] positions of sequence b (its cache of C = seq_lens[b] tokens ends with
+// them), row cu_q[b] + i at position C - n + i attending causally to L = C - n + i + 1 tokens.
+// A partial last tile of L that is a completed page (it lies below 128 floor(C / 128)) is one
+// more page slot whose tokens from L mod 128 on are masked; otherwise it is the staging tile.
+struct RowGeom {
+  int b;          // sequence (block table and staging row)
+  int n_slots;    // page slots to stream (full pages, plus one masked page)
+  int mask_lim;   // tokens of the last slot that count (128: all)
+  int tail_len;   // staged tokens attended (0: none)
+};
+
+__device__ __forceinline__ RowGeom row_geometry(int row, const int32_t* __restrict__ seq_lens,
+                                                int32_t max_seq_len,
+                                                const int32_t* __restrict__ cu_q, int32_t batch) {
+  RowGeom r;
+  int32_t C, L;
+  if (cu_q == nullptr) {
+    r.b = row;
+    C = seq_lens[row];
+    C = C < 0 ? 0 : (C > max_seq_len ? max_seq_len : C);
+    L = C;
+  } else {
+    int lo = 0, hi = batch;               // the last b with cu_q[b] <= row
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (cu_q[mid] <= row) lo = mid; else hi = mid;
+    }
+    r.b = lo;
+    C = seq_lens[lo];
+    C = C < 0 ? 0 : (C > max_seq_len ? max_seq_len : C);
+    const int32_t n = cu_q[lo + 1] - cu_q[lo];
+    L = C - n + (row - cu_q[lo]) + 1;
+    L = L < 0 ? 0 : (L > C ? C : L);
+  }
+  const int n_full = L / kTile, rem = L % kTile;
+  if (rem != 0 && (n_full + 1) * kTile <= C) {
+    r.n_slots = n_full + 1;
+    r.mask_lim = rem;
+    r.tail_len = 0;
+  } else {
+    r.n_slots = n_full;
+    r.mask_lim = kTile;
+    r.tail_len = rem;
+  }
+  return r;
+}
+
+// Exact attention over the T staged float16 tokens of (sequence sb, KV head g), raw space,
+// for output row `row`, written as split n_splits of each query head's partials. Run by the
 // extra split of decode_pages_kernel; wave w handles heads 2w, 2w+1 of the group; p_sm is
 // 8 x 128 floats of LDS.
 __device__ void tail_partial(const __half* __restrict__ q, int32_t num_q_heads,
                              int32_t num_kv_heads, const __half* __restrict__ k_tail,
-                             const __half* __restrict__ v_tail, int b, int g, int L, float qscale,
-                             int32_t n_splits, float* __restrict__ ws, float (*p_sm)[kTile]) {
+                             const __half* __restrict__ v_tail, int row, int sb, int g, int T,
+                             float qscale, int32_t n_splits, float* __restrict__ ws,
+                             float (*p_sm)[kTile]) {
   const int G = num_q_heads / num_kv_heads;
-  const int T = L % kTile;
   if (T == 0) return;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const __half* kt = k_tail + (int64_t(b) * num_kv_heads + g) * kTile * kDim;
-  const __half* vt = v_tail + (int64_t(b) * num_kv_heads + g) * kTile * kDim;
+  const __half* kt = k_tail + (int64_t(sb) * num_kv_heads + g) * kTile * kDim;
+  const __half* vt = v_tail + (int64_t(sb) * num_kv_heads + g) * kTile * kDim;
   for (int hh = 2 * w; hh < 2 * w + 2; ++hh) {
     if (hh >= G) break;
     const int hq = g * G + hh;
-    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(q + (int64_t(b) * num_q_heads + hq) * kDim);
+    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(q + (int64_t(row) * num_q_heads + hq) * kDim);
     float sc[2];
 #pragma unroll
     for (int half_ = 0; half_ < 2; ++half_) {
@@ -275,7 +325,7 @@ __device__ void tail_partial(const __half* __restrict__ q, int32_t num_q_heads,
       o0 = fmaf(p, h2f(uint16_t(vv & 0xFFFF)), o0);
       o1 = fmaf(p, h2f(uint16_t(vv >> 16)), o1);
     }
-    float* part = ws + ((int64_t(b) * num_q_heads + hq) * (n_splits + 1) + n_splits) * kPartStride;
+    float* part = ws + ((int64_t(row) * num_q_heads + hq) * (n_splits + 1) + n_splits) * kPartStride;
     *reinterpret_cast<float2*>(part + 4 + 2 * l) = make_float2(o0, o1);
     if (l == 0) {
       part[0] = mx;
@@ -285,28 +335,29 @@ __device__ void tail_partial(const __half* __restrict__ q, int32_t num_q_heads,
   }
 }
 
-// One workgroup: (split, KV head g, sequence b). Wave w handles page slots
+// One workgroup: (split, KV head g, output row). Wave w handles page slots
 // split * 4 * tpw + w + 4 k, k < tpw. Writes one partial (m, l, acc) per query head. With
-// tail buffers the grid has one more split, n_splits, which computes the tail partial.
+// tail buffers the grid has one more split, n_splits, which computes the tail partial. The
+// row's sequence, page slots and tail follow row_geometry.
 __global__ void __launch_bounds__(kThreads)
 decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t num_kv_heads,
                     const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
                     int64_t pool_num_pages, const int32_t* __restrict__ block_table,
                     int32_t bt_stride, const int32_t* __restrict__ seq_lens, int32_t max_seq_len,
-                    float qscale, int32_t tpw, int32_t n_splits, int32_t split_base,
-                    const __half* __restrict__ k_tail, const __half* __restrict__ v_tail,
-                    float tail_qscale, float* __restrict__ ws) {
+                    const int32_t* __restrict__ cu_q, int32_t batch, float qscale, int32_t tpw,
+                    int32_t n_splits, int32_t split_base, const __half* __restrict__ k_tail,
+                    const __half* __restrict__ v_tail, float tail_qscale,
+                    float* __restrict__ ws) {
   __shared__ DecodeSmem sm;
-  const int split = split_base + blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int split = split_base + blockIdx.x, g = blockIdx.y, b = blockIdx.z;   // b: output row
   const int G = num_q_heads / num_kv_heads;
-  int32_t L = seq_lens[b];
-  L = L < 0 ? 0 : (L > max_seq_len ? max_seq_len : L);
+  const RowGeom rg = row_geometry(b, seq_lens, max_seq_len, cu_q, batch);
   if (split == n_splits) {   // the extra split (launched only with tail buffers): the tail
-    tail_partial(q, num_q_heads, num_kv_heads, k_tail, v_tail, b, g, L, tail_qscale, n_splits,
-                 ws, reinterpret_cast<float (*)[kTile]>(&sm.acc[0][0][0]));
+    tail_partial(q, num_q_heads, num_kv_heads, k_tail, v_tail, b, rg.b, g, rg.tail_len,
+                 tail_qscale, n_splits, ws, reinterpret_cast<float (*)[kTile]>(&sm.acc[0][0][0]));
     return;
   }
-  const int n_full = L / kTile;
+  const int n_full = rg.n_slots;      // page slots of this row (the last may be masked)
   const int slot0 = split * 4 * tpw;
   if (slot0 >= n_full) return;
 
@@ -383,7 +434,7 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
   const float fk = (l & 1) ? 16.f : 256.f;
   const float fv = (l & 1) ? 16.f : 4.f;
 
-  const int32_t* bt_row = block_table + int64_t(b) * bt_stride;
+  const int32_t* bt_row = block_table + int64_t(rg.b) * bt_stride;
   auto page_of = [&](int slot) -> int64_t {
     if (slot >= n_full) return -1;
     const int32_t page = __builtin_amdgcn_readfirstlane(bt_row[slot]);
@@ -418,7 +469,7 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
   // this page has consumed it, so the loads overlap the rest of the page's work. A page
   // that is not `valid` (its id is out of range) runs the same code and adds nothing: its
   // maximum stays -inf and its weights exp2(s - inf) are 0.
-  auto process = [&](PageRegs& t, int64_t next, bool valid) {
+  auto process = [&](PageRegs& t, int64_t next, bool valid, int lim) {
     // ---- page factors into the wave's LDS slot ------------------------------------------
     {
       const float rk0 = lo_h(t.km[0]), rk1 = hi_h(t.km[0]);
@@ -504,6 +555,13 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
       }
     }
     load_kcodes(t, krec_of(next), lo);
+    if (lim < kTile) {   // a causally cut page: tokens from lim on do not count
+#pragma unroll
+      for (int tb = 0; tb < 8; ++tb)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          if (16 * tb + 4 * gq + side + j >= lim) sc[tb][j] = -INFINITY;
+    }
 
     // ---- online softmax ------------------------------------------------------------------
     float mt = fmaxf(sc[0][0], sc[0][1]);
@@ -588,7 +646,7 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
   const int n_here = wslot < n_full ? min(tpw, (n_full - wslot + 3) >> 2) : 0;
   for (int k = 0; k < n_here; ++k) {
     const int64_t next = k + 1 < n_here ? page_of(wslot + 4 * (k + 1)) : -1;
-    process(t, next, cur >= 0);
+    process(t, next, cur >= 0, wslot + 4 * k == n_full - 1 ? rg.mask_lim : kTile);
     cur = next;
   }
 
@@ -648,18 +706,17 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
 // LDS, then every thread streams its channel of all partials (independent loads).
 __global__ void __launch_bounds__(128)
 decode_merge_kernel(int32_t num_q_heads, const int32_t* __restrict__ seq_lens, int32_t max_seq_len,
-                    int32_t tiles_per_split, int32_t n_splits, int32_t has_tail,
-                    const float* __restrict__ ws, __half* __restrict__ out) {
+                    const int32_t* __restrict__ cu_q, int32_t batch, int32_t tiles_per_split,
+                    int32_t n_splits, int32_t has_tail, const float* __restrict__ ws,
+                    __half* __restrict__ out) {
   __shared__ float wsh[kMaxMergeSplits + 1];
   __shared__ float red[2][2];
   __shared__ float xs[kDim];
-  const int hq = blockIdx.x, b = blockIdx.y;
+  const int hq = blockIdx.x, b = blockIdx.y;   // b: output row
   const int c = threadIdx.x, lane = c & 63, wv = c >> 6;
-  int32_t L = seq_lens[b];
-  L = L < 0 ? 0 : (L > max_seq_len ? max_seq_len : L);
-  const int n_full = L / kTile;
-  const int used = (n_full + tiles_per_split - 1) / tiles_per_split;
-  const bool tail = has_tail && (L % kTile) != 0;
+  const RowGeom rg = row_geometry(b, seq_lens, max_seq_len, cu_q, batch);
+  const int used = (rg.n_slots + tiles_per_split - 1) / tiles_per_split;
+  const bool tail = has_tail && rg.tail_len != 0;
   const float* base = ws + (int64_t(b) * num_q_heads + hq) * (n_splits + 1) * kPartStride;
   // 1. global max over the used splits (and the tail)
   float M = -INFINITY;
@@ -754,13 +811,14 @@ size_t decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv
   return size_t(batch) * num_q_heads * (ns + 1) * kPartStride * sizeof(float);
 }
 
-hipError_t launch_decode(const void* q, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+hipError_t launch_decode(const void* q, int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
                          const void* k_pool, const void* v_pool, int64_t pool_num_pages,
                          const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
-                         int32_t max_seq_len, const void* k_tail, const void* v_tail,
-                         float softmax_scale, void* workspace, void* out, hipStream_t stream) {
-  const int32_t tpw = decode_tiles_per_wave(batch, num_kv_heads, max_seq_len);
-  const int32_t ns = decode_num_splits(batch, num_kv_heads, max_seq_len);
+                         int32_t max_seq_len, const int32_t* cu_q, int32_t batch,
+                         const void* k_tail, const void* v_tail, float softmax_scale,
+                         void* workspace, void* out, hipStream_t stream) {
+  const int32_t tpw = decode_tiles_per_wave(rows, num_kv_heads, max_seq_len);
+  const int32_t ns = decode_num_splits(rows, num_kv_heads, max_seq_len);
   const float qscale = softmax_scale * kLog2e;
   float* ws = static_cast<float*>(workspace);
   const bool has_tail = k_tail != nullptr && v_tail != nullptr;
@@ -769,17 +827,17 @@ hipError_t launch_decode(const void* q, int32_t batch, int32_t num_q_heads, int3
   if (grid_x > 0) {
     // without pages the only split launched is the tail, which must land on index ns
     const int32_t first = max_seq_len >= kTile ? 0 : ns;
-    hipLaunchKernelGGL(decode_pages_kernel, dim3(grid_x, num_kv_heads, batch), dim3(kThreads), 0,
+    hipLaunchKernelGGL(decode_pages_kernel, dim3(grid_x, num_kv_heads, rows), dim3(kThreads), 0,
                        stream, static_cast<const __half*>(q), num_q_heads, num_kv_heads,
                        static_cast<const uint8_t*>(k_pool), static_cast<const uint8_t*>(v_pool),
-                       pool_num_pages, block_table, bt_stride, seq_lens, max_seq_len,
+                       pool_num_pages, block_table, bt_stride, seq_lens, max_seq_len, cu_q, batch,
                        qscale * kInvSqrt128, tpw, ns, first, static_cast<const __half*>(k_tail),
                        static_cast<const __half*>(v_tail), qscale, ws);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(num_q_heads, batch), dim3(128), 0, stream,
-                     num_q_heads, seq_lens, max_seq_len, 4 * tpw, ns, has_tail ? 1 : 0,
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(num_q_heads, rows), dim3(128), 0, stream,
+                     num_q_heads, seq_lens, max_seq_len, cu_q, batch, 4 * tpw, ns, has_tail ? 1 : 0,
                      static_cast<const float*>(ws), static_cast<__half*>(out));
   return hipGetLastError();
 }

@@ -42,10 +42,13 @@ int32_t decode_num_splits(int32_t batch, int32_t num_kv_heads, int32_t max_seq_l
 size_t decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                               int32_t max_seq_len);
 
-hipError_t launch_decode(const void* q, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+// rows output rows; cu_q == nullptr: row b is sequence b (decode, rows == batch), else the
+// query rows of sequence b are cu_q[b] .. cu_q[b+1]-1 (the last positions of its cache)
+hipError_t launch_decode(const void* q, int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
                          const void* k_pool, const void* v_pool, int64_t pool_num_pages,
                          const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
-                         int32_t max_seq_len, const void* k_tail, const void* v_tail,
-                         float softmax_scale, void* workspace, void* out, hipStream_t stream);
+                         int32_t max_seq_len, const int32_t* cu_q, int32_t batch,
+                         const void* k_tail, const void* v_tail, float softmax_scale,
+                         void* workspace, void* out, hipStream_t stream);
 
 }  // namespace kvarn

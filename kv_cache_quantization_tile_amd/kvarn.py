@@ -62,6 +62,9 @@ def _load():
         "kvarn_decode_num_splits": (i32, [P, i32, i32, i32]),
         "kvarn_decode_attention": (ctypes.c_int, [P, vp, i32, i32, i32, vp, vp, i64, vp, i32, vp,
                                                   i32, vp, vp, ctypes.c_float, vp, sz, vp, vp]),
+        "kvarn_chunk_attention": (ctypes.c_int, [P, vp, i32, vp, i32, i32, i32, vp, vp, i64, vp,
+                                                 i32, vp, i32, vp, vp, ctypes.c_float, vp, sz,
+                                                 vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -75,7 +78,7 @@ EXPORTED = ("kvarn_abi_version", "kvarn_format_version", "kvarn_status_str",
             "kvarn_params_from_dtype", "kvarn_params_check", "kvarn_page_bytes",
             "kvarn_quantize_tiles", "kvarn_quantize_kv_tiles", "kvarn_append_tokens",
             "kvarn_write_tokens", "kvarn_dequantize_tiles", "kvarn_decode_workspace_bytes",
-            "kvarn_decode_num_splits", "kvarn_decode_attention")
+            "kvarn_decode_num_splits", "kvarn_decode_attention", "kvarn_chunk_attention")
 
 
 def _check(status: int, what: str):
@@ -295,6 +298,39 @@ def decode_attention(params: Params, q, k_pool, v_pool, block_table, seq_lens, m
                                       _ptr(k_tail), _ptr(v_tail), float(softmax_scale),
                                       _ptr(workspace), workspace.numel(), _ptr(out),
                                       _stream(stream)), "kvarn_decode_attention")
+    return out
+
+
+def chunk_attention(params: Params, q, cu_q, k_pool, v_pool, block_table, seq_lens,
+                    max_seq_len: int, k_tail=None, v_tail=None, softmax_scale: float | None = None,
+                    workspace=None, out=None, stream=None) -> torch.Tensor:
+    """Causal attention of the last cu_q[b+1] - cu_q[b] positions of every sequence (query rows
+    of q [total_q, Hq, 128] float16) over the quantized cache -> out [total_q, Hq, 128]."""
+    _need(q, "q", torch.float16)
+    _need(cu_q, "cu_q", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32)
+    _need(block_table, "block_table", torch.int32)
+    if q.dim() != 3 or q.shape[2] != 128 or not q.is_contiguous():
+        raise ValueError("q must be contiguous [total_q, Hq, 128]")
+    B = seq_lens.shape[0]
+    if cu_q.shape != (B + 1,):
+        raise ValueError("cu_q must be [batch + 1]")
+    total_q, hq = q.shape[0], q.shape[1]
+    hkv = k_pool.shape[1]
+    if block_table.dim() != 2 or block_table.shape[0] != B or not block_table.is_contiguous():
+        raise ValueError("block_table must be contiguous [B, width]")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(128)
+    if workspace is None:
+        workspace = new_workspace(params, max(total_q, 1), hq, hkv, max_seq_len, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib.kvarn_chunk_attention(ctypes.byref(params), _ptr(q), total_q, _ptr(cu_q), B, hq,
+                                     hkv, _ptr(k_pool), _ptr(v_pool), k_pool.shape[0],
+                                     _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
+                                     max_seq_len, _ptr(k_tail), _ptr(v_tail), float(softmax_scale),
+                                     _ptr(workspace), workspace.numel(), _ptr(out),
+                                     _stream(stream)), "kvarn_chunk_attention")
     return out
 
 

@@ -181,6 +181,34 @@ def test_decode_validation():
     assert _decode(p, wsb=need - 1) == WS
 
 
+def _chunk(p, **kw):
+    a = dict(q=FAKE, tq=16, cu=FAKE, B=2, hq=64, hkv=8, kp=FAKE, vp=FAKE, npages=100, bt=FAKE,
+             bts=200, sl=FAKE, mx=16384, kt=None, vt=None, scale=0.088, ws=FAKE, wsb=1 << 30,
+             out=FAKE)
+    a.update(kw)
+    return K.lib.kvarn_chunk_attention(ctypes.byref(p), a["q"], a["tq"], a["cu"], a["B"], a["hq"],
+                                       a["hkv"], a["kp"], a["vp"], a["npages"], a["bt"], a["bts"],
+                                       a["sl"], a["mx"], a["kt"], a["vt"], a["scale"], a["ws"],
+                                       a["wsb"], a["out"], None)
+
+
+def test_chunk_attention_validation():
+    p = K.params_from_dtype()
+    assert _chunk(p, tq=0) == OK
+    assert _chunk(p, B=0) == INVALID                  # rows without a sequence
+    assert _chunk(p, tq=-1) == INVALID
+    assert _chunk(p, tq=70000) == UNSUP
+    assert _chunk(p, cu=None) == INVALID
+    assert _chunk(p, hq=63) == INVALID
+    assert _chunk(p, hq=128) == UNSUP
+    assert _chunk(p, kt=FAKE) == INVALID
+    assert _chunk(p, bts=10) == INVALID
+    assert _chunk(p, scale=float("inf")) == INVALID
+    assert _chunk(p, q=ctypes.c_void_p(0x10002)) == INVALID
+    need = K.decode_workspace_bytes(p, 16, 64, 8, 16384)
+    assert _chunk(p, wsb=need - 1) == WS
+
+
 def test_decode_workspace_formula():
     p = K.params_from_dtype()
     for B, hq, hkv, mx in ((1, 64, 8, 16384), (32, 64, 8, 32768), (1, 64, 8, 131072), (64, 64, 8, 16384), (3, 8, 8, 100)):

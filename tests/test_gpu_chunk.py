@@ -1,0 +1,138 @@
+"""GPU tests of the multi-query read path (kvarn_chunk_attention): after a chunk write, every
+query row of the chunk against the oracle's causal attention over exactly the positions it may
+see (dequantized pages, a causally cut page read up to its limit, raw staging), and one query
+per sequence equal to kvarn_decode_attention bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import kvarn_oracle as O
+from tests import kvarn_testlib as T
+from tests.test_gpu_parity import _build_cache
+from tests.test_gpu_write import _chunk, _extend_block_table
+
+pytestmark = pytest.mark.gpu
+
+SCALE = 1.0 / np.sqrt(128.0)
+
+
+@pytest.fixture(scope="module")
+def K():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need an MI355X; torch.cuda.is_available() is False")
+    from kv_cache_quantization_tile_amd import kvarn
+    return kvarn
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def _written_cache(K, params, lens, lens_new, hkv, seed):
+    spare = max(lens_new) // 128 + 2
+    kp, vp, bt, kt, vt, sl, free = _build_cache(
+        K, params, lens, hkv, seed=seed, spare=spare,
+        width=max((L + n) // 128 for L, n in zip(lens, lens_new)) + 2)
+    bt = _extend_block_table(bt, lens, lens_new, free)
+    kn, vn, cu = _chunk(lens_new, hkv, seed=seed + 1)
+    K.write_tokens(params, kn, vn, cu, sl, kt, vt, bt, kp, vp)
+    sl2 = sl + torch.tensor(lens_new, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    return kp, vp, bt, kt, vt, sl2
+
+
+def _reference_rows(q, cu_q, kp, vp, bt, kt, vt, sl, G, rows_to_check):
+    """Oracle attention of the given query rows over their causal prefix."""
+    qh = q.cpu().numpy()
+    cu = cu_q.cpu().numpy()
+    bt_h, sl_h = bt.cpu().numpy(), sl.cpu().numpy()
+    kt_h, vt_h = kt.cpu().numpy(), vt.cpu().numpy()
+    hkv = kp.shape[1]
+    deq = {}
+    out = {}
+    for r in rows_to_check:
+        b = int(np.searchsorted(cu, r, side="right") - 1)
+        C, n = int(sl_h[b]), int(cu[b + 1] - cu[b])
+        L = C - n + (r - int(cu[b])) + 1
+        for g in range(hkv):
+            if (b, g) not in deq:
+                pages = [int(p) for p in bt_h[b, :C // 128]]
+                ks = [O.dequantize_k_record(x) for x in T.records_of(kp, pages, g)] if pages else []
+                vs = [O.dequantize_v_record(x) for x in T.records_of(vp, pages, g)] if pages else []
+                deq[(b, g)] = (ks, vs)
+            ks, vs = deq[(b, g)]
+            nf, rem = L // 128, L % 128
+            k_parts, v_parts = ks[:nf], vs[:nf]
+            if rem:
+                if nf < len(ks):      # a completed page, cut by the causal limit
+                    k_parts = k_parts + [ks[nf][:rem]]
+                    v_parts = v_parts + [vs[nf][:rem]]
+                else:                 # the staging tile
+                    k_parts = k_parts + [kt_h[b, g, :rem].astype(np.float64)]
+                    v_parts = v_parts + [vt_h[b, g, :rem].astype(np.float64)]
+            kk = np.concatenate(k_parts, 0)
+            vv = np.concatenate(v_parts, 0)
+            for hh in range(G):
+                hq = g * G + hh
+                out[(r, hq)] = O.attention(qh[r, hq].astype(np.float64), kk, vv, SCALE)
+    return out
+
+
+@pytest.mark.parametrize("case", [0, 1])
+def test_chunk_rows_against_oracle(K, case):
+    lens, lens_new = [([0, 5, 200, 356], [300, 130, 56, 400]), ([127, 640], [1, 260])][case]
+    hkv, G = 2, 8
+    params = K.params_from_dtype("kvarn_k4v2_g128", 8)
+    kp, vp, bt, kt, vt, sl = _written_cache(K, params, lens, lens_new, hkv, seed=140 + case)
+    total_q = sum(lens_new)
+    cu_q = torch.tensor([0] + list(np.cumsum(lens_new)), dtype=torch.int32, device="cuda")
+    q = torch.randn((total_q, hkv * G, 128), generator=torch.Generator().manual_seed(150 + case))
+    q = q.to(torch.float16).cuda()
+    mx = int(sl.max().item())
+    say(f"chunk attention: lens {lens} + chunks {lens_new}, {total_q} query rows")
+    out = K.chunk_attention(params, q, cu_q, kp, vp, bt, sl, mx, kt, vt)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(160 + case)
+    cu = cu_q.cpu().numpy()
+    rows = set(rng.choice(total_q, size=min(48, total_q), replace=False).tolist())
+    for b in range(len(lens)):                       # first and last rows of every chunk
+        rows |= {int(cu[b]), int(cu[b + 1]) - 1}
+    ref = _reference_rows(q, cu_q, kp, vp, bt, kt, vt, sl, G, sorted(rows))
+    o = out.cpu().numpy().astype(np.float64)
+    worst = 0.0
+    for (r, hq), want in ref.items():
+        worst = max(worst, T.assert_rows_close(o[r, hq], want, f"row {r} head {hq}"))
+    say(f"  {len(rows)} rows x {hkv * G} heads, max rel err {worst:.2e}")
+
+
+def test_one_query_per_sequence_equals_decode(K):
+    lens, lens_new = [40, 300, 1000, 128], [88, 212, 1, 200]
+    hkv, G = 2, 8
+    params = K.params_from_dtype("kvarn_k4v2_g128", 8)
+    kp, vp, bt, kt, vt, sl = _written_cache(K, params, lens, lens_new, hkv, seed=170)
+    q = torch.randn((len(lens), hkv * G, 128), generator=torch.Generator().manual_seed(171))
+    q = q.to(torch.float16).cuda()
+    mx = int(sl.max().item())
+    cu_q = torch.arange(len(lens) + 1, dtype=torch.int32, device="cuda")
+    a = K.chunk_attention(params, q, cu_q, kp, vp, bt, sl, mx, kt, vt)
+    d = K.decode_attention(params, q, kp, vp, bt, sl, mx, kt, vt)
+    torch.cuda.synchronize()
+    assert torch.equal(a, d)
+    say("one query per sequence: chunk attention == decode attention, bit for bit")
+
+
+def test_queries_below_position_zero_get_zeros(K):
+    """More query rows than cached tokens: rows at negative positions output zeros."""
+    lens, lens_new = [0], [3]
+    hkv, G = 1, 8
+    params = K.params_from_dtype("kvarn_k4v2_g128", 8)
+    kp, vp, bt, kt, vt, sl = _written_cache(K, params, lens, lens_new, hkv, seed=180)
+    q = torch.randn((5, G, 128), generator=torch.Generator().manual_seed(181)).to(torch.float16).cuda()
+    cu_q = torch.tensor([0, 5], dtype=torch.int32, device="cuda")
+    out = K.chunk_attention(params, q, cu_q, kp, vp, bt, sl, 3, kt, vt)
+    torch.cuda.synchronize()
+    assert torch.all(out[:2] == 0)
+    ref = _reference_rows(q, cu_q, kp, vp, bt, kt, vt, sl, G, [2, 3, 4])
+    o = out.cpu().numpy().astype(np.float64)
+    for (r, hq), want in ref.items():
+        T.assert_rows_close(o[r, hq], want, f"row {r} head {hq}")

@@ -15,6 +15,11 @@ Prints one JSON line. Numbers:
   decode_kv_gbps, quantize_tiles_per_s: the two halves, from HIP events around each launch.
   roofline: the dominant kernel (by time) against its bound; roofline_other: the other one.
   cpu_baseline: the float64 CPU oracle on a bounded sample of the same step.
+
+--workload chunked_prefill measures the chunk write and multi-query read path instead: 8
+sequences holding 16384 tokens each; one step writes a 128-token chunk per sequence (one tile
+completed and quantized per sequence and head) and runs causal attention for its 1024 query
+rows over the quantized cache.
 """
 from __future__ import annotations
 
@@ -117,9 +122,11 @@ def main():
                     help="distinct layer copies cycled across steps (defeats the 256 MB MALL)")
     ap.add_argument("--sinkhorn-iters", type=int, default=8)
     ap.add_argument("--context", type=int, default=16384)
-    ap.add_argument("--workload", choices=["one_layer_16k", "prefill_burst"], default="one_layer_16k",
+    ap.add_argument("--workload", choices=["one_layer_16k", "prefill_burst", "chunked_prefill"],
+                    default="one_layer_16k",
                     help="one_layer_16k: batch 1 one decoder layer (default, the headline line); "
-                         "prefill_burst: 64 sequences x 16384 tokens (131072 tiles) + one batched decode")
+                         "prefill_burst: 64 sequences x 16384 tokens (131072 tiles) + one batched "
+                         "decode; chunked_prefill: 128-token chunks written and attended")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
@@ -140,6 +147,8 @@ def main():
     dev = torch.device("cuda:0")
     n_iters = args.sinkhorn_iters
     params = K.params_from_dtype("kvarn_k4v2_g128", n_iters)
+    if args.workload == "chunked_prefill":
+        return chunked_prefill(args, K, synth, params, dev)
     L = max(1, args.layers) if args.workload == "one_layer_16k" else 1
     print(f"[bench] generating {L} copies of {args.workload} (context {args.context})",
           file=sys.stderr, flush=True)
@@ -255,6 +264,94 @@ def main():
         res["cpu_baseline"] = {"value": round(step_bytes / t_step / 1e9, 5), "unit": "GB/s",
                                "cores": cores, "kind": "oracle", "sample": sample,
                                "seconds_per_step": round(t_step, 3)}
+    print(json.dumps(res), flush=True)
+
+
+def chunked_prefill(args, K, synth, params, dev):
+    """Chunk write (kvarn_write_tokens) + multi-query read (kvarn_chunk_attention), steady state:
+    every step rewrites the same 128 positions after the 16384 cached tokens of each of 8
+    sequences, so the cache does not grow between steps."""
+    import torch
+    B, ctx, n = 8, args.context, 128
+    w = synth.prefill_burst(device=dev, seed=11, batch=B, context=ctx + n, n_iters=params.sinkhorn_iters)
+    hq, hkv = w.hq, w.hkv
+    kp = K.new_pool(w.num_pages, hkv, K.KIND_K)
+    vp = K.new_pool(w.num_pages, hkv, K.KIND_V)
+    # the prompt: every tile but the last of each sequence; the last is the chunk
+    keep = torch.tensor([i for i in range(w.tile_src_token.numel()) if (i + 1) % ((ctx + n) // 128) != 0],
+                        dtype=torch.long, device=dev)
+    K.quantize_kv_tiles(params, w.k_src, w.v_src, w.tile_src_token[keep].contiguous(),
+                        w.tile_dst_page[keep].contiguous(), kp, vp)
+    rows = torch.cat([torch.arange(w.seq_start[b] + ctx, w.seq_start[b] + ctx + n, device=dev)
+                      for b in range(B)])
+    kn, vn = w.k_src[rows].contiguous(), w.v_src[rows].contiguous()
+    cu = torch.arange(0, (B + 1) * n, n, dtype=torch.int32, device=dev)
+    sl0 = torch.full((B,), ctx, dtype=torch.int32, device=dev)
+    sl1 = sl0 + n
+    kt = torch.zeros((B, hkv, 128, 128), dtype=torch.float16, device=dev)
+    vt = torch.zeros_like(kt)
+    q = torch.randn((B * n, hq, 128), generator=torch.Generator(device=dev).manual_seed(12),
+                    device=dev).to(torch.float16)
+    ws = K.new_workspace(params, B * n, hq, hkv, ctx + n)
+    out = torch.empty_like(q)
+    step = lambda: (K.write_tokens(params, kn, vn, cu, sl0, kt, vt, w.block_table, kp, vp, n),
+                    K.chunk_attention(params, q, cu, kp, vp, w.block_table, sl1, ctx + n, kt, vt,
+                                      workspace=ws, out=out))
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    marks = [(ev(), ev(), ev()) for _ in range(args.steps)]
+    start, stop = ev(), ev()
+    t_wall = time.perf_counter()
+    start.record()
+    for s in range(args.steps):
+        e0, e1, e2 = marks[s]
+        e0.record()
+        K.write_tokens(params, kn, vn, cu, sl0, kt, vt, w.block_table, kp, vp, n)
+        e1.record()
+        K.chunk_attention(params, q, cu, kp, vp, w.block_table, sl1, ctx + n, kt, vt,
+                          workspace=ws, out=out)
+        e2.record()
+    stop.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_step = start.elapsed_time(stop) / args.steps
+    w_ms = sum(m[0].elapsed_time(m[1]) for m in marks) / args.steps
+    a_ms = sum(m[1].elapsed_time(m[2]) for m in marks) / args.steps
+    pages = (ctx + n) // 128
+    write_bytes = B * hkv * (2 * Q_READ + K_REC + V_REC)                 # chunk in, records out
+    unique_kv = B * hkv * pages * (K_REC + V_REC)                      # each page once
+    per_row_kv = sum(B * hkv * ((ctx + i + 1) // 128) * (K_REC + V_REC) for i in range(n))
+    qo = 2 * B * n * hq * 128 * 2
+    value = (write_bytes + unique_kv + qo) / (ms_step * 1e-3) / 1e9
+    res = {
+        "metric": "decode-attn KV GB/s (% HBM roofline) + tiles quantized/s, k4v2_g128",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16 in/out, f32 compute",
+        "data": "synthetic",
+        "config": {"workload": f"chunked_prefill: {B} sequences x {ctx} cached tokens, "
+                               f"{n}-token chunk written and attended per step",
+                   "batch": B, "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": 128,
+                   "context": ctx, "chunk": n, "kv_cache_dtype": "kvarn_k4v2_g128",
+                   "sinkhorn_iters": params.sinkhorn_iters, "parallelism": "single GPU"},
+        "value_definition": "unique algorithmic bytes of one step (chunk in + records out, every "
+                            "page read once, q + out) / step time",
+        "chunk_tokens_per_s": round(B * n / (ms_step * 1e-3), 1),
+        "write_ms": round(w_ms, 5), "attention_ms": round(a_ms, 5),
+        "roofline": {"kernel": "decode_pages_kernel (one row per query position)", "bound": "hbm",
+                     "achieved": round(per_row_kv / (a_ms * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(per_row_kv / (a_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "traffic": None,
+                     "per_launch": f"{B * n} query rows x their causal prefix of pages x "
+                                   f"{K_REC + V_REC} B (re-reads of shared pages largely served "
+                                   "by L2 / Infinity Cache)",
+                     "launch_ms": round(a_ms, 5)},
+        "wall_s_timed": round(t_wall, 4),
+        "source_hash": source_hash(),
+    }
     print(json.dumps(res), flush=True)
 
 

@@ -149,7 +149,7 @@ def rtn_asym(y: np.ndarray, bits: int, axis: int):
 
 
 def quantize_tiles(x16: np.ndarray, kind: int, n_iters: int = 8, lossless: bool = False,
-                   rotate_channels: bool = True):
+                   rotate_channels: bool = True, k_bits: int = 4):
     """Quantize tiles end to end (stages 1-4 of [README] "How KVarN works").
 
     x16: [..., 128 channels, 128 tokens] float16 (stage 1: the raw tile, channels x tokens).
@@ -163,6 +163,7 @@ def quantize_tiles(x16: np.ndarray, kind: int, n_iters: int = 8, lossless: bool 
 
     lossless=True stops after stage 3 and returns no codes (used to pin the bookkeeping).
     rotate_channels=False skips stage 2 (Xr = X): an ablation of the method, not the method.
+    k_bits: key code width, 4 (kvarn_k4v2_g128) or 2 (kvarn_k2v2_g128); values are 2-bit.
     """
     x = np.asarray(x16, dtype=np.float16).astype(np.float64)
     if x.shape[-2:] != (HEAD_DIM, TILE_TOKENS):
@@ -176,7 +177,7 @@ def quantize_tiles(x16: np.ndarray, kind: int, n_iters: int = 8, lossless: bool 
     if lossless:
         return out
     if kind == KIND_K:
-        codes, scale16, zero16, u = rtn_asym(y, K_BITS, axis=-1)
+        codes, scale16, zero16, u = rtn_asym(y, k_bits, axis=-1)
     elif kind == KIND_V:
         codes, scale16, zero16, u = rtn_asym(y, V_BITS, axis=-2)
     else:
@@ -219,9 +220,20 @@ def dequantize_tiles(codes, r16, s16, scale16, zero16, kind: int,
 #   Then four float16[128] vectors: r (per channel), s (per token), scale, zero
 #     (per channel for K, per token for V).
 
+#   2-bit K record (preset kvarn_k2v2_g128), 5120 bytes: 4096 B of 2-bit codes, token-major:
+#     token t owns bytes [32 t, 32 t + 32) as 8 words; word 2g + d (g in 0..3, d in 0..1)
+#     holds crumb p (bits 2p..2p+1) = channel k2_crumb_channel(g, d, p); then the metadata.
+
 K_RECORD_BYTES = 9216
+K2_RECORD_BYTES = 5120
 V_RECORD_BYTES = 5120
 K_NIBBLE_CHANNEL = (0, 2, 4, 6, 1, 3, 5, 7)
+
+
+def k2_crumb_channel(g: int, d: int, p: int) -> int:
+    """Channel held by crumb p of word 2g + d of a token in a 2-bit K record."""
+    hs, v, e = (p % 8) // 4, p % 4, p // 8
+    return 32 * (2 * d + hs) + 8 * g + 2 * v + e
 
 
 def v_crumb_token(g: int, d: int, p: int) -> int:
@@ -248,6 +260,20 @@ def pack_k_record(codes, r16, s16, scale16, zero16) -> bytes:
             for p in range(8):
                 w |= int(codes[8 * j + K_NIBBLE_CHANNEL[p], t]) << (4 * p)
             words[t, j] = w
+    return words.astype("<u4").tobytes() + _meta_bytes(r16, s16, scale16, zero16)
+
+
+def pack_k2_record(codes, r16, s16, scale16, zero16) -> bytes:
+    codes = np.asarray(codes)
+    assert codes.shape == (128, 128) and codes.max(initial=0) <= 3
+    words = np.zeros((128, 8), dtype=np.uint32)
+    for t in range(128):
+        for g in range(4):
+            for d in range(2):
+                w = 0
+                for p in range(16):
+                    w |= int(codes[k2_crumb_channel(g, d, p), t]) << (2 * p)
+                words[t, 2 * g + d] = w
     return words.astype("<u4").tobytes() + _meta_bytes(r16, s16, scale16, zero16)
 
 
@@ -283,6 +309,33 @@ def unpack_k_record(rec) -> dict:
     return dict(codes=codes, r=r, s=s, scale=sc, zero=zr)
 
 
+def unpack_k2_record(rec) -> dict:
+    buf = np.frombuffer(bytes(rec), dtype=np.uint8)
+    assert buf.size == K2_RECORD_BYTES
+    words = buf[:4096].view("<u4").reshape(128, 4, 2)                  # [t, g, d]
+    codes = np.zeros((128, 128), dtype=np.uint8)
+    for g in range(4):
+        for d in range(2):
+            for p in range(16):
+                codes[k2_crumb_channel(g, d, p), :] = (words[:, g, d] >> np.uint32(2 * p)) & np.uint32(3)
+    r, s, sc, zr = _unpack_meta(buf, 4096)
+    return dict(codes=codes, r=r, s=s, scale=sc, zero=zr)
+
+
+def unpack_record(rec, kind: int, k_bits: int = 4) -> dict:
+    """The record of `kind` for the preset with k_bits-bit keys (4 or 2)."""
+    if kind == KIND_V:
+        return unpack_v_record(rec)
+    return unpack_k_record(rec) if k_bits == 4 else unpack_k2_record(rec)
+
+
+def pack_record(kind: int, codes, r16, s16, scale16, zero16, k_bits: int = 4) -> bytes:
+    if kind == KIND_V:
+        return pack_v_record(codes, r16, s16, scale16, zero16)
+    pack = pack_k_record if k_bits == 4 else pack_k2_record
+    return pack(codes, r16, s16, scale16, zero16)
+
+
 def unpack_v_record(rec) -> dict:
     buf = np.frombuffer(bytes(rec), dtype=np.uint8)
     assert buf.size == V_RECORD_BYTES
@@ -311,9 +364,9 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, softmax_scale: float)
     return (p / p.sum()) @ np.asarray(v, np.float64)
 
 
-def dequantize_k_record(rec) -> np.ndarray:
+def dequantize_k_record(rec, k_bits: int = 4) -> np.ndarray:
     """Unpack one K page record and return the dequantized keys [128 tokens, 128 channels]."""
-    d = unpack_k_record(rec)
+    d = unpack_k_record(rec) if k_bits == 4 else unpack_k2_record(rec)
     return dequantize_tiles(d["codes"], d["r"], d["s"], d["scale"], d["zero"], KIND_K).T
 
 
@@ -323,7 +376,7 @@ def dequantize_v_record(rec) -> np.ndarray:
 
 
 def decode_attention_row(q_row, k_pages, v_pages, k_tail=None, v_tail=None,
-                         softmax_scale: float = 1.0 / np.sqrt(HEAD_DIM)) -> np.ndarray:
+                         softmax_scale: float = 1.0 / np.sqrt(HEAD_DIM), k_bits: int = 4) -> np.ndarray:
     """Decode attention of one query row over one KV head's cache.
 
     k_pages / v_pages: lists of page records (bytes) of that KV head, in block-table order
@@ -332,7 +385,7 @@ def decode_attention_row(q_row, k_pages, v_pages, k_tail=None, v_tail=None,
     k_tail / v_tail: [n_tail, 128] float16 tokens past the last full page (raw, exact).
     Returns float64 [128].
     """
-    ks = [dequantize_k_record(p) for p in k_pages]
+    ks = [dequantize_k_record(p, k_bits) for p in k_pages]
     vs = [dequantize_v_record(p) for p in v_pages]
     if k_tail is not None and len(k_tail):
         ks.append(np.asarray(k_tail, np.float16).astype(np.float64))

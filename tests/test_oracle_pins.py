@@ -263,8 +263,39 @@ def test_v_format_golden_patterns():
     assert rec[4096 + 768:] == bytes.fromhex(g["metadata"]["zero_bytes"]) * 128
 
 
+def test_k2_format_byte_patterns():
+    """2-bit key records: every bit of the crumb -> channel map against hand-derived words."""
+    with open(os.path.join(GOLD, "format_k2_patterns.json")) as f:
+        g = json.load(f)
+    c = np.arange(128)[:, None] * np.ones((1, 128), dtype=np.int64)
+    t = np.ones((128, 1), dtype=np.int64) * np.arange(128)[None, :]
+
+    def words(codes):
+        rec = O.pack_k2_record(codes.astype(np.uint8), *_meta())
+        assert len(rec) == O.K2_RECORD_BYTES
+        return np.frombuffer(rec[:4096], dtype="<u4").reshape(128, 4, 2)     # [t, g, d]
+
+    assert np.all(words(c % 4) == int(g["k2_codes_c_mod_4"]["word"], 16))
+    assert np.all(words((c // 4) % 2) == int(g["k2_codes_c_bit2"]["word"], 16))
+    w = words((c // 8) % 4)
+    for gg in range(4):
+        assert np.all(w[:, gg, :] == int(g["k2_codes_c_div_8_mod_4"]["word_g"][gg], 16))
+    w = words(c // 32)
+    assert np.all(w[:, :, 0] == int(g["k2_codes_c_div_32"]["word_d0"], 16))
+    assert np.all(w[:, :, 1] == int(g["k2_codes_c_div_32"]["word_d1"], 16))
+    w = words(t % 4)
+    for tt in range(128):
+        assert np.all(w[tt] == int(g["k2_codes_t_mod_4"]["word_t"][tt % 4], 16))
+
+
+def test_k2_crumb_map_is_a_permutation():
+    chans = sorted(O.k2_crumb_channel(g, d, p) for g in range(4) for d in range(2) for p in range(16))
+    assert chans == list(range(128))
+
+
 def test_pack_unpack_roundtrip():
     for bits, pack, unpack, size in ((4, O.pack_k_record, O.unpack_k_record, 9216),
+                                     (2, O.pack_k2_record, O.unpack_k2_record, 5120),
                                      (2, O.pack_v_record, O.unpack_v_record, 5120)):
         codes = RNG.integers(0, 1 << bits, (128, 128)).astype(np.uint8)
         meta = [RNG.standard_normal(128).astype(np.float16) for _ in range(4)]

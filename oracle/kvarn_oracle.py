@@ -221,8 +221,9 @@ def dequantize_tiles(codes, r16, s16, scale16, zero16, kind: int,
 #     (per channel for K, per token for V).
 
 #   2-bit K record (preset kvarn_k2v2_g128), 5120 bytes: 4096 B of 2-bit codes, token-major:
-#     token t owns bytes [32 t, 32 t + 32) as 8 words; word 2g + d (g in 0..3, d in 0..1)
-#     holds crumb p (bits 2p..2p+1) = channel k2_crumb_channel(g, d, p); then the metadata.
+#     token t owns bytes [32 t, 32 t + 32) as 8 words; word w = 2g + d (g in 0..3, d in 0..1)
+#     holds channels 16 w .. 16 w + 15, crumb p (bits 2p..2p+1) = channel
+#     k2_crumb_channel(g, d, p); then the metadata.
 
 K_RECORD_BYTES = 9216
 K2_RECORD_BYTES = 5120
@@ -231,9 +232,11 @@ K_NIBBLE_CHANNEL = (0, 2, 4, 6, 1, 3, 5, 7)
 
 
 def k2_crumb_channel(g: int, d: int, p: int) -> int:
-    """Channel held by crumb p of word 2g + d of a token in a 2-bit K record."""
+    """Channel held by crumb p of word 2g + d of a token in a 2-bit K record: word 2g + d holds
+    channels 32 g + 16 d .. + 15 (two groups of 8, hs = (p mod 8) div 4), crumb p of a group
+    holding offset 2 (p mod 4) + p div 8."""
     hs, v, e = (p % 8) // 4, p % 4, p // 8
-    return 32 * (2 * d + hs) + 8 * g + 2 * v + e
+    return 32 * g + 8 * (2 * d + hs) + 2 * v + e
 
 
 def v_crumb_token(g: int, d: int, p: int) -> int:

@@ -278,11 +278,11 @@ def test_k2_format_byte_patterns():
     assert np.all(words(c % 4) == int(g["k2_codes_c_mod_4"]["word"], 16))
     assert np.all(words((c // 4) % 2) == int(g["k2_codes_c_bit2"]["word"], 16))
     w = words((c // 8) % 4)
-    for gg in range(4):
-        assert np.all(w[:, gg, :] == int(g["k2_codes_c_div_8_mod_4"]["word_g"][gg], 16))
+    assert np.all(w[:, :, 0] == int(g["k2_codes_c_div_8_mod_4"]["word_d0"], 16))
+    assert np.all(w[:, :, 1] == int(g["k2_codes_c_div_8_mod_4"]["word_d1"], 16))
     w = words(c // 32)
-    assert np.all(w[:, :, 0] == int(g["k2_codes_c_div_32"]["word_d0"], 16))
-    assert np.all(w[:, :, 1] == int(g["k2_codes_c_div_32"]["word_d1"], 16))
+    for gg in range(4):
+        assert np.all(w[:, gg, :] == int(g["k2_codes_c_div_32"]["word_g"][gg], 16))
     w = words(t % 4)
     for tt in range(128):
         assert np.all(w[tt] == int(g["k2_codes_t_mod_4"]["word_t"][tt % 4], 16))

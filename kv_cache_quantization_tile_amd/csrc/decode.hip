@@ -53,17 +53,6 @@ union H8 {
   uint32_t u[4];
 };
 
-__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
-  return uint32_t(f2h_rn(a)) | (uint32_t(f2h_rn(b)) << 16);
-}
-
-// float16 high part (hi == true) or float16 low part f16(x - f32(f16(x))) of a float, returned
-// as the exact float value of that float16
-__device__ __forceinline__ float split16(float x, bool hi) {
-  const float h = h2f(f2h_rn(x));
-  return hi ? h : h2f(f2h_rn(x - h));
-}
-
 // (t & mask) | magic in one 3-input bit operation (truth table 0xEA: S0 & S1 | S2)
 __device__ __forceinline__ uint32_t and_or(uint32_t t, uint32_t mask, uint32_t magic) {
   return __builtin_amdgcn_bitop3_b32(t, mask, magic, 0xEA);
@@ -89,14 +78,6 @@ __device__ __forceinline__ uint32_t v_pair(uint32_t w, int i) {
 // 2^x on the transcendental unit (results below 2^-126 flush to 0, which softmax weights
 // of that size may)
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ __forceinline__ void load_h4(const uint8_t* p, float (&o)[4]) {
-  const uint2 v = *reinterpret_cast<const uint2*>(p);
-  o[0] = h2f(uint16_t(v.x & 0xFFFF));
-  o[1] = h2f(uint16_t(v.x >> 16));
-  o[2] = h2f(uint16_t(v.y & 0xFFFF));
-  o[3] = h2f(uint16_t(v.y >> 16));
-}
 
 __device__ __forceinline__ void load_h8(const uint8_t* p, float* o) {
   const uint4 v = *reinterpret_cast<const uint4*>(p);
@@ -127,8 +108,20 @@ struct DecodeSmem {
 
 // Raw loads of one page: key codes (16 B per 16-token block), value codes (8 B per
 // 16-channel block), and entries 2l, 2l+1 of the 4 float16 metadata arrays of each record.
+// Key record geometry by key code width (4: kvarn_k4v2_g128, 2: kvarn_k2v2_g128).
+template <int KB> struct KeyRec;
+template <> struct KeyRec<4> {
+  static constexpr int kRecord = kKRecord, kCodeBytes = kKCodeBytes;
+  typedef uint4 Codes;    // one 16-token block: 4 words = the 4 k-steps of 8 channels
+};
+template <> struct KeyRec<2> {
+  static constexpr int kRecord = kK2Record, kCodeBytes = kK2CodeBytes;
+  typedef uint2 Codes;    // one 16-token block: 2 words, each 2 k-steps of 8 channels
+};
+
+template <int KB>
 struct PageRegs {
-  uint4 kc[8];
+  typename KeyRec<KB>::Codes kc[8];
   uint2 vc[8];
   uint32_t km[4], vm[4];
 };
@@ -151,22 +144,30 @@ struct LaneOffsets {
   uint32_t k, v, m;   // key codes, value codes, metadata
 };
 
-__device__ __forceinline__ void load_meta(PageRegs& t, __amdgpu_buffer_rsrc_t kr,
+template <int KB>
+__device__ __forceinline__ void load_meta(PageRegs<KB>& t, __amdgpu_buffer_rsrc_t kr,
                                           __amdgpu_buffer_rsrc_t vr, const LaneOffsets& o) {
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
-    t.km[a] = __builtin_amdgcn_raw_buffer_load_b32(kr, o.m, kKCodeBytes + 256 * a, kStreamLoad);
+    t.km[a] = __builtin_amdgcn_raw_buffer_load_b32(kr, o.m, KeyRec<KB>::kCodeBytes + 256 * a, kStreamLoad);
     t.vm[a] = __builtin_amdgcn_raw_buffer_load_b32(vr, o.m, kVCodeBytes + 256 * a, kStreamLoad);
   }
 }
-__device__ __forceinline__ void load_kcodes(PageRegs& t, __amdgpu_buffer_rsrc_t kr, const LaneOffsets& o) {
+template <int KB>
+__device__ __forceinline__ void load_kcodes(PageRegs<KB>& t, __amdgpu_buffer_rsrc_t kr, const LaneOffsets& o) {
 #pragma unroll
   for (int tb = 0; tb < 8; ++tb) {
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(kr, o.k, 1024 * tb, kStreamLoad);
-    t.kc[tb] = make_uint4(v.x, v.y, v.z, v.w);
+    if constexpr (KB == 4) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(kr, o.k, 1024 * tb, kStreamLoad);
+      t.kc[tb] = make_uint4(v.x, v.y, v.z, v.w);
+    } else {   // 32 bytes per token: the value records' lane offsets
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(kr, o.v, 512 * tb, kStreamLoad);
+      t.kc[tb] = make_uint2(v.x, v.y);
+    }
   }
 }
-__device__ __forceinline__ void load_vcodes(PageRegs& t, __amdgpu_buffer_rsrc_t vr, const LaneOffsets& o) {
+template <int KB>
+__device__ __forceinline__ void load_vcodes(PageRegs<KB>& t, __amdgpu_buffer_rsrc_t vr, const LaneOffsets& o) {
 #pragma unroll
   for (int bb = 0; bb < 8; ++bb) {
     const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(vr, o.v, 512 * bb, kStreamLoad);
@@ -338,7 +339,8 @@ __device__ void tail_partial(const __half* __restrict__ q, int32_t num_q_heads,
 // One workgroup: (split, KV head g, output row). Wave w handles page slots
 // split * 4 * tpw + w + 4 k, k < tpw. Writes one partial (m, l, acc) per query head. With
 // tail buffers the grid has one more split, n_splits, which computes the tail partial. The
-// row's sequence, page slots and tail follow row_geometry.
+// row's sequence, page slots and tail follow row_geometry. KB: key code width.
+template <int KB>
 __global__ void __launch_bounds__(kThreads)
 decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t num_kv_heads,
                     const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
@@ -429,9 +431,10 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
     for (int i = 0; i < 4; ++i) acc[bb][i] = 0.f;
 
   WaveMeta& wm = sm.meta[w];
-  // key channel 2l + j: nibble pair v = l % 4 -> b = 2 (even v) or 6; value token 2l + j:
-  // C row (2l + j) % 4 -> crumb pair parity -> b = 8 (rows 0,1) or 6 (rows 2,3)
-  const float fk = (l & 1) ? 16.f : 256.f;
+  // key channel 2l + j: 4-bit keys: nibble pair v = l % 4 -> b = 2 (even v) or 6; 2-bit keys:
+  // crumb pair parity l % 2 -> b = 8 or 6; value token 2l + j: C row (2l + j) % 4 -> crumb
+  // pair parity -> b = 8 (rows 0,1) or 6 (rows 2,3)
+  const float fk = (l & 1) ? 16.f : (KB == 4 ? 256.f : 4.f);
   const float fv = (l & 1) ? 16.f : 4.f;
 
   const int32_t* bt_row = block_table + int64_t(rg.b) * bt_stride;
@@ -456,8 +459,8 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
   auto krec_of = [&](int64_t page) {
     const uint32_t ps = __builtin_amdgcn_readfirstlane(uint32_t(page < 0 ? 0 : page));
     const uint32_t r = ps * uint32_t(num_kv_heads) + uint32_t(g);
-    return record_rsrc(uniform_ptr(k_pool + uint64_t(r) * uint32_t(kKRecord)),
-                       page < 0 ? 0 : kKRecord);
+    return record_rsrc(uniform_ptr(k_pool + uint64_t(r) * uint32_t(KeyRec<KB>::kRecord)),
+                       page < 0 ? 0 : KeyRec<KB>::kRecord);
   };
   auto vrec_of = [&](int64_t page) {
     const uint32_t ps = __builtin_amdgcn_readfirstlane(uint32_t(page < 0 ? 0 : page));
@@ -469,7 +472,7 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
   // this page has consumed it, so the loads overlap the rest of the page's work. A page
   // that is not `valid` (its id is out of range) runs the same code and adds nothing: its
   // maximum stays -inf and its weights exp2(s - inf) are 0.
-  auto process = [&](PageRegs& t, int64_t next, bool valid, int lim) {
+  auto process = [&](PageRegs<KB>& t, int64_t next, bool valid, int lim) {
     // ---- page factors into the wave's LDS slot ------------------------------------------
     {
       const float rk0 = lo_h(t.km[0]), rk1 = hi_h(t.km[0]);
@@ -532,16 +535,21 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
     float sc[8][2];
     {
       const float4v binit = {bias, bias, bias, bias};
-      const uint4* kc = t.kc;
 #pragma unroll
       for (int tb = 0; tb < 8; ++tb) {
         float4v c = binit;
-        const uint32_t dw[4] = {kc[tb].x, kc[tb].y, kc[tb].z, kc[tb].w};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           H8 a;
+          if constexpr (KB == 4) {
+            const uint32_t dw[4] = {t.kc[tb].x, t.kc[tb].y, t.kc[tb].z, t.kc[tb].w};
 #pragma unroll
-          for (int v = 0; v < 4; ++v) a.u[v] = k_pair(dw[s], v);
+            for (int v = 0; v < 4; ++v) a.u[v] = k_pair(dw[s], v);
+          } else {   // word d = s / 2 holds k-steps 2d, 2d+1 in crumbs 4 (s % 2) + v (+ 8)
+            const uint32_t word = (s >> 1) ? t.kc[tb].y : t.kc[tb].x;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) a.u[v] = v_pair(word, 4 * (s & 1) + v);
+          }
           c = mfma16x16x32(a.v, bq[s].v, c);
         }
         const float2 st = wm.kt[8 * tb + 2 * gq + (side >> 1)];
@@ -635,7 +643,7 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
     load_vcodes(t, vrec_of(next), lo);
   };
 
-  PageRegs t;
+  PageRegs<KB> t;
   const int wslot = __builtin_amdgcn_readfirstlane(slot0 + w);   // this wave's first slot
   int64_t cur = page_of(wslot);
   load_meta(t, krec_of(cur), vrec_of(cur), lo);
@@ -811,7 +819,7 @@ size_t decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv
   return size_t(batch) * num_q_heads * (ns + 1) * kPartStride * sizeof(float);
 }
 
-hipError_t launch_decode(const void* q, int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
+hipError_t launch_decode(int k_bits, const void* q, int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
                          const void* k_pool, const void* v_pool, int64_t pool_num_pages,
                          const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
                          int32_t max_seq_len, const int32_t* cu_q, int32_t batch,
@@ -827,7 +835,8 @@ hipError_t launch_decode(const void* q, int32_t rows, int32_t num_q_heads, int32
   if (grid_x > 0) {
     // without pages the only split launched is the tail, which must land on index ns
     const int32_t first = max_seq_len >= kTile ? 0 : ns;
-    hipLaunchKernelGGL(decode_pages_kernel, dim3(grid_x, num_kv_heads, rows), dim3(kThreads), 0,
+    auto kernel = k_bits == 4 ? decode_pages_kernel<4> : decode_pages_kernel<2>;
+    hipLaunchKernelGGL(kernel, dim3(grid_x, num_kv_heads, rows), dim3(kThreads), 0,
                        stream, static_cast<const __half*>(q), num_q_heads, num_kv_heads,
                        static_cast<const uint8_t*>(k_pool), static_cast<const uint8_t*>(v_pool),
                        pool_num_pages, block_table, bt_stride, seq_lens, max_seq_len, cu_q, batch,

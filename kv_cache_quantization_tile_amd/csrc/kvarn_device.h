@@ -12,6 +12,8 @@ constexpr int kTile = 128;        // tokens per tile / page
 constexpr int kKRecord = 9216;    // bytes of a key page record
 constexpr int kVRecord = 5120;    // bytes of a value page record
 constexpr int kKCodeBytes = 8192; // 4-bit codes of a key record
+constexpr int kK2Record = 5120;   // bytes of a 2-bit key page record (preset kvarn_k2v2_g128)
+constexpr int kK2CodeBytes = 4096; // 2-bit codes of such a record
 constexpr int kVCodeBytes = 4096; // 2-bit codes of a value record
 constexpr float kInvSqrt128 = 0.08838834764831845f;  // 1 / sqrt(128), fp32-rounded
 

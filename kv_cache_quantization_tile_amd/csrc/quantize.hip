@@ -117,6 +117,17 @@ __device__ __forceinline__ uint32_t bytes_to_nibbles(uint32_t e) {
   return (x | (x >> 8)) & 0x0000FFFFu;
 }
 
+// 4 codes (bytes, each <= 3) -> 4 crumbs in the low 8 bits, byte k -> crumb k
+__device__ __forceinline__ uint32_t bytes_to_crumbs(uint32_t e) {
+  const uint32_t x = (e | (e >> 6)) & 0x000F000Fu;
+  return (x | (x >> 12)) & 0x000000FFu;
+}
+
+// Key record geometry by key code width (4: kvarn_k4v2_g128, 2: kvarn_k2v2_g128).
+template <int KB> struct KeyFormat;
+template <> struct KeyFormat<4> { static constexpr int kRecord = kKRecord, kCodeBytes = kKCodeBytes; };
+template <> struct KeyFormat<2> { static constexpr int kRecord = kK2Record, kCodeBytes = kK2CodeBytes; };
+
 // x += c * x(lane under DPP control CTRL) for 8 values, one v_fmac_f32_dpp each. The DPP
 // source is read from the register the instruction writes (all lanes read before any
 // writes). A DPP read of a VGPR needs 2 wait states after the VALU write of that VGPR: the
@@ -274,8 +285,8 @@ __device__ __forceinline__ void rotate_tile_mfma(RowPtr row_ptr, int w, int l, f
 }
 
 // The tile quantizer proper. row_ptr(t) gives the 16-byte aligned address of token t's
-// 128 channels. Writes one record at `rec`.
-template <int KIND, typename RowPtr>
+// 128 channels. Writes one record at `rec`; KB is the key code width (ignored for values).
+template <int KIND, int KB, typename RowPtr>
 __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_iters, QuantSmem& sm) {
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63;
@@ -306,7 +317,6 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
   float* gc0 = &sm.gc[w][r][0][0];
   float* gc1 = &sm.gc[w][r][1][0];
   float* gr0 = &sm.gr[w][0][0];
-  float* gr1 = &sm.gr[w][1][0];
   float ir[8], is[8];      // 1/r for my channels, 1/s for my tokens
 #pragma unroll
   for (int i = 0; i < 8; ++i) { ir[i] = kInvSqrt128; is[i] = 1.f; }
@@ -450,7 +460,7 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const float lo = omn[k] * ir_own[k], hi_ = omx[k] * ir_own[k];   // y = z / r, r > 0
-      const uint16_t sc16 = f2h_rn((hi_ - lo) * (1.f / 15.f));
+      const uint16_t sc16 = f2h_rn((hi_ - lo) * (KB == 4 ? 1.f / 15.f : 1.f / 3.f));
       const uint16_t zr16 = f2h_rn(lo);
       const float sc = h2f(sc16);
       const float inv = sc > 0.f ? __builtin_amdgcn_rcpf(sc) : 0.f;
@@ -468,17 +478,38 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
     float A[8], B[8];
     lds_read8(&ga[8 * cb], A);
     lds_read8(&gb[8 * cb], B);
-    // word (t, cb) = channels 8cb..8cb+7 of token t; nibble p <- channel {0,2,4,6,1,3,5,7}[p]
+    if constexpr (KB == 4) {
+      // word (t, cb) = channels 8cb..8cb+7 of token t; nibble p <- channel {0,2,4,6,1,3,5,7}[p]
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      uint32_t e = 0, o = 0;
+      for (int j = 0; j < 8; ++j) {
+        uint32_t e = 0, o = 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float u = fminf(fmaf(x[j][i], A[i], B[i]), 15.f);
-        if (i & 1) o = __builtin_amdgcn_cvt_pk_u8_f32(u, i >> 1, o);
-        else e = __builtin_amdgcn_cvt_pk_u8_f32(u, i >> 1, e);
+        for (int i = 0; i < 8; ++i) {
+          const float u = fminf(fmaf(x[j][i], A[i], B[i]), 15.f);
+          if (i & 1) o = __builtin_amdgcn_cvt_pk_u8_f32(u, i >> 1, o);
+          else e = __builtin_amdgcn_cvt_pk_u8_f32(u, i >> 1, e);
+        }
+        out[tok(j) * 16 + cb] = bytes_to_nibbles(e) | (bytes_to_nibbles(o) << 16);
       }
-      out[tok(j) * 16 + cb] = bytes_to_nibbles(e) | (bytes_to_nibbles(o) << 16);
+    } else {
+      // 2-bit keys: token t's word w = 2 g + d holds channel 32 g + 8 (2 d + hs) + 2 v + e in
+      // crumb 4 hs + v + 8 e, i.e. channels 16 w .. 16 w + 15. This thread's 8 channels
+      // (cb = 2 w + hs) fill crumbs 4 hs .. +3 (even channels) and 8 + 4 hs .. +3 (odd
+      // channels); the thread with cb ^ 1 (lane l ^ 1) holds the other half of the word.
+      const int hs = cb & 1;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        uint32_t e = 0, o = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float u = fminf(fmaf(x[j][i], A[i], B[i]), 3.f);
+          if (i & 1) o = __builtin_amdgcn_cvt_pk_u8_f32(u, i >> 1, o);
+          else e = __builtin_amdgcn_cvt_pk_u8_f32(u, i >> 1, e);
+        }
+        const uint32_t mine = (bytes_to_crumbs(e) | (bytes_to_crumbs(o) << 16)) << (8 * hs);
+        const uint32_t other = __float_as_uint(dpp_f<kDppQuadXor1>(__uint_as_float(mine)));
+        if (hs == 0) out[tok(j) * 8 + (cb >> 1)] = mine | other;
+      }
     }
   } else {
     // values: one group per token, over the 128 channels; z = x / r
@@ -556,14 +587,14 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
   }
   // metadata: 4 x 128 float16 = 256 words, one per thread
   {
-    const int codes_words = (KIND == 0 ? kKCodeBytes : kVCodeBytes) / 4;
+    const int codes_words = (KIND == 0 ? KeyFormat<KB>::kCodeBytes : kVCodeBytes) / 4;
     const uint16_t* mm = &sm.meta[0][0];
     out[codes_words + tid] = uint32_t(mm[2 * tid]) | (uint32_t(mm[2 * tid + 1]) << 16);
   }
 }
 
 // Four workgroups per CU (16 waves) keep a whole layer's tiles resident in one round.
-template <int KIND>
+template <int KIND, int KB>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 quantize_tiles_kernel(const __half* __restrict__ src, int64_t token_stride, int64_t head_stride,
                       int64_t src_num_tokens, const int64_t* __restrict__ tile_src_token,
@@ -577,12 +608,13 @@ quantize_tiles_kernel(const __half* __restrict__ src, int64_t token_stride, int6
   if (t0 < 0 || t0 > src_num_tokens - kTile || page < 0 || page >= pool_num_pages) return;
   const __half* base = src + t0 * token_stride + int64_t(h) * head_stride;
   auto row_ptr = [=](int t) { return base + int64_t(t) * token_stride; };
-  constexpr int kRec = KIND == 0 ? kKRecord : kVRecord;
+  constexpr int kRec = KIND == 0 ? KeyFormat<KB>::kRecord : kVRecord;
   uint8_t* rec = pool + (page * num_kv_heads + h) * int64_t(kRec);
-  quantize_tile<KIND>(row_ptr, rec, n_iters, sm);
+  quantize_tile<KIND, KB>(row_ptr, rec, n_iters, sm);
 }
 
 // Keys and values of the same tiles in one launch: grid (n_tiles, num_kv_heads, 2), z = kind.
+template <int KB>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 quantize_kv_kernel(const __half* __restrict__ k_src, const __half* __restrict__ v_src,
                    int64_t token_stride, int64_t head_stride, int64_t src_num_tokens,
@@ -600,13 +632,15 @@ quantize_kv_kernel(const __half* __restrict__ k_src, const __half* __restrict__ 
   const __half* base = (is_k ? k_src : v_src) + t0 * token_stride + int64_t(h) * head_stride;
   auto row_ptr = [=](int t) { return base + int64_t(t) * token_stride; };
   if (is_k)
-    quantize_tile<0>(row_ptr, k_pool + (page * num_kv_heads + h) * int64_t(kKRecord), n_iters, sm);
+    quantize_tile<0, KB>(row_ptr, k_pool + (page * num_kv_heads + h) * int64_t(KeyFormat<KB>::kRecord),
+                         n_iters, sm);
   else
-    quantize_tile<1>(row_ptr, v_pool + (page * num_kv_heads + h) * int64_t(kVRecord), n_iters, sm);
+    quantize_tile<1, KB>(row_ptr, v_pool + (page * num_kv_heads + h) * int64_t(kVRecord), n_iters, sm);
 }
 
 // Append one token per (sequence, head) into staging; quantize the staging tile it fills.
 // grid: (batch, num_kv_heads, 2 kinds)
+template <int KB>
 __global__ void __launch_bounds__(kThreads)
 append_tokens_kernel(const __half* __restrict__ k_new, const __half* __restrict__ v_new,
                      int32_t num_kv_heads, const int32_t* __restrict__ seq_lens,
@@ -632,9 +666,10 @@ append_tokens_kernel(const __half* __restrict__ k_new, const __half* __restrict_
   // the filled row is read from the new-token buffer, never from the staging just written
   auto row_ptr = [=](int t) { return t == kTile - 1 ? src_new : stage + int64_t(t) * kDim; };
   if (kind == 0) {
-    quantize_tile<0>(row_ptr, k_pool + (page * num_kv_heads + h) * int64_t(kKRecord), n_iters, sm);
+    quantize_tile<0, KB>(row_ptr, k_pool + (page * num_kv_heads + h) * int64_t(KeyFormat<KB>::kRecord),
+                         n_iters, sm);
   } else {
-    quantize_tile<1>(row_ptr, v_pool + (page * num_kv_heads + h) * int64_t(kVRecord), n_iters, sm);
+    quantize_tile<1, KB>(row_ptr, v_pool + (page * num_kv_heads + h) * int64_t(kVRecord), n_iters, sm);
   }
 }
 
@@ -644,6 +679,7 @@ append_tokens_kernel(const __half* __restrict__ k_new, const __half* __restrict_
 // grid: (tile slots, batch, num_kv_heads * 2); slot j is tile t = L / 128 + j, quantized when
 // complete (128 t + 128 <= L + n). Its rows below L come from staging (only the tile that was
 // partial before the chunk has such rows), the others straight from the new-token buffer.
+template <int KB>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 write_tiles_kernel(const __half* __restrict__ k_new, const __half* __restrict__ v_new,
                    int32_t total_new, const int32_t* __restrict__ cu_new, int32_t max_new,
@@ -674,9 +710,10 @@ write_tiles_kernel(const __half* __restrict__ k_new, const __half* __restrict__ 
     return a < L ? stage + int64_t(r) * kDim : src + (a - L) * row_stride;
   };
   if (kind == 0)
-    quantize_tile<0>(row_ptr, k_pool + (page * num_kv_heads + h) * int64_t(kKRecord), n_iters, sm);
+    quantize_tile<0, KB>(row_ptr, k_pool + (page * num_kv_heads + h) * int64_t(KeyFormat<KB>::kRecord),
+                         n_iters, sm);
   else
-    quantize_tile<1>(row_ptr, v_pool + (page * num_kv_heads + h) * int64_t(kVRecord), n_iters, sm);
+    quantize_tile<1, KB>(row_ptr, v_pool + (page * num_kv_heads + h) * int64_t(kVRecord), n_iters, sm);
 }
 
 // Chunk write, part 2 (after part 1, which reads the staging rows this overwrites): the new
@@ -711,12 +748,12 @@ write_staging_kernel(const __half* __restrict__ k_new, const __half* __restrict_
 // Page records back to float16 tiles (read side, then the inverse rotation H^-1 = H):
 // grid (n_tiles, num_kv_heads), one workgroup per record, the thread layout of the
 // quantizer (channels 8cb..+7 x tokens 8tb..+7). dst: [n_tiles][num_kv_heads][token][channel].
-template <int KIND>
+template <int KIND, int KB>
 __global__ void __launch_bounds__(kThreads)
 dequantize_tiles_kernel(const uint8_t* __restrict__ pool, int64_t pool_num_pages,
                         const int32_t* __restrict__ pages, int32_t num_kv_heads,
                         __half* __restrict__ dst) {
-  constexpr int kRec = KIND == 0 ? kKRecord : kVRecord;
+  constexpr int kRec = KIND == 0 ? KeyFormat<KB>::kRecord : kVRecord;
   __shared__ uint4 rec_sm[kRec / 16];
   const int tile = blockIdx.x, h = blockIdx.y;
   const int64_t page = pages[tile];
@@ -727,7 +764,7 @@ dequantize_tiles_kernel(const uint8_t* __restrict__ pool, int64_t pool_num_pages
   __syncthreads();
   const uint32_t* words = reinterpret_cast<const uint32_t*>(rec_sm);
   const uint16_t* meta = reinterpret_cast<const uint16_t*>(
-      reinterpret_cast<const uint8_t*>(rec_sm) + (KIND == 0 ? kKCodeBytes : kVCodeBytes));
+      reinterpret_cast<const uint8_t*>(rec_sm) + (KIND == 0 ? KeyFormat<KB>::kCodeBytes : kVCodeBytes));
   const int w = tid >> 6, l = tid & 63, cb = l & 15, tb = 4 * w + (l >> 4);
   float x[8][8];
 #pragma unroll
@@ -735,14 +772,20 @@ dequantize_tiles_kernel(const uint8_t* __restrict__ pool, int64_t pool_num_pages
     const int t = 8 * tb + j;
     const float st = h2f(meta[kTile + t]);
     uint32_t kw = 0;
-    if constexpr (KIND == 0) kw = words[t * 16 + cb];   // channels 8cb..8cb+7 of token t
+    if constexpr (KIND == 0 && KB == 4) kw = words[t * 16 + cb];   // channels 8cb..8cb+7 of token t
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int c = 8 * cb + i;
       uint32_t code;
       float sc, zr;
       if constexpr (KIND == 0) {
-        code = (kw >> (4 * ((i & 1) ? 4 + (i >> 1) : (i >> 1)))) & 15u;   // nibble of channel i
+        if constexpr (KB == 4) {
+          code = (kw >> (4 * ((i & 1) ? 4 + (i >> 1) : (i >> 1)))) & 15u;   // nibble of channel i
+        } else {   // word c / 16 of token t, crumb 4 hs + v + 8 e, hs = bit 3 of c
+          const int hs = (c >> 3) & 1;
+          const int p = 4 * hs + ((c & 7) >> 1) + 8 * (c & 1);
+          code = (words[t * 8 + (c >> 4)] >> (2 * p)) & 3u;
+        }
         sc = h2f(meta[2 * kDim + c]);
         zr = h2f(meta[3 * kDim + c]);
       } else {
@@ -773,93 +816,117 @@ dequantize_tiles_kernel(const uint8_t* __restrict__ pool, int64_t pool_num_pages
 
 }  // namespace
 
-hipError_t launch_dequantize_tiles(int kind, const void* pool, int64_t pool_num_pages,
+hipError_t launch_dequantize_tiles(int kind, int k_bits, const void* pool, int64_t pool_num_pages,
                                    const int32_t* pages, int32_t n_tiles, int32_t num_kv_heads,
                                    void* dst, hipStream_t stream) {
   dim3 grid(n_tiles, num_kv_heads), block(kThreads);
-  if (kind == 0)
-    hipLaunchKernelGGL(dequantize_tiles_kernel<0>, grid, block, 0, stream,
-                       static_cast<const uint8_t*>(pool), pool_num_pages, pages, num_kv_heads,
-                       static_cast<__half*>(dst));
+  const auto* pl = static_cast<const uint8_t*>(pool);
+  auto* d = static_cast<__half*>(dst);
+  if (kind == 1)
+    hipLaunchKernelGGL((dequantize_tiles_kernel<1, 4>), grid, block, 0, stream, pl, pool_num_pages,
+                       pages, num_kv_heads, d);
+  else if (k_bits == 4)
+    hipLaunchKernelGGL((dequantize_tiles_kernel<0, 4>), grid, block, 0, stream, pl, pool_num_pages,
+                       pages, num_kv_heads, d);
   else
-    hipLaunchKernelGGL(dequantize_tiles_kernel<1>, grid, block, 0, stream,
-                       static_cast<const uint8_t*>(pool), pool_num_pages, pages, num_kv_heads,
-                       static_cast<__half*>(dst));
+    hipLaunchKernelGGL((dequantize_tiles_kernel<0, 2>), grid, block, 0, stream, pl, pool_num_pages,
+                       pages, num_kv_heads, d);
   return hipGetLastError();
 }
 
-hipError_t launch_quantize_tiles(int kind, const void* src, int64_t token_stride,
+hipError_t launch_quantize_tiles(int kind, int k_bits, const void* src, int64_t token_stride,
                                  int64_t head_stride, int64_t src_num_tokens,
                                  const int64_t* tile_src_token, const int32_t* tile_dst_page,
                                  int32_t n_tiles, int32_t num_kv_heads, void* pool,
                                  int64_t pool_num_pages, int n_iters, hipStream_t stream) {
   dim3 grid(n_tiles, num_kv_heads), block(kThreads);
-  if (kind == 0) {
-    hipLaunchKernelGGL(quantize_tiles_kernel<0>, grid, block, 0, stream,
-                       static_cast<const __half*>(src), token_stride, head_stride, src_num_tokens,
-                       tile_src_token, tile_dst_page, num_kv_heads, static_cast<uint8_t*>(pool),
+  const auto* sp = static_cast<const __half*>(src);
+  auto* pl = static_cast<uint8_t*>(pool);
+  if (kind == 1)
+    hipLaunchKernelGGL((quantize_tiles_kernel<1, 4>), grid, block, 0, stream, sp, token_stride,
+                       head_stride, src_num_tokens, tile_src_token, tile_dst_page, num_kv_heads, pl,
                        pool_num_pages, n_iters);
-  } else {
-    hipLaunchKernelGGL(quantize_tiles_kernel<1>, grid, block, 0, stream,
-                       static_cast<const __half*>(src), token_stride, head_stride, src_num_tokens,
-                       tile_src_token, tile_dst_page, num_kv_heads, static_cast<uint8_t*>(pool),
+  else if (k_bits == 4)
+    hipLaunchKernelGGL((quantize_tiles_kernel<0, 4>), grid, block, 0, stream, sp, token_stride,
+                       head_stride, src_num_tokens, tile_src_token, tile_dst_page, num_kv_heads, pl,
                        pool_num_pages, n_iters);
-  }
+  else
+    hipLaunchKernelGGL((quantize_tiles_kernel<0, 2>), grid, block, 0, stream, sp, token_stride,
+                       head_stride, src_num_tokens, tile_src_token, tile_dst_page, num_kv_heads, pl,
+                       pool_num_pages, n_iters);
   return hipGetLastError();
 }
 
-hipError_t launch_quantize_kv(const void* k_src, const void* v_src, int64_t token_stride,
-                              int64_t head_stride, int64_t src_num_tokens,
+hipError_t launch_quantize_kv(int k_bits, const void* k_src, const void* v_src,
+                              int64_t token_stride, int64_t head_stride, int64_t src_num_tokens,
                               const int64_t* tile_src_token, const int32_t* tile_dst_page,
                               int32_t n_tiles, int32_t num_kv_heads, void* k_pool, void* v_pool,
                               int64_t pool_num_pages, int n_iters, hipStream_t stream) {
   dim3 grid(n_tiles, num_kv_heads, 2), block(kThreads);
-  hipLaunchKernelGGL(quantize_kv_kernel, grid, block, 0, stream,
-                     static_cast<const __half*>(k_src), static_cast<const __half*>(v_src),
-                     token_stride, head_stride, src_num_tokens, tile_src_token, tile_dst_page,
-                     num_kv_heads, static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool),
-                     pool_num_pages, n_iters);
+  const auto* ks = static_cast<const __half*>(k_src);
+  const auto* vs = static_cast<const __half*>(v_src);
+  auto* kp = static_cast<uint8_t*>(k_pool);
+  auto* vp = static_cast<uint8_t*>(v_pool);
+  if (k_bits == 4)
+    hipLaunchKernelGGL(quantize_kv_kernel<4>, grid, block, 0, stream, ks, vs, token_stride,
+                       head_stride, src_num_tokens, tile_src_token, tile_dst_page, num_kv_heads,
+                       kp, vp, pool_num_pages, n_iters);
+  else
+    hipLaunchKernelGGL(quantize_kv_kernel<2>, grid, block, 0, stream, ks, vs, token_stride,
+                       head_stride, src_num_tokens, tile_src_token, tile_dst_page, num_kv_heads,
+                       kp, vp, pool_num_pages, n_iters);
   return hipGetLastError();
 }
 
-hipError_t launch_write_tokens(const void* k_new, const void* v_new, int32_t total_new,
-                               const int32_t* cu_new, int32_t max_new, int32_t batch,
-                               int32_t num_kv_heads,
-                               const int32_t* seq_lens, void* k_tail, void* v_tail,
-                               const int32_t* block_table, int32_t bt_stride, void* k_pool,
-                               void* v_pool, int64_t pool_num_pages, int n_iters,
-                               hipStream_t stream) {
+hipError_t launch_write_tokens(int k_bits, const void* k_new, const void* v_new,
+                               int32_t total_new, const int32_t* cu_new, int32_t max_new,
+                               int32_t batch, int32_t num_kv_heads, const int32_t* seq_lens,
+                               void* k_tail, void* v_tail, const int32_t* block_table,
+                               int32_t bt_stride, void* k_pool, void* v_pool,
+                               int64_t pool_num_pages, int n_iters, hipStream_t stream) {
   // tiles completed by n tokens: at most n / 128 + 1
   dim3 grid1(max_new / kTile + 1, batch, num_kv_heads * 2), block(kThreads);
-  hipLaunchKernelGGL(write_tiles_kernel, grid1, block, 0, stream,
-                     static_cast<const __half*>(k_new), static_cast<const __half*>(v_new),
-                     total_new, cu_new, max_new, num_kv_heads, seq_lens,
-                     static_cast<const __half*>(k_tail),
-                     static_cast<const __half*>(v_tail), block_table, bt_stride,
-                     static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), pool_num_pages,
-                     n_iters);
+  const auto* kn = static_cast<const __half*>(k_new);
+  const auto* vn = static_cast<const __half*>(v_new);
+  if (k_bits == 4)
+    hipLaunchKernelGGL(write_tiles_kernel<4>, grid1, block, 0, stream, kn, vn, total_new, cu_new,
+                       max_new, num_kv_heads, seq_lens, static_cast<const __half*>(k_tail),
+                       static_cast<const __half*>(v_tail), block_table, bt_stride,
+                       static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool),
+                       pool_num_pages, n_iters);
+  else
+    hipLaunchKernelGGL(write_tiles_kernel<2>, grid1, block, 0, stream, kn, vn, total_new, cu_new,
+                       max_new, num_kv_heads, seq_lens, static_cast<const __half*>(k_tail),
+                       static_cast<const __half*>(v_tail), block_table, bt_stride,
+                       static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool),
+                       pool_num_pages, n_iters);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 grid2(batch, num_kv_heads, 2);
-  hipLaunchKernelGGL(write_staging_kernel, grid2, block, 0, stream,
-                     static_cast<const __half*>(k_new), static_cast<const __half*>(v_new),
-                     total_new, cu_new, max_new, num_kv_heads, seq_lens, static_cast<__half*>(k_tail),
+  hipLaunchKernelGGL(write_staging_kernel, grid2, block, 0, stream, kn, vn, total_new, cu_new,
+                     max_new, num_kv_heads, seq_lens, static_cast<__half*>(k_tail),
                      static_cast<__half*>(v_tail));
   return hipGetLastError();
 }
 
-hipError_t launch_append_tokens(const void* k_new, const void* v_new, int32_t batch,
+hipError_t launch_append_tokens(int k_bits, const void* k_new, const void* v_new, int32_t batch,
                                 int32_t num_kv_heads, const int32_t* seq_lens, void* k_tail,
                                 void* v_tail, const int32_t* block_table, int32_t bt_stride,
                                 void* k_pool, void* v_pool, int64_t pool_num_pages, int n_iters,
                                 hipStream_t stream) {
   dim3 grid(batch, num_kv_heads, 2), block(kThreads);
-  hipLaunchKernelGGL(append_tokens_kernel, grid, block, 0, stream,
-                     static_cast<const __half*>(k_new), static_cast<const __half*>(v_new),
-                     num_kv_heads, seq_lens, static_cast<__half*>(k_tail),
-                     static_cast<__half*>(v_tail), block_table, bt_stride,
-                     static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool),
-                     pool_num_pages, n_iters);
+  const auto* kn = static_cast<const __half*>(k_new);
+  const auto* vn = static_cast<const __half*>(v_new);
+  auto* kt = static_cast<__half*>(k_tail);
+  auto* vt = static_cast<__half*>(v_tail);
+  auto* kp = static_cast<uint8_t*>(k_pool);
+  auto* vp = static_cast<uint8_t*>(v_pool);
+  if (k_bits == 4)
+    hipLaunchKernelGGL(append_tokens_kernel<4>, grid, block, 0, stream, kn, vn, num_kv_heads,
+                       seq_lens, kt, vt, block_table, bt_stride, kp, vp, pool_num_pages, n_iters);
+  else
+    hipLaunchKernelGGL(append_tokens_kernel<2>, grid, block, 0, stream, kn, vn, num_kv_heads,
+                       seq_lens, kt, vt, block_table, bt_stride, kp, vp, pool_num_pages, n_iters);
   return hipGetLastError();
 }
 

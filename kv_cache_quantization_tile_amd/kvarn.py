@@ -117,10 +117,38 @@ def page_bytes(params: Params, kind: int) -> int:
     return int(lib.kvarn_page_bytes(ctypes.byref(params), kind))
 
 
-def new_pool(num_pages: int, num_kv_heads: int, kind: int, device="cuda") -> torch.Tensor:
-    """A zeroed page pool [num_pages, num_kv_heads, record bytes] of uint8."""
-    nb = K_PAGE_BYTES if kind == KIND_K else V_PAGE_BYTES
+def new_pool(num_pages: int, num_kv_heads: int, kind: int, device="cuda",
+             params: Params | None = None) -> torch.Tensor:
+    """A zeroed page pool [num_pages, num_kv_heads, record bytes] of uint8 (record size of
+    the preset in params; kvarn_k4v2_g128 when omitted)."""
+    if params is None:
+        nb = K_PAGE_BYTES if kind == KIND_K else V_PAGE_BYTES
+    else:
+        nb = page_bytes(params, kind)
     return torch.zeros((num_pages, num_kv_heads, nb), dtype=torch.uint8, device=device)
+
+
+def _pool_n(params: Params, pool, kind: int) -> int:
+    _pool_ok(params, pool, kind, "pool")
+    return pool.shape[0]
+
+
+def _pools_n(params: Params, k_pool, v_pool) -> int:
+    """Checks a key / value pool pair against the preset; returns their page count."""
+    _pool_ok(params, k_pool, KIND_K, "k_pool")
+    _pool_ok(params, v_pool, KIND_V, "v_pool")
+    if k_pool.shape[0] != v_pool.shape[0]:
+        raise ValueError("k_pool and v_pool must have the same number of pages")
+    return k_pool.shape[0]
+
+
+def _pool_ok(params: Params, pool, kind: int, name: str):
+    """The kernels address records by the preset's record size: the pool must match it."""
+    if pool is None:
+        return
+    if pool.dim() != 3 or pool.dtype != torch.uint8 or pool.shape[2] != page_bytes(params, kind):
+        raise ValueError(f"{name} must be uint8 [pages, Hkv, {page_bytes(params, kind)}] for "
+                         f"this preset")
 
 
 # ----------------------------------------------------------------------------- quantize
@@ -144,7 +172,7 @@ def quantize_tiles(params: Params, kind: int, src: torch.Tensor, tile_src_token:
         raise ValueError("tile_src_token and tile_dst_page differ in length")
     _check(lib.kvarn_quantize_tiles(ctypes.byref(params), kind, _ptr(src), src.stride(0),
                                     src.stride(1), src.shape[0], _ptr(tile_src_token),
-                                    _ptr(tile_dst_page), n, hkv, _ptr(pool), pool.shape[0],
+                                    _ptr(tile_dst_page), n, hkv, _ptr(pool), _pool_n(params, pool, kind),
                                     _stream(stream)), "kvarn_quantize_tiles")
     return pool
 
@@ -164,8 +192,7 @@ def _kv_quant_args(params, k_src, v_src, tile_src_token, tile_dst_page, k_pool, 
         nb = page_bytes(params, kind)
         if t.dim() != 3 or t.shape[1] != hkv or t.shape[2] != nb or not t.is_contiguous():
             raise ValueError(f"{nm} must be contiguous [pages, {hkv}, {nb}]")
-    if k_pool.shape[0] != v_pool.shape[0]:
-        raise ValueError("k_pool and v_pool must have the same number of pages")
+    _pools_n(params, k_pool, v_pool)
     n = tile_src_token.numel()
     if tile_dst_page.numel() != n:
         raise ValueError("tile_src_token and tile_dst_page differ in length")
@@ -197,7 +224,7 @@ def dequantize_tiles(params: Params, kind: int, pool, pages, out=None, stream=No
     _need(out, "out", torch.float16)
     if tuple(out.shape) != (n, hkv, 128, 128) or not out.is_contiguous():
         raise ValueError(f"out must be contiguous [{n}, {hkv}, 128, 128]")
-    _check(lib.kvarn_dequantize_tiles(ctypes.byref(params), kind, _ptr(pool), pool.shape[0],
+    _check(lib.kvarn_dequantize_tiles(ctypes.byref(params), kind, _ptr(pool), _pool_n(params, pool, kind),
                                       _ptr(pages), n, hkv, _ptr(out), _stream(stream)),
            "kvarn_dequantize_tiles")
     return out
@@ -220,7 +247,8 @@ def append_tokens(params: Params, k_new, v_new, seq_lens, k_tail, v_tail, block_
     _check(lib.kvarn_append_tokens(ctypes.byref(params), _ptr(k_new), _ptr(v_new), B, hkv,
                                    _ptr(seq_lens), _ptr(k_tail), _ptr(v_tail), _ptr(block_table),
                                    block_table.shape[1], _ptr(k_pool), _ptr(v_pool),
-                                   k_pool.shape[0], _stream(stream)), "kvarn_append_tokens")
+                                   _pools_n(params, k_pool, v_pool),
+                                   _stream(stream)), "kvarn_append_tokens")
 
 
 def write_tokens(params: Params, k_new, v_new, cu_new, seq_lens, k_tail, v_tail, block_table,
@@ -252,7 +280,8 @@ def write_tokens(params: Params, k_new, v_new, cu_new, seq_lens, k_tail, v_tail,
                                   _ptr(cu_new), max(int(max_new_tokens), 0), B, hkv,
                                   _ptr(seq_lens), _ptr(k_tail), _ptr(v_tail), _ptr(block_table),
                                   block_table.shape[1], _ptr(k_pool), _ptr(v_pool),
-                                  k_pool.shape[0], _stream(stream)), "kvarn_write_tokens")
+                                  _pools_n(params, k_pool, v_pool),
+                                  _stream(stream)), "kvarn_write_tokens")
 
 
 # ----------------------------------------------------------------------------- decode
@@ -293,7 +322,8 @@ def decode_attention(params: Params, q, k_pool, v_pool, block_table, seq_lens, m
     if out is None:
         out = torch.empty_like(q)
     _check(lib.kvarn_decode_attention(ctypes.byref(params), _ptr(q), B, hq, hkv, _ptr(k_pool),
-                                      _ptr(v_pool), k_pool.shape[0], _ptr(block_table),
+                                      _ptr(v_pool), _pools_n(params, k_pool, v_pool),
+                                      _ptr(block_table),
                                       block_table.shape[1], _ptr(seq_lens), max_seq_len,
                                       _ptr(k_tail), _ptr(v_tail), float(softmax_scale),
                                       _ptr(workspace), workspace.numel(), _ptr(out),
@@ -326,7 +356,8 @@ def chunk_attention(params: Params, q, cu_q, k_pool, v_pool, block_table, seq_le
     if out is None:
         out = torch.empty_like(q)
     _check(lib.kvarn_chunk_attention(ctypes.byref(params), _ptr(q), total_q, _ptr(cu_q), B, hq,
-                                     hkv, _ptr(k_pool), _ptr(v_pool), k_pool.shape[0],
+                                     hkv, _ptr(k_pool), _ptr(v_pool),
+                                     _pools_n(params, k_pool, v_pool),
                                      _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
                                      max_seq_len, _ptr(k_tail), _ptr(v_tail), float(softmax_scale),
                                      _ptr(workspace), workspace.numel(), _ptr(out),
@@ -360,7 +391,7 @@ def prepare_quantize(params: Params, kind: int, src, tile_src_token, tile_dst_pa
     hkv = src.shape[1]
     args = (ctypes.byref(params), kind, _ptr(src), src.stride(0), src.stride(1), src.shape[0],
             _ptr(tile_src_token), _ptr(tile_dst_page), tile_src_token.numel(), hkv, _ptr(pool),
-            pool.shape[0], _stream(stream))
+            _pool_n(params, pool, kind), _stream(stream))
     return Prepared(lib.kvarn_quantize_tiles, args, "kvarn_quantize_tiles")
 
 
@@ -379,7 +410,8 @@ def prepare_decode(params: Params, q, k_pool, v_pool, block_table, seq_lens, max
     hkv = k_pool.shape[1]
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(128)
-    args = (ctypes.byref(params), _ptr(q), B, hq, hkv, _ptr(k_pool), _ptr(v_pool), k_pool.shape[0],
+    args = (ctypes.byref(params), _ptr(q), B, hq, hkv, _ptr(k_pool), _ptr(v_pool),
+            _pools_n(params, k_pool, v_pool),
             _ptr(block_table), block_table.shape[1], _ptr(seq_lens), max_seq_len, _ptr(k_tail),
             _ptr(v_tail), float(softmax_scale), _ptr(workspace), workspace.numel(), _ptr(out),
             _stream(stream))

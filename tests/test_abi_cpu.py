@@ -40,7 +40,9 @@ def test_params_from_dtype():
     out = K.Params()
     for bad in ("", "fp8", "kvarn_k4v2", "kvarn_k4v2_g", "kvarn_kv2_g128", "kvarn_k4v2_g128x", "kvarn_k0v2_g128"):
         assert K.lib.kvarn_params_from_dtype(bad.encode(), 8, ctypes.byref(out)) == INVALID, bad
-    for unsup in ("kvarn_k4v4_g128", "kvarn_k2v2_g128", "kvarn_k4v2_g64"):
+    p2 = K.params_from_dtype("kvarn_k2v2_g128", 4)
+    assert (p2.k_bits, p2.v_bits, p2.group, p2.sinkhorn_iters) == (2, 2, 128, 4)
+    for unsup in ("kvarn_k4v4_g128", "kvarn_k3v2_g128", "kvarn_k2v4_g128", "kvarn_k4v2_g64"):
         assert K.lib.kvarn_params_from_dtype(unsup.encode(), 8, ctypes.byref(out)) == UNSUP, unsup
     assert K.lib.kvarn_params_from_dtype(b"kvarn_k4v2_g128", -1, ctypes.byref(out)) == INVALID
     assert K.lib.kvarn_params_from_dtype(b"kvarn_k4v2_g128", 65, ctypes.byref(out)) == INVALID
@@ -53,6 +55,8 @@ def test_page_bytes():
     p = K.params_from_dtype()
     assert K.page_bytes(p, K.KIND_K) == 9216 and K.page_bytes(p, K.KIND_V) == 5120
     assert K.page_bytes(p, 7) == 0
+    p2 = K.params_from_dtype("kvarn_k2v2_g128")
+    assert K.page_bytes(p2, K.KIND_K) == 5120 and K.page_bytes(p2, K.KIND_V) == 5120
     bad = K.Params(128, 64, 4, 2, 128, 8)
     assert K.lib.kvarn_params_check(ctypes.byref(bad)) == UNSUP
     assert K.page_bytes(bad, K.KIND_K) == 0

@@ -40,8 +40,8 @@ def say(*a):
 
 
 def _quantize_layer(K, params, w):
-    kp = K.new_pool(w.num_pages, w.hkv, K.KIND_K)
-    vp = K.new_pool(w.num_pages, w.hkv, K.KIND_V)
+    kp = K.new_pool(w.num_pages, w.hkv, K.KIND_K, params=params)
+    vp = K.new_pool(w.num_pages, w.hkv, K.KIND_V, params=params)
     K.quantize_kv_tiles(params, w.k_src, w.v_src, w.tile_src_token, w.tile_dst_page, kp, vp)
     torch.cuda.synchronize()
     return kp, vp
@@ -130,7 +130,7 @@ def _decode_steps(K, params, w, steps, check_at, seed):
             for kind, pool, stage, new in ((O.KIND_K, kp, pre[0], kn), (O.KIND_V, vp, pre[1], vn)):
                 tile = stage[b].clone()
                 tile[:, 127] = new[b]
-                ref = K.new_pool(1, hkv, kind)
+                ref = K.new_pool(1, hkv, kind, params=params)
                 K.quantize_tiles(params, kind, tile.permute(1, 0, 2).contiguous(),
                                  torch.zeros(1, dtype=torch.int64, device="cuda"),
                                  torch.zeros(1, dtype=torch.int32, device="cuda"), ref)

@@ -25,7 +25,7 @@ def say(*a):
 
 def _quantize(K, params, kind, src, tile_tok, tile_page, num_pages):
     hkv = src.shape[1]
-    pool = K.new_pool(num_pages, hkv, kind)
+    pool = K.new_pool(num_pages, hkv, kind, params=params)
     K.quantize_tiles(params, kind, src, tile_tok, tile_page, pool)
     torch.cuda.synchronize()
     return pool
@@ -149,7 +149,7 @@ def test_quantize_kv_matches_separate_launches(K):
     pages = torch.randperm(n + 3, generator=g)[:n].to(torch.int32)
     params = K.params_from_dtype("kvarn_k4v2_g128", 8)
     say(f"quantize_kv_tiles n={n} hkv={hkv}")
-    kp, vp = K.new_pool(n + 3, hkv, O.KIND_K), K.new_pool(n + 3, hkv, O.KIND_V)
+    kp, vp = K.new_pool(n + 3, hkv, O.KIND_K, params=params), K.new_pool(n + 3, hkv, O.KIND_V, params=params)
     K.quantize_kv_tiles(params, ksrc.cuda(), vsrc.cuda(), tok.cuda(), pages.cuda(), kp, vp)
     kref = _quantize(K, params, O.KIND_K, ksrc.cuda(), tok.cuda(), pages.cuda(), n + 3)
     vref = _quantize(K, params, O.KIND_V, vsrc.cuda(), tok.cuda(), pages.cuda(), n + 3)
@@ -228,8 +228,8 @@ def _build_cache(K, params, lens, hkv, seed, spare=2, dist="normal", width=None)
             ktail[b, :, :r] = k[start + L - r:start + L].permute(1, 0, 2)
             vtail[b, :, :r] = v[start + L - r:start + L].permute(1, 0, 2)
         start += L
-    kp = K.new_pool(n_pages, hkv, O.KIND_K)
-    vp = K.new_pool(n_pages, hkv, O.KIND_V)
+    kp = K.new_pool(n_pages, hkv, O.KIND_K, params=params)
+    vp = K.new_pool(n_pages, hkv, O.KIND_V, params=params)
     if toks:
         tt = torch.tensor(toks, dtype=torch.int64).cuda()
         pp = torch.tensor(pages, dtype=torch.int32).cuda()
@@ -348,7 +348,7 @@ def test_append_fill_and_decode(K):
                 tile = stage[b].clone()
                 tile[:, 127] = new[b]
                 src = tile.permute(1, 0, 2).contiguous()          # [128 tok, hkv, 128]
-                ref = K.new_pool(1, hkv, kind)
+                ref = K.new_pool(1, hkv, kind, params=params)
                 K.quantize_tiles(params, kind, src, torch.zeros(1, dtype=torch.int64).cuda(),
                                  torch.zeros(1, dtype=torch.int32).cuda(), ref)
                 torch.cuda.synchronize()

@@ -111,7 +111,7 @@ def test_write_pages_equal_quantize_tiles_and_decode(K):
             for kind, stage0, new, pool in ((O.KIND_K, kt0, kn, kp), (O.KIND_V, vt0, vn, vp)):
                 tile = torch.stack([stage0[b, :, a - 128 * t] if a < L else new[int(cu_h[b]) + a - L]
                                     for a in range(128 * t, 128 * t + 128)])       # [128, hkv, 128]
-                ref = K.new_pool(1, hkv, kind)
+                ref = K.new_pool(1, hkv, kind, params=params)
                 K.quantize_tiles(params, kind, tile.contiguous(),
                                  torch.zeros(1, dtype=torch.int64, device="cuda"),
                                  torch.zeros(1, dtype=torch.int32, device="cuda"), ref)

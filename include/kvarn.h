@@ -7,7 +7,8 @@
  * orthonormal Hadamard matrix, normalized by an iterative log-space Sinkhorn-style
  * alternation of column-std and row-std normalization, then quantized by asymmetric
  * round-to-nearest, keys 4-bit with scales per channel, values 2-bit with scales per token
- * (preset "kvarn_k4v2_g128", README "Quick start"; 128 = tile / page size).
+ * (preset "kvarn_k4v2_g128", README "Quick start"; 128 = tile / page size). The preset
+ * "kvarn_k2v2_g128" (2-bit keys; the pages report 2-bit results) is also implemented.
  * The read path is decode attention that dequantizes the tiles on the fly: the query is
  * rotated by H for QK and the accumulated values are rotated back by H^T.
  *
@@ -55,7 +56,7 @@ typedef enum {
 
 typedef enum { KVARN_K = 0, KVARN_V = 1 } kvarn_kind;
 
-/* Quantizer parameters. Only head_dim = tile_tokens = group = 128, k_bits = 4,
+/* Quantizer parameters. Only head_dim = tile_tokens = group = 128, k_bits = 4 or 2,
  * v_bits = 2 are implemented (README "Quick start": other page sizes are not yet
  * supported). sinkhorn_iters is the number of (column step, row step) pairs of the
  * normalization (README "How KVarN works", stage 3); 0..64 accepted. */
@@ -78,7 +79,7 @@ KVARN_API const char* kvarn_status_str(kvarn_status status);
 /* Parse a kv-cache dtype string of the form "kvarn_k<kb>v<vb>_g<group>" (README "Quick
  * start": kv_cache_dtype="kvarn_k4v2_g128") into params, with the given iteration count.
  * Returns INVALID_ARG for a malformed string or NULL pointer, UNSUPPORTED for a well-formed
- * preset other than k4v2_g128. `out_host` is written only on success. */
+ * preset other than k4v2_g128 and k2v2_g128. `out_host` is written only on success. */
 KVARN_API kvarn_status kvarn_params_from_dtype(const char* kv_cache_dtype, int32_t sinkhorn_iters,
                                      kvarn_params* out_host);
 
@@ -86,7 +87,8 @@ KVARN_API kvarn_status kvarn_params_from_dtype(const char* kv_cache_dtype, int32
 KVARN_API kvarn_status kvarn_params_check(const kvarn_params* params);
 
 /* Bytes of one page record (one 128-token tile of one KV head) of the given kind:
- * 9216 for keys, 5120 for values; 0 if params are invalid or unsupported.
+ * 9216 for 4-bit keys, 5120 for 2-bit keys and for values; 0 if params are invalid or
+ * unsupported. Every pool passed with these params must use this record size.
  *
  * Page format v1 (little-endian):
  *   K record: bytes [0, 8192) are 4-bit codes, token-major: token t owns bytes
@@ -96,7 +98,11 @@ KVARN_API kvarn_status kvarn_params_check(const kvarn_params* params);
  *     8c + 2g + d (g = 0..3, d = 0..1); crumb p (bits 2p..2p+1) of word (c, g, d) holds
  *     token 32 s + (j < 4 ? 4g + j : 12 + 4g + j) where i = p mod 8, s = 2d + i / 4,
  *     j = 2 (i mod 4) + p / 8.
- *   Both then hold four float16[128] vectors: r (per-channel normalizer), s (per-token
+ *   2-bit K record (k_bits = 2): bytes [0, 4096) are 2-bit codes, token-major: token t
+ *     owns bytes [32t, 32t+32) as 8 32-bit words; word w = 2g + d holds channels
+ *     16w .. 16w+15, crumb p (bits 2p..2p+1) holding channel 32g + 8(2d + p mod 8 / 4)
+ *     + 2 (p mod 4) + p / 8.
+ *   All then hold four float16[128] vectors: r (per-channel normalizer), s (per-token
  *   normalizer), scale and zero (per channel for K, per token for V).
  *   A tile X (channels x tokens, rotated Xr = H X) is recovered as
  *     Xr[c][t] = r[c] * s[t] * (zero[g] + scale[g] * code[c][t]),  X = H Xr,

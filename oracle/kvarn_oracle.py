@@ -149,7 +149,7 @@ def rtn_asym(y: np.ndarray, bits: int, axis: int):
 
 
 def quantize_tiles(x16: np.ndarray, kind: int, n_iters: int = 8, lossless: bool = False,
-                   rotate_channels: bool = True, k_bits: int = 4):
+                   rotate_channels: bool = True, k_bits: int = 4, v_bits: int = 2):
     """Quantize tiles end to end (stages 1-4 of [README] "How KVarN works").
 
     x16: [..., 128 channels, 128 tokens] float16 (stage 1: the raw tile, channels x tokens).
@@ -163,7 +163,8 @@ def quantize_tiles(x16: np.ndarray, kind: int, n_iters: int = 8, lossless: bool 
 
     lossless=True stops after stage 3 and returns no codes (used to pin the bookkeeping).
     rotate_channels=False skips stage 2 (Xr = X): an ablation of the method, not the method.
-    k_bits: key code width, 4 (kvarn_k4v2_g128) or 2 (kvarn_k2v2_g128); values are 2-bit.
+    k_bits, v_bits: code widths of the preset (kvarn_k4v2_g128: 4, 2; kvarn_k2v2_g128: 2, 2;
+    kvarn_k4v4_g128: 4, 4).
     """
     x = np.asarray(x16, dtype=np.float16).astype(np.float64)
     if x.shape[-2:] != (HEAD_DIM, TILE_TOKENS):
@@ -179,7 +180,7 @@ def quantize_tiles(x16: np.ndarray, kind: int, n_iters: int = 8, lossless: bool 
     if kind == KIND_K:
         codes, scale16, zero16, u = rtn_asym(y, k_bits, axis=-1)
     elif kind == KIND_V:
-        codes, scale16, zero16, u = rtn_asym(y, V_BITS, axis=-2)
+        codes, scale16, zero16, u = rtn_asym(y, v_bits, axis=-2)
     else:
         raise ValueError("kind must be KIND_K or KIND_V")
     out.update(codes=codes, scale=scale16, zero=zero16, u=u)
@@ -220,6 +221,9 @@ def dequantize_tiles(codes, r16, s16, scale16, zero16, kind: int,
 #   Then four float16[128] vectors: r (per channel), s (per token), scale, zero
 #     (per channel for K, per token for V).
 
+#   4-bit V record (preset kvarn_k4v4_g128), 9216 bytes: 8192 B of 4-bit codes, channel-major:
+#     channel c owns the 16 words 16c + 4g + m (g, m in 0..3); nibble q (bits 4q..4q+3) of
+#     word (c, g, m) holds token v4_nibble_token(g, m, q); then the metadata.
 #   2-bit K record (preset kvarn_k2v2_g128), 5120 bytes: 4096 B of 2-bit codes, token-major:
 #     token t owns bytes [32 t, 32 t + 32) as 8 words; word w = 2g + d (g in 0..3, d in 0..1)
 #     holds channels 16 w .. 16 w + 15, crumb p (bits 2p..2p+1) = channel
@@ -228,6 +232,7 @@ def dequantize_tiles(codes, r16, s16, scale16, zero16, kind: int,
 K_RECORD_BYTES = 9216
 K2_RECORD_BYTES = 5120
 V_RECORD_BYTES = 5120
+V4_RECORD_BYTES = 9216
 K_NIBBLE_CHANNEL = (0, 2, 4, 6, 1, 3, 5, 7)
 
 
@@ -246,6 +251,13 @@ def v_crumb_token(g: int, d: int, p: int) -> int:
     slot = 2 * (i % 4) + half
     within = 4 * g + slot if slot < 4 else 12 + 4 * g + slot
     return 32 * step + within
+
+
+def v4_nibble_token(g: int, m: int, q: int) -> int:
+    """Token held by nibble q of word (g, m) of a channel in a 4-bit V record: the token that
+    crumb 4 (m mod 2) + (q mod 4) + 8 (q div 4) of word (g, m div 2) holds in a 2-bit V record
+    (the same token order, one code per nibble)."""
+    return v_crumb_token(g, m // 2, 4 * (m % 2) + (q % 4) + 8 * (q // 4))
 
 
 def _meta_bytes(r16, s16, scale16, zero16) -> bytes:
@@ -294,6 +306,20 @@ def pack_v_record(codes, r16, s16, scale16, zero16) -> bytes:
     return words.astype("<u4").tobytes() + _meta_bytes(r16, s16, scale16, zero16)
 
 
+def pack_v4_record(codes, r16, s16, scale16, zero16) -> bytes:
+    codes = np.asarray(codes)
+    assert codes.shape == (128, 128) and codes.max(initial=0) <= 15
+    words = np.zeros(128 * 16, dtype=np.uint32)
+    for c in range(128):
+        for g in range(4):
+            for m in range(4):
+                w = 0
+                for q in range(8):
+                    w |= int(codes[c, v4_nibble_token(g, m, q)]) << (4 * q)
+                words[16 * c + 4 * g + m] = w
+    return words.astype("<u4").tobytes() + _meta_bytes(r16, s16, scale16, zero16)
+
+
 def _unpack_meta(buf: np.ndarray, off: int):
     m = buf[off:off + 1024].view("<f2").reshape(4, 128)
     return m[0].copy(), m[1].copy(), m[2].copy(), m[3].copy()
@@ -325,17 +351,32 @@ def unpack_k2_record(rec) -> dict:
     return dict(codes=codes, r=r, s=s, scale=sc, zero=zr)
 
 
-def unpack_record(rec, kind: int, k_bits: int = 4) -> dict:
-    """The record of `kind` for the preset with k_bits-bit keys (4 or 2)."""
+def unpack_v4_record(rec) -> dict:
+    buf = np.frombuffer(bytes(rec), dtype=np.uint8)
+    assert buf.size == V4_RECORD_BYTES
+    words = buf[:8192].view("<u4").reshape(128, 4, 4)                  # [c, g, m]
+    codes = np.zeros((128, 128), dtype=np.uint8)
+    for g in range(4):
+        for m in range(4):
+            for q in range(8):
+                codes[:, v4_nibble_token(g, m, q)] = (words[:, g, m] >> np.uint32(4 * q)) & np.uint32(15)
+    r, s, sc, zr = _unpack_meta(buf, 8192)
+    return dict(codes=codes, r=r, s=s, scale=sc, zero=zr)
+
+
+def unpack_record(rec, kind: int, k_bits: int = 4, v_bits: int = 2) -> dict:
+    """The record of `kind` for the preset with k_bits-bit keys and v_bits-bit values."""
     if kind == KIND_V:
-        return unpack_v_record(rec)
+        return unpack_v_record(rec) if v_bits == 2 else unpack_v4_record(rec)
     return unpack_k_record(rec) if k_bits == 4 else unpack_k2_record(rec)
 
 
-def pack_record(kind: int, codes, r16, s16, scale16, zero16, k_bits: int = 4) -> bytes:
+def pack_record(kind: int, codes, r16, s16, scale16, zero16, k_bits: int = 4,
+                v_bits: int = 2) -> bytes:
     if kind == KIND_V:
-        return pack_v_record(codes, r16, s16, scale16, zero16)
-    pack = pack_k_record if k_bits == 4 else pack_k2_record
+        pack = pack_v_record if v_bits == 2 else pack_v4_record
+    else:
+        pack = pack_k_record if k_bits == 4 else pack_k2_record
     return pack(codes, r16, s16, scale16, zero16)
 
 
@@ -373,13 +414,14 @@ def dequantize_k_record(rec, k_bits: int = 4) -> np.ndarray:
     return dequantize_tiles(d["codes"], d["r"], d["s"], d["scale"], d["zero"], KIND_K).T
 
 
-def dequantize_v_record(rec) -> np.ndarray:
-    d = unpack_v_record(rec)
+def dequantize_v_record(rec, v_bits: int = 2) -> np.ndarray:
+    d = unpack_v_record(rec) if v_bits == 2 else unpack_v4_record(rec)
     return dequantize_tiles(d["codes"], d["r"], d["s"], d["scale"], d["zero"], KIND_V).T
 
 
 def decode_attention_row(q_row, k_pages, v_pages, k_tail=None, v_tail=None,
-                         softmax_scale: float = 1.0 / np.sqrt(HEAD_DIM), k_bits: int = 4) -> np.ndarray:
+                         softmax_scale: float = 1.0 / np.sqrt(HEAD_DIM), k_bits: int = 4,
+                         v_bits: int = 2) -> np.ndarray:
     """Decode attention of one query row over one KV head's cache.
 
     k_pages / v_pages: lists of page records (bytes) of that KV head, in block-table order
@@ -389,7 +431,7 @@ def decode_attention_row(q_row, k_pages, v_pages, k_tail=None, v_tail=None,
     Returns float64 [128].
     """
     ks = [dequantize_k_record(p, k_bits) for p in k_pages]
-    vs = [dequantize_v_record(p) for p in v_pages]
+    vs = [dequantize_v_record(p, v_bits) for p in v_pages]
     if k_tail is not None and len(k_tail):
         ks.append(np.asarray(k_tail, np.float16).astype(np.float64))
         vs.append(np.asarray(v_tail, np.float16).astype(np.float64))

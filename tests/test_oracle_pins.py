@@ -288,6 +288,32 @@ def test_k2_format_byte_patterns():
         assert np.all(w[tt] == int(g["k2_codes_t_mod_4"]["word_t"][tt % 4], 16))
 
 
+def test_v4_format_byte_patterns():
+    """4-bit value records: every bit of the nibble -> token map against hand-derived words."""
+    with open(os.path.join(GOLD, "format_v4_patterns.json")) as f:
+        g = json.load(f)
+    t = np.ones((128, 1), dtype=np.int64) * np.arange(128)[None, :]
+
+    def words(codes):
+        rec = O.pack_v4_record(codes.astype(np.uint8), *_meta())
+        assert len(rec) == O.V4_RECORD_BYTES
+        return np.frombuffer(rec[:8192], dtype="<u4").reshape(128, 4, 4)     # [c, g, m]
+
+    assert np.all(words(t % 4) == int(g["v4_codes_t_mod_4"]["word"], 16))
+    assert np.all(words((t // 16) % 2) == int(g["v4_codes_t_bit4"]["word"], 16))
+    w = words((t // 4) % 4)
+    for gg in range(4):
+        assert np.all(w[:, gg, :] == int(g["v4_codes_t_div_4_mod_4"]["word_g"][gg], 16))
+    w = words(t // 32)
+    for m in range(4):
+        assert np.all(w[:, :, m] == int(g["v4_codes_t_div_32"]["word_m"][m], 16))
+
+
+def test_v4_nibble_map_is_a_permutation():
+    toks = sorted(O.v4_nibble_token(g, m, q) for g in range(4) for m in range(4) for q in range(8))
+    assert toks == list(range(128))
+
+
 def test_k2_crumb_map_is_a_permutation():
     chans = sorted(O.k2_crumb_channel(g, d, p) for g in range(4) for d in range(2) for p in range(16))
     assert chans == list(range(128))
@@ -296,6 +322,7 @@ def test_k2_crumb_map_is_a_permutation():
 def test_pack_unpack_roundtrip():
     for bits, pack, unpack, size in ((4, O.pack_k_record, O.unpack_k_record, 9216),
                                      (2, O.pack_k2_record, O.unpack_k2_record, 5120),
+                                     (4, O.pack_v4_record, O.unpack_v4_record, 9216),
                                      (2, O.pack_v_record, O.unpack_v_record, 5120)):
         codes = RNG.integers(0, 1 << bits, (128, 128)).astype(np.uint8)
         meta = [RNG.standard_normal(128).astype(np.float16) for _ in range(4)]

@@ -36,7 +36,6 @@ sys.path.insert(0, ROOT)
 
 # Algorithmic work units (what the method must move / compute, not what the kernels do)
 Q_READ = 128 * 128 * 2                 # float16 tile in
-V_REC = 5120                           # value page record out (keys: the preset's record size)
 HBM_PEAK_GBPS = 8000.0                 # MI355X HBM3E
 # fp32 FMA on the vector ALUs without packed-FP32 forms: 256 CU x 4 SIMD x 16 lanes x 2 x 2.4 GHz
 ALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
@@ -72,7 +71,7 @@ def load_traffic(kernel: str, src_hash: str, workload: str):
     return kernels[kernel].get("bytes_per_launch")
 
 
-def cpu_baseline(w, n_iters: int, budget_s: float, k_bits: int = 4):
+def cpu_baseline(w, n_iters: int, budget_s: float, k_bits: int = 4, v_bits: int = 2):
     """The float64 oracle on a bounded sample of one step, scaled to the whole step."""
     import numpy as np
     from oracle import kvarn_oracle as O
@@ -92,7 +91,7 @@ def cpu_baseline(w, n_iters: int, budget_s: float, k_bits: int = 4):
     tiles_v = np.stack([v[128 * i:128 * (i + 1), 0, :].T for i in range(nq)])
     t0 = time.perf_counter()
     rk = O.quantize_tiles(tiles_k, O.KIND_K, n_iters, k_bits=k_bits)
-    rv = O.quantize_tiles(tiles_v, O.KIND_V, n_iters)
+    rv = O.quantize_tiles(tiles_v, O.KIND_V, n_iters, v_bits=v_bits)
     tq = (time.perf_counter() - t0) / (2 * nq)               # seconds per tile
     # decode: all query heads of KV head 0 over as many pages as fit the budget
     pages = max(1, min(T // 128, int(budget_s / max(tq, 1e-3) / 4)))
@@ -121,7 +120,7 @@ def main():
     ap.add_argument("--layers", type=int, default=64,
                     help="distinct layer copies cycled across steps (defeats the 256 MB MALL)")
     ap.add_argument("--sinkhorn-iters", type=int, default=8)
-    ap.add_argument("--preset", default="kvarn_k4v2_g128", choices=["kvarn_k4v2_g128", "kvarn_k2v2_g128"],
+    ap.add_argument("--preset", default="kvarn_k4v2_g128", choices=["kvarn_k4v2_g128", "kvarn_k2v2_g128", "kvarn_k4v4_g128"],
                     help="kv_cache_dtype preset (the released k4v2_g128 by default)")
     ap.add_argument("--context", type=int, default=16384)
     ap.add_argument("--workload", choices=["one_layer_16k", "prefill_burst", "chunked_prefill"],
@@ -152,6 +151,7 @@ def main():
     if args.workload == "chunked_prefill":
         return chunked_prefill(args, K, synth, params, dev)
     k_rec = K.page_bytes(params, K.KIND_K)
+    v_rec = K.page_bytes(params, K.KIND_V)
     L = max(1, args.layers) if args.workload == "one_layer_16k" else 1
     print(f"[bench] generating {L} copies of {args.workload} (context {args.context})",
           file=sys.stderr, flush=True)
@@ -213,9 +213,9 @@ def main():
     ms_step = total_ms / args.steps
 
     # algorithmic bytes
-    q_bytes = n_tiles * (Q_READ + k_rec) + n_tiles * (Q_READ + V_REC)
+    q_bytes = n_tiles * (Q_READ + k_rec) + n_tiles * (Q_READ + v_rec)
     full_pages = T // 128
-    d_bytes = B * hkv * full_pages * (k_rec + V_REC) + 2 * B * hq * 128 * 2
+    d_bytes = B * hkv * full_pages * (k_rec + v_rec) + 2 * B * hq * 128 * 2
     step_bytes = q_bytes + d_bytes
     value = step_bytes / (ms_step * 1e-3) / 1e9
     tiles_per_s = 2 * n_tiles / (q_ms * 1e-3)
@@ -236,7 +236,7 @@ def main():
                 "achieved": round(decode_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(decode_gbps / HBM_PEAK_GBPS, 4),
                 "traffic": load_traffic("decode_pages_kernel", src_hash, args.workload),
-                "per_launch": f"{B * hkv * full_pages} K+V page pairs x {k_rec + V_REC} B + q/out",
+                "per_launch": f"{B * hkv * full_pages} K+V page pairs x {k_rec + v_rec} B + q/out",
                 "launch_ms": round(d_ms, 5)}
     dominant, other = (quant_roof, dec_roof) if q_ms >= d_ms else (dec_roof, quant_roof)
 
@@ -263,7 +263,7 @@ def main():
         "source_hash": src_hash,
     }
     if not args.no_cpu_baseline:
-        t_step, cores, sample = cpu_baseline(w0, n_iters, args.cpu_budget, params.k_bits)
+        t_step, cores, sample = cpu_baseline(w0, n_iters, args.cpu_budget, params.k_bits, params.v_bits)
         res["cpu_baseline"] = {"value": round(step_bytes / t_step / 1e9, 5), "unit": "GB/s",
                                "cores": cores, "kind": "oracle", "sample": sample,
                                "seconds_per_step": round(t_step, 3)}
@@ -281,6 +281,7 @@ def chunked_prefill(args, K, synth, params, dev):
     kp = K.new_pool(w.num_pages, hkv, K.KIND_K, params=params)
     vp = K.new_pool(w.num_pages, hkv, K.KIND_V, params=params)
     k_rec = K.page_bytes(params, K.KIND_K)
+    v_rec = K.page_bytes(params, K.KIND_V)
     # the prompt: every tile but the last of each sequence; the last is the chunk
     keep = torch.tensor([i for i in range(w.tile_src_token.numel()) if (i + 1) % ((ctx + n) // 128) != 0],
                         dtype=torch.long, device=dev)
@@ -324,9 +325,9 @@ def chunked_prefill(args, K, synth, params, dev):
     w_ms = sum(m[0].elapsed_time(m[1]) for m in marks) / args.steps
     a_ms = sum(m[1].elapsed_time(m[2]) for m in marks) / args.steps
     pages = (ctx + n) // 128
-    write_bytes = B * hkv * (2 * Q_READ + k_rec + V_REC)                 # chunk in, records out
-    unique_kv = B * hkv * pages * (k_rec + V_REC)                      # each page once
-    per_row_kv = sum(B * hkv * ((ctx + i + 1) // 128) * (k_rec + V_REC) for i in range(n))
+    write_bytes = B * hkv * (2 * Q_READ + k_rec + v_rec)                 # chunk in, records out
+    unique_kv = B * hkv * pages * (k_rec + v_rec)                      # each page once
+    per_row_kv = sum(B * hkv * ((ctx + i + 1) // 128) * (k_rec + v_rec) for i in range(n))
     qo = 2 * B * n * hq * 128 * 2
     value = (write_bytes + unique_kv + qo) / (ms_step * 1e-3) / 1e9
     res = {
@@ -350,7 +351,7 @@ def chunked_prefill(args, K, synth, params, dev):
                      "frac": round(per_row_kv / (a_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                      "traffic": None,
                      "per_launch": f"{B * n} query rows x their causal prefix of pages x "
-                                   f"{k_rec + V_REC} B (re-reads of shared pages largely served "
+                                   f"{k_rec + v_rec} B (re-reads of shared pages largely served "
                                    "by L2 / Infinity Cache)",
                      "launch_ms": round(a_ms, 5)},
         "wall_s_timed": round(t_wall, 4),

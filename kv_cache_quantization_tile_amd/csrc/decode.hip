@@ -106,9 +106,11 @@ struct DecodeSmem {
   WaveMeta meta[4];
 };
 
-// Raw loads of one page: key codes (16 B per 16-token block), value codes (8 B per
-// 16-channel block), and entries 2l, 2l+1 of the 4 float16 metadata arrays of each record.
-// Key record geometry by key code width (4: kvarn_k4v2_g128, 2: kvarn_k2v2_g128).
+// Raw loads of one page: key codes (16 B per 16-token block at 4 bits, 8 B at 2), value
+// codes (8 B per 16-channel block at 2 bits, 16 B at 4), and entries 2l, 2l+1 of the 4
+// float16 metadata arrays of each record.
+// Key record geometry by key code width (4: kvarn_k4v2_g128 / kvarn_k4v4_g128,
+// 2: kvarn_k2v2_g128).
 template <int KB> struct KeyRec;
 template <> struct KeyRec<4> {
   static constexpr int kRecord = kKRecord, kCodeBytes = kKCodeBytes;
@@ -119,10 +121,22 @@ template <> struct KeyRec<2> {
   typedef uint2 Codes;    // one 16-token block: 2 words, each 2 k-steps of 8 channels
 };
 
-template <int KB>
+// Value record geometry by value code width (2: kvarn_k4v2_g128 / kvarn_k2v2_g128,
+// 4: kvarn_k4v4_g128).
+template <int VB> struct ValRec;
+template <> struct ValRec<2> {
+  static constexpr int kRecord = kVRecord, kCodeBytes = kVCodeBytes;
+  typedef uint2 Codes;    // one 16-channel block: 2 words, each 2 k-steps of 8 tokens
+};
+template <> struct ValRec<4> {
+  static constexpr int kRecord = kV4Record, kCodeBytes = kV4CodeBytes;
+  typedef uint4 Codes;    // one 16-channel block: 4 words = the 4 k-steps of 8 tokens
+};
+
+template <int KB, int VB>
 struct PageRegs {
   typename KeyRec<KB>::Codes kc[8];
-  uint2 vc[8];
+  typename ValRec<VB>::Codes vc[8];
   uint32_t km[4], vm[4];
 };
 
@@ -144,17 +158,18 @@ struct LaneOffsets {
   uint32_t k, v, m;   // key codes, value codes, metadata
 };
 
-template <int KB>
-__device__ __forceinline__ void load_meta(PageRegs<KB>& t, __amdgpu_buffer_rsrc_t kr,
+template <int KB, int VB>
+__device__ __forceinline__ void load_meta(PageRegs<KB, VB>& t, __amdgpu_buffer_rsrc_t kr,
                                           __amdgpu_buffer_rsrc_t vr, const LaneOffsets& o) {
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
     t.km[a] = __builtin_amdgcn_raw_buffer_load_b32(kr, o.m, KeyRec<KB>::kCodeBytes + 256 * a, kStreamLoad);
-    t.vm[a] = __builtin_amdgcn_raw_buffer_load_b32(vr, o.m, kVCodeBytes + 256 * a, kStreamLoad);
+    t.vm[a] = __builtin_amdgcn_raw_buffer_load_b32(vr, o.m, ValRec<VB>::kCodeBytes + 256 * a, kStreamLoad);
   }
 }
-template <int KB>
-__device__ __forceinline__ void load_kcodes(PageRegs<KB>& t, __amdgpu_buffer_rsrc_t kr, const LaneOffsets& o) {
+template <int KB, int VB>
+__device__ __forceinline__ void load_kcodes(PageRegs<KB, VB>& t, __amdgpu_buffer_rsrc_t kr,
+                                            const LaneOffsets& o) {
 #pragma unroll
   for (int tb = 0; tb < 8; ++tb) {
     if constexpr (KB == 4) {
@@ -166,12 +181,18 @@ __device__ __forceinline__ void load_kcodes(PageRegs<KB>& t, __amdgpu_buffer_rsr
     }
   }
 }
-template <int KB>
-__device__ __forceinline__ void load_vcodes(PageRegs<KB>& t, __amdgpu_buffer_rsrc_t vr, const LaneOffsets& o) {
+template <int KB, int VB>
+__device__ __forceinline__ void load_vcodes(PageRegs<KB, VB>& t, __amdgpu_buffer_rsrc_t vr,
+                                            const LaneOffsets& o) {
 #pragma unroll
   for (int bb = 0; bb < 8; ++bb) {
-    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(vr, o.v, 512 * bb, kStreamLoad);
-    t.vc[bb] = make_uint2(v.x, v.y);
+    if constexpr (VB == 2) {
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(vr, o.v, 512 * bb, kStreamLoad);
+      t.vc[bb] = make_uint2(v.x, v.y);
+    } else {   // 64 bytes per channel: the 4-bit key records' lane offsets
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(vr, o.k, 1024 * bb, kStreamLoad);
+      t.vc[bb] = make_uint4(v.x, v.y, v.z, v.w);
+    }
   }
 }
 
@@ -339,8 +360,8 @@ __device__ void tail_partial(const __half* __restrict__ q, int32_t num_q_heads,
 // One workgroup: (split, KV head g, output row). Wave w handles page slots
 // split * 4 * tpw + w + 4 k, k < tpw. Writes one partial (m, l, acc) per query head. With
 // tail buffers the grid has one more split, n_splits, which computes the tail partial. The
-// row's sequence, page slots and tail follow row_geometry. KB: key code width.
-template <int KB>
+// row's sequence, page slots and tail follow row_geometry. KB, VB: key and value code widths.
+template <int KB, int VB>
 __global__ void __launch_bounds__(kThreads)
 decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t num_kv_heads,
                     const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
@@ -432,10 +453,10 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
 
   WaveMeta& wm = sm.meta[w];
   // key channel 2l + j: 4-bit keys: nibble pair v = l % 4 -> b = 2 (even v) or 6; 2-bit keys:
-  // crumb pair parity l % 2 -> b = 8 or 6; value token 2l + j: C row (2l + j) % 4 -> crumb
-  // pair parity -> b = 8 (rows 0,1) or 6 (rows 2,3)
+  // crumb pair parity l % 2 -> b = 8 or 6; value token 2l + j: C row (2l + j) % 4 -> pair
+  // parity -> 2-bit values: b = 8 (rows 0,1) or 6 (rows 2,3); 4-bit values: b = 2 or 6
   const float fk = (l & 1) ? 16.f : (KB == 4 ? 256.f : 4.f);
-  const float fv = (l & 1) ? 16.f : 4.f;
+  const float fv = (l & 1) ? 16.f : (VB == 2 ? 4.f : 256.f);
 
   const int32_t* bt_row = block_table + int64_t(rg.b) * bt_stride;
   auto page_of = [&](int slot) -> int64_t {
@@ -465,14 +486,14 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
   auto vrec_of = [&](int64_t page) {
     const uint32_t ps = __builtin_amdgcn_readfirstlane(uint32_t(page < 0 ? 0 : page));
     const uint32_t r = ps * uint32_t(num_kv_heads) + uint32_t(g);
-    return record_rsrc(uniform_ptr(v_pool + uint64_t(r) * uint32_t(kVRecord)),
-                       page < 0 ? 0 : kVRecord);
+    return record_rsrc(uniform_ptr(v_pool + uint64_t(r) * uint32_t(ValRec<VB>::kRecord)),
+                       page < 0 ? 0 : ValRec<VB>::kRecord);
   };
   // Processes the page held in t; each part of t is reloaded with page `next` as soon as
   // this page has consumed it, so the loads overlap the rest of the page's work. A page
   // that is not `valid` (its id is out of range) runs the same code and adds nothing: its
   // maximum stays -inf and its weights exp2(s - inf) are 0.
-  auto process = [&](PageRegs<KB>& t, int64_t next, bool valid, int lim) {
+  auto process = [&](PageRegs<KB, VB>& t, int64_t next, bool valid, int lim) {
     // ---- page factors into the wave's LDS slot ------------------------------------------
     {
       const float rk0 = lo_h(t.km[0]), rk1 = hi_h(t.km[0]);
@@ -621,17 +642,28 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
     const float4v vinit = {vcorr, vcorr, vcorr, vcorr};
 #pragma unroll
     for (int bb = 0; bb < 8; ++bb) {
-      const uint2 vc = t.vc[bb];
       float4v c = vinit;
+      if constexpr (VB == 2) {
+        const uint2 vc = t.vc[bb];
 #pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        const uint32_t word = d ? vc.y : vc.x;
+        for (int d = 0; d < 2; ++d) {
+          const uint32_t word = d ? vc.y : vc.x;
 #pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {
+          for (int hs = 0; hs < 2; ++hs) {
+            H8 a;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) a.u[v] = v_pair(word, 4 * hs + v);
+            c = mfma16x16x32(a.v, bp[2 * d + hs].v, c);
+          }
+        }
+      } else {   // word m = k-step m; nibbles v, 4 + v = its tokens 2v, 2v + 1
+        const uint32_t words[4] = {t.vc[bb].x, t.vc[bb].y, t.vc[bb].z, t.vc[bb].w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
           H8 a;
 #pragma unroll
-          for (int v = 0; v < 4; ++v) a.u[v] = v_pair(word, 4 * hs + v);
-          c = mfma16x16x32(a.v, bp[2 * d + hs].v, c);
+          for (int v = 0; v < 4; ++v) a.u[v] = k_pair(words[m], v);
+          c = mfma16x16x32(a.v, bp[m].v, c);
         }
       }
       const float4 rv = wm.vr[4 * bb + gq];
@@ -643,7 +675,7 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
     load_vcodes(t, vrec_of(next), lo);
   };
 
-  PageRegs<KB> t;
+  PageRegs<KB, VB> t;
   const int wslot = __builtin_amdgcn_readfirstlane(slot0 + w);   // this wave's first slot
   int64_t cur = page_of(wslot);
   load_meta(t, krec_of(cur), vrec_of(cur), lo);
@@ -819,12 +851,13 @@ size_t decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv
   return size_t(batch) * num_q_heads * (ns + 1) * kPartStride * sizeof(float);
 }
 
-hipError_t launch_decode(int k_bits, const void* q, int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
-                         const void* k_pool, const void* v_pool, int64_t pool_num_pages,
-                         const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
-                         int32_t max_seq_len, const int32_t* cu_q, int32_t batch,
-                         const void* k_tail, const void* v_tail, float softmax_scale,
-                         void* workspace, void* out, hipStream_t stream) {
+hipError_t launch_decode(int k_bits, int v_bits, const void* q, int32_t rows,
+                         int32_t num_q_heads, int32_t num_kv_heads, const void* k_pool,
+                         const void* v_pool, int64_t pool_num_pages, const int32_t* block_table,
+                         int32_t bt_stride, const int32_t* seq_lens, int32_t max_seq_len,
+                         const int32_t* cu_q, int32_t batch, const void* k_tail,
+                         const void* v_tail, float softmax_scale, void* workspace, void* out,
+                         hipStream_t stream) {
   const int32_t tpw = decode_tiles_per_wave(rows, num_kv_heads, max_seq_len);
   const int32_t ns = decode_num_splits(rows, num_kv_heads, max_seq_len);
   const float qscale = softmax_scale * kLog2e;
@@ -835,14 +868,16 @@ hipError_t launch_decode(int k_bits, const void* q, int32_t rows, int32_t num_q_
   if (grid_x > 0) {
     // without pages the only split launched is the tail, which must land on index ns
     const int32_t first = max_seq_len >= kTile ? 0 : ns;
-    auto kernel = k_bits == 4 ? decode_pages_kernel<4> : decode_pages_kernel<2>;
-    hipLaunchKernelGGL(kernel, dim3(grid_x, num_kv_heads, rows), dim3(kThreads), 0,
-                       stream, static_cast<const __half*>(q), num_q_heads, num_kv_heads,
-                       static_cast<const uint8_t*>(k_pool), static_cast<const uint8_t*>(v_pool),
-                       pool_num_pages, block_table, bt_stride, seq_lens, max_seq_len, cu_q, batch,
-                       qscale * kInvSqrt128, tpw, ns, first, static_cast<const __half*>(k_tail),
-                       static_cast<const __half*>(v_tail), qscale, ws);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = with_preset(k_bits, v_bits, [&](auto kb, auto vb) {
+      hipLaunchKernelGGL((decode_pages_kernel<decltype(kb)::value, decltype(vb)::value>),
+                         dim3(grid_x, num_kv_heads, rows), dim3(kThreads), 0, stream,
+                         static_cast<const __half*>(q), num_q_heads, num_kv_heads,
+                         static_cast<const uint8_t*>(k_pool), static_cast<const uint8_t*>(v_pool),
+                         pool_num_pages, block_table, bt_stride, seq_lens, max_seq_len, cu_q,
+                         batch, qscale * kInvSqrt128, tpw, ns, first,
+                         static_cast<const __half*>(k_tail), static_cast<const __half*>(v_tail),
+                         qscale, ws);
+    });
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(decode_merge_kernel, dim3(num_q_heads, rows), dim3(128), 0, stream,

@@ -14,6 +14,8 @@ constexpr int kVRecord = 5120;    // bytes of a value page record
 constexpr int kKCodeBytes = 8192; // 4-bit codes of a key record
 constexpr int kK2Record = 5120;   // bytes of a 2-bit key page record (preset kvarn_k2v2_g128)
 constexpr int kK2CodeBytes = 4096; // 2-bit codes of such a record
+constexpr int kV4Record = 9216;   // bytes of a 4-bit value page record (preset kvarn_k4v4_g128)
+constexpr int kV4CodeBytes = 8192; // 4-bit codes of such a record
 constexpr int kVCodeBytes = 4096; // 2-bit codes of a value record
 constexpr float kInvSqrt128 = 0.08838834764831845f;  // 1 / sqrt(128), fp32-rounded
 

@@ -1,41 +1,62 @@
 // Internal launchers of the KVarN HIP kernels (called by the C ABI after validation).
-// k_bits: key code width of the preset (4: kvarn_k4v2_g128, 2: kvarn_k2v2_g128).
+// k_bits / v_bits: key and value code widths of the preset (4/2: kvarn_k4v2_g128,
+// 2/2: kvarn_k2v2_g128, 4/4: kvarn_k4v4_g128).
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace kvarn {
 
-hipError_t launch_quantize_tiles(int kind, int k_bits, const void* src, int64_t token_stride,
-                                 int64_t head_stride, int64_t src_num_tokens,
+// Calls f(kb, vb) with the preset's code widths as std::integral_constant<int, ...> values
+// (one kernel instantiation per preset), then returns the launch status;
+// hipErrorInvalidValue for a pair that is no preset.
+template <typename F>
+hipError_t with_preset(int k_bits, int v_bits, F&& f) {
+  using B2 = std::integral_constant<int, 2>;
+  using B4 = std::integral_constant<int, 4>;
+  if (k_bits == 4 && v_bits == 2)
+    f(B4{}, B2{});
+  else if (k_bits == 2 && v_bits == 2)
+    f(B2{}, B2{});
+  else if (k_bits == 4 && v_bits == 4)
+    f(B4{}, B4{});
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_tiles(int kind, int k_bits, int v_bits, const void* src,
+                                 int64_t token_stride, int64_t head_stride, int64_t src_num_tokens,
                                  const int64_t* tile_src_token, const int32_t* tile_dst_page,
                                  int32_t n_tiles, int32_t num_kv_heads, void* pool,
                                  int64_t pool_num_pages, int n_iters, hipStream_t stream);
 
-hipError_t launch_quantize_kv(int k_bits, const void* k_src, const void* v_src,
+hipError_t launch_quantize_kv(int k_bits, int v_bits, const void* k_src, const void* v_src,
                               int64_t token_stride, int64_t head_stride, int64_t src_num_tokens,
                               const int64_t* tile_src_token, const int32_t* tile_dst_page,
                               int32_t n_tiles, int32_t num_kv_heads, void* k_pool, void* v_pool,
                               int64_t pool_num_pages, int n_iters, hipStream_t stream);
 
-hipError_t launch_dequantize_tiles(int kind, int k_bits, const void* pool, int64_t pool_num_pages,
-                                   const int32_t* pages, int32_t n_tiles, int32_t num_kv_heads,
-                                   void* dst, hipStream_t stream);
+hipError_t launch_dequantize_tiles(int kind, int k_bits, int v_bits, const void* pool,
+                                   int64_t pool_num_pages, const int32_t* pages, int32_t n_tiles,
+                                   int32_t num_kv_heads, void* dst, hipStream_t stream);
 
-hipError_t launch_write_tokens(int k_bits, const void* k_new, const void* v_new,
+hipError_t launch_write_tokens(int k_bits, int v_bits, const void* k_new, const void* v_new,
                                int32_t total_new, const int32_t* cu_new, int32_t max_new,
                                int32_t batch, int32_t num_kv_heads, const int32_t* seq_lens,
                                void* k_tail, void* v_tail, const int32_t* block_table,
                                int32_t bt_stride, void* k_pool, void* v_pool,
                                int64_t pool_num_pages, int n_iters, hipStream_t stream);
 
-hipError_t launch_append_tokens(int k_bits, const void* k_new, const void* v_new, int32_t batch,
-                                int32_t num_kv_heads, const int32_t* seq_lens, void* k_tail,
-                                void* v_tail, const int32_t* block_table, int32_t bt_stride,
-                                void* k_pool, void* v_pool, int64_t pool_num_pages, int n_iters,
-                                hipStream_t stream);
+hipError_t launch_append_tokens(int k_bits, int v_bits, const void* k_new, const void* v_new,
+                                int32_t batch, int32_t num_kv_heads, const int32_t* seq_lens,
+                                void* k_tail, void* v_tail, const int32_t* block_table,
+                                int32_t bt_stride, void* k_pool, void* v_pool,
+                                int64_t pool_num_pages, int n_iters, hipStream_t stream);
 
 int32_t decode_tiles_per_wave(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len);
 int32_t decode_num_splits(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len);
@@ -44,11 +65,12 @@ size_t decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv
 
 // rows output rows; cu_q == nullptr: row b is sequence b (decode, rows == batch), else the
 // query rows of sequence b are cu_q[b] .. cu_q[b+1]-1 (the last positions of its cache)
-hipError_t launch_decode(int k_bits, const void* q, int32_t rows, int32_t num_q_heads,
-                         int32_t num_kv_heads, const void* k_pool, const void* v_pool,
-                         int64_t pool_num_pages, const int32_t* block_table, int32_t bt_stride,
-                         const int32_t* seq_lens, int32_t max_seq_len, const int32_t* cu_q,
-                         int32_t batch, const void* k_tail, const void* v_tail,
-                         float softmax_scale, void* workspace, void* out, hipStream_t stream);
+hipError_t launch_decode(int k_bits, int v_bits, const void* q, int32_t rows,
+                         int32_t num_q_heads, int32_t num_kv_heads, const void* k_pool,
+                         const void* v_pool, int64_t pool_num_pages, const int32_t* block_table,
+                         int32_t bt_stride, const int32_t* seq_lens, int32_t max_seq_len,
+                         const int32_t* cu_q, int32_t batch, const void* k_tail,
+                         const void* v_tail, float softmax_scale, void* workspace, void* out,
+                         hipStream_t stream);
 
 }  // namespace kvarn

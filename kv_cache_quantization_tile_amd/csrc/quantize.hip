@@ -123,10 +123,13 @@ __device__ __forceinline__ uint32_t bytes_to_crumbs(uint32_t e) {
   return (x | (x >> 12)) & 0x000000FFu;
 }
 
-// Key record geometry by key code width (4: kvarn_k4v2_g128, 2: kvarn_k2v2_g128).
-template <int KB> struct KeyFormat;
-template <> struct KeyFormat<4> { static constexpr int kRecord = kKRecord, kCodeBytes = kKCodeBytes; };
-template <> struct KeyFormat<2> { static constexpr int kRecord = kK2Record, kCodeBytes = kK2CodeBytes; };
+// Record geometry by kind and code width (presets kvarn_k4v2_g128, kvarn_k2v2_g128,
+// kvarn_k4v4_g128).
+template <int KIND, int BITS> struct RecFormat;
+template <> struct RecFormat<0, 4> { static constexpr int kRecord = kKRecord, kCodeBytes = kKCodeBytes; };
+template <> struct RecFormat<0, 2> { static constexpr int kRecord = kK2Record, kCodeBytes = kK2CodeBytes; };
+template <> struct RecFormat<1, 2> { static constexpr int kRecord = kVRecord, kCodeBytes = kVCodeBytes; };
+template <> struct RecFormat<1, 4> { static constexpr int kRecord = kV4Record, kCodeBytes = kV4CodeBytes; };
 
 // x += c * x(lane under DPP control CTRL) for 8 values, one v_fmac_f32_dpp each. The DPP
 // source is read from the register the instruction writes (all lanes read before any
@@ -285,8 +288,8 @@ __device__ __forceinline__ void rotate_tile_mfma(RowPtr row_ptr, int w, int l, f
 }
 
 // The tile quantizer proper. row_ptr(t) gives the 16-byte aligned address of token t's
-// 128 channels. Writes one record at `rec`; KB is the key code width (ignored for values).
-template <int KIND, int KB, typename RowPtr>
+// 128 channels. Writes one record at `rec`; BITS is the code width of this kind.
+template <int KIND, int BITS, typename RowPtr>
 __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_iters, QuantSmem& sm) {
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63;
@@ -460,7 +463,7 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const float lo = omn[k] * ir_own[k], hi_ = omx[k] * ir_own[k];   // y = z / r, r > 0
-      const uint16_t sc16 = f2h_rn((hi_ - lo) * (KB == 4 ? 1.f / 15.f : 1.f / 3.f));
+      const uint16_t sc16 = f2h_rn((hi_ - lo) * (BITS == 4 ? 1.f / 15.f : 1.f / 3.f));
       const uint16_t zr16 = f2h_rn(lo);
       const float sc = h2f(sc16);
       const float inv = sc > 0.f ? __builtin_amdgcn_rcpf(sc) : 0.f;
@@ -478,7 +481,7 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
     float A[8], B[8];
     lds_read8(&ga[8 * cb], A);
     lds_read8(&gb[8 * cb], B);
-    if constexpr (KB == 4) {
+    if constexpr (BITS == 4) {
       // word (t, cb) = channels 8cb..8cb+7 of token t; nibble p <- channel {0,2,4,6,1,3,5,7}[p]
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -527,7 +530,7 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
     }
     const float lo = row16_scatter8<1>(mn, l) * is_own;   // y = z / s, s > 0
     const float hi_ = row16_scatter8<2>(mx, l) * is_own;
-    const uint16_t sc16 = f2h_rn((hi_ - lo) * (1.f / 3.f));
+    const uint16_t sc16 = f2h_rn((hi_ - lo) * (BITS == 2 ? 1.f / 3.f : 1.f / 15.f));
     const uint16_t zr16 = f2h_rn(lo);
     const float sc = h2f(sc16);
     const float inv = sc > 0.f ? __builtin_amdgcn_rcpf(sc) : 0.f;
@@ -545,7 +548,7 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
       uint32_t lo4 = 0, hi4 = 0;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float u = fminf(fmaf(x[j][i], A[j], B[j]), 3.f);
+        const float u = fminf(fmaf(x[j][i], A[j], B[j]), BITS == 2 ? 3.f : 15.f);
         if (j < 4) lo4 = __builtin_amdgcn_cvt_pk_u8_f32(u, j, lo4);
         else hi4 = __builtin_amdgcn_cvt_pk_u8_f32(u, j - 4, hi4);
       }
@@ -557,7 +560,25 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
   __syncthreads();
 
   // ---- 4c. value codes into the record layout; metadata ---------------------------------
-  if constexpr (KIND == 1) {
+  if constexpr (KIND == 1 && BITS == 4) {
+    // 2048 words: word (c, g, m); nibble q = v + 4 e <- token 32m + (j < 4 ? 4g + j : 12 + 4g + j),
+    // j = 2v + e (the 2-bit records' token order, one nibble per code)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int wi = tid + kThreads * k;
+      const int c = wi >> 4, g = (wi >> 2) & 3, m = wi & 3;
+      const uint8_t* row = &sm.codes[c * kTile];
+      const uint32_t a = *reinterpret_cast<const uint32_t*>(row + 32 * m + 4 * g);       // slots 0..3
+      const uint32_t b = *reinterpret_cast<const uint32_t*>(row + 32 * m + 16 + 4 * g);  // slots 4..7
+      uint32_t word = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t code = (j < 4 ? a >> (8 * j) : b >> (8 * (j - 4))) & 15u;
+        word |= code << (4 * ((j >> 1) + 4 * (j & 1)));
+      }
+      out[wi] = word;
+    }
+  } else if constexpr (KIND == 1) {
     // 1024 words: word (c, g, d); crumb p <- token 32s + (j < 4 ? 4g + j : 12 + 4g + j),
     // i = p % 8, s = 2d + i / 4, j = 2 (i % 4) + p / 8
 #pragma unroll
@@ -587,14 +608,14 @@ __device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_i
   }
   // metadata: 4 x 128 float16 = 256 words, one per thread
   {
-    const int codes_words = (KIND == 0 ? KeyFormat<KB>::kCodeBytes : kVCodeBytes) / 4;
+    const int codes_words = RecFormat<KIND, BITS>::kCodeBytes / 4;
     const uint16_t* mm = &sm.meta[0][0];
     out[codes_words + tid] = uint32_t(mm[2 * tid]) | (uint32_t(mm[2 * tid + 1]) << 16);
   }
 }
 
 // Four workgroups per CU (16 waves) keep a whole layer's tiles resident in one round.
-template <int KIND, int KB>
+template <int KIND, int BITS>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 quantize_tiles_kernel(const __half* __restrict__ src, int64_t token_stride, int64_t head_stride,
                       int64_t src_num_tokens, const int64_t* __restrict__ tile_src_token,
@@ -608,13 +629,13 @@ quantize_tiles_kernel(const __half* __restrict__ src, int64_t token_stride, int6
   if (t0 < 0 || t0 > src_num_tokens - kTile || page < 0 || page >= pool_num_pages) return;
   const __half* base = src + t0 * token_stride + int64_t(h) * head_stride;
   auto row_ptr = [=](int t) { return base + int64_t(t) * token_stride; };
-  constexpr int kRec = KIND == 0 ? KeyFormat<KB>::kRecord : kVRecord;
+  constexpr int kRec = RecFormat<KIND, BITS>::kRecord;
   uint8_t* rec = pool + (page * num_kv_heads + h) * int64_t(kRec);
-  quantize_tile<KIND, KB>(row_ptr, rec, n_iters, sm);
+  quantize_tile<KIND, BITS>(row_ptr, rec, n_iters, sm);
 }
 
 // Keys and values of the same tiles in one launch: grid (n_tiles, num_kv_heads, 2), z = kind.
-template <int KB>
+template <int KB, int VB>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 quantize_kv_kernel(const __half* __restrict__ k_src, const __half* __restrict__ v_src,
                    int64_t token_stride, int64_t head_stride, int64_t src_num_tokens,
@@ -632,15 +653,16 @@ quantize_kv_kernel(const __half* __restrict__ k_src, const __half* __restrict__ 
   const __half* base = (is_k ? k_src : v_src) + t0 * token_stride + int64_t(h) * head_stride;
   auto row_ptr = [=](int t) { return base + int64_t(t) * token_stride; };
   if (is_k)
-    quantize_tile<0, KB>(row_ptr, k_pool + (page * num_kv_heads + h) * int64_t(KeyFormat<KB>::kRecord),
+    quantize_tile<0, KB>(row_ptr, k_pool + (page * num_kv_heads + h) * int64_t(RecFormat<0, KB>::kRecord),
                          n_iters, sm);
   else
-    quantize_tile<1, KB>(row_ptr, v_pool + (page * num_kv_heads + h) * int64_t(kVRecord), n_iters, sm);
+    quantize_tile<1, VB>(row_ptr, v_pool + (page * num_kv_heads + h) * int64_t(RecFormat<1, VB>::kRecord),
+                         n_iters, sm);
 }
 
 // Append one token per (sequence, head) into staging; quantize the staging tile it fills.
 // grid: (batch, num_kv_heads, 2 kinds)
-template <int KB>
+template <int KB, int VB>
 __global__ void __launch_bounds__(kThreads)
 append_tokens_kernel(const __half* __restrict__ k_new, const __half* __restrict__ v_new,
                      int32_t num_kv_heads, const int32_t* __restrict__ seq_lens,
@@ -666,10 +688,11 @@ append_tokens_kernel(const __half* __restrict__ k_new, const __half* __restrict_
   // the filled row is read from the new-token buffer, never from the staging just written
   auto row_ptr = [=](int t) { return t == kTile - 1 ? src_new : stage + int64_t(t) * kDim; };
   if (kind == 0) {
-    quantize_tile<0, KB>(row_ptr, k_pool + (page * num_kv_heads + h) * int64_t(KeyFormat<KB>::kRecord),
+    quantize_tile<0, KB>(row_ptr, k_pool + (page * num_kv_heads + h) * int64_t(RecFormat<0, KB>::kRecord),
                          n_iters, sm);
   } else {
-    quantize_tile<1, KB>(row_ptr, v_pool + (page * num_kv_heads + h) * int64_t(kVRecord), n_iters, sm);
+    quantize_tile<1, VB>(row_ptr, v_pool + (page * num_kv_heads + h) * int64_t(RecFormat<1, VB>::kRecord),
+                         n_iters, sm);
   }
 }
 
@@ -679,7 +702,7 @@ append_tokens_kernel(const __half* __restrict__ k_new, const __half* __restrict_
 // grid: (tile slots, batch, num_kv_heads * 2); slot j is tile t = L / 128 + j, quantized when
 // complete (128 t + 128 <= L + n). Its rows below L come from staging (only the tile that was
 // partial before the chunk has such rows), the others straight from the new-token buffer.
-template <int KB>
+template <int KB, int VB>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 write_tiles_kernel(const __half* __restrict__ k_new, const __half* __restrict__ v_new,
                    int32_t total_new, const int32_t* __restrict__ cu_new, int32_t max_new,
@@ -710,10 +733,11 @@ write_tiles_kernel(const __half* __restrict__ k_new, const __half* __restrict__ 
     return a < L ? stage + int64_t(r) * kDim : src + (a - L) * row_stride;
   };
   if (kind == 0)
-    quantize_tile<0, KB>(row_ptr, k_pool + (page * num_kv_heads + h) * int64_t(KeyFormat<KB>::kRecord),
+    quantize_tile<0, KB>(row_ptr, k_pool + (page * num_kv_heads + h) * int64_t(RecFormat<0, KB>::kRecord),
                          n_iters, sm);
   else
-    quantize_tile<1, KB>(row_ptr, v_pool + (page * num_kv_heads + h) * int64_t(kVRecord), n_iters, sm);
+    quantize_tile<1, VB>(row_ptr, v_pool + (page * num_kv_heads + h) * int64_t(RecFormat<1, VB>::kRecord),
+                         n_iters, sm);
 }
 
 // Chunk write, part 2 (after part 1, which reads the staging rows this overwrites): the new
@@ -748,12 +772,12 @@ write_staging_kernel(const __half* __restrict__ k_new, const __half* __restrict_
 // Page records back to float16 tiles (read side, then the inverse rotation H^-1 = H):
 // grid (n_tiles, num_kv_heads), one workgroup per record, the thread layout of the
 // quantizer (channels 8cb..+7 x tokens 8tb..+7). dst: [n_tiles][num_kv_heads][token][channel].
-template <int KIND, int KB>
+template <int KIND, int BITS>
 __global__ void __launch_bounds__(kThreads)
 dequantize_tiles_kernel(const uint8_t* __restrict__ pool, int64_t pool_num_pages,
                         const int32_t* __restrict__ pages, int32_t num_kv_heads,
                         __half* __restrict__ dst) {
-  constexpr int kRec = KIND == 0 ? KeyFormat<KB>::kRecord : kVRecord;
+  constexpr int kRec = RecFormat<KIND, BITS>::kRecord;
   __shared__ uint4 rec_sm[kRec / 16];
   const int tile = blockIdx.x, h = blockIdx.y;
   const int64_t page = pages[tile];
@@ -764,7 +788,7 @@ dequantize_tiles_kernel(const uint8_t* __restrict__ pool, int64_t pool_num_pages
   __syncthreads();
   const uint32_t* words = reinterpret_cast<const uint32_t*>(rec_sm);
   const uint16_t* meta = reinterpret_cast<const uint16_t*>(
-      reinterpret_cast<const uint8_t*>(rec_sm) + (KIND == 0 ? KeyFormat<KB>::kCodeBytes : kVCodeBytes));
+      reinterpret_cast<const uint8_t*>(rec_sm) + RecFormat<KIND, BITS>::kCodeBytes);
   const int w = tid >> 6, l = tid & 63, cb = l & 15, tb = 4 * w + (l >> 4);
   float x[8][8];
 #pragma unroll
@@ -772,14 +796,14 @@ dequantize_tiles_kernel(const uint8_t* __restrict__ pool, int64_t pool_num_pages
     const int t = 8 * tb + j;
     const float st = h2f(meta[kTile + t]);
     uint32_t kw = 0;
-    if constexpr (KIND == 0 && KB == 4) kw = words[t * 16 + cb];   // channels 8cb..8cb+7 of token t
+    if constexpr (KIND == 0 && BITS == 4) kw = words[t * 16 + cb];   // channels 8cb..8cb+7 of token t
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int c = 8 * cb + i;
       uint32_t code;
       float sc, zr;
       if constexpr (KIND == 0) {
-        if constexpr (KB == 4) {
+        if constexpr (BITS == 4) {
           code = (kw >> (4 * ((i & 1) ? 4 + (i >> 1) : (i >> 1)))) & 15u;   // nibble of channel i
         } else {   // word c / 16 of token t, crumb 4 hs + v + 8 e, hs = bit 3 of c
           const int hs = (c >> 3) & 1;
@@ -793,8 +817,13 @@ dequantize_tiles_kernel(const uint8_t* __restrict__ pool, int64_t pool_num_pages
         const int s_ = t >> 5, rem = t & 31;
         const int g = rem < 16 ? rem >> 2 : (rem - 16) >> 2;
         const int jj = rem < 16 ? rem & 3 : 4 + (rem & 3);
-        const int p = 4 * (s_ & 1) + (jj >> 1) + 8 * (jj & 1);
-        code = (words[8 * c + 2 * g + (s_ >> 1)] >> (2 * p)) & 3u;
+        if constexpr (BITS == 2) {
+          const int p = 4 * (s_ & 1) + (jj >> 1) + 8 * (jj & 1);
+          code = (words[8 * c + 2 * g + (s_ >> 1)] >> (2 * p)) & 3u;
+        } else {   // word (c, g, m = s_), nibble (jj / 2) + 4 (jj % 2)
+          const int qn = (jj >> 1) + 4 * (jj & 1);
+          code = (words[16 * c + 4 * g + s_] >> (4 * qn)) & 15u;
+        }
         sc = h2f(meta[2 * kDim + t]);
         zr = h2f(meta[3 * kDim + t]);
       }
@@ -816,48 +845,43 @@ dequantize_tiles_kernel(const uint8_t* __restrict__ pool, int64_t pool_num_pages
 
 }  // namespace
 
-hipError_t launch_dequantize_tiles(int kind, int k_bits, const void* pool, int64_t pool_num_pages,
-                                   const int32_t* pages, int32_t n_tiles, int32_t num_kv_heads,
-                                   void* dst, hipStream_t stream) {
+hipError_t launch_dequantize_tiles(int kind, int k_bits, int v_bits, const void* pool,
+                                   int64_t pool_num_pages, const int32_t* pages, int32_t n_tiles,
+                                   int32_t num_kv_heads, void* dst, hipStream_t stream) {
   dim3 grid(n_tiles, num_kv_heads), block(kThreads);
   const auto* pl = static_cast<const uint8_t*>(pool);
   auto* d = static_cast<__half*>(dst);
-  if (kind == 1)
-    hipLaunchKernelGGL((dequantize_tiles_kernel<1, 4>), grid, block, 0, stream, pl, pool_num_pages,
-                       pages, num_kv_heads, d);
-  else if (k_bits == 4)
-    hipLaunchKernelGGL((dequantize_tiles_kernel<0, 4>), grid, block, 0, stream, pl, pool_num_pages,
-                       pages, num_kv_heads, d);
-  else
-    hipLaunchKernelGGL((dequantize_tiles_kernel<0, 2>), grid, block, 0, stream, pl, pool_num_pages,
-                       pages, num_kv_heads, d);
-  return hipGetLastError();
+  return with_preset(k_bits, v_bits, [&](auto kb, auto vb) {
+    if (kind == 1)
+      hipLaunchKernelGGL((dequantize_tiles_kernel<1, decltype(vb)::value>), grid, block, 0, stream,
+                         pl, pool_num_pages, pages, num_kv_heads, d);
+    else
+      hipLaunchKernelGGL((dequantize_tiles_kernel<0, decltype(kb)::value>), grid, block, 0, stream,
+                         pl, pool_num_pages, pages, num_kv_heads, d);
+  });
 }
 
-hipError_t launch_quantize_tiles(int kind, int k_bits, const void* src, int64_t token_stride,
-                                 int64_t head_stride, int64_t src_num_tokens,
+hipError_t launch_quantize_tiles(int kind, int k_bits, int v_bits, const void* src,
+                                 int64_t token_stride, int64_t head_stride, int64_t src_num_tokens,
                                  const int64_t* tile_src_token, const int32_t* tile_dst_page,
                                  int32_t n_tiles, int32_t num_kv_heads, void* pool,
                                  int64_t pool_num_pages, int n_iters, hipStream_t stream) {
   dim3 grid(n_tiles, num_kv_heads), block(kThreads);
   const auto* sp = static_cast<const __half*>(src);
   auto* pl = static_cast<uint8_t*>(pool);
-  if (kind == 1)
-    hipLaunchKernelGGL((quantize_tiles_kernel<1, 4>), grid, block, 0, stream, sp, token_stride,
-                       head_stride, src_num_tokens, tile_src_token, tile_dst_page, num_kv_heads, pl,
-                       pool_num_pages, n_iters);
-  else if (k_bits == 4)
-    hipLaunchKernelGGL((quantize_tiles_kernel<0, 4>), grid, block, 0, stream, sp, token_stride,
-                       head_stride, src_num_tokens, tile_src_token, tile_dst_page, num_kv_heads, pl,
-                       pool_num_pages, n_iters);
-  else
-    hipLaunchKernelGGL((quantize_tiles_kernel<0, 2>), grid, block, 0, stream, sp, token_stride,
-                       head_stride, src_num_tokens, tile_src_token, tile_dst_page, num_kv_heads, pl,
-                       pool_num_pages, n_iters);
-  return hipGetLastError();
+  return with_preset(k_bits, v_bits, [&](auto kb, auto vb) {
+    if (kind == 1)
+      hipLaunchKernelGGL((quantize_tiles_kernel<1, decltype(vb)::value>), grid, block, 0, stream,
+                         sp, token_stride, head_stride, src_num_tokens, tile_src_token,
+                         tile_dst_page, num_kv_heads, pl, pool_num_pages, n_iters);
+    else
+      hipLaunchKernelGGL((quantize_tiles_kernel<0, decltype(kb)::value>), grid, block, 0, stream,
+                         sp, token_stride, head_stride, src_num_tokens, tile_src_token,
+                         tile_dst_page, num_kv_heads, pl, pool_num_pages, n_iters);
+  });
 }
 
-hipError_t launch_quantize_kv(int k_bits, const void* k_src, const void* v_src,
+hipError_t launch_quantize_kv(int k_bits, int v_bits, const void* k_src, const void* v_src,
                               int64_t token_stride, int64_t head_stride, int64_t src_num_tokens,
                               const int64_t* tile_src_token, const int32_t* tile_dst_page,
                               int32_t n_tiles, int32_t num_kv_heads, void* k_pool, void* v_pool,
@@ -867,18 +891,15 @@ hipError_t launch_quantize_kv(int k_bits, const void* k_src, const void* v_src,
   const auto* vs = static_cast<const __half*>(v_src);
   auto* kp = static_cast<uint8_t*>(k_pool);
   auto* vp = static_cast<uint8_t*>(v_pool);
-  if (k_bits == 4)
-    hipLaunchKernelGGL(quantize_kv_kernel<4>, grid, block, 0, stream, ks, vs, token_stride,
-                       head_stride, src_num_tokens, tile_src_token, tile_dst_page, num_kv_heads,
-                       kp, vp, pool_num_pages, n_iters);
-  else
-    hipLaunchKernelGGL(quantize_kv_kernel<2>, grid, block, 0, stream, ks, vs, token_stride,
-                       head_stride, src_num_tokens, tile_src_token, tile_dst_page, num_kv_heads,
-                       kp, vp, pool_num_pages, n_iters);
-  return hipGetLastError();
+  return with_preset(k_bits, v_bits, [&](auto kb, auto vb) {
+    hipLaunchKernelGGL((quantize_kv_kernel<decltype(kb)::value, decltype(vb)::value>), grid, block,
+                       0, stream, ks, vs, token_stride, head_stride, src_num_tokens,
+                       tile_src_token, tile_dst_page, num_kv_heads, kp, vp, pool_num_pages,
+                       n_iters);
+  });
 }
 
-hipError_t launch_write_tokens(int k_bits, const void* k_new, const void* v_new,
+hipError_t launch_write_tokens(int k_bits, int v_bits, const void* k_new, const void* v_new,
                                int32_t total_new, const int32_t* cu_new, int32_t max_new,
                                int32_t batch, int32_t num_kv_heads, const int32_t* seq_lens,
                                void* k_tail, void* v_tail, const int32_t* block_table,
@@ -888,19 +909,14 @@ hipError_t launch_write_tokens(int k_bits, const void* k_new, const void* v_new,
   dim3 grid1(max_new / kTile + 1, batch, num_kv_heads * 2), block(kThreads);
   const auto* kn = static_cast<const __half*>(k_new);
   const auto* vn = static_cast<const __half*>(v_new);
-  if (k_bits == 4)
-    hipLaunchKernelGGL(write_tiles_kernel<4>, grid1, block, 0, stream, kn, vn, total_new, cu_new,
-                       max_new, num_kv_heads, seq_lens, static_cast<const __half*>(k_tail),
+  const hipError_t e = with_preset(k_bits, v_bits, [&](auto kb, auto vb) {
+    hipLaunchKernelGGL((write_tiles_kernel<decltype(kb)::value, decltype(vb)::value>), grid1,
+                       block, 0, stream, kn, vn, total_new, cu_new, max_new, num_kv_heads,
+                       seq_lens, static_cast<const __half*>(k_tail),
                        static_cast<const __half*>(v_tail), block_table, bt_stride,
                        static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool),
                        pool_num_pages, n_iters);
-  else
-    hipLaunchKernelGGL(write_tiles_kernel<2>, grid1, block, 0, stream, kn, vn, total_new, cu_new,
-                       max_new, num_kv_heads, seq_lens, static_cast<const __half*>(k_tail),
-                       static_cast<const __half*>(v_tail), block_table, bt_stride,
-                       static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool),
-                       pool_num_pages, n_iters);
-  const hipError_t e = hipGetLastError();
+  });
   if (e != hipSuccess) return e;
   dim3 grid2(batch, num_kv_heads, 2);
   hipLaunchKernelGGL(write_staging_kernel, grid2, block, 0, stream, kn, vn, total_new, cu_new,
@@ -909,11 +925,11 @@ hipError_t launch_write_tokens(int k_bits, const void* k_new, const void* v_new,
   return hipGetLastError();
 }
 
-hipError_t launch_append_tokens(int k_bits, const void* k_new, const void* v_new, int32_t batch,
-                                int32_t num_kv_heads, const int32_t* seq_lens, void* k_tail,
-                                void* v_tail, const int32_t* block_table, int32_t bt_stride,
-                                void* k_pool, void* v_pool, int64_t pool_num_pages, int n_iters,
-                                hipStream_t stream) {
+hipError_t launch_append_tokens(int k_bits, int v_bits, const void* k_new, const void* v_new,
+                                int32_t batch, int32_t num_kv_heads, const int32_t* seq_lens,
+                                void* k_tail, void* v_tail, const int32_t* block_table,
+                                int32_t bt_stride, void* k_pool, void* v_pool,
+                                int64_t pool_num_pages, int n_iters, hipStream_t stream) {
   dim3 grid(batch, num_kv_heads, 2), block(kThreads);
   const auto* kn = static_cast<const __half*>(k_new);
   const auto* vn = static_cast<const __half*>(v_new);
@@ -921,13 +937,11 @@ hipError_t launch_append_tokens(int k_bits, const void* k_new, const void* v_new
   auto* vt = static_cast<__half*>(v_tail);
   auto* kp = static_cast<uint8_t*>(k_pool);
   auto* vp = static_cast<uint8_t*>(v_pool);
-  if (k_bits == 4)
-    hipLaunchKernelGGL(append_tokens_kernel<4>, grid, block, 0, stream, kn, vn, num_kv_heads,
-                       seq_lens, kt, vt, block_table, bt_stride, kp, vp, pool_num_pages, n_iters);
-  else
-    hipLaunchKernelGGL(append_tokens_kernel<2>, grid, block, 0, stream, kn, vn, num_kv_heads,
-                       seq_lens, kt, vt, block_table, bt_stride, kp, vp, pool_num_pages, n_iters);
-  return hipGetLastError();
+  return with_preset(k_bits, v_bits, [&](auto kb, auto vb) {
+    hipLaunchKernelGGL((append_tokens_kernel<decltype(kb)::value, decltype(vb)::value>), grid,
+                       block, 0, stream, kn, vn, num_kv_heads, seq_lens, kt, vt, block_table,
+                       bt_stride, kp, vp, pool_num_pages, n_iters);
+  });
 }
 
 }  // namespace kvarn

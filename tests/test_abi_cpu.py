@@ -42,7 +42,9 @@ def test_params_from_dtype():
         assert K.lib.kvarn_params_from_dtype(bad.encode(), 8, ctypes.byref(out)) == INVALID, bad
     p2 = K.params_from_dtype("kvarn_k2v2_g128", 4)
     assert (p2.k_bits, p2.v_bits, p2.group, p2.sinkhorn_iters) == (2, 2, 128, 4)
-    for unsup in ("kvarn_k4v4_g128", "kvarn_k3v2_g128", "kvarn_k2v4_g128", "kvarn_k4v2_g64"):
+    p4 = K.params_from_dtype("kvarn_k4v4_g128", 8)
+    assert (p4.k_bits, p4.v_bits, p4.group) == (4, 4, 128)
+    for unsup in ("kvarn_k3v2_g128", "kvarn_k2v4_g128", "kvarn_k4v3_g128", "kvarn_k4v2_g64"):
         assert K.lib.kvarn_params_from_dtype(unsup.encode(), 8, ctypes.byref(out)) == UNSUP, unsup
     assert K.lib.kvarn_params_from_dtype(b"kvarn_k4v2_g128", -1, ctypes.byref(out)) == INVALID
     assert K.lib.kvarn_params_from_dtype(b"kvarn_k4v2_g128", 65, ctypes.byref(out)) == INVALID
@@ -57,6 +59,8 @@ def test_page_bytes():
     assert K.page_bytes(p, 7) == 0
     p2 = K.params_from_dtype("kvarn_k2v2_g128")
     assert K.page_bytes(p2, K.KIND_K) == 5120 and K.page_bytes(p2, K.KIND_V) == 5120
+    p4 = K.params_from_dtype("kvarn_k4v4_g128")
+    assert K.page_bytes(p4, K.KIND_K) == 9216 and K.page_bytes(p4, K.KIND_V) == 9216
     bad = K.Params(128, 64, 4, 2, 128, 8)
     assert K.lib.kvarn_params_check(ctypes.byref(bad)) == UNSUP
     assert K.page_bytes(bad, K.KIND_K) == 0
@@ -83,7 +87,7 @@ def test_quantize_validation():
     assert _quant(p, ts=1023) == INVALID              # stride not a multiple of 8
     assert _quant(p, src=ctypes.c_void_p(0x10008)) == INVALID   # misaligned
     assert _quant(p, ntok=-1) == INVALID
-    bad = K.Params(128, 128, 4, 4, 128, 8)
+    bad = K.Params(128, 128, 2, 4, 128, 8)
     assert _quant(bad) == UNSUP
     assert K.lib.kvarn_quantize_tiles(None, 0, FAKE, 8, 8, 1, FAKE, FAKE, 1, 1, FAKE, 1, None) == INVALID
 
@@ -110,7 +114,7 @@ def test_quantize_kv_validation():
     assert _quant_kv(p, vsrc=ctypes.c_void_p(0x10004)) == INVALID
     assert _quant_kv(p, kpool=ctypes.c_void_p(0x10008)) == INVALID
     assert _quant_kv(p, npages=-1) == INVALID
-    assert _quant_kv(K.Params(128, 128, 4, 4, 128, 8)) == UNSUP
+    assert _quant_kv(K.Params(128, 128, 2, 4, 128, 8)) == UNSUP
 
 
 def _dequant(p, **kw):
@@ -130,7 +134,7 @@ def test_dequantize_validation():
     assert _dequant(p, hkv=0) == INVALID
     assert _dequant(p, npages=-2) == INVALID
     assert _dequant(p, dst=ctypes.c_void_p(0x10002)) == INVALID
-    assert _dequant(K.Params(128, 128, 4, 4, 128, 8)) == UNSUP
+    assert _dequant(K.Params(128, 128, 2, 4, 128, 8)) == UNSUP
 
 
 def _write(p, **kw):
@@ -158,7 +162,7 @@ def test_write_tokens_validation():
     assert _write(p, kn=ctypes.c_void_p(0x10004)) == INVALID
     assert _write(p, vp=ctypes.c_void_p(0x10008)) == INVALID
     assert _write(p, npages=-1) == INVALID
-    assert _write(K.Params(128, 128, 4, 4, 128, 8)) == UNSUP
+    assert _write(K.Params(128, 128, 2, 4, 128, 8)) == UNSUP
 
 
 def _decode(p, **kw):

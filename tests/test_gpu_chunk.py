@@ -59,7 +59,8 @@ def _reference_rows(q, cu_q, kp, vp, bt, kt, vt, sl, G, rows_to_check):
                 pages = [int(p) for p in bt_h[b, :C // 128]]
                 ks = [O.dequantize_k_record(x, T.key_bits_of(kp))
                       for x in T.records_of(kp, pages, g)] if pages else []
-                vs = [O.dequantize_v_record(x) for x in T.records_of(vp, pages, g)] if pages else []
+                vs = [O.dequantize_v_record(x, T.value_bits_of(vp))
+                      for x in T.records_of(vp, pages, g)] if pages else []
                 deq[(b, g)] = (ks, vs)
             ks, vs = deq[(b, g)]
             nf, rem = L // 128, L % 128

@@ -29,7 +29,7 @@ def say(*a):
 @pytest.mark.parametrize("n_iters", [0, 1, 8])
 def test_k2_quantize_against_oracle(K, n_iters):
     n, hkv = 12, 3
-    tiles = synth.tile_batch(n * hkv, "cpu", seed=60 + n_iters)
+    tiles, kinds = synth.tile_batch(n * hkv, "cpu", seed=60 + n_iters, return_kinds=True)
     src = tiles.view(n, hkv, 128, 128).permute(0, 2, 1, 3).reshape(n * 128, hkv, 128).contiguous()
     tok = torch.arange(n, dtype=torch.int64) * 128
     page = torch.randperm(n, generator=torch.Generator().manual_seed(61)).to(torch.int32)
@@ -44,7 +44,10 @@ def test_k2_quantize_against_oracle(K, n_iters):
         st = T.QuantStats()
         for h in range(hkv):
             recs = T.records_of(pool, page.tolist(), h)
-            T.check_quantized_tiles(x16[:, h], recs, kind, n_iters, st, k_bits=2)
+            # offset-dominated tiles make the normalization ill-conditioned: weaker check
+            ill = [i for i in range(n) if kinds[i * hkv + h] == synth.OFFSET_TILE_KIND]
+            T.check_quantized_tiles(x16[:, h], recs, kind, n_iters, st, ill_conditioned=ill,
+                                    k_bits=2)
         say(f"k2v2 N={n_iters} kind={kind}: {st}")
         T.assert_rate(st)
 

@@ -7,8 +7,10 @@
  * orthonormal Hadamard matrix, normalized by an iterative log-space Sinkhorn-style
  * alternation of column-std and row-std normalization, then quantized by asymmetric
  * round-to-nearest, keys 4-bit with scales per channel, values 2-bit with scales per token
- * (preset "kvarn_k4v2_g128", README "Quick start"; 128 = tile / page size). The preset
- * "kvarn_k2v2_g128" (2-bit keys; the pages report 2-bit results) is also implemented.
+ * (preset "kvarn_k4v2_g128", README "Quick start"; 128 = tile / page size). The presets
+ * "kvarn_k2v2_g128" (2-bit keys; the pages report 2-bit results) and "kvarn_k4v4_g128"
+ * (4-bit values; another key / value width choice of the same naming, README "How KVarN
+ * works", the preset paragraph) are also implemented.
  * The read path is decode attention that dequantizes the tiles on the fly: the query is
  * rotated by H for QK and the accumulated values are rotated back by H^T.
  *
@@ -56,9 +58,9 @@ typedef enum {
 
 typedef enum { KVARN_K = 0, KVARN_V = 1 } kvarn_kind;
 
-/* Quantizer parameters. Only head_dim = tile_tokens = group = 128, k_bits = 4 or 2,
- * v_bits = 2 are implemented (README "Quick start": other page sizes are not yet
- * supported). sinkhorn_iters is the number of (column step, row step) pairs of the
+/* Quantizer parameters. Only head_dim = tile_tokens = group = 128 with (k_bits, v_bits)
+ * = (4, 2), (2, 2) or (4, 4) are implemented (README "Quick start": other page sizes are
+ * not yet supported). sinkhorn_iters is the number of (column step, row step) pairs of the
  * normalization (README "How KVarN works", stage 3); 0..64 accepted. */
 typedef struct {
     int32_t head_dim;
@@ -79,7 +81,8 @@ KVARN_API const char* kvarn_status_str(kvarn_status status);
 /* Parse a kv-cache dtype string of the form "kvarn_k<kb>v<vb>_g<group>" (README "Quick
  * start": kv_cache_dtype="kvarn_k4v2_g128") into params, with the given iteration count.
  * Returns INVALID_ARG for a malformed string or NULL pointer, UNSUPPORTED for a well-formed
- * preset other than k4v2_g128 and k2v2_g128. `out_host` is written only on success. */
+ * preset other than k4v2_g128, k2v2_g128 and k4v4_g128. `out_host` is written only on
+ * success. */
 KVARN_API kvarn_status kvarn_params_from_dtype(const char* kv_cache_dtype, int32_t sinkhorn_iters,
                                      kvarn_params* out_host);
 
@@ -87,7 +90,7 @@ KVARN_API kvarn_status kvarn_params_from_dtype(const char* kv_cache_dtype, int32
 KVARN_API kvarn_status kvarn_params_check(const kvarn_params* params);
 
 /* Bytes of one page record (one 128-token tile of one KV head) of the given kind:
- * 9216 for 4-bit keys, 5120 for 2-bit keys and for values; 0 if params are invalid or
+ * 9216 for 4-bit keys or values, 5120 for 2-bit keys or values; 0 if params are invalid or
  * unsupported. Every pool passed with these params must use this record size.
  *
  * Page format v1 (little-endian):
@@ -102,6 +105,10 @@ KVARN_API kvarn_status kvarn_params_check(const kvarn_params* params);
  *     owns bytes [32t, 32t+32) as 8 32-bit words; word w = 2g + d holds channels
  *     16w .. 16w+15, crumb p (bits 2p..2p+1) holding channel 32g + 8(2d + p mod 8 / 4)
  *     + 2 (p mod 4) + p / 8.
+ *   4-bit V record (v_bits = 4): bytes [0, 8192) are 4-bit codes, channel-major: channel c
+ *     owns the 16 words 16c + 4g + m (g = 0..3, m = 0..3); nibble q (bits 4q..4q+3) of word
+ *     (c, g, m) holds token 32 m + (j < 4 ? 4g + j : 12 + 4g + j), j = 2 (q mod 4) + q / 4
+ *     (the 2-bit V record's token order, one nibble per code).
  *   All then hold four float16[128] vectors: r (per-channel normalizer), s (per-token
  *   normalizer), scale and zero (per channel for K, per token for V).
  *   A tile X (channels x tokens, rotated Xr = H X) is recovered as

@@ -399,50 +399,7 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
   // Each lane keeps the 16 channels whose B-operand entries it builds:
   // qo[4 s + j] = channel 32 gq + 8 s + 2 side + j.
   float qo[16];
-  float maxq;
-  {
-    float qr[32];
-    const __half* qrow = q + (int64_t(b) * num_q_heads + int64_t(g) * G + (head_ok ? h : 0)) * kDim + 32 * gq;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) load_h8(reinterpret_cast<const uint8_t*>(qrow + 8 * k), &qr[8 * k]);
-    if (!head_ok) {
-#pragma unroll
-      for (int j = 0; j < 32; ++j) qr[j] = 0.f;
-    }
-#pragma unroll
-    for (int hb = 1; hb < 32; hb <<= 1) {
-#pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        if ((j & hb) == 0) {
-          const float a = qr[j], c = qr[j + hb];
-          qr[j] = a + c;
-          qr[j + hb] = a - c;
-        }
-      }
-    }
-    const bool up16 = (gq & 1) != 0, up32 = (gq & 2) != 0;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const float p = swz_xor_f<16>(qr[j]);
-      qr[j] = up16 ? (p - qr[j]) : (qr[j] + p);
-    }
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const float p = shfl_xor32_f(qr[j]);
-      qr[j] = up32 ? (p - qr[j]) : (qr[j] + p);
-    }
-    float mq = 0.f;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      qr[j] *= qscale;  // includes 1/sqrt(128) of H
-      mq = fmaxf(mq, fabsf(qr[j]));
-    }
-    maxq = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max(mq))));
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) qo[4 * s + j] = hi ? qr[8 * s + j] : qr[8 * s + 4 + j];
-  }
+  float maxq;   // computed below, once the first page loads are issued
 
   float m_run = -INFINITY, l_part = 0.f;
   float acc[8][4];
@@ -681,6 +638,50 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
   load_meta(t, krec_of(cur), vrec_of(cur), lo);
   load_kcodes(t, krec_of(cur), lo);
   load_vcodes(t, vrec_of(cur), lo);
+  // q is rotated while the first page's loads are in flight
+  {
+    float qr[32];
+    const __half* qrow = q + (int64_t(b) * num_q_heads + int64_t(g) * G + (head_ok ? h : 0)) * kDim + 32 * gq;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) load_h8(reinterpret_cast<const uint8_t*>(qrow + 8 * k), &qr[8 * k]);
+    if (!head_ok) {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) qr[j] = 0.f;
+    }
+#pragma unroll
+    for (int hb = 1; hb < 32; hb <<= 1) {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        if ((j & hb) == 0) {
+          const float a = qr[j], c = qr[j + hb];
+          qr[j] = a + c;
+          qr[j + hb] = a - c;
+        }
+      }
+    }
+    const bool up16 = (gq & 1) != 0, up32 = (gq & 2) != 0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const float p = swz_xor_f<16>(qr[j]);
+      qr[j] = up16 ? (p - qr[j]) : (qr[j] + p);
+    }
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const float p = shfl_xor32_f(qr[j]);
+      qr[j] = up32 ? (p - qr[j]) : (qr[j] + p);
+    }
+    float mq = 0.f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      qr[j] *= qscale;  // includes 1/sqrt(128) of H
+      mq = fmaxf(mq, fabsf(qr[j]));
+    }
+    maxq = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max(mq))));
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) qo[4 * s + j] = hi ? qr[8 * s + j] : qr[8 * s + 4 + j];
+  }
   // pages of this wave: slots wslot, wslot + 4, ... below n_full, at most tpw of them
   // (a loop with one exit keeps the running state in place across iterations)
   const int n_here = wslot < n_full ? min(tpw, (n_full - wslot + 3) >> 2) : 0;

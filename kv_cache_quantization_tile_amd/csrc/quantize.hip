@@ -290,7 +290,8 @@ __device__ __forceinline__ void rotate_tile_mfma(RowPtr row_ptr, int w, int l, f
 // The tile quantizer proper. row_ptr(t) gives the 16-byte aligned address of token t's
 // 128 channels. Writes one record at `rec`; BITS is the code width of this kind.
 template <int KIND, int BITS, typename RowPtr>
-__device__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_iters, QuantSmem& sm) {
+__device__ __forceinline__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_iters,
+                                              QuantSmem& sm) {
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63;
   const int cb = l & 15;

@@ -147,8 +147,11 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kBufferFlags = 0x00020000;   // raw (untyped) 32-bit data
 // Page records are read once per decode step: nontemporal loads (cache policy bit nt) keep
-// them from displacing reused lines (measured: 0.85 vs 0.75 of HBM peak for this pattern)
+// them from displacing reused lines (measured: 0.85 vs 0.75 of HBM peak for this pattern).
+// The multi-query read re-reads every page once per query row: there the loads are plain
+// (kReuseLoad), so that the rows that follow find the page in L2.
 constexpr int kStreamLoad = 2;
+constexpr int kReuseLoad = 0;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t record_rsrc(const uint8_t* rec, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(rec), (short)0, bytes, kBufferFlags);
@@ -158,39 +161,39 @@ struct LaneOffsets {
   uint32_t k, v, m;   // key codes, value codes, metadata
 };
 
-template <int KB, int VB>
+template <int AUX, int KB, int VB>
 __device__ __forceinline__ void load_meta(PageRegs<KB, VB>& t, __amdgpu_buffer_rsrc_t kr,
                                           __amdgpu_buffer_rsrc_t vr, const LaneOffsets& o) {
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
-    t.km[a] = __builtin_amdgcn_raw_buffer_load_b32(kr, o.m, KeyRec<KB>::kCodeBytes + 256 * a, kStreamLoad);
-    t.vm[a] = __builtin_amdgcn_raw_buffer_load_b32(vr, o.m, ValRec<VB>::kCodeBytes + 256 * a, kStreamLoad);
+    t.km[a] = __builtin_amdgcn_raw_buffer_load_b32(kr, o.m, KeyRec<KB>::kCodeBytes + 256 * a, AUX);
+    t.vm[a] = __builtin_amdgcn_raw_buffer_load_b32(vr, o.m, ValRec<VB>::kCodeBytes + 256 * a, AUX);
   }
 }
-template <int KB, int VB>
+template <int AUX, int KB, int VB>
 __device__ __forceinline__ void load_kcodes(PageRegs<KB, VB>& t, __amdgpu_buffer_rsrc_t kr,
                                             const LaneOffsets& o) {
 #pragma unroll
   for (int tb = 0; tb < 8; ++tb) {
     if constexpr (KB == 4) {
-      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(kr, o.k, 1024 * tb, kStreamLoad);
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(kr, o.k, 1024 * tb, AUX);
       t.kc[tb] = make_uint4(v.x, v.y, v.z, v.w);
     } else {   // 32 bytes per token: the value records' lane offsets
-      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(kr, o.v, 512 * tb, kStreamLoad);
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(kr, o.v, 512 * tb, AUX);
       t.kc[tb] = make_uint2(v.x, v.y);
     }
   }
 }
-template <int KB, int VB>
+template <int AUX, int KB, int VB>
 __device__ __forceinline__ void load_vcodes(PageRegs<KB, VB>& t, __amdgpu_buffer_rsrc_t vr,
                                             const LaneOffsets& o) {
 #pragma unroll
   for (int bb = 0; bb < 8; ++bb) {
     if constexpr (VB == 2) {
-      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(vr, o.v, 512 * bb, kStreamLoad);
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(vr, o.v, 512 * bb, AUX);
       t.vc[bb] = make_uint2(v.x, v.y);
     } else {   // 64 bytes per channel: the 4-bit key records' lane offsets
-      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(vr, o.k, 1024 * bb, kStreamLoad);
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(vr, o.k, 1024 * bb, AUX);
       t.vc[bb] = make_uint4(v.x, v.y, v.z, v.w);
     }
   }
@@ -357,11 +360,17 @@ __device__ void tail_partial(const __half* __restrict__ q, int32_t num_q_heads,
   }
 }
 
-// One workgroup: (split, KV head g, output row). Wave w handles page slots
+// One workgroup: (output row, KV head g, split) = (blockIdx.x, y, z). Wave w handles page slots
 // split * 4 * tpw + w + 4 k, k < tpw. Writes one partial (m, l, acc) per query head. With
 // tail buffers the grid has one more split, n_splits, which computes the tail partial. The
-// row's sequence, page slots and tail follow row_geometry. KB, VB: key and value code widths.
-template <int KB, int VB>
+// row's sequence, page slots and tail follow row_geometry. KB, VB: key and value code widths;
+// AUX: cache policy of the page loads.
+// RW (multi-row layout, for many query rows): workgroup z holds output rows 4z .. 4z+3 of the
+// n_rows, one per wave; each wave walks page slots split * 4 * tpw + k, k < 4 * tpw, of its own
+// row and writes its own partials (no combine across waves). Rows of one sequence share
+// their pages, so the four waves read each page within a short window and three of the four
+// reads hit L2. The tail split handles the tails of the four rows in turn.
+template <int KB, int VB, int AUX, bool RW>
 __global__ void __launch_bounds__(kThreads)
 decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t num_kv_heads,
                     const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
@@ -370,21 +379,38 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
                     const int32_t* __restrict__ cu_q, int32_t batch, float qscale, int32_t tpw,
                     int32_t n_splits, int32_t split_base, const __half* __restrict__ k_tail,
                     const __half* __restrict__ v_tail, float tail_qscale,
-                    float* __restrict__ ws) {
+                    float* __restrict__ ws, int32_t n_rows) {
   __shared__ DecodeSmem sm;
-  const int split = split_base + blockIdx.x, g = blockIdx.y, b = blockIdx.z;   // b: output row
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int split = split_base + blockIdx.z, g = blockIdx.y;
+  // output row: the workgroup's, or in the multi-row layout this wave's
+  const int b = RW ? __builtin_amdgcn_readfirstlane(4 * int(blockIdx.x) + w) : int(blockIdx.x);
   const int G = num_q_heads / num_kv_heads;
-  const RowGeom rg = row_geometry(b, seq_lens, max_seq_len, cu_q, batch);
   if (split == n_splits) {   // the extra split (launched only with tail buffers): the tail
-    tail_partial(q, num_q_heads, num_kv_heads, k_tail, v_tail, b, rg.b, g, rg.tail_len,
-                 tail_qscale, n_splits, ws, reinterpret_cast<float (*)[kTile]>(&sm.acc[0][0][0]));
+    float (*p_sm)[kTile] = reinterpret_cast<float (*)[kTile]>(&sm.acc[0][0][0]);
+    if constexpr (RW) {
+      for (int rr = 0; rr < 4; ++rr) {   // uniform over the workgroup
+        const int row = 4 * int(blockIdx.x) + rr;
+        if (row >= n_rows) break;
+        const RowGeom rgr = row_geometry(row, seq_lens, max_seq_len, cu_q, batch);
+        tail_partial(q, num_q_heads, num_kv_heads, k_tail, v_tail, row, rgr.b, g, rgr.tail_len,
+                     tail_qscale, n_splits, ws, p_sm);
+        __syncthreads();
+      }
+    } else {
+      const RowGeom rgt = row_geometry(b, seq_lens, max_seq_len, cu_q, batch);
+      tail_partial(q, num_q_heads, num_kv_heads, k_tail, v_tail, b, rgt.b, g, rgt.tail_len,
+                   tail_qscale, n_splits, ws, p_sm);
+    }
     return;
   }
+  // (the multi-row layout has no workgroup barrier past this point: waves leave on their own)
+  if (RW && b >= n_rows) return;
+  const RowGeom rg = row_geometry(b, seq_lens, max_seq_len, cu_q, batch);
   const int n_full = rg.n_slots;      // page slots of this row (the last may be masked)
   const int slot0 = split * 4 * tpw;
   if (slot0 >= n_full) return;
 
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int n = l & 15, gq = l >> 4;
   const int h = n & 7;
   const bool hi = n < 8;
@@ -474,7 +500,7 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
           make_float2(fmaf(vs * sv0, lo_h(t.vm[3]), -p0), fmaf(vs * sv1, hi_h(t.vm[3]), -p1));
       reinterpret_cast<float2*>(wm.vr)[l] = make_float2(lo_h(t.vm[0]) * ivs, hi_h(t.vm[0]) * ivs);
     }
-    load_meta(t, krec_of(next), vrec_of(next), lo);
+    load_meta<AUX>(t, krec_of(next), vrec_of(next), lo);
     // LDS operations of one wave complete in order: the writes above land before the reads
     // below, and after the previous page's reads
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -540,7 +566,7 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
         }
       }
     }
-    load_kcodes(t, krec_of(next), lo);
+    load_kcodes<AUX>(t, krec_of(next), lo);
     if (lim < kTile) {   // a causally cut page: tokens from lim on do not count
 #pragma unroll
       for (int tb = 0; tb < 8; ++tb)
@@ -629,15 +655,17 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
       acc[bb][2] = fmaf(rv.z, c[2], acc[bb][2]);
       acc[bb][3] = fmaf(rv.w, c[3], acc[bb][3]);
     }
-    load_vcodes(t, vrec_of(next), lo);
+    load_vcodes<AUX>(t, vrec_of(next), lo);
   };
 
   PageRegs<KB, VB> t;
-  const int wslot = __builtin_amdgcn_readfirstlane(slot0 + w);   // this wave's first slot
+  // this wave's first slot and slot step
+  const int wslot = __builtin_amdgcn_readfirstlane(RW ? slot0 : slot0 + w);
+  constexpr int kSlotStep = RW ? 1 : 4;
   int64_t cur = page_of(wslot);
-  load_meta(t, krec_of(cur), vrec_of(cur), lo);
-  load_kcodes(t, krec_of(cur), lo);
-  load_vcodes(t, vrec_of(cur), lo);
+  load_meta<AUX>(t, krec_of(cur), vrec_of(cur), lo);
+  load_kcodes<AUX>(t, krec_of(cur), lo);
+  load_vcodes<AUX>(t, vrec_of(cur), lo);
   // q is rotated while the first page's loads are in flight
   {
     float qr[32];
@@ -682,12 +710,14 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
 #pragma unroll
       for (int j = 0; j < 4; ++j) qo[4 * s + j] = hi ? qr[8 * s + j] : qr[8 * s + 4 + j];
   }
-  // pages of this wave: slots wslot, wslot + 4, ... below n_full, at most tpw of them
-  // (a loop with one exit keeps the running state in place across iterations)
-  const int n_here = wslot < n_full ? min(tpw, (n_full - wslot + 3) >> 2) : 0;
+  // pages of this wave: slots wslot, wslot + step, ... below n_full, at most tpw of them
+  // (4 tpw consecutive slots in the multi-row layout); a loop with one exit keeps the
+  // running state in place across iterations
+  const int n_here = RW ? min(4 * tpw, n_full - wslot)
+                        : (wslot < n_full ? min(tpw, (n_full - wslot + 3) >> 2) : 0);
   for (int k = 0; k < n_here; ++k) {
-    const int64_t next = k + 1 < n_here ? page_of(wslot + 4 * (k + 1)) : -1;
-    process(t, next, cur >= 0, wslot + 4 * k == n_full - 1 ? rg.mask_lim : kTile);
+    const int64_t next = k + 1 < n_here ? page_of(wslot + kSlotStep * (k + 1)) : -1;
+    process(t, next, cur >= 0, wslot + kSlotStep * k == n_full - 1 ? rg.mask_lim : kTile);
     cur = next;
   }
 
@@ -707,6 +737,21 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
     for (int bb = 0; bb < 8; ++bb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) sm.acc[w][h][16 * bb + 4 * gq + i] = acc[bb][i];
+  }
+  if constexpr (RW) {   // this wave's own row: its partials as they stand
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int hh = 0; hh < G; ++hh) {
+      float* part = ws + ((int64_t(b) * num_q_heads + int64_t(g) * G + hh) * (n_splits + 1) + split) * kPartStride;
+      *reinterpret_cast<float2*>(part + 4 + 2 * l) =
+          *reinterpret_cast<const float2*>(&sm.acc[w][hh][2 * l]);
+      if (l == 0) {
+        part[0] = sm.m[w][hh];
+        part[1] = sm.l[w][hh];
+      }
+    }
+    return;
   }
   __syncthreads();
   {
@@ -864,20 +909,30 @@ hipError_t launch_decode(int k_bits, int v_bits, const void* q, int32_t rows,
   const float qscale = softmax_scale * kLog2e;
   float* ws = static_cast<float*>(workspace);
   const bool has_tail = k_tail != nullptr && v_tail != nullptr;
+  const bool multi_row = cu_q != nullptr && rows > batch;
   // page splits (only if a full page can exist) plus, with tail buffers, one tail split
   const int32_t grid_x = (max_seq_len >= kTile ? ns : 0) + (has_tail ? 1 : 0);
   if (grid_x > 0) {
     // without pages the only split launched is the tail, which must land on index ns
     const int32_t first = max_seq_len >= kTile ? 0 : ns;
     const hipError_t e = with_preset(k_bits, v_bits, [&](auto kb, auto vb) {
-      hipLaunchKernelGGL((decode_pages_kernel<decltype(kb)::value, decltype(vb)::value>),
-                         dim3(grid_x, num_kv_heads, rows), dim3(kThreads), 0, stream,
+      constexpr int KB = decltype(kb)::value, VB = decltype(vb)::value;
+      // decode streams every page once; the multi-query read (cu_q) re-reads them per row,
+      // and with more rows than sequences takes the multi-row layout (one row per wave)
+      auto kernel = !cu_q        ? decode_pages_kernel<KB, VB, kStreamLoad, false>
+                    : multi_row ? decode_pages_kernel<KB, VB, kReuseLoad, true>
+                                : decode_pages_kernel<KB, VB, kReuseLoad, false>;
+      // rows fastest, splits slowest: workgroups are dealt to the 8 XCDs round-robin in
+      // linear order, so consecutive ones must all carry work (a split axis of period 2,
+      // pages + tail, would leave every page workgroup on the even XCDs)
+      hipLaunchKernelGGL(kernel, dim3(multi_row ? (rows + 3) / 4 : rows, num_kv_heads, grid_x),
+                         dim3(kThreads), 0, stream,
                          static_cast<const __half*>(q), num_q_heads, num_kv_heads,
                          static_cast<const uint8_t*>(k_pool), static_cast<const uint8_t*>(v_pool),
                          pool_num_pages, block_table, bt_stride, seq_lens, max_seq_len, cu_q,
                          batch, qscale * kInvSqrt128, tpw, ns, first,
                          static_cast<const __half*>(k_tail), static_cast<const __half*>(v_tail),
-                         qscale, ws);
+                         qscale, ws, rows);
     });
     if (e != hipSuccess) return e;
   }

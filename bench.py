@@ -39,6 +39,7 @@ Q_READ = 128 * 128 * 2                 # float16 tile in
 HBM_PEAK_GBPS = 8000.0                 # MI355X HBM3E
 # fp32 FMA on the vector ALUs without packed-FP32 forms: 256 CU x 4 SIMD x 16 lanes x 2 x 2.4 GHz
 ALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+MFMA_F16_PEAK_TFLOPS = 2500.0          # MI355X dense float16 matrix cores
 
 
 def quant_flop_per_tile(n_iters: int) -> int:
@@ -329,6 +330,7 @@ def chunked_prefill(args, K, synth, params, dev):
     unique_kv = B * hkv * pages * (k_rec + v_rec)                      # each page once
     per_row_kv = sum(B * hkv * ((ctx + i + 1) // 128) * (k_rec + v_rec) for i in range(n))
     qo = 2 * B * n * hq * 128 * 2
+    attn_flops = sum(B * hq * 4 * 128 * (ctx + i + 1) for i in range(n))   # QK + PV, 2 FLOP/MAC
     value = (write_bytes + unique_kv + qo) / (ms_step * 1e-3) / 1e9
     res = {
         "metric": "decode-attn KV GB/s (% HBM roofline) + tiles quantized/s, k4v2_g128",
@@ -345,15 +347,18 @@ def chunked_prefill(args, K, synth, params, dev):
                             "page read once, q + out) / step time",
         "chunk_tokens_per_s": round(B * n / (ms_step * 1e-3), 1),
         "write_ms": round(w_ms, 5), "attention_ms": round(a_ms, 5),
-        "roofline": {"kernel": "decode_pages_kernel (one row per query position)", "bound": "hbm",
-                     "achieved": round(per_row_kv / (a_ms * 1e-3) / 1e9, 1),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(per_row_kv / (a_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        # many query rows per page: attention is a dense contraction, so the bound is the
+        # float16 matrix-core peak, priced on the attention's own FLOPs (QK and PV over each
+        # row's causal prefix); the page stream per row is reported beside it
+        "roofline": {"kernel": "decode_pages_kernel (one row per query position)", "bound": "mfma",
+                     "achieved": round(attn_flops / (a_ms * 1e-3) / 1e12, 2),
+                     "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_flops / (a_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
                      "traffic": None,
-                     "per_launch": f"{B * n} query rows x their causal prefix of pages x "
-                                   f"{k_rec + v_rec} B (re-reads of shared pages largely served "
-                                   "by L2 / Infinity Cache)",
-                     "launch_ms": round(a_ms, 5)},
+                     "per_launch": f"{B * n} query rows x {hq} heads x 4 x 128 FLOP per causal "
+                                   f"key = {attn_flops / 1e9:.1f} GFLOP",
+                     "launch_ms": round(a_ms, 5),
+                     "row_page_stream_gbps": round(per_row_kv / (a_ms * 1e-3) / 1e9, 1)},
         "wall_s_timed": round(t_wall, 4),
         "source_hash": source_hash(),
     }

@@ -298,7 +298,7 @@ def chunked_prefill(args, K, synth, params, dev):
     vt = torch.zeros_like(kt)
     q = torch.randn((B * n, hq, 128), generator=torch.Generator(device=dev).manual_seed(12),
                     device=dev).to(torch.float16)
-    ws = K.new_workspace(params, B * n, hq, hkv, ctx + n)
+    ws = K.new_chunk_workspace(params, B * n, hq, hkv, ctx + n)
     out = torch.empty_like(q)
     step = lambda: (K.write_tokens(params, kn, vn, cu, sl0, kt, vt, w.block_table, kp, vp, n),
                     K.chunk_attention(params, q, cu, kp, vp, w.block_table, sl1, ctx + n, kt, vt,

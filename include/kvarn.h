@@ -217,10 +217,12 @@ KVARN_API kvarn_status kvarn_write_tokens(const kvarn_params* params, const void
  * of the partial last tile from the staging tiles (ignored when k_tail_dev / v_tail_dev are
  * NULL). out_dev: float16 [total_q, num_q_heads, 128]. cu_q_dev: int32 [batch + 1],
  * non-decreasing, cu_q_dev[0] = 0, cu_q_dev[batch] = total_q.
- * Limits and other arguments as kvarn_decode_attention with total_q in place of batch
- * (workspace from kvarn_decode_workspace_bytes(params, total_q, ...)); total_q <= 65535
- * (UNSUPPORTED above). Each query row costs one decode row: pages shared by the rows of a
- * sequence are re-read, mostly from the caches. */
+ * Limits and other arguments as kvarn_decode_attention with total_q in place of batch;
+ * workspace_dev: >= kvarn_chunk_workspace_bytes(params, total_q, ...) bytes; total_q <= 65535
+ * (UNSUPPORTED above). With one query row per sequence the read runs the decode kernels
+ * (bit-identical to kvarn_decode_attention); with more rows than sequences a wave holds 16
+ * query vectors (rows x heads of one sequence and KV head) and streams each page once for
+ * all of them. */
 KVARN_API kvarn_status kvarn_chunk_attention(const kvarn_params* params, const void* q_dev,
                                    int32_t total_q, const int32_t* cu_q_dev, int32_t batch,
                                    int32_t num_q_heads, int32_t num_kv_heads,
@@ -249,6 +251,11 @@ KVARN_API kvarn_status kvarn_dequantize_tiles(const kvarn_params* params, kvarn_
 KVARN_API size_t kvarn_decode_workspace_bytes(const kvarn_params* params, int32_t batch,
                                     int32_t num_q_heads, int32_t num_kv_heads,
                                     int32_t max_seq_len);
+
+/* Workspace bytes kvarn_chunk_attention needs for total_q query rows (0 if invalid). */
+KVARN_API size_t kvarn_chunk_workspace_bytes(const kvarn_params* params, int32_t total_q,
+                                   int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t max_seq_len);
 
 /* Number of key splits the decode uses for this shape (0 if invalid); informative. */
 KVARN_API int32_t kvarn_decode_num_splits(const kvarn_params* params, int32_t batch,

@@ -216,6 +216,16 @@ size_t kvarn_decode_workspace_bytes(const kvarn_params* params, int32_t batch, i
   return kvarn::decode_workspace_bytes(batch, num_q_heads, num_kv_heads, max_seq_len);
 }
 
+size_t kvarn_chunk_workspace_bytes(const kvarn_params* params, int32_t total_q,
+                                   int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t max_seq_len) {
+  if (kvarn_params_check(params) != KVARN_OK) return 0;
+  if (total_q <= 0 || total_q > 65535 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      max_seq_len < 0 || num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > kMaxGroup)
+    return 0;
+  return kvarn::chunk_workspace_bytes(total_q, num_q_heads, num_kv_heads, max_seq_len);
+}
+
 int32_t kvarn_decode_num_splits(const kvarn_params* params, int32_t batch, int32_t num_kv_heads,
                                 int32_t max_seq_len) {
   if (kvarn_params_check(params) != KVARN_OK) return 0;
@@ -288,7 +298,7 @@ kvarn_status kvarn_chunk_attention(const kvarn_params* params, const void* q, in
   }
   if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return KVARN_ERR_INVALID_ARG;
   if (k_tail && (!aligned16(k_tail) || !aligned16(v_tail))) return KVARN_ERR_INVALID_ARG;
-  if (workspace_bytes < kvarn::decode_workspace_bytes(total_q, num_q_heads, num_kv_heads, max_seq_len))
+  if (workspace_bytes < kvarn::chunk_workspace_bytes(total_q, num_q_heads, num_kv_heads, max_seq_len))
     return KVARN_ERR_WORKSPACE;
   return launch_status(kvarn::launch_decode(
       params->k_bits, params->v_bits, q, total_q, num_q_heads, num_kv_heads, k_pool, v_pool, pool_num_pages, block_table,

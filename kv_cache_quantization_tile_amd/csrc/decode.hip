@@ -241,6 +241,35 @@ __device__ __forceinline__ uint32_t swap8_into(uint32_t old, uint32_t src) {
 constexpr int kHiBanks = 0x3;   // lanes 0..7 of a row: high-part columns
 constexpr int kLoBanks = 0xC;   // lanes 8..15: low-part columns
 
+// Page factors of the record pair held in t, for the B operands, into this wave's LDS slot
+// (lane l: channels and tokens 2l, 2l + 1). fk, fv: the lane's unpack factors 2^(10 - b);
+// maxq: the wave's largest |q_rot| (sets the power of two ks that keeps the QK B operand
+// below 2^14; vs does the same for the PV one).
+template <int KB, int VB>
+__device__ __forceinline__ void page_factors(const PageRegs<KB, VB>& t, WaveMeta& wm, int l,
+                                             float maxq, float fk, float fv) {
+  const float rk0 = lo_h(t.km[0]), rk1 = hi_h(t.km[0]);
+  const float ka0 = rk0 * lo_h(t.km[2]) * fk, ka1 = rk1 * hi_h(t.km[2]) * fk;
+  const float sv0 = lo_h(t.vm[1]), sv1 = hi_h(t.vm[1]);
+  const float vp0 = sv0 * lo_h(t.vm[2]) * fv, vp1 = sv1 * hi_h(t.vm[2]) * fv;
+  const float mka = wave_max(fmaxf(ka0, ka1));
+  const float mvp = wave_max(fmaxf(vp0, vp1));
+  const int eks = pow2_norm_exp(maxq * __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mka))));
+  const int evs = pow2_norm_exp(__int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mvp))));
+  const float ks = __builtin_ldexpf(1.f, eks), iks = __builtin_ldexpf(1.f, -eks);
+  const float vs = __builtin_ldexpf(1.f, evs), ivs = __builtin_ldexpf(1.f, -evs);
+  const float a0 = ka0 * ks, a1 = ka1 * ks;
+  reinterpret_cast<float2*>(wm.ka)[l] = make_float2(a0, a1);
+  reinterpret_cast<float2*>(wm.kb)[l] =
+      make_float2(fmaf(ks * rk0, lo_h(t.km[3]), -a0), fmaf(ks * rk1, hi_h(t.km[3]), -a1));
+  wm.kt[l] = make_float2(lo_h(t.km[1]) * iks, hi_h(t.km[1]) * iks);
+  const float p0 = vp0 * vs, p1 = vp1 * vs;
+  wm.vp[l] = make_float2(p0, p1);
+  wm.vz[l] =
+      make_float2(fmaf(vs * sv0, lo_h(t.vm[3]), -p0), fmaf(vs * sv1, hi_h(t.vm[3]), -p1));
+  reinterpret_cast<float2*>(wm.vr)[l] = make_float2(lo_h(t.vm[0]) * ivs, hi_h(t.vm[0]) * ivs);
+}
+
 // What one output row attends to. Decode (cu_q == nullptr): row b is sequence b, attending
 // to its L = seq_lens[b] tokens: the full pages, then the L mod 128 staged tokens. Several
 // queries per sequence (cu_q != nullptr): rows cu_q[b] .. cu_q[b+1]-1 are the last
@@ -365,12 +394,7 @@ __device__ void tail_partial(const __half* __restrict__ q, int32_t num_q_heads,
 // tail buffers the grid has one more split, n_splits, which computes the tail partial. The
 // row's sequence, page slots and tail follow row_geometry. KB, VB: key and value code widths;
 // AUX: cache policy of the page loads.
-// RW (multi-row layout, for many query rows): workgroup z holds output rows 4z .. 4z+3 of the
-// n_rows, one per wave; each wave walks page slots split * 4 * tpw + k, k < 4 * tpw, of its own
-// row and writes its own partials (no combine across waves). Rows of one sequence share
-// their pages, so the four waves read each page within a short window and three of the four
-// reads hit L2. The tail split handles the tails of the four rows in turn.
-template <int KB, int VB, int AUX, bool RW>
+template <int KB, int VB, int AUX>
 __global__ void __launch_bounds__(kThreads)
 decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t num_kv_heads,
                     const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
@@ -379,34 +403,17 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
                     const int32_t* __restrict__ cu_q, int32_t batch, float qscale, int32_t tpw,
                     int32_t n_splits, int32_t split_base, const __half* __restrict__ k_tail,
                     const __half* __restrict__ v_tail, float tail_qscale,
-                    float* __restrict__ ws, int32_t n_rows) {
+                    float* __restrict__ ws) {
   __shared__ DecodeSmem sm;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int split = split_base + blockIdx.z, g = blockIdx.y;
-  // output row: the workgroup's, or in the multi-row layout this wave's
-  const int b = RW ? __builtin_amdgcn_readfirstlane(4 * int(blockIdx.x) + w) : int(blockIdx.x);
+  const int split = split_base + blockIdx.z, g = blockIdx.y, b = blockIdx.x;   // b: output row
   const int G = num_q_heads / num_kv_heads;
+  const RowGeom rg = row_geometry(b, seq_lens, max_seq_len, cu_q, batch);
   if (split == n_splits) {   // the extra split (launched only with tail buffers): the tail
-    float (*p_sm)[kTile] = reinterpret_cast<float (*)[kTile]>(&sm.acc[0][0][0]);
-    if constexpr (RW) {
-      for (int rr = 0; rr < 4; ++rr) {   // uniform over the workgroup
-        const int row = 4 * int(blockIdx.x) + rr;
-        if (row >= n_rows) break;
-        const RowGeom rgr = row_geometry(row, seq_lens, max_seq_len, cu_q, batch);
-        tail_partial(q, num_q_heads, num_kv_heads, k_tail, v_tail, row, rgr.b, g, rgr.tail_len,
-                     tail_qscale, n_splits, ws, p_sm);
-        __syncthreads();
-      }
-    } else {
-      const RowGeom rgt = row_geometry(b, seq_lens, max_seq_len, cu_q, batch);
-      tail_partial(q, num_q_heads, num_kv_heads, k_tail, v_tail, b, rgt.b, g, rgt.tail_len,
-                   tail_qscale, n_splits, ws, p_sm);
-    }
+    tail_partial(q, num_q_heads, num_kv_heads, k_tail, v_tail, b, rg.b, g, rg.tail_len,
+                 tail_qscale, n_splits, ws, reinterpret_cast<float (*)[kTile]>(&sm.acc[0][0][0]));
     return;
   }
-  // (the multi-row layout has no workgroup barrier past this point: waves leave on their own)
-  if (RW && b >= n_rows) return;
-  const RowGeom rg = row_geometry(b, seq_lens, max_seq_len, cu_q, batch);
   const int n_full = rg.n_slots;      // page slots of this row (the last may be masked)
   const int slot0 = split * 4 * tpw;
   if (slot0 >= n_full) return;
@@ -478,28 +485,7 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
   // maximum stays -inf and its weights exp2(s - inf) are 0.
   auto process = [&](PageRegs<KB, VB>& t, int64_t next, bool valid, int lim) {
     // ---- page factors into the wave's LDS slot ------------------------------------------
-    {
-      const float rk0 = lo_h(t.km[0]), rk1 = hi_h(t.km[0]);
-      const float ka0 = rk0 * lo_h(t.km[2]) * fk, ka1 = rk1 * hi_h(t.km[2]) * fk;
-      const float sv0 = lo_h(t.vm[1]), sv1 = hi_h(t.vm[1]);
-      const float vp0 = sv0 * lo_h(t.vm[2]) * fv, vp1 = sv1 * hi_h(t.vm[2]) * fv;
-      const float mka = wave_max(fmaxf(ka0, ka1));
-      const float mvp = wave_max(fmaxf(vp0, vp1));
-      const int eks = pow2_norm_exp(maxq * __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mka))));
-      const int evs = pow2_norm_exp(__int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mvp))));
-      const float ks = __builtin_ldexpf(1.f, eks), iks = __builtin_ldexpf(1.f, -eks);
-      const float vs = __builtin_ldexpf(1.f, evs), ivs = __builtin_ldexpf(1.f, -evs);
-      const float a0 = ka0 * ks, a1 = ka1 * ks;
-      reinterpret_cast<float2*>(wm.ka)[l] = make_float2(a0, a1);
-      reinterpret_cast<float2*>(wm.kb)[l] =
-          make_float2(fmaf(ks * rk0, lo_h(t.km[3]), -a0), fmaf(ks * rk1, hi_h(t.km[3]), -a1));
-      wm.kt[l] = make_float2(lo_h(t.km[1]) * iks, hi_h(t.km[1]) * iks);
-      const float p0 = vp0 * vs, p1 = vp1 * vs;
-      wm.vp[l] = make_float2(p0, p1);
-      wm.vz[l] =
-          make_float2(fmaf(vs * sv0, lo_h(t.vm[3]), -p0), fmaf(vs * sv1, hi_h(t.vm[3]), -p1));
-      reinterpret_cast<float2*>(wm.vr)[l] = make_float2(lo_h(t.vm[0]) * ivs, hi_h(t.vm[0]) * ivs);
-    }
+    page_factors(t, wm, l, maxq, fk, fv);
     load_meta<AUX>(t, krec_of(next), vrec_of(next), lo);
     // LDS operations of one wave complete in order: the writes above land before the reads
     // below, and after the previous page's reads
@@ -659,9 +645,7 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
   };
 
   PageRegs<KB, VB> t;
-  // this wave's first slot and slot step
-  const int wslot = __builtin_amdgcn_readfirstlane(RW ? slot0 : slot0 + w);
-  constexpr int kSlotStep = RW ? 1 : 4;
+  const int wslot = __builtin_amdgcn_readfirstlane(slot0 + w);   // this wave's first slot
   int64_t cur = page_of(wslot);
   load_meta<AUX>(t, krec_of(cur), vrec_of(cur), lo);
   load_kcodes<AUX>(t, krec_of(cur), lo);
@@ -710,14 +694,12 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
 #pragma unroll
       for (int j = 0; j < 4; ++j) qo[4 * s + j] = hi ? qr[8 * s + j] : qr[8 * s + 4 + j];
   }
-  // pages of this wave: slots wslot, wslot + step, ... below n_full, at most tpw of them
-  // (4 tpw consecutive slots in the multi-row layout); a loop with one exit keeps the
-  // running state in place across iterations
-  const int n_here = RW ? min(4 * tpw, n_full - wslot)
-                        : (wslot < n_full ? min(tpw, (n_full - wslot + 3) >> 2) : 0);
+  // pages of this wave: slots wslot, wslot + 4, ... below n_full, at most tpw of them
+  // (a loop with one exit keeps the running state in place across iterations)
+  const int n_here = wslot < n_full ? min(tpw, (n_full - wslot + 3) >> 2) : 0;
   for (int k = 0; k < n_here; ++k) {
-    const int64_t next = k + 1 < n_here ? page_of(wslot + kSlotStep * (k + 1)) : -1;
-    process(t, next, cur >= 0, wslot + kSlotStep * k == n_full - 1 ? rg.mask_lim : kTile);
+    const int64_t next = k + 1 < n_here ? page_of(wslot + 4 * (k + 1)) : -1;
+    process(t, next, cur >= 0, wslot + 4 * k == n_full - 1 ? rg.mask_lim : kTile);
     cur = next;
   }
 
@@ -737,21 +719,6 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
     for (int bb = 0; bb < 8; ++bb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) sm.acc[w][h][16 * bb + 4 * gq + i] = acc[bb][i];
-  }
-  if constexpr (RW) {   // this wave's own row: its partials as they stand
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    for (int hh = 0; hh < G; ++hh) {
-      float* part = ws + ((int64_t(b) * num_q_heads + int64_t(g) * G + hh) * (n_splits + 1) + split) * kPartStride;
-      *reinterpret_cast<float2*>(part + 4 + 2 * l) =
-          *reinterpret_cast<const float2*>(&sm.acc[w][hh][2 * l]);
-      if (l == 0) {
-        part[0] = sm.m[w][hh];
-        part[1] = sm.l[w][hh];
-      }
-    }
-    return;
   }
   __syncthreads();
   {
@@ -782,6 +749,366 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
         part[0] = M;
         part[1] = Lt;
       }
+    }
+  }
+}
+
+// ---- multi-query read ------------------------------------------------------------------
+//
+// Many query rows per sequence: a wave holds 16 query vectors of one sequence and KV head,
+// R = floor(16 / G) consecutive rows x the G heads of the group, one per MFMA column. The page
+// walk, the per-page factors and the code unpacking are shared by the 16 queries; each
+// query's own causal limit masks its scores. QK takes the key codes as the A operand and the
+// scaled queries as B (C: 16 tokens x 16 queries); the float16 high and low parts of B are two
+// MFMAs into the same accumulator, so the float32-level product needs no lane exchange. The
+// softmax weights of a C fragment pair are already the PV B operand (the value record's token
+// order), again as high + low parts; C of PV is 16 channels x 16 queries.
+//
+// Workgroups: the rows are cut into windows of 4R global row indices; workgroup j of the grid
+// is window m of sequence b with j = m + b (a window that two sequences share appears once per
+// sequence), found by a binary search over cu_q; wave w takes rows 4R m + R w .. + R - 1 of the
+// window that belong to sequence b. grid: (ceil(rows / 4R) + batch, KV heads, splits [+ tail]).
+
+struct MqSmem {
+  WaveMeta meta[4];
+  union {
+    float4 q[4][8][64];   // q_rot per wave: [k][lane] = channels 32 gq + 4k .. 4k + 3
+    float p[8][kTile];    // tail split: softmax weights of the staged tokens
+  };
+};
+
+struct MqWindow {
+  int b;          // sequence
+  int r0, r1;     // its rows in this window: r0 .. r1 - 1 (r1 <= r0: none)
+};
+
+__device__ __forceinline__ MqWindow mq_window(int j, int rows_per_window,
+                                              const int32_t* __restrict__ cu_q, int32_t batch,
+                                              int32_t n_rows) {
+  // the last b with floor(cu_q[b] / W) + b <= j
+  int lo = 0, hi = batch;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu_q[mid] / rows_per_window + mid <= j) lo = mid; else hi = mid;
+  }
+  MqWindow r;
+  r.b = lo;
+  const int m = j - lo;
+  const int64_t w0 = int64_t(m) * rows_per_window;
+  int64_t a = cu_q[lo], e = cu_q[lo + 1];
+  if (a < w0) a = w0;
+  if (e > w0 + rows_per_window) e = w0 + rows_per_window;
+  if (a < 0) a = 0;
+  if (e > n_rows) e = n_rows;
+  r.r0 = int(a);
+  r.r1 = int(e);
+  return r;
+}
+
+template <int KB, int VB>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+mq_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t num_kv_heads,
+                const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
+                int64_t pool_num_pages, const int32_t* __restrict__ block_table,
+                int32_t bt_stride, const int32_t* __restrict__ seq_lens, int32_t max_seq_len,
+                const int32_t* __restrict__ cu_q, int32_t batch, int32_t n_rows, float qscale,
+                int32_t slots_per_split, int32_t n_splits, int32_t split_base,
+                const __half* __restrict__ k_tail, const __half* __restrict__ v_tail,
+                float tail_qscale, float* __restrict__ ws) {
+  __shared__ MqSmem sm;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int split = split_base + blockIdx.z, g = blockIdx.y;
+  const int G = num_q_heads / num_kv_heads;
+  const int R = 16 / G;                                   // rows per wave
+  const MqWindow win = mq_window(blockIdx.x, 4 * R, cu_q, batch, n_rows);
+  if (split == n_splits) {   // the tails of the window's rows, one row after the other
+    for (int row = win.r0; row < win.r1; ++row) {   // uniform over the workgroup
+      const RowGeom rgr = row_geometry(row, seq_lens, max_seq_len, cu_q, batch);
+      tail_partial(q, num_q_heads, num_kv_heads, k_tail, v_tail, row, rgr.b, g, rgr.tail_len,
+                   tail_qscale, n_splits, ws, sm.p);
+      __syncthreads();
+    }
+    return;
+  }
+  // (no workgroup barrier past this point: waves leave on their own)
+  const int wr0 = __builtin_amdgcn_readfirstlane(win.r0 + R * w);   // this wave's rows
+  const int wr1 = __builtin_amdgcn_readfirstlane(min(win.r1, wr0 + R));
+  if (wr0 >= wr1) return;
+  // pages: the slots of the wave's last row (the longest), within this split
+  const RowGeom rg_last = row_geometry(wr1 - 1, seq_lens, max_seq_len, cu_q, batch);
+  const RowGeom rg_first = row_geometry(wr0, seq_lens, max_seq_len, cu_q, batch);
+  const int s0 = __builtin_amdgcn_readfirstlane(split * slots_per_split);
+  const int s1 = __builtin_amdgcn_readfirstlane(min(s0 + slots_per_split, rg_last.n_slots));
+  if (s0 >= s1) return;
+  // tokens of the pages that every row of the wave attends to (no masking below this)
+  const int lp_min = __builtin_amdgcn_readfirstlane(
+      rg_first.n_slots > 0 ? kTile * (rg_first.n_slots - 1) + rg_first.mask_lim : 0);
+
+  const int n = l & 15, gq = l >> 4;
+  const int rl = n / G, hh = n - rl * G;        // this column: row wr0 + rl, head hh
+  const bool col_ok = wr0 + rl < wr1;
+  const int row = col_ok ? wr0 + rl : wr0;
+  // tokens of this column's row held in pages (the rest, if any, is its staged tail)
+  int lp_col = 0;
+  if (col_ok) {
+    const RowGeom rgc = row_geometry(row, seq_lens, max_seq_len, cu_q, batch);
+    lp_col = rgc.n_slots > 0 ? kTile * (rgc.n_slots - 1) + rgc.mask_lim : 0;
+  }
+
+  WaveMeta& wm = sm.meta[w];
+  const float fk = (l & 1) ? 16.f : (KB == 4 ? 256.f : 4.f);
+  const float fv = (l & 1) ? 16.f : (VB == 2 ? 4.f : 256.f);
+  const int32_t* bt_row = block_table + int64_t(rg_last.b) * bt_stride;
+  auto page_of = [&](int slot) -> int64_t {
+    if (slot >= s1) return -1;
+    const int32_t page = __builtin_amdgcn_readfirstlane(bt_row[slot]);
+    return (page < 0 || page >= pool_num_pages) ? -1 : int64_t(page);
+  };
+  auto uniform_ptr = [](const uint8_t* p) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo32 = __builtin_amdgcn_readfirstlane(uint32_t(a));
+    const uint32_t hi32 = __builtin_amdgcn_readfirstlane(uint32_t(a >> 32));
+    return reinterpret_cast<const uint8_t*>((uint64_t(hi32) << 32) | lo32);
+  };
+  const LaneOffsets lo{uint32_t(n * 64 + 16 * gq), uint32_t(n * 32 + 8 * gq), uint32_t(4 * l)};
+  auto krec_of = [&](int64_t page) {
+    const uint32_t ps = __builtin_amdgcn_readfirstlane(uint32_t(page < 0 ? 0 : page));
+    const uint32_t r = ps * uint32_t(num_kv_heads) + uint32_t(g);
+    return record_rsrc(uniform_ptr(k_pool + uint64_t(r) * uint32_t(KeyRec<KB>::kRecord)),
+                       page < 0 ? 0 : KeyRec<KB>::kRecord);
+  };
+  auto vrec_of = [&](int64_t page) {
+    const uint32_t ps = __builtin_amdgcn_readfirstlane(uint32_t(page < 0 ? 0 : page));
+    const uint32_t r = ps * uint32_t(num_kv_heads) + uint32_t(g);
+    return record_rsrc(uniform_ptr(v_pool + uint64_t(r) * uint32_t(ValRec<VB>::kRecord)),
+                       page < 0 ? 0 : ValRec<VB>::kRecord);
+  };
+
+  PageRegs<KB, VB> t;
+  int64_t cur = page_of(s0);
+  load_meta<kReuseLoad>(t, krec_of(cur), vrec_of(cur), lo);
+  load_kcodes<kReuseLoad>(t, krec_of(cur), lo);
+  load_vcodes<kReuseLoad>(t, vrec_of(cur), lo);
+
+  // ---- q_rot of this column: channels 32 gq + j (the 4 lanes of a column hold 128), kept
+  // in LDS (registers are the page loop's)
+  float maxq;
+  {
+    float qr[32];
+    const __half* qrow = q + (int64_t(row) * num_q_heads + int64_t(g) * G + hh) * kDim + 32 * gq;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) load_h8(reinterpret_cast<const uint8_t*>(qrow + 8 * k), &qr[8 * k]);
+    if (!col_ok) {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) qr[j] = 0.f;
+    }
+#pragma unroll
+    for (int hb = 1; hb < 32; hb <<= 1) {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        if ((j & hb) == 0) {
+          const float a = qr[j], c = qr[j + hb];
+          qr[j] = a + c;
+          qr[j + hb] = a - c;
+        }
+      }
+    }
+    const bool up16 = (gq & 1) != 0, up32 = (gq & 2) != 0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const float p = swz_xor_f<16>(qr[j]);
+      qr[j] = up16 ? (p - qr[j]) : (qr[j] + p);
+    }
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const float p = shfl_xor32_f(qr[j]);
+      qr[j] = up32 ? (p - qr[j]) : (qr[j] + p);
+    }
+    float mq = 0.f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      qr[j] *= qscale;  // includes 1/sqrt(128) of H
+      mq = fmaxf(mq, fabsf(qr[j]));
+    }
+    maxq = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max(mq))));
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      sm.q[w][k][l] = make_float4(qr[4 * k], qr[4 * k + 1], qr[4 * k + 2], qr[4 * k + 3]);
+  }
+
+  float m_run = -INFINITY, l_part = 0.f;
+  float acc[8][4];
+#pragma unroll
+  for (int bb = 0; bb < 8; ++bb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[bb][i] = 0.f;
+
+  for (int slot = s0; slot < s1; ++slot) {
+    const int64_t next = page_of(slot + 1);
+    const bool valid = cur >= 0;
+    page_factors(t, wm, l, maxq, fk, fv);
+    load_meta<kReuseLoad>(t, krec_of(next), vrec_of(next), lo);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // ---- B operand of QK: q_rot * ka (high, low), bias = q_rot . kb ---------------------
+    H8 bqh[4], bql[4];
+    float bias;
+    {
+      float bpart = 0.f;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const float4 ka0 = wm.ka[8 * gq + 2 * s], ka1 = wm.ka[8 * gq + 2 * s + 1];
+        const float4 kb0 = wm.kb[8 * gq + 2 * s], kb1 = wm.kb[8 * gq + 2 * s + 1];
+        const float4 q0 = sm.q[w][2 * s][l], q1 = sm.q[w][2 * s + 1][l];
+        const float ka[8] = {ka0.x, ka0.y, ka0.z, ka0.w, ka1.x, ka1.y, ka1.z, ka1.w};
+        const float kb[8] = {kb0.x, kb0.y, kb0.z, kb0.w, kb1.x, kb1.y, kb1.z, kb1.w};
+        const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const float x0 = qv[2 * d], x1 = qv[2 * d + 1];
+          bpart = fmaf(x0, kb[2 * d], fmaf(x1, kb[2 * d + 1], bpart));
+          split_pk(x0 * ka[2 * d], x1 * ka[2 * d + 1], bqh[s].u[d], bql[s].u[d]);
+        }
+      }
+      bias = rows4_sum(bpart);
+    }
+
+    // ---- QK: C rows = tokens 16 tb + 4 gq + i, column = this lane's query ----------------
+    float sc[8][4];
+    {
+      const float4v binit = {bias, bias, bias, bias};
+      const float* kt = reinterpret_cast<const float*>(wm.kt);
+#pragma unroll
+      for (int tb = 0; tb < 8; ++tb) {
+        float4v c = binit;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          H8 a;
+          if constexpr (KB == 4) {
+            const uint32_t dw[4] = {t.kc[tb].x, t.kc[tb].y, t.kc[tb].z, t.kc[tb].w};
+#pragma unroll
+            for (int v = 0; v < 4; ++v) a.u[v] = k_pair(dw[s], v);
+          } else {
+            const uint32_t word = (s >> 1) ? t.kc[tb].y : t.kc[tb].x;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) a.u[v] = v_pair(word, 4 * (s & 1) + v);
+          }
+          c = mfma16x16x32(a.v, bqh[s].v, c);
+          c = mfma16x16x32(a.v, bql[s].v, c);
+        }
+        const float4 st = *reinterpret_cast<const float4*>(kt + 16 * tb + 4 * gq);
+        sc[tb][0] = c[0] * st.x;
+        sc[tb][1] = c[1] * st.y;
+        sc[tb][2] = c[2] * st.z;
+        sc[tb][3] = c[3] * st.w;
+      }
+    }
+    load_kcodes<kReuseLoad>(t, krec_of(next), lo);
+    if (kTile * (slot + 1) > lp_min) {   // some column's limit falls inside this page
+      const int lim = lp_col - kTile * slot;
+#pragma unroll
+      for (int tb = 0; tb < 8; ++tb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (16 * tb + 4 * gq + i >= lim) sc[tb][i] = -INFINITY;
+    }
+
+    // ---- online softmax (per column) -------------------------------------------------------
+    float mt = -INFINITY;
+#pragma unroll
+    for (int tb = 0; tb < 8; ++tb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mt = fmaxf(mt, sc[tb][i]);
+    mt = rows4_max(mt);
+    const float m_new = valid ? fmaxf(m_run, mt) : m_run;
+    const bool live = valid && m_new != -INFINITY;
+    const float alpha = live ? exp2_fast(m_run - m_new) : 1.f;
+    const float m_sub = live ? m_new : INFINITY;
+    H8 bph[4], bpl[4];
+    float vcorr;
+    {
+      float psum = 0.f, zpart = 0.f;
+      const float* vp = reinterpret_cast<const float*>(wm.vp);
+      const float* vz = reinterpret_cast<const float*>(wm.vz);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int tb = 2 * s + e;
+          const float4 vp4 = *reinterpret_cast<const float4*>(vp + 16 * tb + 4 * gq);
+          const float4 vz4 = *reinterpret_cast<const float4*>(vz + 16 * tb + 4 * gq);
+          const float p0 = exp2_fast(sc[tb][0] - m_sub), p1 = exp2_fast(sc[tb][1] - m_sub);
+          const float p2 = exp2_fast(sc[tb][2] - m_sub), p3 = exp2_fast(sc[tb][3] - m_sub);
+          psum += (p0 + p1) + (p2 + p3);
+          zpart = fmaf(p0, vz4.x, fmaf(p1, vz4.y, fmaf(p2, vz4.z, fmaf(p3, vz4.w, zpart))));
+          split_pk(p0 * vp4.x, p1 * vp4.y, bph[s].u[2 * e], bpl[s].u[2 * e]);
+          split_pk(p2 * vp4.z, p3 * vp4.w, bph[s].u[2 * e + 1], bpl[s].u[2 * e + 1]);
+        }
+      }
+      vcorr = rows4_sum(zpart);
+      l_part = fmaf(l_part, alpha, psum);
+    }
+    m_run = m_new;
+
+    // ---- PV: C rows = channels 16 bb + 4 gq + i ---------------------------------------------
+    if (!__all(alpha == 1.f)) {
+#pragma unroll
+      for (int bb = 0; bb < 8; ++bb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[bb][i] *= alpha;
+    }
+    const float4v vinit = {vcorr, vcorr, vcorr, vcorr};
+#pragma unroll
+    for (int bb = 0; bb < 8; ++bb) {
+      float4v c = vinit;
+      if constexpr (VB == 2) {
+        const uint2 vc = t.vc[bb];
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          const uint32_t word = d ? vc.y : vc.x;
+#pragma unroll
+          for (int hs = 0; hs < 2; ++hs) {
+            H8 a;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) a.u[v] = v_pair(word, 4 * hs + v);
+            c = mfma16x16x32(a.v, bph[2 * d + hs].v, c);
+            c = mfma16x16x32(a.v, bpl[2 * d + hs].v, c);
+          }
+        }
+      } else {
+        const uint32_t words[4] = {t.vc[bb].x, t.vc[bb].y, t.vc[bb].z, t.vc[bb].w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          H8 a;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) a.u[v] = k_pair(words[m], v);
+          c = mfma16x16x32(a.v, bph[m].v, c);
+          c = mfma16x16x32(a.v, bpl[m].v, c);
+        }
+      }
+      const float4 rv = wm.vr[4 * bb + gq];
+      acc[bb][0] = fmaf(rv.x, c[0], acc[bb][0]);
+      acc[bb][1] = fmaf(rv.y, c[1], acc[bb][1]);
+      acc[bb][2] = fmaf(rv.z, c[2], acc[bb][2]);
+      acc[bb][3] = fmaf(rv.w, c[3], acc[bb][3]);
+    }
+    load_vcodes<kReuseLoad>(t, vrec_of(next), lo);
+    cur = next;
+  }
+
+  // ---- this column's partial: m, l, acc (channels 16 bb + 4 gq + i) -------------------------
+  const float l_run = rows4_sum(l_part);
+  if (col_ok) {
+    float* part = ws + ((int64_t(row) * num_q_heads + int64_t(g) * G + hh) * (n_splits + 1) + split) * kPartStride;
+#pragma unroll
+    for (int bb = 0; bb < 8; ++bb)
+      *reinterpret_cast<float4*>(part + 4 + 16 * bb + 4 * gq) =
+          make_float4(acc[bb][0], acc[bb][1], acc[bb][2], acc[bb][3]);
+    if (gq == 0) {
+      part[0] = m_run;
+      part[1] = l_run;
     }
   }
 }
@@ -897,6 +1224,39 @@ size_t decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv
   return size_t(batch) * num_q_heads * (ns + 1) * kPartStride * sizeof(float);
 }
 
+// Multi-query read: page slots per split, so that the waves (16 query vectors each) fill the
+// chip for about four rounds of its 2048 resident waves, with at least 8 pages per split.
+int32_t mq_slots_per_split(int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t max_seq_len) {
+  const int64_t max_full = max_seq_len / kTile;
+  if (max_full <= 0) return 1;
+  const int64_t R = 16 / (num_q_heads / num_kv_heads);
+  const int64_t waves = ((int64_t(rows) + R - 1) / R) * num_kv_heads;
+  int64_t ns = (4 * 2048 + waves - 1) / waves;
+  const int64_t cap = (max_full + 7) / 8;
+  if (ns > cap) ns = cap;
+  if (ns > kMaxMergeSplits) ns = kMaxMergeSplits;
+  if (ns < 1) ns = 1;
+  return int32_t((max_full + ns - 1) / ns);
+}
+
+int32_t mq_num_splits(int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t max_seq_len) {
+  const int32_t max_full = max_seq_len / kTile;
+  const int32_t per = mq_slots_per_split(rows, num_q_heads, num_kv_heads, max_seq_len);
+  const int32_t ns = (max_full + per - 1) / per;
+  return ns < 1 ? 1 : ns;
+}
+
+size_t chunk_workspace_bytes(int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t max_seq_len) {
+  // either layout may run (one row per sequence keeps the decode's)
+  int32_t ns = decode_num_splits(rows, num_kv_heads, max_seq_len);
+  const int32_t nm = mq_num_splits(rows, num_q_heads, num_kv_heads, max_seq_len);
+  if (nm > ns) ns = nm;
+  return size_t(rows) * num_q_heads * (ns + 1) * kPartStride * sizeof(float);
+}
+
 hipError_t launch_decode(int k_bits, int v_bits, const void* q, int32_t rows,
                          int32_t num_q_heads, int32_t num_kv_heads, const void* k_pool,
                          const void* v_pool, int64_t pool_num_pages, const int32_t* block_table,
@@ -904,41 +1264,55 @@ hipError_t launch_decode(int k_bits, int v_bits, const void* q, int32_t rows,
                          const int32_t* cu_q, int32_t batch, const void* k_tail,
                          const void* v_tail, float softmax_scale, void* workspace, void* out,
                          hipStream_t stream) {
+  // several query rows of one sequence (more rows than sequences): the multi-query kernel
+  const bool multi_row = cu_q != nullptr && rows > batch;
   const int32_t tpw = decode_tiles_per_wave(rows, num_kv_heads, max_seq_len);
-  const int32_t ns = decode_num_splits(rows, num_kv_heads, max_seq_len);
+  const int32_t per_split =
+      multi_row ? mq_slots_per_split(rows, num_q_heads, num_kv_heads, max_seq_len) : 4 * tpw;
+  const int32_t ns = multi_row ? mq_num_splits(rows, num_q_heads, num_kv_heads, max_seq_len)
+                               : decode_num_splits(rows, num_kv_heads, max_seq_len);
   const float qscale = softmax_scale * kLog2e;
   float* ws = static_cast<float*>(workspace);
   const bool has_tail = k_tail != nullptr && v_tail != nullptr;
-  const bool multi_row = cu_q != nullptr && rows > batch;
   // page splits (only if a full page can exist) plus, with tail buffers, one tail split
-  const int32_t grid_x = (max_seq_len >= kTile ? ns : 0) + (has_tail ? 1 : 0);
-  if (grid_x > 0) {
+  const int32_t n_split_wg = (max_seq_len >= kTile ? ns : 0) + (has_tail ? 1 : 0);
+  if (n_split_wg > 0) {
     // without pages the only split launched is the tail, which must land on index ns
     const int32_t first = max_seq_len >= kTile ? 0 : ns;
+    // rows fastest, splits slowest: workgroups are dealt to the 8 XCDs round-robin in linear
+    // order, so consecutive ones must all carry work (a split axis of period 2, pages +
+    // tail, would leave every page workgroup on the even XCDs)
     const hipError_t e = with_preset(k_bits, v_bits, [&](auto kb, auto vb) {
       constexpr int KB = decltype(kb)::value, VB = decltype(vb)::value;
-      // decode streams every page once; the multi-query read (cu_q) re-reads them per row,
-      // and with more rows than sequences takes the multi-row layout (one row per wave)
-      auto kernel = !cu_q        ? decode_pages_kernel<KB, VB, kStreamLoad, false>
-                    : multi_row ? decode_pages_kernel<KB, VB, kReuseLoad, true>
-                                : decode_pages_kernel<KB, VB, kReuseLoad, false>;
-      // rows fastest, splits slowest: workgroups are dealt to the 8 XCDs round-robin in
-      // linear order, so consecutive ones must all carry work (a split axis of period 2,
-      // pages + tail, would leave every page workgroup on the even XCDs)
-      hipLaunchKernelGGL(kernel, dim3(multi_row ? (rows + 3) / 4 : rows, num_kv_heads, grid_x),
-                         dim3(kThreads), 0, stream,
+      if (multi_row) {   // 16 query vectors per wave, windows of 4R rows per workgroup
+        const int R = 16 / (num_q_heads / num_kv_heads);
+        hipLaunchKernelGGL((mq_pages_kernel<KB, VB>),
+                           dim3((rows + 4 * R - 1) / (4 * R) + batch, num_kv_heads, n_split_wg),
+                           dim3(kThreads), 0, stream, static_cast<const __half*>(q), num_q_heads,
+                           num_kv_heads, static_cast<const uint8_t*>(k_pool),
+                           static_cast<const uint8_t*>(v_pool), pool_num_pages, block_table,
+                           bt_stride, seq_lens, max_seq_len, cu_q, batch, rows,
+                           qscale * kInvSqrt128, per_split, ns, first,
+                           static_cast<const __half*>(k_tail), static_cast<const __half*>(v_tail),
+                           qscale, ws);
+        return;
+      }
+      // decode streams every page once; a read with one query per sequence reuses them
+      auto kernel = cu_q ? decode_pages_kernel<KB, VB, kReuseLoad>
+                         : decode_pages_kernel<KB, VB, kStreamLoad>;
+      hipLaunchKernelGGL(kernel, dim3(rows, num_kv_heads, n_split_wg), dim3(kThreads), 0, stream,
                          static_cast<const __half*>(q), num_q_heads, num_kv_heads,
                          static_cast<const uint8_t*>(k_pool), static_cast<const uint8_t*>(v_pool),
                          pool_num_pages, block_table, bt_stride, seq_lens, max_seq_len, cu_q,
                          batch, qscale * kInvSqrt128, tpw, ns, first,
                          static_cast<const __half*>(k_tail), static_cast<const __half*>(v_tail),
-                         qscale, ws, rows);
+                         qscale, ws);
     });
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(decode_merge_kernel, dim3(num_q_heads, rows), dim3(128), 0, stream,
-                     num_q_heads, seq_lens, max_seq_len, cu_q, batch, 4 * tpw, ns, has_tail ? 1 : 0,
-                     static_cast<const float*>(ws), static_cast<__half*>(out));
+                     num_q_heads, seq_lens, max_seq_len, cu_q, batch, per_split, ns,
+                     has_tail ? 1 : 0, static_cast<const float*>(ws), static_cast<__half*>(out));
   return hipGetLastError();
 }
 

@@ -62,6 +62,14 @@ int32_t decode_tiles_per_wave(int32_t batch, int32_t num_kv_heads, int32_t max_s
 int32_t decode_num_splits(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len);
 size_t decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                               int32_t max_seq_len);
+// multi-query read (several query rows per sequence): page slots per split, splits, and the
+// workspace a chunk read needs (either layout)
+int32_t mq_slots_per_split(int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t max_seq_len);
+int32_t mq_num_splits(int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t max_seq_len);
+size_t chunk_workspace_bytes(int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t max_seq_len);
 
 // rows output rows; cu_q == nullptr: row b is sequence b (decode, rows == batch), else the
 // query rows of sequence b are cu_q[b] .. cu_q[b+1]-1 (the last positions of its cache)

@@ -60,6 +60,7 @@ def _load():
         "kvarn_dequantize_tiles": (ctypes.c_int, [P, ctypes.c_int, vp, i64, vp, i32, i32, vp, vp]),
         "kvarn_decode_workspace_bytes": (sz, [P, i32, i32, i32, i32]),
         "kvarn_decode_num_splits": (i32, [P, i32, i32, i32]),
+        "kvarn_chunk_workspace_bytes": (sz, [P, i32, i32, i32, i32]),
         "kvarn_decode_attention": (ctypes.c_int, [P, vp, i32, i32, i32, vp, vp, i64, vp, i32, vp,
                                                   i32, vp, vp, ctypes.c_float, vp, sz, vp, vp]),
         "kvarn_chunk_attention": (ctypes.c_int, [P, vp, i32, vp, i32, i32, i32, vp, vp, i64, vp,
@@ -78,7 +79,8 @@ EXPORTED = ("kvarn_abi_version", "kvarn_format_version", "kvarn_status_str",
             "kvarn_params_from_dtype", "kvarn_params_check", "kvarn_page_bytes",
             "kvarn_quantize_tiles", "kvarn_quantize_kv_tiles", "kvarn_append_tokens",
             "kvarn_write_tokens", "kvarn_dequantize_tiles", "kvarn_decode_workspace_bytes",
-            "kvarn_decode_num_splits", "kvarn_decode_attention", "kvarn_chunk_attention")
+            "kvarn_decode_num_splits", "kvarn_decode_attention", "kvarn_chunk_attention",
+            "kvarn_chunk_workspace_bytes")
 
 
 def _check(status: int, what: str):
@@ -293,6 +295,18 @@ def decode_workspace_bytes(params: Params, batch: int, num_q_heads: int, num_kv_
                                                 num_kv_heads, max_seq_len))
 
 
+def chunk_workspace_bytes(params: Params, total_q: int, num_q_heads: int, num_kv_heads: int,
+                          max_seq_len: int) -> int:
+    return int(lib.kvarn_chunk_workspace_bytes(ctypes.byref(params), total_q, num_q_heads,
+                                               num_kv_heads, max_seq_len))
+
+
+def new_chunk_workspace(params: Params, total_q, num_q_heads, num_kv_heads, max_seq_len,
+                        device="cuda"):
+    nbytes = chunk_workspace_bytes(params, total_q, num_q_heads, num_kv_heads, max_seq_len)
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
 def decode_num_splits(params: Params, batch: int, num_kv_heads: int, max_seq_len: int) -> int:
     return int(lib.kvarn_decode_num_splits(ctypes.byref(params), batch, num_kv_heads, max_seq_len))
 
@@ -352,7 +366,7 @@ def chunk_attention(params: Params, q, cu_q, k_pool, v_pool, block_table, seq_le
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(128)
     if workspace is None:
-        workspace = new_workspace(params, max(total_q, 1), hq, hkv, max_seq_len, q.device)
+        workspace = new_chunk_workspace(params, max(total_q, 1), hq, hkv, max_seq_len, q.device)
     if out is None:
         out = torch.empty_like(q)
     _check(lib.kvarn_chunk_attention(ctypes.byref(params), _ptr(q), total_q, _ptr(cu_q), B, hq,

@@ -213,8 +213,25 @@ def test_chunk_attention_validation():
     assert _chunk(p, bts=10) == INVALID
     assert _chunk(p, scale=float("inf")) == INVALID
     assert _chunk(p, q=ctypes.c_void_p(0x10002)) == INVALID
-    need = K.decode_workspace_bytes(p, 16, 64, 8, 16384)
+    need = K.chunk_workspace_bytes(p, 16, 64, 8, 16384)
+    assert need >= K.decode_workspace_bytes(p, 16, 64, 8, 16384)
     assert _chunk(p, wsb=need - 1) == WS
+
+
+def test_chunk_workspace_formula():
+    """Either read layout fits: the workspace holds max(decode splits, multi-query splits) + 1
+    partials per (row, query head)."""
+    p = K.params_from_dtype()
+    for tq, hq, hkv, mx in ((1024, 64, 8, 16512), (16, 64, 8, 16384), (3, 8, 8, 100),
+                            (200, 8, 1, 131072), (65535, 8, 8, 1024)):
+        b = K.chunk_workspace_bytes(p, tq, hq, hkv, mx)
+        d = K.decode_workspace_bytes(p, tq, hq, hkv, mx)
+        assert b >= d and b % (tq * hq * 132 * 4) == 0
+        ns = b // (tq * hq * 132 * 4) - 1
+        assert 1 <= ns <= max(1, mx // 128)
+    assert K.chunk_workspace_bytes(p, 0, 64, 8, 1024) == 0
+    assert K.chunk_workspace_bytes(p, 70000, 64, 8, 1024) == 0
+    assert K.chunk_workspace_bytes(p, 16, 128, 8, 1024) == 0
 
 
 def test_decode_workspace_formula():

@@ -1114,19 +1114,27 @@ mq_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t num_k
 }
 
 // Merge the splits of one (sequence, query head): log-sum-exp weights, H^T on the page
-// part (rotated space), plus the raw-space tail; float16 output. One 128-thread workgroup
-// per (query head, sequence): thread c owns channel c; split weights are computed once in
-// LDS, then every thread streams its channel of all partials (independent loads).
-__global__ void __launch_bounds__(128)
+// part (rotated space), plus the raw-space tail; float16 output. One 256-thread workgroup
+// per (pair of query heads, sequence): 128 threads per head, thread c owns channel c; split
+// weights are computed once in LDS, then every thread streams its channel of all partials
+// (independent loads). (Pairs halve the workgroup count of a many-row read.)
+__global__ void __launch_bounds__(256)
 decode_merge_kernel(int32_t num_q_heads, const int32_t* __restrict__ seq_lens, int32_t max_seq_len,
                     const int32_t* __restrict__ cu_q, int32_t batch, int32_t tiles_per_split,
                     int32_t n_splits, int32_t has_tail, const float* __restrict__ ws,
                     __half* __restrict__ out) {
-  __shared__ float wsh[kMaxMergeSplits + 1];
-  __shared__ float red[2][2];
-  __shared__ float xs[kDim];
-  const int hq = blockIdx.x, b = blockIdx.y;   // b: output row
-  const int c = threadIdx.x, lane = c & 63, wv = c >> 6;
+  __shared__ float wsh_[2][kMaxMergeSplits + 1];
+  __shared__ float red_[2][2][2];
+  __shared__ float xs_[2][kDim];
+  const int pair = threadIdx.x >> 7;
+  float* wsh = wsh_[pair];
+  float (*red)[2] = red_[pair];
+  float* xs = xs_[pair];
+  // a head past the last (odd head count) runs along for the barriers and stores nothing
+  const int hq = min(2 * int(blockIdx.x) + pair, num_q_heads - 1);
+  const bool head_ok = 2 * int(blockIdx.x) + pair < num_q_heads;
+  const int b = blockIdx.y;   // b: output row
+  const int c = threadIdx.x & 127, lane = c & 63, wv = c >> 6;
   const RowGeom rg = row_geometry(b, seq_lens, max_seq_len, cu_q, batch);
   const int used = (rg.n_slots + tiles_per_split - 1) / tiles_per_split;
   const bool tail = has_tail && rg.tail_len != 0;
@@ -1193,7 +1201,7 @@ decode_merge_kernel(int32_t num_q_heads, const int32_t* __restrict__ seq_lens, i
   }
   if (tail) a = fmaf(wsh[kMaxMergeSplits], base[n_splits * kPartStride + 4 + c], a);
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  out[(int64_t(b) * num_q_heads + hq) * kDim + c] = __float2half_rn(a * inv);
+  if (head_ok) out[(int64_t(b) * num_q_heads + hq) * kDim + c] = __float2half_rn(a * inv);
 }
 
 }  // namespace
@@ -1310,7 +1318,7 @@ hipError_t launch_decode(int k_bits, int v_bits, const void* q, int32_t rows,
     });
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(num_q_heads, rows), dim3(128), 0, stream,
+  hipLaunchKernelGGL(decode_merge_kernel, dim3((num_q_heads + 1) / 2, rows), dim3(256), 0, stream,
                      num_q_heads, seq_lens, max_seq_len, cu_q, batch, per_split, ns,
                      has_tail ? 1 : 0, static_cast<const float*>(ws), static_cast<__half*>(out));
   return hipGetLastError();

@@ -8,7 +8,9 @@ step), on sampled tiles and sampled (sequence, KV head) rows that the oracle rec
                  120 mod 128 whose staging tiles fill (and are quantized) at step 8;
   long context   131072 tokens, 64 decode steps with appends;
   prefill burst  64 x 16384 tokens (131072 tiles) for 2, 4 and 8 iterations, then one
-                 batched decode step.
+                 batched decode step;
+  chunked prefill  8 sequences x 16384 cached tokens + a 128-token chunk each (chunk write,
+                 then the multi-query read of the 1024 chunk rows).
 
 Inputs are drawn on the GPU by the seeded generators; the sampled tiles and rows are copied
 to the host for the oracle.
@@ -187,3 +189,48 @@ def test_prefill_burst(K, burst, n_iters):
     rows = _rows(np.random.default_rng(409), w.batch, w.hkv)
     err = T.check_decode(q, out, kp, vp, w.block_table, sl, w.hq // w.hkv, rows=rows)
     say(f"  decode: {len(rows) * 8} rows, max rel err {err:.2e}")
+
+
+def test_chunked_prefill_full(K):
+    """The chunked-prefill benchmark's call at full size: 8 sequences x 16384 cached tokens,
+    a 128-token chunk each written by kvarn_write_tokens and read by kvarn_chunk_attention
+    (1024 query rows x 64 heads, the multi-query kernel); sampled (row, KV head) pairs against
+    the oracle's causal attention over the dequantized pages."""
+    B, ctx, n = 8, 16384, 128
+    params = K.params_from_dtype("kvarn_k4v2_g128", 8)
+    w = synth.prefill_burst(device="cuda", seed=11, batch=B, context=ctx + n, n_iters=8)
+    hq, hkv, G = w.hq, w.hkv, w.hq // w.hkv
+    kp = K.new_pool(w.num_pages, hkv, K.KIND_K, params=params)
+    vp = K.new_pool(w.num_pages, hkv, K.KIND_V, params=params)
+    per_seq = (ctx + n) // 128
+    keep = torch.tensor([i for i in range(w.tile_src_token.numel()) if (i + 1) % per_seq != 0],
+                        dtype=torch.long, device="cuda")
+    K.quantize_kv_tiles(params, w.k_src, w.v_src, w.tile_src_token[keep].contiguous(),
+                        w.tile_dst_page[keep].contiguous(), kp, vp)
+    rows = torch.cat([torch.arange(w.seq_start[b] + ctx, w.seq_start[b] + ctx + n, device="cuda")
+                      for b in range(B)])
+    kn, vn = w.k_src[rows].contiguous(), w.v_src[rows].contiguous()
+    cu = torch.arange(0, (B + 1) * n, n, dtype=torch.int32, device="cuda")
+    sl0 = torch.full((B,), ctx, dtype=torch.int32, device="cuda")
+    kt = torch.zeros((B, hkv, 128, 128), dtype=torch.float16, device="cuda")
+    vt = torch.zeros_like(kt)
+    K.write_tokens(params, kn, vn, cu, sl0, kt, vt, w.block_table, kp, vp, n)
+    q = torch.randn((B * n, hq, 128), generator=torch.Generator().manual_seed(12)).to(torch.float16).cuda()
+    out = K.chunk_attention(params, q, cu, kp, vp, w.block_table, sl0 + n, ctx + n, kt, vt)
+    torch.cuda.synchronize()
+    say(f"chunked prefill: {B} x ({ctx} + {n}) tokens, {B * n} query rows x {hq} heads")
+    rng = np.random.default_rng(13)
+    bt = w.block_table.cpu().numpy()
+    qh, o = q.cpu().numpy(), out.cpu().numpy().astype(np.float64)
+    worst = 0.0
+    for _ in range(6):
+        b, i, g = int(rng.integers(B)), int(rng.integers(n)), int(rng.integers(hkv))
+        L = ctx + i + 1                                   # causal prefix of chunk row i
+        pages = [int(p) for p in bt[b, :(L + 127) // 128]]
+        kk = np.concatenate([O.dequantize_k_record(r) for r in T.records_of(kp, pages, g)])[:L]
+        vv = np.concatenate([O.dequantize_v_record(r) for r in T.records_of(vp, pages, g)])[:L]
+        r = b * n + i
+        for hh in range(G):
+            want = O.attention(qh[r, g * G + hh].astype(np.float64), kk, vv, 1.0 / np.sqrt(128.0))
+            worst = max(worst, T.assert_rows_close(o[r, g * G + hh], want, f"row {r} head {g * G + hh}"))
+    say(f"  6 (row, KV head) samples x {G} heads: max rel err {worst:.2e}")

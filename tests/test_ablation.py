@@ -75,7 +75,7 @@ def test_uneven_token_scales_attention(results):
 
 def test_toy_loop_is_deterministic_and_starts_at_the_single_step_error():
     k, v, q_sets = _data("t3")
-    cache = A.caches(k, v, [("KVarN N=8", True, 8)])
+    cache = A.caches(k, v, [("KVarN N=8", True, 8, 4, 2)])
     d1 = A.divergence(k, v, q_sets[0], cache, steps=4)
     d2 = A.divergence(k, v, q_sets[0], cache, steps=4)
     assert d1 == d2
@@ -92,7 +92,7 @@ def test_kernels_match_the_oracle_ablation():
         pytest.fail("GPU tests need an MI355X; torch.cuda.is_available() is False")
     for name in ("one_layer", "uneven_tokens"):
         k, v, q_sets = _data(name)
-        cache = A.caches(k, v, [("rotation + RTN", True, 0), ("KVarN N=8", True, 8)])
+        cache = A.caches(k, v, [("rotation + RTN", True, 0, 4, 2), ("KVarN N=8", True, 8, 4, 2)])
         ref = A.single_step(k, v, A.grouped_queries(q_sets), cache)
         kern = A.kernel_attn_errors(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
                                     torch.from_numpy(q_sets).cuda(), n_list=(0, 8))
@@ -101,3 +101,13 @@ def test_kernels_match_the_oracle_ablation():
         for n, lab in ((0, "rotation + RTN"), (8, "KVarN N=8")):
             e_k, e_o = kern[f"KVarN N={n}"], ref[lab]["attn"]
             assert abs(e_k - e_o) <= 0.02 * e_o + 0.01, (name, n, e_k, e_o)
+
+
+@pytest.mark.parametrize("name", ["one_layer", "long_context", "uneven_tokens", "t3"])
+def test_code_width_orders_reconstruction(results, name):
+    """The presets' code widths: 4-bit values reconstruct about 4-5x better than 2-bit ones
+    (RTN levels 15 vs 3), 2-bit keys much worse than 4-bit ones."""
+    r = results[name]
+    assert r["KVarN N=8, k4v4"]["v"] < 0.3 * r["KVarN N=8"]["v"], r
+    assert r["KVarN N=8, k2v2"]["k"] > 3.0 * r["KVarN N=8"]["k"], r
+    assert r["KVarN N=8, k4v4"]["k"] == r["KVarN N=8"]["k"], r     # same key path

@@ -1233,14 +1233,14 @@ size_t decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv
 }
 
 // Multi-query read: page slots per split, so that the waves (16 query vectors each) fill the
-// chip for about four rounds of its 2048 resident waves, with at least 8 pages per split.
+// chip for about eight rounds of its 2048 resident waves, with at least 8 pages per split.
 int32_t mq_slots_per_split(int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
                            int32_t max_seq_len) {
   const int64_t max_full = max_seq_len / kTile;
   if (max_full <= 0) return 1;
   const int64_t R = 16 / (num_q_heads / num_kv_heads);
   const int64_t waves = ((int64_t(rows) + R - 1) / R) * num_kv_heads;
-  int64_t ns = (4 * 2048 + waves - 1) / waves;
+  int64_t ns = (8 * 2048 + waves - 1) / waves;
   const int64_t cap = (max_full + 7) / 8;
   if (ns > cap) ns = cap;
   if (ns > kMaxMergeSplits) ns = kMaxMergeSplits;

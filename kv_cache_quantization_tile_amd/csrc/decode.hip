@@ -148,8 +148,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kBufferFlags = 0x00020000;   // raw (untyped) 32-bit data
 // Page records are read once per decode step: nontemporal loads (cache policy bit nt) keep
 // them from displacing reused lines (measured: 0.85 vs 0.75 of HBM peak for this pattern).
-// The multi-query read re-reads every page once per query row: there the loads are plain
-// (kReuseLoad), so that the rows that follow find the page in L2.
+// In a multi-query read the waves of one workgroup (other rows of the same sequence) stream
+// the same pages at about the same time: there the loads are plain (kReuseLoad), so that
+// the others find the page in L2.
 constexpr int kStreamLoad = 2;
 constexpr int kReuseLoad = 0;
 

@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkvarn.so")
-SOURCES = ["api.hip", "quantize.hip", "decode.hip"]
+SOURCES = ["api.hip", "quantize.hip", "decode.hip", "mq.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

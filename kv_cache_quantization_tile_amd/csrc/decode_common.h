@@ -1,0 +1,361 @@
+// Device helpers shared by the decode and multi-query read kernels (decode.hip, mq.hip):
+// page record geometry and loads, code unpacking into float16 MFMA operands, per-page
+// factors, the geometry of an output row, and the exact attention over a staged tail.
+// Internal to the library; each including source gets its own copies.
+#pragma once
+
+#include "kvarn_device.h"
+
+namespace kvarn {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kPartStride = 132;  // floats per partial: m, l, pad, pad, acc[128]
+constexpr int kMaxMergeSplits = 4096;  // splits one merge workgroup can weight (LDS)
+
+__device__ __forceinline__ float4v mfma16x16x32(const half8& a, const half8& b, const float4v& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+union H8 {
+  half8 v;
+  uint32_t u[4];
+};
+
+// (t & mask) | magic in one 3-input bit operation (truth table 0xEA: S0 & S1 | S2)
+__device__ __forceinline__ uint32_t and_or(uint32_t t, uint32_t mask, uint32_t magic) {
+  return __builtin_amdgcn_bitop3_b32(t, mask, magic, 0xEA);
+}
+
+// Key codes of word w, nibble pair v (nibbles v and 4 + v = channels 2v and 2v + 1 of the
+// word's 8), as float16x2 1 + code * 2^(b - 10): the nibbles go to mantissa bits b..b+3 with
+// b = 2 for even v and b = 6 for odd v, so two shifted copies of the word serve all four pairs.
+// The operand on the other side carries the matching factor 2^(10 - b) (256 or 16).
+__device__ __forceinline__ uint32_t k_pair(uint32_t w, int v) {
+  const uint32_t t = v < 2 ? (w << 2) : (w >> 6);
+  return and_or(t, (v & 1) ? 0x03C003C0u : 0x003C003Cu, 0x3C003C00u);
+}
+
+// Value codes of word w, crumb pair i (crumbs i and 8 + i), as float16x2 1 + code * 2^(b - 10):
+// b = 8 for even i, 6 for odd i (factor 4 or 16 on the other side); four shifted copies.
+__device__ __forceinline__ uint32_t v_pair(uint32_t w, int i) {
+  const int sh = i == 0 ? 8 : i <= 2 ? 4 : i <= 4 ? 0 : i <= 6 ? -4 : -8;
+  const uint32_t t = sh >= 0 ? (w << sh) : (w >> -sh);
+  return and_or(t, (i & 1) ? 0x00C000C0u : 0x03000300u, 0x3C003C00u);
+}
+
+// 2^x on the transcendental unit (results below 2^-126 flush to 0, which softmax weights
+// of that size may)
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ void load_h8(const uint8_t* p, float* o) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    o[2 * k] = h2f(uint16_t(w[k] & 0xFFFF));
+    o[2 * k + 1] = h2f(uint16_t(w[k] >> 16));
+  }
+}
+
+// Per wave: the float32 factors of the page being processed.
+//   ka[c] = r_c scale_c 2^(10-b_c) ks      kb[c] = ks r_c zero_c - ka[c]     kt[t] = s_t / ks
+//   vp[t] = s_t scale_t 2^(10-b_t) vs      vz[t] = vs s_t zero_t - vp[t]     vr[c] = r_c / vs
+// (ks, vs: the page's powers of two for the B operands.)
+struct WaveMeta {
+  float4 ka[kDim / 4], kb[kDim / 4];   // read 4 channels at a time
+  float2 kt[kTile / 2], vp[kTile / 2], vz[kTile / 2];   // read 2 tokens at a time
+  float4 vr[kDim / 4];
+};
+
+
+// Raw loads of one page: key codes (16 B per 16-token block at 4 bits, 8 B at 2), value
+// codes (8 B per 16-channel block at 2 bits, 16 B at 4), and entries 2l, 2l+1 of the 4
+// float16 metadata arrays of each record.
+// Key record geometry by key code width (4: kvarn_k4v2_g128 / kvarn_k4v4_g128,
+// 2: kvarn_k2v2_g128).
+template <int KB> struct KeyRec;
+template <> struct KeyRec<4> {
+  static constexpr int kRecord = kKRecord, kCodeBytes = kKCodeBytes;
+  typedef uint4 Codes;    // one 16-token block: 4 words = the 4 k-steps of 8 channels
+};
+template <> struct KeyRec<2> {
+  static constexpr int kRecord = kK2Record, kCodeBytes = kK2CodeBytes;
+  typedef uint2 Codes;    // one 16-token block: 2 words, each 2 k-steps of 8 channels
+};
+
+// Value record geometry by value code width (2: kvarn_k4v2_g128 / kvarn_k2v2_g128,
+// 4: kvarn_k4v4_g128).
+template <int VB> struct ValRec;
+template <> struct ValRec<2> {
+  static constexpr int kRecord = kVRecord, kCodeBytes = kVCodeBytes;
+  typedef uint2 Codes;    // one 16-channel block: 2 words, each 2 k-steps of 8 tokens
+};
+template <> struct ValRec<4> {
+  static constexpr int kRecord = kV4Record, kCodeBytes = kV4CodeBytes;
+  typedef uint4 Codes;    // one 16-channel block: 4 words = the 4 k-steps of 8 tokens
+};
+
+template <int KB, int VB>
+struct PageRegs {
+  typename KeyRec<KB>::Codes kc[8];
+  typename ValRec<VB>::Codes vc[8];
+  uint32_t km[4], vm[4];
+};
+
+// Page loads through buffer descriptors: one scalar descriptor per record (base, size), a
+// 32-bit per-lane offset fixed for the kernel and a scalar offset per load, so no per-load
+// address arithmetic runs on the vector ALU (and reads past the record return 0).
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kBufferFlags = 0x00020000;   // raw (untyped) 32-bit data
+// Page records are read once per decode step: nontemporal loads (cache policy bit nt) keep
+// them from displacing reused lines (measured: 0.85 vs 0.75 of HBM peak for this pattern).
+// In a multi-query read the waves of one workgroup (other rows of the same sequence) stream
+// the same pages at about the same time: there the loads are plain (kReuseLoad), so that
+// the others find the page in L2.
+constexpr int kStreamLoad = 2;
+constexpr int kReuseLoad = 0;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t record_rsrc(const uint8_t* rec, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(rec), (short)0, bytes, kBufferFlags);
+}
+
+struct LaneOffsets {
+  uint32_t k, v, m;   // key codes, value codes, metadata
+};
+
+template <int AUX, int KB, int VB>
+__device__ __forceinline__ void load_meta(PageRegs<KB, VB>& t, __amdgpu_buffer_rsrc_t kr,
+                                          __amdgpu_buffer_rsrc_t vr, const LaneOffsets& o) {
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    t.km[a] = __builtin_amdgcn_raw_buffer_load_b32(kr, o.m, KeyRec<KB>::kCodeBytes + 256 * a, AUX);
+    t.vm[a] = __builtin_amdgcn_raw_buffer_load_b32(vr, o.m, ValRec<VB>::kCodeBytes + 256 * a, AUX);
+  }
+}
+template <int AUX, int KB, int VB>
+__device__ __forceinline__ void load_kcodes(PageRegs<KB, VB>& t, __amdgpu_buffer_rsrc_t kr,
+                                            const LaneOffsets& o) {
+#pragma unroll
+  for (int tb = 0; tb < 8; ++tb) {
+    if constexpr (KB == 4) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(kr, o.k, 1024 * tb, AUX);
+      t.kc[tb] = make_uint4(v.x, v.y, v.z, v.w);
+    } else {   // 32 bytes per token: the value records' lane offsets
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(kr, o.v, 512 * tb, AUX);
+      t.kc[tb] = make_uint2(v.x, v.y);
+    }
+  }
+}
+template <int AUX, int KB, int VB>
+__device__ __forceinline__ void load_vcodes(PageRegs<KB, VB>& t, __amdgpu_buffer_rsrc_t vr,
+                                            const LaneOffsets& o) {
+#pragma unroll
+  for (int bb = 0; bb < 8; ++bb) {
+    if constexpr (VB == 2) {
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(vr, o.v, 512 * bb, AUX);
+      t.vc[bb] = make_uint2(v.x, v.y);
+    } else {   // 64 bytes per channel: the 4-bit key records' lane offsets
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(vr, o.k, 1024 * bb, AUX);
+      t.vc[bb] = make_uint4(v.x, v.y, v.z, v.w);
+    }
+  }
+}
+
+__device__ __forceinline__ float lo_h(uint32_t w) { return h2f(uint16_t(w & 0xFFFF)); }
+__device__ __forceinline__ float hi_h(uint32_t w) { return h2f(uint16_t(w >> 16)); }
+
+__device__ __forceinline__ float wave_max(float v) { return rows4_max(row16_max(v)); }
+
+// Exponent k = 14 - e for x = m 2^e, m in [0.5, 1): x 2^k lies in [2^13, 2^14). 0 when x is
+// zero or not finite; clamped to +-100.
+__device__ __forceinline__ int pow2_norm_exp(float x) {
+  if (!(x > 0.f) || !(x <= 3.4e38f)) return 0;
+  const int k = 14 - __builtin_amdgcn_frexp_expf(x);
+  return k < -100 ? -100 : (k > 100 ? 100 : k);
+}
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// float16x2 high parts of (a, b) and low parts f16(a - f16(a)), f16(b - f16(b)): one packed
+// conversion and two mixed-precision FMAs that read the float16 high parts back in place
+__device__ __forceinline__ void split_pk(float a, float b, uint32_t& hi, uint32_t& lo) {
+  uint32_t h, r;
+  asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(h) : "v"(a), "v"(b));
+  asm("v_fma_mixlo_f16 %0, %1, 1.0, -%2 op_sel_hi:[0,0,1]" : "=v"(r) : "v"(a), "v"(h));
+  asm("v_fma_mixhi_f16 %0, %1, 1.0, -%2 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "+v"(r) : "v"(b), "v"(h));
+  hi = h;
+  lo = r;
+}
+
+// Per-lane choice between two values by an all-ones / all-zero mask (one 3-input bit
+// operation, truth table 0xCA: S0 ? S1 : S2 bitwise)
+__device__ __forceinline__ float pick(uint32_t mask, float if_set, float if_clear) {
+  return __uint_as_float(__builtin_amdgcn_bitop3_b32(mask, __float_as_uint(if_set),
+                                                     __float_as_uint(if_clear), 0xCA));
+}
+
+// DPP row_ror:8 move that only writes the lanes of the given banks (bank k = lanes 4k..4k+3
+// of each 16-lane row); the other lanes keep `old`.
+template <int BANKS>
+__device__ __forceinline__ uint32_t swap8_into(uint32_t old, uint32_t src) {
+  return uint32_t(__builtin_amdgcn_update_dpp(int(old), int(src), kDppRowRor8, 0xF, BANKS, false));
+}
+constexpr int kHiBanks = 0x3;   // lanes 0..7 of a row: high-part columns
+constexpr int kLoBanks = 0xC;   // lanes 8..15: low-part columns
+
+// Page factors of the record pair held in t, for the B operands, into this wave's LDS slot
+// (lane l: channels and tokens 2l, 2l + 1). fk, fv: the lane's unpack factors 2^(10 - b);
+// maxq: the wave's largest |q_rot| (sets the power of two ks that keeps the QK B operand
+// below 2^14; vs does the same for the PV one).
+template <int KB, int VB>
+__device__ __forceinline__ void page_factors(const PageRegs<KB, VB>& t, WaveMeta& wm, int l,
+                                             float maxq, float fk, float fv) {
+  const float rk0 = lo_h(t.km[0]), rk1 = hi_h(t.km[0]);
+  const float ka0 = rk0 * lo_h(t.km[2]) * fk, ka1 = rk1 * hi_h(t.km[2]) * fk;
+  const float sv0 = lo_h(t.vm[1]), sv1 = hi_h(t.vm[1]);
+  const float vp0 = sv0 * lo_h(t.vm[2]) * fv, vp1 = sv1 * hi_h(t.vm[2]) * fv;
+  const float mka = wave_max(fmaxf(ka0, ka1));
+  const float mvp = wave_max(fmaxf(vp0, vp1));
+  const int eks = pow2_norm_exp(maxq * __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mka))));
+  const int evs = pow2_norm_exp(__int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mvp))));
+  const float ks = __builtin_ldexpf(1.f, eks), iks = __builtin_ldexpf(1.f, -eks);
+  const float vs = __builtin_ldexpf(1.f, evs), ivs = __builtin_ldexpf(1.f, -evs);
+  const float a0 = ka0 * ks, a1 = ka1 * ks;
+  reinterpret_cast<float2*>(wm.ka)[l] = make_float2(a0, a1);
+  reinterpret_cast<float2*>(wm.kb)[l] =
+      make_float2(fmaf(ks * rk0, lo_h(t.km[3]), -a0), fmaf(ks * rk1, hi_h(t.km[3]), -a1));
+  wm.kt[l] = make_float2(lo_h(t.km[1]) * iks, hi_h(t.km[1]) * iks);
+  const float p0 = vp0 * vs, p1 = vp1 * vs;
+  wm.vp[l] = make_float2(p0, p1);
+  wm.vz[l] =
+      make_float2(fmaf(vs * sv0, lo_h(t.vm[3]), -p0), fmaf(vs * sv1, hi_h(t.vm[3]), -p1));
+  reinterpret_cast<float2*>(wm.vr)[l] = make_float2(lo_h(t.vm[0]) * ivs, hi_h(t.vm[0]) * ivs);
+}
+
+// What one output row attends to. Decode (cu_q == nullptr): row b is sequence b, attending
+// to its L = seq_lens[b] tokens: the full pages, then the L mod 128 staged tokens. Several
+// queries per sequence (cu_q != nullptr): rows cu_q[b] .. cu_q[b+1]-1 are the last
+// n = cu_q[b+1] - cu_q[b] positions of sequence b (its cache of C = seq_lens[b] tokens ends with
+// them), row cu_q[b] + i at position C - n + i attending causally to L = C - n + i + 1 tokens.
+// A partial last tile of L that is a completed page (it lies below 128 floor(C / 128)) is one
+// more page slot whose tokens from L mod 128 on are masked; otherwise it is the staging tile.
+struct RowGeom {
+  int b;          // sequence (block table and staging row)
+  int n_slots;    // page slots to stream (full pages, plus one masked page)
+  int mask_lim;   // tokens of the last slot that count (128: all)
+  int tail_len;   // staged tokens attended (0: none)
+};
+
+__device__ __forceinline__ RowGeom row_geometry(int row, const int32_t* __restrict__ seq_lens,
+                                                int32_t max_seq_len,
+                                                const int32_t* __restrict__ cu_q, int32_t batch) {
+  RowGeom r;
+  int32_t C, L;
+  if (cu_q == nullptr) {
+    r.b = row;
+    C = seq_lens[row];
+    C = C < 0 ? 0 : (C > max_seq_len ? max_seq_len : C);
+    L = C;
+  } else {
+    int lo = 0, hi = batch;               // the last b with cu_q[b] <= row
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (cu_q[mid] <= row) lo = mid; else hi = mid;
+    }
+    r.b = lo;
+    C = seq_lens[lo];
+    C = C < 0 ? 0 : (C > max_seq_len ? max_seq_len : C);
+    const int32_t n = cu_q[lo + 1] - cu_q[lo];
+    L = C - n + (row - cu_q[lo]) + 1;
+    L = L < 0 ? 0 : (L > C ? C : L);
+  }
+  const int n_full = L / kTile, rem = L % kTile;
+  if (rem != 0 && (n_full + 1) * kTile <= C) {
+    r.n_slots = n_full + 1;
+    r.mask_lim = rem;
+    r.tail_len = 0;
+  } else {
+    r.n_slots = n_full;
+    r.mask_lim = kTile;
+    r.tail_len = rem;
+  }
+  return r;
+}
+
+// Exact attention over the T staged float16 tokens of (sequence sb, KV head g), raw space,
+// for output row `row`, written as split n_splits of each query head's partials. Run by the
+// extra split of decode_pages_kernel; wave w handles heads 2w, 2w+1 of the group; p_sm is
+// 8 x 128 floats of LDS.
+__device__ void tail_partial(const __half* __restrict__ q, int32_t num_q_heads,
+                             int32_t num_kv_heads, const __half* __restrict__ k_tail,
+                             const __half* __restrict__ v_tail, int row, int sb, int g, int T,
+                             float qscale, int32_t n_splits, float* __restrict__ ws,
+                             float (*p_sm)[kTile]) {
+  const int G = num_q_heads / num_kv_heads;
+  if (T == 0) return;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const __half* kt = k_tail + (int64_t(sb) * num_kv_heads + g) * kTile * kDim;
+  const __half* vt = v_tail + (int64_t(sb) * num_kv_heads + g) * kTile * kDim;
+  for (int hh = 2 * w; hh < 2 * w + 2; ++hh) {
+    if (hh >= G) break;
+    const int hq = g * G + hh;
+    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(q + (int64_t(row) * num_q_heads + hq) * kDim);
+    float sc[2];
+#pragma unroll
+    for (int half_ = 0; half_ < 2; ++half_) {
+      const int t = l + 64 * half_;
+      float a = -INFINITY;
+      if (t < T) {
+        a = 0.f;
+        const uint8_t* krow = reinterpret_cast<const uint8_t*>(kt + int64_t(t) * kDim);
+        for (int c8 = 0; c8 < 16; ++c8) {
+          float qv[8], kv[8];
+          load_h8(qrow + 16 * c8, qv);
+          load_h8(krow + 16 * c8, kv);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) a = fmaf(qv[i], kv[i], a);
+        }
+        a *= qscale;
+      }
+      sc[half_] = a;
+    }
+    float mx = fmaxf(sc[0], sc[1]);
+    for (int off = 1; off < 64; off <<= 1)
+      mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(((l ^ off) << 2), __float_as_int(mx))));
+    float ps = 0.f;
+#pragma unroll
+    for (int half_ = 0; half_ < 2; ++half_) {
+      const int t = l + 64 * half_;
+      const float p = t < T ? exp2f(sc[half_] - mx) : 0.f;
+      p_sm[hh][t] = p;
+      ps += p;
+    }
+    for (int off = 1; off < 64; off <<= 1)
+      ps += __int_as_float(__builtin_amdgcn_ds_bpermute(((l ^ off) << 2), __float_as_int(ps)));
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    float o0 = 0.f, o1 = 0.f;
+    for (int t = 0; t < T; ++t) {
+      const uint32_t vv = *reinterpret_cast<const uint32_t*>(vt + int64_t(t) * kDim + 2 * l);
+      const float p = p_sm[hh][t];
+      o0 = fmaf(p, h2f(uint16_t(vv & 0xFFFF)), o0);
+      o1 = fmaf(p, h2f(uint16_t(vv >> 16)), o1);
+    }
+    float* part = ws + ((int64_t(row) * num_q_heads + hq) * (n_splits + 1) + n_splits) * kPartStride;
+    *reinterpret_cast<float2*>(part + 4 + 2 * l) = make_float2(o0, o1);
+    if (l == 0) {
+      part[0] = mx;
+      part[1] = ps;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+}  // namespace
+}  // namespace kvarn

@@ -71,6 +71,18 @@ int32_t mq_num_splits(int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
 size_t chunk_workspace_bytes(int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
                              int32_t max_seq_len);
 
+// The page splits (and tail split) of a multi-query read: n_split_wg splits from split_base;
+// partials into workspace for the merge that launch_decode runs next. qscale_pages includes
+// the 1/sqrt(128) of the query rotation; both scales include log2(e).
+hipError_t launch_mq_pages(int k_bits, int v_bits, const void* q, int32_t rows,
+                          int32_t num_q_heads, int32_t num_kv_heads, const void* k_pool,
+                          const void* v_pool, int64_t pool_num_pages, const int32_t* block_table,
+                          int32_t bt_stride, const int32_t* seq_lens, int32_t max_seq_len,
+                          const int32_t* cu_q, int32_t batch, const void* k_tail,
+                          const void* v_tail, float qscale_pages, float qscale_tail,
+                          int32_t slots_per_split, int32_t n_splits, int32_t n_split_wg,
+                          int32_t split_base, void* workspace, hipStream_t stream);
+
 // rows output rows; cu_q == nullptr: row b is sequence b (decode, rows == batch), else the
 // query rows of sequence b are cu_q[b] .. cu_q[b+1]-1 (the last positions of its cache)
 hipError_t launch_decode(int k_bits, int v_bits, const void* q, int32_t rows,

@@ -138,3 +138,23 @@ def test_queries_below_position_zero_get_zeros(K):
     o = out.cpu().numpy().astype(np.float64)
     for (r, hq), want in ref.items():
         T.assert_rows_close(o[r, hq], want, f"row {r} head {hq}")
+
+
+def test_reads_are_deterministic(K):
+    """Decode and multi-query read give identical bytes when run twice (no atomics, fixed
+    split and merge order)."""
+    lens, lens_new = [300, 1000, 0], [50, 130, 9]
+    hkv, G = 2, 8
+    params = K.params_from_dtype("kvarn_k4v2_g128", 8)
+    kp, vp, bt, kt, vt, sl = _written_cache(K, params, lens, lens_new, hkv, seed=190)
+    mx = int(sl.max().item())
+    total_q = sum(lens_new)
+    cu_q = torch.tensor([0] + list(np.cumsum(lens_new)), dtype=torch.int32, device="cuda")
+    q = torch.randn((total_q, hkv * G, 128), generator=torch.Generator().manual_seed(191)).to(torch.float16).cuda()
+    a1 = K.chunk_attention(params, q, cu_q, kp, vp, bt, sl, mx, kt, vt)
+    a2 = K.chunk_attention(params, q, cu_q, kp, vp, bt, sl, mx, kt, vt)
+    qd = q[:len(lens)].contiguous()
+    d1 = K.decode_attention(params, qd, kp, vp, bt, sl, mx, kt, vt)
+    d2 = K.decode_attention(params, qd, kp, vp, bt, sl, mx, kt, vt)
+    torch.cuda.synchronize()
+    assert torch.equal(a1, a2) and torch.equal(d1, d2)

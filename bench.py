@@ -20,6 +20,11 @@ Prints one JSON line. Numbers:
 sequences holding 16384 tokens each; one step writes a 128-token chunk per sequence (one tile
 completed and quantized per sequence and head) and runs causal attention for its 1024 query
 rows over the quantized cache.
+
+--workload batched_paged (32 sequences, lengths U[4096, 32768] in permuted pages) and
+--workload long_context (one 131072-token sequence, 8 copies cycled) measure the decode-bound
+steps: append one token per sequence into staging (quantize-on-fill), then decode attention
+over the pages and the staging tile; the roofline is the decode's HBM fraction.
 """
 from __future__ import annotations
 
@@ -118,17 +123,20 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--layers", type=int, default=64,
-                    help="distinct layer copies cycled across steps (defeats the 256 MB MALL)")
+    ap.add_argument("--layers", type=int, default=None,
+                    help="distinct layer copies cycled across steps (defeats the 256 MB MALL); "
+                         "64 for one_layer_16k, 8 for long_context")
     ap.add_argument("--sinkhorn-iters", type=int, default=8)
     ap.add_argument("--preset", default="kvarn_k4v2_g128", choices=["kvarn_k4v2_g128", "kvarn_k2v2_g128", "kvarn_k4v4_g128"],
                     help="kv_cache_dtype preset (the released k4v2_g128 by default)")
     ap.add_argument("--context", type=int, default=16384)
-    ap.add_argument("--workload", choices=["one_layer_16k", "prefill_burst", "chunked_prefill"],
+    ap.add_argument("--workload", choices=["one_layer_16k", "prefill_burst", "chunked_prefill",
+                                           "batched_paged", "long_context"],
                     default="one_layer_16k",
                     help="one_layer_16k: batch 1 one decoder layer (default, the headline line); "
                          "prefill_burst: 64 sequences x 16384 tokens (131072 tiles) + one batched "
-                         "decode; chunked_prefill: 128-token chunks written and attended")
+                         "decode; chunked_prefill: 128-token chunks written and attended; "
+                         "batched_paged / long_context: append + decode steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
@@ -151,9 +159,11 @@ def main():
     params = K.params_from_dtype(args.preset, n_iters)
     if args.workload == "chunked_prefill":
         return chunked_prefill(args, K, synth, params, dev)
+    if args.workload in ("batched_paged", "long_context"):
+        return decode_steps(args, K, synth, params, dev)
     k_rec = K.page_bytes(params, K.KIND_K)
     v_rec = K.page_bytes(params, K.KIND_V)
-    L = max(1, args.layers) if args.workload == "one_layer_16k" else 1
+    L = max(1, args.layers or 64) if args.workload == "one_layer_16k" else 1
     print(f"[bench] generating {L} copies of {args.workload} (context {args.context})",
           file=sys.stderr, flush=True)
     layers = []
@@ -366,7 +376,7 @@ def chunked_prefill(args, K, synth, params, dev):
         # many query rows per page: attention is a dense contraction, so the bound is the
         # float16 matrix-core peak, priced on the attention's own FLOPs (QK and PV over each
         # row's causal prefix); the page stream per row is reported beside it
-        "roofline": {"kernel": "decode_pages_kernel (one row per query position)", "bound": "mfma",
+        "roofline": {"kernel": "mq_pages_kernel (16 query vectors per wave)", "bound": "mfma",
                      "achieved": round(attn_flops / (a_ms * 1e-3) / 1e12, 2),
                      "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_flops / (a_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
@@ -378,6 +388,212 @@ def chunked_prefill(args, K, synth, params, dev):
         "wall_s_timed": round(t_wall, 4),
         "source_hash": source_hash(),
     }
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_decode(w, n_iters: int, budget_s: float, tail: int, k_bits: int = 4,
+                        v_bits: int = 2):
+    """The float64 oracle's decode (dequantize each K and V page, then attention of the G query
+    heads of a KV head) on a bounded number of pages of sequence 0, KV head 0, scaled to the
+    step's pages over all sequences and KV heads."""
+    import numpy as np
+    from oracle import kvarn_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    nq = 4
+    k = w.k_src[:128 * nq].cpu().numpy()
+    v = w.v_src[:128 * nq].cpu().numpy()
+    tiles_k = np.stack([k[128 * i:128 * (i + 1), 0, :].T for i in range(nq)])
+    tiles_v = np.stack([v[128 * i:128 * (i + 1), 0, :].T for i in range(nq)])
+    rk = O.quantize_tiles(tiles_k, O.KIND_K, n_iters, k_bits=k_bits)
+    rv = O.quantize_tiles(tiles_v, O.KIND_V, n_iters, v_bits=v_bits)
+    q = w.step_inputs(0, device="cpu")[0].numpy()
+    G = w.hq // w.hkv
+    kt = np.asarray(k[:tail, 0, :], np.float64)
+    vt = np.asarray(v[:tail, 0, :], np.float64)
+
+    def run(pages):
+        kd = np.concatenate([O.dequantize_tiles(rk["codes"][i % nq], rk["r"][i % nq],
+                                                rk["s"][i % nq], rk["scale"][i % nq],
+                                                rk["zero"][i % nq], O.KIND_K).T
+                             for i in range(pages)] + [kt])
+        vd = np.concatenate([O.dequantize_tiles(rv["codes"][i % nq], rv["r"][i % nq],
+                                                rv["s"][i % nq], rv["scale"][i % nq],
+                                                rv["zero"][i % nq], O.KIND_V).T
+                             for i in range(pages)] + [vt])
+        for h in range(G):
+            O.attention(q[0, h].astype(np.float64), kd, vd, 1 / math.sqrt(128))
+
+    t0 = time.perf_counter()
+    run(8)
+    per_page = (time.perf_counter() - t0) / 8
+    pages = max(8, min(1024, int(budget_s / max(per_page, 1e-4))))
+    t0 = time.perf_counter()
+    run(pages)
+    per_page = (time.perf_counter() - t0) / pages
+    total_pages = sum(L // 128 for L in w.prompt_lens) * w.hkv
+    return per_page * total_pages, blas_threads, (
+        f"oracle decode of {G} query heads over {pages} pages (+{tail} staged tokens) of one "
+        f"KV head, scaled to {total_pages} (sequence, KV head) pages of one step")
+
+
+def decode_steps(args, K, synth, params, dev):
+    """Decode with appends over a paged cache, the decode-bound workloads. One step appends
+    one K/V token per sequence into its float16 staging tile (kvarn_append_tokens; a tile
+    that fills is quantized into its page) and then runs decode attention of all query heads
+    over the pages and the staging tile (kvarn_decode_attention).
+      batched_paged: 32 sequences, lengths U[4096, 32768] rounded to 128, pages placed by a
+        random permutation, K/V Student-t(3); ~530 MB of pages per step, larger than the
+        256 MB Infinity Cache;
+      long_context: one 131072-token sequence (117.5 MB of pages), so `--layers` distinct
+        copies (8 by default, as layers of a model) are cycled step by step.
+    Every step s starts from prompt length + s: re-running a step (warm-up, the timed pass,
+    the pass with events) rewrites the same staging position with the same token."""
+    import torch
+    S = args.steps
+    L = args.layers if args.layers else (8 if args.workload == "long_context" else 1)
+    print(f"[bench] generating {L} copies of {args.workload}", file=sys.stderr, flush=True)
+    k_rec = K.page_bytes(params, K.KIND_K)
+    v_rec = K.page_bytes(params, K.KIND_V)
+    n_steps = -(-max(S, args.warmup) // L)      # steps per copy
+    copies = []
+    q_launch = None
+    for c in range(L):
+        if args.workload == "batched_paged":
+            w = synth.batched_paged(device=dev, seed=2 + c, steps=n_steps)
+        else:
+            w = synth.long_context(device=dev, seed=3 + c, steps=n_steps)
+        B, hq, hkv = w.batch, w.hq, w.hkv
+        kp = K.new_pool(w.num_pages, hkv, K.KIND_K, params=params)
+        vp = K.new_pool(w.num_pages, hkv, K.KIND_V, params=params)
+        qkv = K.prepare_quantize_kv(params, w.k_src, w.v_src, w.tile_src_token,
+                                    w.tile_dst_page, kp, vp)
+        qkv()
+        if c == 0:                      # the prompt quantize launch, timed once per rep
+            q_launch = (qkv, w.tile_src_token.numel() * hkv)
+        bt = w.block_table.clone()
+        spare = n_steps // 128 + 1
+        for b, Lb in enumerate(w.prompt_lens):      # pages that staging tiles fill into
+            for j in range(spare):
+                bt[b, Lb // 128 + j] = int(w.free_pages[b + j * B])
+        kt = torch.zeros((B, hkv, 128, 128), dtype=torch.float16, device=dev)
+        vt = torch.zeros_like(kt)
+        base = torch.tensor(w.prompt_lens, dtype=torch.int32, device=dev)
+        lens = [base + s for s in range(n_steps + 1)]
+        max_len = max(w.prompt_lens) + n_steps
+        ws = K.new_workspace(params, B, hq, hkv, max_len)
+        out = torch.empty((B, hq, 128), dtype=torch.float16, device=dev)
+        steps = []
+        for s in range(n_steps):
+            q, kn, vn = w.step_inputs(s)
+            app = K.prepare_append(params, kn, vn, lens[s], kt, vt, bt, kp, vp)
+            dec = K.prepare_decode(params, q, kp, vp, bt, lens[s + 1], max_len, ws, out,
+                                   k_tail=kt, v_tail=vt)
+            steps.append((app, dec, q, kn, vn))
+        copies.append((w, steps, kp, vp, kt, vt, lens, ws, out))
+        if c == 0:
+            w0 = w
+        if c > 0:                       # the prompt sources are no longer needed
+            w.k_src = w.k_src[:0]
+            w.v_src = w.v_src[:0]
+    torch.cuda.synchronize()
+    B, hq, hkv = w0.batch, w0.hq, w0.hkv
+
+    def step_index(s):
+        return (s % L, (s // L) if L > 1 else s)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    for s in range(args.warmup):
+        c, i = step_index(s)
+        app, dec = copies[c][1][i][:2]
+        app(); dec()
+    torch.cuda.synchronize()
+    start, stop = ev(), ev()
+    t_wall = time.perf_counter()
+    start.record()
+    for s in range(S):
+        c, i = step_index(s)
+        app, dec = copies[c][1][i][:2]
+        app(); dec()
+    stop.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_step = start.elapsed_time(stop) / S
+    marks = [(ev(), ev(), ev()) for _ in range(S)]
+    torch.cuda.synchronize()
+    for s in range(S):
+        c, i = step_index(s)
+        app, dec = copies[c][1][i][:2]
+        e0, e1, e2 = marks[s]
+        e0.record(); app(); e1.record(); dec(); e2.record()
+    torch.cuda.synchronize()
+    a_ms = sum(m[0].elapsed_time(m[1]) for m in marks) / S
+    d_ms = sum(m[1].elapsed_time(m[2]) for m in marks) / S
+    # the prompt quantize launch of copy 0 (rewrites the same pages)
+    qkv, n_q_tiles = q_launch
+    qe = [(ev(), ev()) for _ in range(4)]
+    for e0, e1 in qe:
+        e0.record(); qkv(); e1.record()
+    torch.cuda.synchronize()
+    pq_ms = min(e0.elapsed_time(e1) for e0, e1 in qe)
+
+    # algorithmic bytes of a step, averaged over the timed steps: K+V records of the full
+    # pages, the staged float16 tokens, q and out; the append's token in and staging write
+    def dec_bytes(c, i):
+        w = copies[c][0]
+        tot = 0
+        for Lb in w.prompt_lens:
+            n = Lb + i + 1
+            tot += hkv * ((n // 128) * (k_rec + v_rec) + 2 * (n % 128) * 256)
+        return tot + 2 * B * hq * 256
+    d_bytes = sum(dec_bytes(*step_index(s)) for s in range(S)) / S
+    a_bytes = 2 * 2 * B * hkv * 256
+    value = (d_bytes + a_bytes) / (ms_step * 1e-3) / 1e9
+    decode_gbps = d_bytes / (d_ms * 1e-3) / 1e9
+    src_hash = source_hash()
+    pages_step = sum(Lb // 128 for Lb in w0.prompt_lens) * hkv
+    res = {
+        "metric": "decode-attn KV GB/s (% HBM roofline) + tiles quantized/s, k4v2_g128",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": S,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16 in/out, f32 compute",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: append 1 token per sequence + 1 decode step",
+                   "batch": B, "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": 128,
+                   "prompt_tokens": sum(w0.prompt_lens), "kv_cache_dtype": args.preset,
+                   "sinkhorn_iters": params.sinkhorn_iters, "copies_cycled": L,
+                   "parallelism": "single GPU"},
+        "timing": "ms_per_step over the timed steps with nothing recorded between launches; "
+                  "append_ms / decode_ms from the same steps run again with HIP events around "
+                  "each call on the launch stream",
+        "value_definition": "algorithmic bytes of one step (decode: K+V records of the full "
+                            "pages + staged float16 tokens + q + out; append: token in + "
+                            "staging write) / step time",
+        "decode_kv_gbps": round(decode_gbps, 1),
+        "decode_hbm_frac": round(decode_gbps / HBM_PEAK_GBPS, 4),
+        "decode_ms": round(d_ms, 5), "append_ms": round(a_ms, 5),
+        "prompt_quantize": {"tiles": 2 * n_q_tiles, "ms": round(pq_ms, 4),
+                            "tiles_per_s": round(2 * n_q_tiles / (pq_ms * 1e-3), 1)},
+        "roofline": {"kernel": "decode (pages + merge)", "bound": "hbm",
+                     "achieved": round(decode_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(decode_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": load_traffic("decode_pages_kernel", src_hash, args.workload),
+                     "per_launch": f"{pages_step} K+V page pairs x {k_rec + v_rec} B + staged "
+                                   "tokens + q/out (mean over the timed steps)",
+                     "launch_ms": round(d_ms, 5)},
+        "wall_s_timed": round(t_wall, 4),
+        "source_hash": src_hash,
+    }
+    if not args.no_cpu_baseline:
+        t_step, cores, sample = cpu_baseline_decode(w0, params.sinkhorn_iters, args.cpu_budget,
+                                                    tail=1 + S // 2, k_bits=params.k_bits,
+                                                    v_bits=params.v_bits)
+        res["cpu_baseline"] = {"value": round(d_bytes / t_step / 1e9, 5), "unit": "GB/s",
+                               "cores": cores, "kind": "oracle", "sample": sample,
+                               "seconds_per_step": round(t_step, 3)}
     print(json.dumps(res), flush=True)
 
 

@@ -248,6 +248,9 @@ kvarn_status kvarn_decode_attention(const kvarn_params* params, const void* q, i
     return KVARN_ERR_INVALID_ARG;
   if (num_q_heads % num_kv_heads != 0) return KVARN_ERR_INVALID_ARG;
   if (num_q_heads / num_kv_heads > kMaxGroup) return KVARN_ERR_UNSUPPORTED;
+  // grid limits: one merge grid row per sequence, one pages workgroup column per
+  // (sequence, KV head)
+  if (batch > 65535 || int64_t(batch) * num_kv_heads > INT32_MAX) return KVARN_ERR_UNSUPPORTED;
   if (!isfinite(softmax_scale)) return KVARN_ERR_INVALID_ARG;
   if (batch == 0) return KVARN_OK;
   if (!q || !seq_lens || !out || !workspace) return KVARN_ERR_INVALID_ARG;
@@ -285,6 +288,7 @@ kvarn_status kvarn_chunk_attention(const kvarn_params* params, const void* q, in
   if (num_q_heads % num_kv_heads != 0) return KVARN_ERR_INVALID_ARG;
   if (num_q_heads / num_kv_heads > kMaxGroup) return KVARN_ERR_UNSUPPORTED;
   if (total_q > 65535) return KVARN_ERR_UNSUPPORTED;      // one grid dimension per query row
+  if (int64_t(total_q) * num_kv_heads > INT32_MAX) return KVARN_ERR_UNSUPPORTED;
   if (!isfinite(softmax_scale)) return KVARN_ERR_INVALID_ARG;
   if (total_q == 0) return KVARN_OK;
   if (batch == 0) return KVARN_ERR_INVALID_ARG;            // query rows without a sequence

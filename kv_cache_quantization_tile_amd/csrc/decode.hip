@@ -43,7 +43,8 @@ struct DecodeSmem {
   WaveMeta meta[4];
 };
 
-// One workgroup: (output row, KV head g, split) = (blockIdx.x, y, z). Wave w handles page slots
+// One workgroup: (output row b, KV head g, split) = (blockIdx.x / Hkv, blockIdx.x % Hkv,
+// blockIdx.y). Wave w handles page slots
 // split * 4 * tpw + w + 4 k, k < tpw. Writes one partial (m, l, acc) per query head. With
 // tail buffers the grid has one more split, n_splits, which computes the tail partial. The
 // row's sequence, page slots and tail follow row_geometry. KB, VB: key and value code widths;
@@ -60,7 +61,10 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
                     float* __restrict__ ws) {
   __shared__ DecodeSmem sm;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int split = split_base + blockIdx.z, g = blockIdx.y, b = blockIdx.x;   // b: output row
+  // KV heads fastest: workgroups are dealt to the 8 XCDs round-robin in linear order, so each
+  // XCD gets the same heads of every sequence and equal work however ragged the lengths
+  const int split = split_base + blockIdx.y;
+  const int g = int(blockIdx.x) % num_kv_heads, b = int(blockIdx.x) / num_kv_heads;   // b: output row
   const int G = num_q_heads / num_kv_heads;
   const RowGeom rg = row_geometry(b, seq_lens, max_seq_len, cu_q, batch);
   if (split == n_splits) {   // the extra split (launched only with tail buffers): the tail
@@ -548,9 +552,9 @@ hipError_t launch_decode(int k_bits, int v_bits, const void* q, int32_t rows,
   if (n_split_wg > 0) {
     // without pages the only split launched is the tail, which must land on index ns
     const int32_t first = max_seq_len >= kTile ? 0 : ns;
-    // rows fastest, splits slowest: workgroups are dealt to the 8 XCDs round-robin in linear
-    // order, so consecutive ones must all carry work (a split axis of period 2, pages +
-    // tail, would leave every page workgroup on the even XCDs)
+    // (KV head, row) fastest, splits slowest: workgroups are dealt to the 8 XCDs round-robin
+    // in linear order, so consecutive ones must all carry work (a split axis of period 2,
+    // pages + tail, would leave every page workgroup on the even XCDs)
     hipError_t e;
     if (multi_row) {
       e = launch_mq_pages(k_bits, v_bits, q, rows, num_q_heads, num_kv_heads, k_pool, v_pool,
@@ -563,7 +567,7 @@ hipError_t launch_decode(int k_bits, int v_bits, const void* q, int32_t rows,
         // decode streams every page once; a read with one query per sequence reuses them
         auto kernel = cu_q ? decode_pages_kernel<KB, VB, kReuseLoad>
                            : decode_pages_kernel<KB, VB, kStreamLoad>;
-        hipLaunchKernelGGL(kernel, dim3(rows, num_kv_heads, n_split_wg), dim3(kThreads), 0,
+        hipLaunchKernelGGL(kernel, dim3(rows * num_kv_heads, n_split_wg), dim3(kThreads), 0,
                            stream, static_cast<const __half*>(q), num_q_heads, num_kv_heads,
                            static_cast<const uint8_t*>(k_pool),
                            static_cast<const uint8_t*>(v_pool), pool_num_pages, block_table,

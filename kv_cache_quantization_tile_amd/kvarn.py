@@ -416,6 +416,25 @@ def prepare_quantize_kv(params: Params, k_src, v_src, tile_src_token, tile_dst_p
     return Prepared(lib.kvarn_quantize_kv_tiles, args, "kvarn_quantize_kv_tiles")
 
 
+def prepare_append(params: Params, k_new, v_new, seq_lens, k_tail, v_tail, block_table,
+                   k_pool, v_pool, stream=None) -> Prepared:
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new"), (k_tail, "k_tail"), (v_tail, "v_tail")):
+        _need(t, nm, torch.float16)
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    _need(seq_lens, "seq_lens", torch.int32)
+    _need(block_table, "block_table", torch.int32)
+    B, hkv = k_new.shape[0], k_new.shape[1]
+    if tuple(k_tail.shape) != (B, hkv, 128, 128) or tuple(v_tail.shape) != (B, hkv, 128, 128):
+        raise ValueError("staging must be [B, Hkv, 128, 128]")
+    if block_table.dim() != 2 or block_table.shape[0] != B or not block_table.is_contiguous():
+        raise ValueError("block_table must be contiguous [B, width]")
+    args = (ctypes.byref(params), _ptr(k_new), _ptr(v_new), B, hkv, _ptr(seq_lens),
+            _ptr(k_tail), _ptr(v_tail), _ptr(block_table), block_table.shape[1], _ptr(k_pool),
+            _ptr(v_pool), _pools_n(params, k_pool, v_pool), _stream(stream))
+    return Prepared(lib.kvarn_append_tokens, args, "kvarn_append_tokens")
+
+
 def prepare_decode(params: Params, q, k_pool, v_pool, block_table, seq_lens, max_seq_len: int,
                    workspace, out, k_tail=None, v_tail=None, softmax_scale=None,
                    stream=None) -> Prepared:

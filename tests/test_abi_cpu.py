@@ -179,6 +179,8 @@ def test_decode_validation():
     assert _decode(p, B=0) == OK
     assert _decode(p, hq=63) == INVALID               # not a multiple of hkv
     assert _decode(p, hq=128) == UNSUP                # 16 query heads per KV head
+    assert _decode(p, B=70000) == UNSUP               # more sequences than merge grid rows
+    assert _decode(p, B=40000, hq=65535, hkv=65535) == UNSUP   # B * Hkv above INT32_MAX
     assert _decode(p, q=None) == INVALID
     assert _decode(p, kt=FAKE) == INVALID             # one tail without the other
     assert _decode(p, bts=10) == INVALID              # block table narrower than max pages
@@ -206,6 +208,7 @@ def test_chunk_attention_validation():
     assert _chunk(p, B=0) == INVALID                  # rows without a sequence
     assert _chunk(p, tq=-1) == INVALID
     assert _chunk(p, tq=70000) == UNSUP
+    assert _chunk(p, tq=40000, hq=65535, hkv=65535) == UNSUP   # rows * Hkv above INT32_MAX
     assert _chunk(p, cu=None) == INVALID
     assert _chunk(p, hq=63) == INVALID
     assert _chunk(p, hq=128) == UNSUP

@@ -219,8 +219,10 @@ KVARN_API kvarn_status kvarn_write_tokens(const kvarn_params* params, const void
  * non-decreasing, cu_q_dev[0] = 0, cu_q_dev[batch] = total_q.
  * Limits and other arguments as kvarn_decode_attention with total_q in place of batch;
  * workspace_dev: >= kvarn_chunk_workspace_bytes(params, total_q, ...) bytes; total_q <= 65535
- * (UNSUPPORTED above). With one query row per sequence the read runs the decode kernels
- * (bit-identical to kvarn_decode_attention); with more rows than sequences a wave holds 16
+ * (UNSUPPORTED above). With one query row per sequence the read runs the decode kernels in
+ * their split layout (the same result as kvarn_decode_attention up to float32 summation
+ * order: a decode of several sequences balances its pages across waves instead); with more
+ * rows than sequences a wave holds 16
  * query vectors (rows x heads of one sequence and KV head) and streams each page once for
  * all of them. */
 KVARN_API kvarn_status kvarn_chunk_attention(const kvarn_params* params, const void* q_dev,
@@ -257,7 +259,10 @@ KVARN_API size_t kvarn_chunk_workspace_bytes(const kvarn_params* params, int32_t
                                    int32_t num_q_heads, int32_t num_kv_heads,
                                    int32_t max_seq_len);
 
-/* Number of key splits the decode uses for this shape (0 if invalid); informative. */
+/* Number of key splits per (sequence, KV head) of the split layout for this shape (0 if
+ * invalid); informative. The split layout serves a decode of one sequence and chunk reads
+ * with one query row per sequence. A decode of 2 .. 1024 sequences instead gives every wave
+ * of one round (2,048 waves) an equal share of all (sequence, KV head, page) entries. */
 KVARN_API int32_t kvarn_decode_num_splits(const kvarn_params* params, int32_t batch,
                                 int32_t num_kv_heads, int32_t max_seq_len);
 

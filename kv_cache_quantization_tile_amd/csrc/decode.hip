@@ -41,15 +41,22 @@ struct DecodeSmem {
   float l[4][8];
   float acc[4][8][kDim];
   WaveMeta meta[4];
+  int32_t pref[kMaxBalancedRows + 1];   // balanced layout: full pages before each sequence
+  int32_t wsum[4];
 };
 
-// One workgroup: (output row b, KV head g, split) = (blockIdx.x / Hkv, blockIdx.x % Hkv,
-// blockIdx.y). Wave w handles page slots
+// Split layout (BAL = false): one workgroup per (output row b, KV head g, split) =
+// (blockIdx.x / Hkv, blockIdx.x % Hkv, blockIdx.y). Wave w handles page slots
 // split * 4 * tpw + w + 4 k, k < tpw. Writes one partial (m, l, acc) per query head. With
 // tail buffers the grid has one more split, n_splits, which computes the tail partial. The
-// row's sequence, page slots and tail follow row_geometry. KB, VB: key and value code widths;
-// AUX: cache policy of the page loads.
-template <int KB, int VB, int AUX>
+// row's sequence, page slots and tail follow row_geometry.
+// Balanced layout (BAL = true; one query row per sequence): the full pages of all (sequence,
+// KV head) segments, in order b, g, page, are one list of T pages, and wave i of the
+// 4 n_page_wg page waves streams list entries [floor(i T / W), floor((i + 1) T / W)), W the
+// wave count, crossing segment boundaries; it writes one partial per segment it touches, at
+// slot i + (b Hkv + g). Ragged lengths then cost no idle waves. Workgroups n_page_wg.. are the
+// tails, one per (b, g). KB, VB: key and value code widths; AUX: cache policy of the page loads.
+template <int KB, int VB, int AUX, bool BAL>
 __global__ void __launch_bounds__(kThreads)
 decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t num_kv_heads,
                     const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
@@ -58,23 +65,44 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
                     const int32_t* __restrict__ cu_q, int32_t batch, float qscale, int32_t tpw,
                     int32_t n_splits, int32_t split_base, const __half* __restrict__ k_tail,
                     const __half* __restrict__ v_tail, float tail_qscale,
-                    float* __restrict__ ws) {
+                    float* __restrict__ ws, int32_t n_page_wg) {
   __shared__ DecodeSmem sm;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  // KV heads fastest: workgroups are dealt to the 8 XCDs round-robin in linear order, so each
-  // XCD gets the same heads of every sequence and equal work however ragged the lengths
-  const int split = split_base + blockIdx.y;
-  const int g = int(blockIdx.x) % num_kv_heads, b = int(blockIdx.x) / num_kv_heads;   // b: output row
   const int G = num_q_heads / num_kv_heads;
+  // split layout: KV heads fastest, so that the workgroups dealt to the 8 XCDs round-robin in
+  // linear order give each XCD the same heads of every sequence
+  int split = 0, g = 0, b = 0;   // b: output row
+  if constexpr (BAL) {
+    if (int(blockIdx.x) >= n_page_wg) {   // a tail workgroup
+      const int k = int(blockIdx.x) - n_page_wg;
+      g = k % num_kv_heads;
+      b = k / num_kv_heads;
+      const RowGeom rt = row_geometry(b, seq_lens, max_seq_len, nullptr, batch);
+      tail_partial_at(q, num_q_heads, num_kv_heads, k_tail, v_tail, b, b, g, rt.tail_len,
+                      tail_qscale,
+                      ws + balanced_tail_offset(n_page_wg, batch, num_q_heads, num_kv_heads) +
+                          (int64_t(b) * num_q_heads + int64_t(g) * G) * kPartStride,
+                      kPartStride, reinterpret_cast<float (*)[kTile]>(&sm.acc[0][0][0]));
+      return;
+    }
+  } else {
+    split = split_base + blockIdx.y;
+    g = int(blockIdx.x) % num_kv_heads;
+    b = int(blockIdx.x) / num_kv_heads;
+  }
   const RowGeom rg = row_geometry(b, seq_lens, max_seq_len, cu_q, batch);
-  if (split == n_splits) {   // the extra split (launched only with tail buffers): the tail
-    tail_partial(q, num_q_heads, num_kv_heads, k_tail, v_tail, b, rg.b, g, rg.tail_len,
-                 tail_qscale, n_splits, ws, reinterpret_cast<float (*)[kTile]>(&sm.acc[0][0][0]));
-    return;
+  if constexpr (!BAL) {
+    if (split == n_splits) {   // the extra split (launched only with tail buffers): the tail
+      tail_partial(q, num_q_heads, num_kv_heads, k_tail, v_tail, b, rg.b, g, rg.tail_len,
+                   tail_qscale, n_splits, ws, reinterpret_cast<float (*)[kTile]>(&sm.acc[0][0][0]));
+      return;
+    }
   }
   const int n_full = rg.n_slots;      // page slots of this row (the last may be masked)
   const int slot0 = split * 4 * tpw;
-  if (slot0 >= n_full) return;
+  if constexpr (!BAL) {
+    if (slot0 >= n_full) return;
+  }
 
   const int n = l & 15, gq = l >> 4;
   const int h = n & 7;
@@ -106,11 +134,12 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
   const float fk = (l & 1) ? 16.f : (KB == 4 ? 256.f : 4.f);
   const float fv = (l & 1) ? 16.f : (VB == 2 ? 4.f : 256.f);
 
-  const int32_t* bt_row = block_table + int64_t(rg.b) * bt_stride;
-  auto page_of = [&](int slot) -> int64_t {
-    if (slot >= n_full) return -1;
-    const int32_t page = __builtin_amdgcn_readfirstlane(bt_row[slot]);
-    return (page < 0 || page >= pool_num_pages) ? -1 : int64_t(page);
+  // record index of page slot `slot` (< n_slots) of block-table row bt_r for KV head gg, or -1
+  // (no slot, or a page outside the pool)
+  auto rec_of = [&](const int32_t* bt_r, int slot, int n_slots, int gg) -> int64_t {
+    if (slot >= n_slots) return -1;
+    const int32_t page = __builtin_amdgcn_readfirstlane(bt_r[slot]);
+    return (page < 0 || page >= pool_num_pages) ? -1 : int64_t(page) * num_kv_heads + gg;
   };
   // record addresses are wave-uniform: their descriptors live in scalar registers
   auto uniform_ptr = [](const uint8_t* p) {
@@ -122,20 +151,18 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
   const LaneOffsets lo{uint32_t(n * 64 + 16 * gq), uint32_t(n * 32 + 8 * gq), uint32_t(4 * l)};
   // record index page * num_kv_heads + g fits 32 bits (the pool's record count is checked
   // on the host); byte offsets are 32 x 32 -> 64-bit products
-  // (the page id is re-read as a scalar here so that the offset arithmetic stays scalar)
-  // A page id below 0 (no page) gives an empty descriptor: its loads return zeros without
-  // touching memory, so the prefetches below need no branch.
-  auto krec_of = [&](int64_t page) {
-    const uint32_t ps = __builtin_amdgcn_readfirstlane(uint32_t(page < 0 ? 0 : page));
-    const uint32_t r = ps * uint32_t(num_kv_heads) + uint32_t(g);
+  // (the index is re-read as a scalar here so that the offset arithmetic stays scalar)
+  // A record index below 0 (no page) gives an empty descriptor: its loads return zeros
+  // without touching memory, so the prefetches below need no branch.
+  auto krec_of = [&](int64_t rec) {
+    const uint32_t r = __builtin_amdgcn_readfirstlane(uint32_t(rec < 0 ? 0 : rec));
     return record_rsrc(uniform_ptr(k_pool + uint64_t(r) * uint32_t(KeyRec<KB>::kRecord)),
-                       page < 0 ? 0 : KeyRec<KB>::kRecord);
+                       rec < 0 ? 0 : KeyRec<KB>::kRecord);
   };
-  auto vrec_of = [&](int64_t page) {
-    const uint32_t ps = __builtin_amdgcn_readfirstlane(uint32_t(page < 0 ? 0 : page));
-    const uint32_t r = ps * uint32_t(num_kv_heads) + uint32_t(g);
+  auto vrec_of = [&](int64_t rec) {
+    const uint32_t r = __builtin_amdgcn_readfirstlane(uint32_t(rec < 0 ? 0 : rec));
     return record_rsrc(uniform_ptr(v_pool + uint64_t(r) * uint32_t(ValRec<VB>::kRecord)),
-                       page < 0 ? 0 : ValRec<VB>::kRecord);
+                       rec < 0 ? 0 : ValRec<VB>::kRecord);
   };
   // Processes the page held in t; each part of t is reloaded with page `next` as soon as
   // this page has consumed it, so the loads overlap the rest of the page's work. A page
@@ -302,16 +329,10 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
     load_vcodes<AUX>(t, vrec_of(next), lo);
   };
 
-  PageRegs<KB, VB> t;
-  const int wslot = __builtin_amdgcn_readfirstlane(slot0 + w);   // this wave's first slot
-  int64_t cur = page_of(wslot);
-  load_meta<AUX>(t, krec_of(cur), vrec_of(cur), lo);
-  load_kcodes<AUX>(t, krec_of(cur), lo);
-  load_vcodes<AUX>(t, vrec_of(cur), lo);
-  // q is rotated while the first page's loads are in flight
-  {
+  // q_rot = H q * softmax_scale * log2(e) of (output row bq, KV head gh) into qo, maxq
+  auto rotate_q = [&](int bq, int gh) {
     float qr[32];
-    const __half* qrow = q + (int64_t(b) * num_q_heads + int64_t(g) * G + (head_ok ? h : 0)) * kDim + 32 * gq;
+    const __half* qrow = q + (int64_t(bq) * num_q_heads + int64_t(gh) * G + (head_ok ? h : 0)) * kDim + 32 * gq;
 #pragma unroll
     for (int k = 0; k < 4; ++k) load_h8(reinterpret_cast<const uint8_t*>(qrow + 8 * k), &qr[8 * k]);
     if (!head_ok) {
@@ -351,23 +372,148 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int j = 0; j < 4; ++j) qo[4 * s + j] = hi ? qr[8 * s + j] : qr[8 * s + 4 + j];
-  }
+  };
+  // the high / low column partners' accumulators and row sums added up: acc on every lane,
+  // the head's l returned
+  auto combine_columns = [&]() {
+#pragma unroll
+    for (int bb = 0; bb < 8; ++bb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[bb][i] += dpp_f<kDppRowRor8>(acc[bb][i]);
+    l_part += dpp_f<kDppRowRor8>(l_part);
+    return rows4_sum(l_part);
+  };
+
+  PageRegs<KB, VB> t;
+  if constexpr (BAL) {
+    // ---- full pages of every sequence and their prefix sums, in LDS ---------------------
+    {
+      const int per = (batch + kThreads - 1) / kThreads;   // <= 4 (batch <= kMaxBalancedRows)
+      int cnt[4], run = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int i = tid * per + k;
+        int v = 0;
+        if (k < per && i < batch) {
+          int32_t L = seq_lens[i];
+          L = L < 0 ? 0 : (L > max_seq_len ? max_seq_len : L);
+          v = L / kTile;
+        }
+        cnt[k] = v;
+        run += v;
+      }
+      int incl = run;   // inclusive scan over the wave
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (l >= off) incl += y;
+      }
+      if (l == 63) sm.wsum[w] = incl;
+      __syncthreads();
+      int excl = incl - run;
+      for (int ww = 0; ww < w; ++ww) excl += sm.wsum[ww];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int i = tid * per + k;
+        if (k < per && i < batch) {
+          sm.pref[i] = excl;
+          excl += cnt[k];
+        }
+      }
+      if (tid == 0) sm.pref[batch] = sm.wsum[0] + sm.wsum[1] + sm.wsum[2] + sm.wsum[3];
+      __syncthreads();
+    }
+    // (no workgroup barrier past this point: waves leave on their own)
+    // list of T pages (< 2^31, checked on the host), spread over min(4 n_page_wg, T) waves
+    const int T = __builtin_amdgcn_readfirstlane(num_kv_heads * sm.pref[batch]);
+    const int n_waves = min(4 * n_page_wg, T);
+    const int wi = __builtin_amdgcn_readfirstlane(4 * int(blockIdx.x) + w);   // wave-uniform
+    if (wi >= n_waves) return;
+    int64_t x = int64_t(T) * wi / n_waves;
+    const int64_t x_end = int64_t(T) * (wi + 1) / n_waves;
+    // list entry y (< T) -> sequence sb (the last with Hkv pref[sb] <= y, which has pages),
+    // KV head sg, page sp of its np full pages
+    auto locate = [&](int64_t y, int& sb, int& sg, int& sp, int& np) {
+      int lo2 = 0, hi2 = batch;
+      while (hi2 - lo2 > 1) {
+        const int mid = (lo2 + hi2) >> 1;
+        if (int64_t(num_kv_heads) * sm.pref[mid] <= y) lo2 = mid; else hi2 = mid;
+      }
+      sb = __builtin_amdgcn_readfirstlane(lo2);
+      np = __builtin_amdgcn_readfirstlane(sm.pref[sb + 1] - sm.pref[sb]);
+      const int off = int(y - int64_t(num_kv_heads) * sm.pref[sb]);
+      sg = __builtin_amdgcn_readfirstlane(off / np);
+      sp = __builtin_amdgcn_readfirstlane(off - sg * np);
+    };
+    int sb, sg, sp, np;
+    locate(x, sb, sg, sp, np);
+    int64_t cur = rec_of(block_table + int64_t(sb) * bt_stride, sp, np, sg);
+    load_meta<AUX>(t, krec_of(cur), vrec_of(cur), lo);
+    load_kcodes<AUX>(t, krec_of(cur), lo);
+    load_vcodes<AUX>(t, vrec_of(cur), lo);
+    while (x < x_end) {
+      // this segment: pages sp .. sp + n - 1 of (sb, sg)
+      const int n = int(min(x_end - x, int64_t(np - sp)));
+      const int32_t* bt_r = block_table + int64_t(sb) * bt_stride;
+      // the list entry after the segment (its loads are issued by the segment's last page)
+      const int64_t x_next = x + n;
+      int nb = sb, ng = sg, nsp = 0, nnp = 0;
+      int64_t after = -1;
+      if (x_next < x_end) {
+        locate(x_next, nb, ng, nsp, nnp);
+        after = rec_of(block_table + int64_t(nb) * bt_stride, nsp, nnp, ng);
+      }
+      rotate_q(sb, sg);
+      m_run = -INFINITY;
+      l_part = 0.f;
+#pragma unroll
+      for (int bb = 0; bb < 8; ++bb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[bb][i] = 0.f;
+      for (int k = 0; k < n; ++k) {
+        const int64_t next = k + 1 < n ? rec_of(bt_r, sp + k + 1, np, sg) : after;
+        process(t, next, cur >= 0, kTile);
+        cur = next;
+      }
+      // this wave's partial of the segment, slot wi + (sb Hkv + sg)
+      const float l_run = combine_columns();
+      if (hi && head_ok) {
+        float* part = ws + ((int64_t(wi) + int64_t(sb) * num_kv_heads + sg) * G + h) * kPartStride;
+        if (gq == 0) {
+          part[0] = m_run;
+          part[1] = l_run;
+        }
+#pragma unroll
+        for (int bb = 0; bb < 8; ++bb)
+          *reinterpret_cast<float4*>(part + 4 + 16 * bb + 4 * gq) =
+              make_float4(acc[bb][0], acc[bb][1], acc[bb][2], acc[bb][3]);
+      }
+      x = x_next;
+      sb = nb;
+      sg = ng;
+      sp = nsp;
+      np = nnp;
+    }
+    return;
+  } else {
+  const int32_t* bt_row = block_table + int64_t(rg.b) * bt_stride;
+  const int wslot = __builtin_amdgcn_readfirstlane(slot0 + w);   // this wave's first slot
+  int64_t cur = rec_of(bt_row, wslot, n_full, g);
+  load_meta<AUX>(t, krec_of(cur), vrec_of(cur), lo);
+  load_kcodes<AUX>(t, krec_of(cur), lo);
+  load_vcodes<AUX>(t, vrec_of(cur), lo);
+  // q is rotated while the first page's loads are in flight
+  rotate_q(b, g);
   // pages of this wave: slots wslot, wslot + 4, ... below n_full, at most tpw of them
   // (a loop with one exit keeps the running state in place across iterations)
   const int n_here = wslot < n_full ? min(tpw, (n_full - wslot + 3) >> 2) : 0;
   for (int k = 0; k < n_here; ++k) {
-    const int64_t next = k + 1 < n_here ? page_of(wslot + 4 * (k + 1)) : -1;
+    const int64_t next = k + 1 < n_here ? rec_of(bt_row, wslot + 4 * (k + 1), n_full, g) : -1;
     process(t, next, cur >= 0, wslot + 4 * k == n_full - 1 ? rg.mask_lim : kTile);
     cur = next;
   }
 
   // ---- combine the high / low columns, then the 4 waves --------------------------------
-#pragma unroll
-  for (int bb = 0; bb < 8; ++bb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[bb][i] += dpp_f<kDppRowRor8>(acc[bb][i]);
-  l_part += dpp_f<kDppRowRor8>(l_part);
-  const float l_run = rows4_sum(l_part);
+  const float l_run = combine_columns();
   if (hi) {
     if (gq == 0) {
       sm.m[w][h] = m_run;
@@ -409,6 +555,7 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
       }
     }
   }
+  }
 }
 
 // Merge the splits of one (sequence, query head): log-sum-exp weights, H^T on the page
@@ -416,14 +563,19 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
 // per (pair of query heads, sequence): 128 threads per head, thread c owns channel c; split
 // weights are computed once in LDS, then every thread streams its channel of all partials
 // (independent loads). (Pairs halve the workgroup count of a many-row read.)
+// BAL: the balanced layout of decode_pages_kernel (n_page_wg page workgroups); the partials of
+// segment (b, g) are the slots i + (b Hkv + g) of the waves i whose page ranges meet it.
+template <bool BAL>
 __global__ void __launch_bounds__(256)
-decode_merge_kernel(int32_t num_q_heads, const int32_t* __restrict__ seq_lens, int32_t max_seq_len,
+decode_merge_kernel(int32_t num_q_heads, int32_t num_kv_heads,
+                    const int32_t* __restrict__ seq_lens, int32_t max_seq_len,
                     const int32_t* __restrict__ cu_q, int32_t batch, int32_t tiles_per_split,
                     int32_t n_splits, int32_t has_tail, const float* __restrict__ ws,
-                    __half* __restrict__ out) {
+                    int32_t n_page_wg, __half* __restrict__ out) {
   __shared__ float wsh_[2][kMaxMergeSplits + 1];
   __shared__ float red_[2][2][2];
   __shared__ float xs_[2][kDim];
+  __shared__ int32_t cnt[4][2];
   const int pair = threadIdx.x >> 7;
   float* wsh = wsh_[pair];
   float (*red)[2] = red_[pair];
@@ -434,13 +586,58 @@ decode_merge_kernel(int32_t num_q_heads, const int32_t* __restrict__ seq_lens, i
   const int b = blockIdx.y;   // b: output row
   const int c = threadIdx.x & 127, lane = c & 63, wv = c >> 6;
   const RowGeom rg = row_geometry(b, seq_lens, max_seq_len, cu_q, batch);
-  const int used = (rg.n_slots + tiles_per_split - 1) / tiles_per_split;
   const bool tail = has_tail && rg.tail_len != 0;
-  const float* base = ws + (int64_t(b) * num_q_heads + hq) * (n_splits + 1) * kPartStride;
+  int used;
+  const float* base;     // the first split's partial
+  int64_t pstride;       // floats from one split's partial to the next
+  const float* tailp;    // the tail partial
+  if constexpr (BAL) {
+    // full pages before sequence b and in all, over the whole workgroup
+    int before = 0, total = 0;
+    for (int k = threadIdx.x; k < batch; k += 256) {
+      int32_t L = seq_lens[k];
+      L = L < 0 ? 0 : (L > max_seq_len ? max_seq_len : L);
+      total += L / kTile;
+      before += k < b ? L / kTile : 0;
+    }
+    for (int off = 32; off >= 1; off >>= 1) {
+      total += __builtin_amdgcn_ds_bpermute((lane ^ off) << 2, total);
+      before += __builtin_amdgcn_ds_bpermute((lane ^ off) << 2, before);
+    }
+    if (lane == 0) {
+      cnt[threadIdx.x >> 6][0] = total;
+      cnt[threadIdx.x >> 6][1] = before;
+    }
+    __syncthreads();
+    total = cnt[0][0] + cnt[1][0] + cnt[2][0] + cnt[3][0];
+    before = cnt[0][1] + cnt[1][1] + cnt[2][1] + cnt[3][1];
+    const int G = num_q_heads / num_kv_heads;
+    const int g = hq / G, hh = hq - g * G;
+    const int P = rg.n_slots;                        // full pages of b
+    const int64_t T = int64_t(num_kv_heads) * total;
+    const int64_t W = T < 4 * int64_t(n_page_wg) ? T : 4 * int64_t(n_page_wg);
+    used = 0;
+    base = ws;
+    if (P > 0) {
+      // wave of list entry y: floor(((y + 1) W - 1) / T)
+      const int64_t F0 = int64_t(num_kv_heads) * before + int64_t(g) * P;
+      const int64_t i0 = ((F0 + 1) * W - 1) / T, i1 = ((F0 + P) * W - 1) / T;
+      used = int(i1 - i0 + 1);
+      base = ws + ((i0 + int64_t(b) * num_kv_heads + g) * G + hh) * kPartStride;
+    }
+    pstride = int64_t(G) * kPartStride;
+    tailp = ws + balanced_tail_offset(n_page_wg, batch, num_q_heads, num_kv_heads) +
+            (int64_t(b) * num_q_heads + hq) * kPartStride;
+  } else {
+    used = (rg.n_slots + tiles_per_split - 1) / tiles_per_split;
+    base = ws + (int64_t(b) * num_q_heads + hq) * (n_splits + 1) * kPartStride;
+    pstride = kPartStride;
+    tailp = base + int64_t(n_splits) * kPartStride;
+  }
   // 1. global max over the used splits (and the tail)
   float M = -INFINITY;
-  for (int s = c; s < used; s += 128) M = fmaxf(M, base[s * kPartStride]);
-  if (tail && c == 0) M = fmaxf(M, base[n_splits * kPartStride]);
+  for (int s = c; s < used; s += 128) M = fmaxf(M, base[s * pstride]);
+  if (tail && c == 0) M = fmaxf(M, tailp[0]);
   for (int off = 32; off >= 1; off >>= 1)
     M = fmaxf(M, __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ off) << 2, __float_as_int(M))));
   if (lane == 0) red[0][wv] = M;
@@ -449,14 +646,14 @@ decode_merge_kernel(int32_t num_q_heads, const int32_t* __restrict__ seq_lens, i
   // 2. split weights exp2(m_s - M) and the total l
   float lsum = 0.f;
   for (int s = c; s < used; s += 128) {
-    const float e = M == -INFINITY ? 0.f : exp2f(base[s * kPartStride] - M);
+    const float e = M == -INFINITY ? 0.f : exp2f(base[s * pstride] - M);
     wsh[s] = e;
-    lsum = fmaf(e, base[s * kPartStride + 1], lsum);
+    lsum = fmaf(e, base[s * pstride + 1], lsum);
   }
   if (c == 0) {
-    const float e = (tail && M != -INFINITY) ? exp2f(base[n_splits * kPartStride] - M) : 0.f;
+    const float e = (tail && M != -INFINITY) ? exp2f(tailp[0] - M) : 0.f;
     wsh[kMaxMergeSplits] = e;
-    if (tail) lsum = fmaf(e, base[n_splits * kPartStride + 1], lsum);
+    if (tail) lsum = fmaf(e, tailp[1], lsum);
   }
   for (int off = 32; off >= 1; off >>= 1)
     lsum += __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ off) << 2, __float_as_int(lsum)));
@@ -467,16 +664,16 @@ decode_merge_kernel(int32_t num_q_heads, const int32_t* __restrict__ seq_lens, i
   float a = 0.f;
   int s = 0;
   for (; s + 4 <= used; s += 4) {
-    const float v0 = base[(s + 0) * kPartStride + 4 + c];
-    const float v1 = base[(s + 1) * kPartStride + 4 + c];
-    const float v2 = base[(s + 2) * kPartStride + 4 + c];
-    const float v3 = base[(s + 3) * kPartStride + 4 + c];
+    const float v0 = base[(s + 0) * pstride + 4 + c];
+    const float v1 = base[(s + 1) * pstride + 4 + c];
+    const float v2 = base[(s + 2) * pstride + 4 + c];
+    const float v3 = base[(s + 3) * pstride + 4 + c];
     a = fmaf(wsh[s], v0, a);
     a = fmaf(wsh[s + 1], v1, a);
     a = fmaf(wsh[s + 2], v2, a);
     a = fmaf(wsh[s + 3], v3, a);
   }
-  for (; s < used; ++s) a = fmaf(wsh[s], base[s * kPartStride + 4 + c], a);
+  for (; s < used; ++s) a = fmaf(wsh[s], base[s * pstride + 4 + c], a);
   // 4. H^T = H over the 128 channels: bits 0..5 across the lanes of a wave, bit 6 via LDS
   {
 #define KVARN_MSTAGE(M_, FN)                          \
@@ -497,7 +694,7 @@ decode_merge_kernel(int32_t num_q_heads, const int32_t* __restrict__ seq_lens, i
     a = (c & 64) ? (p - a) : (a + p);
     a *= kInvSqrt128;
   }
-  if (tail) a = fmaf(wsh[kMaxMergeSplits], base[n_splits * kPartStride + 4 + c], a);
+  if (tail) a = fmaf(wsh[kMaxMergeSplits], tailp[4 + c], a);
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   if (head_ok) out[(int64_t(b) * num_q_heads + hq) * kDim + c] = __float2half_rn(a * inv);
 }
@@ -524,10 +721,26 @@ int32_t decode_num_splits(int32_t batch, int32_t num_kv_heads, int32_t max_seq_l
   return ns < 1 ? 1 : ns;
 }
 
+// Page workgroups of the balanced layout for a decode of this shape (one query row per
+// sequence), or 0 where the split layout runs: a single sequence (its splits are already
+// even), more sequences than the LDS prefix holds, or a page list that could reach 2^31.
+int32_t decode_balanced_wg(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len) {
+  const int64_t max_full = max_seq_len / kTile;
+  const int64_t work = int64_t(batch) * num_kv_heads * max_full;   // >= the page list length
+  if (batch < 2 || batch > kMaxBalancedRows || max_full < 1 || work >= (int64_t(1) << 31)) return 0;
+  const int64_t wg = (work + 3) / 4;
+  return int32_t(wg < kBalancedPageWg ? wg : kBalancedPageWg);
+}
+
 size_t decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                               int32_t max_seq_len) {
   const int32_t ns = decode_num_splits(batch, num_kv_heads, max_seq_len);
-  return size_t(batch) * num_q_heads * (ns + 1) * kPartStride * sizeof(float);
+  const size_t split = size_t(batch) * num_q_heads * (ns + 1) * kPartStride * sizeof(float);
+  const int32_t wg = decode_balanced_wg(batch, num_kv_heads, max_seq_len);
+  if (wg == 0) return split;
+  const size_t bal = size_t(balanced_tail_offset(wg, batch, num_q_heads, num_kv_heads) +
+                            int64_t(batch) * num_q_heads * kPartStride) * sizeof(float);
+  return bal > split ? bal : split;
 }
 
 hipError_t launch_decode(int k_bits, int v_bits, const void* q, int32_t rows,
@@ -539,14 +752,35 @@ hipError_t launch_decode(int k_bits, int v_bits, const void* q, int32_t rows,
                          hipStream_t stream) {
   // several query rows of one sequence (more rows than sequences): the multi-query kernel
   const bool multi_row = cu_q != nullptr && rows > batch;
+  const bool has_tail = k_tail != nullptr && v_tail != nullptr;
+  const float qscale = softmax_scale * kLog2e;
+  float* ws = static_cast<float*>(workspace);
+  // a decode of several sequences: the balanced layout (equal page counts per wave)
+  const int32_t bal_wg = cu_q == nullptr ? decode_balanced_wg(rows, num_kv_heads, max_seq_len) : 0;
+  if (bal_wg > 0) {
+    const int32_t n_wg = bal_wg + (has_tail ? rows * num_kv_heads : 0);
+    const hipError_t e = with_preset(k_bits, v_bits, [&](auto kb, auto vb) {
+      constexpr int KB = decltype(kb)::value, VB = decltype(vb)::value;
+      hipLaunchKernelGGL((decode_pages_kernel<KB, VB, kStreamLoad, true>), dim3(n_wg),
+                         dim3(kThreads), 0, stream, static_cast<const __half*>(q), num_q_heads,
+                         num_kv_heads, static_cast<const uint8_t*>(k_pool),
+                         static_cast<const uint8_t*>(v_pool), pool_num_pages, block_table,
+                         bt_stride, seq_lens, max_seq_len, cu_q, batch, qscale * kInvSqrt128,
+                         1, 1, 0, static_cast<const __half*>(k_tail),
+                         static_cast<const __half*>(v_tail), qscale, ws, bal_wg);
+    });
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_merge_kernel<true>, dim3((num_q_heads + 1) / 2, rows), dim3(256),
+                       0, stream, num_q_heads, num_kv_heads, seq_lens, max_seq_len, cu_q, batch,
+                       1, 1, has_tail ? 1 : 0, static_cast<const float*>(ws), bal_wg,
+                       static_cast<__half*>(out));
+    return hipGetLastError();
+  }
   const int32_t tpw = decode_tiles_per_wave(rows, num_kv_heads, max_seq_len);
   const int32_t per_split =
       multi_row ? mq_slots_per_split(rows, num_q_heads, num_kv_heads, max_seq_len) : 4 * tpw;
   const int32_t ns = multi_row ? mq_num_splits(rows, num_q_heads, num_kv_heads, max_seq_len)
                                : decode_num_splits(rows, num_kv_heads, max_seq_len);
-  const float qscale = softmax_scale * kLog2e;
-  float* ws = static_cast<float*>(workspace);
-  const bool has_tail = k_tail != nullptr && v_tail != nullptr;
   // page splits (only if a full page can exist) plus, with tail buffers, one tail split
   const int32_t n_split_wg = (max_seq_len >= kTile ? ns : 0) + (has_tail ? 1 : 0);
   if (n_split_wg > 0) {
@@ -565,22 +799,23 @@ hipError_t launch_decode(int k_bits, int v_bits, const void* q, int32_t rows,
       e = with_preset(k_bits, v_bits, [&](auto kb, auto vb) {
         constexpr int KB = decltype(kb)::value, VB = decltype(vb)::value;
         // decode streams every page once; a read with one query per sequence reuses them
-        auto kernel = cu_q ? decode_pages_kernel<KB, VB, kReuseLoad>
-                           : decode_pages_kernel<KB, VB, kStreamLoad>;
+        auto kernel = cu_q ? decode_pages_kernel<KB, VB, kReuseLoad, false>
+                           : decode_pages_kernel<KB, VB, kStreamLoad, false>;
         hipLaunchKernelGGL(kernel, dim3(rows * num_kv_heads, n_split_wg), dim3(kThreads), 0,
                            stream, static_cast<const __half*>(q), num_q_heads, num_kv_heads,
                            static_cast<const uint8_t*>(k_pool),
                            static_cast<const uint8_t*>(v_pool), pool_num_pages, block_table,
                            bt_stride, seq_lens, max_seq_len, cu_q, batch, qscale * kInvSqrt128,
                            tpw, ns, first, static_cast<const __half*>(k_tail),
-                           static_cast<const __half*>(v_tail), qscale, ws);
+                           static_cast<const __half*>(v_tail), qscale, ws, 0);
       });
     }
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(decode_merge_kernel, dim3((num_q_heads + 1) / 2, rows), dim3(256), 0, stream,
-                     num_q_heads, seq_lens, max_seq_len, cu_q, batch, per_split, ns,
-                     has_tail ? 1 : 0, static_cast<const float*>(ws), static_cast<__half*>(out));
+  hipLaunchKernelGGL(decode_merge_kernel<false>, dim3((num_q_heads + 1) / 2, rows), dim3(256), 0,
+                     stream, num_q_heads, num_kv_heads, seq_lens, max_seq_len, cu_q, batch,
+                     per_split, ns, has_tail ? 1 : 0, static_cast<const float*>(ws), 0,
+                     static_cast<__half*>(out));
   return hipGetLastError();
 }
 

@@ -16,6 +16,20 @@ constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kPartStride = 132;  // floats per partial: m, l, pad, pad, acc[128]
 constexpr int kMaxMergeSplits = 4096;  // splits one merge workgroup can weight (LDS)
+// Balanced decode layout (one query row per sequence): at most this many sequences (their
+// page prefix sums live in LDS) and 4 * kBalancedPageWg page waves (one round of 2 waves per
+// SIMD on 256 CUs).
+constexpr int kMaxBalancedRows = 1024;
+constexpr int kBalancedPageWg = 512;
+
+// Floats of the balanced layout's page partials: one slot per (page wave, segment) index sum
+// i + (b Hkv + g), G query heads each; the tail partials (one per (row, query head)) follow.
+__host__ __device__ inline int64_t balanced_tail_offset(int32_t n_page_wg, int32_t batch,
+                                                        int32_t num_q_heads,
+                                                        int32_t num_kv_heads) {
+  return (4 * int64_t(n_page_wg) + int64_t(batch) * num_kv_heads) *
+         (num_q_heads / num_kv_heads) * kPartStride;
+}
 
 __device__ __forceinline__ float4v mfma16x16x32(const half8& a, const half8& b, const float4v& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -292,11 +306,11 @@ __device__ __forceinline__ RowGeom row_geometry(int row, const int32_t* __restri
 // for output row `row`, written as split n_splits of each query head's partials. Run by the
 // extra split of decode_pages_kernel; wave w handles heads 2w, 2w+1 of the group; p_sm is
 // 8 x 128 floats of LDS.
-__device__ void tail_partial(const __half* __restrict__ q, int32_t num_q_heads,
-                             int32_t num_kv_heads, const __half* __restrict__ k_tail,
-                             const __half* __restrict__ v_tail, int row, int sb, int g, int T,
-                             float qscale, int32_t n_splits, float* __restrict__ ws,
-                             float (*p_sm)[kTile]) {
+__device__ void tail_partial_at(const __half* __restrict__ q, int32_t num_q_heads,
+                                int32_t num_kv_heads, const __half* __restrict__ k_tail,
+                                const __half* __restrict__ v_tail, int row, int sb, int g, int T,
+                                float qscale, float* __restrict__ part0, int64_t head_stride,
+                                float (*p_sm)[kTile]) {
   const int G = num_q_heads / num_kv_heads;
   if (T == 0) return;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
@@ -347,7 +361,7 @@ __device__ void tail_partial(const __half* __restrict__ q, int32_t num_q_heads,
       o0 = fmaf(p, h2f(uint16_t(vv & 0xFFFF)), o0);
       o1 = fmaf(p, h2f(uint16_t(vv >> 16)), o1);
     }
-    float* part = ws + ((int64_t(row) * num_q_heads + hq) * (n_splits + 1) + n_splits) * kPartStride;
+    float* part = part0 + hh * head_stride;
     *reinterpret_cast<float2*>(part + 4 + 2 * l) = make_float2(o0, o1);
     if (l == 0) {
       part[0] = mx;
@@ -355,6 +369,21 @@ __device__ void tail_partial(const __half* __restrict__ q, int32_t num_q_heads,
     }
     __builtin_amdgcn_wave_barrier();
   }
+}
+
+// The same with the split layout of the workspace: (row, query head, split), the tail in
+// split n_splits.
+__device__ __forceinline__ void tail_partial(const __half* __restrict__ q, int32_t num_q_heads,
+                                             int32_t num_kv_heads,
+                                             const __half* __restrict__ k_tail,
+                                             const __half* __restrict__ v_tail, int row, int sb,
+                                             int g, int T, float qscale, int32_t n_splits,
+                                             float* __restrict__ ws, float (*p_sm)[kTile]) {
+  const int G = num_q_heads / num_kv_heads;
+  tail_partial_at(q, num_q_heads, num_kv_heads, k_tail, v_tail, row, sb, g, T, qscale,
+                  ws + ((int64_t(row) * num_q_heads + int64_t(g) * G) * (n_splits + 1) + n_splits) *
+                           kPartStride,
+                  int64_t(n_splits + 1) * kPartStride, p_sm);
 }
 
 }  // namespace

@@ -217,7 +217,7 @@ def test_chunk_attention_validation():
     assert _chunk(p, scale=float("inf")) == INVALID
     assert _chunk(p, q=ctypes.c_void_p(0x10002)) == INVALID
     need = K.chunk_workspace_bytes(p, 16, 64, 8, 16384)
-    assert need >= K.decode_workspace_bytes(p, 16, 64, 8, 16384)
+    assert need >= 16 * 64 * (K.decode_num_splits(p, 16, 8, 16384) + 1) * 132 * 4   # split layout
     assert _chunk(p, wsb=need - 1) == WS
 
 
@@ -228,7 +228,7 @@ def test_chunk_workspace_formula():
     for tq, hq, hkv, mx in ((1024, 64, 8, 16512), (16, 64, 8, 16384), (3, 8, 8, 100),
                             (200, 8, 1, 131072), (65535, 8, 8, 1024)):
         b = K.chunk_workspace_bytes(p, tq, hq, hkv, mx)
-        d = K.decode_workspace_bytes(p, tq, hq, hkv, mx)
+        d = tq * hq * (K.decode_num_splits(p, tq, hkv, mx) + 1) * 132 * 4   # split layout
         assert b >= d and b % (tq * hq * 132 * 4) == 0
         ns = b // (tq * hq * 132 * 4) - 1
         assert 1 <= ns <= max(1, mx // 128)
@@ -237,11 +237,26 @@ def test_chunk_workspace_formula():
     assert K.chunk_workspace_bytes(p, 16, 128, 8, 1024) == 0
 
 
+def _balanced_partials(B, hq, hkv, mx):
+    """Partials of the balanced decode layout (2..1024 sequences): one slot per (page wave,
+    segment) index sum i + (b Hkv + g) with i < 4 x page workgroups (at most 512, one round of
+    2 waves per SIMD on 256 CUs), G query heads each, then one tail partial per (b, query head)."""
+    work = B * hkv * (mx // 128)
+    if B < 2 or B > 1024 or mx < 128 or work >= 2 ** 31:
+        return 0
+    wg = min((work + 3) // 4, 512)
+    return (4 * wg + B * hkv) * (hq // hkv) + B * hq
+
+
 def test_decode_workspace_formula():
     p = K.params_from_dtype()
-    for B, hq, hkv, mx in ((1, 64, 8, 16384), (32, 64, 8, 32768), (1, 64, 8, 131072), (64, 64, 8, 16384), (3, 8, 8, 100)):
+    for B, hq, hkv, mx in ((1, 64, 8, 16384), (32, 64, 8, 32768), (1, 64, 8, 131072),
+                           (64, 64, 8, 16384), (3, 8, 8, 100), (4, 16, 2, 1400),
+                           (1024, 64, 8, 4096), (1025, 64, 8, 4096)):
         ns = K.decode_num_splits(p, B, hkv, mx)
         assert ns >= 1
-        assert K.decode_workspace_bytes(p, B, hq, hkv, mx) == B * hq * (ns + 1) * 132 * 4
+        split = B * hq * (ns + 1)
+        want = max(split, _balanced_partials(B, hq, hkv, mx)) * 132 * 4
+        assert K.decode_workspace_bytes(p, B, hq, hkv, mx) == want
     assert K.decode_workspace_bytes(p, 1, 64, 8, -1) == 0
     assert K.decode_workspace_bytes(p, 1, 128, 8, 1024) == 0

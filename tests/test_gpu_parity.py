@@ -280,6 +280,51 @@ def test_decode_many_splits_and_max_seq_len_clamp(K):
     say(f"max rel err {err:.3e}")
 
 
+@pytest.mark.parametrize("B,hkv,G,hi", [(3, 1, 8, 260), (300, 1, 2, 700), (1024, 1, 1, 300),
+                                        (1025, 1, 1, 300), (5, 2, 4, 128 * 500)])
+def test_decode_balanced_layout(K, B, hkv, G, hi):
+    """A decode of 2..1024 sequences gives every wave an equal share of all (sequence, KV
+    head, page) entries, crossing sequence boundaries; 1025 sequences take the split layout.
+    Cases: fewer pages than waves (3 sequences of at most 2 pages), several prefix entries per
+    thread (300 and 1024 sequences, lengths from 0 to a few pages, some without a full page),
+    and 5 long sequences (pages per wave above one segment). Every row is compared with the
+    same sequence decoded alone (the split layout: same sums, another float32 order), sampled
+    rows with the oracle."""
+    gen = torch.Generator().manual_seed(900 + B)
+    lens = torch.randint(0, hi + 1, (B,), generator=gen).tolist()
+    lens[0], lens[-1] = 0, hi
+    if B > 3:
+        lens[1], lens[2] = 127, 128
+    params = K.params_from_dtype("kvarn_k4v2_g128", 2)
+    say(f"decode balanced layout B={B} hkv={hkv} G={G} pages={sum(L // 128 for L in lens)}")
+    kp, vp, bt, kt, vt, sl, _ = _build_cache(K, params, lens, hkv, seed=910 + B)
+    q = torch.randn((B, G * hkv, 128), generator=gen).to(torch.float16).cuda()
+    mx = max(lens)
+    out = K.decode_attention(params, q, kp, vp, bt, sl, mx, kt, vt)
+    one = torch.empty_like(out)
+    for b in range(B):
+        one[b:b + 1] = K.decode_attention(params, q[b:b + 1].contiguous(), kp, vp,
+                                          bt[b:b + 1].contiguous(), sl[b:b + 1], mx,
+                                          kt[b:b + 1].contiguous(), vt[b:b + 1].contiguous())
+    torch.cuda.synchronize()
+    of, sf = out.float(), one.float()
+    empty = torch.tensor([L == 0 for L in lens]).cuda()
+    assert torch.all(out[empty] == 0) and torch.all(one[empty] == 0)
+    scale = sf.abs().amax(dim=-1, keepdim=True).clamp_min(1e-30)
+    diff = float(((of - sf).abs() / scale).max())
+    assert diff <= 2e-3, diff
+    rng = np.random.default_rng(920 + B)
+    pick, budget = [], 1200         # oracle pages (K and V records per KV head)
+    for b in [B - 1] + rng.permutation(B).tolist():
+        if len(pick) < 12 and b not in pick and lens[b] // 128 * hkv <= budget:
+            pick.append(b)
+            budget -= lens[b] // 128 * hkv
+    err = T.check_decode(q, out, kp, vp, bt, sl, G, rows=[(b, g) for b in pick for g in range(hkv)],
+                         k_tail=kt, v_tail=vt)
+    say(f"  all rows vs one-sequence decodes: max rel diff {diff:.1e}; {len(pick)} sequences vs "
+        f"the oracle: max rel err {err:.2e}")
+
+
 def test_decode_without_tail_buffers(K):
     """NULL tails: tokens past the last full page are ignored."""
     lens = [128 * 5 + 40, 256]

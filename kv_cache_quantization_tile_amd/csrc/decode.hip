@@ -421,6 +421,11 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
       }
       if (tid == 0) sm.pref[batch] = sm.wsum[0] + sm.wsum[1] + sm.wsum[2] + sm.wsum[3];
       __syncthreads();
+      if (blockIdx.x == 0) {   // for the merge
+        int32_t* wp = reinterpret_cast<int32_t*>(
+            ws + balanced_pref_offset(n_page_wg, batch, num_q_heads, num_kv_heads));
+        for (int i = tid; i <= batch; i += kThreads) wp[i] = sm.pref[i];
+      }
     }
     // (no workgroup barrier past this point: waves leave on their own)
     // list of T pages (< 2^31, checked on the host), spread over min(4 n_page_wg, T) waves
@@ -575,7 +580,6 @@ decode_merge_kernel(int32_t num_q_heads, int32_t num_kv_heads,
   __shared__ float wsh_[2][kMaxMergeSplits + 1];
   __shared__ float red_[2][2][2];
   __shared__ float xs_[2][kDim];
-  __shared__ int32_t cnt[4][2];
   const int pair = threadIdx.x >> 7;
   float* wsh = wsh_[pair];
   float (*red)[2] = red_[pair];
@@ -592,25 +596,10 @@ decode_merge_kernel(int32_t num_q_heads, int32_t num_kv_heads,
   int64_t pstride;       // floats from one split's partial to the next
   const float* tailp;    // the tail partial
   if constexpr (BAL) {
-    // full pages before sequence b and in all, over the whole workgroup
-    int before = 0, total = 0;
-    for (int k = threadIdx.x; k < batch; k += 256) {
-      int32_t L = seq_lens[k];
-      L = L < 0 ? 0 : (L > max_seq_len ? max_seq_len : L);
-      total += L / kTile;
-      before += k < b ? L / kTile : 0;
-    }
-    for (int off = 32; off >= 1; off >>= 1) {
-      total += __builtin_amdgcn_ds_bpermute((lane ^ off) << 2, total);
-      before += __builtin_amdgcn_ds_bpermute((lane ^ off) << 2, before);
-    }
-    if (lane == 0) {
-      cnt[threadIdx.x >> 6][0] = total;
-      cnt[threadIdx.x >> 6][1] = before;
-    }
-    __syncthreads();
-    total = cnt[0][0] + cnt[1][0] + cnt[2][0] + cnt[3][0];
-    before = cnt[0][1] + cnt[1][1] + cnt[2][1] + cnt[3][1];
+    // full pages before sequence b and in all: the prefix sums the pages kernel stored
+    const int32_t* pref = reinterpret_cast<const int32_t*>(
+        ws + balanced_pref_offset(n_page_wg, batch, num_q_heads, num_kv_heads));
+    const int before = pref[b], total = pref[batch];
     const int G = num_q_heads / num_kv_heads;
     const int g = hq / G, hh = hq - g * G;
     const int P = rg.n_slots;                        // full pages of b
@@ -634,10 +623,19 @@ decode_merge_kernel(int32_t num_q_heads, int32_t num_kv_heads,
     pstride = kPartStride;
     tailp = base + int64_t(n_splits) * kPartStride;
   }
-  // 1. global max over the used splits (and the tail)
-  float M = -INFINITY;
-  for (int s = c; s < used; s += 128) M = fmaxf(M, base[s * pstride]);
-  if (tail && c == 0) M = fmaxf(M, tailp[0]);
+  // 1. global max over the used splits (and the tail); the (m, l) of this thread's first
+  // split and of the tail stay in registers for step 2 (one memory round trip fewer)
+  float m_first = -INFINITY, l_first = 0.f, m_tail = -INFINITY, l_tail = 0.f;
+  if (c < used) {
+    m_first = base[c * pstride];
+    l_first = base[c * pstride + 1];
+  }
+  if (tail && c == 0) {
+    m_tail = tailp[0];
+    l_tail = tailp[1];
+  }
+  float M = fmaxf(m_first, m_tail);
+  for (int s = c + 128; s < used; s += 128) M = fmaxf(M, base[s * pstride]);
   for (int off = 32; off >= 1; off >>= 1)
     M = fmaxf(M, __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ off) << 2, __float_as_int(M))));
   if (lane == 0) red[0][wv] = M;
@@ -646,14 +644,16 @@ decode_merge_kernel(int32_t num_q_heads, int32_t num_kv_heads,
   // 2. split weights exp2(m_s - M) and the total l
   float lsum = 0.f;
   for (int s = c; s < used; s += 128) {
-    const float e = M == -INFINITY ? 0.f : exp2f(base[s * pstride] - M);
+    const float ms = s == c ? m_first : base[s * pstride];
+    const float ls = s == c ? l_first : base[s * pstride + 1];
+    const float e = M == -INFINITY ? 0.f : exp2f(ms - M);
     wsh[s] = e;
-    lsum = fmaf(e, base[s * pstride + 1], lsum);
+    lsum = fmaf(e, ls, lsum);
   }
   if (c == 0) {
-    const float e = (tail && M != -INFINITY) ? exp2f(tailp[0] - M) : 0.f;
+    const float e = (tail && M != -INFINITY) ? exp2f(m_tail - M) : 0.f;
     wsh[kMaxMergeSplits] = e;
-    if (tail) lsum = fmaf(e, tailp[1], lsum);
+    if (tail) lsum = fmaf(e, l_tail, lsum);
   }
   for (int off = 32; off >= 1; off >>= 1)
     lsum += __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ off) << 2, __float_as_int(lsum)));
@@ -661,17 +661,32 @@ decode_merge_kernel(int32_t num_q_heads, int32_t num_kv_heads,
   __syncthreads();
   lsum = red[1][0] + red[1][1];
   // 3. weighted sum of the rotated accumulators, channel c
+  // (16 independent loads in flight per round trip, then 8, 4, 1; the order of the sums
+  // does not depend on the unrolling)
   float a = 0.f;
   int s = 0;
-  for (; s + 4 <= used; s += 4) {
-    const float v0 = base[(s + 0) * pstride + 4 + c];
-    const float v1 = base[(s + 1) * pstride + 4 + c];
-    const float v2 = base[(s + 2) * pstride + 4 + c];
-    const float v3 = base[(s + 3) * pstride + 4 + c];
-    a = fmaf(wsh[s], v0, a);
-    a = fmaf(wsh[s + 1], v1, a);
-    a = fmaf(wsh[s + 2], v2, a);
-    a = fmaf(wsh[s + 3], v3, a);
+  for (; s + 16 <= used; s += 16) {
+    float v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) v[k] = base[(s + k) * pstride + 4 + c];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) a = fmaf(wsh[s + k], v[k], a);
+  }
+  if (s + 8 <= used) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = base[(s + k) * pstride + 4 + c];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) a = fmaf(wsh[s + k], v[k], a);
+    s += 8;
+  }
+  if (s + 4 <= used) {
+    float v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = base[(s + k) * pstride + 4 + c];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a = fmaf(wsh[s + k], v[k], a);
+    s += 4;
   }
   for (; s < used; ++s) a = fmaf(wsh[s], base[s * pstride + 4 + c], a);
   // 4. H^T = H over the 128 channels: bits 0..5 across the lanes of a wave, bit 6 via LDS
@@ -738,8 +753,8 @@ size_t decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv
   const size_t split = size_t(batch) * num_q_heads * (ns + 1) * kPartStride * sizeof(float);
   const int32_t wg = decode_balanced_wg(batch, num_kv_heads, max_seq_len);
   if (wg == 0) return split;
-  const size_t bal = size_t(balanced_tail_offset(wg, batch, num_q_heads, num_kv_heads) +
-                            int64_t(batch) * num_q_heads * kPartStride) * sizeof(float);
+  const size_t bal = size_t(balanced_pref_offset(wg, batch, num_q_heads, num_kv_heads) + batch + 1) *
+                    sizeof(float);
   return bal > split ? bal : split;
 }
 

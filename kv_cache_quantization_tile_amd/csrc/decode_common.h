@@ -30,6 +30,14 @@ __host__ __device__ inline int64_t balanced_tail_offset(int32_t n_page_wg, int32
   return (4 * int64_t(n_page_wg) + int64_t(batch) * num_kv_heads) *
          (num_q_heads / num_kv_heads) * kPartStride;
 }
+// ... and the page prefix sums (batch + 1 int32: full pages before each sequence, then the
+// total) after the tail partials.
+__host__ __device__ inline int64_t balanced_pref_offset(int32_t n_page_wg, int32_t batch,
+                                                        int32_t num_q_heads,
+                                                        int32_t num_kv_heads) {
+  return balanced_tail_offset(n_page_wg, batch, num_q_heads, num_kv_heads) +
+         int64_t(batch) * num_q_heads * kPartStride;
+}
 
 __device__ __forceinline__ float4v mfma16x16x32(const half8& a, const half8& b, const float4v& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);

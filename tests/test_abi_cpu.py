@@ -237,15 +237,16 @@ def test_chunk_workspace_formula():
     assert K.chunk_workspace_bytes(p, 16, 128, 8, 1024) == 0
 
 
-def _balanced_partials(B, hq, hkv, mx):
-    """Partials of the balanced decode layout (2..1024 sequences): one slot per (page wave,
-    segment) index sum i + (b Hkv + g) with i < 4 x page workgroups (at most 512, one round of
-    2 waves per SIMD on 256 CUs), G query heads each, then one tail partial per (b, query head)."""
+def _balanced_bytes(B, hq, hkv, mx):
+    """Workspace of the balanced decode layout (2..1024 sequences): one partial slot per (page
+    wave, segment) index sum i + (b Hkv + g) with i < 4 x page workgroups (at most 512, one
+    round of 2 waves per SIMD on 256 CUs), G query heads each; one tail partial per (b, query
+    head); then B + 1 int32 page prefix sums."""
     work = B * hkv * (mx // 128)
     if B < 2 or B > 1024 or mx < 128 or work >= 2 ** 31:
         return 0
     wg = min((work + 3) // 4, 512)
-    return (4 * wg + B * hkv) * (hq // hkv) + B * hq
+    return (((4 * wg + B * hkv) * (hq // hkv) + B * hq) * 132 + B + 1) * 4
 
 
 def test_decode_workspace_formula():
@@ -255,8 +256,8 @@ def test_decode_workspace_formula():
                            (1024, 64, 8, 4096), (1025, 64, 8, 4096)):
         ns = K.decode_num_splits(p, B, hkv, mx)
         assert ns >= 1
-        split = B * hq * (ns + 1)
-        want = max(split, _balanced_partials(B, hq, hkv, mx)) * 132 * 4
+        split = B * hq * (ns + 1) * 132 * 4
+        want = max(split, _balanced_bytes(B, hq, hkv, mx))
         assert K.decode_workspace_bytes(p, B, hq, hkv, mx) == want
     assert K.decode_workspace_bytes(p, 1, 64, 8, -1) == 0
     assert K.decode_workspace_bytes(p, 1, 128, 8, 1024) == 0

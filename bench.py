@@ -118,6 +118,18 @@ def cpu_baseline(w, n_iters: int, budget_s: float, k_bits: int = 4, v_bits: int 
                                   f"{n_tiles_step} tiles and {w.hkv} KV heads x {T // 128} pages")
 
 
+def calibration_copy(args, dev):
+    """One device copy of --calibration-copy-mb MiB (its HBM counters scale the kernels')."""
+    if not args.calibration_copy_mb:
+        return
+    import torch
+    a = torch.empty(args.calibration_copy_mb << 20, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -191,12 +203,7 @@ def main():
     n_tiles = w0.tile_src_token.numel() * hkv          # per kind
     torch.cuda.synchronize()
 
-    if args.calibration_copy_mb:
-        a = torch.empty(args.calibration_copy_mb << 20, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-        b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
+    calibration_copy(args, dev)
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
     # warmup
@@ -322,6 +329,7 @@ def chunked_prefill(args, K, synth, params, dev):
     step = lambda: (K.write_tokens(params, kn, vn, cu, sl0, kt, vt, w.block_table, kp, vp, n),
                     K.chunk_attention(params, q, cu, kp, vp, w.block_table, sl1, ctx + n, kt, vt,
                                       workspace=ws, out=out))
+    calibration_copy(args, dev)
     ev = lambda: torch.cuda.Event(enable_timing=True)
     for _ in range(args.warmup):
         step()
@@ -380,7 +388,7 @@ def chunked_prefill(args, K, synth, params, dev):
                      "achieved": round(attn_flops / (a_ms * 1e-3) / 1e12, 2),
                      "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_flops / (a_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
-                     "traffic": None,
+                     "traffic": load_traffic("mq_pages_kernel", source_hash(), "chunked_prefill"),
                      "per_launch": f"{B * n} query rows x {hq} heads x 4 x 128 FLOP per causal "
                                    f"key = {attn_flops / 1e9:.1f} GFLOP",
                      "launch_ms": round(a_ms, 5),
@@ -493,13 +501,15 @@ def decode_steps(args, K, synth, params, dev):
             dec = K.prepare_decode(params, q, kp, vp, bt, lens[s + 1], max_len, ws, out,
                                    k_tail=kt, v_tail=vt)
             steps.append((app, dec, q, kn, vn))
-        copies.append((w, steps, kp, vp, kt, vt, lens, ws, out))
+        # every buffer the prepared calls point to stays referenced here
+        copies.append((w, steps, kp, vp, kt, vt, lens, ws, out, bt))
         if c == 0:
             w0 = w
         if c > 0:                       # the prompt sources are no longer needed
             w.k_src = w.k_src[:0]
             w.v_src = w.v_src[:0]
     torch.cuda.synchronize()
+    calibration_copy(args, dev)
     B, hq, hkv = w0.batch, w0.hq, w0.hkv
 
     def step_index(s):

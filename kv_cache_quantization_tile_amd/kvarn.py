@@ -387,8 +387,9 @@ class Prepared:
     (same buffers, same stream) with no per-call Python checks. For benchmark loops and graph
     capture, where a few microseconds of host work per launch would dominate."""
 
-    def __init__(self, fn, args, what):
-        self._fn, self._args, self._what = fn, args, what
+    def __init__(self, fn, args, what, keep=()):
+        # keep: the tensors whose addresses are in args, held so that they outlive the call
+        self._fn, self._args, self._what, self._keep = fn, args, what, tuple(keep)
 
     def __call__(self):
         st = self._fn(*self._args)
@@ -406,14 +407,16 @@ def prepare_quantize(params: Params, kind: int, src, tile_src_token, tile_dst_pa
     args = (ctypes.byref(params), kind, _ptr(src), src.stride(0), src.stride(1), src.shape[0],
             _ptr(tile_src_token), _ptr(tile_dst_page), tile_src_token.numel(), hkv, _ptr(pool),
             _pool_n(params, pool, kind), _stream(stream))
-    return Prepared(lib.kvarn_quantize_tiles, args, "kvarn_quantize_tiles")
+    return Prepared(lib.kvarn_quantize_tiles, args, "kvarn_quantize_tiles",
+                    (src, tile_src_token, tile_dst_page, pool))
 
 
 def prepare_quantize_kv(params: Params, k_src, v_src, tile_src_token, tile_dst_page, k_pool,
                         v_pool, stream=None) -> Prepared:
     args = _kv_quant_args(params, k_src, v_src, tile_src_token, tile_dst_page, k_pool, v_pool,
                           stream)
-    return Prepared(lib.kvarn_quantize_kv_tiles, args, "kvarn_quantize_kv_tiles")
+    return Prepared(lib.kvarn_quantize_kv_tiles, args, "kvarn_quantize_kv_tiles",
+                    (k_src, v_src, tile_src_token, tile_dst_page, k_pool, v_pool))
 
 
 def prepare_append(params: Params, k_new, v_new, seq_lens, k_tail, v_tail, block_table,
@@ -432,7 +435,8 @@ def prepare_append(params: Params, k_new, v_new, seq_lens, k_tail, v_tail, block
     args = (ctypes.byref(params), _ptr(k_new), _ptr(v_new), B, hkv, _ptr(seq_lens),
             _ptr(k_tail), _ptr(v_tail), _ptr(block_table), block_table.shape[1], _ptr(k_pool),
             _ptr(v_pool), _pools_n(params, k_pool, v_pool), _stream(stream))
-    return Prepared(lib.kvarn_append_tokens, args, "kvarn_append_tokens")
+    return Prepared(lib.kvarn_append_tokens, args, "kvarn_append_tokens",
+                    (k_new, v_new, seq_lens, k_tail, v_tail, block_table, k_pool, v_pool))
 
 
 def prepare_decode(params: Params, q, k_pool, v_pool, block_table, seq_lens, max_seq_len: int,
@@ -448,4 +452,5 @@ def prepare_decode(params: Params, q, k_pool, v_pool, block_table, seq_lens, max
             _ptr(block_table), block_table.shape[1], _ptr(seq_lens), max_seq_len, _ptr(k_tail),
             _ptr(v_tail), float(softmax_scale), _ptr(workspace), workspace.numel(), _ptr(out),
             _stream(stream))
-    return Prepared(lib.kvarn_decode_attention, args, "kvarn_decode_attention")
+    return Prepared(lib.kvarn_decode_attention, args, "kvarn_decode_attention",
+                    (q, k_pool, v_pool, block_table, seq_lens, workspace, out, k_tail, v_tail))

@@ -51,11 +51,12 @@ struct DecodeSmem {
 // tail buffers the grid has one more split, n_splits, which computes the tail partial. The
 // row's sequence, page slots and tail follow row_geometry.
 // Balanced layout (BAL = true; one query row per sequence): the full pages of all (sequence,
-// KV head) segments, in order b, g, page, are one list of T pages, and wave i of the
-// 4 n_page_wg page waves streams list entries [floor(i T / W), floor((i + 1) T / W)), W the
-// wave count, crossing segment boundaries; it writes one partial per segment it touches, at
-// slot i + (b Hkv + g). Ragged lengths then cost no idle waves. Workgroups n_page_wg.. are the
-// tails, one per (b, g). KB, VB: key and value code widths; AUX: cache policy of the page loads.
+// KV head) segments, in order b, g, page, are one list of T pages, and wave i < W =
+// min(4 n_page_wg, T) streams list entries [floor(i T / W), floor((i + 1) T / W)) (at least
+// one), crossing segment boundaries; it writes one partial per segment it touches, at slot
+// i + (b Hkv + g). Ragged lengths then cost no idle waves. Workgroup 0 also stores the page
+// prefix sums for the merge. Workgroups n_page_wg.. are the tails, one per (b, g).
+// KB, VB: key and value code widths; AUX: cache policy of the page loads.
 template <int KB, int VB, int AUX, bool BAL>
 __global__ void __launch_bounds__(kThreads)
 decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t num_kv_heads,

@@ -92,7 +92,7 @@ def cpu_baseline(w, n_iters: int, budget_s: float, k_bits: int = 4, v_bits: int 
     T = k.shape[0]
     n_tiles_step = 2 * (T // 128) * w.hkv
     # quantize: a batch of tiles of KV head 0, both kinds
-    nq = 16
+    nq = min(16, T // 128)
     tiles_k = np.stack([k[128 * i:128 * (i + 1), 0, :].T for i in range(nq)])
     tiles_v = np.stack([v[128 * i:128 * (i + 1), 0, :].T for i in range(nq)])
     t0 = time.perf_counter()

@@ -78,7 +78,11 @@ def load_traffic(kernel: str, src_hash: str, workload: str):
 
 
 def cpu_baseline(w, n_iters: int, budget_s: float, k_bits: int = 4, v_bits: int = 2):
-    """The float64 oracle on a bounded sample of one step, scaled to the whole step."""
+    """The float64 oracle on a time-bounded sample of one step, scaled to the whole step: tiles
+    of the step quantized in batches of 16 (one KV head and kind per batch, in step order)
+    for about budget_s / 2 seconds or until every tile of the step is done, then the decode
+    (dequantize the pages, attention of every query head of the group) of chunks of pages for
+    about budget_s / 2 seconds or until every (page, KV head) pair of the step is done."""
     import numpy as np
     from oracle import kvarn_oracle as O
     try:
@@ -90,32 +94,51 @@ def cpu_baseline(w, n_iters: int, budget_s: float, k_bits: int = 4, v_bits: int 
     v = w.v_src.cpu().numpy()
     q = w.step_inputs(0, device="cpu")[0].numpy()
     T = k.shape[0]
-    n_tiles_step = 2 * (T // 128) * w.hkv
-    # quantize: a batch of tiles of KV head 0, both kinds
-    nq = min(16, T // 128)
-    tiles_k = np.stack([k[128 * i:128 * (i + 1), 0, :].T for i in range(nq)])
-    tiles_v = np.stack([v[128 * i:128 * (i + 1), 0, :].T for i in range(nq)])
-    t0 = time.perf_counter()
-    rk = O.quantize_tiles(tiles_k, O.KIND_K, n_iters, k_bits=k_bits)
-    rv = O.quantize_tiles(tiles_v, O.KIND_V, n_iters, v_bits=v_bits)
-    tq = (time.perf_counter() - t0) / (2 * nq)               # seconds per tile
-    # decode: all query heads of KV head 0 over as many pages as fit the budget
-    pages = max(1, min(T // 128, int(budget_s / max(tq, 1e-3) / 4)))
-    t0 = time.perf_counter()
-    kd = np.concatenate([O.dequantize_tiles(rk["codes"][i % nq], rk["r"][i % nq], rk["s"][i % nq],
-                                            rk["scale"][i % nq], rk["zero"][i % nq], O.KIND_K).T
-                         for i in range(pages)])
-    vd = np.concatenate([O.dequantize_tiles(rv["codes"][i % nq], rv["r"][i % nq], rv["s"][i % nq],
-                                            rv["scale"][i % nq], rv["zero"][i % nq], O.KIND_V).T
-                         for i in range(pages)])
+    n_pages = T // 128
+    n_tiles_step = 2 * n_pages * w.hkv
+    nb = min(16, n_pages)
+    batches = [(h, kind, t0) for h in range(w.hkv) for kind in (O.KIND_K, O.KIND_V)
+               for t0 in range(0, n_pages - nb + 1, nb)]
+    recs = {}
+    n_q, t_q = 0, 0.0
+    for h, kind, t0 in batches:
+        src = k if kind == O.KIND_K else v
+        tiles = np.stack([src[128 * (t0 + i):128 * (t0 + i + 1), h, :].T for i in range(nb)])
+        start = time.perf_counter()
+        r = O.quantize_tiles(tiles, kind, n_iters, k_bits=k_bits, v_bits=v_bits)
+        t_q += time.perf_counter() - start
+        n_q += nb
+        recs.setdefault(kind, r)
+        if t_q >= budget_s / 2 and O.KIND_V in recs:
+            break
+    tq = t_q / n_q                                            # seconds per tile
     G = w.hq // w.hkv
-    for h in range(G):
-        O.attention(q[0, h].astype(np.float64), kd, vd, 1 / math.sqrt(128))
-    td = (time.perf_counter() - t0) * (T // 128) / pages * w.hkv   # whole decode step
+    rk, rv = recs[O.KIND_K], recs[O.KIND_V]
+    # decode: chunks of at most 256 pages of one KV head (every query head of the group);
+    # the attention cost is linear in the pages, so the time per page scales to the step
+    chunk = min(256, n_pages)
+    n_d, t_d = 0, 0.0
+    while n_d < n_pages * w.hkv:
+        g = (n_d // n_pages) % w.hkv
+        start = time.perf_counter()
+        kd = np.concatenate([O.dequantize_tiles(rk["codes"][i % nb], rk["r"][i % nb], rk["s"][i % nb],
+                                                rk["scale"][i % nb], rk["zero"][i % nb], O.KIND_K).T
+                             for i in range(chunk)])
+        vd = np.concatenate([O.dequantize_tiles(rv["codes"][i % nb], rv["r"][i % nb], rv["s"][i % nb],
+                                                rv["scale"][i % nb], rv["zero"][i % nb], O.KIND_V).T
+                             for i in range(chunk)])
+        for h in range(G):
+            O.attention(q[0, g * G + h].astype(np.float64), kd, vd, 1 / math.sqrt(128))
+        t_d += time.perf_counter() - start
+        n_d += chunk
+        if t_d >= budget_s / 2:
+            break
+    td = t_d / n_d * n_pages * w.hkv                          # whole decode step
     t_step = tq * n_tiles_step + td
-    return t_step, blas_threads, (f"{2 * nq} tiles quantized (K and V, KV head 0) and decode of "
-                                  f"{G} query heads over {pages} pages of KV head 0, scaled to "
-                                  f"{n_tiles_step} tiles and {w.hkv} KV heads x {T // 128} pages")
+    return t_step, blas_threads, (f"{n_q} of the step's {n_tiles_step} tiles quantized and "
+                                  f"{n_d} of its {n_pages * w.hkv} (page, KV head) pairs decoded "
+                                  f"({G} query heads, chunks of {chunk} pages), "
+                                  f"{t_q + t_d:.1f} s, scaled to the step")
 
 
 def calibration_copy(args, dev):
@@ -435,17 +458,20 @@ def cpu_baseline_decode(w, n_iters: int, budget_s: float, tail: int, k_bits: int
         for h in range(G):
             O.attention(q[0, h].astype(np.float64), kd, vd, 1 / math.sqrt(128))
 
-    t0 = time.perf_counter()
-    run(8)
-    per_page = (time.perf_counter() - t0) / 8
-    pages = max(8, min(1024, int(budget_s / max(per_page, 1e-4))))
-    t0 = time.perf_counter()
-    run(pages)
-    per_page = (time.perf_counter() - t0) / pages
+    # chunks of 256 pages (+ the staged tokens) for about budget_s seconds, or every page of
+    # the step once
     total_pages = sum(L // 128 for L in w.prompt_lens) * w.hkv
+    done, spent = 0, 0.0
+    while done < total_pages and spent < budget_s:
+        t0 = time.perf_counter()
+        run(256)
+        spent += time.perf_counter() - t0
+        done += 256
+    per_page = spent / done
     return per_page * total_pages, blas_threads, (
-        f"oracle decode of {G} query heads over {pages} pages (+{tail} staged tokens) of one "
-        f"KV head, scaled to {total_pages} (sequence, KV head) pages of one step")
+        f"oracle decode of {G} query heads over {done} pages in chunks of 256 (+{tail} staged "
+        f"tokens each), {spent:.1f} s, scaled to the {total_pages} (sequence, KV head) pages of "
+        f"one step")
 
 
 def decode_steps(args, K, synth, params, dev):

@@ -277,8 +277,8 @@ def main():
                   "unit": "TFLOP/s", "frac": round(q_achieved / ALU_PEAK_TFLOPS, 4),
                   "traffic": load_traffic("quantize_kv_kernel", src_hash, args.workload),
                   "hbm_gbps": round(q_bytes / (q_launch_ms * 1e-3) / 1e9, 1),
-                  # the published fp32 vector figure counts packed-FP32 forms, kept out of this
-                  # build's code: the fraction of it, for reference
+                  # the published fp32 vector figure counts packed-FP32 forms, kept out of the
+                  # library's code: the fraction of it, for reference
                   "frac_of_packed_fp32_peak": round(q_achieved / (2 * ALU_PEAK_TFLOPS), 4),
                   "per_launch": f"{2 * n_tiles} K+V tiles x {flop_tile} FLOP",
                   "launch_ms": round(q_launch_ms, 5)}

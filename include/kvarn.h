@@ -51,7 +51,7 @@ extern "C" {
 typedef enum {
     KVARN_OK = 0,
     KVARN_ERR_INVALID_ARG = 1, /* NULL pointer, bad size, misalignment, bad enum      */
-    KVARN_ERR_UNSUPPORTED = 2, /* a valid request outside what this build implements */
+    KVARN_ERR_UNSUPPORTED = 2, /* a valid request outside what this library implements */
     KVARN_ERR_WORKSPACE = 3,   /* workspace smaller than kvarn_decode_workspace_bytes */
     KVARN_ERR_HIP = 4          /* the HIP runtime refused a launch                    */
 } kvarn_status;

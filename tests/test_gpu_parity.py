@@ -325,6 +325,48 @@ def test_decode_balanced_layout(K, B, hkv, G, hi):
         f"the oracle: max rel err {err:.2e}")
 
 
+def test_decode_balanced_random_shapes(K):
+    """24 seeded shapes (2..40 sequences, 1..8 KV heads, groups 1..8, lengths 0..3000, pages
+    out of the pool in a few block tables, with and without tails, 2 presets): the balanced
+    layout's output equals each sequence decoded alone (split layout) within float32
+    summation-order differences, and empty rows are zeros."""
+    rng = np.random.default_rng(930)
+    worst = 0.0
+    for case in range(24):
+        B = int(rng.integers(2, 41))
+        hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([1, 2, 3, 4, 8]))
+        lens = rng.integers(0, 3001, size=B).tolist()
+        preset = "kvarn_k4v2_g128" if case % 3 else "kvarn_k2v2_g128"
+        params = K.params_from_dtype(preset, 1)
+        kp, vp, bt, kt, vt, sl, _ = _build_cache(K, params, lens, hkv, seed=940 + case)
+        if case % 4 == 1:                       # a few entries outside the pool
+            bt = bt.cpu()
+            for b in range(0, B, 3):
+                if lens[b] >= 128:
+                    bt[b, int(rng.integers(0, lens[b] // 128))] = kp.shape[0] + 5
+            bt = bt.cuda()
+        tails = case % 5 != 2
+        q = torch.from_numpy(rng.standard_normal((B, G * hkv, 128))).to(torch.float16).cuda()
+        mx = max(lens)
+        args = (kt, vt) if tails else (None, None)
+        out = K.decode_attention(params, q, kp, vp, bt, sl, mx, *args)
+        one = torch.empty_like(out)
+        for b in range(B):
+            tb = (kt[b:b + 1].contiguous(), vt[b:b + 1].contiguous()) if tails else (None, None)
+            one[b:b + 1] = K.decode_attention(params, q[b:b + 1].contiguous(), kp, vp,
+                                              bt[b:b + 1].contiguous(), sl[b:b + 1], mx, *tb)
+        torch.cuda.synchronize()
+        of, sf = out.float(), one.float()
+        scale = sf.abs().amax(dim=-1, keepdim=True).clamp_min(1e-30)
+        diff = float(((of - sf).abs() / scale).max())
+        assert diff <= 2e-3, (case, B, hkv, G, diff)
+        zero_rows = (sf.abs().amax(dim=-1) == 0)
+        assert torch.all(of[zero_rows] == 0), case
+        worst = max(worst, diff)
+    say(f"24 shapes: balanced layout vs one-sequence decodes, max rel diff {worst:.1e}")
+
+
 def test_decode_without_tail_buffers(K):
     """NULL tails: tokens past the last full page are ignored."""
     lens = [128 * 5 + 40, 256]

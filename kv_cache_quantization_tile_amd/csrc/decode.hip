@@ -571,18 +571,20 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
 // (independent loads). (Pairs halve the workgroup count of a many-row read.)
 // BAL: the balanced layout of decode_pages_kernel (n_page_wg page workgroups); the partials of
 // segment (b, g) are the slots i + (b Hkv + g) of the waves i whose page ranges meet it.
+// The split weights live in dynamic LDS, w_cap + 1 floats per head (w_cap >= the splits any
+// row uses; the tail's weight at index w_cap): a small read keeps its workgroups small.
 template <bool BAL>
 __global__ void __launch_bounds__(256)
 decode_merge_kernel(int32_t num_q_heads, int32_t num_kv_heads,
                     const int32_t* __restrict__ seq_lens, int32_t max_seq_len,
                     const int32_t* __restrict__ cu_q, int32_t batch, int32_t tiles_per_split,
                     int32_t n_splits, int32_t has_tail, const float* __restrict__ ws,
-                    int32_t n_page_wg, __half* __restrict__ out) {
-  __shared__ float wsh_[2][kMaxMergeSplits + 1];
+                    int32_t n_page_wg, int32_t w_cap, __half* __restrict__ out) {
+  extern __shared__ float merge_w[];
   __shared__ float red_[2][2][2];
   __shared__ float xs_[2][kDim];
   const int pair = threadIdx.x >> 7;
-  float* wsh = wsh_[pair];
+  float* wsh = merge_w + pair * (w_cap + 1);
   float (*red)[2] = red_[pair];
   float* xs = xs_[pair];
   // a head past the last (odd head count) runs along for the barriers and stores nothing
@@ -653,7 +655,7 @@ decode_merge_kernel(int32_t num_q_heads, int32_t num_kv_heads,
   }
   if (c == 0) {
     const float e = (tail && M != -INFINITY) ? exp2f(m_tail - M) : 0.f;
-    wsh[kMaxMergeSplits] = e;
+    wsh[w_cap] = e;
     if (tail) lsum = fmaf(e, l_tail, lsum);
   }
   for (int off = 32; off >= 1; off >>= 1)
@@ -710,7 +712,7 @@ decode_merge_kernel(int32_t num_q_heads, int32_t num_kv_heads,
     a = (c & 64) ? (p - a) : (a + p);
     a *= kInvSqrt128;
   }
-  if (tail) a = fmaf(wsh[kMaxMergeSplits], tailp[4 + c], a);
+  if (tail) a = fmaf(wsh[w_cap], tailp[4 + c], a);
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   if (head_ok) out[(int64_t(b) * num_q_heads + hq) * kDim + c] = __float2half_rn(a * inv);
 }
@@ -787,10 +789,12 @@ hipError_t launch_decode(int k_bits, int v_bits, const void* q, int32_t rows,
                          static_cast<const __half*>(v_tail), qscale, ws, bal_wg);
     });
     if (e != hipSuccess) return e;
+    // a segment's partials come from at most all 4 bal_wg waves
+    const int32_t cap = 4 * bal_wg;
     hipLaunchKernelGGL(decode_merge_kernel<true>, dim3((num_q_heads + 1) / 2, rows), dim3(256),
-                       0, stream, num_q_heads, num_kv_heads, seq_lens, max_seq_len, cu_q, batch,
-                       1, 1, has_tail ? 1 : 0, static_cast<const float*>(ws), bal_wg,
-                       static_cast<__half*>(out));
+                       2 * (cap + 1) * sizeof(float), stream, num_q_heads, num_kv_heads, seq_lens,
+                       max_seq_len, cu_q, batch, 1, 1, has_tail ? 1 : 0,
+                       static_cast<const float*>(ws), bal_wg, cap, static_cast<__half*>(out));
     return hipGetLastError();
   }
   const int32_t tpw = decode_tiles_per_wave(rows, num_kv_heads, max_seq_len);
@@ -829,10 +833,11 @@ hipError_t launch_decode(int k_bits, int v_bits, const void* q, int32_t rows,
     }
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(decode_merge_kernel<false>, dim3((num_q_heads + 1) / 2, rows), dim3(256), 0,
-                     stream, num_q_heads, num_kv_heads, seq_lens, max_seq_len, cu_q, batch,
-                     per_split, ns, has_tail ? 1 : 0, static_cast<const float*>(ws), 0,
-                     static_cast<__half*>(out));
+  // every row uses at most ns splits (ns <= kMaxMergeSplits by the split sizing)
+  hipLaunchKernelGGL(decode_merge_kernel<false>, dim3((num_q_heads + 1) / 2, rows), dim3(256),
+                     2 * (ns + 1) * sizeof(float), stream, num_q_heads, num_kv_heads, seq_lens,
+                     max_seq_len, cu_q, batch, per_split, ns, has_tail ? 1 : 0,
+                     static_cast<const float*>(ws), 0, ns, static_cast<__half*>(out));
   return hipGetLastError();
 }
 

@@ -565,10 +565,11 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
 }
 
 // Merge the splits of one (sequence, query head): log-sum-exp weights, H^T on the page
-// part (rotated space), plus the raw-space tail; float16 output. One 256-thread workgroup
-// per (pair of query heads, sequence): 128 threads per head, thread c owns channel c; split
-// weights are computed once in LDS, then every thread streams its channel of all partials
-// (independent loads). (Pairs halve the workgroup count of a many-row read.)
+// part (rotated space), plus the raw-space tail; float16 output. One wave per (query head,
+// sequence), four heads per 256-thread workgroup: lane l owns channels l and l + 64, so every
+// reduction and the whole H^T stay inside the wave (no workgroup barrier). Split weights are
+// computed once into the wave's LDS slot, then every lane streams its two channels of all
+// partials (independent loads).
 // BAL: the balanced layout of decode_pages_kernel (n_page_wg page workgroups); the partials of
 // segment (b, g) are the slots i + (b Hkv + g) of the waves i whose page ranges meet it.
 // The split weights live in dynamic LDS, w_cap + 1 floats per head (w_cap >= the splits any
@@ -581,17 +582,12 @@ decode_merge_kernel(int32_t num_q_heads, int32_t num_kv_heads,
                     int32_t n_splits, int32_t has_tail, const float* __restrict__ ws,
                     int32_t n_page_wg, int32_t w_cap, __half* __restrict__ out) {
   extern __shared__ float merge_w[];
-  __shared__ float red_[2][2][2];
-  __shared__ float xs_[2][kDim];
-  const int pair = threadIdx.x >> 7;
-  float* wsh = merge_w + pair * (w_cap + 1);
-  float (*red)[2] = red_[pair];
-  float* xs = xs_[pair];
-  // a head past the last (odd head count) runs along for the barriers and stores nothing
-  const int hq = min(2 * int(blockIdx.x) + pair, num_q_heads - 1);
-  const bool head_ok = 2 * int(blockIdx.x) + pair < num_q_heads;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float* wsh = merge_w + wv * (w_cap + 1);
+  // a head past the last runs along and stores nothing
+  const int hq = min(4 * int(blockIdx.x) + wv, num_q_heads - 1);
+  const bool head_ok = 4 * int(blockIdx.x) + wv < num_q_heads;
   const int b = blockIdx.y;   // b: output row
-  const int c = threadIdx.x & 127, lane = c & 63, wv = c >> 6;
   const RowGeom rg = row_geometry(b, seq_lens, max_seq_len, cu_q, batch);
   const bool tail = has_tail && rg.tail_len != 0;
   int used;
@@ -626,78 +622,85 @@ decode_merge_kernel(int32_t num_q_heads, int32_t num_kv_heads,
     pstride = kPartStride;
     tailp = base + int64_t(n_splits) * kPartStride;
   }
-  // 1. global max over the used splits (and the tail); the (m, l) of this thread's first
-  // split and of the tail stay in registers for step 2 (one memory round trip fewer)
+  // 1. global max over the used splits (and the tail); the (m, l) of this lane's first split
+  // and of the tail stay in registers for step 2 (one memory round trip fewer)
   float m_first = -INFINITY, l_first = 0.f, m_tail = -INFINITY, l_tail = 0.f;
-  if (c < used) {
-    m_first = base[c * pstride];
-    l_first = base[c * pstride + 1];
+  if (lane < used) {
+    m_first = base[lane * pstride];
+    l_first = base[lane * pstride + 1];
   }
-  if (tail && c == 0) {
+  if (tail && lane == 0) {
     m_tail = tailp[0];
     l_tail = tailp[1];
   }
   float M = fmaxf(m_first, m_tail);
-  for (int s = c + 128; s < used; s += 128) M = fmaxf(M, base[s * pstride]);
+  for (int s = lane + 64; s < used; s += 64) M = fmaxf(M, base[s * pstride]);
   for (int off = 32; off >= 1; off >>= 1)
     M = fmaxf(M, __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ off) << 2, __float_as_int(M))));
-  if (lane == 0) red[0][wv] = M;
-  __syncthreads();
-  M = fmaxf(red[0][0], red[0][1]);
-  // 2. split weights exp2(m_s - M) and the total l
+  // 2. split weights exp2(m_s - M) into the wave's LDS slot, and the total l
   float lsum = 0.f;
-  for (int s = c; s < used; s += 128) {
-    const float ms = s == c ? m_first : base[s * pstride];
-    const float ls = s == c ? l_first : base[s * pstride + 1];
+  for (int s = lane; s < used; s += 64) {
+    const float ms = s == lane ? m_first : base[s * pstride];
+    const float ls = s == lane ? l_first : base[s * pstride + 1];
     const float e = M == -INFINITY ? 0.f : exp2f(ms - M);
     wsh[s] = e;
     lsum = fmaf(e, ls, lsum);
   }
-  if (c == 0) {
+  if (lane == 0) {
     const float e = (tail && M != -INFINITY) ? exp2f(m_tail - M) : 0.f;
     wsh[w_cap] = e;
     if (tail) lsum = fmaf(e, l_tail, lsum);
   }
   for (int off = 32; off >= 1; off >>= 1)
     lsum += __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ off) << 2, __float_as_int(lsum)));
-  if (lane == 0) red[1][wv] = lsum;
-  __syncthreads();
-  lsum = red[1][0] + red[1][1];
-  // 3. weighted sum of the rotated accumulators, channel c
+  // the wave's LDS writes land before its reads below
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // 3. weighted sum of the rotated accumulators, channels lane and lane + 64
   // (16 independent loads in flight per round trip, then 8, 4, 1; the order of the sums
   // does not depend on the unrolling)
-  float a = 0.f;
+  float a0 = 0.f, a1 = 0.f;
+  const float* acc0 = base + 4 + lane;
   int s = 0;
-  for (; s + 16 <= used; s += 16) {
-    float v[16];
+  for (; s + 8 <= used; s += 8) {
+    float v0[8], v1[8];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) v[k] = base[(s + k) * pstride + 4 + c];
+    for (int k = 0; k < 8; ++k) {
+      v0[k] = acc0[(s + k) * pstride];
+      v1[k] = acc0[(s + k) * pstride + 64];
+    }
 #pragma unroll
-    for (int k = 0; k < 16; ++k) a = fmaf(wsh[s + k], v[k], a);
-  }
-  if (s + 8 <= used) {
-    float v[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = base[(s + k) * pstride + 4 + c];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) a = fmaf(wsh[s + k], v[k], a);
-    s += 8;
+    for (int k = 0; k < 8; ++k) {
+      a0 = fmaf(wsh[s + k], v0[k], a0);
+      a1 = fmaf(wsh[s + k], v1[k], a1);
+    }
   }
   if (s + 4 <= used) {
-    float v[4];
+    float v0[4], v1[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) v[k] = base[(s + k) * pstride + 4 + c];
+    for (int k = 0; k < 4; ++k) {
+      v0[k] = acc0[(s + k) * pstride];
+      v1[k] = acc0[(s + k) * pstride + 64];
+    }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) a = fmaf(wsh[s + k], v[k], a);
+    for (int k = 0; k < 4; ++k) {
+      a0 = fmaf(wsh[s + k], v0[k], a0);
+      a1 = fmaf(wsh[s + k], v1[k], a1);
+    }
     s += 4;
   }
-  for (; s < used; ++s) a = fmaf(wsh[s], base[s * pstride + 4 + c], a);
-  // 4. H^T = H over the 128 channels: bits 0..5 across the lanes of a wave, bit 6 via LDS
+  for (; s < used; ++s) {
+    a0 = fmaf(wsh[s], acc0[s * pstride], a0);
+    a1 = fmaf(wsh[s], acc0[s * pstride + 64], a1);
+  }
+  // 4. H^T = H over the 128 channels: bits 0..5 across the lanes, bit 6 within the lane
   {
 #define KVARN_MSTAGE(M_, FN)                          \
     {                                                 \
-      const float p = FN(a);                          \
-      a = (lane & (M_)) ? (p - a) : (a + p);          \
+      const float p0 = FN(a0), p1 = FN(a1);           \
+      a0 = (lane & (M_)) ? (p0 - a0) : (a0 + p0);     \
+      a1 = (lane & (M_)) ? (p1 - a1) : (a1 + p1);     \
     }
     KVARN_MSTAGE(1, dpp_f<kDppQuadXor1>)
     KVARN_MSTAGE(2, dpp_f<kDppQuadXor2>)
@@ -706,15 +709,20 @@ decode_merge_kernel(int32_t num_q_heads, int32_t num_kv_heads,
     KVARN_MSTAGE(16, swz_xor_f<16>)
     KVARN_MSTAGE(32, shfl_xor32_f)
 #undef KVARN_MSTAGE
-    xs[c] = a;
-    __syncthreads();
-    const float p = xs[c ^ 64];
-    a = (c & 64) ? (p - a) : (a + p);
-    a *= kInvSqrt128;
+    const float lo = a0 + a1, hi = a0 - a1;
+    a0 = lo * kInvSqrt128;
+    a1 = hi * kInvSqrt128;
   }
-  if (tail) a = fmaf(wsh[w_cap], tailp[4 + c], a);
+  if (tail) {
+    a0 = fmaf(wsh[w_cap], tailp[4 + lane], a0);
+    a1 = fmaf(wsh[w_cap], tailp[4 + 64 + lane], a1);
+  }
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  if (head_ok) out[(int64_t(b) * num_q_heads + hq) * kDim + c] = __float2half_rn(a * inv);
+  if (head_ok) {
+    __half* o = out + (int64_t(b) * num_q_heads + hq) * kDim;
+    o[lane] = __float2half_rn(a0 * inv);
+    o[lane + 64] = __float2half_rn(a1 * inv);
+  }
 }
 
 }  // namespace
@@ -791,8 +799,8 @@ hipError_t launch_decode(int k_bits, int v_bits, const void* q, int32_t rows,
     if (e != hipSuccess) return e;
     // a segment's partials come from at most all 4 bal_wg waves
     const int32_t cap = 4 * bal_wg;
-    hipLaunchKernelGGL(decode_merge_kernel<true>, dim3((num_q_heads + 1) / 2, rows), dim3(256),
-                       2 * (cap + 1) * sizeof(float), stream, num_q_heads, num_kv_heads, seq_lens,
+    hipLaunchKernelGGL(decode_merge_kernel<true>, dim3((num_q_heads + 3) / 4, rows), dim3(256),
+                       4 * (cap + 1) * sizeof(float), stream, num_q_heads, num_kv_heads, seq_lens,
                        max_seq_len, cu_q, batch, 1, 1, has_tail ? 1 : 0,
                        static_cast<const float*>(ws), bal_wg, cap, static_cast<__half*>(out));
     return hipGetLastError();
@@ -834,8 +842,8 @@ hipError_t launch_decode(int k_bits, int v_bits, const void* q, int32_t rows,
     if (e != hipSuccess) return e;
   }
   // every row uses at most ns splits (ns <= kMaxMergeSplits by the split sizing)
-  hipLaunchKernelGGL(decode_merge_kernel<false>, dim3((num_q_heads + 1) / 2, rows), dim3(256),
-                     2 * (ns + 1) * sizeof(float), stream, num_q_heads, num_kv_heads, seq_lens,
+  hipLaunchKernelGGL(decode_merge_kernel<false>, dim3((num_q_heads + 3) / 4, rows), dim3(256),
+                     4 * (ns + 1) * sizeof(float), stream, num_q_heads, num_kv_heads, seq_lens,
                      max_seq_len, cu_q, batch, per_split, ns, has_tail ? 1 : 0,
                      static_cast<const float*>(ws), 0, ns, static_cast<__half*>(out));
   return hipGetLastError();

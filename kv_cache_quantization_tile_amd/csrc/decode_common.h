@@ -15,7 +15,7 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kPartStride = 132;  // floats per partial: m, l, pad, pad, acc[128]
-constexpr int kMaxMergeSplits = 4096;  // splits one merge workgroup can weight (LDS)
+constexpr int kMaxMergeSplits = 4000;  // splits one merge wave can weight (4 heads x (4000 + 1) floats of LDS < 64 KB)
 // Balanced decode layout (one query row per sequence): at most this many sequences (their
 // page prefix sums live in LDS) and 4 * kBalancedPageWg page waves (one round of 2 waves per
 // SIMD on 256 CUs).

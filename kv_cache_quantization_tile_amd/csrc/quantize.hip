@@ -111,12 +111,6 @@ __device__ __forceinline__ uint16_t normalizer16(float v) {
   return f2h_rn(fminf(fmaxf(v, 6.103515625e-05f), 65504.f));
 }
 
-// 4 key codes (bytes, each <= 15) -> 4 nibbles in the low 16 bits, byte k -> nibble k
-__device__ __forceinline__ uint32_t bytes_to_nibbles(uint32_t e) {
-  const uint32_t x = (e | (e >> 4)) & 0x00FF00FFu;
-  return (x | (x >> 8)) & 0x0000FFFFu;
-}
-
 // 4 codes (bytes, each <= 3) -> 4 crumbs in the low 8 bits, byte k -> crumb k
 __device__ __forceinline__ uint32_t bytes_to_crumbs(uint32_t e) {
   const uint32_t x = (e | (e >> 6)) & 0x000F000Fu;
@@ -483,17 +477,20 @@ __device__ __forceinline__ void quantize_tile(RowPtr row_ptr, uint8_t* __restric
     lds_read8(&ga[8 * cb], A);
     lds_read8(&gb[8 * cb], B);
     if constexpr (BITS == 4) {
-      // word (t, cb) = channels 8cb..8cb+7 of token t; nibble p <- channel {0,2,4,6,1,3,5,7}[p]
+      // word (t, cb) = channels 8cb..8cb+7 of token t; nibble p <- channel {0,2,4,6,1,3,5,7}[p]:
+      // channel i's code goes to byte i / 4 of register i % 4 (registers hold channels {0, 4},
+      // {1, 5}, {2, 6}, {3, 7}); codes are at most 15, so shift-ors interleave them into nibbles
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        uint32_t e = 0, o = 0;
+        uint32_t r[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const float u = fminf(fmaf(x[j][i], A[i], B[i]), 15.f);
-          if (i & 1) o = __builtin_amdgcn_cvt_pk_u8_f32(u, i >> 1, o);
-          else e = __builtin_amdgcn_cvt_pk_u8_f32(u, i >> 1, e);
+          r[i & 3] = __builtin_amdgcn_cvt_pk_u8_f32(u, i >> 2, r[i & 3]);
         }
-        out[tok(j) * 16 + cb] = bytes_to_nibbles(e) | (bytes_to_nibbles(o) << 16);
+        const uint32_t lo = r[0] | (r[2] << 4);   // nibbles 0..3: channels 0, 2, 4, 6
+        const uint32_t hi = r[1] | (r[3] << 4);   // nibbles 4..7: channels 1, 3, 5, 7
+        out[tok(j) * 16 + cb] = lo | (hi << 16);
       }
     } else {
       // 2-bit keys: token t's word w = 2 g + d holds channel 32 g + 8 (2 d + hs) + 2 v + e in

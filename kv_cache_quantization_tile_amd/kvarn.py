@@ -141,6 +141,8 @@ def _pools_n(params: Params, k_pool, v_pool) -> int:
     _pool_ok(params, v_pool, KIND_V, "v_pool")
     if k_pool.shape[0] != v_pool.shape[0]:
         raise ValueError("k_pool and v_pool must have the same number of pages")
+    if k_pool.shape[1] != v_pool.shape[1]:
+        raise ValueError("k_pool and v_pool must have the same number of KV heads")
     return k_pool.shape[0]
 
 
@@ -151,6 +153,45 @@ def _pool_ok(params: Params, pool, kind: int, name: str):
     if pool.dim() != 3 or pool.dtype != torch.uint8 or pool.shape[2] != page_bytes(params, kind):
         raise ValueError(f"{name} must be uint8 [pages, Hkv, {page_bytes(params, kind)}] for "
                          f"this preset")
+
+
+def _staging_ok(k_tail, v_tail, B: int, hkv: int):
+    """Staging tiles: both or neither, float16 contiguous [B, Hkv, 128, 128] on the GPU."""
+    if (k_tail is None) != (v_tail is None):
+        raise ValueError("pass both k_tail and v_tail, or neither")
+    if k_tail is None:
+        return
+    for t, nm in ((k_tail, "k_tail"), (v_tail, "v_tail")):
+        _need(t, nm, torch.float16)
+        if tuple(t.shape) != (B, hkv, 128, 128) or not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous [{B}, {hkv}, 128, 128]")
+
+
+def _decode_shapes(q, k_pool, v_pool, block_table, seq_lens, k_tail, v_tail, rows=None):
+    """Shape checks shared by the read calls; returns (rows, Hq, Hkv). The kernels read
+    seq_lens[batch], block_table[batch, width], the pools' records and the staging tiles
+    at these shapes, so every one is checked here (batch = block_table rows)."""
+    _need(q, "q", torch.float16)
+    _need(seq_lens, "seq_lens", torch.int32)
+    _need(block_table, "block_table", torch.int32)
+    if q.dim() != 3 or q.shape[2] != 128 or not q.is_contiguous():
+        raise ValueError("q must be contiguous [rows, Hq, 128]")
+    for t, nm in ((k_pool, "k_pool"), (v_pool, "v_pool")):
+        _need(t, nm, torch.uint8)
+        if t.dim() != 3 or not t.is_contiguous():
+            raise ValueError(f"{nm} must be a contiguous [pages, Hkv, record] pool")
+    if k_pool.shape[1] != v_pool.shape[1]:
+        raise ValueError("k_pool and v_pool must have the same number of KV heads")
+    B = block_table.shape[0] if block_table.dim() == 2 else -1
+    if block_table.dim() != 2 or not block_table.is_contiguous():
+        raise ValueError("block_table must be contiguous [batch, width]")
+    if seq_lens.dim() != 1 or seq_lens.shape[0] != B:
+        raise ValueError(f"seq_lens must be [{B}] (one length per block-table row)")
+    if rows is None and q.shape[0] != B:
+        raise ValueError(f"q must hold one row per sequence ({B})")
+    hkv = k_pool.shape[1]
+    _staging_ok(k_tail, v_tail, B, hkv)
+    return q.shape[0], q.shape[1], hkv
 
 
 # ----------------------------------------------------------------------------- quantize
@@ -242,8 +283,14 @@ def append_tokens(params: Params, k_new, v_new, seq_lens, k_tail, v_tail, block_
     _need(seq_lens, "seq_lens", torch.int32)
     _need(block_table, "block_table", torch.int32)
     B, hkv = k_new.shape[0], k_new.shape[1]
+    if k_new.dim() != 3 or k_new.shape[2] != 128 or tuple(v_new.shape) != tuple(k_new.shape):
+        raise ValueError("k_new / v_new must be [B, Hkv, 128]")
+    if seq_lens.dim() != 1 or seq_lens.shape[0] != B:
+        raise ValueError(f"seq_lens must be [{B}]")
     if tuple(k_tail.shape) != (B, hkv, 128, 128) or tuple(v_tail.shape) != (B, hkv, 128, 128):
         raise ValueError("staging must be [B, Hkv, 128, 128]")
+    if k_pool.shape[1] != hkv:
+        raise ValueError(f"pools must have {hkv} KV heads")
     if block_table.dim() != 2 or block_table.shape[0] != B or not block_table.is_contiguous():
         raise ValueError("block_table must be contiguous [B, width]")
     _check(lib.kvarn_append_tokens(ctypes.byref(params), _ptr(k_new), _ptr(v_new), B, hkv,
@@ -320,21 +367,16 @@ def decode_attention(params: Params, q, k_pool, v_pool, block_table, seq_lens, m
                      k_tail=None, v_tail=None, softmax_scale: float | None = None,
                      workspace=None, out=None, stream=None) -> torch.Tensor:
     """Paged decode attention; q [B, Hq, 128] float16 -> out [B, Hq, 128] float16."""
-    _need(q, "q", torch.float16)
-    _need(seq_lens, "seq_lens", torch.int32)
-    _need(block_table, "block_table", torch.int32)
-    if q.dim() != 3 or q.shape[2] != 128 or not q.is_contiguous():
-        raise ValueError("q must be contiguous [B, Hq, 128]")
-    B, hq = q.shape[0], q.shape[1]
-    hkv = k_pool.shape[1]
-    if block_table.dim() != 2 or block_table.shape[0] != B or not block_table.is_contiguous():
-        raise ValueError("block_table must be contiguous [B, width]")
+    B, hq, hkv = _decode_shapes(q, k_pool, v_pool, block_table, seq_lens, k_tail, v_tail)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(128)
     if workspace is None:
         workspace = new_workspace(params, B, hq, hkv, max_seq_len, q.device)
     if out is None:
         out = torch.empty_like(q)
+    _need(out, "out", torch.float16)
+    if tuple(out.shape) != tuple(q.shape) or not out.is_contiguous():
+        raise ValueError("out must be contiguous and shaped like q")
     _check(lib.kvarn_decode_attention(ctypes.byref(params), _ptr(q), B, hq, hkv, _ptr(k_pool),
                                       _ptr(v_pool), _pools_n(params, k_pool, v_pool),
                                       _ptr(block_table),
@@ -350,25 +392,21 @@ def chunk_attention(params: Params, q, cu_q, k_pool, v_pool, block_table, seq_le
                     workspace=None, out=None, stream=None) -> torch.Tensor:
     """Causal attention of the last cu_q[b+1] - cu_q[b] positions of every sequence (query rows
     of q [total_q, Hq, 128] float16) over the quantized cache -> out [total_q, Hq, 128]."""
-    _need(q, "q", torch.float16)
     _need(cu_q, "cu_q", torch.int32)
-    _need(seq_lens, "seq_lens", torch.int32)
-    _need(block_table, "block_table", torch.int32)
-    if q.dim() != 3 or q.shape[2] != 128 or not q.is_contiguous():
-        raise ValueError("q must be contiguous [total_q, Hq, 128]")
+    total_q, hq, hkv = _decode_shapes(q, k_pool, v_pool, block_table, seq_lens, k_tail, v_tail,
+                                      rows=True)
     B = seq_lens.shape[0]
     if cu_q.shape != (B + 1,):
         raise ValueError("cu_q must be [batch + 1]")
-    total_q, hq = q.shape[0], q.shape[1]
-    hkv = k_pool.shape[1]
-    if block_table.dim() != 2 or block_table.shape[0] != B or not block_table.is_contiguous():
-        raise ValueError("block_table must be contiguous [B, width]")
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(128)
     if workspace is None:
         workspace = new_chunk_workspace(params, max(total_q, 1), hq, hkv, max_seq_len, q.device)
     if out is None:
         out = torch.empty_like(q)
+    _need(out, "out", torch.float16)
+    if tuple(out.shape) != tuple(q.shape) or not out.is_contiguous():
+        raise ValueError("out must be contiguous and shaped like q")
     _check(lib.kvarn_chunk_attention(ctypes.byref(params), _ptr(q), total_q, _ptr(cu_q), B, hq,
                                      hkv, _ptr(k_pool), _ptr(v_pool),
                                      _pools_n(params, k_pool, v_pool),
@@ -428,8 +466,14 @@ def prepare_append(params: Params, k_new, v_new, seq_lens, k_tail, v_tail, block
     _need(seq_lens, "seq_lens", torch.int32)
     _need(block_table, "block_table", torch.int32)
     B, hkv = k_new.shape[0], k_new.shape[1]
+    if k_new.dim() != 3 or k_new.shape[2] != 128 or tuple(v_new.shape) != tuple(k_new.shape):
+        raise ValueError("k_new / v_new must be [B, Hkv, 128]")
+    if seq_lens.dim() != 1 or seq_lens.shape[0] != B:
+        raise ValueError(f"seq_lens must be [{B}]")
     if tuple(k_tail.shape) != (B, hkv, 128, 128) or tuple(v_tail.shape) != (B, hkv, 128, 128):
         raise ValueError("staging must be [B, Hkv, 128, 128]")
+    if k_pool.shape[1] != hkv:
+        raise ValueError(f"pools must have {hkv} KV heads")
     if block_table.dim() != 2 or block_table.shape[0] != B or not block_table.is_contiguous():
         raise ValueError("block_table must be contiguous [B, width]")
     args = (ctypes.byref(params), _ptr(k_new), _ptr(v_new), B, hkv, _ptr(seq_lens),
@@ -442,9 +486,11 @@ def prepare_append(params: Params, k_new, v_new, seq_lens, k_tail, v_tail, block
 def prepare_decode(params: Params, q, k_pool, v_pool, block_table, seq_lens, max_seq_len: int,
                    workspace, out, k_tail=None, v_tail=None, softmax_scale=None,
                    stream=None) -> Prepared:
-    _need(q, "q", torch.float16)
-    B, hq = q.shape[0], q.shape[1]
-    hkv = k_pool.shape[1]
+    B, hq, hkv = _decode_shapes(q, k_pool, v_pool, block_table, seq_lens, k_tail, v_tail)
+    _need(workspace, "workspace", torch.uint8)
+    _need(out, "out", torch.float16)
+    if tuple(out.shape) != tuple(q.shape) or not out.is_contiguous():
+        raise ValueError("out must be contiguous and shaped like q")
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(128)
     args = (ctypes.byref(params), _ptr(q), B, hq, hkv, _ptr(k_pool), _ptr(v_pool),

@@ -19,7 +19,8 @@
  *     frees or retains them. Host pointers are named *_host or are plain structs.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). All GPU work
  *     is enqueued on it; calls return once the work is queued.
- *   - The library allocates no memory and keeps no global state. It is re-entrant.
+ *   - The library allocates no memory. It keeps no global state except the fixed decode
+ *     scratch of kvarn_decode_attention_noalloc (one per GPU, below). It is re-entrant.
  *   - Arguments are validated on the host before anything is enqueued. On any error
  *     nothing is enqueued and outputs are untouched.
  *   - Device-resident indices (page ids, token offsets, sequence lengths) cannot be checked
@@ -294,6 +295,31 @@ KVARN_API kvarn_status kvarn_decode_attention(const kvarn_params* params, const 
                                     const void* v_tail_dev, float softmax_scale,
                                     void* workspace_dev, size_t workspace_bytes,
                                     void* out_dev, void* stream);
+
+/* For callers that cannot allocate (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): kvarn_decode_attention without a workspace argument.
+ * Every argument, the result and every error are those of kvarn_decode_attention; the
+ * split partials live in a fixed device scratch buffer of
+ * kvarn_decode_noalloc_max_workspace_bytes() bytes (32 MiB) that the library holds on each
+ * GPU it runs on until the process ends. A shape whose kvarn_decode_workspace_bytes exceeds
+ * it returns KVARN_ERR_WORKSPACE with nothing enqueued. The call allocates no memory; its
+ * first call on a device looks up that device's scratch address (KVARN_ERR_HIP on failure).
+ * `stream` must belong to the current device (KVARN_ERR_INVALID_ARG otherwise). The scratch
+ * needs no clearing (every partial the merge reads is written by the same call). All calls
+ * on one GPU share its scratch: calls that overlap in time on one GPU (concurrent streams,
+ * or host threads enqueueing on different streams) race and give undefined output; calls
+ * ordered on one stream are safe. */
+KVARN_API size_t kvarn_decode_noalloc_max_workspace_bytes(void);
+KVARN_API kvarn_status kvarn_decode_attention_noalloc(const kvarn_params* params,
+                                            const void* q_dev, int32_t batch,
+                                            int32_t num_q_heads, int32_t num_kv_heads,
+                                            const void* k_pool_dev, const void* v_pool_dev,
+                                            int64_t pool_num_pages,
+                                            const int32_t* block_table_dev,
+                                            int32_t block_table_stride,
+                                            const int32_t* seq_lens_dev, int32_t max_seq_len,
+                                            const void* k_tail_dev, const void* v_tail_dev,
+                                            float softmax_scale, void* out_dev, void* stream);
 
 #ifdef __cplusplus
 }

@@ -233,14 +233,17 @@ int32_t kvarn_decode_num_splits(const kvarn_params* params, int32_t batch, int32
   return kvarn::decode_num_splits(batch, num_kv_heads, max_seq_len);
 }
 
-kvarn_status kvarn_decode_attention(const kvarn_params* params, const void* q, int32_t batch,
-                                    int32_t num_q_heads, int32_t num_kv_heads, const void* k_pool,
-                                    const void* v_pool, int64_t pool_num_pages,
-                                    const int32_t* block_table, int32_t block_table_stride,
-                                    const int32_t* seq_lens, int32_t max_seq_len,
-                                    const void* k_tail, const void* v_tail, float softmax_scale,
-                                    void* workspace, size_t workspace_bytes, void* out,
-                                    void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Every check of kvarn_decode_attention except the workspace size.
+kvarn_status check_decode(const kvarn_params* params, const void* q, int32_t batch,
+                          int32_t num_q_heads, int32_t num_kv_heads, const void* k_pool,
+                          const void* v_pool, int64_t pool_num_pages, const int32_t* block_table,
+                          int32_t block_table_stride, const int32_t* seq_lens,
+                          int32_t max_seq_len, const void* k_tail, const void* v_tail,
+                          float softmax_scale, const void* out) {
   const kvarn_status st = kvarn_params_check(params);
   if (st != KVARN_OK) return st;
   if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_seq_len < 0 ||
@@ -253,7 +256,7 @@ kvarn_status kvarn_decode_attention(const kvarn_params* params, const void* q, i
   if (batch > 65535 || int64_t(batch) * num_kv_heads > INT32_MAX) return KVARN_ERR_UNSUPPORTED;
   if (!isfinite(softmax_scale)) return KVARN_ERR_INVALID_ARG;
   if (batch == 0) return KVARN_OK;
-  if (!q || !seq_lens || !out || !workspace) return KVARN_ERR_INVALID_ARG;
+  if (!q || !seq_lens || !out) return KVARN_ERR_INVALID_ARG;
   if ((k_tail == nullptr) != (v_tail == nullptr)) return KVARN_ERR_INVALID_ARG;
   if (max_seq_len >= 128) {
     if (!k_pool || !v_pool || !block_table) return KVARN_ERR_INVALID_ARG;
@@ -262,14 +265,71 @@ kvarn_status kvarn_decode_attention(const kvarn_params* params, const void* q, i
     if (block_table_stride < max_seq_len / 128) return KVARN_ERR_INVALID_ARG;
     if (!aligned16(k_pool) || !aligned16(v_pool)) return KVARN_ERR_INVALID_ARG;
   }
-  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return KVARN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(out)) return KVARN_ERR_INVALID_ARG;
   if (k_tail && (!aligned16(k_tail) || !aligned16(v_tail))) return KVARN_ERR_INVALID_ARG;
+  return KVARN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvarn_status kvarn_decode_attention(const kvarn_params* params, const void* q, int32_t batch,
+                                    int32_t num_q_heads, int32_t num_kv_heads, const void* k_pool,
+                                    const void* v_pool, int64_t pool_num_pages,
+                                    const int32_t* block_table, int32_t block_table_stride,
+                                    const int32_t* seq_lens, int32_t max_seq_len,
+                                    const void* k_tail, const void* v_tail, float softmax_scale,
+                                    void* workspace, size_t workspace_bytes, void* out,
+                                    void* stream) {
+  const kvarn_status st =
+      check_decode(params, q, batch, num_q_heads, num_kv_heads, k_pool, v_pool, pool_num_pages,
+                   block_table, block_table_stride, seq_lens, max_seq_len, k_tail, v_tail,
+                   softmax_scale, out);
+  if (st != KVARN_OK || batch == 0) return st;
+  if (!workspace) return KVARN_ERR_INVALID_ARG;
+  if (!aligned16(workspace)) return KVARN_ERR_INVALID_ARG;
   if (workspace_bytes < kvarn::decode_workspace_bytes(batch, num_q_heads, num_kv_heads, max_seq_len))
     return KVARN_ERR_WORKSPACE;
   return launch_status(kvarn::launch_decode(
       params->k_bits, params->v_bits, q, batch, num_q_heads, num_kv_heads, k_pool, v_pool, pool_num_pages, block_table,
       block_table_stride, seq_lens, max_seq_len, nullptr, batch, k_tail, v_tail, softmax_scale,
       workspace, out, static_cast<hipStream_t>(stream)));
+}
+
+size_t kvarn_decode_noalloc_max_workspace_bytes(void) { return kvarn::kDecodeScratchBytes; }
+
+kvarn_status kvarn_decode_attention_noalloc(const kvarn_params* params, const void* q,
+                                            int32_t batch, int32_t num_q_heads,
+                                            int32_t num_kv_heads, const void* k_pool,
+                                            const void* v_pool, int64_t pool_num_pages,
+                                            const int32_t* block_table,
+                                            int32_t block_table_stride, const int32_t* seq_lens,
+                                            int32_t max_seq_len, const void* k_tail,
+                                            const void* v_tail, float softmax_scale, void* out,
+                                            void* stream) {
+  const kvarn_status st =
+      check_decode(params, q, batch, num_q_heads, num_kv_heads, k_pool, v_pool, pool_num_pages,
+                   block_table, block_table_stride, seq_lens, max_seq_len, k_tail, v_tail,
+                   softmax_scale, out);
+  if (st != KVARN_OK || batch == 0) return st;
+  if (kvarn::decode_workspace_bytes(batch, num_q_heads, num_kv_heads, max_seq_len) >
+      kvarn::kDecodeScratchBytes)
+    return KVARN_ERR_WORKSPACE;
+  // the stream must belong to the current device, whose scratch copy the kernels use
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int cur = 0, sdev = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return KVARN_ERR_HIP;
+  if (s != nullptr) {
+    if (hipStreamGetDevice(s, &sdev) != hipSuccess) return KVARN_ERR_HIP;
+    if (sdev != cur) return KVARN_ERR_INVALID_ARG;
+  }
+  void* ws = nullptr;
+  if (kvarn::decode_scratch(&ws) != hipSuccess) return KVARN_ERR_HIP;
+  return launch_status(kvarn::launch_decode(
+      params->k_bits, params->v_bits, q, batch, num_q_heads, num_kv_heads, k_pool, v_pool,
+      pool_num_pages, block_table, block_table_stride, seq_lens, max_seq_len, nullptr, batch,
+      k_tail, v_tail, softmax_scale, ws, out, s));
 }
 
 kvarn_status kvarn_chunk_attention(const kvarn_params* params, const void* q, int32_t total_q,

@@ -30,6 +30,8 @@
 // softmax (rows 0,1 of each C fragment on the high lane, rows 2,3 on the low lane) and swap
 // halves with bank-masked DPP moves. B operands are scaled by a power of two per page so that
 // their largest float16 high part is near 2^14 (no overflow, full low-part precision).
+#include <mutex>
+
 #include "decode_common.h"
 #include "kvarn_launch.h"
 
@@ -757,6 +759,37 @@ int32_t decode_balanced_wg(int32_t batch, int32_t num_kv_heads, int32_t max_seq_
   if (batch < 2 || batch > kMaxBalancedRows || max_full < 1 || work >= (int64_t(1) << 31)) return 0;
   const int64_t wg = (work + 3) / 4;
   return int32_t(wg < kBalancedPageWg ? wg : kBalancedPageWg);
+}
+
+// Fixed device scratch of the entry point that allocates nothing (callers that cannot call
+// hipMalloc: graph capture, tight serving loops). Each GPU the library runs on holds its own
+// copy until the process ends. In host code `scratch` names a host-side stand-in, never a
+// device address: kernels get the address decode_scratch() obtained for the current device.
+__device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  *ptr = nullptr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    // once per device, with that device current: the address of this device's copy
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 size_t decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

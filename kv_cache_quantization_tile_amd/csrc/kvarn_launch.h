@@ -58,6 +58,11 @@ hipError_t launch_append_tokens(int k_bits, int v_bits, const void* k_new, const
                                 int32_t bt_stride, void* k_pool, void* v_pool,
                                 int64_t pool_num_pages, int n_iters, hipStream_t stream);
 
+// Bytes of the fixed device scratch that kvarn_decode_attention_noalloc uses as its
+// workspace, and the address of the current device's copy (taken once per device).
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+hipError_t decode_scratch(void** ptr);
+
 int32_t decode_tiles_per_wave(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len);
 int32_t decode_num_splits(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len);
 size_t decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

@@ -63,6 +63,10 @@ def _load():
         "kvarn_chunk_workspace_bytes": (sz, [P, i32, i32, i32, i32]),
         "kvarn_decode_attention": (ctypes.c_int, [P, vp, i32, i32, i32, vp, vp, i64, vp, i32, vp,
                                                   i32, vp, vp, ctypes.c_float, vp, sz, vp, vp]),
+        "kvarn_decode_noalloc_max_workspace_bytes": (sz, []),
+        "kvarn_decode_attention_noalloc": (ctypes.c_int, [P, vp, i32, i32, i32, vp, vp, i64, vp,
+                                                          i32, vp, i32, vp, vp, ctypes.c_float,
+                                                          vp, vp]),
         "kvarn_chunk_attention": (ctypes.c_int, [P, vp, i32, vp, i32, i32, i32, vp, vp, i64, vp,
                                                  i32, vp, i32, vp, vp, ctypes.c_float, vp, sz,
                                                  vp, vp]),
@@ -80,7 +84,8 @@ EXPORTED = ("kvarn_abi_version", "kvarn_format_version", "kvarn_status_str",
             "kvarn_quantize_tiles", "kvarn_quantize_kv_tiles", "kvarn_append_tokens",
             "kvarn_write_tokens", "kvarn_dequantize_tiles", "kvarn_decode_workspace_bytes",
             "kvarn_decode_num_splits", "kvarn_decode_attention", "kvarn_chunk_attention",
-            "kvarn_chunk_workspace_bytes")
+            "kvarn_chunk_workspace_bytes", "kvarn_decode_noalloc_max_workspace_bytes",
+            "kvarn_decode_attention_noalloc")
 
 
 def _check(status: int, what: str):
@@ -384,6 +389,35 @@ def decode_attention(params: Params, q, k_pool, v_pool, block_table, seq_lens, m
                                       _ptr(k_tail), _ptr(v_tail), float(softmax_scale),
                                       _ptr(workspace), workspace.numel(), _ptr(out),
                                       _stream(stream)), "kvarn_decode_attention")
+    return out
+
+
+def decode_noalloc_max_workspace_bytes() -> int:
+    return int(lib.kvarn_decode_noalloc_max_workspace_bytes())
+
+
+def decode_attention_noalloc(params: Params, q, k_pool, v_pool, block_table, seq_lens,
+                             max_seq_len: int, k_tail=None, v_tail=None,
+                             softmax_scale: float | None = None, out=None,
+                             stream=None) -> torch.Tensor:
+    """decode_attention with the library's fixed device scratch as its workspace (the entry
+    point that allocates nothing; calls that overlap on one GPU race). out is allocated here
+    when omitted, so a caller that must not allocate passes it."""
+    B, hq, hkv = _decode_shapes(q, k_pool, v_pool, block_table, seq_lens, k_tail, v_tail)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(128)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.float16)
+    if tuple(out.shape) != tuple(q.shape) or not out.is_contiguous():
+        raise ValueError("out must be contiguous and shaped like q")
+    _check(lib.kvarn_decode_attention_noalloc(ctypes.byref(params), _ptr(q), B, hq, hkv,
+                                              _ptr(k_pool), _ptr(v_pool),
+                                              _pools_n(params, k_pool, v_pool),
+                                              _ptr(block_table), block_table.shape[1],
+                                              _ptr(seq_lens), max_seq_len, _ptr(k_tail),
+                                              _ptr(v_tail), float(softmax_scale), _ptr(out),
+                                              _stream(stream)), "kvarn_decode_attention_noalloc")
     return out
 
 

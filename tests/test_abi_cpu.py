@@ -191,6 +191,43 @@ def test_decode_validation():
     assert _decode(p, wsb=need - 1) == WS
 
 
+def _noalloc(p, **kw):
+    a = dict(q=FAKE, B=2, hq=64, hkv=8, kp=FAKE, vp=FAKE, npages=100, bt=FAKE, bts=200, sl=FAKE,
+             mx=16384, kt=None, vt=None, scale=0.088, out=FAKE)
+    a.update(kw)
+    return K.lib.kvarn_decode_attention_noalloc(ctypes.byref(p), a["q"], a["B"], a["hq"], a["hkv"],
+                                                a["kp"], a["vp"], a["npages"], a["bt"], a["bts"],
+                                                a["sl"], a["mx"], a["kt"], a["vt"], a["scale"],
+                                                a["out"], None)
+
+
+def test_decode_noalloc_validation():
+    """The entry point that allocates nothing: the checks of kvarn_decode_attention, and
+    KVARN_ERR_WORKSPACE for a shape whose workspace exceeds the fixed 32 MiB scratch (all
+    rejected on the host, before any HIP call)."""
+    p = K.params_from_dtype()
+    cap = K.decode_noalloc_max_workspace_bytes()
+    assert cap == 32 << 20
+    assert _noalloc(p, B=0) == OK
+    assert _noalloc(p, hq=63) == INVALID
+    assert _noalloc(p, hq=128) == UNSUP
+    assert _noalloc(p, B=70000) == UNSUP
+    assert _noalloc(p, q=None) == INVALID
+    assert _noalloc(p, out=None) == INVALID
+    assert _noalloc(p, kt=FAKE) == INVALID
+    assert _noalloc(p, bts=10) == INVALID
+    assert _noalloc(p, scale=float("nan")) == INVALID
+    assert _noalloc(p, out=ctypes.c_void_p(0x10002)) == INVALID
+    assert _noalloc(p, kp=None) == INVALID
+    # 1024 sequences of 4096 tokens need ~78 MB of partials: more than the scratch holds
+    big = K.decode_workspace_bytes(p, 1024, 64, 8, 4096)
+    assert big > cap
+    assert _noalloc(p, B=1024, bts=64, mx=4096) == WS
+    # the decode workloads' shapes fit
+    for B, mx in ((1, 16384), (32, 32784), (1, 131136), (64, 16384)):
+        assert K.decode_workspace_bytes(p, B, 64, 8, mx) <= cap, (B, mx)
+
+
 def _chunk(p, **kw):
     a = dict(q=FAKE, tq=16, cu=FAKE, B=2, hq=64, hkv=8, kp=FAKE, vp=FAKE, npages=100, bt=FAKE,
              bts=200, sl=FAKE, mx=16384, kt=None, vt=None, scale=0.088, ws=FAKE, wsb=1 << 30,

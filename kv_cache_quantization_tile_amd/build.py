@@ -1,4 +1,5 @@
-"""Build the KVarN HIP library in-tree: kv_cache_quantization_tile_amd/libkvarn.so.
+"""Build the KVarN HIP library in-tree: kv_cache_quantization_tile_amd/libkvarn.so, and the
+benchmark's streaming-read probe beside it (libkvarn_probe.so, measurement only).
 
 Runs hipcc for gfx950 on every call (the build is a few seconds). Usable as a script:
     python -m kv_cache_quantization_tile_amd.build
@@ -15,6 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkvarn.so")
 SOURCES = ["api.hip", "quantize.hip", "decode.hip", "mq.hip"]
+PROBE_LIB = os.path.join(PKG, "libkvarn_probe.so")
+PROBE_SOURCES = ["probe/stream_read.hip"]
 ARCH = "gfx950"
 
 FLAGS = [
@@ -35,11 +38,10 @@ def hipcc() -> str:
     return exe
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into libkvarn.so (atomically replaced). Returns its path."""
-    tmp = LIB + ".tmp"
+def _compile(sources, out: str, verbose: bool) -> str:
+    tmp = out + ".tmp"
     cmd = [hipcc(), *FLAGS, "-I", os.path.join(ROOT, "include"),
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+           *[os.path.join(CSRC, s) for s in sources], "-o", tmp]
     proc = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     log = "\n".join(l for l in (proc.stdout + proc.stderr).splitlines() if noise not in l)
@@ -47,7 +49,15 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + log)
     if verbose and log.strip():
         print(log, file=sys.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source into libkvarn.so and the probe into libkvarn_probe.so (each
+    atomically replaced). Returns the library's path."""
+    _compile(SOURCES, LIB, verbose)
+    _compile(PROBE_SOURCES, PROBE_LIB, verbose)
     return LIB
 
 

@@ -110,6 +110,11 @@ __device__ __forceinline__ void lds_read8(const float* p, float (&v)[8]) {
 __device__ __forceinline__ uint16_t normalizer16(float v) {
   return f2h_rn(fminf(fmaxf(v, 6.103515625e-05f), 65504.f));
 }
+// float16 bits of a scale or zero point: saturated to the finite range [-65504, 65504] first
+// (a near-constant group can normalize to values beyond float16; the record stays finite)
+__device__ __forceinline__ uint16_t meta16(float v) {
+  return f2h_rn(fminf(fmaxf(v, -65504.f), 65504.f));
+}
 
 // 4 codes (bytes, each <= 3) -> 4 crumbs in the low 8 bits, byte k -> crumb k
 __device__ __forceinline__ uint32_t bytes_to_crumbs(uint32_t e) {
@@ -458,8 +463,8 @@ __device__ __forceinline__ void quantize_tile(RowPtr row_ptr, uint8_t* __restric
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const float lo = omn[k] * ir_own[k], hi_ = omx[k] * ir_own[k];   // y = z / r, r > 0
-      const uint16_t sc16 = f2h_rn((hi_ - lo) * (BITS == 4 ? 1.f / 15.f : 1.f / 3.f));
-      const uint16_t zr16 = f2h_rn(lo);
+      const uint16_t sc16 = meta16((hi_ - lo) * (BITS == 4 ? 1.f / 15.f : 1.f / 3.f));
+      const uint16_t zr16 = meta16(lo);
       const float sc = h2f(sc16);
       const float inv = sc > 0.f ? __builtin_amdgcn_rcpf(sc) : 0.f;
       A2[k] = ir_own[k] * inv;
@@ -528,8 +533,8 @@ __device__ __forceinline__ void quantize_tile(RowPtr row_ptr, uint8_t* __restric
     }
     const float lo = row16_scatter8<1>(mn, l) * is_own;   // y = z / s, s > 0
     const float hi_ = row16_scatter8<2>(mx, l) * is_own;
-    const uint16_t sc16 = f2h_rn((hi_ - lo) * (BITS == 2 ? 1.f / 3.f : 1.f / 15.f));
-    const uint16_t zr16 = f2h_rn(lo);
+    const uint16_t sc16 = meta16((hi_ - lo) * (BITS == 2 ? 1.f / 3.f : 1.f / 15.f));
+    const uint16_t zr16 = meta16(lo);
     const float sc = h2f(sc16);
     const float inv = sc > 0.f ? __builtin_amdgcn_rcpf(sc) : 0.f;
     if ((l & 8) == 0) {

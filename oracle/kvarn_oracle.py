@@ -25,7 +25,8 @@ Readings taken where the pages are silent (all listed with reasons in the design
   * a zero / non-finite std skips that update;
   * normalizers rounded to float16 (clipped to [2^-14, 65504]) and the tile is quantized
     against the stored float16 values;
-  * asymmetric RTN: zero = group min, scale = (max - min) / (2^b - 1), both stored float16,
+  * asymmetric RTN: zero = group min, scale = (max - min) / (2^b - 1), both stored float16
+    (saturated to +-65504, as the normalizers are clipped to the float16 range),
     code = round-half-even((y - zero) / scale) clipped to [0, 2^b - 1]; scale 0 => code 0.
 
 Parity status: every function below is pinned by tests that do not re-type its formula
@@ -127,6 +128,13 @@ def store_normalizer(log_v: np.ndarray) -> np.ndarray:
     return to_fp16(np.clip(np.exp(log_v), FP16_MIN_NORMAL, FP16_MAX))
 
 
+def store_meta(v: np.ndarray) -> np.ndarray:
+    """A scale or zero point as stored: float16 round-to-nearest-even, saturated to the finite
+    range [-65504, 65504] (the stored format holds float16 metadata, like the normalizers, and
+    a finite input never yields an infinite record)."""
+    return to_fp16(np.clip(v, -FP16_MAX, FP16_MAX))
+
+
 def rtn_asym(y: np.ndarray, bits: int, axis: int):
     """Stage 4 ([README] "How KVarN works", stage 4): asymmetric round-to-nearest.
 
@@ -137,8 +145,8 @@ def rtn_asym(y: np.ndarray, bits: int, axis: int):
     qmax = (1 << bits) - 1
     mn = y.min(axis=axis, keepdims=True)
     mx = y.max(axis=axis, keepdims=True)
-    scale16 = to_fp16((mx - mn) / qmax)
-    zero16 = to_fp16(mn)
+    scale16 = store_meta((mx - mn) / qmax)
+    zero16 = store_meta(mn)
     sc = scale16.astype(np.float64)
     zr = zero16.astype(np.float64)
     live = sc > 0
@@ -438,6 +446,24 @@ def decode_attention_row(q_row, k_pages, v_pages, k_tail=None, v_tail=None,
     k = np.concatenate(ks, axis=0)
     v = np.concatenate(vs, axis=0)
     return attention(np.asarray(q_row, np.float16).astype(np.float64), k, v, softmax_scale)
+
+
+def causal_attention(q_rows: np.ndarray, positions, k: np.ndarray, v: np.ndarray,
+                     softmax_scale: float) -> np.ndarray:
+    """Causal attention of several query rows over one cache (the read path of a prefill chunk
+    or of draft tokens): row i sits at cache position positions[i] and attends to the keys at
+    positions 0 .. positions[i], inclusive; a row at a negative position (before the cache
+    starts) has no keys and returns zeros.
+
+    q_rows: [n, 128]; k, v: [C, 128] (the cache in position order). Returns float64 [n, 128].
+    """
+    q_rows = np.asarray(q_rows, np.float64)
+    out = np.zeros((q_rows.shape[0], np.asarray(v).shape[1]), dtype=np.float64)
+    for i, p in enumerate(positions):
+        if p < 0:
+            continue
+        out[i] = attention(q_rows[i], k[:p + 1], v[:p + 1], softmax_scale)
+    return out
 
 
 def merge_partials(m: np.ndarray, l: np.ndarray, acc: np.ndarray) -> np.ndarray:

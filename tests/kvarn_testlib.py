@@ -1,13 +1,15 @@
 """Shared parity machinery for the GPU tests: the HIP path against the CPU oracle.
 
 Criteria (tolerances stated for the method's output, checked element by element):
-  L1 metadata: r, s within 1e-3 relative of the oracle's float16 values; scale within 1e-3
-     relative and zero within 1e-3 * max(|zero|, scale), each widened by the relative r, s
-     difference its group sees (scale and zero come from y = Xr / (r s) on each side's own
-     stored r, s, so a 1-ulp normalizer flip carries over to them) and by the float32 bound
-     on y that L2 uses (delta below): zero = min y moves by up to delta, scale = range / levels
-     by up to 2 delta / levels. That term only matters for a group whose range is a tiny
-     fraction of its values (e.g. the DC channel of a nearly constant tile).
+  L1 metadata: r, s within 1e-3 relative of the oracle's float16 values. scale within 1e-3
+     relative and zero within 1e-3 * max(|zero|, scale), widened per group by what the allowed
+     normalizer differences can do to it: scale and zero are float16 roundings of the range
+     and minimum of y = Xr / (r s), each side with its own stored r, s, so |min_gpu - min_oracle|
+     is at most the larger |y_gpu - y_oracle| at the two sides' argmin elements, plus the float32
+     evaluation bound delta on y (below); the same for the max. Only the elements that set a
+     group's min or max widen its bar. Every scale or zero beyond the plain 1e-3 must have a
+     float16 normalizer difference at one of those elements (a documented cascade); their count
+     is reported and its rate asserted (META_PLAIN_RATE).
   L2 conditional codes: codes re-derived by the oracle from its float64 rotated tile and the
      GPU's own stored r, s, scale, zero must equal the GPU codes, except where the unrounded
      code value lies within a tie band of a rounding boundary: TIE_BAND plus the float32
@@ -16,6 +18,12 @@ Criteria (tolerances stated for the method's output, checked element by element)
      bound is delta = 32 ulp(|x_t|_1 / sqrt(128)) / (r_c s_t).
   L3 unconditional codes: GPU codes differ from the oracle's in at most 1e-4 of all codes,
      each by exactly 1 (rounding ties, and cascades of a 1-ulp float16 metadata flip).
+     Offset-dominated groups are the one exception: a group whose largest |y| exceeds 512
+     times its scale (so one float16 ulp of its zero point, or a 1-ulp normalizer flip, moves
+     its values by more than half a code step) codes the same values with a different zero
+     point when its float16 zero differs by one ulp, so its codes may differ by several
+     levels. Such groups are held to L2 and to a reconstruction bound (the GPU tile's
+     reconstruction error at most 5% above the oracle's) and kept out of the L3 rate.
   Attention: per (sequence, query head) row, max|o_gpu - o_oracle| <= 2e-3 max|o_oracle|.
 """
 from __future__ import annotations
@@ -29,6 +37,13 @@ TIE_BAND = 1e-4
 META_RTOL = 1e-3
 CODE_MISMATCH_RATE = 1e-4
 ATTN_RTOL = 2e-3
+# plain-1e-3 scale / zero differences (each one asserted to be a cascade of a normalizer flip)
+# as a fraction of all scales and zeros. Stress batches with offset-dominated tiles: worst
+# measured 2.9e-3 (36 mixed tiles at two iterations, value scales: the offset tiles' DC-channel
+# normalizer is not converged at N = 2 and one 1-ulp flip of it moves every token's range);
+# the workloads' data is held to 2e-4 by its own tests (measured at most 4.6e-5)
+META_PLAIN_RATE = 5e-3
+OFFSET_DOMINATED = 512.0      # max |y| / scale of a group beyond which it is offset-dominated
 
 
 def records_of(pool: torch.Tensor, pages, head: int):
@@ -46,14 +61,22 @@ class QuantStats:
         self.meta_exact = 0
         self.meta_total = 0
         self.max_meta_rel = 0.0
+        self.meta_plain_over = 0        # scales and zeros beyond the plain 1e-3
+        self.meta_plain_total = 0
+        self.offset_groups = 0          # offset-dominated groups (kept out of the L3 rate)
 
     def rate(self):
         return self.l3_mismatch / max(self.codes, 1)
 
+    def plain_rate(self):
+        return self.meta_plain_over / max(self.meta_plain_total, 1)
+
     def __repr__(self):
         return (f"codes={self.codes} L3 mismatches={self.l3_mismatch} ({self.rate():.2e}) "
                 f"L2 outside-tie={self.l2_mismatch} meta exact {self.meta_exact}/{self.meta_total} "
-                f"max meta rel {self.max_meta_rel:.2e}")
+                f"max meta rel {self.max_meta_rel:.2e} scale/zero beyond plain 1e-3: "
+                f"{self.meta_plain_over}/{self.meta_plain_total} ({self.plain_rate():.2e}) "
+                f"offset-dominated groups {self.offset_groups}")
 
 
 def reconstruction_error(x_ct: np.ndarray, d: dict, kind: int) -> float:
@@ -62,118 +85,109 @@ def reconstruction_error(x_ct: np.ndarray, d: dict, kind: int) -> float:
 
 
 def check_quantized_tiles(tiles_tc: np.ndarray, records, kind: int, n_iters: int,
-                          stats: QuantStats | None = None, rate_exempt=(),
-                          ill_conditioned=(), k_bits: int = 4, v_bits: int = 2) -> QuantStats:
+                          stats: QuantStats | None = None, k_bits: int = 4,
+                          v_bits: int = 2) -> QuantStats:
     """tiles_tc: [n, 128 tokens, 128 channels] float16 (the source layout); records: the GPU
-    page records of those tiles. Asserts L1 and L2, accumulates L3 statistics.
-
-    Tiles listed in rate_exempt are ill-conditioned on purpose (values identical up to below
-    float16 resolution, so a 1-ulp metadata difference moves many tied codes at once); they
-    are held to L1, L2 and |code difference| <= 1 but kept out of the L3 rate.
-
-    Tiles listed in ill_conditioned make the normalization itself ill-conditioned (a row that
-    becomes constant up to ~1e-4 relative, where a float32 std cannot match a float64 one);
-    they are held to L2 (codes correctly rounded for the stored metadata), finite metadata
-    and a reconstruction error at most 5% above the oracle's."""
+    page records of those tiles. Asserts L1 and L2 (every tile, every group) and L3's
+    |code difference| <= 1 outside offset-dominated groups; accumulates the L3 and plain
+    metadata statistics (asserted by the caller: assert_rate)."""
     stats = stats or QuantStats()
     x = np.ascontiguousarray(np.swapaxes(tiles_tc, -1, -2))  # channels x tokens
     ref = O.quantize_tiles(x, kind, n_iters, k_bits=k_bits, v_bits=v_bits)
     unpack = lambda rec: O.unpack_record(rec, kind, k_bits, v_bits)
     bits = k_bits if kind == O.KIND_K else v_bits
     qmax = (1 << bits) - 1
+    ax = 1 if kind == O.KIND_K else 0          # the axis a group runs along (c x t tile)
+    grp = (lambda v: v[:, None]) if kind == O.KIND_K else (lambda v: v[None, :])
     for i, rec in enumerate(records):
         g = unpack(rec)
-        if i in ill_conditioned:
-            for key in ("r", "s", "scale", "zero"):
-                assert np.all(np.isfinite(g[key].astype(np.float64))), (key, i)
-            e_gpu = reconstruction_error(x[i].astype(np.float64), g, kind)
-            e_ref = reconstruction_error(x[i].astype(np.float64), {k_: ref[k_][i] for k_ in ("codes", "r", "s", "scale", "zero")}, kind)
-            assert e_gpu <= 1.05 * e_ref + 1e-6 * float(np.linalg.norm(x[i].astype(np.float64))), (i, e_gpu, e_ref)
-        # ---- L1
-        # scale and zero are float16 roundings of the range and minimum of y = Xr / (r s) taken
-        # with each side's own stored r, s: a 1-ulp flip of those (allowed above) moves them by
-        # the group's relative r, s differences, which are added to their tolerance, as is the
-        # float32 evaluation bound on y (delta, the L2 band in units of y) over the group
-        delta_g = _delta_group(x[i], ref["r"][i], ref["s"][i], kind)
-        dev = {}
-        for key in ("r", "s", "scale") if i not in ill_conditioned else ():
+        for key in ("r", "s", "scale", "zero"):
+            assert np.all(np.isfinite(g[key].astype(np.float64))), (key, i)
+        # ---- L1: r, s at the plain bar
+        for key in ("r", "s"):
             a = g[key].astype(np.float64)
             b = ref[key][i].astype(np.float64)
-            with np.errstate(invalid="ignore"):
-                rel = np.abs(a - b) / np.maximum(np.abs(b), 1e-30)
-            # identical values match, including a float16 overflow to inf on both sides
-            rel = np.where(a == b, 0.0, rel)
-            dev[key] = rel
+            rel = np.where(a == b, 0.0, np.abs(a - b) / np.maximum(np.abs(b), 1e-30))
             stats.max_meta_rel = max(stats.max_meta_rel, float(rel.max()))
-            if key != "scale":
-                ok = rel <= META_RTOL
-            else:   # absolute form, so that a zero-range group is held to 2 delta / levels
-                with np.errstate(invalid="ignore"):
-                    ok = (a == b) | (np.abs(a - b) <= (META_RTOL + 1.01 * _cascade(dev, kind)) * np.abs(b)
-                                     + 1.01 * 2.0 * delta_g / qmax)
-            assert np.all(ok), (key, i, float(rel.max()), _meta_report(g, ref, i))
+            assert np.all(rel <= META_RTOL), (key, i, float(rel.max()), _meta_report(g, ref, i))
             stats.meta_exact += int(np.sum(g[key] == ref[key][i]))
             stats.meta_total += 128
-        if i not in ill_conditioned:
-            za, zb = g["zero"].astype(np.float64), ref["zero"][i].astype(np.float64)
-            zt = (META_RTOL * np.maximum(np.abs(zb), ref["scale"][i].astype(np.float64))
-                  + 1.01 * (_cascade(dev, kind) * np.abs(zb) + delta_g) + 1e-30)
-            with np.errstate(invalid="ignore"):
-                zok = (za == zb) | (np.abs(za - zb) <= zt)
-            assert np.all(zok), ("zero", i, za[~zok][:4], zb[~zok][:4], _meta_report(g, ref, i))
-            stats.meta_exact += int(np.sum(g["zero"] == ref["zero"][i]))
-            stats.meta_total += 128
+        # ---- L1: scale, zero against the per-group cascade bound
+        r_g, s_g = g["r"].astype(np.float64), g["s"].astype(np.float64)
+        y_g = ref["xr"][i] / (r_g[:, None] * s_g[None, :])     # oracle's Xr, GPU's normalizers
+        y_o = ref["y"][i]
+        dy = np.abs(y_g - y_o)
+        delta = _delta(x[i], r_g, s_g)                          # float32 bound on y
+        d_max = delta.max(axis=ax)
+        at = lambda arr, idx: np.take_along_axis(arr, np.expand_dims(idx, ax), ax).squeeze(ax)
+        lo_o, lo_g = y_o.argmin(ax), y_g.argmin(ax)
+        hi_o, hi_g = y_o.argmax(ax), y_g.argmax(ax)
+        a_lo = np.maximum(at(dy, lo_o), at(dy, lo_g)) + d_max
+        a_hi = np.maximum(at(dy, hi_o), at(dy, hi_g)) + d_max
+        sa, sb = g["scale"].astype(np.float64), ref["scale"][i].astype(np.float64)
+        za, zb = g["zero"].astype(np.float64), ref["zero"][i].astype(np.float64)
+        tol_s = META_RTOL * np.abs(sb) + 1.01 * (a_lo + a_hi) / qmax
+        tol_z = META_RTOL * np.maximum(np.abs(zb), sb) + 1.01 * a_lo
+        ok_s = (sa == sb) | (np.abs(sa - sb) <= tol_s)
+        ok_z = (za == zb) | (np.abs(za - zb) <= tol_z)
+        assert np.all(ok_s), ("scale", i, sa[~ok_s][:4], sb[~ok_s][:4], _meta_report(g, ref, i))
+        assert np.all(ok_z), ("zero", i, za[~ok_z][:4], zb[~ok_z][:4], _meta_report(g, ref, i))
+        # plain-bar exceedances: outside offset-dominated groups (where the float32 bound on y
+        # is a visible share of the range) each must come from a normalizer flip at its min /
+        # max elements
+        offset = np.abs(y_o).max(axis=ax) > OFFSET_DOMINATED * sb
+        plain_s = np.abs(sa - sb) > META_RTOL * np.abs(sb)
+        plain_z = np.abs(za - zb) > META_RTOL * np.maximum(np.abs(zb), sb)
+        flip = (g["r"][:, None] != ref["r"][i][:, None]) | (g["s"][None, :] != ref["s"][i][None, :])
+        f_lo = at(flip, lo_o) | at(flip, lo_g)
+        f_hi = at(flip, hi_o) | at(flip, hi_g)
+        assert not np.any(plain_z & ~f_lo & ~offset), ("zero beyond 1e-3 without a flip", i)
+        assert not np.any(plain_s & ~(f_lo | f_hi) & ~offset), ("scale beyond 1e-3 without a flip", i)
+        stats.meta_plain_over += int(plain_s.sum() + plain_z.sum())
+        stats.meta_plain_total += 256
+        stats.meta_exact += int(np.sum(g["scale"] == ref["scale"][i]) + np.sum(g["zero"] == ref["zero"][i]))
+        stats.meta_total += 256
+        stats.max_meta_rel = max(stats.max_meta_rel, float(np.max(np.where(sa == sb, 0, np.abs(sa - sb) / np.maximum(sb, 1e-30)))))
         # ---- L2: the oracle's rounding step applied to the GPU's own metadata
-        r, s = g["r"].astype(np.float64), g["s"].astype(np.float64)
-        y = ref["xr"][i] / (r[:, None] * s[None, :])
-        sc, zr = g["scale"].astype(np.float64), g["zero"].astype(np.float64)
-        if kind == O.KIND_K:
-            sc_b, zr_b = sc[:, None], zr[:, None]
-        else:
-            sc_b, zr_b = sc[None, :], zr[None, :]
-        live = (sc_b > 0) & np.isfinite(zr_b) & np.isfinite(sc_b)
+        sc_b, zr_b = grp(sa), grp(za)
+        live = sc_b > 0
         with np.errstate(invalid="ignore", over="ignore"):
-            u = np.where(live, (y - np.where(live, zr_b, 0.0)) / np.where(live, sc_b, 1.0), 0.0)
+            u = np.where(live, (y_g - np.where(live, zr_b, 0.0)) / np.where(live, sc_b, 1.0), 0.0)
         re = np.clip(np.rint(u), 0, qmax)
-        re = np.where(live, re, g["codes"])   # overflowed groups: compared at L3 only
+        re = np.where(live, re, 0)
         diff = re != g["codes"]
         if diff.any():
             frac = np.abs(u - np.floor(u) - 0.5)
             xscale = np.abs(x[i].astype(np.float64)).sum(axis=0)[None, :] / np.sqrt(128.0)
-            step = r[:, None] * s[None, :] * np.where(sc_b > 0, sc_b, np.inf)
+            step = r_g[:, None] * s_g[None, :] * np.where(sc_b > 0, sc_b, np.inf)
             band = TIE_BAND + 32 * 2.0 ** -24 * xscale / step
             near_tie = frac <= band
             outside = diff & ~near_tie
             stats.l2_mismatch += int(outside.sum())
             assert not outside.any(), (i, int(outside.sum()), u[outside][:5], g["codes"][outside][:5])
-        # ---- L3
-        if i in ill_conditioned:
-            continue
+        # ---- L3 outside offset-dominated groups; those get the reconstruction bound
+        stats.offset_groups += int(offset.sum())
+        keep = ~np.broadcast_to(grp(offset), (128, 128))
         d = g["codes"].astype(int) - ref["codes"][i].astype(int)
-        assert np.all(np.abs(d) <= 1), (i, int(np.abs(d).max()))
-        if i not in rate_exempt:
-            stats.l3_mismatch += int(np.count_nonzero(d))
-            stats.codes += d.size
+        assert np.all(np.abs(d[keep]) <= 1), (i, int(np.abs(d[keep]).max()))
+        stats.l3_mismatch += int(np.count_nonzero(d[keep]))
+        stats.codes += int(keep.sum())
+        if offset.any():
+            xf = x[i].astype(np.float64)
+            e_gpu = reconstruction_error(xf, g, kind)
+            e_ref = reconstruction_error(xf, {k_: ref[k_][i] for k_ in ("codes", "r", "s", "scale", "zero")}, kind)
+            assert e_gpu <= 1.05 * e_ref + 1e-6 * float(np.linalg.norm(xf)), (i, e_gpu, e_ref)
     return stats
 
 
-def _delta_group(x_ct: np.ndarray, r16: np.ndarray, s16: np.ndarray, kind: int) -> np.ndarray:
-    """Per group, the largest float32 evaluation bound on y = Xr / (r s) among its elements:
-    32 ulp of the token's |x|_1 / sqrt(128) (the rotated value's bound), over r_c s_t. Keys:
-    a group is a channel (max over tokens); values: a token (max over channels)."""
+def _delta(x_ct: np.ndarray, r16: np.ndarray, s16: np.ndarray) -> np.ndarray:
+    """Per element, the float32 evaluation bound on y = Xr / (r s): 32 ulp of the token's
+    |x|_1 / sqrt(128) (the rotated value's bound), over r_c s_t."""
     xs = np.abs(x_ct.astype(np.float64)).sum(axis=0) / np.sqrt(128.0)       # per token
     rs = r16.astype(np.float64)[:, None] * s16.astype(np.float64)[None, :]
     with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
         d = 32 * 2.0 ** -24 * xs[None, :] / rs
-    d = np.where(np.isfinite(d), d, 0.0)
-    return d.max(axis=1) if kind == O.KIND_K else d.max(axis=0)
-
-
-def _cascade(dev: dict, kind: int) -> np.ndarray:
-    """Per group: relative r, s difference (GPU vs oracle) its elements can see. Keys: a
-    group is a channel (its r, any token's s); values: a token (its s, any channel's r)."""
-    dr, ds = dev["r"], dev["s"]
-    return dr + ds.max() if kind == O.KIND_K else ds + dr.max()
+    return np.where(np.isfinite(d), d, 0.0)
 
 
 def _meta_report(g: dict, ref: dict, i: int) -> str:
@@ -186,8 +200,9 @@ def _meta_report(g: dict, ref: dict, i: int) -> str:
     return ", ".join(out)
 
 
-def assert_rate(stats: QuantStats):
+def assert_rate(stats: QuantStats, meta_plain_rate: float = META_PLAIN_RATE):
     assert stats.rate() <= CODE_MISMATCH_RATE, repr(stats)
+    assert stats.plain_rate() <= meta_plain_rate, repr(stats)
 
 
 def key_bits_of(k_pool) -> int:

@@ -42,41 +42,33 @@ def _written_cache(K, params, lens, lens_new, hkv, seed):
 
 
 def _reference_rows(q, cu_q, kp, vp, bt, kt, vt, sl, G, rows_to_check):
-    """Oracle attention of the given query rows over their causal prefix."""
+    """Oracle causal attention (O.causal_attention) of the given query rows: the cache of
+    sequence b in position order is its dequantized pages followed by the staged tokens of
+    its partial last tile; row cu_q[b] + i sits at position C - n + i."""
     qh = q.cpu().numpy()
     cu = cu_q.cpu().numpy()
     bt_h, sl_h = bt.cpu().numpy(), sl.cpu().numpy()
     kt_h, vt_h = kt.cpu().numpy(), vt.cpu().numpy()
     hkv = kp.shape[1]
-    deq = {}
+    cache = {}
     out = {}
     for r in rows_to_check:
         b = int(np.searchsorted(cu, r, side="right") - 1)
         C, n = int(sl_h[b]), int(cu[b + 1] - cu[b])
-        L = C - n + (r - int(cu[b])) + 1
+        pos = C - n + (r - int(cu[b]))
         for g in range(hkv):
-            if (b, g) not in deq:
+            if (b, g) not in cache:
                 pages = [int(p) for p in bt_h[b, :C // 128]]
-                ks = [O.dequantize_k_record(x, T.key_bits_of(kp))
-                      for x in T.records_of(kp, pages, g)] if pages else []
-                vs = [O.dequantize_v_record(x, T.value_bits_of(vp))
-                      for x in T.records_of(vp, pages, g)] if pages else []
-                deq[(b, g)] = (ks, vs)
-            ks, vs = deq[(b, g)]
-            nf, rem = L // 128, L % 128
-            k_parts, v_parts = ks[:nf], vs[:nf]
-            if rem:
-                if nf < len(ks):      # a completed page, cut by the causal limit
-                    k_parts = k_parts + [ks[nf][:rem]]
-                    v_parts = v_parts + [vs[nf][:rem]]
-                else:                 # the staging tile
-                    k_parts = k_parts + [kt_h[b, g, :rem].astype(np.float64)]
-                    v_parts = v_parts + [vt_h[b, g, :rem].astype(np.float64)]
-            kk = np.concatenate(k_parts, 0)
-            vv = np.concatenate(v_parts, 0)
-            for hh in range(G):
-                hq = g * G + hh
-                out[(r, hq)] = O.attention(qh[r, hq].astype(np.float64), kk, vv, SCALE)
+                ks = [O.dequantize_k_record(x, T.key_bits_of(kp)) for x in T.records_of(kp, pages, g)]
+                vs = [O.dequantize_v_record(x, T.value_bits_of(vp)) for x in T.records_of(vp, pages, g)]
+                ks.append(kt_h[b, g, :C % 128].astype(np.float64))
+                vs.append(vt_h[b, g, :C % 128].astype(np.float64))
+                cache[(b, g)] = (np.concatenate(ks, 0), np.concatenate(vs, 0))
+            kk, vv = cache[(b, g)]
+            hqs = [g * G + hh for hh in range(G)]
+            res = O.causal_attention(qh[r, hqs].astype(np.float64), [pos] * G, kk, vv, SCALE)
+            for hh, hq in enumerate(hqs):
+                out[(r, hq)] = res[hh]
     return out
 
 

@@ -65,7 +65,9 @@ def _check_sampled_tiles(w, kp, vp, n_iters, seed, n=N_TILES):
         recs = [sel[k].tobytes() for k in range(sel.shape[0])]
         st = T.check_quantized_tiles(tiles, recs, kind, n_iters)
         say(f"  kind={kind} {st}")
-        T.assert_rate(st)
+        # the workloads' data (no offset-dominated tiles): scales and zeros beyond the plain
+        # 1e-3 at most 2e-4 of them, within twice the L3 code rate
+        T.assert_rate(st, meta_plain_rate=2e-4)
 
 
 def _rows(rng, batch, hkv, n=N_KV_ROWS):
@@ -225,12 +227,14 @@ def test_chunked_prefill_full(K):
     worst = 0.0
     for _ in range(6):
         b, i, g = int(rng.integers(B)), int(rng.integers(n)), int(rng.integers(hkv))
-        L = ctx + i + 1                                   # causal prefix of chunk row i
-        pages = [int(p) for p in bt[b, :(L + 127) // 128]]
-        kk = np.concatenate([O.dequantize_k_record(r) for r in T.records_of(kp, pages, g)])[:L]
-        vv = np.concatenate([O.dequantize_v_record(r) for r in T.records_of(vp, pages, g)])[:L]
+        pages = [int(p) for p in bt[b, :(ctx + n) // 128]]     # the whole cache: full pages
+        kk = np.concatenate([O.dequantize_k_record(r) for r in T.records_of(kp, pages, g)])
+        vv = np.concatenate([O.dequantize_v_record(r) for r in T.records_of(vp, pages, g)])
         r = b * n + i
+        # chunk row i sits at position ctx + i and attends causally (oracle causal rows)
+        wants = O.causal_attention(qh[r, g * G:(g + 1) * G].astype(np.float64), [ctx + i] * G,
+                                   kk, vv, 1.0 / np.sqrt(128.0))
         for hh in range(G):
-            want = O.attention(qh[r, g * G + hh].astype(np.float64), kk, vv, 1.0 / np.sqrt(128.0))
+            want = wants[hh]
             worst = max(worst, T.assert_rows_close(o[r, g * G + hh], want, f"row {r} head {g * G + hh}"))
     say(f"  6 (row, KV head) samples x {G} heads: max rel err {worst:.2e}")

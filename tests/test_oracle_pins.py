@@ -453,3 +453,88 @@ def test_population_std_is_exactly_zero_for_identical_values():
     assert np.all(O.population_std(y.T, axis=-2) == 0.0)
     z = RNG.standard_normal((128, 128))
     assert np.allclose(O.population_std(z, axis=-1), np.sqrt(np.mean((z - z.mean(-1, keepdims=True)) ** 2, -1)), rtol=1e-13)
+
+
+# ----------------------------------------------------------------------------- rounding, clips
+
+
+def test_rtn_rounds_half_to_even():
+    """Values exactly on half-levels (scale 1, zero 0 exactly representable) round to the even
+    code: 0.5 -> 0, 1.5 -> 2, 2.5 -> 2, ... (round-half-even; half-up would give 1, 2, 3 ...)."""
+    half = np.arange(15) + 0.5
+    row = np.concatenate([[0.0, 15.0], half, np.full(128 - 17, 7.0)])
+    y = np.tile(row, (128, 1))                       # key groups = rows
+    codes, sc, zr, u = O.rtn_asym(y, 4, axis=-1)
+    assert np.all(sc == 1.0) and np.all(zr == 0.0)
+    assert np.array_equal(u[0, 2:17], half)          # exact ties
+    assert codes[0, 2:17].tolist() == [0, 2, 2, 4, 4, 6, 6, 8, 8, 10, 10, 12, 12, 14, 14]
+    # 2-bit value groups (columns): scale 1 with the range [0, 3]
+    col = np.concatenate([[0.0, 3.0, 0.5, 1.5, 2.5], np.full(123, 1.0)])
+    codes, sc, zr, _ = O.rtn_asym(np.tile(col[:, None], (1, 128)), 2, axis=-2)
+    assert np.all(sc == 1.0) and codes[2:5, 0].tolist() == [0, 2, 2]
+
+
+def test_store_normalizer_clip_bounds():
+    """Normalizers are clipped to the float16 normal range [2^-14, 65504], then rounded."""
+    v = np.array([1e-9, 2.0 ** -14, 2.0 ** -14 * 0.75, 3.0, 65504.0, 65519.0, 1e6, 1e30])
+    got = O.store_normalizer(np.log(v)).astype(np.float64)
+    assert got.tolist() == [2.0 ** -14, 2.0 ** -14, 2.0 ** -14, 3.0, 65504.0, 65504.0, 65504.0,
+                            65504.0]
+    # driven past the lower bound by a real tile: tiny values leave every token std below
+    # 2^-14, so s is stored at the bound and the codes still cover each group's range
+    x = (RNG.standard_normal((128, 128)) * 2.0 ** -20).astype(np.float16)
+    for kind in (O.KIND_K, O.KIND_V):
+        out = O.quantize_tiles(x, kind, 8)
+        assert np.all(out["s"] == np.float16(2.0 ** -14))
+        axis = -1 if kind == O.KIND_K else -2
+        assert np.all(out["codes"].max(axis=axis) == (15 if kind == O.KIND_K else 3))
+
+
+def test_store_meta_saturates():
+    """Scales and zeros round to float16 nearest-even and saturate to +-65504 (no inf)."""
+    v = np.array([-1e9, -65520.0, -65504.0, -0.1, 0.0, 1.0 / 3, 65519.0, 65520.0, 2e5])
+    got = O.store_meta(v).astype(np.float64)
+    assert got.tolist() == [-65504.0, -65504.0, -65504.0, float(np.float16(-0.1)), 0.0,
+                            float(np.float16(1.0 / 3)), 65504.0, 65504.0, 65504.0]
+
+
+def test_overflowing_group_gives_finite_record_and_decode():
+    """A near-constant tile (5 + 1e-3 noise) at one iteration: the rotated DC channel's
+    normalized values reach ~1.9e5, beyond float16. Its zero saturates to 65504 and its codes
+    clip at 15, so the record stays finite and a decode over it returns finite output."""
+    rng = np.random.default_rng(7)
+    x = (5 + 1e-3 * rng.standard_normal((128, 128))).astype(np.float16)
+    out = O.quantize_tiles(x, O.KIND_K, 1)
+    assert np.abs(out["y"]).max() > 65504
+    for key in ("r", "s", "scale", "zero"):
+        assert np.all(np.isfinite(out[key].astype(np.float64)))
+    assert out["zero"][0] == np.float16(65504) and np.all(out["codes"][0] == 15)
+    rec_k = O.pack_k_record(out["codes"], out["r"], out["s"], out["scale"], out["zero"])
+    vo = O.quantize_tiles(x, O.KIND_V, 1)
+    rec_v = O.pack_v_record(vo["codes"], vo["r"], vo["s"], vo["scale"], vo["zero"])
+    o = O.decode_attention_row(rng.standard_normal(128).astype(np.float16), [rec_k], [rec_v])
+    assert np.all(np.isfinite(o))
+
+
+def test_causal_attention_matches_sdpa():
+    """Causal rows against torch's scaled_dot_product_attention (float64) with a causal mask
+    over the last n positions of the cache; a row before the cache start is zeros."""
+    C, n = 300, 40
+    q = RNG.standard_normal((n, 128))
+    k = RNG.standard_normal((C, 128))
+    v = RNG.standard_normal((C, 128))
+    sm = 1 / np.sqrt(128)
+    pos = np.arange(C - n, C)
+    got = O.causal_attention(q, pos, k, v, sm)
+    mask = torch.tensor(np.arange(C)[None, :] <= pos[:, None])
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.tensor(q)[None, None], torch.tensor(k)[None, None], torch.tensor(v)[None, None],
+        attn_mask=mask[None, None], scale=sm)[0, 0].numpy()
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-13)
+    # square causal case (the chunk is the whole cache)
+    got = O.causal_attention(q, np.arange(n), k[:n], v[:n], sm)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.tensor(q)[None, None], torch.tensor(k[:n])[None, None], torch.tensor(v[:n])[None, None],
+        is_causal=True, scale=sm)[0, 0].numpy()
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-13)
+    assert np.all(O.causal_attention(q[:2], [-1, -5], k, v, sm) == 0)

@@ -157,7 +157,8 @@ def rtn_asym(y: np.ndarray, bits: int, axis: int):
 
 
 def quantize_tiles(x16: np.ndarray, kind: int, n_iters: int = 8, lossless: bool = False,
-                   rotate_channels: bool = True, k_bits: int = 4, v_bits: int = 2):
+                   rotate_channels: bool = True, k_bits: int = 4, v_bits: int = 2,
+                   fmt: int = 1):
     """Quantize tiles end to end (stages 1-4 of [README] "How KVarN works").
 
     x16: [..., 128 channels, 128 tokens] float16 (stage 1: the raw tile, channels x tokens).
@@ -173,6 +174,12 @@ def quantize_tiles(x16: np.ndarray, kind: int, n_iters: int = 8, lossless: bool 
     rotate_channels=False skips stage 2 (Xr = X): an ablation of the method, not the method.
     k_bits, v_bits: code widths of the preset (kvarn_k4v2_g128: 4, 2; kvarn_k2v2_g128: 2, 2;
     kvarn_k4v4_g128: 4, 4).
+    fmt=2 is the folded record format: each group's own normalizer is folded into its scale
+    and zero, so the round-to-nearest runs on Z = Xr / s (keys, groups = channels) or
+    Z = Xr / r (values, groups = tokens) and the record stores only the other normalizer.
+    Its dict then reports the folded-away normalizer as 1 (r for keys, s for values), 'scale'
+    and 'zero' as the folded values and 'y' as Z, so that r s (zero + scale code) is still the
+    reconstruction of Xr.
     """
     x = np.asarray(x16, dtype=np.float16).astype(np.float64)
     if x.shape[-2:] != (HEAD_DIM, TILE_TOKENS):
@@ -185,12 +192,23 @@ def quantize_tiles(x16: np.ndarray, kind: int, n_iters: int = 8, lossless: bool 
     out = dict(r=r16, s=s16, xr=xr, y=y)
     if lossless:
         return out
+    if kind not in (KIND_K, KIND_V):
+        raise ValueError("kind must be KIND_K or KIND_V")
+    if fmt == 2:
+        # fold the group's normalizer: keys code Xr / s per channel, values Xr / r per token
+        one = np.ones_like(r16)
+        if kind == KIND_K:
+            y = xr / s16.astype(np.float64)[..., None, :]
+            out.update(r=one, y=y)
+        else:
+            y = xr / r16.astype(np.float64)[..., :, None]
+            out.update(s=np.ones_like(s16), y=y)
+    elif fmt != 1:
+        raise ValueError("fmt must be 1 or 2")
     if kind == KIND_K:
         codes, scale16, zero16, u = rtn_asym(y, k_bits, axis=-1)
-    elif kind == KIND_V:
-        codes, scale16, zero16, u = rtn_asym(y, v_bits, axis=-2)
     else:
-        raise ValueError("kind must be KIND_K or KIND_V")
+        codes, scale16, zero16, u = rtn_asym(y, v_bits, axis=-2)
     out.update(codes=codes, scale=scale16, zero=zero16, u=u)
     return out
 
@@ -271,6 +289,37 @@ def v4_nibble_token(g: int, m: int, q: int) -> int:
 def _meta_bytes(r16, s16, scale16, zero16) -> bytes:
     parts = [np.asarray(v, dtype="<f2").reshape(128) for v in (r16, s16, scale16, zero16)]
     return b"".join(p.tobytes() for p in parts)
+
+
+# Format 2 (folded) of the same records: the code bytes, then three float16[128] vectors:
+# keys s, scale', zero' (per channel, of Z = Xr / s); values r, scale', zero' (per token, of
+# Z = Xr / r). The record is 256 bytes shorter.
+META_BYTES = {1: 1024, 2: 768}
+
+
+def code_bytes(kind: int, k_bits: int = 4, v_bits: int = 2) -> int:
+    bits = k_bits if kind == KIND_K else v_bits
+    return 8192 if bits == 4 else 4096
+
+
+def record_bytes(kind: int, k_bits: int = 4, v_bits: int = 2, fmt: int = 1) -> int:
+    return code_bytes(kind, k_bits, v_bits) + META_BYTES[fmt]
+
+
+def record_layout(nbytes: int):
+    """(code bits, format) of a record from its size: 9216 / 5120 bytes are format 1 with 4 /
+    2-bit codes, 8960 / 4864 format 2."""
+    return {9216: (4, 1), 5120: (2, 1), 8960: (4, 2), 4864: (2, 2)}[nbytes]
+
+
+def fold_record(rec1: bytes, kind: int) -> bytes:
+    """Format-2 layout of a format-1 record whose folded-away normalizer is exactly 1 (the
+    byte arrangement only: codes kept, the all-ones vector dropped)."""
+    cb = len(rec1) - 1024
+    m = np.frombuffer(rec1[cb:], dtype="<f2").reshape(4, 128)
+    keep = (1, 2, 3) if kind == KIND_K else (0, 2, 3)
+    assert np.all(m[0 if kind == KIND_K else 1] == 1.0)
+    return rec1[:cb] + b"".join(m[k].tobytes() for k in keep)
 
 
 def pack_k_record(codes, r16, s16, scale16, zero16) -> bytes:
@@ -372,20 +421,36 @@ def unpack_v4_record(rec) -> dict:
     return dict(codes=codes, r=r, s=s, scale=sc, zero=zr)
 
 
-def unpack_record(rec, kind: int, k_bits: int = 4, v_bits: int = 2) -> dict:
-    """The record of `kind` for the preset with k_bits-bit keys and v_bits-bit values."""
+def unpack_record(rec, kind: int, k_bits: int = 4, v_bits: int = 2, fmt: int = 1) -> dict:
+    """The record of `kind` for the preset with k_bits-bit keys and v_bits-bit values, in
+    record format fmt (format 2 reports the folded-away normalizer as ones)."""
+    rec = bytes(rec)
+    if fmt == 2:
+        cb = code_bytes(kind, k_bits, v_bits)
+        assert len(rec) == cb + META_BYTES[2]
+        m = np.frombuffer(rec[cb:], dtype="<f2").reshape(3, 128)
+        one = np.ones(128, dtype=np.float16)
+        r16, s16 = (one, m[0]) if kind == KIND_K else (m[0], one)
+        rec = rec[:cb] + _meta_bytes(r16, s16, m[1], m[2])
     if kind == KIND_V:
         return unpack_v_record(rec) if v_bits == 2 else unpack_v4_record(rec)
     return unpack_k_record(rec) if k_bits == 4 else unpack_k2_record(rec)
 
 
 def pack_record(kind: int, codes, r16, s16, scale16, zero16, k_bits: int = 4,
-                v_bits: int = 2) -> bytes:
+                v_bits: int = 2, fmt: int = 1) -> bytes:
     if kind == KIND_V:
         pack = pack_v_record if v_bits == 2 else pack_v4_record
     else:
         pack = pack_k_record if k_bits == 4 else pack_k2_record
-    return pack(codes, r16, s16, scale16, zero16)
+    if fmt == 1:
+        return pack(codes, r16, s16, scale16, zero16)
+    if fmt != 2:
+        raise ValueError("fmt must be 1 or 2")
+    one = np.ones(128, dtype=np.float16)
+    rec1 = pack(codes, one if kind == KIND_K else r16, s16 if kind == KIND_K else one,
+                scale16, zero16)
+    return fold_record(rec1, kind)
 
 
 def unpack_v_record(rec) -> dict:
@@ -416,20 +481,20 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, softmax_scale: float)
     return (p / p.sum()) @ np.asarray(v, np.float64)
 
 
-def dequantize_k_record(rec, k_bits: int = 4) -> np.ndarray:
+def dequantize_k_record(rec, k_bits: int = 4, fmt: int = 1) -> np.ndarray:
     """Unpack one K page record and return the dequantized keys [128 tokens, 128 channels]."""
-    d = unpack_k_record(rec) if k_bits == 4 else unpack_k2_record(rec)
+    d = unpack_record(rec, KIND_K, k_bits=k_bits, fmt=fmt)
     return dequantize_tiles(d["codes"], d["r"], d["s"], d["scale"], d["zero"], KIND_K).T
 
 
-def dequantize_v_record(rec, v_bits: int = 2) -> np.ndarray:
-    d = unpack_v_record(rec) if v_bits == 2 else unpack_v4_record(rec)
+def dequantize_v_record(rec, v_bits: int = 2, fmt: int = 1) -> np.ndarray:
+    d = unpack_record(rec, KIND_V, v_bits=v_bits, fmt=fmt)
     return dequantize_tiles(d["codes"], d["r"], d["s"], d["scale"], d["zero"], KIND_V).T
 
 
 def decode_attention_row(q_row, k_pages, v_pages, k_tail=None, v_tail=None,
                          softmax_scale: float = 1.0 / np.sqrt(HEAD_DIM), k_bits: int = 4,
-                         v_bits: int = 2) -> np.ndarray:
+                         v_bits: int = 2, fmt: int = 1) -> np.ndarray:
     """Decode attention of one query row over one KV head's cache.
 
     k_pages / v_pages: lists of page records (bytes) of that KV head, in block-table order
@@ -438,8 +503,8 @@ def decode_attention_row(q_row, k_pages, v_pages, k_tail=None, v_tail=None,
     k_tail / v_tail: [n_tail, 128] float16 tokens past the last full page (raw, exact).
     Returns float64 [128].
     """
-    ks = [dequantize_k_record(p, k_bits) for p in k_pages]
-    vs = [dequantize_v_record(p, v_bits) for p in v_pages]
+    ks = [dequantize_k_record(p, k_bits, fmt) for p in k_pages]
+    vs = [dequantize_v_record(p, v_bits, fmt) for p in v_pages]
     if k_tail is not None and len(k_tail):
         ks.append(np.asarray(k_tail, np.float16).astype(np.float64))
         vs.append(np.asarray(v_tail, np.float16).astype(np.float64))

@@ -538,3 +538,61 @@ def test_causal_attention_matches_sdpa():
         is_causal=True, scale=sm)[0, 0].numpy()
     assert np.allclose(got, ref, rtol=1e-12, atol=1e-13)
     assert np.all(O.causal_attention(q[:2], [-1, -5], k, v, sm) == 0)
+
+
+# ----------------------------------------------------------------------------- folded format
+
+
+def test_folded_format_byte_patterns():
+    """Format 2 metadata offsets and byte values, derived by hand (tests/golden)."""
+    g = json.load(open(os.path.join(GOLD, "format_folded_patterns.json")))
+    for case in g["cases"]:
+        kind, kb, vb = case["kind"], case["k_bits"], case["v_bits"]
+        bits = kb if kind == O.KIND_K else vb
+        vec = {k: np.full(128, v, dtype=np.float16) for k, v in case["fill"].items()}
+        for k, (i, v) in case["set"].items():
+            vec[k][i] = v
+        one = np.ones(128, dtype=np.float16)
+        r16, s16 = (one, vec["first"]) if kind == O.KIND_K else (vec["first"], one)
+        rec = O.pack_record(kind, np.zeros((128, 128), np.uint8), r16, s16, vec["scale"],
+                            vec["zero"], kb, vb, fmt=2)
+        assert len(rec) == case["record_bytes"] == O.record_bytes(kind, kb, vb, 2)
+        assert O.record_layout(len(rec)) == (bits, 2)
+        for off, lo, hi in case["bytes"]:
+            assert (rec[off], rec[off + 1]) == (lo, hi), (case["kind"], off)
+
+
+@pytest.mark.parametrize("kind,kb,vb", [(O.KIND_K, 4, 2), (O.KIND_V, 4, 2), (O.KIND_K, 2, 2),
+                                        (O.KIND_V, 4, 4)])
+def test_folded_format_roundtrip_and_fold_identity(kind, kb, vb):
+    """Format 2 packs and unpacks losslessly (the folded-away normalizer reads back as 1), and
+    folding changes the codes only at rounding ties: asymmetric round-to-nearest is invariant
+    to a positive factor per group, so the folded codes equal the separate-format codes up
+    to the float16 rounding of the folded scale and zero, and both reconstruct the tile with
+    the same accuracy."""
+    x = (RNG.standard_t(4, (8, 128, 128)) * RNG.lognormal(0, 1, (8, 128, 1))).astype(np.float16)
+    a = O.quantize_tiles(x, kind, 8, k_bits=kb, v_bits=vb, fmt=1)
+    b = O.quantize_tiles(x, kind, 8, k_bits=kb, v_bits=vb, fmt=2)
+    gone = "r" if kind == O.KIND_K else "s"
+    kept = "s" if kind == O.KIND_K else "r"
+    assert np.all(b[gone] == 1) and np.array_equal(b[kept], a[kept])
+    for i in range(x.shape[0]):
+        rec = O.pack_record(kind, b["codes"][i], b["r"][i], b["s"][i], b["scale"][i],
+                            b["zero"][i], kb, vb, fmt=2)
+        d = O.unpack_record(rec, kind, kb, vb, fmt=2)
+        for key in ("codes", "r", "s", "scale", "zero"):
+            assert np.array_equal(d[key], b[key][i]), key
+    diff = b["codes"].astype(int) - a["codes"].astype(int)
+    assert np.abs(diff).max() <= 1 and np.count_nonzero(diff) <= 0.03 * diff.size
+    # the differing codes sit at ties of the separate format: folded and separate scale and
+    # zero differ by their float16 roundings (relative 2^-10 each), which moves the unrounded
+    # code by at most 2^-10 (u + |zero| / scale)
+    frac = np.abs(a["u"] - np.floor(a["u"]) - 0.5)
+    grp = (lambda v: v[..., :, None]) if kind == O.KIND_K else (lambda v: v[..., None, :])
+    with np.errstate(divide="ignore", invalid="ignore"):
+        zs = np.abs(grp(a["zero"].astype(float))) / grp(a["scale"].astype(float))
+    bound = 2.0 ** -10 * (np.abs(a["u"]) + np.broadcast_to(zs, a["u"].shape) + 1)
+    assert np.all(frac[diff != 0] <= bound[diff != 0])
+    ea = np.linalg.norm(O.dequantize_tiles(a["codes"], a["r"], a["s"], a["scale"], a["zero"], kind) - x)
+    eb = np.linalg.norm(O.dequantize_tiles(b["codes"], b["r"], b["s"], b["scale"], b["zero"], kind) - x)
+    assert abs(eb - ea) <= 0.02 * ea

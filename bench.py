@@ -446,7 +446,7 @@ def quantize_and_decode(args, K, synth, params, dev, probe):
         if n == n_iters:
             t = q_ms
         else:
-            p_n = K.params_from_dtype(args.preset, n)
+            p_n = K.params_from_dtype(args.preset, n, format=params.format)
             f = K.prepare_quantize_kv(p_n, w0.k_src, w0.v_src, w0.tile_src_token,
                                       w0.tile_dst_page, calls[0][2], calls[0][3])
             (ts,), _ = evented_steps(lambda s: [f], 4, 0)
@@ -501,7 +501,8 @@ def quantize_and_decode(args, K, synth, params, dev, probe):
         "data": "synthetic",
         "config": {"workload": wl, "batch": B, "num_q_heads": hq, "num_kv_heads": hkv,
                    "head_dim": 128, "context": T, "kv_cache_dtype": args.preset,
-                   "sinkhorn_iters": n_iters, "page_pool_copies": L,
+                   "sinkhorn_iters": n_iters, "record_format": params.format,
+                   "page_pool_copies": L,
                    "parallelism": "single GPU"},
         "timing": "ms_per_step over the timed steps with nothing recorded between launches; "
                   "launch_ms and the percentiles (mean/p10/p50/p90 over the steps) from the same "
@@ -725,7 +726,8 @@ def decode_steps(args, K, synth, params, dev, probe, workload=None, steps=None, 
         "config": {"workload": f"{workload}: append 1 token per sequence + 1 decode step",
                    "batch": B, "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": 128,
                    "prompt_tokens": sum(w0.prompt_lens), "kv_cache_dtype": args.preset,
-                   "sinkhorn_iters": params.sinkhorn_iters, "copies_cycled": L,
+                   "sinkhorn_iters": params.sinkhorn_iters, "record_format": params.format,
+                   "copies_cycled": L,
                    "parallelism": "single GPU"},
         "timing": "ms_per_step over the timed steps with nothing recorded between launches; "
                   "append_ms / decode_ms and percentiles from the same steps run again with HIP "
@@ -1017,6 +1019,9 @@ def main():
     ap.add_argument("--preset", default="kvarn_k4v2_g128",
                     choices=["kvarn_k4v2_g128", "kvarn_k2v2_g128", "kvarn_k4v4_g128"],
                     help="kv_cache_dtype preset (the released k4v2_g128 by default)")
+    ap.add_argument("--format", type=int, default=1, choices=[1, 2],
+                    help="page record format: 1 separate normalizers and scales (default), "
+                         "2 folded (each group's normalizer folded into its scale and zero)")
     ap.add_argument("--context", type=int, default=16384)
     ap.add_argument("--workload", choices=WORKLOADS, default="prefill_burst",
                     help="prefill_burst (default, the headline line): 64 sequences x 16384 "
@@ -1059,7 +1064,7 @@ def main():
     from kv_cache_quantization_tile_amd import synth
 
     dev = torch.device("cuda:0")
-    params = K.params_from_dtype(args.preset, args.sinkhorn_iters)
+    params = K.params_from_dtype(args.preset, args.sinkhorn_iters, format=args.format)
     probe = hbm_read_probe(dev)
     print(f"[bench] read probe {probe['gbps_median']} GB/s", file=sys.stderr, flush=True)
     valu = valu_calibration(dev)

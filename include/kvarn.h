@@ -46,8 +46,11 @@ extern "C" {
 #define KVARN_API
 #endif
 
-#define KVARN_ABI_VERSION 1
-#define KVARN_FORMAT_VERSION 1
+#define KVARN_ABI_VERSION 2
+/* Page record formats (kvarn_params.format): */
+#define KVARN_FORMAT_SEPARATE 1 /* normalizers and group scale / zero stored apart      */
+#define KVARN_FORMAT_FOLDED 2   /* each group's normalizer folded into its scale / zero */
+#define KVARN_FORMAT_VERSION KVARN_FORMAT_FOLDED   /* highest format this library reads  */
 
 typedef enum {
     KVARN_OK = 0,
@@ -62,7 +65,10 @@ typedef enum { KVARN_K = 0, KVARN_V = 1 } kvarn_kind;
 /* Quantizer parameters. Only head_dim = tile_tokens = group = 128 with (k_bits, v_bits)
  * = (4, 2), (2, 2) or (4, 4) are implemented (README "Quick start": other page sizes are
  * not yet supported). sinkhorn_iters is the number of (column step, row step) pairs of the
- * normalization (README "How KVarN works", stage 3); 0..64 accepted. */
+ * normalization (README "How KVarN works", stage 3); 0..64 accepted. format selects the page
+ * record layout (KVARN_FORMAT_SEPARATE or KVARN_FORMAT_FOLDED, see kvarn_page_bytes);
+ * kvarn_params_from_dtype sets KVARN_FORMAT_SEPARATE, anything else is INVALID_ARG. Every
+ * call that reads or writes records must use the params the pool was written with. */
 typedef struct {
     int32_t head_dim;
     int32_t tile_tokens;
@@ -70,6 +76,7 @@ typedef struct {
     int32_t v_bits;
     int32_t group;
     int32_t sinkhorn_iters;
+    int32_t format;
 } kvarn_params;
 
 /* Library ABI version (KVARN_ABI_VERSION) and page-format version. */
@@ -90,11 +97,12 @@ KVARN_API kvarn_status kvarn_params_from_dtype(const char* kv_cache_dtype, int32
 /* Check a params struct: OK, INVALID_ARG (NULL / out of range) or UNSUPPORTED. */
 KVARN_API kvarn_status kvarn_params_check(const kvarn_params* params);
 
-/* Bytes of one page record (one 128-token tile of one KV head) of the given kind:
- * 9216 for 4-bit keys or values, 5120 for 2-bit keys or values; 0 if params are invalid or
- * unsupported. Every pool passed with these params must use this record size.
+/* Bytes of one page record (one 128-token tile of one KV head) of the given kind: format
+ * KVARN_FORMAT_SEPARATE 9216 for 4-bit keys or values, 5120 for 2-bit ones; format
+ * KVARN_FORMAT_FOLDED 8960 and 4864; 0 if params are invalid or unsupported. Every pool
+ * passed with these params must use this record size.
  *
- * Page format v1 (little-endian):
+ * Page format 1, KVARN_FORMAT_SEPARATE (little-endian):
  *   K record: bytes [0, 8192) are 4-bit codes, token-major: token t owns bytes
  *     [64t, 64t+64) as 16 32-bit words; word j holds channels 8j..8j+7 with nibble p
  *     (bits 4p..4p+3) holding channel 8j + {0,2,4,6,1,3,5,7}[p].
@@ -115,7 +123,17 @@ KVARN_API kvarn_status kvarn_params_check(const kvarn_params* params);
  *   A tile X (channels x tokens, rotated Xr = H X) is recovered as
  *     Xr[c][t] = r[c] * s[t] * (zero[g] + scale[g] * code[c][t]),  X = H Xr,
  *   with g = c for K and g = t for V, H the normalized natural-order Sylvester
- *   Hadamard matrix (symmetric, its own inverse). */
+ *   Hadamard matrix (symmetric, its own inverse).
+ *
+ * Page format 2, KVARN_FORMAT_FOLDED: the same code bytes, then three float16[128] vectors.
+ * The group's own normalizer is folded into its scale and zero point, which are taken of
+ * the tile divided by the other normalizer only (the asymmetric round-to-nearest of README
+ * "How KVarN works" stage 4 is invariant to a positive factor per group):
+ *   K record: s (per token), scale'[c], zero'[c] of Z = Xr / s per channel, so
+ *     Xr[c][t] = s[t] * (zero'[c] + scale'[c] * code[c][t]);
+ *   V record: r (per channel), scale'[t], zero'[t] of Z = Xr / r per token, so
+ *     Xr[c][t] = r[c] * (zero'[t] + scale'[t] * code[c][t]).
+ * 256 B fewer per record (3.6% of a k4v2 page pair). */
 KVARN_API size_t kvarn_page_bytes(const kvarn_params* params, kvarn_kind kind);
 
 /* Quantize tiles into a page pool (README "How KVarN works", stages 1-4).

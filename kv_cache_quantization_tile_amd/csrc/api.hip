@@ -52,6 +52,8 @@ kvarn_status kvarn_params_check(const kvarn_params* p) {
   if (p->head_dim <= 0 || p->tile_tokens <= 0 || p->group <= 0 || p->k_bits <= 0 ||
       p->v_bits <= 0 || p->sinkhorn_iters < 0 || p->sinkhorn_iters > kMaxIters)
     return KVARN_ERR_INVALID_ARG;
+  if (p->format != KVARN_FORMAT_SEPARATE && p->format != KVARN_FORMAT_FOLDED)
+    return KVARN_ERR_INVALID_ARG;
   // presets kvarn_k4v2_g128 (released), kvarn_k2v2_g128 and kvarn_k4v4_g128
   const bool preset = (p->k_bits == 4 && p->v_bits == 2) || (p->k_bits == 2 && p->v_bits == 2) ||
                       (p->k_bits == 4 && p->v_bits == 4);
@@ -80,6 +82,7 @@ kvarn_status kvarn_params_from_dtype(const char* dtype, int32_t sinkhorn_iters, 
   p.v_bits = vb;
   p.group = grp;
   p.sinkhorn_iters = sinkhorn_iters;
+  p.format = KVARN_FORMAT_SEPARATE;
   if (kb == 0 || vb == 0 || grp == 0) return KVARN_ERR_INVALID_ARG;
   const kvarn_status st = kvarn_params_check(&p);
   if (st != KVARN_OK) return st;
@@ -89,8 +92,10 @@ kvarn_status kvarn_params_from_dtype(const char* dtype, int32_t sinkhorn_iters, 
 
 size_t kvarn_page_bytes(const kvarn_params* p, kvarn_kind kind) {
   if (kvarn_params_check(p) != KVARN_OK) return 0;
-  if (kind == KVARN_K) return p->k_bits == 4 ? 9216 : 5120;
-  if (kind == KVARN_V) return p->v_bits == 4 ? 9216 : 5120;
+  // codes, then 4 (separate) or 3 (folded) float16 vectors of 128
+  const size_t meta = p->format == KVARN_FORMAT_SEPARATE ? 1024 : 768;
+  if (kind == KVARN_K) return (p->k_bits == 4 ? 8192 : 4096) + meta;
+  if (kind == KVARN_V) return (p->v_bits == 4 ? 8192 : 4096) + meta;
   return 0;
 }
 
@@ -112,7 +117,7 @@ kvarn_status kvarn_quantize_tiles(const kvarn_params* params, kvarn_kind kind, c
       (src_head_stride % 8) != 0)
     return KVARN_ERR_INVALID_ARG;
   return launch_status(kvarn::launch_quantize_tiles(
-      int(kind), params->k_bits, params->v_bits, src, src_token_stride, src_head_stride, src_num_tokens, tile_src_token,
+      int(kind), params->k_bits, params->v_bits, params->format, src, src_token_stride, src_head_stride, src_num_tokens, tile_src_token,
       tile_dst_page, n_tiles, num_kv_heads, pool, pool_num_pages, params->sinkhorn_iters,
       static_cast<hipStream_t>(stream)));
 }
@@ -135,7 +140,7 @@ kvarn_status kvarn_quantize_kv_tiles(const kvarn_params* params, const void* k_s
       (src_token_stride % 8) != 0 || (src_head_stride % 8) != 0)
     return KVARN_ERR_INVALID_ARG;
   return launch_status(kvarn::launch_quantize_kv(
-      params->k_bits, params->v_bits,
+      params->k_bits, params->v_bits, params->format,
       k_src, v_src, src_token_stride, src_head_stride, src_num_tokens, tile_src_token,
       tile_dst_page, n_tiles, num_kv_heads, k_pool, v_pool, pool_num_pages,
       params->sinkhorn_iters, static_cast<hipStream_t>(stream)));
@@ -152,7 +157,7 @@ kvarn_status kvarn_dequantize_tiles(const kvarn_params* params, kvarn_kind kind,
   if (n_tiles == 0) return KVARN_OK;
   if (!pool || !pages || !dst) return KVARN_ERR_INVALID_ARG;
   if (!aligned16(pool) || !aligned16(dst)) return KVARN_ERR_INVALID_ARG;
-  return launch_status(kvarn::launch_dequantize_tiles(int(kind), params->k_bits, params->v_bits, pool, pool_num_pages, pages,
+  return launch_status(kvarn::launch_dequantize_tiles(int(kind), params->k_bits, params->v_bits, params->format, pool, pool_num_pages, pages,
                                                       n_tiles, num_kv_heads, dst,
                                                       static_cast<hipStream_t>(stream)));
 }
@@ -174,7 +179,7 @@ kvarn_status kvarn_append_tokens(const kvarn_params* params, const void* k_new, 
       !aligned16(k_pool) || !aligned16(v_pool))
     return KVARN_ERR_INVALID_ARG;
   return launch_status(kvarn::launch_append_tokens(
-      params->k_bits, params->v_bits,
+      params->k_bits, params->v_bits, params->format,
       k_new, v_new, batch, num_kv_heads, seq_lens, k_tail, v_tail, block_table,
       block_table_stride, k_pool, v_pool, pool_num_pages, params->sinkhorn_iters,
       static_cast<hipStream_t>(stream)));
@@ -201,7 +206,7 @@ kvarn_status kvarn_write_tokens(const kvarn_params* params, const void* k_new, c
       !aligned16(k_pool) || !aligned16(v_pool))
     return KVARN_ERR_INVALID_ARG;
   return launch_status(kvarn::launch_write_tokens(
-      params->k_bits, params->v_bits,
+      params->k_bits, params->v_bits, params->format,
       k_new, v_new, total_new_tokens, cu_new, max_new_tokens, batch, num_kv_heads, seq_lens, k_tail, v_tail,
       block_table, block_table_stride, k_pool, v_pool, pool_num_pages, params->sinkhorn_iters,
       static_cast<hipStream_t>(stream)));
@@ -292,7 +297,7 @@ kvarn_status kvarn_decode_attention(const kvarn_params* params, const void* q, i
   if (workspace_bytes < kvarn::decode_workspace_bytes(batch, num_q_heads, num_kv_heads, max_seq_len))
     return KVARN_ERR_WORKSPACE;
   return launch_status(kvarn::launch_decode(
-      params->k_bits, params->v_bits, q, batch, num_q_heads, num_kv_heads, k_pool, v_pool, pool_num_pages, block_table,
+      params->k_bits, params->v_bits, params->format, q, batch, num_q_heads, num_kv_heads, k_pool, v_pool, pool_num_pages, block_table,
       block_table_stride, seq_lens, max_seq_len, nullptr, batch, k_tail, v_tail, softmax_scale,
       workspace, out, static_cast<hipStream_t>(stream)));
 }
@@ -327,7 +332,7 @@ kvarn_status kvarn_decode_attention_noalloc(const kvarn_params* params, const vo
   void* ws = nullptr;
   if (kvarn::decode_scratch(&ws) != hipSuccess) return KVARN_ERR_HIP;
   return launch_status(kvarn::launch_decode(
-      params->k_bits, params->v_bits, q, batch, num_q_heads, num_kv_heads, k_pool, v_pool,
+      params->k_bits, params->v_bits, params->format, q, batch, num_q_heads, num_kv_heads, k_pool, v_pool,
       pool_num_pages, block_table, block_table_stride, seq_lens, max_seq_len, nullptr, batch,
       k_tail, v_tail, softmax_scale, ws, out, s));
 }
@@ -365,7 +370,7 @@ kvarn_status kvarn_chunk_attention(const kvarn_params* params, const void* q, in
   if (workspace_bytes < kvarn::chunk_workspace_bytes(total_q, num_q_heads, num_kv_heads, max_seq_len))
     return KVARN_ERR_WORKSPACE;
   return launch_status(kvarn::launch_decode(
-      params->k_bits, params->v_bits, q, total_q, num_q_heads, num_kv_heads, k_pool, v_pool, pool_num_pages, block_table,
+      params->k_bits, params->v_bits, params->format, q, total_q, num_q_heads, num_kv_heads, k_pool, v_pool, pool_num_pages, block_table,
       block_table_stride, seq_lens, max_seq_len, cu_q, batch, k_tail, v_tail, softmax_scale,
       workspace, out, static_cast<hipStream_t>(stream)));
 }

@@ -59,7 +59,7 @@ struct DecodeSmem {
 // i + (b Hkv + g). Ragged lengths then cost no idle waves. Workgroup 0 also stores the page
 // prefix sums for the merge. Workgroups n_page_wg.. are the tails, one per (b, g).
 // KB, VB: key and value code widths; AUX: cache policy of the page loads.
-template <int KB, int VB, int AUX, bool BAL>
+template <int KB, int VB, int FMT, int AUX, bool BAL>
 __global__ void __launch_bounds__(kThreads)
 decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t num_kv_heads,
                     const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
@@ -159,13 +159,13 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
   // without touching memory, so the prefetches below need no branch.
   auto krec_of = [&](int64_t rec) {
     const uint32_t r = __builtin_amdgcn_readfirstlane(uint32_t(rec < 0 ? 0 : rec));
-    return record_rsrc(uniform_ptr(k_pool + uint64_t(r) * uint32_t(KeyRec<KB>::kRecord)),
-                       rec < 0 ? 0 : KeyRec<KB>::kRecord);
+    return record_rsrc(uniform_ptr(k_pool + uint64_t(r) * uint32_t(key_record<KB, FMT>())),
+                       rec < 0 ? 0 : key_record<KB, FMT>());
   };
   auto vrec_of = [&](int64_t rec) {
     const uint32_t r = __builtin_amdgcn_readfirstlane(uint32_t(rec < 0 ? 0 : rec));
-    return record_rsrc(uniform_ptr(v_pool + uint64_t(r) * uint32_t(ValRec<VB>::kRecord)),
-                       rec < 0 ? 0 : ValRec<VB>::kRecord);
+    return record_rsrc(uniform_ptr(v_pool + uint64_t(r) * uint32_t(val_record<VB, FMT>())),
+                       rec < 0 ? 0 : val_record<VB, FMT>());
   };
   // Processes the page held in t; each part of t is reloaded with page `next` as soon as
   // this page has consumed it, so the loads overlap the rest of the page's work. A page
@@ -173,8 +173,8 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
   // maximum stays -inf and its weights exp2(s - inf) are 0.
   auto process = [&](PageRegs<KB, VB>& t, int64_t next, bool valid, int lim) {
     // ---- page factors into the wave's LDS slot ------------------------------------------
-    page_factors(t, wm, l, maxq, fk, fv);
-    load_meta<AUX>(t, krec_of(next), vrec_of(next), lo);
+    page_factors<FMT>(t, wm, l, maxq, fk, fv);
+    load_meta<AUX, FMT>(t, krec_of(next), vrec_of(next), lo);
     // LDS operations of one wave complete in order: the writes above land before the reads
     // below, and after the previous page's reads
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -455,7 +455,7 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
     int sb, sg, sp, np;
     locate(x, sb, sg, sp, np);
     int64_t cur = rec_of(block_table + int64_t(sb) * bt_stride, sp, np, sg);
-    load_meta<AUX>(t, krec_of(cur), vrec_of(cur), lo);
+    load_meta<AUX, FMT>(t, krec_of(cur), vrec_of(cur), lo);
     load_kcodes<AUX>(t, krec_of(cur), lo);
     load_vcodes<AUX>(t, vrec_of(cur), lo);
     while (x < x_end) {
@@ -506,7 +506,7 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
   const int32_t* bt_row = block_table + int64_t(rg.b) * bt_stride;
   const int wslot = __builtin_amdgcn_readfirstlane(slot0 + w);   // this wave's first slot
   int64_t cur = rec_of(bt_row, wslot, n_full, g);
-  load_meta<AUX>(t, krec_of(cur), vrec_of(cur), lo);
+  load_meta<AUX, FMT>(t, krec_of(cur), vrec_of(cur), lo);
   load_kcodes<AUX>(t, krec_of(cur), lo);
   load_vcodes<AUX>(t, vrec_of(cur), lo);
   // q is rotated while the first page's loads are in flight
@@ -803,7 +803,7 @@ size_t decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv
   return bal > split ? bal : split;
 }
 
-hipError_t launch_decode(int k_bits, int v_bits, const void* q, int32_t rows,
+hipError_t launch_decode(int k_bits, int v_bits, int fmt, const void* q, int32_t rows,
                          int32_t num_q_heads, int32_t num_kv_heads, const void* k_pool,
                          const void* v_pool, int64_t pool_num_pages, const int32_t* block_table,
                          int32_t bt_stride, const int32_t* seq_lens, int32_t max_seq_len,
@@ -819,9 +819,9 @@ hipError_t launch_decode(int k_bits, int v_bits, const void* q, int32_t rows,
   const int32_t bal_wg = cu_q == nullptr ? decode_balanced_wg(rows, num_kv_heads, max_seq_len) : 0;
   if (bal_wg > 0) {
     const int32_t n_wg = bal_wg + (has_tail ? rows * num_kv_heads : 0);
-    const hipError_t e = with_preset(k_bits, v_bits, [&](auto kb, auto vb) {
-      constexpr int KB = decltype(kb)::value, VB = decltype(vb)::value;
-      hipLaunchKernelGGL((decode_pages_kernel<KB, VB, kStreamLoad, true>), dim3(n_wg),
+    const hipError_t e = with_preset(k_bits, v_bits, fmt, [&](auto kb, auto vb, auto fm) {
+      constexpr int KB = decltype(kb)::value, VB = decltype(vb)::value, FM = decltype(fm)::value;
+      hipLaunchKernelGGL((decode_pages_kernel<KB, VB, FM, kStreamLoad, true>), dim3(n_wg),
                          dim3(kThreads), 0, stream, static_cast<const __half*>(q), num_q_heads,
                          num_kv_heads, static_cast<const uint8_t*>(k_pool),
                          static_cast<const uint8_t*>(v_pool), pool_num_pages, block_table,
@@ -853,16 +853,16 @@ hipError_t launch_decode(int k_bits, int v_bits, const void* q, int32_t rows,
     // pages + tail, would leave every page workgroup on the even XCDs)
     hipError_t e;
     if (multi_row) {
-      e = launch_mq_pages(k_bits, v_bits, q, rows, num_q_heads, num_kv_heads, k_pool, v_pool,
+      e = launch_mq_pages(k_bits, v_bits, fmt, q, rows, num_q_heads, num_kv_heads, k_pool, v_pool,
                           pool_num_pages, block_table, bt_stride, seq_lens, max_seq_len, cu_q,
                           batch, k_tail, v_tail, qscale * kInvSqrt128, qscale, per_split, ns,
                           n_split_wg, first, workspace, stream);
     } else {
-      e = with_preset(k_bits, v_bits, [&](auto kb, auto vb) {
-        constexpr int KB = decltype(kb)::value, VB = decltype(vb)::value;
+      e = with_preset(k_bits, v_bits, fmt, [&](auto kb, auto vb, auto fm) {
+        constexpr int KB = decltype(kb)::value, VB = decltype(vb)::value, FM = decltype(fm)::value;
         // decode streams every page once; a read with one query per sequence reuses them
-        auto kernel = cu_q ? decode_pages_kernel<KB, VB, kReuseLoad, false>
-                           : decode_pages_kernel<KB, VB, kStreamLoad, false>;
+        auto kernel = cu_q ? decode_pages_kernel<KB, VB, FM, kReuseLoad, false>
+                           : decode_pages_kernel<KB, VB, FM, kStreamLoad, false>;
         hipLaunchKernelGGL(kernel, dim3(rows * num_kv_heads, n_split_wg), dim3(kThreads), 0,
                            stream, static_cast<const __half*>(q), num_q_heads, num_kv_heads,
                            static_cast<const uint8_t*>(k_pool),

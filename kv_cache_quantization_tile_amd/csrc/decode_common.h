@@ -122,6 +122,10 @@ template <> struct ValRec<4> {
   typedef uint4 Codes;    // one 16-channel block: 4 words = the 4 k-steps of 8 tokens
 };
 
+// Record bytes by code width and format.
+template <int KB, int FMT> constexpr int key_record() { return KeyRec<KB>::kCodeBytes + meta_bytes<FMT>(); }
+template <int VB, int FMT> constexpr int val_record() { return ValRec<VB>::kCodeBytes + meta_bytes<FMT>(); }
+
 template <int KB, int VB>
 struct PageRegs {
   typename KeyRec<KB>::Codes kc[8];
@@ -151,11 +155,11 @@ struct LaneOffsets {
   uint32_t k, v, m;   // key codes, value codes, metadata
 };
 
-template <int AUX, int KB, int VB>
+template <int AUX, int FMT, int KB, int VB>
 __device__ __forceinline__ void load_meta(PageRegs<KB, VB>& t, __amdgpu_buffer_rsrc_t kr,
                                           __amdgpu_buffer_rsrc_t vr, const LaneOffsets& o) {
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
+  for (int a = 0; a < meta_slots<FMT>(); ++a) {
     t.km[a] = __builtin_amdgcn_raw_buffer_load_b32(kr, o.m, KeyRec<KB>::kCodeBytes + 256 * a, AUX);
     t.vm[a] = __builtin_amdgcn_raw_buffer_load_b32(vr, o.m, ValRec<VB>::kCodeBytes + 256 * a, AUX);
   }
@@ -235,13 +239,17 @@ constexpr int kLoBanks = 0xC;   // lanes 8..15: low-part columns
 // (lane l: channels and tokens 2l, 2l + 1). fk, fv: the lane's unpack factors 2^(10 - b);
 // maxq: the wave's largest |q_rot| (sets the power of two ks that keeps the QK B operand
 // below 2^14; vs does the same for the PV one).
-template <int KB, int VB>
+// Format 1 slots: keys and values r, s, scale, zero. Format 2 (folded): keys s, scale',
+// zero' (r folded into the per-channel scale and zero: rk = 1); values r, scale', zero' (s
+// folded into the per-token scale and zero: sv = 1).
+template <int FMT, int KB, int VB>
 __device__ __forceinline__ void page_factors(const PageRegs<KB, VB>& t, WaveMeta& wm, int l,
                                              float maxq, float fk, float fv) {
-  const float rk0 = lo_h(t.km[0]), rk1 = hi_h(t.km[0]);
-  const float ka0 = rk0 * lo_h(t.km[2]) * fk, ka1 = rk1 * hi_h(t.km[2]) * fk;
-  const float sv0 = lo_h(t.vm[1]), sv1 = hi_h(t.vm[1]);
-  const float vp0 = sv0 * lo_h(t.vm[2]) * fv, vp1 = sv1 * hi_h(t.vm[2]) * fv;
+  constexpr int kS = FMT == 1 ? 1 : 0, kSc = FMT == 1 ? 2 : 1, kZr = FMT == 1 ? 3 : 2;
+  const float rk0 = FMT == 1 ? lo_h(t.km[0]) : 1.f, rk1 = FMT == 1 ? hi_h(t.km[0]) : 1.f;
+  const float ka0 = rk0 * lo_h(t.km[kSc]) * fk, ka1 = rk1 * hi_h(t.km[kSc]) * fk;
+  const float sv0 = FMT == 1 ? lo_h(t.vm[1]) : 1.f, sv1 = FMT == 1 ? hi_h(t.vm[1]) : 1.f;
+  const float vp0 = sv0 * lo_h(t.vm[kSc]) * fv, vp1 = sv1 * hi_h(t.vm[kSc]) * fv;
   const float mka = wave_max(fmaxf(ka0, ka1));
   const float mvp = wave_max(fmaxf(vp0, vp1));
   const int eks = pow2_norm_exp(maxq * __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mka))));
@@ -251,12 +259,12 @@ __device__ __forceinline__ void page_factors(const PageRegs<KB, VB>& t, WaveMeta
   const float a0 = ka0 * ks, a1 = ka1 * ks;
   reinterpret_cast<float2*>(wm.ka)[l] = make_float2(a0, a1);
   reinterpret_cast<float2*>(wm.kb)[l] =
-      make_float2(fmaf(ks * rk0, lo_h(t.km[3]), -a0), fmaf(ks * rk1, hi_h(t.km[3]), -a1));
-  wm.kt[l] = make_float2(lo_h(t.km[1]) * iks, hi_h(t.km[1]) * iks);
+      make_float2(fmaf(ks * rk0, lo_h(t.km[kZr]), -a0), fmaf(ks * rk1, hi_h(t.km[kZr]), -a1));
+  wm.kt[l] = make_float2(lo_h(t.km[kS]) * iks, hi_h(t.km[kS]) * iks);
   const float p0 = vp0 * vs, p1 = vp1 * vs;
   wm.vp[l] = make_float2(p0, p1);
   wm.vz[l] =
-      make_float2(fmaf(vs * sv0, lo_h(t.vm[3]), -p0), fmaf(vs * sv1, hi_h(t.vm[3]), -p1));
+      make_float2(fmaf(vs * sv0, lo_h(t.vm[kZr]), -p0), fmaf(vs * sv1, hi_h(t.vm[kZr]), -p1));
   reinterpret_cast<float2*>(wm.vr)[l] = make_float2(lo_h(t.vm[0]) * ivs, hi_h(t.vm[0]) * ivs);
 }
 

@@ -19,6 +19,13 @@ constexpr int kV4CodeBytes = 8192; // 4-bit codes of such a record
 constexpr int kVCodeBytes = 4096; // 2-bit codes of a value record
 constexpr float kInvSqrt128 = 0.08838834764831845f;  // 1 / sqrt(128), fp32-rounded
 
+// Float16 metadata after a record's codes: format 1 holds r, s, scale, zero (4 x 128 values);
+// format 2 (folded) holds the normalizer of the other axis, then the group scale and zero
+// with the group's own normalizer folded in (3 x 128): keys s, scale', zero' (per channel,
+// of Xr / s); values r, scale', zero' (per token, of Xr / r).
+template <int FMT> constexpr int meta_bytes() { return FMT == 1 ? 1024 : 768; }
+template <int FMT> constexpr int meta_slots() { return FMT == 1 ? 4 : 3; }
+
 // ---- cross-lane moves -------------------------------------------------------------
 // DPP controls (GCN/CDNA encoding).
 constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]

@@ -58,7 +58,7 @@ __device__ __forceinline__ MqWindow mq_window(int j, int rows_per_window,
   return r;
 }
 
-template <int KB, int VB>
+template <int KB, int VB, int FMT>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 mq_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t num_kv_heads,
                 const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
@@ -127,19 +127,19 @@ mq_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t num_k
   auto krec_of = [&](int64_t page) {
     const uint32_t ps = __builtin_amdgcn_readfirstlane(uint32_t(page < 0 ? 0 : page));
     const uint32_t r = ps * uint32_t(num_kv_heads) + uint32_t(g);
-    return record_rsrc(uniform_ptr(k_pool + uint64_t(r) * uint32_t(KeyRec<KB>::kRecord)),
-                       page < 0 ? 0 : KeyRec<KB>::kRecord);
+    return record_rsrc(uniform_ptr(k_pool + uint64_t(r) * uint32_t(key_record<KB, FMT>())),
+                       page < 0 ? 0 : key_record<KB, FMT>());
   };
   auto vrec_of = [&](int64_t page) {
     const uint32_t ps = __builtin_amdgcn_readfirstlane(uint32_t(page < 0 ? 0 : page));
     const uint32_t r = ps * uint32_t(num_kv_heads) + uint32_t(g);
-    return record_rsrc(uniform_ptr(v_pool + uint64_t(r) * uint32_t(ValRec<VB>::kRecord)),
-                       page < 0 ? 0 : ValRec<VB>::kRecord);
+    return record_rsrc(uniform_ptr(v_pool + uint64_t(r) * uint32_t(val_record<VB, FMT>())),
+                       page < 0 ? 0 : val_record<VB, FMT>());
   };
 
   PageRegs<KB, VB> t;
   int64_t cur = page_of(s0);
-  load_meta<kReuseLoad>(t, krec_of(cur), vrec_of(cur), lo);
+  load_meta<kReuseLoad, FMT>(t, krec_of(cur), vrec_of(cur), lo);
   load_kcodes<kReuseLoad>(t, krec_of(cur), lo);
   load_vcodes<kReuseLoad>(t, vrec_of(cur), lo);
 
@@ -199,8 +199,8 @@ mq_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t num_k
   for (int slot = s0; slot < s1; ++slot) {
     const int64_t next = page_of(slot + 1);
     const bool valid = cur >= 0;
-    page_factors(t, wm, l, maxq, fk, fv);
-    load_meta<kReuseLoad>(t, krec_of(next), vrec_of(next), lo);
+    page_factors<FMT>(t, wm, l, maxq, fk, fv);
+    load_meta<kReuseLoad, FMT>(t, krec_of(next), vrec_of(next), lo);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -401,7 +401,7 @@ size_t chunk_workspace_bytes(int32_t rows, int32_t num_q_heads, int32_t num_kv_h
   return size_t(rows) * num_q_heads * (ns + 1) * kPartStride * sizeof(float);
 }
 
-hipError_t launch_mq_pages(int k_bits, int v_bits, const void* q, int32_t rows,
+hipError_t launch_mq_pages(int k_bits, int v_bits, int fmt, const void* q, int32_t rows,
                           int32_t num_q_heads, int32_t num_kv_heads, const void* k_pool,
                           const void* v_pool, int64_t pool_num_pages, const int32_t* block_table,
                           int32_t bt_stride, const int32_t* seq_lens, int32_t max_seq_len,
@@ -411,9 +411,9 @@ hipError_t launch_mq_pages(int k_bits, int v_bits, const void* q, int32_t rows,
                           int32_t split_base, void* workspace, hipStream_t stream) {
   // 16 query vectors per wave, windows of 4R rows per workgroup
   const int R = 16 / (num_q_heads / num_kv_heads);
-  return with_preset(k_bits, v_bits, [&](auto kb, auto vb) {
-    constexpr int KB = decltype(kb)::value, VB = decltype(vb)::value;
-    hipLaunchKernelGGL((mq_pages_kernel<KB, VB>),
+  return with_preset(k_bits, v_bits, fmt, [&](auto kb, auto vb, auto fm) {
+    constexpr int KB = decltype(kb)::value, VB = decltype(vb)::value, FM = decltype(fm)::value;
+    hipLaunchKernelGGL((mq_pages_kernel<KB, VB, FM>),
                        dim3((rows + 4 * R - 1) / (4 * R) + batch, num_kv_heads, n_split_wg),
                        dim3(kThreads), 0, stream, static_cast<const __half*>(q), num_q_heads,
                        num_kv_heads, static_cast<const uint8_t*>(k_pool),

@@ -124,11 +124,17 @@ __device__ __forceinline__ uint32_t bytes_to_crumbs(uint32_t e) {
 
 // Record geometry by kind and code width (presets kvarn_k4v2_g128, kvarn_k2v2_g128,
 // kvarn_k4v4_g128).
-template <int KIND, int BITS> struct RecFormat;
-template <> struct RecFormat<0, 4> { static constexpr int kRecord = kKRecord, kCodeBytes = kKCodeBytes; };
-template <> struct RecFormat<0, 2> { static constexpr int kRecord = kK2Record, kCodeBytes = kK2CodeBytes; };
-template <> struct RecFormat<1, 2> { static constexpr int kRecord = kVRecord, kCodeBytes = kVCodeBytes; };
-template <> struct RecFormat<1, 4> { static constexpr int kRecord = kV4Record, kCodeBytes = kV4CodeBytes; };
+template <int KIND, int BITS> struct CodeBytes;
+template <> struct CodeBytes<0, 4> { static constexpr int kBytes = kKCodeBytes; };
+template <> struct CodeBytes<0, 2> { static constexpr int kBytes = kK2CodeBytes; };
+template <> struct CodeBytes<1, 2> { static constexpr int kBytes = kVCodeBytes; };
+template <> struct CodeBytes<1, 4> { static constexpr int kBytes = kV4CodeBytes; };
+// FMT 1: codes, then r, s, scale, zero; FMT 2 (folded): codes, then keys s, scale', zero' /
+// values r, scale', zero'
+template <int KIND, int BITS, int FMT> struct RecFormat {
+  static constexpr int kCodeBytes = CodeBytes<KIND, BITS>::kBytes;
+  static constexpr int kRecord = kCodeBytes + meta_bytes<FMT>();
+};
 
 // x += c * x(lane under DPP control CTRL) for 8 values, one v_fmac_f32_dpp each. The DPP
 // source is read from the register the instruction writes (all lanes read before any
@@ -288,9 +294,12 @@ __device__ __forceinline__ void rotate_tile_mfma(RowPtr row_ptr, int w, int l, f
 
 // The tile quantizer proper. row_ptr(t) gives the 16-byte aligned address of token t's
 // 128 channels. Writes one record at `rec`; BITS is the code width of this kind.
-template <int KIND, int BITS, typename RowPtr>
+template <int KIND, int BITS, int FMT, typename RowPtr>
 __device__ __forceinline__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_iters,
                                               QuantSmem& sm) {
+  // metadata slots of the record: format 1 r, s, scale, zero; format 2 the other axis's
+  // normalizer, scale', zero' (the group's normalizer folded in)
+  constexpr int kSlotSc = FMT == 1 ? 2 : 1, kSlotZr = FMT == 1 ? 3 : 2;
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63;
   const int cb = l & 15;
@@ -415,11 +424,15 @@ __device__ __forceinline__ void quantize_tile(RowPtr row_ptr, uint8_t* __restric
   // 1 / (sqrt(128) r): divides x (unnormalized) by the stored r
   const float ir_own[2] = {__builtin_amdgcn_rcpf(h2f(r16a)) * kInvSqrt128,
                            __builtin_amdgcn_rcpf(h2f(r16b)) * kInvSqrt128};
-  if (w == 0) {            // every channel once
-    sm.meta[0][ch_own] = r16a;
-    sm.meta[0][ch_own + 1] = r16b;
+  if (FMT == 1 || KIND == 1) {
+    if (w == 0) {            // every channel once
+      sm.meta[0][ch_own] = r16a;
+      sm.meta[0][ch_own + 1] = r16b;
+    }
   }
-  if ((l & 8) == 0) sm.meta[1][tok(tok_own)] = s16;   // every token once
+  if (FMT == 1 || KIND == 0) {
+    if ((l & 8) == 0) sm.meta[FMT == 1 ? 1 : 0][tok(tok_own)] = s16;   // every token once
+  }
   gc0[tok_own] = is_own;
   lds_read8(gc0, is);
   *reinterpret_cast<float2*>(&gr0[ch_own]) = make_float2(ir_own[0], ir_own[1]);
@@ -462,16 +475,19 @@ __device__ __forceinline__ void quantize_tile(RowPtr row_ptr, uint8_t* __restric
     float A2[2], B2[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const float lo = omn[k] * ir_own[k], hi_ = omx[k] * ir_own[k];   // y = z / r, r > 0
+      // format 1: the group is y = z / r (r > 0); format 2 codes z = Xr / s itself (r folded
+      // into the stored scale and zero); x carries sqrt(128)
+      const float to_g = FMT == 1 ? ir_own[k] : kInvSqrt128;
+      const float lo = omn[k] * to_g, hi_ = omx[k] * to_g;
       const uint16_t sc16 = meta16((hi_ - lo) * (BITS == 4 ? 1.f / 15.f : 1.f / 3.f));
       const uint16_t zr16 = meta16(lo);
       const float sc = h2f(sc16);
       const float inv = sc > 0.f ? __builtin_amdgcn_rcpf(sc) : 0.f;
-      A2[k] = ir_own[k] * inv;
+      A2[k] = to_g * inv;
       B2[k] = -h2f(zr16) * inv;
       if (w == 0) {
-        sm.meta[2][ch_own + k] = sc16;
-        sm.meta[3][ch_own + k] = zr16;
+        sm.meta[kSlotSc][ch_own + k] = sc16;
+        sm.meta[kSlotZr][ch_own + k] = zr16;
       }
     }
     float* ga = &sm.red[0][w][0];
@@ -531,17 +547,20 @@ __device__ __forceinline__ void quantize_tile(RowPtr row_ptr, uint8_t* __restric
 #pragma unroll
       for (int i = 1; i < 8; ++i) { mn[j] = fminf(mn[j], x[j][i]); mx[j] = fmaxf(mx[j], x[j][i]); }
     }
-    const float lo = row16_scatter8<1>(mn, l) * is_own;   // y = z / s, s > 0
-    const float hi_ = row16_scatter8<2>(mx, l) * is_own;
+    // format 1: the group is y = z / s (s > 0); format 2 codes z = Xr / r itself (s folded
+    // into the stored scale and zero)
+    const float to_g = FMT == 1 ? is_own : 1.f;
+    const float lo = row16_scatter8<1>(mn, l) * to_g;
+    const float hi_ = row16_scatter8<2>(mx, l) * to_g;
     const uint16_t sc16 = meta16((hi_ - lo) * (BITS == 2 ? 1.f / 3.f : 1.f / 15.f));
     const uint16_t zr16 = meta16(lo);
     const float sc = h2f(sc16);
     const float inv = sc > 0.f ? __builtin_amdgcn_rcpf(sc) : 0.f;
     if ((l & 8) == 0) {
-      sm.meta[2][tok(tok_own)] = sc16;
-      sm.meta[3][tok(tok_own)] = zr16;
+      sm.meta[kSlotSc][tok(tok_own)] = sc16;
+      sm.meta[kSlotZr][tok(tok_own)] = zr16;
     }
-    gc0[tok_own] = is_own * inv;
+    gc0[tok_own] = to_g * inv;
     gc1[tok_own] = -h2f(zr16) * inv;
     float A[8], B[8];
     lds_read8(gc0, A);
@@ -609,16 +628,17 @@ __device__ __forceinline__ void quantize_tile(RowPtr row_ptr, uint8_t* __restric
       out[wi] = word;
     }
   }
-  // metadata: 4 x 128 float16 = 256 words, one per thread
+  // metadata: 4 (format 1) or 3 (format 2) x 128 float16 = 256 or 192 words
   {
-    const int codes_words = RecFormat<KIND, BITS>::kCodeBytes / 4;
+    const int codes_words = RecFormat<KIND, BITS, FMT>::kCodeBytes / 4;
     const uint16_t* mm = &sm.meta[0][0];
-    out[codes_words + tid] = uint32_t(mm[2 * tid]) | (uint32_t(mm[2 * tid + 1]) << 16);
+    if (tid < meta_bytes<FMT>() / 4)
+      out[codes_words + tid] = uint32_t(mm[2 * tid]) | (uint32_t(mm[2 * tid + 1]) << 16);
   }
 }
 
 // Four workgroups per CU (16 waves) keep a whole layer's tiles resident in one round.
-template <int KIND, int BITS>
+template <int KIND, int BITS, int FMT>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 quantize_tiles_kernel(const __half* __restrict__ src, int64_t token_stride, int64_t head_stride,
                       int64_t src_num_tokens, const int64_t* __restrict__ tile_src_token,
@@ -632,13 +652,13 @@ quantize_tiles_kernel(const __half* __restrict__ src, int64_t token_stride, int6
   if (t0 < 0 || t0 > src_num_tokens - kTile || page < 0 || page >= pool_num_pages) return;
   const __half* base = src + t0 * token_stride + int64_t(h) * head_stride;
   auto row_ptr = [=](int t) { return base + int64_t(t) * token_stride; };
-  constexpr int kRec = RecFormat<KIND, BITS>::kRecord;
+  constexpr int kRec = RecFormat<KIND, BITS, FMT>::kRecord;
   uint8_t* rec = pool + (page * num_kv_heads + h) * int64_t(kRec);
-  quantize_tile<KIND, BITS>(row_ptr, rec, n_iters, sm);
+  quantize_tile<KIND, BITS, FMT>(row_ptr, rec, n_iters, sm);
 }
 
 // Keys and values of the same tiles in one launch: grid (n_tiles, num_kv_heads, 2), z = kind.
-template <int KB, int VB>
+template <int KB, int VB, int FMT>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 quantize_kv_kernel(const __half* __restrict__ k_src, const __half* __restrict__ v_src,
                    int64_t token_stride, int64_t head_stride, int64_t src_num_tokens,
@@ -656,16 +676,16 @@ quantize_kv_kernel(const __half* __restrict__ k_src, const __half* __restrict__ 
   const __half* base = (is_k ? k_src : v_src) + t0 * token_stride + int64_t(h) * head_stride;
   auto row_ptr = [=](int t) { return base + int64_t(t) * token_stride; };
   if (is_k)
-    quantize_tile<0, KB>(row_ptr, k_pool + (page * num_kv_heads + h) * int64_t(RecFormat<0, KB>::kRecord),
+    quantize_tile<0, KB, FMT>(row_ptr, k_pool + (page * num_kv_heads + h) * int64_t(RecFormat<0, KB, FMT>::kRecord),
                          n_iters, sm);
   else
-    quantize_tile<1, VB>(row_ptr, v_pool + (page * num_kv_heads + h) * int64_t(RecFormat<1, VB>::kRecord),
+    quantize_tile<1, VB, FMT>(row_ptr, v_pool + (page * num_kv_heads + h) * int64_t(RecFormat<1, VB, FMT>::kRecord),
                          n_iters, sm);
 }
 
 // Append one token per (sequence, head) into staging; quantize the staging tile it fills.
 // grid: (batch, num_kv_heads, 2 kinds)
-template <int KB, int VB>
+template <int KB, int VB, int FMT>
 __global__ void __launch_bounds__(kThreads)
 append_tokens_kernel(const __half* __restrict__ k_new, const __half* __restrict__ v_new,
                      int32_t num_kv_heads, const int32_t* __restrict__ seq_lens,
@@ -691,10 +711,10 @@ append_tokens_kernel(const __half* __restrict__ k_new, const __half* __restrict_
   // the filled row is read from the new-token buffer, never from the staging just written
   auto row_ptr = [=](int t) { return t == kTile - 1 ? src_new : stage + int64_t(t) * kDim; };
   if (kind == 0) {
-    quantize_tile<0, KB>(row_ptr, k_pool + (page * num_kv_heads + h) * int64_t(RecFormat<0, KB>::kRecord),
+    quantize_tile<0, KB, FMT>(row_ptr, k_pool + (page * num_kv_heads + h) * int64_t(RecFormat<0, KB, FMT>::kRecord),
                          n_iters, sm);
   } else {
-    quantize_tile<1, VB>(row_ptr, v_pool + (page * num_kv_heads + h) * int64_t(RecFormat<1, VB>::kRecord),
+    quantize_tile<1, VB, FMT>(row_ptr, v_pool + (page * num_kv_heads + h) * int64_t(RecFormat<1, VB, FMT>::kRecord),
                          n_iters, sm);
   }
 }
@@ -705,7 +725,7 @@ append_tokens_kernel(const __half* __restrict__ k_new, const __half* __restrict_
 // grid: (tile slots, batch, num_kv_heads * 2); slot j is tile t = L / 128 + j, quantized when
 // complete (128 t + 128 <= L + n). Its rows below L come from staging (only the tile that was
 // partial before the chunk has such rows), the others straight from the new-token buffer.
-template <int KB, int VB>
+template <int KB, int VB, int FMT>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 write_tiles_kernel(const __half* __restrict__ k_new, const __half* __restrict__ v_new,
                    int32_t total_new, const int32_t* __restrict__ cu_new, int32_t max_new,
@@ -736,10 +756,10 @@ write_tiles_kernel(const __half* __restrict__ k_new, const __half* __restrict__ 
     return a < L ? stage + int64_t(r) * kDim : src + (a - L) * row_stride;
   };
   if (kind == 0)
-    quantize_tile<0, KB>(row_ptr, k_pool + (page * num_kv_heads + h) * int64_t(RecFormat<0, KB>::kRecord),
+    quantize_tile<0, KB, FMT>(row_ptr, k_pool + (page * num_kv_heads + h) * int64_t(RecFormat<0, KB, FMT>::kRecord),
                          n_iters, sm);
   else
-    quantize_tile<1, VB>(row_ptr, v_pool + (page * num_kv_heads + h) * int64_t(RecFormat<1, VB>::kRecord),
+    quantize_tile<1, VB, FMT>(row_ptr, v_pool + (page * num_kv_heads + h) * int64_t(RecFormat<1, VB, FMT>::kRecord),
                          n_iters, sm);
 }
 
@@ -775,29 +795,33 @@ write_staging_kernel(const __half* __restrict__ k_new, const __half* __restrict_
 // Page records back to float16 tiles (read side, then the inverse rotation H^-1 = H):
 // grid (n_tiles, num_kv_heads), one workgroup per record, the thread layout of the
 // quantizer (channels 8cb..+7 x tokens 8tb..+7). dst: [n_tiles][num_kv_heads][token][channel].
-template <int KIND, int BITS>
+template <int KIND, int BITS, int FMT>
 __global__ void __launch_bounds__(kThreads)
 dequantize_tiles_kernel(const uint8_t* __restrict__ pool, int64_t pool_num_pages,
                         const int32_t* __restrict__ pages, int32_t num_kv_heads,
                         __half* __restrict__ dst) {
-  constexpr int kRec = RecFormat<KIND, BITS>::kRecord;
-  __shared__ uint4 rec_sm[kRec / 16];
+  constexpr int kRec = RecFormat<KIND, BITS, FMT>::kRecord;
+  // metadata slots: format 1 r, s, scale, zero; format 2 keys s, scale', zero' (r = 1),
+  // values r, scale', zero' (s = 1)
+  constexpr int kR = 0, kS = FMT == 1 ? 1 : 0, kSc = FMT == 1 ? 2 : 1, kZr = FMT == 1 ? 3 : 2;
+  constexpr bool kHasR = FMT == 1 || KIND == 1, kHasS = FMT == 1 || KIND == 0;
+  __shared__ uint4 rec_sm[(kRec + 15) / 16];
   const int tile = blockIdx.x, h = blockIdx.y;
   const int64_t page = pages[tile];
   if (page < 0 || page >= pool_num_pages) return;
   const uint4* rec = reinterpret_cast<const uint4*>(pool + (page * num_kv_heads + h) * int64_t(kRec));
   const int tid = threadIdx.x;
-  for (int i = tid; i < kRec / 16; i += kThreads) rec_sm[i] = rec[i];
+  for (int i = tid; i < kRec / 16; i += kThreads) rec_sm[i] = rec[i];   // kRec % 16 == 0
   __syncthreads();
   const uint32_t* words = reinterpret_cast<const uint32_t*>(rec_sm);
   const uint16_t* meta = reinterpret_cast<const uint16_t*>(
-      reinterpret_cast<const uint8_t*>(rec_sm) + RecFormat<KIND, BITS>::kCodeBytes);
+      reinterpret_cast<const uint8_t*>(rec_sm) + RecFormat<KIND, BITS, FMT>::kCodeBytes);
   const int w = tid >> 6, l = tid & 63, cb = l & 15, tb = 4 * w + (l >> 4);
   float x[8][8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int t = 8 * tb + j;
-    const float st = h2f(meta[kTile + t]);
+    const float st = kHasS ? h2f(meta[kS * kTile + t]) : 1.f;
     uint32_t kw = 0;
     if constexpr (KIND == 0 && BITS == 4) kw = words[t * 16 + cb];   // channels 8cb..8cb+7 of token t
 #pragma unroll
@@ -813,8 +837,8 @@ dequantize_tiles_kernel(const uint8_t* __restrict__ pool, int64_t pool_num_pages
           const int p = 4 * hs + ((c & 7) >> 1) + 8 * (c & 1);
           code = (words[t * 8 + (c >> 4)] >> (2 * p)) & 3u;
         }
-        sc = h2f(meta[2 * kDim + c]);
-        zr = h2f(meta[3 * kDim + c]);
+        sc = h2f(meta[kSc * kDim + c]);
+        zr = h2f(meta[kZr * kDim + c]);
       } else {
         // token t of channel c: word 8c + 2g + d, crumb p (the record's crumb order)
         const int s_ = t >> 5, rem = t & 31;
@@ -827,10 +851,10 @@ dequantize_tiles_kernel(const uint8_t* __restrict__ pool, int64_t pool_num_pages
           const int qn = (jj >> 1) + 4 * (jj & 1);
           code = (words[16 * c + 4 * g + s_] >> (4 * qn)) & 15u;
         }
-        sc = h2f(meta[2 * kDim + t]);
-        zr = h2f(meta[3 * kDim + t]);
+        sc = h2f(meta[kSc * kDim + t]);
+        zr = h2f(meta[kZr * kDim + t]);
       }
-      x[j][i] = h2f(meta[c]) * st * fmaf(sc, float(code), zr);
+      x[j][i] = (kHasR ? h2f(meta[kR * kDim + c]) : 1.f) * st * fmaf(sc, float(code), zr);
     }
   }
   fwht_channels_f32(x, cb);
@@ -848,23 +872,23 @@ dequantize_tiles_kernel(const uint8_t* __restrict__ pool, int64_t pool_num_pages
 
 }  // namespace
 
-hipError_t launch_dequantize_tiles(int kind, int k_bits, int v_bits, const void* pool,
+hipError_t launch_dequantize_tiles(int kind, int k_bits, int v_bits, int fmt, const void* pool,
                                    int64_t pool_num_pages, const int32_t* pages, int32_t n_tiles,
                                    int32_t num_kv_heads, void* dst, hipStream_t stream) {
   dim3 grid(n_tiles, num_kv_heads), block(kThreads);
   const auto* pl = static_cast<const uint8_t*>(pool);
   auto* d = static_cast<__half*>(dst);
-  return with_preset(k_bits, v_bits, [&](auto kb, auto vb) {
+  return with_preset(k_bits, v_bits, fmt, [&](auto kb, auto vb, auto fm) {
     if (kind == 1)
-      hipLaunchKernelGGL((dequantize_tiles_kernel<1, decltype(vb)::value>), grid, block, 0, stream,
+      hipLaunchKernelGGL((dequantize_tiles_kernel<1, decltype(vb)::value, decltype(fm)::value>), grid, block, 0, stream,
                          pl, pool_num_pages, pages, num_kv_heads, d);
     else
-      hipLaunchKernelGGL((dequantize_tiles_kernel<0, decltype(kb)::value>), grid, block, 0, stream,
+      hipLaunchKernelGGL((dequantize_tiles_kernel<0, decltype(kb)::value, decltype(fm)::value>), grid, block, 0, stream,
                          pl, pool_num_pages, pages, num_kv_heads, d);
   });
 }
 
-hipError_t launch_quantize_tiles(int kind, int k_bits, int v_bits, const void* src,
+hipError_t launch_quantize_tiles(int kind, int k_bits, int v_bits, int fmt, const void* src,
                                  int64_t token_stride, int64_t head_stride, int64_t src_num_tokens,
                                  const int64_t* tile_src_token, const int32_t* tile_dst_page,
                                  int32_t n_tiles, int32_t num_kv_heads, void* pool,
@@ -872,19 +896,19 @@ hipError_t launch_quantize_tiles(int kind, int k_bits, int v_bits, const void* s
   dim3 grid(n_tiles, num_kv_heads), block(kThreads);
   const auto* sp = static_cast<const __half*>(src);
   auto* pl = static_cast<uint8_t*>(pool);
-  return with_preset(k_bits, v_bits, [&](auto kb, auto vb) {
+  return with_preset(k_bits, v_bits, fmt, [&](auto kb, auto vb, auto fm) {
     if (kind == 1)
-      hipLaunchKernelGGL((quantize_tiles_kernel<1, decltype(vb)::value>), grid, block, 0, stream,
+      hipLaunchKernelGGL((quantize_tiles_kernel<1, decltype(vb)::value, decltype(fm)::value>), grid, block, 0, stream,
                          sp, token_stride, head_stride, src_num_tokens, tile_src_token,
                          tile_dst_page, num_kv_heads, pl, pool_num_pages, n_iters);
     else
-      hipLaunchKernelGGL((quantize_tiles_kernel<0, decltype(kb)::value>), grid, block, 0, stream,
+      hipLaunchKernelGGL((quantize_tiles_kernel<0, decltype(kb)::value, decltype(fm)::value>), grid, block, 0, stream,
                          sp, token_stride, head_stride, src_num_tokens, tile_src_token,
                          tile_dst_page, num_kv_heads, pl, pool_num_pages, n_iters);
   });
 }
 
-hipError_t launch_quantize_kv(int k_bits, int v_bits, const void* k_src, const void* v_src,
+hipError_t launch_quantize_kv(int k_bits, int v_bits, int fmt, const void* k_src, const void* v_src,
                               int64_t token_stride, int64_t head_stride, int64_t src_num_tokens,
                               const int64_t* tile_src_token, const int32_t* tile_dst_page,
                               int32_t n_tiles, int32_t num_kv_heads, void* k_pool, void* v_pool,
@@ -894,15 +918,15 @@ hipError_t launch_quantize_kv(int k_bits, int v_bits, const void* k_src, const v
   const auto* vs = static_cast<const __half*>(v_src);
   auto* kp = static_cast<uint8_t*>(k_pool);
   auto* vp = static_cast<uint8_t*>(v_pool);
-  return with_preset(k_bits, v_bits, [&](auto kb, auto vb) {
-    hipLaunchKernelGGL((quantize_kv_kernel<decltype(kb)::value, decltype(vb)::value>), grid, block,
+  return with_preset(k_bits, v_bits, fmt, [&](auto kb, auto vb, auto fm) {
+    hipLaunchKernelGGL((quantize_kv_kernel<decltype(kb)::value, decltype(vb)::value, decltype(fm)::value>), grid, block,
                        0, stream, ks, vs, token_stride, head_stride, src_num_tokens,
                        tile_src_token, tile_dst_page, num_kv_heads, kp, vp, pool_num_pages,
                        n_iters);
   });
 }
 
-hipError_t launch_write_tokens(int k_bits, int v_bits, const void* k_new, const void* v_new,
+hipError_t launch_write_tokens(int k_bits, int v_bits, int fmt, const void* k_new, const void* v_new,
                                int32_t total_new, const int32_t* cu_new, int32_t max_new,
                                int32_t batch, int32_t num_kv_heads, const int32_t* seq_lens,
                                void* k_tail, void* v_tail, const int32_t* block_table,
@@ -912,8 +936,8 @@ hipError_t launch_write_tokens(int k_bits, int v_bits, const void* k_new, const 
   dim3 grid1(max_new / kTile + 1, batch, num_kv_heads * 2), block(kThreads);
   const auto* kn = static_cast<const __half*>(k_new);
   const auto* vn = static_cast<const __half*>(v_new);
-  const hipError_t e = with_preset(k_bits, v_bits, [&](auto kb, auto vb) {
-    hipLaunchKernelGGL((write_tiles_kernel<decltype(kb)::value, decltype(vb)::value>), grid1,
+  const hipError_t e = with_preset(k_bits, v_bits, fmt, [&](auto kb, auto vb, auto fm) {
+    hipLaunchKernelGGL((write_tiles_kernel<decltype(kb)::value, decltype(vb)::value, decltype(fm)::value>), grid1,
                        block, 0, stream, kn, vn, total_new, cu_new, max_new, num_kv_heads,
                        seq_lens, static_cast<const __half*>(k_tail),
                        static_cast<const __half*>(v_tail), block_table, bt_stride,
@@ -928,7 +952,7 @@ hipError_t launch_write_tokens(int k_bits, int v_bits, const void* k_new, const 
   return hipGetLastError();
 }
 
-hipError_t launch_append_tokens(int k_bits, int v_bits, const void* k_new, const void* v_new,
+hipError_t launch_append_tokens(int k_bits, int v_bits, int fmt, const void* k_new, const void* v_new,
                                 int32_t batch, int32_t num_kv_heads, const int32_t* seq_lens,
                                 void* k_tail, void* v_tail, const int32_t* block_table,
                                 int32_t bt_stride, void* k_pool, void* v_pool,
@@ -940,8 +964,8 @@ hipError_t launch_append_tokens(int k_bits, int v_bits, const void* k_new, const
   auto* vt = static_cast<__half*>(v_tail);
   auto* kp = static_cast<uint8_t*>(k_pool);
   auto* vp = static_cast<uint8_t*>(v_pool);
-  return with_preset(k_bits, v_bits, [&](auto kb, auto vb) {
-    hipLaunchKernelGGL((append_tokens_kernel<decltype(kb)::value, decltype(vb)::value>), grid,
+  return with_preset(k_bits, v_bits, fmt, [&](auto kb, auto vb, auto fm) {
+    hipLaunchKernelGGL((append_tokens_kernel<decltype(kb)::value, decltype(vb)::value, decltype(fm)::value>), grid,
                        block, 0, stream, kn, vn, num_kv_heads, seq_lens, kt, vt, block_table,
                        bt_stride, kp, vp, pool_num_pages, n_iters);
   });

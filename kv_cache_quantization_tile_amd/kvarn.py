@@ -29,10 +29,15 @@ class KvarnError(RuntimeError):
         self.status = status
 
 
+FORMAT_SEPARATE = 1     # page records with r, s, scale, zero stored apart
+FORMAT_FOLDED = 2       # each group's normalizer folded into its scale and zero
+
+
 class Params(ctypes.Structure):
     _fields_ = [("head_dim", ctypes.c_int32), ("tile_tokens", ctypes.c_int32),
                 ("k_bits", ctypes.c_int32), ("v_bits", ctypes.c_int32),
-                ("group", ctypes.c_int32), ("sinkhorn_iters", ctypes.c_int32)]
+                ("group", ctypes.c_int32), ("sinkhorn_iters", ctypes.c_int32),
+                ("format", ctypes.c_int32)]
 
 
 def _load():
@@ -113,10 +118,14 @@ def _need(t, name, dtype, device=True):
 # ----------------------------------------------------------------------------- params
 
 
-def params_from_dtype(kv_cache_dtype: str = "kvarn_k4v2_g128", sinkhorn_iters: int = 8) -> Params:
+def params_from_dtype(kv_cache_dtype: str = "kvarn_k4v2_g128", sinkhorn_iters: int = 8,
+                      format: int = FORMAT_SEPARATE) -> Params:
+    """Params of a preset string; `format` selects the page record layout."""
     p = Params()
     _check(lib.kvarn_params_from_dtype(kv_cache_dtype.encode(), sinkhorn_iters, ctypes.byref(p)),
            f"kv_cache_dtype {kv_cache_dtype!r}")
+    p.format = format
+    _check(lib.kvarn_params_check(ctypes.byref(p)), f"format {format}")
     return p
 
 

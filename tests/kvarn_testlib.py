@@ -86,15 +86,15 @@ def reconstruction_error(x_ct: np.ndarray, d: dict, kind: int) -> float:
 
 def check_quantized_tiles(tiles_tc: np.ndarray, records, kind: int, n_iters: int,
                           stats: QuantStats | None = None, k_bits: int = 4,
-                          v_bits: int = 2) -> QuantStats:
+                          v_bits: int = 2, fmt: int = 1) -> QuantStats:
     """tiles_tc: [n, 128 tokens, 128 channels] float16 (the source layout); records: the GPU
     page records of those tiles. Asserts L1 and L2 (every tile, every group) and L3's
     |code difference| <= 1 outside offset-dominated groups; accumulates the L3 and plain
     metadata statistics (asserted by the caller: assert_rate)."""
     stats = stats or QuantStats()
     x = np.ascontiguousarray(np.swapaxes(tiles_tc, -1, -2))  # channels x tokens
-    ref = O.quantize_tiles(x, kind, n_iters, k_bits=k_bits, v_bits=v_bits)
-    unpack = lambda rec: O.unpack_record(rec, kind, k_bits, v_bits)
+    ref = O.quantize_tiles(x, kind, n_iters, k_bits=k_bits, v_bits=v_bits, fmt=fmt)
+    unpack = lambda rec: O.unpack_record(rec, kind, k_bits, v_bits, fmt)
     bits = k_bits if kind == O.KIND_K else v_bits
     qmax = (1 << bits) - 1
     ax = 1 if kind == O.KIND_K else 0          # the axis a group runs along (c x t tile)
@@ -206,21 +206,27 @@ def assert_rate(stats: QuantStats, meta_plain_rate: float = META_PLAIN_RATE):
 
 
 def key_bits_of(k_pool) -> int:
-    """Key code width of a pool, from its record size (9216 B: 4-bit, 5120 B: 2-bit)."""
-    return 4 if k_pool.shape[2] == O.K_RECORD_BYTES else 2
+    """Key code width of a pool, from its record size."""
+    return O.record_layout(k_pool.shape[2])[0]
 
 
 def value_bits_of(v_pool) -> int:
-    """Value code width of a pool, from its record size (5120 B: 2-bit, 9216 B: 4-bit)."""
-    return 4 if v_pool.shape[2] == O.V4_RECORD_BYTES else 2
+    """Value code width of a pool, from its record size."""
+    return O.record_layout(v_pool.shape[2])[0]
+
+
+def format_of(pool) -> int:
+    """Record format of a pool (1 separate, 2 folded), from its record size."""
+    return O.record_layout(pool.shape[2])[1]
 
 
 def oracle_rows(q: np.ndarray, hq_list, G: int, k_recs, v_recs, k_tail=None, v_tail=None,
-                softmax_scale=1.0 / np.sqrt(128), k_bits: int = 4, v_bits: int = 2):
+                softmax_scale=1.0 / np.sqrt(128), k_bits: int = 4, v_bits: int = 2,
+                fmt: int = 1):
     """Oracle outputs for query heads hq_list (all sharing one KV head whose page records are
     k_recs / v_recs, plus float16 tails [n_tail, 128]). q: [Hq, 128] float16."""
-    ks = [O.dequantize_k_record(r, k_bits) for r in k_recs]
-    vs = [O.dequantize_v_record(r, v_bits) for r in v_recs]
+    ks = [O.dequantize_k_record(r, k_bits, fmt) for r in k_recs]
+    vs = [O.dequantize_v_record(r, v_bits, fmt) for r in v_recs]
     if k_tail is not None and len(k_tail):
         ks.append(np.asarray(k_tail, np.float16).astype(np.float64))
         vs.append(np.asarray(v_tail, np.float16).astype(np.float64))
@@ -268,7 +274,7 @@ def check_decode(q_gpu, out_gpu, k_pool, v_pool, block_table, seq_lens, G, rows=
         no_keys = not pages and (tail_k is None or tail_k.shape[0] == 0)
         ref = None if no_keys else oracle_rows(q[b], hqs, G, krec, vrec, tail_k, tail_v,
                                                softmax_scale, key_bits_of(k_pool),
-                                               value_bits_of(v_pool))
+                                               value_bits_of(v_pool), format_of(k_pool))
         for hq in hqs:
             if no_keys:            # L = 0, or every page skipped and no tail: zeros
                 assert np.all(out[b, hq] == 0), f"b={b} hq={hq}: expected zeros"

@@ -27,8 +27,8 @@ def test_header_symbols_exported():
 
 
 def test_versions_and_status_strings():
-    assert K.lib.kvarn_abi_version() == 1
-    assert K.lib.kvarn_format_version() == 1
+    assert K.lib.kvarn_abi_version() == 2
+    assert K.lib.kvarn_format_version() == 2            # formats 1 (separate) and 2 (folded)
     for s in range(5):
         assert K.lib.kvarn_status_str(s).decode() == K.STATUS[s]
     assert K.lib.kvarn_status_str(99) == b"unknown status"
@@ -36,7 +36,7 @@ def test_versions_and_status_strings():
 
 def test_params_from_dtype():
     p = K.params_from_dtype("kvarn_k4v2_g128", 8)
-    assert (p.head_dim, p.tile_tokens, p.k_bits, p.v_bits, p.group, p.sinkhorn_iters) == (128, 128, 4, 2, 128, 8)
+    assert (p.head_dim, p.tile_tokens, p.k_bits, p.v_bits, p.group, p.sinkhorn_iters, p.format) == (128, 128, 4, 2, 128, 8, 1)
     out = K.Params()
     for bad in ("", "fp8", "kvarn_k4v2", "kvarn_k4v2_g", "kvarn_kv2_g128", "kvarn_k4v2_g128x", "kvarn_k0v2_g128"):
         assert K.lib.kvarn_params_from_dtype(bad.encode(), 8, ctypes.byref(out)) == INVALID, bad
@@ -61,9 +61,21 @@ def test_page_bytes():
     assert K.page_bytes(p2, K.KIND_K) == 5120 and K.page_bytes(p2, K.KIND_V) == 5120
     p4 = K.params_from_dtype("kvarn_k4v4_g128")
     assert K.page_bytes(p4, K.KIND_K) == 9216 and K.page_bytes(p4, K.KIND_V) == 9216
-    bad = K.Params(128, 64, 4, 2, 128, 8)
+    bad = K.Params(128, 64, 4, 2, 128, 8, 1)
     assert K.lib.kvarn_params_check(ctypes.byref(bad)) == UNSUP
     assert K.page_bytes(bad, K.KIND_K) == 0
+    # folded format: 3 metadata vectors instead of 4
+    for preset, kb, vb in (("kvarn_k4v2_g128", 8960, 4864), ("kvarn_k2v2_g128", 4864, 4864),
+                           ("kvarn_k4v4_g128", 8960, 8960)):
+        pf = K.params_from_dtype(preset, 8, format=K.FORMAT_FOLDED)
+        assert (K.page_bytes(pf, K.KIND_K), K.page_bytes(pf, K.KIND_V)) == (kb, vb)
+    for fmt in (0, 3, -1):
+        pf = K.params_from_dtype()
+        pf.format = fmt
+        assert K.lib.kvarn_params_check(ctypes.byref(pf)) == INVALID
+        assert K.page_bytes(pf, K.KIND_K) == 0
+    with pytest.raises(K.KvarnError):
+        K.params_from_dtype("kvarn_k4v2_g128", 8, format=3)
 
 
 def _quant(p, **kw):
@@ -87,7 +99,7 @@ def test_quantize_validation():
     assert _quant(p, ts=1023) == INVALID              # stride not a multiple of 8
     assert _quant(p, src=ctypes.c_void_p(0x10008)) == INVALID   # misaligned
     assert _quant(p, ntok=-1) == INVALID
-    bad = K.Params(128, 128, 2, 4, 128, 8)
+    bad = K.Params(128, 128, 2, 4, 128, 8, 1)
     assert _quant(bad) == UNSUP
     assert K.lib.kvarn_quantize_tiles(None, 0, FAKE, 8, 8, 1, FAKE, FAKE, 1, 1, FAKE, 1, None) == INVALID
 
@@ -114,7 +126,7 @@ def test_quantize_kv_validation():
     assert _quant_kv(p, vsrc=ctypes.c_void_p(0x10004)) == INVALID
     assert _quant_kv(p, kpool=ctypes.c_void_p(0x10008)) == INVALID
     assert _quant_kv(p, npages=-1) == INVALID
-    assert _quant_kv(K.Params(128, 128, 2, 4, 128, 8)) == UNSUP
+    assert _quant_kv(K.Params(128, 128, 2, 4, 128, 8, 1)) == UNSUP
 
 
 def _dequant(p, **kw):
@@ -134,7 +146,7 @@ def test_dequantize_validation():
     assert _dequant(p, hkv=0) == INVALID
     assert _dequant(p, npages=-2) == INVALID
     assert _dequant(p, dst=ctypes.c_void_p(0x10002)) == INVALID
-    assert _dequant(K.Params(128, 128, 2, 4, 128, 8)) == UNSUP
+    assert _dequant(K.Params(128, 128, 2, 4, 128, 8, 1)) == UNSUP
 
 
 def _write(p, **kw):
@@ -162,7 +174,7 @@ def test_write_tokens_validation():
     assert _write(p, kn=ctypes.c_void_p(0x10004)) == INVALID
     assert _write(p, vp=ctypes.c_void_p(0x10008)) == INVALID
     assert _write(p, npages=-1) == INVALID
-    assert _write(K.Params(128, 128, 2, 4, 128, 8)) == UNSUP
+    assert _write(K.Params(128, 128, 2, 4, 128, 8, 1)) == UNSUP
 
 
 def _decode(p, **kw):

@@ -35,11 +35,18 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Value codes are staged in LDS as one 128-byte row of token codes per channel. Row c starts at
+// dword 36 c + 2 (c >> 3): the 32 lanes of one pass of a 4-byte write (16 channel blocks, two
+// token groups) and of the packing reads (4 channels, 4 token groups, 2 steps) then fall into
+// 32 distinct banks. A stride of 32 dwords puts all 16 channel blocks in one bank.
+constexpr int kCodeRowBase = 36;
+__device__ __forceinline__ int codes_row(int c) { return kCodeRowBase * c + 2 * (c >> 3); }
+
 struct QuantSmem {
-  float red[2][4][kDim];       // per-wave partial sums over tokens, per channel (2 buffers)
-  float gr[4][2][kDim];        // per-wave broadcast of per-channel values
+  float red[2][4][kDim];       // per-wave partial sums over tokens, channel vectors (2 buffers)
+  float gr[4][2][kDim];        // per-wave broadcast of channel vectors (chan_pair_slot order)
   float gc[4][4][2][8];        // per-wave, per-row broadcast of per-token values
-  uint8_t codes[kTile * kDim]; // value codes, [channel][token]
+  uint32_t codes[kCodeRowBase * kDim + 2 * 16];  // value codes: row c at codes_row(c)
   uint16_t meta[4][kDim];      // r, s, scale, zero as float16 bits
 };
 
@@ -104,6 +111,22 @@ __device__ __forceinline__ void lds_read8(const float* p, float (&v)[8]) {
   const float4 b = *reinterpret_cast<const float4*>(p + 4);
   v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+// Per-channel float vectors in LDS (128 floats): channel 8 cb + o lives at float
+// 64 (o >> 2) + 4 cb + ((o & 3) ^ 2 (o >> 2)). The two channels an owner lane holds
+// (o = off, off + 1 with off even) are one aligned float2, and a lane's block of 8 channels is
+// two float4 loads; the float2 stores of a 16-lane pass hit distinct bank pairs except for one
+// 2-way overlap, where channel-major order (a 32-byte stride) costs 4-way conflicts on the
+// stores and 2-way ones on the block loads.
+__device__ __forceinline__ int chan_pair_slot(int cb, int off) {
+  return 64 * (off >> 2) + 4 * cb + ((off & 3) ^ (2 * (off >> 2)));
+}
+__device__ __forceinline__ void chan_read8(const float* p, int cb, float (&v)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p + 4 * cb);        // o = 0, 1, 2, 3
+  const float4 b = *reinterpret_cast<const float4*>(p + 64 + 4 * cb);   // o = 6, 7, 4, 5
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.z; v[5] = b.w; v[6] = b.x; v[7] = b.y;
 }
 
 // float16 bits of a normalizer: clipped to [2^-14, 65504] first
@@ -326,6 +349,7 @@ __device__ __forceinline__ void quantize_tile(RowPtr row_ptr, uint8_t* __restric
   const int tok_own = l & 7;
   const int ch_off = 4 * (r & 1) + 2 * (r >> 1);
   const int ch_own = 8 * cb + ch_off;
+  const int own_slot = chan_pair_slot(cb, ch_off);  // my channel pair in a channel vector
   float* gc0 = &sm.gc[w][r][0][0];
   float* gc1 = &sm.gc[w][r][1][0];
   float* gr0 = &sm.gr[w][0][0];
@@ -336,12 +360,12 @@ __device__ __forceinline__ void quantize_tile(RowPtr row_ptr, uint8_t* __restric
   float vr_own[2] = {128.f, 128.f};    // ... of my two channels, in units of x (128 = never)
   int buf = 0;
   auto cross_wave_sum = [&](const float (&o)[2], float (&t)[2]) {
-    *reinterpret_cast<float2*>(&sm.red[buf][w][ch_own]) = make_float2(o[0], o[1]);
+    *reinterpret_cast<float2*>(&sm.red[buf][w][own_slot]) = make_float2(o[0], o[1]);
     __syncthreads();
-    float2 a = *reinterpret_cast<const float2*>(&sm.red[buf][0][ch_own]);
+    float2 a = *reinterpret_cast<const float2*>(&sm.red[buf][0][own_slot]);
 #pragma unroll
     for (int ww = 1; ww < 4; ++ww) {
-      const float2 b = *reinterpret_cast<const float2*>(&sm.red[buf][ww][ch_own]);
+      const float2 b = *reinterpret_cast<const float2*>(&sm.red[buf][ww][own_slot]);
       a.x += b.x;
       a.y += b.y;
     }
@@ -391,8 +415,8 @@ __device__ __forceinline__ void quantize_tile(RowPtr row_ptr, uint8_t* __restric
     cross_wave_sum(o, mean_c);
     mean_c[0] *= 1.f / kTile;
     mean_c[1] *= 1.f / kTile;
-    *reinterpret_cast<float2*>(&gr0[ch_own]) = make_float2(-mean_c[0], -mean_c[1]);
-    lds_read8(&gr0[8 * cb], m);             // minus the means of my 8 channels
+    *reinterpret_cast<float2*>(&gr0[own_slot]) = make_float2(-mean_c[0], -mean_c[1]);
+    chan_read8(gr0, cb, m);             // minus the means of my 8 channels
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       float a = 0.f;
@@ -411,9 +435,9 @@ __device__ __forceinline__ void quantize_tile(RowPtr row_ptr, uint8_t* __restric
       const float var = var_c[k] * (1.f / kTile);
       vr_own[k] = var > 1e-12f * mean_c[k] * mean_c[k] ? var : vr_own[k];
     }
-    *reinterpret_cast<float2*>(&gr0[ch_own]) =
+    *reinterpret_cast<float2*>(&gr0[own_slot]) =
         make_float2(__builtin_amdgcn_rsqf(vr_own[0]), __builtin_amdgcn_rsqf(vr_own[1]));
-    lds_read8(&gr0[8 * cb], ir);
+    chan_read8(gr0, cb, ir);
   }
 
   // ---- 4a. stored normalizers (float16) and their inverses on every lane ----------------
@@ -435,8 +459,8 @@ __device__ __forceinline__ void quantize_tile(RowPtr row_ptr, uint8_t* __restric
   }
   gc0[tok_own] = is_own;
   lds_read8(gc0, is);
-  *reinterpret_cast<float2*>(&gr0[ch_own]) = make_float2(ir_own[0], ir_own[1]);
-  lds_read8(&gr0[8 * cb], ir);
+  *reinterpret_cast<float2*>(&gr0[own_slot]) = make_float2(ir_own[0], ir_own[1]);
+  chan_read8(gr0, cb, ir);
 
   // ---- 4b. asymmetric RTN --------------------------------------------------------------
   // code = clamp(rne((y - zero) / scale), 0, top) with y = x / (r s): computed as
@@ -462,13 +486,13 @@ __device__ __forceinline__ void quantize_tile(RowPtr row_ptr, uint8_t* __restric
     rows4_scatter8<2>(mx, omx);
     // the 4 waves' partials through the (free) broadcast area; both red buffers are free
     // once every thread is past this barrier
-    *reinterpret_cast<float2*>(&sm.gr[w][0][ch_own]) = make_float2(omn[0], omn[1]);
-    *reinterpret_cast<float2*>(&sm.gr[w][1][ch_own]) = make_float2(omx[0], omx[1]);
+    *reinterpret_cast<float2*>(&sm.gr[w][0][own_slot]) = make_float2(omn[0], omn[1]);
+    *reinterpret_cast<float2*>(&sm.gr[w][1][own_slot]) = make_float2(omx[0], omx[1]);
     __syncthreads();
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) {
-      const float2 a = *reinterpret_cast<const float2*>(&sm.gr[ww][0][ch_own]);
-      const float2 b = *reinterpret_cast<const float2*>(&sm.gr[ww][1][ch_own]);
+      const float2 a = *reinterpret_cast<const float2*>(&sm.gr[ww][0][own_slot]);
+      const float2 b = *reinterpret_cast<const float2*>(&sm.gr[ww][1][own_slot]);
       omn[0] = fminf(omn[0], a.x); omn[1] = fminf(omn[1], a.y);
       omx[0] = fmaxf(omx[0], b.x); omx[1] = fmaxf(omx[1], b.y);
     }
@@ -492,11 +516,11 @@ __device__ __forceinline__ void quantize_tile(RowPtr row_ptr, uint8_t* __restric
     }
     float* ga = &sm.red[0][w][0];
     float* gb = &sm.red[1][w][0];
-    *reinterpret_cast<float2*>(&ga[ch_own]) = make_float2(A2[0], A2[1]);
-    *reinterpret_cast<float2*>(&gb[ch_own]) = make_float2(B2[0], B2[1]);
+    *reinterpret_cast<float2*>(&ga[own_slot]) = make_float2(A2[0], A2[1]);
+    *reinterpret_cast<float2*>(&gb[own_slot]) = make_float2(B2[0], B2[1]);
     float A[8], B[8];
-    lds_read8(&ga[8 * cb], A);
-    lds_read8(&gb[8 * cb], B);
+    chan_read8(ga, cb, A);
+    chan_read8(gb, cb, B);
     if constexpr (BITS == 4) {
       // word (t, cb) = channels 8cb..8cb+7 of token t; nibble p <- channel {0,2,4,6,1,3,5,7}[p]:
       // channel i's code goes to byte i / 4 of register i % 4 (registers hold channels {0, 4},
@@ -575,8 +599,8 @@ __device__ __forceinline__ void quantize_tile(RowPtr row_ptr, uint8_t* __restric
         else hi4 = __builtin_amdgcn_cvt_pk_u8_f32(u, j - 4, hi4);
       }
       // slots 0..3 and 4..7 are two runs of 4 consecutive tokens
-      *reinterpret_cast<uint32_t*>(&sm.codes[(8 * cb + i) * kTile + tok(0)]) = lo4;
-      *reinterpret_cast<uint32_t*>(&sm.codes[(8 * cb + i) * kTile + tok(4)]) = hi4;
+      sm.codes[codes_row(8 * cb + i) + tok(0) / 4] = lo4;
+      sm.codes[codes_row(8 * cb + i) + tok(4) / 4] = hi4;
     }
   }
   __syncthreads();
@@ -589,9 +613,9 @@ __device__ __forceinline__ void quantize_tile(RowPtr row_ptr, uint8_t* __restric
     for (int k = 0; k < 8; ++k) {
       const int wi = tid + kThreads * k;
       const int c = wi >> 4, g = (wi >> 2) & 3, m = wi & 3;
-      const uint8_t* row = &sm.codes[c * kTile];
-      const uint32_t a = *reinterpret_cast<const uint32_t*>(row + 32 * m + 4 * g);       // slots 0..3
-      const uint32_t b = *reinterpret_cast<const uint32_t*>(row + 32 * m + 16 + 4 * g);  // slots 4..7
+      const uint32_t* row = &sm.codes[codes_row(c)];
+      const uint32_t a = row[8 * m + g];       // slots 0..3
+      const uint32_t b = row[8 * m + 4 + g];   // slots 4..7
       uint32_t word = 0;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -607,13 +631,13 @@ __device__ __forceinline__ void quantize_tile(RowPtr row_ptr, uint8_t* __restric
     for (int k = 0; k < 4; ++k) {
       const int wi = tid + kThreads * k;
       const int c = wi >> 3, g = (wi >> 1) & 3, d = wi & 1;
-      const uint8_t* row = &sm.codes[c * kTile];
+      const uint32_t* row = &sm.codes[codes_row(c)];
       uint32_t word = 0;
 #pragma unroll
       for (int sl = 0; sl < 2; ++sl) {  // the two 32-token steps of this word
         const int s_ = 2 * d + sl;
-        const uint32_t a = *reinterpret_cast<const uint32_t*>(row + 32 * s_ + 4 * g);       // slots 0..3
-        const uint32_t b = *reinterpret_cast<const uint32_t*>(row + 32 * s_ + 16 + 4 * g);  // slots 4..7
+        const uint32_t a = row[8 * s_ + g];       // slots 0..3
+        const uint32_t b = row[8 * s_ + 4 + g];   // slots 4..7
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           // slot 2v -> low-half crumb i = 4 sl + v, slot 2v+1 -> high-half crumb 8 + i

@@ -38,9 +38,9 @@ def hipcc() -> str:
     return exe
 
 
-def _compile(sources, out: str, verbose: bool) -> str:
+def _compile(sources, out: str, verbose: bool, extra=()) -> str:
     tmp = out + ".tmp"
-    cmd = [hipcc(), *FLAGS, "-I", os.path.join(ROOT, "include"),
+    cmd = [hipcc(), *FLAGS, *extra, "-I", os.path.join(ROOT, "include"),
            *[os.path.join(CSRC, s) for s in sources], "-o", tmp]
     proc = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
@@ -59,6 +59,12 @@ def build(verbose: bool = False) -> str:
     _compile(SOURCES, LIB, verbose)
     _compile(PROBE_SOURCES, PROBE_LIB, verbose)
     return LIB
+
+
+def build_variant(out: str, extra_flags, verbose: bool = False) -> str:
+    """The same library built to `out` with extra hipcc flags (tests build instrumented
+    variants this way); the in-tree libkvarn.so is untouched."""
+    return _compile(SOURCES, out, verbose, extra=list(extra_flags))
 
 
 if __name__ == "__main__":

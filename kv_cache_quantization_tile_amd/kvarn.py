@@ -12,7 +12,9 @@ import os
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvarn.so")
+# KVARN_LIBRARY names another build of the same library (the host-ASan build of the ABI tests)
+_LIB_PATH = os.environ.get("KVARN_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                            "libkvarn.so")
 
 KIND_K = 0
 KIND_V = 1

@@ -27,7 +27,10 @@ Readings taken where the pages are silent (all listed with reasons in the design
     against the stored float16 values;
   * asymmetric RTN: zero = group min, scale = (max - min) / (2^b - 1), both stored float16
     (saturated to +-65504, as the normalizers are clipped to the float16 range),
-    code = round-half-even((y - zero) / scale) clipped to [0, 2^b - 1]; scale 0 => code 0.
+    code = round-half-even((y - zero) / scale) clipped to [0, 2^b - 1]; scale 0 => code 0;
+  * group size 64 (presets _g64, the finer setting of the pages' group-size knob): keys in
+    two groups of 64 consecutive tokens per channel, values in two groups of 64 consecutive
+    channels per token, each with its own scale and zero; normalization is unchanged.
 
 Parity status: every function below is pinned by tests that do not re-type its formula
 (closed forms, invariants, library routines, brute force, hand-derived byte patterns).
@@ -135,30 +138,44 @@ def store_meta(v: np.ndarray) -> np.ndarray:
     return to_fp16(np.clip(v, -FP16_MAX, FP16_MAX))
 
 
-def rtn_asym(y: np.ndarray, bits: int, axis: int):
+def rtn_asym(y: np.ndarray, bits: int, axis: int, group: int = 128):
     """Stage 4 ([README] "How KVarN works", stage 4): asymmetric round-to-nearest.
 
-    Groups run along `axis` (the group is every element sharing the other index).
+    Groups run along `axis`: `group` consecutive elements of it that share the other indices
+    (group = the axis length: one group per row or column; group 64: its two halves).
     Returns (codes uint8, scale16, zero16, u) where u is the unrounded code value in float64
-    (kept for the analysis of rounding ties).
+    (kept for the analysis of rounding ties). scale16 and zero16 drop the group axis when it
+    holds one group; with two groups (group 64) they are [..., 2, n] with the half first.
     """
     qmax = (1 << bits) - 1
-    mn = y.min(axis=axis, keepdims=True)
-    mx = y.max(axis=axis, keepdims=True)
+    ax = axis % y.ndim
+    ng = y.shape[ax] // group
+    if ng * group != y.shape[ax]:
+        raise ValueError("the group size must divide the axis")
+    yg = y.reshape(y.shape[:ax] + (ng, group) + y.shape[ax + 1:])   # (half, element) at ax
+    mn = yg.min(axis=ax + 1, keepdims=True)
+    mx = yg.max(axis=ax + 1, keepdims=True)
     scale16 = store_meta((mx - mn) / qmax)
     zero16 = store_meta(mn)
     sc = scale16.astype(np.float64)
     zr = zero16.astype(np.float64)
     live = sc > 0
-    u = np.where(live, (y - zr) / np.where(live, sc, 1.0), 0.0)
+    u = np.where(live, (yg - zr) / np.where(live, sc, 1.0), 0.0)
     codes = np.clip(np.rint(u), 0, qmax).astype(np.uint8)
-    codes = np.where(live, codes, 0).astype(np.uint8)
-    return codes, np.squeeze(scale16, axis), np.squeeze(zero16, axis), u
+    codes = np.where(live, codes, 0).astype(np.uint8).reshape(y.shape)
+    u = u.reshape(y.shape)
+    scale16 = np.squeeze(scale16, ax + 1)
+    zero16 = np.squeeze(zero16, ax + 1)
+    if ng == 1:
+        scale16, zero16 = np.squeeze(scale16, ax), np.squeeze(zero16, ax)
+    elif ax == y.ndim - 1:          # [..., n, halves] -> [..., halves, n]
+        scale16, zero16 = np.moveaxis(scale16, -1, -2), np.moveaxis(zero16, -1, -2)
+    return codes, scale16, zero16, u
 
 
 def quantize_tiles(x16: np.ndarray, kind: int, n_iters: int = 8, lossless: bool = False,
                    rotate_channels: bool = True, k_bits: int = 4, v_bits: int = 2,
-                   fmt: int = 1):
+                   fmt: int = 1, group: int = 128):
     """Quantize tiles end to end (stages 1-4 of [README] "How KVarN works").
 
     x16: [..., 128 channels, 128 tokens] float16 (stage 1: the raw tile, channels x tokens).
@@ -180,6 +197,10 @@ def quantize_tiles(x16: np.ndarray, kind: int, n_iters: int = 8, lossless: bool 
     Its dict then reports the folded-away normalizer as 1 (r for keys, s for values), 'scale'
     and 'zero' as the folded values and 'y' as Z, so that r s (zero + scale code) is still the
     reconstruction of Xr.
+    group: elements per quantization group (the preset's _g<G>): 128 = one group per channel
+    (keys) or token (values); 64 = keys in two 64-token groups per channel, values in two
+    64-channel groups per token (a finer scale grid, the pages' group-size knob). With 64,
+    'scale' and 'zero' are [..., 2, 128], half 0 first.
     """
     x = np.asarray(x16, dtype=np.float16).astype(np.float64)
     if x.shape[-2:] != (HEAD_DIM, TILE_TOKENS):
@@ -205,30 +226,42 @@ def quantize_tiles(x16: np.ndarray, kind: int, n_iters: int = 8, lossless: bool 
             out.update(s=np.ones_like(s16), y=y)
     elif fmt != 1:
         raise ValueError("fmt must be 1 or 2")
+    if group not in (128, 64):
+        raise ValueError("group must be 128 or 64")
     if kind == KIND_K:
-        codes, scale16, zero16, u = rtn_asym(y, k_bits, axis=-1)
+        codes, scale16, zero16, u = rtn_asym(y, k_bits, axis=-1, group=group)
     else:
-        codes, scale16, zero16, u = rtn_asym(y, v_bits, axis=-2)
+        codes, scale16, zero16, u = rtn_asym(y, v_bits, axis=-2, group=group)
     out.update(codes=codes, scale=scale16, zero=zero16, u=u)
     return out
 
 
 def dequantize_tiles(codes, r16, s16, scale16, zero16, kind: int,
-                     rotate_channels: bool = True) -> np.ndarray:
+                     rotate_channels: bool = True, group: int = 128) -> np.ndarray:
     """Inverse of quantize_tiles up to rounding: X_hat = H (r s^T * (zero + scale * code)).
 
     The scales are re-applied per channel for keys and per token for values
-    ([README] "How KVarN works", stage 4); H is symmetric and its own inverse.
-    Returns float64 [..., 128 c, 128 t]. rotate_channels=False inverts a tile quantized
-    without stage 2 (the ablation of quantize_tiles).
+    ([README] "How KVarN works", stage 4); H is symmetric and its own inverse. With group 64
+    the scale and zero are [..., 2, 128] and element (c, t) takes the half of t (keys) or of
+    c (values). Returns float64 [..., 128 c, 128 t]. rotate_channels=False inverts a tile
+    quantized without stage 2 (the ablation of quantize_tiles).
     """
     codes = np.asarray(codes, dtype=np.float64)
     sc = np.asarray(scale16, dtype=np.float64)
     zr = np.asarray(zero16, dtype=np.float64)
-    if kind == KIND_K:
-        yhat = zr[..., :, None] + sc[..., :, None] * codes
+    if group == 128:
+        sc_e = sc[..., :, None] if kind == KIND_K else sc[..., None, :]
+        zr_e = zr[..., :, None] if kind == KIND_K else zr[..., None, :]
+    elif group == 64:
+        if kind == KIND_K:     # [..., half, c] -> [..., c, t]: token t takes half t // 64
+            sc_e = np.repeat(np.swapaxes(sc, -1, -2), 64, axis=-1)
+            zr_e = np.repeat(np.swapaxes(zr, -1, -2), 64, axis=-1)
+        else:                  # [..., half, t] -> [..., c, t]: channel c takes half c // 64
+            sc_e = np.repeat(sc, 64, axis=-2)
+            zr_e = np.repeat(zr, 64, axis=-2)
     else:
-        yhat = zr[..., None, :] + sc[..., None, :] * codes
+        raise ValueError("group must be 128 or 64")
+    yhat = zr_e + sc_e * codes
     r = np.asarray(r16, dtype=np.float64)
     s = np.asarray(s16, dtype=np.float64)
     xr_hat = r[..., :, None] * s[..., None, :] * yhat
@@ -287,14 +320,24 @@ def v4_nibble_token(g: int, m: int, q: int) -> int:
 
 
 def _meta_bytes(r16, s16, scale16, zero16) -> bytes:
-    parts = [np.asarray(v, dtype="<f2").reshape(128) for v in (r16, s16, scale16, zero16)]
+    """r, s, then the scale vectors and the zero vectors (one each for group 128; half 0 then
+    half 1 for group 64), float16 little-endian."""
+    parts = [np.asarray(r16, dtype="<f2").reshape(128), np.asarray(s16, dtype="<f2").reshape(128),
+             np.asarray(scale16, dtype="<f2").reshape(-1), np.asarray(zero16, dtype="<f2").reshape(-1)]
     return b"".join(p.tobytes() for p in parts)
 
 
-# Format 2 (folded) of the same records: the code bytes, then three float16[128] vectors:
-# keys s, scale', zero' (per channel, of Z = Xr / s); values r, scale', zero' (per token, of
-# Z = Xr / r). The record is 256 bytes shorter.
+# Format 2 (folded) of the same records: the code bytes, then keys s, scale', zero' (per
+# channel, of Z = Xr / s); values r, scale', zero' (per token, of Z = Xr / r). One float16[128]
+# vector fewer.
+# Group 64 (presets _g64): two scale and two zero vectors (half 0 = tokens 0..63 of a key
+# channel / channels 0..63 of a value token, then half 1) in place of one each.
 META_BYTES = {1: 1024, 2: 768}
+
+
+def meta_bytes(fmt: int = 1, group: int = 128) -> int:
+    """Metadata bytes of a record: 256 per float16[128] vector."""
+    return 256 * ((2 if fmt == 1 else 1) + 2 * (128 // group))
 
 
 def code_bytes(kind: int, k_bits: int = 4, v_bits: int = 2) -> int:
@@ -302,24 +345,33 @@ def code_bytes(kind: int, k_bits: int = 4, v_bits: int = 2) -> int:
     return 8192 if bits == 4 else 4096
 
 
-def record_bytes(kind: int, k_bits: int = 4, v_bits: int = 2, fmt: int = 1) -> int:
-    return code_bytes(kind, k_bits, v_bits) + META_BYTES[fmt]
+def record_bytes(kind: int, k_bits: int = 4, v_bits: int = 2, fmt: int = 1, group: int = 128) -> int:
+    return code_bytes(kind, k_bits, v_bits) + meta_bytes(fmt, group)
+
+
+_LAYOUTS = {cb + meta_bytes(f, g): (bits, f, g) for bits, cb in ((4, 8192), (2, 4096))
+            for f in (1, 2) for g in (128, 64)}
 
 
 def record_layout(nbytes: int):
     """(code bits, format) of a record from its size: 9216 / 5120 bytes are format 1 with 4 /
-    2-bit codes, 8960 / 4864 format 2."""
-    return {9216: (4, 1), 5120: (2, 1), 8960: (4, 2), 4864: (2, 2)}[nbytes]
+    2-bit codes, 8960 / 4864 format 2; group 64 adds 512 bytes to either."""
+    return _LAYOUTS[nbytes][:2]
 
 
-def fold_record(rec1: bytes, kind: int) -> bytes:
+def record_group(nbytes: int) -> int:
+    """Group size (128 or 64) of a record from its size."""
+    return _LAYOUTS[nbytes][2]
+
+
+def fold_record(rec1: bytes, kind: int, group: int = 128) -> bytes:
     """Format-2 layout of a format-1 record whose folded-away normalizer is exactly 1 (the
     byte arrangement only: codes kept, the all-ones vector dropped)."""
-    cb = len(rec1) - 1024
-    m = np.frombuffer(rec1[cb:], dtype="<f2").reshape(4, 128)
-    keep = (1, 2, 3) if kind == KIND_K else (0, 2, 3)
-    assert np.all(m[0 if kind == KIND_K else 1] == 1.0)
-    return rec1[:cb] + b"".join(m[k].tobytes() for k in keep)
+    cb = len(rec1) - meta_bytes(1, group)
+    m = np.frombuffer(rec1[cb:], dtype="<f2").reshape(-1, 128)
+    drop = 0 if kind == KIND_K else 1
+    assert np.all(m[drop] == 1.0)
+    return rec1[:cb] + b"".join(m[k].tobytes() for k in range(m.shape[0]) if k != drop)
 
 
 def pack_k_record(codes, r16, s16, scale16, zero16) -> bytes:
@@ -377,72 +429,81 @@ def pack_v4_record(codes, r16, s16, scale16, zero16) -> bytes:
     return words.astype("<u4").tobytes() + _meta_bytes(r16, s16, scale16, zero16)
 
 
-def _unpack_meta(buf: np.ndarray, off: int):
-    m = buf[off:off + 1024].view("<f2").reshape(4, 128)
-    return m[0].copy(), m[1].copy(), m[2].copy(), m[3].copy()
+def _unpack_meta(buf: np.ndarray, off: int, group: int = 128):
+    ng = 128 // group
+    m = buf[off:off + meta_bytes(1, group)].view("<f2").reshape(2 + 2 * ng, 128)
+    sc, zr = m[2:2 + ng].copy(), m[2 + ng:].copy()
+    if ng == 1:
+        sc, zr = sc[0], zr[0]
+    return m[0].copy(), m[1].copy(), sc, zr
 
 
-def unpack_k_record(rec) -> dict:
+def unpack_k_record(rec, group: int = 128) -> dict:
     buf = np.frombuffer(bytes(rec), dtype=np.uint8)
-    assert buf.size == K_RECORD_BYTES
+    assert buf.size == 8192 + meta_bytes(1, group)
     words = buf[:8192].view("<u4").reshape(128, 16)
     codes = np.zeros((128, 128), dtype=np.uint8)
     for p in range(8):
         nib = (words >> np.uint32(4 * p)) & np.uint32(0xF)        # [t, j]
         for j in range(16):
             codes[8 * j + K_NIBBLE_CHANNEL[p], :] = nib[:, j]
-    r, s, sc, zr = _unpack_meta(buf, 8192)
+    r, s, sc, zr = _unpack_meta(buf, 8192, group)
     return dict(codes=codes, r=r, s=s, scale=sc, zero=zr)
 
 
-def unpack_k2_record(rec) -> dict:
+def unpack_k2_record(rec, group: int = 128) -> dict:
     buf = np.frombuffer(bytes(rec), dtype=np.uint8)
-    assert buf.size == K2_RECORD_BYTES
+    assert buf.size == 4096 + meta_bytes(1, group)
     words = buf[:4096].view("<u4").reshape(128, 4, 2)                  # [t, g, d]
     codes = np.zeros((128, 128), dtype=np.uint8)
     for g in range(4):
         for d in range(2):
             for p in range(16):
                 codes[k2_crumb_channel(g, d, p), :] = (words[:, g, d] >> np.uint32(2 * p)) & np.uint32(3)
-    r, s, sc, zr = _unpack_meta(buf, 4096)
+    r, s, sc, zr = _unpack_meta(buf, 4096, group)
     return dict(codes=codes, r=r, s=s, scale=sc, zero=zr)
 
 
-def unpack_v4_record(rec) -> dict:
+def unpack_v4_record(rec, group: int = 128) -> dict:
     buf = np.frombuffer(bytes(rec), dtype=np.uint8)
-    assert buf.size == V4_RECORD_BYTES
+    assert buf.size == 8192 + meta_bytes(1, group)
     words = buf[:8192].view("<u4").reshape(128, 4, 4)                  # [c, g, m]
     codes = np.zeros((128, 128), dtype=np.uint8)
     for g in range(4):
         for m in range(4):
             for q in range(8):
                 codes[:, v4_nibble_token(g, m, q)] = (words[:, g, m] >> np.uint32(4 * q)) & np.uint32(15)
-    r, s, sc, zr = _unpack_meta(buf, 8192)
+    r, s, sc, zr = _unpack_meta(buf, 8192, group)
     return dict(codes=codes, r=r, s=s, scale=sc, zero=zr)
 
 
-def unpack_record(rec, kind: int, k_bits: int = 4, v_bits: int = 2, fmt: int = 1) -> dict:
+def unpack_record(rec, kind: int, k_bits: int = 4, v_bits: int = 2, fmt: int = 1,
+                  group: int = 128) -> dict:
     """The record of `kind` for the preset with k_bits-bit keys and v_bits-bit values, in
-    record format fmt (format 2 reports the folded-away normalizer as ones)."""
+    record format fmt (format 2 reports the folded-away normalizer as ones) and group size
+    `group` (64: scale and zero are [2, 128])."""
     rec = bytes(rec)
     if fmt == 2:
         cb = code_bytes(kind, k_bits, v_bits)
-        assert len(rec) == cb + META_BYTES[2]
-        m = np.frombuffer(rec[cb:], dtype="<f2").reshape(3, 128)
+        assert len(rec) == cb + meta_bytes(2, group)
+        m = np.frombuffer(rec[cb:], dtype="<f2").reshape(-1, 128)
+        ng = 128 // group
         one = np.ones(128, dtype=np.float16)
         r16, s16 = (one, m[0]) if kind == KIND_K else (m[0], one)
-        rec = rec[:cb] + _meta_bytes(r16, s16, m[1], m[2])
+        rec = rec[:cb] + _meta_bytes(r16, s16, m[1:1 + ng], m[1 + ng:])
     if kind == KIND_V:
-        return unpack_v_record(rec) if v_bits == 2 else unpack_v4_record(rec)
-    return unpack_k_record(rec) if k_bits == 4 else unpack_k2_record(rec)
+        return unpack_v_record(rec, group) if v_bits == 2 else unpack_v4_record(rec, group)
+    return unpack_k_record(rec, group) if k_bits == 4 else unpack_k2_record(rec, group)
 
 
 def pack_record(kind: int, codes, r16, s16, scale16, zero16, k_bits: int = 4,
-                v_bits: int = 2, fmt: int = 1) -> bytes:
+                v_bits: int = 2, fmt: int = 1, group: int = 128) -> bytes:
     if kind == KIND_V:
         pack = pack_v_record if v_bits == 2 else pack_v4_record
     else:
         pack = pack_k_record if k_bits == 4 else pack_k2_record
+    if np.asarray(scale16).size != 128 * (128 // group):
+        raise ValueError("scale / zero do not match the group size")
     if fmt == 1:
         return pack(codes, r16, s16, scale16, zero16)
     if fmt != 2:
@@ -450,19 +511,19 @@ def pack_record(kind: int, codes, r16, s16, scale16, zero16, k_bits: int = 4,
     one = np.ones(128, dtype=np.float16)
     rec1 = pack(codes, one if kind == KIND_K else r16, s16 if kind == KIND_K else one,
                 scale16, zero16)
-    return fold_record(rec1, kind)
+    return fold_record(rec1, kind, group)
 
 
-def unpack_v_record(rec) -> dict:
+def unpack_v_record(rec, group: int = 128) -> dict:
     buf = np.frombuffer(bytes(rec), dtype=np.uint8)
-    assert buf.size == V_RECORD_BYTES
+    assert buf.size == 4096 + meta_bytes(1, group)
     words = buf[:4096].view("<u4").reshape(128, 4, 2)
     codes = np.zeros((128, 128), dtype=np.uint8)
     for g in range(4):
         for d in range(2):
             for p in range(16):
                 codes[:, v_crumb_token(g, d, p)] = (words[:, g, d] >> np.uint32(2 * p)) & np.uint32(3)
-    r, s, sc, zr = _unpack_meta(buf, 4096)
+    r, s, sc, zr = _unpack_meta(buf, 4096, group)
     return dict(codes=codes, r=r, s=s, scale=sc, zero=zr)
 
 
@@ -481,20 +542,22 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, softmax_scale: float)
     return (p / p.sum()) @ np.asarray(v, np.float64)
 
 
-def dequantize_k_record(rec, k_bits: int = 4, fmt: int = 1) -> np.ndarray:
+def dequantize_k_record(rec, k_bits: int = 4, fmt: int = 1, group: int = 128) -> np.ndarray:
     """Unpack one K page record and return the dequantized keys [128 tokens, 128 channels]."""
-    d = unpack_record(rec, KIND_K, k_bits=k_bits, fmt=fmt)
-    return dequantize_tiles(d["codes"], d["r"], d["s"], d["scale"], d["zero"], KIND_K).T
+    d = unpack_record(rec, KIND_K, k_bits=k_bits, fmt=fmt, group=group)
+    return dequantize_tiles(d["codes"], d["r"], d["s"], d["scale"], d["zero"], KIND_K,
+                            group=group).T
 
 
-def dequantize_v_record(rec, v_bits: int = 2, fmt: int = 1) -> np.ndarray:
-    d = unpack_record(rec, KIND_V, v_bits=v_bits, fmt=fmt)
-    return dequantize_tiles(d["codes"], d["r"], d["s"], d["scale"], d["zero"], KIND_V).T
+def dequantize_v_record(rec, v_bits: int = 2, fmt: int = 1, group: int = 128) -> np.ndarray:
+    d = unpack_record(rec, KIND_V, v_bits=v_bits, fmt=fmt, group=group)
+    return dequantize_tiles(d["codes"], d["r"], d["s"], d["scale"], d["zero"], KIND_V,
+                            group=group).T
 
 
 def decode_attention_row(q_row, k_pages, v_pages, k_tail=None, v_tail=None,
                          softmax_scale: float = 1.0 / np.sqrt(HEAD_DIM), k_bits: int = 4,
-                         v_bits: int = 2, fmt: int = 1) -> np.ndarray:
+                         v_bits: int = 2, fmt: int = 1, group: int = 128) -> np.ndarray:
     """Decode attention of one query row over one KV head's cache.
 
     k_pages / v_pages: lists of page records (bytes) of that KV head, in block-table order
@@ -503,8 +566,8 @@ def decode_attention_row(q_row, k_pages, v_pages, k_tail=None, v_tail=None,
     k_tail / v_tail: [n_tail, 128] float16 tokens past the last full page (raw, exact).
     Returns float64 [128].
     """
-    ks = [dequantize_k_record(p, k_bits, fmt) for p in k_pages]
-    vs = [dequantize_v_record(p, v_bits, fmt) for p in v_pages]
+    ks = [dequantize_k_record(p, k_bits, fmt, group) for p in k_pages]
+    vs = [dequantize_v_record(p, v_bits, fmt, group) for p in v_pages]
     if k_tail is not None and len(k_tail):
         ks.append(np.asarray(k_tail, np.float16).astype(np.float64))
         vs.append(np.asarray(v_tail, np.float16).astype(np.float64))

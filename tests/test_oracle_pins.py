@@ -596,3 +596,147 @@ def test_folded_format_roundtrip_and_fold_identity(kind, kb, vb):
     ea = np.linalg.norm(O.dequantize_tiles(a["codes"], a["r"], a["s"], a["scale"], a["zero"], kind) - x)
     eb = np.linalg.norm(O.dequantize_tiles(b["codes"], b["r"], b["s"], b["scale"], b["zero"], kind) - x)
     assert abs(eb - ea) <= 0.02 * ea
+
+
+# ----------------------------------------------------------------------------- group size 64
+
+
+G64_PRESETS = [(O.KIND_K, 4, 2), (O.KIND_V, 4, 2), (O.KIND_K, 2, 2), (O.KIND_V, 4, 4)]
+
+
+def test_g64_metadata_byte_patterns():
+    """Group-64 metadata: vector order, offsets and float16 bit patterns derived by hand
+    (tests/golden/format_g64_patterns.json), every preset width and both formats."""
+    g = json.load(open(os.path.join(GOLD, "format_g64_patterns.json")))
+    val = g["values"]
+    r16, s16 = np.full(128, val["r"], np.float16), np.full(128, val["s"], np.float16)
+    sc = np.stack([np.full(128, val["scale0"]), np.full(128, val["scale1"])]).astype(np.float16)
+    zr = np.stack([np.full(128, val["zero0"]), np.full(128, val["zero1"])]).astype(np.float16)
+    for case in g["cases"]:
+        kind = O.KIND_K if case["kind"] == "K" else O.KIND_V
+        kb, vb, fmt = case["k_bits"], case["v_bits"], case["fmt"]
+        one = np.ones(128, np.float16)
+        rr, ss = (r16, s16) if fmt == 1 else ((one, s16) if kind == O.KIND_K else (r16, one))
+        rec = O.pack_record(kind, np.zeros((128, 128), np.uint8), rr, ss, sc, zr, kb, vb,
+                            fmt=fmt, group=64)
+        assert len(rec) == case["record_bytes"] == O.record_bytes(kind, kb, vb, fmt, 64)
+        bits = kb if kind == O.KIND_K else vb
+        assert O.record_layout(len(rec)) == (bits, fmt) and O.record_group(len(rec)) == 64
+        meta = rec[case["code_bytes"]:]
+        assert len(meta) == 256 * len(case["vectors"])
+        for off, name, hexpat in case["vectors"]:
+            word = int(hexpat, 16)
+            want = bytes([word & 0xFF, word >> 8]) * 128
+            assert meta[off:off + 256] == want, (case["kind"], fmt, name)
+
+
+def test_g64_record_sizes_are_distinct():
+    """Every (code width, format, group) record size is distinct, so a pool's record size
+    names its layout: 4-bit 9216 / 8960 / 9728 / 9472, 2-bit 5120 / 4864 / 5632 / 5376."""
+    sizes = {}
+    for bits in (4, 2):
+        for fmt in (1, 2):
+            for grp in (128, 64):
+                n = O.record_bytes(O.KIND_K, bits, 2, fmt, grp)
+                assert n not in sizes
+                sizes[n] = (bits, fmt, grp)
+                assert O.record_layout(n) == (bits, fmt) and O.record_group(n) == grp
+    assert sorted(sizes) == [4864, 5120, 5376, 5632, 8960, 9216, 9472, 9728]
+
+
+@pytest.mark.parametrize("kind", [O.KIND_K, O.KIND_V])
+def test_g64_dequantize_hand_values(kind):
+    """Dequantization with two groups, values computed by hand: codes 1, r = 1, s = 2,
+    scale 0.5 / 0.25 and zero -1 / -2 for halves 0 / 1, no rotation: x = r s (zero + scale)
+    = 2 (-1 + 0.5) = -1 in half 0 and 2 (-2 + 0.25) = -3.5 in half 1 (tokens 64.. of every key
+    channel; channels 64.. of every value token)."""
+    codes = np.ones((128, 128), np.uint8)
+    sc = np.stack([np.full(128, 0.5), np.full(128, 0.25)]).astype(np.float16)
+    zr = np.stack([np.full(128, -1.0), np.full(128, -2.0)]).astype(np.float16)
+    x = O.dequantize_tiles(codes, np.ones(128, np.float16), np.full(128, 2.0, np.float16), sc, zr,
+                           kind, rotate_channels=False, group=64)       # [c, t]
+    if kind == O.KIND_K:
+        assert np.all(x[:, :64] == -1.0) and np.all(x[:, 64:] == -3.5)
+    else:
+        assert np.all(x[:64, :] == -1.0) and np.all(x[64:, :] == -3.5)
+
+
+@pytest.mark.parametrize("axis", [-1, -2])
+def test_g64_reduces_to_g128_when_halves_share_extremes(axis):
+    """A special case that reduces to the 128-element groups: when each half of a group holds
+    the group's minimum and its maximum, both halves get the full group's scale and zero, and
+    every code equals the 128-element code."""
+    y = RNG.normal(size=(4, 128, 128))
+    yt = np.moveaxis(y, axis, -1)            # the group axis last (a view)
+    mn, mx = yt.min(-1), yt.max(-1)
+    for half in (0, 64):
+        yt[..., half] = mn - 1.0
+        yt[..., half + 1] = mx + 1.0
+    c1, s1, z1, _ = O.rtn_asym(y, 4, axis, group=128)
+    c2, s2, z2, _ = O.rtn_asym(y, 4, axis, group=64)
+    assert np.array_equal(c1, c2)
+    assert s2.shape == (4, 2, 128) and np.array_equal(s2[:, 0], s1) and np.array_equal(s2[:, 1], s1)
+    assert np.array_equal(z2[:, 0], z1) and np.array_equal(z2[:, 1], z1)
+
+
+@pytest.mark.parametrize("kind", [O.KIND_K, O.KIND_V])
+def test_g64_rtn_error_bound_per_half(kind):
+    """Every element is reconstructed within half a step of its own half's scale (plus the
+    float16 roundings of that half's scale and zero): the halves are cut here by slicing,
+    not by the oracle's reshape, so a swapped or shifted half fails the bound."""
+    y = RNG.standard_t(3, (3, 128, 128)) * RNG.lognormal(0, 1, (3, 1, 128))
+    bits = 4 if kind == O.KIND_K else 2
+    axis = -1 if kind == O.KIND_K else -2
+    codes, sc, zr, _ = O.rtn_asym(y, bits, axis, group=64)
+    qmax = (1 << bits) - 1
+    for h in (0, 1):
+        sl = slice(64 * h, 64 * h + 64)
+        yh = y[..., :, sl] if kind == O.KIND_K else y[..., sl, :]
+        ch = codes[..., :, sl] if kind == O.KIND_K else codes[..., sl, :]
+        s_h = sc[:, h].astype(np.float64)
+        z_h = zr[:, h].astype(np.float64)
+        mn, mx = yh.min(axis), yh.max(axis)
+        e = lambda v: v[..., :, None] if kind == O.KIND_K else v[..., None, :]
+        err = np.abs(yh - (e(z_h) + e(s_h) * ch))
+        bound = 0.5 * s_h + qmax * np.abs(s_h - (mx - mn) / qmax) + np.abs(z_h - mn) + 1e-12
+        assert np.all(err <= e(bound)), h
+
+
+def test_g64_half_assignment_through_the_pipeline():
+    """A rotated tile with one large entry at rotated channel 3, token 5 (built as X = H E, so
+    that H X = E; H is its own inverse): after normalization that entry still dominates its
+    groups, so with group 64 the key channel 3 scale of half 0 (tokens 0..63) and the value
+    token 5 scale of half 0 (channels 0..63) are several times the other half's."""
+    e = RNG.normal(size=(128, 128))
+    e[3, 5] = 60.0
+    x = (O.hadamard(128) @ e).astype(np.float16)
+    k = O.quantize_tiles(x, O.KIND_K, 8, group=64)
+    v = O.quantize_tiles(x, O.KIND_V, 8, group=64)
+    sk = k["scale"].astype(np.float64)
+    sv = v["scale"].astype(np.float64)
+    assert sk[0, 3] > 3 * sk[1, 3]
+    assert sv[0, 5] > 3 * sv[1, 5]
+    # elsewhere the halves are alike (both a draw of the same distribution)
+    others = np.delete(np.arange(128), [3])
+    assert np.median(sk[0, others] / sk[1, others]) == pytest.approx(1.0, rel=0.2)
+
+
+@pytest.mark.parametrize("kind,kb,vb", G64_PRESETS)
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_g64_roundtrip_and_finer_error(kind, kb, vb, fmt):
+    """Group-64 records pack and unpack losslessly, and the finer groups do not reconstruct
+    worse than 128-element groups (their range is a subset of the full group's)."""
+    x = (RNG.standard_t(4, (6, 128, 128)) * RNG.lognormal(0, 1, (6, 128, 1))).astype(np.float16)
+    a = O.quantize_tiles(x, kind, 8, k_bits=kb, v_bits=vb, fmt=fmt, group=128)
+    b = O.quantize_tiles(x, kind, 8, k_bits=kb, v_bits=vb, fmt=fmt, group=64)
+    assert b["scale"].shape == (6, 2, 128) and np.array_equal(b["r"], a["r"])
+    for i in range(x.shape[0]):
+        rec = O.pack_record(kind, b["codes"][i], b["r"][i], b["s"][i], b["scale"][i],
+                            b["zero"][i], kb, vb, fmt=fmt, group=64)
+        assert len(rec) == O.record_bytes(kind, kb, vb, fmt, 64)
+        d = O.unpack_record(rec, kind, kb, vb, fmt=fmt, group=64)
+        for key in ("codes", "r", "s", "scale", "zero"):
+            assert np.array_equal(d[key], b[key][i]), key
+    xa = O.dequantize_tiles(a["codes"], a["r"], a["s"], a["scale"], a["zero"], kind)
+    xb = O.dequantize_tiles(b["codes"], b["r"], b["s"], b["scale"], b["zero"], kind, group=64)
+    assert np.linalg.norm(xb - x) <= np.linalg.norm(xa - x)

@@ -10,7 +10,10 @@
  * (preset "kvarn_k4v2_g128", README "Quick start"; 128 = tile / page size). The presets
  * "kvarn_k2v2_g128" (2-bit keys; the pages report 2-bit results) and "kvarn_k4v4_g128"
  * (4-bit values; another key / value width choice of the same naming, README "How KVarN
- * works", the preset paragraph) are also implemented.
+ * works", the preset paragraph) are also implemented, and each of the three with group
+ * size 64 ("_g64": keys in two 64-token groups per channel, values in two 64-channel groups
+ * per token, each group with its own scale and zero; the finer setting of the group-size
+ * knob the quick-start blog's configuration example describes).
  * The read path is decode attention that dequantizes the tiles on the fly: the query is
  * rotated by H for QK and the accumulated values are rotated back by H^T.
  *
@@ -62,9 +65,9 @@ typedef enum {
 
 typedef enum { KVARN_K = 0, KVARN_V = 1 } kvarn_kind;
 
-/* Quantizer parameters. Only head_dim = tile_tokens = group = 128 with (k_bits, v_bits)
- * = (4, 2), (2, 2) or (4, 4) are implemented (README "Quick start": other page sizes are
- * not yet supported). sinkhorn_iters is the number of (column step, row step) pairs of the
+/* Quantizer parameters. Only head_dim = tile_tokens = 128, group = 128 or 64, with
+ * (k_bits, v_bits) = (4, 2), (2, 2) or (4, 4) are implemented (README "Quick start": other
+ * page sizes are not yet supported). sinkhorn_iters is the number of (column step, row step) pairs of the
  * normalization (README "How KVarN works", stage 3); 0..64 accepted. format selects the page
  * record layout (KVARN_FORMAT_SEPARATE or KVARN_FORMAT_FOLDED, see kvarn_page_bytes);
  * kvarn_params_from_dtype sets KVARN_FORMAT_SEPARATE, anything else is INVALID_ARG. Every
@@ -89,7 +92,7 @@ KVARN_API const char* kvarn_status_str(kvarn_status status);
 /* Parse a kv-cache dtype string of the form "kvarn_k<kb>v<vb>_g<group>" (README "Quick
  * start": kv_cache_dtype="kvarn_k4v2_g128") into params, with the given iteration count.
  * Returns INVALID_ARG for a malformed string or NULL pointer, UNSUPPORTED for a well-formed
- * preset other than k4v2_g128, k2v2_g128 and k4v4_g128. `out_host` is written only on
+ * preset other than k4v2, k2v2 and k4v4 with group 128 or 64. `out_host` is written only on
  * success. */
 KVARN_API kvarn_status kvarn_params_from_dtype(const char* kv_cache_dtype, int32_t sinkhorn_iters,
                                      kvarn_params* out_host);
@@ -99,8 +102,9 @@ KVARN_API kvarn_status kvarn_params_check(const kvarn_params* params);
 
 /* Bytes of one page record (one 128-token tile of one KV head) of the given kind: format
  * KVARN_FORMAT_SEPARATE 9216 for 4-bit keys or values, 5120 for 2-bit ones; format
- * KVARN_FORMAT_FOLDED 8960 and 4864; 0 if params are invalid or unsupported. Every pool
- * passed with these params must use this record size.
+ * KVARN_FORMAT_FOLDED 8960 and 4864; group 64 adds 512 to each (9728, 5632, 9472, 5376);
+ * 0 if params are invalid or unsupported. Every pool passed with these params must use
+ * this record size.
  *
  * Page format 1, KVARN_FORMAT_SEPARATE (little-endian):
  *   K record: bytes [0, 8192) are 4-bit codes, token-major: token t owns bytes
@@ -133,7 +137,14 @@ KVARN_API kvarn_status kvarn_params_check(const kvarn_params* params);
  *     Xr[c][t] = s[t] * (zero'[c] + scale'[c] * code[c][t]);
  *   V record: r (per channel), scale'[t], zero'[t] of Z = Xr / r per token, so
  *     Xr[c][t] = r[c] * (zero'[t] + scale'[t] * code[c][t]).
- * 256 B fewer per record (3.6% of a k4v2 page pair). */
+ * 256 B fewer per record (3.6% of a k4v2 page pair).
+ *
+ * Group 64 (params.group = 64), either format: in place of one scale and one zero vector,
+ * scale of half 0, scale of half 1, zero of half 0, zero of half 1 (each float16[128]), where
+ * half h of a key channel c is tokens [64h, 64h + 64) and half h of a value token t is
+ * channels [64h, 64h + 64): format 1 is codes, r, s, scale0, scale1, zero0, zero1; format 2
+ * is codes, s (K) or r (V), scale'0, scale'1, zero'0, zero'1. Element (c, t) takes
+ * g = (c, t / 64) for K and (t, c / 64) for V in the reconstruction above. */
 KVARN_API size_t kvarn_page_bytes(const kvarn_params* params, kvarn_kind kind);
 
 /* Quantize tiles into a page pool (README "How KVarN works", stages 1-4).

@@ -54,10 +54,12 @@ kvarn_status kvarn_params_check(const kvarn_params* p) {
     return KVARN_ERR_INVALID_ARG;
   if (p->format != KVARN_FORMAT_SEPARATE && p->format != KVARN_FORMAT_FOLDED)
     return KVARN_ERR_INVALID_ARG;
-  // presets kvarn_k4v2_g128 (released), kvarn_k2v2_g128 and kvarn_k4v4_g128
+  // presets kvarn_k4v2_g128 (released), kvarn_k2v2_g128 and kvarn_k4v4_g128, each also with
+  // group 64 (_g64)
   const bool preset = (p->k_bits == 4 && p->v_bits == 2) || (p->k_bits == 2 && p->v_bits == 2) ||
                       (p->k_bits == 4 && p->v_bits == 4);
-  if (p->head_dim != 128 || p->tile_tokens != 128 || p->group != 128 || !preset)
+  if (p->head_dim != 128 || p->tile_tokens != 128 || (p->group != 128 && p->group != 64) ||
+      !preset)
     return KVARN_ERR_UNSUPPORTED;
   return KVARN_OK;
 }
@@ -92,8 +94,10 @@ kvarn_status kvarn_params_from_dtype(const char* dtype, int32_t sinkhorn_iters, 
 
 size_t kvarn_page_bytes(const kvarn_params* p, kvarn_kind kind) {
   if (kvarn_params_check(p) != KVARN_OK) return 0;
-  // codes, then 4 (separate) or 3 (folded) float16 vectors of 128
-  const size_t meta = p->format == KVARN_FORMAT_SEPARATE ? 1024 : 768;
+  // codes, then float16 vectors of 128: the normalizers (2 separate, 1 folded), then one
+  // scale and one zero vector per group of a key channel / value token (1 for group 128, 2
+  // for group 64)
+  const size_t meta = 256 * ((p->format == KVARN_FORMAT_SEPARATE ? 2 : 1) + 2 * (128 / p->group));
   if (kind == KVARN_K) return (p->k_bits == 4 ? 8192 : 4096) + meta;
   if (kind == KVARN_V) return (p->v_bits == 4 ? 8192 : 4096) + meta;
   return 0;
@@ -117,7 +121,7 @@ kvarn_status kvarn_quantize_tiles(const kvarn_params* params, kvarn_kind kind, c
       (src_head_stride % 8) != 0)
     return KVARN_ERR_INVALID_ARG;
   return launch_status(kvarn::launch_quantize_tiles(
-      int(kind), params->k_bits, params->v_bits, params->format, src, src_token_stride, src_head_stride, src_num_tokens, tile_src_token,
+      int(kind), params->k_bits, params->v_bits, params->format, params->group, src, src_token_stride, src_head_stride, src_num_tokens, tile_src_token,
       tile_dst_page, n_tiles, num_kv_heads, pool, pool_num_pages, params->sinkhorn_iters,
       static_cast<hipStream_t>(stream)));
 }
@@ -140,7 +144,7 @@ kvarn_status kvarn_quantize_kv_tiles(const kvarn_params* params, const void* k_s
       (src_token_stride % 8) != 0 || (src_head_stride % 8) != 0)
     return KVARN_ERR_INVALID_ARG;
   return launch_status(kvarn::launch_quantize_kv(
-      params->k_bits, params->v_bits, params->format,
+      params->k_bits, params->v_bits, params->format, params->group,
       k_src, v_src, src_token_stride, src_head_stride, src_num_tokens, tile_src_token,
       tile_dst_page, n_tiles, num_kv_heads, k_pool, v_pool, pool_num_pages,
       params->sinkhorn_iters, static_cast<hipStream_t>(stream)));
@@ -157,7 +161,7 @@ kvarn_status kvarn_dequantize_tiles(const kvarn_params* params, kvarn_kind kind,
   if (n_tiles == 0) return KVARN_OK;
   if (!pool || !pages || !dst) return KVARN_ERR_INVALID_ARG;
   if (!aligned16(pool) || !aligned16(dst)) return KVARN_ERR_INVALID_ARG;
-  return launch_status(kvarn::launch_dequantize_tiles(int(kind), params->k_bits, params->v_bits, params->format, pool, pool_num_pages, pages,
+  return launch_status(kvarn::launch_dequantize_tiles(int(kind), params->k_bits, params->v_bits, params->format, params->group, pool, pool_num_pages, pages,
                                                       n_tiles, num_kv_heads, dst,
                                                       static_cast<hipStream_t>(stream)));
 }
@@ -179,7 +183,7 @@ kvarn_status kvarn_append_tokens(const kvarn_params* params, const void* k_new, 
       !aligned16(k_pool) || !aligned16(v_pool))
     return KVARN_ERR_INVALID_ARG;
   return launch_status(kvarn::launch_append_tokens(
-      params->k_bits, params->v_bits, params->format,
+      params->k_bits, params->v_bits, params->format, params->group,
       k_new, v_new, batch, num_kv_heads, seq_lens, k_tail, v_tail, block_table,
       block_table_stride, k_pool, v_pool, pool_num_pages, params->sinkhorn_iters,
       static_cast<hipStream_t>(stream)));
@@ -206,7 +210,7 @@ kvarn_status kvarn_write_tokens(const kvarn_params* params, const void* k_new, c
       !aligned16(k_pool) || !aligned16(v_pool))
     return KVARN_ERR_INVALID_ARG;
   return launch_status(kvarn::launch_write_tokens(
-      params->k_bits, params->v_bits, params->format,
+      params->k_bits, params->v_bits, params->format, params->group,
       k_new, v_new, total_new_tokens, cu_new, max_new_tokens, batch, num_kv_heads, seq_lens, k_tail, v_tail,
       block_table, block_table_stride, k_pool, v_pool, pool_num_pages, params->sinkhorn_iters,
       static_cast<hipStream_t>(stream)));
@@ -297,7 +301,7 @@ kvarn_status kvarn_decode_attention(const kvarn_params* params, const void* q, i
   if (workspace_bytes < kvarn::decode_workspace_bytes(batch, num_q_heads, num_kv_heads, max_seq_len))
     return KVARN_ERR_WORKSPACE;
   return launch_status(kvarn::launch_decode(
-      params->k_bits, params->v_bits, params->format, q, batch, num_q_heads, num_kv_heads, k_pool, v_pool, pool_num_pages, block_table,
+      params->k_bits, params->v_bits, params->format, params->group, q, batch, num_q_heads, num_kv_heads, k_pool, v_pool, pool_num_pages, block_table,
       block_table_stride, seq_lens, max_seq_len, nullptr, batch, k_tail, v_tail, softmax_scale,
       workspace, out, static_cast<hipStream_t>(stream)));
 }
@@ -332,7 +336,7 @@ kvarn_status kvarn_decode_attention_noalloc(const kvarn_params* params, const vo
   void* ws = nullptr;
   if (kvarn::decode_scratch(&ws) != hipSuccess) return KVARN_ERR_HIP;
   return launch_status(kvarn::launch_decode(
-      params->k_bits, params->v_bits, params->format, q, batch, num_q_heads, num_kv_heads, k_pool, v_pool,
+      params->k_bits, params->v_bits, params->format, params->group, q, batch, num_q_heads, num_kv_heads, k_pool, v_pool,
       pool_num_pages, block_table, block_table_stride, seq_lens, max_seq_len, nullptr, batch,
       k_tail, v_tail, softmax_scale, ws, out, s));
 }
@@ -370,7 +374,7 @@ kvarn_status kvarn_chunk_attention(const kvarn_params* params, const void* q, in
   if (workspace_bytes < kvarn::chunk_workspace_bytes(total_q, num_q_heads, num_kv_heads, max_seq_len))
     return KVARN_ERR_WORKSPACE;
   return launch_status(kvarn::launch_decode(
-      params->k_bits, params->v_bits, params->format, q, total_q, num_q_heads, num_kv_heads, k_pool, v_pool, pool_num_pages, block_table,
+      params->k_bits, params->v_bits, params->format, params->group, q, total_q, num_q_heads, num_kv_heads, k_pool, v_pool, pool_num_pages, block_table,
       block_table_stride, seq_lens, max_seq_len, cu_q, batch, k_tail, v_tail, softmax_scale,
       workspace, out, static_cast<hipStream_t>(stream)));
 }

@@ -38,11 +38,12 @@
 namespace kvarn {
 namespace {
 
+template <int NG>
 struct DecodeSmem {
   float m[4][8];
   float l[4][8];
   float acc[4][8][kDim];
-  WaveMeta meta[4];
+  WaveMeta<NG> meta[4];
   int32_t pref[kMaxBalancedRows + 1];   // balanced layout: full pages before each sequence
   int32_t wsum[4];
 };
@@ -59,7 +60,7 @@ struct DecodeSmem {
 // i + (b Hkv + g). Ragged lengths then cost no idle waves. Workgroup 0 also stores the page
 // prefix sums for the merge. Workgroups n_page_wg.. are the tails, one per (b, g).
 // KB, VB: key and value code widths; AUX: cache policy of the page loads.
-template <int KB, int VB, int FMT, int AUX, bool BAL>
+template <int KB, int VB, int FMT, int NG, int AUX, bool BAL>
 __global__ void __launch_bounds__(kThreads)
 decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t num_kv_heads,
                     const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
@@ -69,7 +70,7 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
                     int32_t n_splits, int32_t split_base, const __half* __restrict__ k_tail,
                     const __half* __restrict__ v_tail, float tail_qscale,
                     float* __restrict__ ws, int32_t n_page_wg) {
-  __shared__ DecodeSmem sm;
+  __shared__ DecodeSmem<NG> sm;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int G = num_q_heads / num_kv_heads;
   // split layout: KV heads fastest, so that the workgroups dealt to the 8 XCDs round-robin in
@@ -130,7 +131,7 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[bb][i] = 0.f;
 
-  WaveMeta& wm = sm.meta[w];
+  WaveMeta<NG>& wm = sm.meta[w];
   // key channel 2l + j: 4-bit keys: nibble pair v = l % 4 -> b = 2 (even v) or 6; 2-bit keys:
   // crumb pair parity l % 2 -> b = 8 or 6; value token 2l + j: C row (2l + j) % 4 -> pair
   // parity -> 2-bit values: b = 8 (rows 0,1) or 6 (rows 2,3); 4-bit values: b = 2 or 6
@@ -159,13 +160,13 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
   // without touching memory, so the prefetches below need no branch.
   auto krec_of = [&](int64_t rec) {
     const uint32_t r = __builtin_amdgcn_readfirstlane(uint32_t(rec < 0 ? 0 : rec));
-    return record_rsrc(uniform_ptr(k_pool + uint64_t(r) * uint32_t(key_record<KB, FMT>())),
-                       rec < 0 ? 0 : key_record<KB, FMT>());
+    return record_rsrc(uniform_ptr(k_pool + uint64_t(r) * uint32_t(key_record<KB, FMT, NG>())),
+                       rec < 0 ? 0 : key_record<KB, FMT, NG>());
   };
   auto vrec_of = [&](int64_t rec) {
     const uint32_t r = __builtin_amdgcn_readfirstlane(uint32_t(rec < 0 ? 0 : rec));
-    return record_rsrc(uniform_ptr(v_pool + uint64_t(r) * uint32_t(val_record<VB, FMT>())),
-                       rec < 0 ? 0 : val_record<VB, FMT>());
+    return record_rsrc(uniform_ptr(v_pool + uint64_t(r) * uint32_t(val_record<VB, FMT, NG>())),
+                       rec < 0 ? 0 : val_record<VB, FMT, NG>());
   };
   // Processes the page held in t; each part of t is reloaded with page `next` as soon as
   // this page has consumed it, so the loads overlap the rest of the page's work. A page
@@ -173,48 +174,50 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
   // maximum stays -inf and its weights exp2(s - inf) are 0.
   auto process = [&](PageRegs<KB, VB>& t, int64_t next, bool valid, int lim) {
     // ---- page factors into the wave's LDS slot ------------------------------------------
-    page_factors<FMT>(t, wm, l, maxq, fk, fv);
-    load_meta<AUX, FMT>(t, krec_of(next), vrec_of(next), lo);
+    page_factors<FMT, NG>(t, wm, l, maxq, fk, fv);
+    load_meta<AUX, FMT, NG>(t, krec_of(next), vrec_of(next), lo);
     // LDS operations of one wave complete in order: the writes above land before the reads
     // below, and after the previous page's reads
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // ---- B operand of QK (q'' high / low), bias + column-sum correction ---------------
-    H8 bq[4];
-    float bias;
-    {
-      float bpart = 0.f;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int c4 = 8 * gq + 2 * s + (side >> 1);   // channels 4 c4 .. 4 c4 + 3
-        const float4 ka = wm.ka[c4];
-        const float4 kb = wm.kb[c4];
-        const float* q4 = &qo[4 * s];
-        bpart = fmaf(q4[0], kb.x, bpart);
-        bpart = fmaf(q4[1], kb.y, bpart);
-        bpart = fmaf(q4[2], kb.z, bpart);
-        bpart = fmaf(q4[3], kb.w, bpart);
-        uint32_t h01, l01, h23, l23;
-        split_pk(q4[0] * ka.x, q4[1] * ka.y, h01, l01);
-        split_pk(q4[2] * ka.z, q4[3] * ka.w, h23, l23);
-        // dwords 0,1 = channels 0..3 of the 8 (built by the high lane), 2,3 = channels 4..7
-        bq[s].u[0] = swap8_into<kLoBanks>(h01, l01);
-        bq[s].u[1] = swap8_into<kLoBanks>(h23, l23);
-        bq[s].u[2] = swap8_into<kHiBanks>(l01, h01);
-        bq[s].u[3] = swap8_into<kHiBanks>(l23, h23);
-      }
-      bpart += dpp_f<kDppRowRor8>(bpart);
-      bias = pick(lo_mask, 0.f, rows4_sum(bpart));   // added once: on the high columns
-    }
-
-    // ---- QK: this lane finishes rows side, side+1 of each fragment -------------------------
+    // ---- QK, per key group (NG = 2: token blocks 0..3 take the factors of tokens 0..63,
+    // blocks 4..7 those of tokens 64..127): the B operand (q'' high / low) and the bias +
+    // column-sum correction of the group, then its token blocks; this lane finishes rows
+    // side, side+1 of each fragment
     float sc[8][2];
-    {
+#pragma unroll
+    for (int hq = 0; hq < NG; ++hq) {
+      H8 bq[4];
+      float bias;
+      {
+        float bpart = 0.f;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int c4 = 8 * gq + 2 * s + (side >> 1);   // channels 4 c4 .. 4 c4 + 3
+          const float4 ka = wm.ka[hq][c4];
+          const float4 kb = wm.kb[hq][c4];
+          const float* q4 = &qo[4 * s];
+          bpart = fmaf(q4[0], kb.x, bpart);
+          bpart = fmaf(q4[1], kb.y, bpart);
+          bpart = fmaf(q4[2], kb.z, bpart);
+          bpart = fmaf(q4[3], kb.w, bpart);
+          uint32_t h01, l01, h23, l23;
+          split_pk(q4[0] * ka.x, q4[1] * ka.y, h01, l01);
+          split_pk(q4[2] * ka.z, q4[3] * ka.w, h23, l23);
+          // dwords 0,1 = channels 0..3 of the 8 (built by the high lane), 2,3 = channels 4..7
+          bq[s].u[0] = swap8_into<kLoBanks>(h01, l01);
+          bq[s].u[1] = swap8_into<kLoBanks>(h23, l23);
+          bq[s].u[2] = swap8_into<kHiBanks>(l01, h01);
+          bq[s].u[3] = swap8_into<kHiBanks>(l23, h23);
+        }
+        bpart += dpp_f<kDppRowRor8>(bpart);
+        bias = pick(lo_mask, 0.f, rows4_sum(bpart));   // added once: on the high columns
+      }
       const float4v binit = {bias, bias, bias, bias};
 #pragma unroll
-      for (int tb = 0; tb < 8; ++tb) {
+      for (int tb = 8 / NG * hq; tb < 8 / NG * (hq + 1); ++tb) {
         float4v c = binit;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -258,10 +261,11 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
     const float m_new = fmaxf(m_run, valid ? mt : -INFINITY);
     const float alpha = valid ? exp2_fast(m_run - m_new) : 1.f;
     const float m_sub = valid ? m_new : INFINITY;
-    H8 bp[4];
-    float vcorr;
-    {
-      float psum = 0.f, zpart = 0.f;
+    // B operand of PV for value group hv (the softmax weights times the group's value
+    // factors, high / low) and its zero-point correction. NG = 1 turns the scores into
+    // weights here, adding them to psum; NG = 2 reads weights computed beforehand.
+    auto pv_operands = [&](int hv, H8 (&bp)[4], float& psum) -> float {
+      float zpart = 0.f;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         uint32_t hh[2], ll[2];
@@ -269,10 +273,14 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
         for (int e = 0; e < 2; ++e) {
           const int tb = 2 * s + e;
           const int t2 = 8 * tb + 2 * gq + (side >> 1);   // tokens 2 t2, 2 t2 + 1
-          const float2 vp = wm.vp[t2];
-          const float2 vz = wm.vz[t2];
-          const float p0 = exp2_fast(sc[tb][0] - m_sub), p1 = exp2_fast(sc[tb][1] - m_sub);
-          psum += p0 + p1;
+          const float2 vp = wm.vp[hv][t2];
+          const float2 vz = wm.vz[hv][t2];
+          float p0 = sc[tb][0], p1 = sc[tb][1];
+          if constexpr (NG == 1) {
+            p0 = exp2_fast(p0 - m_sub);
+            p1 = exp2_fast(p1 - m_sub);
+            psum += p0 + p1;
+          }
           zpart = fmaf(p0, vz.x, fmaf(p1, vz.y, zpart));
           split_pk(p0 * vp.x, p1 * vp.y, hh[e], ll[e]);
         }
@@ -284,50 +292,80 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
         bp[s].u[3] = swap8_into<kHiBanks>(ll[1], hh[1]);
       }
       zpart += dpp_f<kDppRowRor8>(zpart);
-      vcorr = pick(lo_mask, 0.f, rows4_sum(zpart));  // added once: on the high columns
-      l_part = fmaf(l_part, alpha, psum);
-    }
-    m_run = m_new;
-
-    // ---- PV ---------------------------------------------------------------------------
-    if (!__all(alpha == 1.f)) {   // some head's running maximum moved: rescale in place
+      return pick(lo_mask, 0.f, rows4_sum(zpart));  // added once: on the high columns
+    };
+    // PV of channel blocks bb0 .. bb0 + 8 / NG - 1 (one value group)
+    auto pv_blocks = [&](const H8 (&bp)[4], float vcorr, int bb0) {
+      const float4v vinit = {vcorr, vcorr, vcorr, vcorr};
 #pragma unroll
-      for (int bb = 0; bb < 8; ++bb)
+      for (int k = 0; k < 8 / NG; ++k) {
+        const int bb = bb0 + k;
+        float4v c = vinit;
+        if constexpr (VB == 2) {
+          const uint2 vc = t.vc[bb];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[bb][i] *= alpha;
-    }
-    const float4v vinit = {vcorr, vcorr, vcorr, vcorr};
+          for (int d = 0; d < 2; ++d) {
+            const uint32_t word = d ? vc.y : vc.x;
 #pragma unroll
-    for (int bb = 0; bb < 8; ++bb) {
-      float4v c = vinit;
-      if constexpr (VB == 2) {
-        const uint2 vc = t.vc[bb];
+            for (int hs = 0; hs < 2; ++hs) {
+              H8 a;
 #pragma unroll
-        for (int d = 0; d < 2; ++d) {
-          const uint32_t word = d ? vc.y : vc.x;
+              for (int v = 0; v < 4; ++v) a.u[v] = v_pair(word, 4 * hs + v);
+              c = mfma16x16x32(a.v, bp[2 * d + hs].v, c);
+            }
+          }
+        } else {   // word m = k-step m; nibbles v, 4 + v = its tokens 2v, 2v + 1
+          const uint32_t words[4] = {t.vc[bb].x, t.vc[bb].y, t.vc[bb].z, t.vc[bb].w};
 #pragma unroll
-          for (int hs = 0; hs < 2; ++hs) {
+          for (int m = 0; m < 4; ++m) {
             H8 a;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) a.u[v] = v_pair(word, 4 * hs + v);
-            c = mfma16x16x32(a.v, bp[2 * d + hs].v, c);
+            for (int v = 0; v < 4; ++v) a.u[v] = k_pair(words[m], v);
+            c = mfma16x16x32(a.v, bp[m].v, c);
           }
         }
-      } else {   // word m = k-step m; nibbles v, 4 + v = its tokens 2v, 2v + 1
-        const uint32_t words[4] = {t.vc[bb].x, t.vc[bb].y, t.vc[bb].z, t.vc[bb].w};
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          H8 a;
-#pragma unroll
-          for (int v = 0; v < 4; ++v) a.u[v] = k_pair(words[m], v);
-          c = mfma16x16x32(a.v, bp[m].v, c);
-        }
+        const float4 rv = wm.vr[4 * bb + gq];
+        acc[bb][0] = fmaf(rv.x, c[0], acc[bb][0]);
+        acc[bb][1] = fmaf(rv.y, c[1], acc[bb][1]);
+        acc[bb][2] = fmaf(rv.z, c[2], acc[bb][2]);
+        acc[bb][3] = fmaf(rv.w, c[3], acc[bb][3]);
       }
-      const float4 rv = wm.vr[4 * bb + gq];
-      acc[bb][0] = fmaf(rv.x, c[0], acc[bb][0]);
-      acc[bb][1] = fmaf(rv.y, c[1], acc[bb][1]);
-      acc[bb][2] = fmaf(rv.z, c[2], acc[bb][2]);
-      acc[bb][3] = fmaf(rv.w, c[3], acc[bb][3]);
+    };
+    auto rescale = [&]() {
+      if (!__all(alpha == 1.f)) {   // some head's running maximum moved: rescale in place
+#pragma unroll
+        for (int bb = 0; bb < 8; ++bb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[bb][i] *= alpha;
+      }
+    };
+    // ---- softmax weights and PV (NG = 2: channel blocks 0..3 take the value factors of
+    // channels 0..63, blocks 4..7 those of channels 64..127) --------------------------------
+    if constexpr (NG == 1) {
+      H8 bp[4];
+      float psum = 0.f;
+      const float vcorr = pv_operands(0, bp, psum);
+      l_part = fmaf(l_part, alpha, psum);
+      m_run = m_new;
+      rescale();
+      pv_blocks(bp, vcorr, 0);
+    } else {
+      float psum = 0.f;
+#pragma unroll
+      for (int tb = 0; tb < 8; ++tb) {
+        sc[tb][0] = exp2_fast(sc[tb][0] - m_sub);
+        sc[tb][1] = exp2_fast(sc[tb][1] - m_sub);
+        psum += sc[tb][0] + sc[tb][1];
+      }
+      l_part = fmaf(l_part, alpha, psum);
+      m_run = m_new;
+      rescale();
+#pragma unroll
+      for (int hv = 0; hv < NG; ++hv) {
+        H8 bp[4];
+        const float vcorr = pv_operands(hv, bp, psum);
+        pv_blocks(bp, vcorr, 8 / NG * hv);
+      }
     }
     load_vcodes<AUX>(t, vrec_of(next), lo);
   };
@@ -455,7 +493,7 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
     int sb, sg, sp, np;
     locate(x, sb, sg, sp, np);
     int64_t cur = rec_of(block_table + int64_t(sb) * bt_stride, sp, np, sg);
-    load_meta<AUX, FMT>(t, krec_of(cur), vrec_of(cur), lo);
+    load_meta<AUX, FMT, NG>(t, krec_of(cur), vrec_of(cur), lo);
     load_kcodes<AUX>(t, krec_of(cur), lo);
     load_vcodes<AUX>(t, vrec_of(cur), lo);
     while (x < x_end) {
@@ -506,7 +544,7 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
   const int32_t* bt_row = block_table + int64_t(rg.b) * bt_stride;
   const int wslot = __builtin_amdgcn_readfirstlane(slot0 + w);   // this wave's first slot
   int64_t cur = rec_of(bt_row, wslot, n_full, g);
-  load_meta<AUX, FMT>(t, krec_of(cur), vrec_of(cur), lo);
+  load_meta<AUX, FMT, NG>(t, krec_of(cur), vrec_of(cur), lo);
   load_kcodes<AUX>(t, krec_of(cur), lo);
   load_vcodes<AUX>(t, vrec_of(cur), lo);
   // q is rotated while the first page's loads are in flight
@@ -803,7 +841,7 @@ size_t decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv
   return bal > split ? bal : split;
 }
 
-hipError_t launch_decode(int k_bits, int v_bits, int fmt, const void* q, int32_t rows,
+hipError_t launch_decode(int k_bits, int v_bits, int fmt, int group, const void* q, int32_t rows,
                          int32_t num_q_heads, int32_t num_kv_heads, const void* k_pool,
                          const void* v_pool, int64_t pool_num_pages, const int32_t* block_table,
                          int32_t bt_stride, const int32_t* seq_lens, int32_t max_seq_len,
@@ -819,9 +857,10 @@ hipError_t launch_decode(int k_bits, int v_bits, int fmt, const void* q, int32_t
   const int32_t bal_wg = cu_q == nullptr ? decode_balanced_wg(rows, num_kv_heads, max_seq_len) : 0;
   if (bal_wg > 0) {
     const int32_t n_wg = bal_wg + (has_tail ? rows * num_kv_heads : 0);
-    const hipError_t e = with_preset(k_bits, v_bits, fmt, [&](auto kb, auto vb, auto fm) {
-      constexpr int KB = decltype(kb)::value, VB = decltype(vb)::value, FM = decltype(fm)::value;
-      hipLaunchKernelGGL((decode_pages_kernel<KB, VB, FM, kStreamLoad, true>), dim3(n_wg),
+    const hipError_t e = with_preset(k_bits, v_bits, fmt, group, [&](auto kb, auto vb, auto fm, auto ng) {
+      constexpr int KB = decltype(kb)::value, VB = decltype(vb)::value, FM = decltype(fm)::value,
+                    NG = decltype(ng)::value;
+      hipLaunchKernelGGL((decode_pages_kernel<KB, VB, FM, NG, kStreamLoad, true>), dim3(n_wg),
                          dim3(kThreads), 0, stream, static_cast<const __half*>(q), num_q_heads,
                          num_kv_heads, static_cast<const uint8_t*>(k_pool),
                          static_cast<const uint8_t*>(v_pool), pool_num_pages, block_table,
@@ -853,16 +892,17 @@ hipError_t launch_decode(int k_bits, int v_bits, int fmt, const void* q, int32_t
     // pages + tail, would leave every page workgroup on the even XCDs)
     hipError_t e;
     if (multi_row) {
-      e = launch_mq_pages(k_bits, v_bits, fmt, q, rows, num_q_heads, num_kv_heads, k_pool, v_pool,
+      e = launch_mq_pages(k_bits, v_bits, fmt, group, q, rows, num_q_heads, num_kv_heads, k_pool, v_pool,
                           pool_num_pages, block_table, bt_stride, seq_lens, max_seq_len, cu_q,
                           batch, k_tail, v_tail, qscale * kInvSqrt128, qscale, per_split, ns,
                           n_split_wg, first, workspace, stream);
     } else {
-      e = with_preset(k_bits, v_bits, fmt, [&](auto kb, auto vb, auto fm) {
-        constexpr int KB = decltype(kb)::value, VB = decltype(vb)::value, FM = decltype(fm)::value;
+      e = with_preset(k_bits, v_bits, fmt, group, [&](auto kb, auto vb, auto fm, auto ng) {
+        constexpr int KB = decltype(kb)::value, VB = decltype(vb)::value, FM = decltype(fm)::value,
+                    NG = decltype(ng)::value;
         // decode streams every page once; a read with one query per sequence reuses them
-        auto kernel = cu_q ? decode_pages_kernel<KB, VB, FM, kReuseLoad, false>
-                           : decode_pages_kernel<KB, VB, FM, kStreamLoad, false>;
+        auto kernel = cu_q ? decode_pages_kernel<KB, VB, FM, NG, kReuseLoad, false>
+                           : decode_pages_kernel<KB, VB, FM, NG, kStreamLoad, false>;
         hipLaunchKernelGGL(kernel, dim3(rows * num_kv_heads, n_split_wg), dim3(kThreads), 0,
                            stream, static_cast<const __half*>(q), num_q_heads, num_kv_heads,
                            static_cast<const uint8_t*>(k_pool),

@@ -87,17 +87,20 @@ __device__ __forceinline__ void load_h8(const uint8_t* p, float* o) {
 // Per wave: the float32 factors of the page being processed.
 //   ka[c] = r_c scale_c 2^(10-b_c) ks      kb[c] = ks r_c zero_c - ka[c]     kt[t] = s_t / ks
 //   vp[t] = s_t scale_t 2^(10-b_t) vs      vz[t] = vs s_t zero_t - vp[t]     vr[c] = r_c / vs
-// (ks, vs: the page's powers of two for the B operands.)
+// (ks, vs: the page's powers of two for the B operands.) With NG = 2 (group 64) the key
+// factors ka, kb come per token half (tokens 64 h ..) and the value factors vp, vz per
+// channel half (channels 64 h ..).
+template <int NG>
 struct WaveMeta {
-  float4 ka[kDim / 4], kb[kDim / 4];   // read 4 channels at a time
-  float2 kt[kTile / 2], vp[kTile / 2], vz[kTile / 2];   // read 2 tokens at a time
+  float4 ka[NG][kDim / 4], kb[NG][kDim / 4];   // read 4 channels at a time
+  float2 kt[kTile / 2], vp[NG][kTile / 2], vz[NG][kTile / 2];   // read 2 tokens at a time
   float4 vr[kDim / 4];
 };
 
 
 // Raw loads of one page: key codes (16 B per 16-token block at 4 bits, 8 B at 2), value
-// codes (8 B per 16-channel block at 2 bits, 16 B at 4), and entries 2l, 2l+1 of the 4
-// float16 metadata arrays of each record.
+// codes (8 B per 16-channel block at 2 bits, 16 B at 4), and entries 2l, 2l+1 of each
+// float16 metadata array of the records.
 // Key record geometry by key code width (4: kvarn_k4v2_g128 / kvarn_k4v4_g128,
 // 2: kvarn_k2v2_g128).
 template <int KB> struct KeyRec;
@@ -123,14 +126,14 @@ template <> struct ValRec<4> {
 };
 
 // Record bytes by code width and format.
-template <int KB, int FMT> constexpr int key_record() { return KeyRec<KB>::kCodeBytes + meta_bytes<FMT>(); }
-template <int VB, int FMT> constexpr int val_record() { return ValRec<VB>::kCodeBytes + meta_bytes<FMT>(); }
+template <int KB, int FMT, int NG> constexpr int key_record() { return KeyRec<KB>::kCodeBytes + meta_bytes<FMT, NG>(); }
+template <int VB, int FMT, int NG> constexpr int val_record() { return ValRec<VB>::kCodeBytes + meta_bytes<FMT, NG>(); }
 
 template <int KB, int VB>
 struct PageRegs {
   typename KeyRec<KB>::Codes kc[8];
   typename ValRec<VB>::Codes vc[8];
-  uint32_t km[4], vm[4];
+  uint32_t km[kMaxMetaSlots], vm[kMaxMetaSlots];   // the first meta_slots are loaded
 };
 
 // Page loads through buffer descriptors: one scalar descriptor per record (base, size), a
@@ -155,11 +158,11 @@ struct LaneOffsets {
   uint32_t k, v, m;   // key codes, value codes, metadata
 };
 
-template <int AUX, int FMT, int KB, int VB>
+template <int AUX, int FMT, int NG, int KB, int VB>
 __device__ __forceinline__ void load_meta(PageRegs<KB, VB>& t, __amdgpu_buffer_rsrc_t kr,
                                           __amdgpu_buffer_rsrc_t vr, const LaneOffsets& o) {
 #pragma unroll
-  for (int a = 0; a < meta_slots<FMT>(); ++a) {
+  for (int a = 0; a < meta_slots<FMT, NG>(); ++a) {
     t.km[a] = __builtin_amdgcn_raw_buffer_load_b32(kr, o.m, KeyRec<KB>::kCodeBytes + 256 * a, AUX);
     t.vm[a] = __builtin_amdgcn_raw_buffer_load_b32(vr, o.m, ValRec<VB>::kCodeBytes + 256 * a, AUX);
   }
@@ -238,33 +241,46 @@ constexpr int kLoBanks = 0xC;   // lanes 8..15: low-part columns
 // Page factors of the record pair held in t, for the B operands, into this wave's LDS slot
 // (lane l: channels and tokens 2l, 2l + 1). fk, fv: the lane's unpack factors 2^(10 - b);
 // maxq: the wave's largest |q_rot| (sets the power of two ks that keeps the QK B operand
-// below 2^14; vs does the same for the PV one).
-// Format 1 slots: keys and values r, s, scale, zero. Format 2 (folded): keys s, scale',
-// zero' (r folded into the per-channel scale and zero: rk = 1); values r, scale', zero' (s
-// folded into the per-token scale and zero: sv = 1).
-template <int FMT, int KB, int VB>
-__device__ __forceinline__ void page_factors(const PageRegs<KB, VB>& t, WaveMeta& wm, int l,
+// below 2^14; vs does the same for the PV one; both over every group of the page).
+// Format 1 slots: keys and values r, s, scales, zeros. Format 2 (folded): keys s, scales',
+// zeros' (r folded into the per-channel scales and zeros: rk = 1); values r, scales', zeros'
+// (s folded into the per-token scales and zeros: sv = 1). NG = 2: one scale and one zero
+// slot per half.
+template <int FMT, int NG, int KB, int VB>
+__device__ __forceinline__ void page_factors(const PageRegs<KB, VB>& t, WaveMeta<NG>& wm, int l,
                                              float maxq, float fk, float fv) {
-  constexpr int kS = FMT == 1 ? 1 : 0, kSc = FMT == 1 ? 2 : 1, kZr = FMT == 1 ? 3 : 2;
+  constexpr int kS = FMT == 1 ? 1 : 0;
   const float rk0 = FMT == 1 ? lo_h(t.km[0]) : 1.f, rk1 = FMT == 1 ? hi_h(t.km[0]) : 1.f;
-  const float ka0 = rk0 * lo_h(t.km[kSc]) * fk, ka1 = rk1 * hi_h(t.km[kSc]) * fk;
   const float sv0 = FMT == 1 ? lo_h(t.vm[1]) : 1.f, sv1 = FMT == 1 ? hi_h(t.vm[1]) : 1.f;
-  const float vp0 = sv0 * lo_h(t.vm[kSc]) * fv, vp1 = sv1 * hi_h(t.vm[kSc]) * fv;
-  const float mka = wave_max(fmaxf(ka0, ka1));
-  const float mvp = wave_max(fmaxf(vp0, vp1));
+  float ka0[NG], ka1[NG], vp0[NG], vp1[NG];
+  float mk = 0.f, mv = 0.f;
+#pragma unroll
+  for (int h = 0; h < NG; ++h) {
+    ka0[h] = rk0 * lo_h(t.km[slot_scale<FMT, NG>(h)]) * fk;
+    ka1[h] = rk1 * hi_h(t.km[slot_scale<FMT, NG>(h)]) * fk;
+    vp0[h] = sv0 * lo_h(t.vm[slot_scale<FMT, NG>(h)]) * fv;
+    vp1[h] = sv1 * hi_h(t.vm[slot_scale<FMT, NG>(h)]) * fv;
+    mk = h ? fmaxf(mk, fmaxf(ka0[h], ka1[h])) : fmaxf(ka0[h], ka1[h]);
+    mv = h ? fmaxf(mv, fmaxf(vp0[h], vp1[h])) : fmaxf(vp0[h], vp1[h]);
+  }
+  const float mka = wave_max(mk);
+  const float mvp = wave_max(mv);
   const int eks = pow2_norm_exp(maxq * __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mka))));
   const int evs = pow2_norm_exp(__int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mvp))));
   const float ks = __builtin_ldexpf(1.f, eks), iks = __builtin_ldexpf(1.f, -eks);
   const float vs = __builtin_ldexpf(1.f, evs), ivs = __builtin_ldexpf(1.f, -evs);
-  const float a0 = ka0 * ks, a1 = ka1 * ks;
-  reinterpret_cast<float2*>(wm.ka)[l] = make_float2(a0, a1);
-  reinterpret_cast<float2*>(wm.kb)[l] =
-      make_float2(fmaf(ks * rk0, lo_h(t.km[kZr]), -a0), fmaf(ks * rk1, hi_h(t.km[kZr]), -a1));
+#pragma unroll
+  for (int h = 0; h < NG; ++h) {
+    const float a0 = ka0[h] * ks, a1 = ka1[h] * ks;
+    const uint32_t kz = t.km[slot_zero<FMT, NG>(h)], vzr = t.vm[slot_zero<FMT, NG>(h)];
+    reinterpret_cast<float2*>(wm.ka[h])[l] = make_float2(a0, a1);
+    reinterpret_cast<float2*>(wm.kb[h])[l] =
+        make_float2(fmaf(ks * rk0, lo_h(kz), -a0), fmaf(ks * rk1, hi_h(kz), -a1));
+    const float p0 = vp0[h] * vs, p1 = vp1[h] * vs;
+    wm.vp[h][l] = make_float2(p0, p1);
+    wm.vz[h][l] = make_float2(fmaf(vs * sv0, lo_h(vzr), -p0), fmaf(vs * sv1, hi_h(vzr), -p1));
+  }
   wm.kt[l] = make_float2(lo_h(t.km[kS]) * iks, hi_h(t.km[kS]) * iks);
-  const float p0 = vp0 * vs, p1 = vp1 * vs;
-  wm.vp[l] = make_float2(p0, p1);
-  wm.vz[l] =
-      make_float2(fmaf(vs * sv0, lo_h(t.vm[kZr]), -p0), fmaf(vs * sv1, hi_h(t.vm[kZr]), -p1));
   reinterpret_cast<float2*>(wm.vr)[l] = make_float2(lo_h(t.vm[0]) * ivs, hi_h(t.vm[0]) * ivs);
 }
 

@@ -19,12 +19,19 @@ constexpr int kV4CodeBytes = 8192; // 4-bit codes of such a record
 constexpr int kVCodeBytes = 4096; // 2-bit codes of a value record
 constexpr float kInvSqrt128 = 0.08838834764831845f;  // 1 / sqrt(128), fp32-rounded
 
-// Float16 metadata after a record's codes: format 1 holds r, s, scale, zero (4 x 128 values);
-// format 2 (folded) holds the normalizer of the other axis, then the group scale and zero
-// with the group's own normalizer folded in (3 x 128): keys s, scale', zero' (per channel,
-// of Xr / s); values r, scale', zero' (per token, of Xr / r).
-template <int FMT> constexpr int meta_bytes() { return FMT == 1 ? 1024 : 768; }
-template <int FMT> constexpr int meta_slots() { return FMT == 1 ? 4 : 3; }
+// Float16 metadata after a record's codes, in slots of 128 values: format 1 holds r, s, then
+// the group scales and zeros; format 2 (folded) holds the normalizer of the other axis, then
+// the scales and zeros with the group's own normalizer folded in (keys s, scale', zero' per
+// channel, of Xr / s; values r, scale', zero' per token, of Xr / r). NG groups per key channel
+// or value token: 1 (group 128: one scale slot, one zero slot) or 2 (group 64: the scales of
+// halves 0 and 1, then the zeros of halves 0 and 1; half 0 = tokens 0..63 of a key channel,
+// channels 0..63 of a value token).
+template <int FMT> constexpr int norm_slots() { return FMT == 1 ? 2 : 1; }
+template <int FMT, int NG> constexpr int meta_slots() { return norm_slots<FMT>() + 2 * NG; }
+template <int FMT, int NG> constexpr int meta_bytes() { return 256 * meta_slots<FMT, NG>(); }
+template <int FMT, int NG> constexpr int slot_scale(int h) { return norm_slots<FMT>() + h; }
+template <int FMT, int NG> constexpr int slot_zero(int h) { return norm_slots<FMT>() + NG + h; }
+constexpr int kMaxMetaSlots = 6;
 
 // ---- cross-lane moves -------------------------------------------------------------
 // DPP controls (GCN/CDNA encoding).

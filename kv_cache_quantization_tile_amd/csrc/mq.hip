@@ -22,8 +22,9 @@ namespace {
 // sequence), found by a binary search over cu_q; wave w takes rows 4R m + R w .. + R - 1 of the
 // window that belong to sequence b. grid: (ceil(rows / 4R) + batch, KV heads, splits [+ tail]).
 
+template <int NG>
 struct MqSmem {
-  WaveMeta meta[4];
+  WaveMeta<NG> meta[4];
   union {
     float4 q[4][8][64];   // q_rot per wave: [k][lane] = channels 32 gq + 4k .. 4k + 3
     float p[8][kTile];    // tail split: softmax weights of the staged tokens
@@ -58,7 +59,7 @@ __device__ __forceinline__ MqWindow mq_window(int j, int rows_per_window,
   return r;
 }
 
-template <int KB, int VB, int FMT>
+template <int KB, int VB, int FMT, int NG>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 mq_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t num_kv_heads,
                 const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
@@ -68,7 +69,7 @@ mq_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t num_k
                 int32_t slots_per_split, int32_t n_splits, int32_t split_base,
                 const __half* __restrict__ k_tail, const __half* __restrict__ v_tail,
                 float tail_qscale, float* __restrict__ ws) {
-  __shared__ MqSmem sm;
+  __shared__ MqSmem<NG> sm;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int split = split_base + blockIdx.z, g = blockIdx.y;
   const int G = num_q_heads / num_kv_heads;
@@ -108,7 +109,7 @@ mq_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t num_k
     lp_col = rgc.n_slots > 0 ? kTile * (rgc.n_slots - 1) + rgc.mask_lim : 0;
   }
 
-  WaveMeta& wm = sm.meta[w];
+  WaveMeta<NG>& wm = sm.meta[w];
   const float fk = (l & 1) ? 16.f : (KB == 4 ? 256.f : 4.f);
   const float fv = (l & 1) ? 16.f : (VB == 2 ? 4.f : 256.f);
   const int32_t* bt_row = block_table + int64_t(rg_last.b) * bt_stride;
@@ -127,19 +128,19 @@ mq_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t num_k
   auto krec_of = [&](int64_t page) {
     const uint32_t ps = __builtin_amdgcn_readfirstlane(uint32_t(page < 0 ? 0 : page));
     const uint32_t r = ps * uint32_t(num_kv_heads) + uint32_t(g);
-    return record_rsrc(uniform_ptr(k_pool + uint64_t(r) * uint32_t(key_record<KB, FMT>())),
-                       page < 0 ? 0 : key_record<KB, FMT>());
+    return record_rsrc(uniform_ptr(k_pool + uint64_t(r) * uint32_t(key_record<KB, FMT, NG>())),
+                       page < 0 ? 0 : key_record<KB, FMT, NG>());
   };
   auto vrec_of = [&](int64_t page) {
     const uint32_t ps = __builtin_amdgcn_readfirstlane(uint32_t(page < 0 ? 0 : page));
     const uint32_t r = ps * uint32_t(num_kv_heads) + uint32_t(g);
-    return record_rsrc(uniform_ptr(v_pool + uint64_t(r) * uint32_t(val_record<VB, FMT>())),
-                       page < 0 ? 0 : val_record<VB, FMT>());
+    return record_rsrc(uniform_ptr(v_pool + uint64_t(r) * uint32_t(val_record<VB, FMT, NG>())),
+                       page < 0 ? 0 : val_record<VB, FMT, NG>());
   };
 
   PageRegs<KB, VB> t;
   int64_t cur = page_of(s0);
-  load_meta<kReuseLoad, FMT>(t, krec_of(cur), vrec_of(cur), lo);
+  load_meta<kReuseLoad, FMT, NG>(t, krec_of(cur), vrec_of(cur), lo);
   load_kcodes<kReuseLoad>(t, krec_of(cur), lo);
   load_vcodes<kReuseLoad>(t, vrec_of(cur), lo);
 
@@ -199,42 +200,43 @@ mq_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t num_k
   for (int slot = s0; slot < s1; ++slot) {
     const int64_t next = page_of(slot + 1);
     const bool valid = cur >= 0;
-    page_factors<FMT>(t, wm, l, maxq, fk, fv);
-    load_meta<kReuseLoad, FMT>(t, krec_of(next), vrec_of(next), lo);
+    page_factors<FMT, NG>(t, wm, l, maxq, fk, fv);
+    load_meta<kReuseLoad, FMT, NG>(t, krec_of(next), vrec_of(next), lo);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // ---- B operand of QK: q_rot * ka (high, low), bias = q_rot . kb ---------------------
-    H8 bqh[4], bql[4];
-    float bias;
-    {
-      float bpart = 0.f;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const float4 ka0 = wm.ka[8 * gq + 2 * s], ka1 = wm.ka[8 * gq + 2 * s + 1];
-        const float4 kb0 = wm.kb[8 * gq + 2 * s], kb1 = wm.kb[8 * gq + 2 * s + 1];
-        const float4 q0 = sm.q[w][2 * s][l], q1 = sm.q[w][2 * s + 1][l];
-        const float ka[8] = {ka0.x, ka0.y, ka0.z, ka0.w, ka1.x, ka1.y, ka1.z, ka1.w};
-        const float kb[8] = {kb0.x, kb0.y, kb0.z, kb0.w, kb1.x, kb1.y, kb1.z, kb1.w};
-        const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const float x0 = qv[2 * d], x1 = qv[2 * d + 1];
-          bpart = fmaf(x0, kb[2 * d], fmaf(x1, kb[2 * d + 1], bpart));
-          split_pk(x0 * ka[2 * d], x1 * ka[2 * d + 1], bqh[s].u[d], bql[s].u[d]);
-        }
-      }
-      bias = rows4_sum(bpart);
-    }
-
-    // ---- QK: C rows = tokens 16 tb + 4 gq + i, column = this lane's query ----------------
+    // ---- QK per key group (NG = 2: token blocks 0..3 take the factors of tokens 0..63,
+    // blocks 4..7 those of 64..127): B operand q_rot * ka (high, low), bias = q_rot . kb;
+    // C rows = tokens 16 tb + 4 gq + i, column = this lane's query
     float sc[8][4];
-    {
+#pragma unroll
+    for (int hq = 0; hq < NG; ++hq) {
+      H8 bqh[4], bql[4];
+      float bias;
+      {
+        float bpart = 0.f;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const float4 ka0 = wm.ka[hq][8 * gq + 2 * s], ka1 = wm.ka[hq][8 * gq + 2 * s + 1];
+          const float4 kb0 = wm.kb[hq][8 * gq + 2 * s], kb1 = wm.kb[hq][8 * gq + 2 * s + 1];
+          const float4 q0 = sm.q[w][2 * s][l], q1 = sm.q[w][2 * s + 1][l];
+          const float ka[8] = {ka0.x, ka0.y, ka0.z, ka0.w, ka1.x, ka1.y, ka1.z, ka1.w};
+          const float kb[8] = {kb0.x, kb0.y, kb0.z, kb0.w, kb1.x, kb1.y, kb1.z, kb1.w};
+          const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const float x0 = qv[2 * d], x1 = qv[2 * d + 1];
+            bpart = fmaf(x0, kb[2 * d], fmaf(x1, kb[2 * d + 1], bpart));
+            split_pk(x0 * ka[2 * d], x1 * ka[2 * d + 1], bqh[s].u[d], bql[s].u[d]);
+          }
+        }
+        bias = rows4_sum(bpart);
+      }
       const float4v binit = {bias, bias, bias, bias};
       const float* kt = reinterpret_cast<const float*>(wm.kt);
 #pragma unroll
-      for (int tb = 0; tb < 8; ++tb) {
+      for (int tb = 8 / NG * hq; tb < 8 / NG * (hq + 1); ++tb) {
         float4v c = binit;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -279,12 +281,13 @@ mq_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t num_k
     const bool live = valid && m_new != -INFINITY;
     const float alpha = live ? exp2_fast(m_run - m_new) : 1.f;
     const float m_sub = live ? m_new : INFINITY;
-    H8 bph[4], bpl[4];
-    float vcorr;
-    {
-      float psum = 0.f, zpart = 0.f;
-      const float* vp = reinterpret_cast<const float*>(wm.vp);
-      const float* vz = reinterpret_cast<const float*>(wm.vz);
+    // B operand of PV for value group hv (the softmax weights times the group's value
+    // factors, high / low) and its zero-point correction. NG = 1 turns the scores into
+    // weights here, adding them to psum; NG = 2 reads weights computed beforehand.
+    auto pv_operands = [&](int hv, H8 (&bph)[4], H8 (&bpl)[4], float& psum) -> float {
+      float zpart = 0.f;
+      const float* vp = reinterpret_cast<const float*>(wm.vp[hv]);
+      const float* vz = reinterpret_cast<const float*>(wm.vz[hv]);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
 #pragma unroll
@@ -292,60 +295,96 @@ mq_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t num_k
           const int tb = 2 * s + e;
           const float4 vp4 = *reinterpret_cast<const float4*>(vp + 16 * tb + 4 * gq);
           const float4 vz4 = *reinterpret_cast<const float4*>(vz + 16 * tb + 4 * gq);
-          const float p0 = exp2_fast(sc[tb][0] - m_sub), p1 = exp2_fast(sc[tb][1] - m_sub);
-          const float p2 = exp2_fast(sc[tb][2] - m_sub), p3 = exp2_fast(sc[tb][3] - m_sub);
-          psum += (p0 + p1) + (p2 + p3);
+          float p0 = sc[tb][0], p1 = sc[tb][1], p2 = sc[tb][2], p3 = sc[tb][3];
+          if constexpr (NG == 1) {
+            p0 = exp2_fast(p0 - m_sub);
+            p1 = exp2_fast(p1 - m_sub);
+            p2 = exp2_fast(p2 - m_sub);
+            p3 = exp2_fast(p3 - m_sub);
+            psum += (p0 + p1) + (p2 + p3);
+          }
           zpart = fmaf(p0, vz4.x, fmaf(p1, vz4.y, fmaf(p2, vz4.z, fmaf(p3, vz4.w, zpart))));
           split_pk(p0 * vp4.x, p1 * vp4.y, bph[s].u[2 * e], bpl[s].u[2 * e]);
           split_pk(p2 * vp4.z, p3 * vp4.w, bph[s].u[2 * e + 1], bpl[s].u[2 * e + 1]);
         }
       }
-      vcorr = rows4_sum(zpart);
-      l_part = fmaf(l_part, alpha, psum);
-    }
-    m_run = m_new;
-
-    // ---- PV: C rows = channels 16 bb + 4 gq + i ---------------------------------------------
-    if (!__all(alpha == 1.f)) {
+      return rows4_sum(zpart);
+    };
+    // PV of channel blocks bb0 .. bb0 + 8 / NG - 1 (one value group); C rows = channels
+    // 16 bb + 4 gq + i
+    auto pv_blocks = [&](const H8 (&bph)[4], const H8 (&bpl)[4], float vcorr, int bb0) {
+      const float4v vinit = {vcorr, vcorr, vcorr, vcorr};
 #pragma unroll
-      for (int bb = 0; bb < 8; ++bb)
+      for (int k = 0; k < 8 / NG; ++k) {
+        const int bb = bb0 + k;
+        float4v c = vinit;
+        if constexpr (VB == 2) {
+          const uint2 vc = t.vc[bb];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[bb][i] *= alpha;
-    }
-    const float4v vinit = {vcorr, vcorr, vcorr, vcorr};
+          for (int d = 0; d < 2; ++d) {
+            const uint32_t word = d ? vc.y : vc.x;
 #pragma unroll
-    for (int bb = 0; bb < 8; ++bb) {
-      float4v c = vinit;
-      if constexpr (VB == 2) {
-        const uint2 vc = t.vc[bb];
+            for (int hs = 0; hs < 2; ++hs) {
+              H8 a;
 #pragma unroll
-        for (int d = 0; d < 2; ++d) {
-          const uint32_t word = d ? vc.y : vc.x;
+              for (int v = 0; v < 4; ++v) a.u[v] = v_pair(word, 4 * hs + v);
+              c = mfma16x16x32(a.v, bph[2 * d + hs].v, c);
+              c = mfma16x16x32(a.v, bpl[2 * d + hs].v, c);
+            }
+          }
+        } else {
+          const uint32_t words[4] = {t.vc[bb].x, t.vc[bb].y, t.vc[bb].z, t.vc[bb].w};
 #pragma unroll
-          for (int hs = 0; hs < 2; ++hs) {
+          for (int m = 0; m < 4; ++m) {
             H8 a;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) a.u[v] = v_pair(word, 4 * hs + v);
-            c = mfma16x16x32(a.v, bph[2 * d + hs].v, c);
-            c = mfma16x16x32(a.v, bpl[2 * d + hs].v, c);
+            for (int v = 0; v < 4; ++v) a.u[v] = k_pair(words[m], v);
+            c = mfma16x16x32(a.v, bph[m].v, c);
+            c = mfma16x16x32(a.v, bpl[m].v, c);
           }
         }
-      } else {
-        const uint32_t words[4] = {t.vc[bb].x, t.vc[bb].y, t.vc[bb].z, t.vc[bb].w};
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          H8 a;
-#pragma unroll
-          for (int v = 0; v < 4; ++v) a.u[v] = k_pair(words[m], v);
-          c = mfma16x16x32(a.v, bph[m].v, c);
-          c = mfma16x16x32(a.v, bpl[m].v, c);
-        }
+        const float4 rv = wm.vr[4 * bb + gq];
+        acc[bb][0] = fmaf(rv.x, c[0], acc[bb][0]);
+        acc[bb][1] = fmaf(rv.y, c[1], acc[bb][1]);
+        acc[bb][2] = fmaf(rv.z, c[2], acc[bb][2]);
+        acc[bb][3] = fmaf(rv.w, c[3], acc[bb][3]);
       }
-      const float4 rv = wm.vr[4 * bb + gq];
-      acc[bb][0] = fmaf(rv.x, c[0], acc[bb][0]);
-      acc[bb][1] = fmaf(rv.y, c[1], acc[bb][1]);
-      acc[bb][2] = fmaf(rv.z, c[2], acc[bb][2]);
-      acc[bb][3] = fmaf(rv.w, c[3], acc[bb][3]);
+    };
+    auto rescale = [&]() {
+      if (!__all(alpha == 1.f)) {
+#pragma unroll
+        for (int bb = 0; bb < 8; ++bb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[bb][i] *= alpha;
+      }
+    };
+    // ---- softmax weights and PV (NG = 2: channel blocks 0..3 take the value factors of
+    // channels 0..63, blocks 4..7 those of channels 64..127) --------------------------------
+    if constexpr (NG == 1) {
+      H8 bph[4], bpl[4];
+      float psum = 0.f;
+      const float vcorr = pv_operands(0, bph, bpl, psum);
+      l_part = fmaf(l_part, alpha, psum);
+      m_run = m_new;
+      rescale();
+      pv_blocks(bph, bpl, vcorr, 0);
+    } else {
+      float psum = 0.f;
+#pragma unroll
+      for (int tb = 0; tb < 8; ++tb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[tb][i] = exp2_fast(sc[tb][i] - m_sub);
+        psum += (sc[tb][0] + sc[tb][1]) + (sc[tb][2] + sc[tb][3]);
+      }
+      l_part = fmaf(l_part, alpha, psum);
+      m_run = m_new;
+      rescale();
+#pragma unroll
+      for (int hv = 0; hv < NG; ++hv) {
+        H8 bph[4], bpl[4];
+        const float vcorr = pv_operands(hv, bph, bpl, psum);
+        pv_blocks(bph, bpl, vcorr, 8 / NG * hv);
+      }
     }
     load_vcodes<kReuseLoad>(t, vrec_of(next), lo);
     cur = next;
@@ -401,7 +440,7 @@ size_t chunk_workspace_bytes(int32_t rows, int32_t num_q_heads, int32_t num_kv_h
   return size_t(rows) * num_q_heads * (ns + 1) * kPartStride * sizeof(float);
 }
 
-hipError_t launch_mq_pages(int k_bits, int v_bits, int fmt, const void* q, int32_t rows,
+hipError_t launch_mq_pages(int k_bits, int v_bits, int fmt, int group, const void* q, int32_t rows,
                           int32_t num_q_heads, int32_t num_kv_heads, const void* k_pool,
                           const void* v_pool, int64_t pool_num_pages, const int32_t* block_table,
                           int32_t bt_stride, const int32_t* seq_lens, int32_t max_seq_len,
@@ -411,9 +450,10 @@ hipError_t launch_mq_pages(int k_bits, int v_bits, int fmt, const void* q, int32
                           int32_t split_base, void* workspace, hipStream_t stream) {
   // 16 query vectors per wave, windows of 4R rows per workgroup
   const int R = 16 / (num_q_heads / num_kv_heads);
-  return with_preset(k_bits, v_bits, fmt, [&](auto kb, auto vb, auto fm) {
-    constexpr int KB = decltype(kb)::value, VB = decltype(vb)::value, FM = decltype(fm)::value;
-    hipLaunchKernelGGL((mq_pages_kernel<KB, VB, FM>),
+  return with_preset(k_bits, v_bits, fmt, group, [&](auto kb, auto vb, auto fm, auto ng) {
+    constexpr int KB = decltype(kb)::value, VB = decltype(vb)::value, FM = decltype(fm)::value,
+                    NG = decltype(ng)::value;
+    hipLaunchKernelGGL((mq_pages_kernel<KB, VB, FM, NG>),
                        dim3((rows + 4 * R - 1) / (4 * R) + batch, num_kv_heads, n_split_wg),
                        dim3(kThreads), 0, stream, static_cast<const __half*>(q), num_q_heads,
                        num_kv_heads, static_cast<const uint8_t*>(k_pool),

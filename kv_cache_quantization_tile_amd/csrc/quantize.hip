@@ -45,9 +45,9 @@ __device__ __forceinline__ int codes_row(int c) { return kCodeRowBase * c + 2 * 
 struct QuantSmem {
   float red[2][4][kDim];       // per-wave partial sums over tokens, channel vectors (2 buffers)
   float gr[4][2][kDim];        // per-wave broadcast of channel vectors (chan_pair_slot order)
-  float gc[4][4][2][8];        // per-wave, per-row broadcast of per-token values
+  float gc[4][4][2][2][8];     // per-wave, per-row, per-half broadcast of per-token values
   uint32_t codes[kCodeRowBase * kDim + 2 * 16];  // value codes: row c at codes_row(c)
-  uint16_t meta[4][kDim];      // r, s, scale, zero as float16 bits
+  uint16_t meta[kMaxMetaSlots][kDim];  // the record's metadata slots as float16 bits
 };
 
 constexpr int kDppRowRor4 = 0x124;  // rotate right by 4 inside a 16-lane row
@@ -61,10 +61,10 @@ __device__ __forceinline__ float combine(float a, float b) {
 
 // Reduce-scatter over the 16 lanes of a row: every lane holds v[0..7] (one value per token
 // of its token block); lane l returns the row-wide reduction of v[l & 7] (lanes l and l ^ 8
-// agree). Each stage keeps the half of the values whose index bit matches the lane bit and
+// agree); with FULL = false, the reduction over the 8 lanes whose bit 3 equals l's. Each stage keeps the half of the values whose index bit matches the lane bit and
 // adds the partner's copy of that half: bits 0 and 1 with quad permutes, bit 2 with a
 // rotation by 4 (any partner with the other bit 2 works, since bit 3 is summed last).
-template <int OP>
+template <int OP, bool FULL = true>
 __device__ __forceinline__ float row16_scatter8(const float (&v)[8], int l) {
   const bool b0 = (l & 1) != 0, b1 = (l & 2) != 0, b2 = (l & 4) != 0;
   float a[4], c[2];
@@ -82,6 +82,11 @@ __device__ __forceinline__ float row16_scatter8(const float (&v)[8], int l) {
   }
   const float send = b2 ? c[0] : c[1];
   const float keep = b2 ? c[1] : c[0];
+  if constexpr (!FULL) {
+    // partner exactly lane l ^ 4 (a rotation by 4 would pair lanes 0..3 with 12..15, across
+    // the halves): the reduction stays inside the 8 lanes whose bit 3 equals l's
+    return combine<OP>(keep, swz_xor_f<4>(send));
+  }
   const float e = combine<OP>(keep, dpp_f<kDppRowRor4>(send));
   return combine<OP>(e, dpp_f<kDppRowRor8>(e));
 }
@@ -154,9 +159,9 @@ template <> struct CodeBytes<1, 2> { static constexpr int kBytes = kVCodeBytes; 
 template <> struct CodeBytes<1, 4> { static constexpr int kBytes = kV4CodeBytes; };
 // FMT 1: codes, then r, s, scale, zero; FMT 2 (folded): codes, then keys s, scale', zero' /
 // values r, scale', zero'
-template <int KIND, int BITS, int FMT> struct RecFormat {
+template <int KIND, int BITS, int FMT, int NG> struct RecFormat {
   static constexpr int kCodeBytes = CodeBytes<KIND, BITS>::kBytes;
-  static constexpr int kRecord = kCodeBytes + meta_bytes<FMT>();
+  static constexpr int kRecord = kCodeBytes + meta_bytes<FMT, NG>();
 };
 
 // x += c * x(lane under DPP control CTRL) for 8 values, one v_fmac_f32_dpp each. The DPP
@@ -317,12 +322,12 @@ __device__ __forceinline__ void rotate_tile_mfma(RowPtr row_ptr, int w, int l, f
 
 // The tile quantizer proper. row_ptr(t) gives the 16-byte aligned address of token t's
 // 128 channels. Writes one record at `rec`; BITS is the code width of this kind.
-template <int KIND, int BITS, int FMT, typename RowPtr>
+template <int KIND, int BITS, int FMT, int NG, typename RowPtr>
 __device__ __forceinline__ void quantize_tile(RowPtr row_ptr, uint8_t* __restrict__ rec, int n_iters,
                                               QuantSmem& sm) {
-  // metadata slots of the record: format 1 r, s, scale, zero; format 2 the other axis's
-  // normalizer, scale', zero' (the group's normalizer folded in)
-  constexpr int kSlotSc = FMT == 1 ? 2 : 1, kSlotZr = FMT == 1 ? 3 : 2;
+  // metadata slots of the record: format 1 r, s, then scales and zeros; format 2 the other
+  // axis's normalizer, then scales' and zeros' (the group's normalizer folded in); NG = 2
+  // (group 64) has a scale and a zero slot per half (slot_scale / slot_zero)
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63;
   const int cb = l & 15;
@@ -350,8 +355,7 @@ __device__ __forceinline__ void quantize_tile(RowPtr row_ptr, uint8_t* __restric
   const int ch_off = 4 * (r & 1) + 2 * (r >> 1);
   const int ch_own = 8 * cb + ch_off;
   const int own_slot = chan_pair_slot(cb, ch_off);  // my channel pair in a channel vector
-  float* gc0 = &sm.gc[w][r][0][0];
-  float* gc1 = &sm.gc[w][r][1][0];
+  float* gc0 = &sm.gc[w][r][0][0][0];
   float* gr0 = &sm.gr[w][0][0];
   float ir[8], is[8];      // 1/r for my channels, 1/s for my tokens
 #pragma unroll
@@ -489,8 +493,10 @@ __device__ __forceinline__ void quantize_tile(RowPtr row_ptr, uint8_t* __restric
     *reinterpret_cast<float2*>(&sm.gr[w][0][own_slot]) = make_float2(omn[0], omn[1]);
     *reinterpret_cast<float2*>(&sm.gr[w][1][own_slot]) = make_float2(omx[0], omx[1]);
     __syncthreads();
+    // NG = 2: a group is the 64 tokens of waves 2h, 2h + 1 (h = w / 2)
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
+    for (int k2 = 0; k2 < 4 / NG; ++k2) {
+      const int ww = NG == 1 ? k2 : (w & 2) + k2;
       const float2 a = *reinterpret_cast<const float2*>(&sm.gr[ww][0][own_slot]);
       const float2 b = *reinterpret_cast<const float2*>(&sm.gr[ww][1][own_slot]);
       omn[0] = fminf(omn[0], a.x); omn[1] = fminf(omn[1], a.y);
@@ -509,9 +515,9 @@ __device__ __forceinline__ void quantize_tile(RowPtr row_ptr, uint8_t* __restric
       const float inv = sc > 0.f ? __builtin_amdgcn_rcpf(sc) : 0.f;
       A2[k] = to_g * inv;
       B2[k] = -h2f(zr16) * inv;
-      if (w == 0) {
-        sm.meta[kSlotSc][ch_own + k] = sc16;
-        sm.meta[kSlotZr][ch_own + k] = zr16;
+      if ((w & (NG == 1 ? 3 : 1)) == 0) {   // one wave per group
+        sm.meta[slot_scale<FMT, NG>(w >> 1 & (NG - 1))][ch_own + k] = sc16;
+        sm.meta[slot_zero<FMT, NG>(w >> 1 & (NG - 1))][ch_own + k] = zr16;
       }
     }
     float* ga = &sm.red[0][w][0];
@@ -574,21 +580,25 @@ __device__ __forceinline__ void quantize_tile(RowPtr row_ptr, uint8_t* __restric
     // format 1: the group is y = z / s (s > 0); format 2 codes z = Xr / r itself (s folded
     // into the stored scale and zero)
     const float to_g = FMT == 1 ? is_own : 1.f;
-    const float lo = row16_scatter8<1>(mn, l) * to_g;
-    const float hi_ = row16_scatter8<2>(mx, l) * to_g;
+    // NG = 2: a group is the 64 channels of the lanes with the same bit 3 (cb < 8, cb >= 8)
+    const float lo = row16_scatter8<1, NG == 1>(mn, l) * to_g;
+    const float hi_ = row16_scatter8<2, NG == 1>(mx, l) * to_g;
+    const int hh = NG == 1 ? 0 : (l >> 3) & 1;
     const uint16_t sc16 = meta16((hi_ - lo) * (BITS == 2 ? 1.f / 3.f : 1.f / 15.f));
     const uint16_t zr16 = meta16(lo);
     const float sc = h2f(sc16);
     const float inv = sc > 0.f ? __builtin_amdgcn_rcpf(sc) : 0.f;
-    if ((l & 8) == 0) {
-      sm.meta[kSlotSc][tok(tok_own)] = sc16;
-      sm.meta[kSlotZr][tok(tok_own)] = zr16;
+    if (NG == 2 || (l & 8) == 0) {
+      sm.meta[slot_scale<FMT, NG>(hh)][tok(tok_own)] = sc16;
+      sm.meta[slot_zero<FMT, NG>(hh)][tok(tok_own)] = zr16;
     }
-    gc0[tok_own] = to_g * inv;
-    gc1[tok_own] = -h2f(zr16) * inv;
+    float* ga = &sm.gc[w][r][hh][0][0];
+    float* gb = &sm.gc[w][r][hh][1][0];
+    ga[tok_own] = to_g * inv;
+    gb[tok_own] = -h2f(zr16) * inv;
     float A[8], B[8];
-    lds_read8(gc0, A);
-    lds_read8(gc1, B);
+    lds_read8(ga, A);
+    lds_read8(gb, B);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       uint32_t lo4 = 0, hi4 = 0;
@@ -652,17 +662,18 @@ __device__ __forceinline__ void quantize_tile(RowPtr row_ptr, uint8_t* __restric
       out[wi] = word;
     }
   }
-  // metadata: 4 (format 1) or 3 (format 2) x 128 float16 = 256 or 192 words
+  // metadata: meta_slots x 128 float16 (3 to 6 slots: 192 to 384 words)
   {
-    const int codes_words = RecFormat<KIND, BITS, FMT>::kCodeBytes / 4;
+    const int codes_words = RecFormat<KIND, BITS, FMT, NG>::kCodeBytes / 4;
     const uint16_t* mm = &sm.meta[0][0];
-    if (tid < meta_bytes<FMT>() / 4)
-      out[codes_words + tid] = uint32_t(mm[2 * tid]) | (uint32_t(mm[2 * tid + 1]) << 16);
+#pragma unroll
+    for (int k = tid; k < meta_bytes<FMT, NG>() / 4; k += kThreads)
+      out[codes_words + k] = uint32_t(mm[2 * k]) | (uint32_t(mm[2 * k + 1]) << 16);
   }
 }
 
 // Four workgroups per CU (16 waves) keep a whole layer's tiles resident in one round.
-template <int KIND, int BITS, int FMT>
+template <int KIND, int BITS, int FMT, int NG>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 quantize_tiles_kernel(const __half* __restrict__ src, int64_t token_stride, int64_t head_stride,
                       int64_t src_num_tokens, const int64_t* __restrict__ tile_src_token,
@@ -676,13 +687,13 @@ quantize_tiles_kernel(const __half* __restrict__ src, int64_t token_stride, int6
   if (t0 < 0 || t0 > src_num_tokens - kTile || page < 0 || page >= pool_num_pages) return;
   const __half* base = src + t0 * token_stride + int64_t(h) * head_stride;
   auto row_ptr = [=](int t) { return base + int64_t(t) * token_stride; };
-  constexpr int kRec = RecFormat<KIND, BITS, FMT>::kRecord;
+  constexpr int kRec = RecFormat<KIND, BITS, FMT, NG>::kRecord;
   uint8_t* rec = pool + (page * num_kv_heads + h) * int64_t(kRec);
-  quantize_tile<KIND, BITS, FMT>(row_ptr, rec, n_iters, sm);
+  quantize_tile<KIND, BITS, FMT, NG>(row_ptr, rec, n_iters, sm);
 }
 
 // Keys and values of the same tiles in one launch: grid (n_tiles, num_kv_heads, 2), z = kind.
-template <int KB, int VB, int FMT>
+template <int KB, int VB, int FMT, int NG>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 quantize_kv_kernel(const __half* __restrict__ k_src, const __half* __restrict__ v_src,
                    int64_t token_stride, int64_t head_stride, int64_t src_num_tokens,
@@ -700,16 +711,16 @@ quantize_kv_kernel(const __half* __restrict__ k_src, const __half* __restrict__ 
   const __half* base = (is_k ? k_src : v_src) + t0 * token_stride + int64_t(h) * head_stride;
   auto row_ptr = [=](int t) { return base + int64_t(t) * token_stride; };
   if (is_k)
-    quantize_tile<0, KB, FMT>(row_ptr, k_pool + (page * num_kv_heads + h) * int64_t(RecFormat<0, KB, FMT>::kRecord),
+    quantize_tile<0, KB, FMT, NG>(row_ptr, k_pool + (page * num_kv_heads + h) * int64_t(RecFormat<0, KB, FMT, NG>::kRecord),
                          n_iters, sm);
   else
-    quantize_tile<1, VB, FMT>(row_ptr, v_pool + (page * num_kv_heads + h) * int64_t(RecFormat<1, VB, FMT>::kRecord),
+    quantize_tile<1, VB, FMT, NG>(row_ptr, v_pool + (page * num_kv_heads + h) * int64_t(RecFormat<1, VB, FMT, NG>::kRecord),
                          n_iters, sm);
 }
 
 // Append one token per (sequence, head) into staging; quantize the staging tile it fills.
 // grid: (batch, num_kv_heads, 2 kinds)
-template <int KB, int VB, int FMT>
+template <int KB, int VB, int FMT, int NG>
 __global__ void __launch_bounds__(kThreads)
 append_tokens_kernel(const __half* __restrict__ k_new, const __half* __restrict__ v_new,
                      int32_t num_kv_heads, const int32_t* __restrict__ seq_lens,
@@ -735,10 +746,10 @@ append_tokens_kernel(const __half* __restrict__ k_new, const __half* __restrict_
   // the filled row is read from the new-token buffer, never from the staging just written
   auto row_ptr = [=](int t) { return t == kTile - 1 ? src_new : stage + int64_t(t) * kDim; };
   if (kind == 0) {
-    quantize_tile<0, KB, FMT>(row_ptr, k_pool + (page * num_kv_heads + h) * int64_t(RecFormat<0, KB, FMT>::kRecord),
+    quantize_tile<0, KB, FMT, NG>(row_ptr, k_pool + (page * num_kv_heads + h) * int64_t(RecFormat<0, KB, FMT, NG>::kRecord),
                          n_iters, sm);
   } else {
-    quantize_tile<1, VB, FMT>(row_ptr, v_pool + (page * num_kv_heads + h) * int64_t(RecFormat<1, VB, FMT>::kRecord),
+    quantize_tile<1, VB, FMT, NG>(row_ptr, v_pool + (page * num_kv_heads + h) * int64_t(RecFormat<1, VB, FMT, NG>::kRecord),
                          n_iters, sm);
   }
 }
@@ -749,7 +760,7 @@ append_tokens_kernel(const __half* __restrict__ k_new, const __half* __restrict_
 // grid: (tile slots, batch, num_kv_heads * 2); slot j is tile t = L / 128 + j, quantized when
 // complete (128 t + 128 <= L + n). Its rows below L come from staging (only the tile that was
 // partial before the chunk has such rows), the others straight from the new-token buffer.
-template <int KB, int VB, int FMT>
+template <int KB, int VB, int FMT, int NG>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 write_tiles_kernel(const __half* __restrict__ k_new, const __half* __restrict__ v_new,
                    int32_t total_new, const int32_t* __restrict__ cu_new, int32_t max_new,
@@ -780,10 +791,10 @@ write_tiles_kernel(const __half* __restrict__ k_new, const __half* __restrict__ 
     return a < L ? stage + int64_t(r) * kDim : src + (a - L) * row_stride;
   };
   if (kind == 0)
-    quantize_tile<0, KB, FMT>(row_ptr, k_pool + (page * num_kv_heads + h) * int64_t(RecFormat<0, KB, FMT>::kRecord),
+    quantize_tile<0, KB, FMT, NG>(row_ptr, k_pool + (page * num_kv_heads + h) * int64_t(RecFormat<0, KB, FMT, NG>::kRecord),
                          n_iters, sm);
   else
-    quantize_tile<1, VB, FMT>(row_ptr, v_pool + (page * num_kv_heads + h) * int64_t(RecFormat<1, VB, FMT>::kRecord),
+    quantize_tile<1, VB, FMT, NG>(row_ptr, v_pool + (page * num_kv_heads + h) * int64_t(RecFormat<1, VB, FMT, NG>::kRecord),
                          n_iters, sm);
 }
 
@@ -819,15 +830,16 @@ write_staging_kernel(const __half* __restrict__ k_new, const __half* __restrict_
 // Page records back to float16 tiles (read side, then the inverse rotation H^-1 = H):
 // grid (n_tiles, num_kv_heads), one workgroup per record, the thread layout of the
 // quantizer (channels 8cb..+7 x tokens 8tb..+7). dst: [n_tiles][num_kv_heads][token][channel].
-template <int KIND, int BITS, int FMT>
+template <int KIND, int BITS, int FMT, int NG>
 __global__ void __launch_bounds__(kThreads)
 dequantize_tiles_kernel(const uint8_t* __restrict__ pool, int64_t pool_num_pages,
                         const int32_t* __restrict__ pages, int32_t num_kv_heads,
                         __half* __restrict__ dst) {
-  constexpr int kRec = RecFormat<KIND, BITS, FMT>::kRecord;
-  // metadata slots: format 1 r, s, scale, zero; format 2 keys s, scale', zero' (r = 1),
-  // values r, scale', zero' (s = 1)
-  constexpr int kR = 0, kS = FMT == 1 ? 1 : 0, kSc = FMT == 1 ? 2 : 1, kZr = FMT == 1 ? 3 : 2;
+  constexpr int kRec = RecFormat<KIND, BITS, FMT, NG>::kRecord;
+  // metadata slots: format 1 r, s, scales, zeros; format 2 keys s, scales', zeros' (r = 1),
+  // values r, scales', zeros' (s = 1); NG = 2: the scale and zero of half h (token / 64 for
+  // keys, channel / 64 for values) in slots slot_scale(h), slot_zero(h)
+  constexpr int kR = 0, kS = FMT == 1 ? 1 : 0;
   constexpr bool kHasR = FMT == 1 || KIND == 1, kHasS = FMT == 1 || KIND == 0;
   __shared__ uint4 rec_sm[(kRec + 15) / 16];
   const int tile = blockIdx.x, h = blockIdx.y;
@@ -839,7 +851,7 @@ dequantize_tiles_kernel(const uint8_t* __restrict__ pool, int64_t pool_num_pages
   __syncthreads();
   const uint32_t* words = reinterpret_cast<const uint32_t*>(rec_sm);
   const uint16_t* meta = reinterpret_cast<const uint16_t*>(
-      reinterpret_cast<const uint8_t*>(rec_sm) + RecFormat<KIND, BITS, FMT>::kCodeBytes);
+      reinterpret_cast<const uint8_t*>(rec_sm) + RecFormat<KIND, BITS, FMT, NG>::kCodeBytes);
   const int w = tid >> 6, l = tid & 63, cb = l & 15, tb = 4 * w + (l >> 4);
   float x[8][8];
 #pragma unroll
@@ -861,8 +873,9 @@ dequantize_tiles_kernel(const uint8_t* __restrict__ pool, int64_t pool_num_pages
           const int p = 4 * hs + ((c & 7) >> 1) + 8 * (c & 1);
           code = (words[t * 8 + (c >> 4)] >> (2 * p)) & 3u;
         }
-        sc = h2f(meta[kSc * kDim + c]);
-        zr = h2f(meta[kZr * kDim + c]);
+        const int hg = NG == 1 ? 0 : t >> 6;
+        sc = h2f(meta[slot_scale<FMT, NG>(hg) * kDim + c]);
+        zr = h2f(meta[slot_zero<FMT, NG>(hg) * kDim + c]);
       } else {
         // token t of channel c: word 8c + 2g + d, crumb p (the record's crumb order)
         const int s_ = t >> 5, rem = t & 31;
@@ -875,8 +888,9 @@ dequantize_tiles_kernel(const uint8_t* __restrict__ pool, int64_t pool_num_pages
           const int qn = (jj >> 1) + 4 * (jj & 1);
           code = (words[16 * c + 4 * g + s_] >> (4 * qn)) & 15u;
         }
-        sc = h2f(meta[kSc * kDim + t]);
-        zr = h2f(meta[kZr * kDim + t]);
+        const int hg = NG == 1 ? 0 : c >> 6;
+        sc = h2f(meta[slot_scale<FMT, NG>(hg) * kDim + t]);
+        zr = h2f(meta[slot_zero<FMT, NG>(hg) * kDim + t]);
       }
       x[j][i] = (kHasR ? h2f(meta[kR * kDim + c]) : 1.f) * st * fmaf(sc, float(code), zr);
     }
@@ -896,23 +910,23 @@ dequantize_tiles_kernel(const uint8_t* __restrict__ pool, int64_t pool_num_pages
 
 }  // namespace
 
-hipError_t launch_dequantize_tiles(int kind, int k_bits, int v_bits, int fmt, const void* pool,
+hipError_t launch_dequantize_tiles(int kind, int k_bits, int v_bits, int fmt, int group, const void* pool,
                                    int64_t pool_num_pages, const int32_t* pages, int32_t n_tiles,
                                    int32_t num_kv_heads, void* dst, hipStream_t stream) {
   dim3 grid(n_tiles, num_kv_heads), block(kThreads);
   const auto* pl = static_cast<const uint8_t*>(pool);
   auto* d = static_cast<__half*>(dst);
-  return with_preset(k_bits, v_bits, fmt, [&](auto kb, auto vb, auto fm) {
+  return with_preset(k_bits, v_bits, fmt, group, [&](auto kb, auto vb, auto fm, auto ng) {
     if (kind == 1)
-      hipLaunchKernelGGL((dequantize_tiles_kernel<1, decltype(vb)::value, decltype(fm)::value>), grid, block, 0, stream,
+      hipLaunchKernelGGL((dequantize_tiles_kernel<1, decltype(vb)::value, decltype(fm)::value, decltype(ng)::value>), grid, block, 0, stream,
                          pl, pool_num_pages, pages, num_kv_heads, d);
     else
-      hipLaunchKernelGGL((dequantize_tiles_kernel<0, decltype(kb)::value, decltype(fm)::value>), grid, block, 0, stream,
+      hipLaunchKernelGGL((dequantize_tiles_kernel<0, decltype(kb)::value, decltype(fm)::value, decltype(ng)::value>), grid, block, 0, stream,
                          pl, pool_num_pages, pages, num_kv_heads, d);
   });
 }
 
-hipError_t launch_quantize_tiles(int kind, int k_bits, int v_bits, int fmt, const void* src,
+hipError_t launch_quantize_tiles(int kind, int k_bits, int v_bits, int fmt, int group, const void* src,
                                  int64_t token_stride, int64_t head_stride, int64_t src_num_tokens,
                                  const int64_t* tile_src_token, const int32_t* tile_dst_page,
                                  int32_t n_tiles, int32_t num_kv_heads, void* pool,
@@ -920,19 +934,19 @@ hipError_t launch_quantize_tiles(int kind, int k_bits, int v_bits, int fmt, cons
   dim3 grid(n_tiles, num_kv_heads), block(kThreads);
   const auto* sp = static_cast<const __half*>(src);
   auto* pl = static_cast<uint8_t*>(pool);
-  return with_preset(k_bits, v_bits, fmt, [&](auto kb, auto vb, auto fm) {
+  return with_preset(k_bits, v_bits, fmt, group, [&](auto kb, auto vb, auto fm, auto ng) {
     if (kind == 1)
-      hipLaunchKernelGGL((quantize_tiles_kernel<1, decltype(vb)::value, decltype(fm)::value>), grid, block, 0, stream,
+      hipLaunchKernelGGL((quantize_tiles_kernel<1, decltype(vb)::value, decltype(fm)::value, decltype(ng)::value>), grid, block, 0, stream,
                          sp, token_stride, head_stride, src_num_tokens, tile_src_token,
                          tile_dst_page, num_kv_heads, pl, pool_num_pages, n_iters);
     else
-      hipLaunchKernelGGL((quantize_tiles_kernel<0, decltype(kb)::value, decltype(fm)::value>), grid, block, 0, stream,
+      hipLaunchKernelGGL((quantize_tiles_kernel<0, decltype(kb)::value, decltype(fm)::value, decltype(ng)::value>), grid, block, 0, stream,
                          sp, token_stride, head_stride, src_num_tokens, tile_src_token,
                          tile_dst_page, num_kv_heads, pl, pool_num_pages, n_iters);
   });
 }
 
-hipError_t launch_quantize_kv(int k_bits, int v_bits, int fmt, const void* k_src, const void* v_src,
+hipError_t launch_quantize_kv(int k_bits, int v_bits, int fmt, int group, const void* k_src, const void* v_src,
                               int64_t token_stride, int64_t head_stride, int64_t src_num_tokens,
                               const int64_t* tile_src_token, const int32_t* tile_dst_page,
                               int32_t n_tiles, int32_t num_kv_heads, void* k_pool, void* v_pool,
@@ -942,15 +956,15 @@ hipError_t launch_quantize_kv(int k_bits, int v_bits, int fmt, const void* k_src
   const auto* vs = static_cast<const __half*>(v_src);
   auto* kp = static_cast<uint8_t*>(k_pool);
   auto* vp = static_cast<uint8_t*>(v_pool);
-  return with_preset(k_bits, v_bits, fmt, [&](auto kb, auto vb, auto fm) {
-    hipLaunchKernelGGL((quantize_kv_kernel<decltype(kb)::value, decltype(vb)::value, decltype(fm)::value>), grid, block,
+  return with_preset(k_bits, v_bits, fmt, group, [&](auto kb, auto vb, auto fm, auto ng) {
+    hipLaunchKernelGGL((quantize_kv_kernel<decltype(kb)::value, decltype(vb)::value, decltype(fm)::value, decltype(ng)::value>), grid, block,
                        0, stream, ks, vs, token_stride, head_stride, src_num_tokens,
                        tile_src_token, tile_dst_page, num_kv_heads, kp, vp, pool_num_pages,
                        n_iters);
   });
 }
 
-hipError_t launch_write_tokens(int k_bits, int v_bits, int fmt, const void* k_new, const void* v_new,
+hipError_t launch_write_tokens(int k_bits, int v_bits, int fmt, int group, const void* k_new, const void* v_new,
                                int32_t total_new, const int32_t* cu_new, int32_t max_new,
                                int32_t batch, int32_t num_kv_heads, const int32_t* seq_lens,
                                void* k_tail, void* v_tail, const int32_t* block_table,
@@ -960,8 +974,8 @@ hipError_t launch_write_tokens(int k_bits, int v_bits, int fmt, const void* k_ne
   dim3 grid1(max_new / kTile + 1, batch, num_kv_heads * 2), block(kThreads);
   const auto* kn = static_cast<const __half*>(k_new);
   const auto* vn = static_cast<const __half*>(v_new);
-  const hipError_t e = with_preset(k_bits, v_bits, fmt, [&](auto kb, auto vb, auto fm) {
-    hipLaunchKernelGGL((write_tiles_kernel<decltype(kb)::value, decltype(vb)::value, decltype(fm)::value>), grid1,
+  const hipError_t e = with_preset(k_bits, v_bits, fmt, group, [&](auto kb, auto vb, auto fm, auto ng) {
+    hipLaunchKernelGGL((write_tiles_kernel<decltype(kb)::value, decltype(vb)::value, decltype(fm)::value, decltype(ng)::value>), grid1,
                        block, 0, stream, kn, vn, total_new, cu_new, max_new, num_kv_heads,
                        seq_lens, static_cast<const __half*>(k_tail),
                        static_cast<const __half*>(v_tail), block_table, bt_stride,
@@ -976,7 +990,7 @@ hipError_t launch_write_tokens(int k_bits, int v_bits, int fmt, const void* k_ne
   return hipGetLastError();
 }
 
-hipError_t launch_append_tokens(int k_bits, int v_bits, int fmt, const void* k_new, const void* v_new,
+hipError_t launch_append_tokens(int k_bits, int v_bits, int fmt, int group, const void* k_new, const void* v_new,
                                 int32_t batch, int32_t num_kv_heads, const int32_t* seq_lens,
                                 void* k_tail, void* v_tail, const int32_t* block_table,
                                 int32_t bt_stride, void* k_pool, void* v_pool,
@@ -988,8 +1002,8 @@ hipError_t launch_append_tokens(int k_bits, int v_bits, int fmt, const void* k_n
   auto* vt = static_cast<__half*>(v_tail);
   auto* kp = static_cast<uint8_t*>(k_pool);
   auto* vp = static_cast<uint8_t*>(v_pool);
-  return with_preset(k_bits, v_bits, fmt, [&](auto kb, auto vb, auto fm) {
-    hipLaunchKernelGGL((append_tokens_kernel<decltype(kb)::value, decltype(vb)::value, decltype(fm)::value>), grid,
+  return with_preset(k_bits, v_bits, fmt, group, [&](auto kb, auto vb, auto fm, auto ng) {
+    hipLaunchKernelGGL((append_tokens_kernel<decltype(kb)::value, decltype(vb)::value, decltype(fm)::value, decltype(ng)::value>), grid,
                        block, 0, stream, kn, vn, num_kv_heads, seq_lens, kt, vt, block_table,
                        bt_stride, kp, vp, pool_num_pages, n_iters);
   });

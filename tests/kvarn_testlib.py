@@ -79,26 +79,46 @@ class QuantStats:
                 f"offset-dominated groups {self.offset_groups}")
 
 
-def reconstruction_error(x_ct: np.ndarray, d: dict, kind: int) -> float:
-    xh = O.dequantize_tiles(d["codes"], d["r"], d["s"], d["scale"], d["zero"], kind)
+def reconstruction_error(x_ct: np.ndarray, d: dict, kind: int, group: int = 128) -> float:
+    xh = O.dequantize_tiles(d["codes"], d["r"], d["s"], d["scale"], d["zero"], kind, group=group)
     return float(np.linalg.norm(xh - x_ct))
+
+
+def grouped(a: np.ndarray, kind: int, group: int = 128) -> np.ndarray:
+    """A per-element [128 c, 128 t] array as [groups, elements of a group], groups in the order
+    of meta_groups: keys (channel, token half), values (channel half, token); one group per
+    channel / token at group 128."""
+    ng = 128 // group
+    a = np.asarray(a)
+    if kind == O.KIND_K:
+        return a.reshape(128, ng, group).reshape(128 * ng, group)
+    return a.reshape(ng, group, 128).transpose(0, 2, 1).reshape(ng * 128, group)
+
+
+def meta_groups(v, kind: int, group: int = 128) -> np.ndarray:
+    """A record's scale or zero ([128], or [2, 128] half-major at group 64) in group order."""
+    ng = 128 // group
+    v = np.asarray(v).reshape(ng, 128)
+    return (v.T if kind == O.KIND_K else v).reshape(-1)
 
 
 def check_quantized_tiles(tiles_tc: np.ndarray, records, kind: int, n_iters: int,
                           stats: QuantStats | None = None, k_bits: int = 4,
-                          v_bits: int = 2, fmt: int = 1) -> QuantStats:
+                          v_bits: int = 2, fmt: int = 1, group: int = 128) -> QuantStats:
     """tiles_tc: [n, 128 tokens, 128 channels] float16 (the source layout); records: the GPU
     page records of those tiles. Asserts L1 and L2 (every tile, every group) and L3's
     |code difference| <= 1 outside offset-dominated groups; accumulates the L3 and plain
-    metadata statistics (asserted by the caller: assert_rate)."""
+    metadata statistics (asserted by the caller: assert_rate). group 64: every half of a key
+    channel / value token is a group of its own, with its own scale and zero."""
     stats = stats or QuantStats()
     x = np.ascontiguousarray(np.swapaxes(tiles_tc, -1, -2))  # channels x tokens
-    ref = O.quantize_tiles(x, kind, n_iters, k_bits=k_bits, v_bits=v_bits, fmt=fmt)
-    unpack = lambda rec: O.unpack_record(rec, kind, k_bits, v_bits, fmt)
+    ref = O.quantize_tiles(x, kind, n_iters, k_bits=k_bits, v_bits=v_bits, fmt=fmt, group=group)
+    unpack = lambda rec: O.unpack_record(rec, kind, k_bits, v_bits, fmt, group)
     bits = k_bits if kind == O.KIND_K else v_bits
     qmax = (1 << bits) - 1
-    ax = 1 if kind == O.KIND_K else 0          # the axis a group runs along (c x t tile)
-    grp = (lambda v: v[:, None]) if kind == O.KIND_K else (lambda v: v[None, :])
+    G = lambda a: grouped(a, kind, group)                     # [groups, elements]
+    M = lambda v: meta_groups(v, kind, group)                 # [groups]
+    n_groups = 128 * (128 // group)
     for i, rec in enumerate(records):
         g = unpack(rec)
         for key in ("r", "s", "scale", "zero"):
@@ -114,18 +134,17 @@ def check_quantized_tiles(tiles_tc: np.ndarray, records, kind: int, n_iters: int
             stats.meta_total += 128
         # ---- L1: scale, zero against the per-group cascade bound
         r_g, s_g = g["r"].astype(np.float64), g["s"].astype(np.float64)
-        y_g = ref["xr"][i] / (r_g[:, None] * s_g[None, :])     # oracle's Xr, GPU's normalizers
-        y_o = ref["y"][i]
+        y_ct = ref["xr"][i] / (r_g[:, None] * s_g[None, :])   # oracle's Xr, GPU's normalizers
+        y_g, y_o = G(y_ct), G(ref["y"][i])
         dy = np.abs(y_g - y_o)
-        delta = _delta(x[i], r_g, s_g)                          # float32 bound on y
-        d_max = delta.max(axis=ax)
-        at = lambda arr, idx: np.take_along_axis(arr, np.expand_dims(idx, ax), ax).squeeze(ax)
-        lo_o, lo_g = y_o.argmin(ax), y_g.argmin(ax)
-        hi_o, hi_g = y_o.argmax(ax), y_g.argmax(ax)
+        d_max = G(_delta(x[i], r_g, s_g)).max(axis=1)         # float32 bound on y, per group
+        at = lambda arr, idx: np.take_along_axis(arr, idx[:, None], 1)[:, 0]
+        lo_o, lo_g = y_o.argmin(1), y_g.argmin(1)
+        hi_o, hi_g = y_o.argmax(1), y_g.argmax(1)
         a_lo = np.maximum(at(dy, lo_o), at(dy, lo_g)) + d_max
         a_hi = np.maximum(at(dy, hi_o), at(dy, hi_g)) + d_max
-        sa, sb = g["scale"].astype(np.float64), ref["scale"][i].astype(np.float64)
-        za, zb = g["zero"].astype(np.float64), ref["zero"][i].astype(np.float64)
+        sa, sb = M(g["scale"]).astype(np.float64), M(ref["scale"][i]).astype(np.float64)
+        za, zb = M(g["zero"]).astype(np.float64), M(ref["zero"][i]).astype(np.float64)
         tol_s = META_RTOL * np.abs(sb) + 1.01 * (a_lo + a_hi) / qmax
         tol_z = META_RTOL * np.maximum(np.abs(zb), sb) + 1.01 * a_lo
         ok_s = (sa == sb) | (np.abs(sa - sb) <= tol_s)
@@ -135,47 +154,48 @@ def check_quantized_tiles(tiles_tc: np.ndarray, records, kind: int, n_iters: int
         # plain-bar exceedances: outside offset-dominated groups (where the float32 bound on y
         # is a visible share of the range) each must come from a normalizer flip at its min /
         # max elements
-        offset = np.abs(y_o).max(axis=ax) > OFFSET_DOMINATED * sb
+        offset = np.abs(y_o).max(axis=1) > OFFSET_DOMINATED * sb
         plain_s = np.abs(sa - sb) > META_RTOL * np.abs(sb)
         plain_z = np.abs(za - zb) > META_RTOL * np.maximum(np.abs(zb), sb)
-        flip = (g["r"][:, None] != ref["r"][i][:, None]) | (g["s"][None, :] != ref["s"][i][None, :])
+        flip = G((g["r"][:, None] != ref["r"][i][:, None]) | (g["s"][None, :] != ref["s"][i][None, :]))
         f_lo = at(flip, lo_o) | at(flip, lo_g)
         f_hi = at(flip, hi_o) | at(flip, hi_g)
         assert not np.any(plain_z & ~f_lo & ~offset), ("zero beyond 1e-3 without a flip", i)
         assert not np.any(plain_s & ~(f_lo | f_hi) & ~offset), ("scale beyond 1e-3 without a flip", i)
         stats.meta_plain_over += int(plain_s.sum() + plain_z.sum())
-        stats.meta_plain_total += 256
-        stats.meta_exact += int(np.sum(g["scale"] == ref["scale"][i]) + np.sum(g["zero"] == ref["zero"][i]))
-        stats.meta_total += 256
+        stats.meta_plain_total += 2 * n_groups
+        stats.meta_exact += int(np.sum(sa == sb) + np.sum(za == zb))
+        stats.meta_total += 2 * n_groups
         stats.max_meta_rel = max(stats.max_meta_rel, float(np.max(np.where(sa == sb, 0, np.abs(sa - sb) / np.maximum(sb, 1e-30)))))
         # ---- L2: the oracle's rounding step applied to the GPU's own metadata
-        sc_b, zr_b = grp(sa), grp(za)
+        codes_g, codes_o = G(g["codes"]), G(ref["codes"][i])
+        sc_b, zr_b = sa[:, None], za[:, None]
         live = sc_b > 0
         with np.errstate(invalid="ignore", over="ignore"):
             u = np.where(live, (y_g - np.where(live, zr_b, 0.0)) / np.where(live, sc_b, 1.0), 0.0)
         re = np.clip(np.rint(u), 0, qmax)
         re = np.where(live, re, 0)
-        diff = re != g["codes"]
+        diff = re != codes_g
         if diff.any():
             frac = np.abs(u - np.floor(u) - 0.5)
             xscale = np.abs(x[i].astype(np.float64)).sum(axis=0)[None, :] / np.sqrt(128.0)
-            step = r_g[:, None] * s_g[None, :] * np.where(sc_b > 0, sc_b, np.inf)
-            band = TIE_BAND + 32 * 2.0 ** -24 * xscale / step
+            rs = G(np.broadcast_to(xscale / (r_g[:, None] * s_g[None, :]), (128, 128)))
+            band = TIE_BAND + 32 * 2.0 ** -24 * rs / np.where(sc_b > 0, sc_b, np.inf)
             near_tie = frac <= band
             outside = diff & ~near_tie
             stats.l2_mismatch += int(outside.sum())
-            assert not outside.any(), (i, int(outside.sum()), u[outside][:5], g["codes"][outside][:5])
+            assert not outside.any(), (i, int(outside.sum()), u[outside][:5], codes_g[outside][:5])
         # ---- L3 outside offset-dominated groups; those get the reconstruction bound
         stats.offset_groups += int(offset.sum())
-        keep = ~np.broadcast_to(grp(offset), (128, 128))
-        d = g["codes"].astype(int) - ref["codes"][i].astype(int)
+        d = codes_g.astype(int) - codes_o.astype(int)
+        keep = ~offset
         assert np.all(np.abs(d[keep]) <= 1), (i, int(np.abs(d[keep]).max()))
         stats.l3_mismatch += int(np.count_nonzero(d[keep]))
-        stats.codes += int(keep.sum())
+        stats.codes += int(keep.sum()) * group
         if offset.any():
             xf = x[i].astype(np.float64)
-            e_gpu = reconstruction_error(xf, g, kind)
-            e_ref = reconstruction_error(xf, {k_: ref[k_][i] for k_ in ("codes", "r", "s", "scale", "zero")}, kind)
+            e_gpu = reconstruction_error(xf, g, kind, group)
+            e_ref = reconstruction_error(xf, {k_: ref[k_][i] for k_ in ("codes", "r", "s", "scale", "zero")}, kind, group)
             assert e_gpu <= 1.05 * e_ref + 1e-6 * float(np.linalg.norm(xf)), (i, e_gpu, e_ref)
     return stats
 
@@ -220,13 +240,18 @@ def format_of(pool) -> int:
     return O.record_layout(pool.shape[2])[1]
 
 
+def group_of(pool) -> int:
+    """Group size of a pool's records (128 or 64), from its record size."""
+    return O.record_group(pool.shape[2])
+
+
 def oracle_rows(q: np.ndarray, hq_list, G: int, k_recs, v_recs, k_tail=None, v_tail=None,
                 softmax_scale=1.0 / np.sqrt(128), k_bits: int = 4, v_bits: int = 2,
-                fmt: int = 1):
+                fmt: int = 1, group: int = 128):
     """Oracle outputs for query heads hq_list (all sharing one KV head whose page records are
     k_recs / v_recs, plus float16 tails [n_tail, 128]). q: [Hq, 128] float16."""
-    ks = [O.dequantize_k_record(r, k_bits, fmt) for r in k_recs]
-    vs = [O.dequantize_v_record(r, v_bits, fmt) for r in v_recs]
+    ks = [O.dequantize_k_record(r, k_bits, fmt, group) for r in k_recs]
+    vs = [O.dequantize_v_record(r, v_bits, fmt, group) for r in v_recs]
     if k_tail is not None and len(k_tail):
         ks.append(np.asarray(k_tail, np.float16).astype(np.float64))
         vs.append(np.asarray(v_tail, np.float16).astype(np.float64))
@@ -274,7 +299,8 @@ def check_decode(q_gpu, out_gpu, k_pool, v_pool, block_table, seq_lens, G, rows=
         no_keys = not pages and (tail_k is None or tail_k.shape[0] == 0)
         ref = None if no_keys else oracle_rows(q[b], hqs, G, krec, vrec, tail_k, tail_v,
                                                softmax_scale, key_bits_of(k_pool),
-                                               value_bits_of(v_pool), format_of(k_pool))
+                                               value_bits_of(v_pool), format_of(k_pool),
+                                               group_of(k_pool))
         for hq in hqs:
             if no_keys:            # L = 0, or every page skipped and no tail: zeros
                 assert np.all(out[b, hq] == 0), f"b={b} hq={hq}: expected zeros"

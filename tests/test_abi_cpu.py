@@ -44,8 +44,12 @@ def test_params_from_dtype():
     assert (p2.k_bits, p2.v_bits, p2.group, p2.sinkhorn_iters) == (2, 2, 128, 4)
     p4 = K.params_from_dtype("kvarn_k4v4_g128", 8)
     assert (p4.k_bits, p4.v_bits, p4.group) == (4, 4, 128)
-    for unsup in ("kvarn_k3v2_g128", "kvarn_k2v4_g128", "kvarn_k4v3_g128", "kvarn_k4v2_g64"):
+    for unsup in ("kvarn_k3v2_g128", "kvarn_k2v4_g128", "kvarn_k4v3_g128", "kvarn_k4v2_g32",
+                  "kvarn_k4v2_g256", "kvarn_k2v4_g64"):
         assert K.lib.kvarn_params_from_dtype(unsup.encode(), 8, ctypes.byref(out)) == UNSUP, unsup
+    for name, kb, vb in (("kvarn_k4v2_g64", 4, 2), ("kvarn_k2v2_g64", 2, 2), ("kvarn_k4v4_g64", 4, 4)):
+        pg = K.params_from_dtype(name, 8)
+        assert (pg.k_bits, pg.v_bits, pg.group) == (kb, vb, 64)
     assert K.lib.kvarn_params_from_dtype(b"kvarn_k4v2_g128", -1, ctypes.byref(out)) == INVALID
     assert K.lib.kvarn_params_from_dtype(b"kvarn_k4v2_g128", 65, ctypes.byref(out)) == INVALID
     assert K.lib.kvarn_params_from_dtype(None, 8, ctypes.byref(out)) == INVALID
@@ -69,6 +73,18 @@ def test_page_bytes():
                            ("kvarn_k4v4_g128", 8960, 8960)):
         pf = K.params_from_dtype(preset, 8, format=K.FORMAT_FOLDED)
         assert (K.page_bytes(pf, K.KIND_K), K.page_bytes(pf, K.KIND_V)) == (kb, vb)
+    # group 64: two scale and two zero vectors instead of one each (+512 B), both formats
+    for preset, kb, vb in (("kvarn_k4v2_g64", 9728, 5632), ("kvarn_k2v2_g64", 5632, 5632),
+                           ("kvarn_k4v4_g64", 9728, 9728)):
+        pg = K.params_from_dtype(preset, 8)
+        assert (K.page_bytes(pg, K.KIND_K), K.page_bytes(pg, K.KIND_V)) == (kb, vb)
+        pgf = K.params_from_dtype(preset, 8, format=K.FORMAT_FOLDED)
+        assert (K.page_bytes(pgf, K.KIND_K), K.page_bytes(pgf, K.KIND_V)) == (kb - 256, vb - 256)
+    for grp in (32, 96, 256, 0):
+        pg = K.params_from_dtype()
+        pg.group = grp
+        assert K.lib.kvarn_params_check(ctypes.byref(pg)) == (INVALID if grp == 0 else UNSUP)
+        assert K.page_bytes(pg, K.KIND_K) == 0
     for fmt in (0, 3, -1):
         pf = K.params_from_dtype()
         pf.format = fmt

@@ -60,8 +60,9 @@ def _reference_rows(q, cu_q, kp, vp, bt, kt, vt, sl, G, rows_to_check):
             if (b, g) not in cache:
                 pages = [int(p) for p in bt_h[b, :C // 128]]
                 fm = T.format_of(kp)
-                ks = [O.dequantize_k_record(x, T.key_bits_of(kp), fm) for x in T.records_of(kp, pages, g)]
-                vs = [O.dequantize_v_record(x, T.value_bits_of(vp), fm) for x in T.records_of(vp, pages, g)]
+                gs = T.group_of(kp)
+                ks = [O.dequantize_k_record(x, T.key_bits_of(kp), fm, gs) for x in T.records_of(kp, pages, g)]
+                vs = [O.dequantize_v_record(x, T.value_bits_of(vp), fm, gs) for x in T.records_of(vp, pages, g)]
                 ks.append(kt_h[b, g, :C % 128].astype(np.float64))
                 vs.append(vt_h[b, g, :C % 128].astype(np.float64))
                 cache[(b, g)] = (np.concatenate(ks, 0), np.concatenate(vs, 0))

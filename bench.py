@@ -1017,7 +1017,7 @@ def main():
     ap.add_argument("--sweep-iters", type=int, nargs="*", default=[2, 4],
                     help="other iteration counts at which the quantize launch is timed")
     ap.add_argument("--preset", default="kvarn_k4v2_g128",
-                    choices=["kvarn_k4v2_g128", "kvarn_k2v2_g128", "kvarn_k4v4_g128"],
+                    choices=[f"kvarn_{w}_g{g}" for g in (128, 64) for w in ("k4v2", "k2v2", "k4v4")],
                     help="kv_cache_dtype preset (the released k4v2_g128 by default)")
     ap.add_argument("--format", type=int, default=1, choices=[1, 2],
                     help="page record format: 1 separate normalizers and scales (default), "

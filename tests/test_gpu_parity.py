@@ -308,6 +308,26 @@ def test_decode_many_splits_and_max_seq_len_clamp(K):
     say(f"max rel err {err:.3e}")
 
 
+@pytest.mark.parametrize("preset,fmt,pages", [("kvarn_k4v2_g128", 1, 300), ("kvarn_k4v2_g128", 1, 256),
+                                               ("kvarn_k4v4_g128", 1, 300), ("kvarn_k2v2_g64", 2, 300)])
+def test_decode_one_sequence_several_pages_per_wave(K, preset, fmt, pages):
+    """One sequence over 8 KV heads long enough for several pages per wave in one round of
+    page waves (the split layout's page loop with its prefetch of the next page, at small
+    size): 300 pages give waves with unequal page counts, 256 equal ones."""
+    hkv, G = 8, 8
+    lens = [128 * pages + 77]
+    params = K.params_from_dtype(preset, 8, format=fmt)
+    ns = K.decode_num_splits(params, 1, hkv, lens[0])
+    assert hkv * ns * 4 <= 1024 and hkv * pages > 1024      # >= 2 pages per wave, one round
+    say(f"decode one sequence, several pages per wave: {preset} fmt={fmt} pages={pages} splits={ns}")
+    kp, vp, bt, kt, vt, sl, _ = _build_cache(K, params, lens, hkv, seed=90 + pages)
+    q = torch.randn((1, G * hkv, 128), generator=torch.Generator().manual_seed(91)).to(torch.float16).cuda()
+    out = K.decode_attention(params, q, kp, vp, bt, sl, lens[0], kt, vt)
+    torch.cuda.synchronize()
+    err = T.check_decode(q, out, kp, vp, bt, sl, G, rows=[(0, 0), (0, 5)], k_tail=kt, v_tail=vt)
+    say(f"max rel err {err:.3e}")
+
+
 @pytest.mark.parametrize("B,hkv,G,hi", [(3, 1, 8, 260), (300, 1, 2, 700), (1024, 1, 1, 300),
                                         (1025, 1, 1, 300), (5, 2, 4, 128 * 500)])
 def test_decode_balanced_layout(K, B, hkv, G, hi):

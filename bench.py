@@ -786,6 +786,7 @@ PMC_PASSES = {
     "a": ["SQ_ACTIVE_INST_VALU", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_LDS",
           "SQ_LDS_BANK_CONFLICT", "SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY",
           "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE"],
+    "l": ["TCC_HIT_sum", "TCC_MISS_sum"],     # L2 hits and misses, summed over the channels
 }
 PROFILE_KERNELS = {
     "prefill_burst": ["quantize_kv_kernel", "decode_pages_kernel", "decode_merge_kernel"],
@@ -990,6 +991,21 @@ def reduce_profiles(d: str, out_dir: str):
                              f"{derived['valu_issue']:.3f}  valu_busy {derived['valu_busy']:.3f}  "
                              f"mfma_busy {derived['mfma_busy']:.3f}  lds_conflict "
                              f"{derived['lds_conflict']:.4f}")
+            # L2 (TCC) hit rate per kernel, from its own pass
+            ldir = os.path.join(d, f"l_{wl}")
+            if os.path.isdir(ldir):
+                cl, _ = _read_counters(ldir)
+                lines.append("#   L2: hit_rate = TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum) "
+                             "per dispatch (requests of 128 bytes)")
+                for k in PROFILE_KERNELS[wl]:
+                    if k not in cl or k not in cw:
+                        continue
+                    hit = sum(cl[k]["TCC_HIT_sum"]) / len(cl[k]["TCC_HIT_sum"])
+                    miss = sum(cl[k]["TCC_MISS_sum"]) / len(cl[k]["TCC_MISS_sum"])
+                    cw[k]["l2_hit_rate"] = round(hit / max(hit + miss, 1.0), 4)
+                    cw[k]["raw"].update({"TCC_HIT_sum": round(hit, 1), "TCC_MISS_sum": round(miss, 1)})
+                    lines.append(f"#   {k:24s} L2 hits {hit:14.0f}  misses {miss:14.0f}  "
+                                 f"hit_rate {cw[k]['l2_hit_rate']:.3f}")
             counters["workloads"][wl] = cw
         path = os.path.join(out_dir, PROFILE_FILES[wl] + ".txt")
         with open(path, "w") as f:

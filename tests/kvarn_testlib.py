@@ -64,6 +64,7 @@ class QuantStats:
         self.meta_plain_over = 0        # scales and zeros beyond the plain 1e-3
         self.meta_plain_total = 0
         self.offset_groups = 0          # offset-dominated groups (kept out of the L3 rate)
+        self.l3_at_ties = 0             # L3 mismatches whose oracle code value sits in the tie band
 
     def rate(self):
         return self.l3_mismatch / max(self.codes, 1)
@@ -76,7 +77,7 @@ class QuantStats:
                 f"L2 outside-tie={self.l2_mismatch} meta exact {self.meta_exact}/{self.meta_total} "
                 f"max meta rel {self.max_meta_rel:.2e} scale/zero beyond plain 1e-3: "
                 f"{self.meta_plain_over}/{self.meta_plain_total} ({self.plain_rate():.2e}) "
-                f"offset-dominated groups {self.offset_groups}")
+                f"offset-dominated groups {self.offset_groups} L3 at oracle ties {self.l3_at_ties}")
 
 
 def reconstruction_error(x_ct: np.ndarray, d: dict, kind: int, group: int = 128) -> float:
@@ -191,6 +192,14 @@ def check_quantized_tiles(tiles_tc: np.ndarray, records, kind: int, n_iters: int
         keep = ~offset
         assert np.all(np.abs(d[keep]) <= 1), (i, int(np.abs(d[keep]).max()))
         stats.l3_mismatch += int(np.count_nonzero(d[keep]))
+        if np.any(d[keep]):
+            # mismatches at an oracle code value within the tie band of a rounding boundary
+            u_o = G(ref["u"][i])
+            xs = np.abs(x[i].astype(np.float64)).sum(axis=0)[None, :] / np.sqrt(128.0)
+            rs = G(np.broadcast_to(xs / (r_g[:, None] * s_g[None, :]), (128, 128)))
+            band_o = TIE_BAND + 32 * 2.0 ** -24 * rs / np.where(sb[:, None] > 0, sb[:, None], np.inf)
+            tie_o = np.abs(u_o - np.floor(u_o) - 0.5) <= band_o
+            stats.l3_at_ties += int(np.count_nonzero((d != 0) & tie_o & keep[:, None]))
         stats.codes += int(keep.sum()) * group
         if offset.any():
             xf = x[i].astype(np.float64)
@@ -220,8 +229,13 @@ def _meta_report(g: dict, ref: dict, i: int) -> str:
     return ", ".join(out)
 
 
-def assert_rate(stats: QuantStats, meta_plain_rate: float = META_PLAIN_RATE):
-    assert stats.rate() <= CODE_MISMATCH_RATE, repr(stats)
+def assert_rate(stats: QuantStats, meta_plain_rate: float = META_PLAIN_RATE,
+                ties_apart: bool = False):
+    """The L3 and plain-metadata rates. ties_apart: the L3 rate counts only mismatches outside
+    the oracle's tie band (for constructed inputs whose repeated values put many of the oracle's
+    own code values on rounding ties; those codes are held to L2)."""
+    l3 = stats.l3_mismatch - (stats.l3_at_ties if ties_apart else 0)
+    assert l3 / max(stats.codes, 1) <= CODE_MISMATCH_RATE, repr(stats)
     assert stats.plain_rate() <= meta_plain_rate, repr(stats)
 
 

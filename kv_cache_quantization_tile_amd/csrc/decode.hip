@@ -476,6 +476,19 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
     if (wi >= n_waves) return;
     int64_t x = int64_t(T) * wi / n_waves;
     const int64_t x_end = int64_t(T) * (wi + 1) / n_waves;
+    const int64_t x_begin = x;
+    // Issue priority by progress: 3 in the first quarter of this wave's pages, down to 0 in
+    // the last. The waves that share a SIMD then keep pace with each other (the one behind
+    // wins the issue arbitration) instead of one finishing first and leaving the other alone.
+    auto set_prio = [&](int64_t xc) {
+      const int q4 = int((xc - x_begin) * 4 / (x_end - x_begin));
+      switch (q4) {
+        case 0: __builtin_amdgcn_s_setprio(3); break;
+        case 1: __builtin_amdgcn_s_setprio(2); break;
+        case 2: __builtin_amdgcn_s_setprio(1); break;
+        default: __builtin_amdgcn_s_setprio(0); break;
+      }
+    };
     // list entry y (< T) -> sequence sb (the last with Hkv pref[sb] <= y, which has pages),
     // KV head sg, page sp of its np full pages
     auto locate = [&](int64_t y, int& sb, int& sg, int& sp, int& np) {
@@ -517,6 +530,7 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
         for (int i = 0; i < 4; ++i) acc[bb][i] = 0.f;
       for (int k = 0; k < n; ++k) {
         const int64_t next = k + 1 < n ? rec_of(bt_r, sp + k + 1, np, sg) : after;
+        set_prio(x + k);
         process(t, next, cur >= 0, kTile);
         cur = next;
       }

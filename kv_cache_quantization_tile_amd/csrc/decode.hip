@@ -71,6 +71,7 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
                     const __half* __restrict__ v_tail, float tail_qscale,
                     float* __restrict__ ws, int32_t n_page_wg) {
   __shared__ DecodeSmem<NG> sm;
+  static_assert(sizeof(DecodeSmem<NG>) >= sizeof(TailSmem), "the tail reuses the LDS");
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int G = num_q_heads / num_kv_heads;
   // split layout: KV heads fastest, so that the workgroups dealt to the 8 XCDs round-robin in
@@ -86,7 +87,7 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
                       tail_qscale,
                       ws + balanced_tail_offset(n_page_wg, batch, num_q_heads, num_kv_heads) +
                           (int64_t(b) * num_q_heads + int64_t(g) * G) * kPartStride,
-                      kPartStride, reinterpret_cast<float (*)[kTile]>(&sm.acc[0][0][0]));
+                      kPartStride, *reinterpret_cast<TailSmem*>(&sm));
       return;
     }
   } else {
@@ -98,7 +99,7 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
   if constexpr (!BAL) {
     if (split == n_splits) {   // the extra split (launched only with tail buffers): the tail
       tail_partial(q, num_q_heads, num_kv_heads, k_tail, v_tail, b, rg.b, g, rg.tail_len,
-                   tail_qscale, n_splits, ws, reinterpret_cast<float (*)[kTile]>(&sm.acc[0][0][0]));
+                   tail_qscale, n_splits, ws, *reinterpret_cast<TailSmem*>(&sm));
       return;
     }
   }

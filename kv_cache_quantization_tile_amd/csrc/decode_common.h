@@ -334,72 +334,197 @@ __device__ __forceinline__ RowGeom row_geometry(int row, const int32_t* __restri
   return r;
 }
 
-// Exact attention over the T staged float16 tokens of (sequence sb, KV head g), raw space,
-// for output row `row`, written as split n_splits of each query head's partials. Run by the
-// extra split of decode_pages_kernel; wave w handles heads 2w, 2w+1 of the group; p_sm is
-// 8 x 128 floats of LDS.
+// Shared memory of the staged-token attention: per wave, first its value columns staged as
+// float16 rows of 32 tokens (64 channels at a time), then its partial output; the per-wave
+// score maxima and weight sums.
+struct TailSmem {
+  float o[4][8][kDim];
+  float m[4][8];
+  float l[4][8];
+};
+
+// The wave's staged tokens in the order the matrix cores see them. Score block mb, row rho
+// (rho = 4 j + i of the result held by lane group j) is token 16 (rho / 8) + 8 mb + rho mod 8,
+// so the 8 scores of lane group j are, as the 8 contraction entries 8 j .. 8 j + 7 of the value
+// product, tokens 16 (j / 2) + 8 mb + 4 (j mod 2) + i (entry 4 mb + i), and lanes 0..31 hold
+// tokens 0..15, lanes 32..63 tokens 16..31 of the wave's 32.
+__device__ __forceinline__ int tail_token(int mb, int rho) { return 16 * (rho >> 3) + 8 * mb + (rho & 7); }
+
+// Exact attention over the T < 128 staged float16 tokens of (sequence sb, KV head g), raw
+// space, for output row `row`: one partial (score max, weight sum, weighted value sum) per
+// query head of the group, written at part0 + h head_stride (h < G <= 8). Wave w takes tokens
+// 32 w .. 32 w + 31 for all heads: scores on the matrix cores (tokens x channels times
+// channels x heads, heads padded to 16), its own softmax, weights times values on the matrix
+// cores (the weights split into a float16 high and low part, so they keep float32 accuracy),
+// the values transposed through the wave's LDS rows; the four wave partials are then merged.
+// Called by all 256 threads of a workgroup (T uniform); ts must not be in use elsewhere.
 __device__ void tail_partial_at(const __half* __restrict__ q, int32_t num_q_heads,
                                 int32_t num_kv_heads, const __half* __restrict__ k_tail,
                                 const __half* __restrict__ v_tail, int row, int sb, int g, int T,
                                 float qscale, float* __restrict__ part0, int64_t head_stride,
-                                float (*p_sm)[kTile]) {
+                                TailSmem& ts) {
   const int G = num_q_heads / num_kv_heads;
   if (T == 0) return;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const __half* kt = k_tail + (int64_t(sb) * num_kv_heads + g) * kTile * kDim;
-  const __half* vt = v_tail + (int64_t(sb) * num_kv_heads + g) * kTile * kDim;
-  for (int hh = 2 * w; hh < 2 * w + 2; ++hh) {
-    if (hh >= G) break;
-    const int hq = g * G + hh;
-    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(q + (int64_t(row) * num_q_heads + hq) * kDim);
-    float sc[2];
+  const int n = l & 15, j = l >> 4, hl = l >> 5;
+  const int tw = 32 * w;
+  const int nw = (T + 31) >> 5;   // waves with tokens (uniform); the others go to the merge
+  if (w < nw) {
+    const __half* kt = k_tail + (int64_t(sb) * num_kv_heads + g) * kTile * kDim;
+    const __half* vt = v_tail + (int64_t(sb) * num_kv_heads + g) * kTile * kDim;
+    // values first (they do not wait for the scores): phase ph, lane l holds channels
+    // 64 ph + 2 (l mod 32), + 1 of tokens 16 hl + u, u < 16
+    uint32_t vv[2][16];
 #pragma unroll
-    for (int half_ = 0; half_ < 2; ++half_) {
-      const int t = l + 64 * half_;
-      float a = -INFINITY;
-      if (t < T) {
-        a = 0.f;
-        const uint8_t* krow = reinterpret_cast<const uint8_t*>(kt + int64_t(t) * kDim);
-        for (int c8 = 0; c8 < 16; ++c8) {
-          float qv[8], kv[8];
-          load_h8(qrow + 16 * c8, qv);
-          load_h8(krow + 16 * c8, kv);
+    for (int ph = 0; ph < 2; ++ph)
 #pragma unroll
-          for (int i = 0; i < 8; ++i) a = fmaf(qv[i], kv[i], a);
-        }
-        a *= qscale;
+      for (int u = 0; u < 16; ++u) {
+        const int t = tw + 16 * hl + u;
+        const __half* src = vt + int64_t(t) * kDim + 64 * ph + 2 * (l & 31);
+        vv[ph][u] = t < T ? *reinterpret_cast<const uint32_t*>(src) : 0u;
       }
-      sc[half_] = a;
-    }
-    float mx = fmaxf(sc[0], sc[1]);
-    for (int off = 1; off < 64; off <<= 1)
-      mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(((l ^ off) << 2), __float_as_int(mx))));
-    float ps = 0.f;
+    // ---- scores: A = keys (16 tokens x 32 channels per k-step), B = queries (32 channels x 16
+    // heads; heads from G on are zero)
+    const __half* qg = q + (int64_t(row) * num_q_heads + int64_t(g) * G) * kDim;
+    H8 bq[4];
 #pragma unroll
-    for (int half_ = 0; half_ < 2; ++half_) {
-      const int t = l + 64 * half_;
-      const float p = t < T ? exp2f(sc[half_] - mx) : 0.f;
-      p_sm[hh][t] = p;
-      ps += p;
+    for (int kk = 0; kk < 4; ++kk) {
+      const uint4 z = make_uint4(0, 0, 0, 0);
+      const uint4 v = n < G ? *reinterpret_cast<const uint4*>(qg + n * kDim + 32 * kk + 8 * j) : z;
+      bq[kk].u[0] = v.x; bq[kk].u[1] = v.y; bq[kk].u[2] = v.z; bq[kk].u[3] = v.w;
     }
-    for (int off = 1; off < 64; off <<= 1)
-      ps += __int_as_float(__builtin_amdgcn_ds_bpermute(((l ^ off) << 2), __float_as_int(ps)));
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_wave_barrier();
-    float o0 = 0.f, o1 = 0.f;
-    for (int t = 0; t < T; ++t) {
-      const uint32_t vv = *reinterpret_cast<const uint32_t*>(vt + int64_t(t) * kDim + 2 * l);
-      const float p = p_sm[hh][t];
-      o0 = fmaf(p, h2f(uint16_t(vv & 0xFFFF)), o0);
-      o1 = fmaf(p, h2f(uint16_t(vv >> 16)), o1);
+    float4v sacc[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int t = tw + tail_token(mb, n);
+      H8 a[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const uint4 z = make_uint4(0, 0, 0, 0);
+        const __half* src = kt + int64_t(t) * kDim + 32 * kk + 8 * j;
+        const uint4 v = t < T ? *reinterpret_cast<const uint4*>(src) : z;
+        a[kk].u[0] = v.x; a[kk].u[1] = v.y; a[kk].u[2] = v.z; a[kk].u[3] = v.w;
+      }
+      sacc[mb] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) sacc[mb] = mfma16x16x32(a[kk].v, bq[kk].v, sacc[mb]);
     }
-    float* part = part0 + hh * head_stride;
-    *reinterpret_cast<float2*>(part + 4 + 2 * l) = make_float2(o0, o1);
-    if (l == 0) {
-      part[0] = mx;
-      part[1] = ps;
+    // ---- this wave's softmax per head n (lanes n, n + 16, n + 32, n + 48 share a head)
+    auto xor_lanes = [&](float x, int m) {
+      return __int_as_float(__builtin_amdgcn_ds_bpermute((l ^ m) << 2, __float_as_int(x)));
+    };
+    float sc[2][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = tw + tail_token(mb, 4 * j + i);
+        sc[mb][i] = t < T ? sacc[mb][i] * qscale : -INFINITY;
+        mx = fmaxf(mx, sc[mb][i]);
+      }
+    mx = fmaxf(mx, xor_lanes(mx, 16));
+    mx = fmaxf(mx, xor_lanes(mx, 32));
+    float ps = 0.f;
+    H8 ahi, alo;   // weights as the A operand of the value product: entry 4 mb + i
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = exp2f(sc[mb][i] - mx);   // mx is finite: the wave has a token
+        ps += p;
+        const _Float16 hi = _Float16(p);
+        ahi.v[4 * mb + i] = hi;
+        alo.v[4 * mb + i] = _Float16(p - float(hi));
+      }
+    ps += xor_lanes(ps, 16);
+    ps += xor_lanes(ps, 32);
+    // ---- weights x values: per phase, the wave's 64 value channels as LDS rows of the 32
+    // tokens in contraction order (row r: 4 chunks of 8 entries, chunk c stored at c ^ (r/2 mod 4))
+    uint32_t* vtr = reinterpret_cast<uint32_t*>(&ts.o[w][0][0]);
+    float4v oacc[8];
+#pragma unroll
+    for (int ph = 0; ph < 2; ++ph) {
+      // lane l: rows 2 (l mod 32) and + 1 (the low and high channel), entries 16 hl .. 16 hl + 15;
+      // entry 16 hl + e' (e' = 8 j' + 4 mb + i) is token 16 hl + 8 mb + 4 j' + i = vv[ph][u]
+      uint32_t lo[8], hi[8];
+#pragma unroll
+      for (int e2 = 0; e2 < 8; ++e2) {
+        const int e0 = 2 * e2, e1 = 2 * e2 + 1;
+        const int u0 = 8 * ((e0 >> 2) & 1) + 4 * (e0 >> 3) + (e0 & 3);
+        const int u1 = 8 * ((e1 >> 2) & 1) + 4 * (e1 >> 3) + (e1 & 3);
+        lo[e2] = (vv[ph][u0] & 0xFFFFu) | (vv[ph][u1] << 16);
+        hi[e2] = (vv[ph][u0] >> 16) | (vv[ph][u1] & 0xFFFF0000u);
+      }
+      const int r0 = 2 * (l & 31);
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const int c = 2 * hl + c2;
+        const int s0 = c ^ ((r0 >> 1) & 3), s1 = c ^ (((r0 + 1) >> 1) & 3);
+        *reinterpret_cast<uint4*>(vtr + 16 * r0 + 4 * s0) =
+            make_uint4(lo[4 * c2], lo[4 * c2 + 1], lo[4 * c2 + 2], lo[4 * c2 + 3]);
+        *reinterpret_cast<uint4*>(vtr + 16 * (r0 + 1) + 4 * s1) =
+            make_uint4(hi[4 * c2], hi[4 * c2 + 1], hi[4 * c2 + 2], hi[4 * c2 + 3]);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int r = 16 * nb + n;
+        const uint4 v = *reinterpret_cast<const uint4*>(vtr + 16 * r + 4 * (j ^ ((r >> 1) & 3)));
+        H8 bv;
+        bv.u[0] = v.x; bv.u[1] = v.y; bv.u[2] = v.z; bv.u[3] = v.w;
+        float4v acc = mfma16x16x32(ahi.v, bv.v, float4v{0.f, 0.f, 0.f, 0.f});
+        oacc[4 * ph + nb] = mfma16x16x32(alo.v, bv.v, acc);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_wave_barrier();
     }
-    __builtin_amdgcn_wave_barrier();
+    // ---- the wave's partial: output (head 4 j + i, channel 16 nb + n) from oacc[nb][i]
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * j + i;
+      if (h < G) {
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) ts.o[w][h][16 * nb + n] = oacc[nb][i];
+      }
+    }
+    if (j == 0 && n < G) {
+      ts.m[w][n] = mx;
+      ts.l[w][n] = ps;
+    }
+  }
+  __syncthreads();
+  // ---- merge of the four wave partials: thread = head tid / 32, channels 4 (tid mod 32) + 0..3
+  const int h = tid >> 5, c4 = 4 * (tid & 31);
+  if (h < G) {
+    float mw[4], M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      mw[v] = v < nw ? ts.m[v][h] : -INFINITY;
+      M = fmaxf(M, mw[v]);
+    }
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float lsum = 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      if (v >= nw) break;
+      const float f = exp2f(mw[v] - M);
+      const float4 x = *reinterpret_cast<const float4*>(&ts.o[v][h][c4]);
+      acc.x = fmaf(f, x.x, acc.x);
+      acc.y = fmaf(f, x.y, acc.y);
+      acc.z = fmaf(f, x.z, acc.z);
+      acc.w = fmaf(f, x.w, acc.w);
+      lsum = fmaf(f, ts.l[v][h], lsum);
+    }
+    float* part = part0 + h * head_stride;
+    *reinterpret_cast<float4*>(part + 4 + c4) = acc;
+    if ((tid & 31) == 0) {
+      part[0] = M;
+      part[1] = lsum;
+    }
   }
 }
 
@@ -410,12 +535,12 @@ __device__ __forceinline__ void tail_partial(const __half* __restrict__ q, int32
                                              const __half* __restrict__ k_tail,
                                              const __half* __restrict__ v_tail, int row, int sb,
                                              int g, int T, float qscale, int32_t n_splits,
-                                             float* __restrict__ ws, float (*p_sm)[kTile]) {
+                                             float* __restrict__ ws, TailSmem& ts) {
   const int G = num_q_heads / num_kv_heads;
   tail_partial_at(q, num_q_heads, num_kv_heads, k_tail, v_tail, row, sb, g, T, qscale,
                   ws + ((int64_t(row) * num_q_heads + int64_t(g) * G) * (n_splits + 1) + n_splits) *
                            kPartStride,
-                  int64_t(n_splits + 1) * kPartStride, p_sm);
+                  int64_t(n_splits + 1) * kPartStride, ts);
 }
 
 }  // namespace

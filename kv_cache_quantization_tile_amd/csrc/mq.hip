@@ -27,7 +27,7 @@ struct MqSmem {
   WaveMeta<NG> meta[4];
   union {
     float4 q[4][8][64];   // q_rot per wave: [k][lane] = channels 32 gq + 4k .. 4k + 3
-    float p[8][kTile];    // tail split: softmax weights of the staged tokens
+    TailSmem tail;        // tail split: the staged-token attention
   };
 };
 
@@ -79,7 +79,7 @@ mq_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t num_k
     for (int row = win.r0; row < win.r1; ++row) {   // uniform over the workgroup
       const RowGeom rgr = row_geometry(row, seq_lens, max_seq_len, cu_q, batch);
       tail_partial(q, num_q_heads, num_kv_heads, k_tail, v_tail, row, rgr.b, g, rgr.tail_len,
-                   tail_qscale, n_splits, ws, sm.p);
+                   tail_qscale, n_splits, ws, sm.tail);
       __syncthreads();
     }
     return;

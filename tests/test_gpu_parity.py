@@ -303,6 +303,37 @@ def test_decode_ragged_gqa(K, G, hkv):
     say(f"max rel err {err:.3e}")
 
 
+TAIL_LENS = [1, 31, 32, 33, 63, 64, 65, 96, 97, 127]
+
+
+@pytest.mark.parametrize("G,hkv,single", [(8, 2, False), (4, 1, False), (1, 3, False),
+                                          (8, 1, True), (2, 2, True)])
+def test_decode_tail_lengths_across_wave_boundaries(K, G, hkv, single):
+    """Staged tails of every length class of the staged-token attention (one to four waves
+    of 32 tokens, each boundary from both sides), after two pages and alone; the staging rows
+    past each tail hold NaN, so a key or value read there shows in the output. single: one
+    sequence per call (the split layout), else all in one batch (the balanced layout)."""
+    lens = [256 + t for t in TAIL_LENS] + [5, 100]
+    params = K.params_from_dtype("kvarn_k4v2_g128", 4)
+    say(f"decode tail lengths G={G} hkv={hkv} single={single}")
+    kp, vp, bt, kt, vt, sl, _ = _build_cache(K, params, lens, hkv, seed=60 + 10 * G + hkv)
+    for b, L in enumerate(lens):
+        kt[b, :, L % 128:] = float("nan")
+        vt[b, :, L % 128:] = float("nan")
+    q = torch.randn((len(lens), G * hkv, 128), generator=torch.Generator().manual_seed(61)).to(torch.float16).cuda()
+    if single:
+        out = torch.empty((len(lens), G * hkv, 128), dtype=torch.float16, device="cuda")
+        for b, L in enumerate(lens):
+            out[b:b + 1] = K.decode_attention(params, q[b:b + 1], kp, vp, bt[b:b + 1], sl[b:b + 1], L,
+                                              kt[b:b + 1].contiguous(), vt[b:b + 1].contiguous())
+    else:
+        out = K.decode_attention(params, q, kp, vp, bt, sl, max(lens), kt, vt)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    err = T.check_decode(q, out, kp, vp, bt, sl, G, k_tail=kt, v_tail=vt)
+    say(f"max rel err {err:.3e}")
+
+
 def test_decode_many_splits_and_max_seq_len_clamp(K):
     """Long enough for several splits; max_seq_len above every length (unused splits)."""
     lens = [128 * 37 + 5, 128 * 60, 128 * 3]

@@ -372,11 +372,24 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
   };
 
   // q_rot = H q * softmax_scale * log2(e) of (output row bq, KV head gh) into qo, maxq
-  auto rotate_q = [&](int bq, int gh) {
-    float qr[32];
+  // (split in two: the loads of a wave's first q go out before its first page's, so that the
+  // rotation waits for q alone, not for the page queued ahead of it)
+  auto q_loads = [&](int bq, int gh, uint4 (&raw)[4]) {
     const __half* qrow = q + (int64_t(bq) * num_q_heads + int64_t(gh) * G + (head_ok ? h : 0)) * kDim + 32 * gq;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) load_h8(reinterpret_cast<const uint8_t*>(qrow + 8 * k), &qr[8 * k]);
+    for (int k = 0; k < 4; ++k) raw[k] = *reinterpret_cast<const uint4*>(qrow + 8 * k);
+  };
+  auto rotate_loaded_q = [&](const uint4 (&raw)[4]) {
+    float qr[32];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t wd[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qr[8 * k + 2 * e] = h2f(uint16_t(wd[e] & 0xFFFF));
+        qr[8 * k + 2 * e + 1] = h2f(uint16_t(wd[e] >> 16));
+      }
+    }
     if (!head_ok) {
 #pragma unroll
       for (int j = 0; j < 32; ++j) qr[j] = 0.f;
@@ -506,10 +519,13 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
     };
     int sb, sg, sp, np;
     locate(x, sb, sg, sp, np);
+    uint4 qraw[4];
+    q_loads(sb, sg, qraw);
     int64_t cur = rec_of(block_table + int64_t(sb) * bt_stride, sp, np, sg);
     load_meta<AUX, FMT, NG>(t, krec_of(cur), vrec_of(cur), lo);
     load_kcodes<AUX>(t, krec_of(cur), lo);
     load_vcodes<AUX>(t, vrec_of(cur), lo);
+    rotate_loaded_q(qraw);   // the first segment's q (later ones: at the end of the previous)
     while (x < x_end) {
       // this segment: pages sp .. sp + n - 1 of (sb, sg)
       const int n = int(min(x_end - x, int64_t(np - sp)));
@@ -522,7 +538,6 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
         locate(x_next, nb, ng, nsp, nnp);
         after = rec_of(block_table + int64_t(nb) * bt_stride, nsp, nnp, ng);
       }
-      rotate_q(sb, sg);
       m_run = -INFINITY;
       l_part = 0.f;
 #pragma unroll
@@ -553,17 +568,24 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
       sg = ng;
       sp = nsp;
       np = nnp;
+      if (x < x_end) {   // the next segment's q, while its first page's loads are in flight
+        uint4 qn[4];
+        q_loads(sb, sg, qn);
+        rotate_loaded_q(qn);
+      }
     }
     return;
   } else {
   const int32_t* bt_row = block_table + int64_t(rg.b) * bt_stride;
   const int wslot = __builtin_amdgcn_readfirstlane(slot0 + w);   // this wave's first slot
+  uint4 qraw[4];
+  q_loads(b, g, qraw);
   int64_t cur = rec_of(bt_row, wslot, n_full, g);
   load_meta<AUX, FMT, NG>(t, krec_of(cur), vrec_of(cur), lo);
   load_kcodes<AUX>(t, krec_of(cur), lo);
   load_vcodes<AUX>(t, vrec_of(cur), lo);
   // q is rotated while the first page's loads are in flight
-  rotate_q(b, g);
+  rotate_loaded_q(qraw);
   // pages of this wave: slots wslot, wslot + 4, ... below n_full, at most tpw of them
   // (a loop with one exit keeps the running state in place across iterations)
   const int n_here = wslot < n_full ? min(tpw, (n_full - wslot + 3) >> 2) : 0;

@@ -490,18 +490,20 @@ decode_pages_kernel(const __half* __restrict__ q, int32_t num_q_heads, int32_t n
     if (wi >= n_waves) return;
     int64_t x = int64_t(T) * wi / n_waves;
     const int64_t x_end = int64_t(T) * (wi + 1) / n_waves;
-    const int64_t x_begin = x;
     // Issue priority by progress: 3 in the first quarter of this wave's pages, down to 0 in
     // the last. The waves that share a SIMD then keep pace with each other (the one behind
     // wins the issue arbitration) instead of one finishing first and leaving the other alone.
+    // With the wave's n entries starting at x0, quarter k starts at entry x0 + ceil(k n / 4),
+    // the first entry xc with floor(4 (xc - x0) / n) >= k: three bounds found once instead of
+    // a 64-bit division per page.
+    const int64_t n_mine = x_end - x;
+    const int64_t quarter1 = x + (n_mine + 3) / 4, quarter2 = x + (2 * n_mine + 3) / 4,
+                  quarter3 = x + (3 * n_mine + 3) / 4;
     auto set_prio = [&](int64_t xc) {
-      const int q4 = int((xc - x_begin) * 4 / (x_end - x_begin));
-      switch (q4) {
-        case 0: __builtin_amdgcn_s_setprio(3); break;
-        case 1: __builtin_amdgcn_s_setprio(2); break;
-        case 2: __builtin_amdgcn_s_setprio(1); break;
-        default: __builtin_amdgcn_s_setprio(0); break;
-      }
+      if (xc < quarter1) __builtin_amdgcn_s_setprio(3);
+      else if (xc < quarter2) __builtin_amdgcn_s_setprio(2);
+      else if (xc < quarter3) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
     };
     // list entry y (< T) -> sequence sb (the last with Hkv pref[sb] <= y, which has pages),
     // KV head sg, page sp of its np full pages

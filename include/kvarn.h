@@ -310,7 +310,8 @@ KVARN_API int32_t kvarn_decode_num_splits(const kvarn_params* params, int32_t ba
  *   q_dev, out_dev: [batch, num_q_heads, 128] float16, contiguous, 16-byte aligned.
  *   num_q_heads % num_kv_heads == 0 and num_q_heads / num_kv_heads <= 8.
  *   batch <= 65535 and batch * num_kv_heads <= INT32_MAX (grid limits; UNSUPPORTED above).
- *   k_tail_dev / v_tail_dev may be NULL: then tail tokens are ignored.
+ *   k_tail_dev / v_tail_dev may be NULL: then tail tokens are ignored. Staging rows from
+ *   L mod 128 on are never read (they may hold anything, NaN included).
  *   Pages outside [0, pool_num_pages) are skipped. A sequence with L = 0, or with every
  *   page skipped and no tail, gets out = 0.
  *   workspace_dev: >= kvarn_decode_workspace_bytes(...) bytes, 16-byte aligned; it holds

@@ -8,7 +8,8 @@ step), on sampled tiles and sampled (sequence, KV head) rows that the oracle rec
                  120 mod 128 whose staging tiles fill (and are quantized) at step 8;
   long context   131072 tokens, 64 decode steps with appends;
   prefill burst  64 x 16384 tokens (131072 tiles) for 2, 4 and 8 iterations, then one
-                 batched decode step;
+                 batched decode step; at 8 iterations also with the group-64 and k4v4
+                 presets in the folded record format and with k2v2;
   chunked prefill  8 sequences x 16384 cached tokens + a 128-token chunk each (chunk write,
                  then the multi-query read of the 1024 chunk rows).
 
@@ -49,8 +50,9 @@ def _quantize_layer(K, params, w):
     return kp, vp
 
 
-def _check_sampled_tiles(w, kp, vp, n_iters, seed, n=N_TILES):
-    """Oracle check of n random (tile, head) pairs per kind."""
+def _check_sampled_tiles(w, kp, vp, n_iters, seed, n=N_TILES, **fmt):
+    """Oracle check of n random (tile, head) pairs per kind (fmt: the preset's k_bits,
+    v_bits, fmt and group when not the default k4v2_g128 format 1)."""
     rng = np.random.default_rng(seed)
     n_t = w.tile_src_token.numel()
     tok = w.tile_src_token.cpu().numpy()
@@ -63,7 +65,7 @@ def _check_sampled_tiles(w, kp, vp, n_iters, seed, n=N_TILES):
         sel = pool[torch.as_tensor(page[ti], dtype=torch.long, device=pool.device),
                    torch.as_tensor(hh, dtype=torch.long, device=pool.device)].cpu().numpy()
         recs = [sel[k].tobytes() for k in range(sel.shape[0])]
-        st = T.check_quantized_tiles(tiles, recs, kind, n_iters)
+        st = T.check_quantized_tiles(tiles, recs, kind, n_iters, **fmt)
         say(f"  kind={kind} {st}")
         # the workloads' data (no offset-dominated tiles): scales and zeros beyond the plain
         # 1e-3 at most 2e-4 of them, within twice the L3 code rate
@@ -191,6 +193,29 @@ def test_prefill_burst(K, burst, n_iters):
     rows = _rows(np.random.default_rng(409), w.batch, w.hkv)
     err = T.check_decode(q, out, kp, vp, w.block_table, sl, w.hq // w.hkv, rows=rows)
     say(f"  decode: {len(rows) * 8} rows, max rel err {err:.2e}")
+
+
+@pytest.mark.parametrize("preset,kb,vb,fmt,group", [("kvarn_k4v2_g64", 4, 2, 2, 64),
+                                                    ("kvarn_k4v4_g128", 4, 4, 2, 128),
+                                                    ("kvarn_k2v2_g128", 2, 2, 1, 128)])
+def test_prefill_burst_other_presets(K, burst, preset, kb, vb, fmt, group):
+    """The prefill burst at full size (131072 K+V tiles, N = 8, one batched decode) with other
+    presets and the folded record format, as `bench.py --preset ... --format ...` runs it."""
+    w = burst
+    params = K.params_from_dtype(preset, 8, format=fmt)
+    say(f"prefill burst {preset} format {fmt}: {w.tile_src_token.numel() * w.hkv * 2} tiles")
+    kp, vp = _quantize_layer(K, params, w)
+    _check_sampled_tiles(w, kp, vp, 8, seed=450 + kb + vb + fmt, n=128,
+                         k_bits=kb, v_bits=vb, fmt=fmt, group=group)
+    q = w.step_inputs(0)[0]
+    sl = torch.tensor(w.prompt_lens, dtype=torch.int32, device="cuda")
+    out = K.decode_attention(params, q, kp, vp, w.block_table, sl, max(w.prompt_lens))
+    torch.cuda.synchronize()
+    rows = _rows(np.random.default_rng(460 + kb + vb + fmt), w.batch, w.hkv)
+    err = T.check_decode(q, out, kp, vp, w.block_table, sl, w.hq // w.hkv, rows=rows)
+    say(f"  decode: {len(rows) * 8} rows, max rel err {err:.2e}")
+    del kp, vp
+    torch.cuda.empty_cache()
 
 
 def test_chunked_prefill_full(K):

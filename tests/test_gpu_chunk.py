@@ -41,7 +41,7 @@ def _written_cache(K, params, lens, lens_new, hkv, seed):
     return kp, vp, bt, kt, vt, sl2
 
 
-def _reference_rows(q, cu_q, kp, vp, bt, kt, vt, sl, G, rows_to_check):
+def _reference_rows(q, cu_q, kp, vp, bt, kt, vt, sl, G, rows_to_check, scale=SCALE):
     """Oracle causal attention (O.causal_attention) of the given query rows: the cache of
     sequence b in position order is its dequantized pages followed by the staged tokens of
     its partial last tile; row cu_q[b] + i sits at position C - n + i."""
@@ -68,10 +68,41 @@ def _reference_rows(q, cu_q, kp, vp, bt, kt, vt, sl, G, rows_to_check):
                 cache[(b, g)] = (np.concatenate(ks, 0), np.concatenate(vs, 0))
             kk, vv = cache[(b, g)]
             hqs = [g * G + hh for hh in range(G)]
-            res = O.causal_attention(qh[r, hqs].astype(np.float64), [pos] * G, kk, vv, SCALE)
+            res = O.causal_attention(qh[r, hqs].astype(np.float64), [pos] * G, kk, vv, scale)
             for hh, hq in enumerate(hqs):
                 out[(r, hq)] = res[hh]
     return out
+
+
+@pytest.mark.parametrize("factor", [40.0, 1e-3])
+def test_chunk_softmax_extremes(K, factor):
+    """The multi-query read at softmax scales 40x and 1e-3x of 1/sqrt(128) (nearly one-hot
+    and nearly uniform causal attention), rows against the oracle."""
+    scale = factor * SCALE
+    lens, lens_new = [130, 0, 300], [140, 70, 100]
+    hkv, G = 2, 8
+    params = K.params_from_dtype("kvarn_k4v2_g128", 8)
+    kp, vp, bt, kt, vt, sl = _written_cache(K, params, lens, lens_new, hkv, seed=170 + int(factor))
+    total_q = sum(lens_new)
+    cu_q = torch.tensor([0] + list(np.cumsum(lens_new)), dtype=torch.int32, device="cuda")
+    q = torch.randn((total_q, hkv * G, 128), generator=torch.Generator().manual_seed(171))
+    q = q.to(torch.float16).cuda()
+    say(f"chunk attention softmax scale x{factor}: {total_q} query rows")
+    out = K.chunk_attention(params, q, cu_q, kp, vp, bt, sl, int(sl.max().item()), kt, vt,
+                            softmax_scale=scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    rng = np.random.default_rng(172)
+    cu = cu_q.cpu().numpy()
+    rows = set(rng.choice(total_q, size=32, replace=False).tolist())
+    for b in range(len(lens)):
+        rows |= {int(cu[b]), int(cu[b + 1]) - 1}
+    ref = _reference_rows(q, cu_q, kp, vp, bt, kt, vt, sl, G, sorted(rows), scale=scale)
+    o = out.cpu().numpy().astype(np.float64)
+    worst = 0.0
+    for (r, hq), want in ref.items():
+        worst = max(worst, T.assert_rows_close(o[r, hq], want, f"row {r} head {hq}"))
+    say(f"{len(ref)} rows, max rel err {worst:.3e}")
 
 
 @pytest.mark.parametrize("case", [0, 1])

@@ -303,6 +303,26 @@ def test_decode_ragged_gqa(K, G, hkv):
     say(f"max rel err {err:.3e}")
 
 
+@pytest.mark.parametrize("factor", [40.0, 1e-3])
+@pytest.mark.parametrize("single", [False, True])
+def test_decode_softmax_extremes(K, factor, single):
+    """Softmax scales far from 1/sqrt(128): 40x (nearly one-hot attention, scores spanning
+    hundreds of log2 units, most weights flushed to zero) and 1e-3x (nearly uniform weights,
+    the output close to the mean of the values), over pages and staged tails, both layouts."""
+    scale = factor / np.sqrt(128.0)
+    lens = [128 * 3 + 77, 128 * 5, 200, 128 * 2 + 1] if not single else [128 * 6 + 45]
+    hkv, G = 2, 4
+    params = K.params_from_dtype("kvarn_k4v2_g128", 8)
+    say(f"decode softmax scale x{factor} single={single}")
+    kp, vp, bt, kt, vt, sl, _ = _build_cache(K, params, lens, hkv, seed=70 + int(single))
+    q = torch.randn((len(lens), G * hkv, 128), generator=torch.Generator().manual_seed(71)).to(torch.float16).cuda()
+    out = K.decode_attention(params, q, kp, vp, bt, sl, max(lens), kt, vt, softmax_scale=scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    err = T.check_decode(q, out, kp, vp, bt, sl, G, k_tail=kt, v_tail=vt, softmax_scale=scale)
+    say(f"max rel err {err:.3e}")
+
+
 TAIL_LENS = [1, 31, 32, 33, 63, 64, 65, 96, 97, 127]
 
 

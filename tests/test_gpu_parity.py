@@ -115,6 +115,34 @@ def test_quantize_degenerate_tiles(K, kind, preset, fmt):
     T.assert_rate(st, ties_apart=True)
 
 
+@pytest.mark.parametrize("kind", [O.KIND_K, O.KIND_V])
+def test_quantize_float16_range_ends(K, kind):
+    """Inputs at both ends of the float16 range: every value a float16 subnormal (~2e-6),
+    subnormals with a few outliers 1000x larger, values up to +-60000 near the float16
+    maximum, and a tile whose first half is subnormal and second half near the maximum."""
+    rng = np.random.default_rng(8)
+    tiles = np.zeros((4, 128, 128), np.float32)
+    tiles[0] = rng.standard_normal((128, 128)) * 2e-6
+    tiles[1] = rng.standard_normal((128, 128)) * 2e-6
+    tiles[1][rng.random((128, 128)) < 0.01] *= 1000.0
+    tiles[2] = np.clip(rng.standard_normal((128, 128)) * 2e4, -60000, 60000)
+    tiles[3, :64] = rng.standard_normal((64, 128)) * 2e-6
+    tiles[3, 64:] = np.clip(rng.standard_normal((64, 128)) * 2e4, -60000, 60000)
+    x16 = tiles.astype(np.float16)
+    assert np.isfinite(x16).all() and np.abs(x16[0]).max() < 6.1e-5   # tile 0 all subnormal
+    n = x16.shape[0]
+    src = torch.from_numpy(x16).reshape(n * 128, 1, 128)
+    tok = torch.arange(n, dtype=torch.int64) * 128
+    st = T.QuantStats()
+    for iters in (1, 8):
+        say(f"float16 range ends kind={kind} iters={iters}")
+        params = K.params_from_dtype("kvarn_k4v2_g128", iters)
+        pool = _quantize(K, params, kind, src.cuda(), tok.cuda(), torch.arange(n, dtype=torch.int32).cuda(), n)
+        T.check_quantized_tiles(x16, T.records_of(pool, range(n), 0), kind, iters, st)
+    say(st)
+    T.assert_rate(st, ties_apart=True)
+
+
 def test_saturated_zero_page_decodes_finite(K):
     """A near-constant tile (5 + 1e-3 noise) at one iteration normalizes its rotated DC channel
     to ~1.9e5, beyond float16: both sides store that key channel's zero saturated at 65504

@@ -33,31 +33,35 @@ from oracle import kvarn_oracle as O
 
 SOFTMAX_SCALE = 1.0 / math.sqrt(128.0)
 
-# (label, channel rotation, normalization iterations, key bits, value bits); the last two rows
-# are the other presets' code widths (kvarn_k2v2_g128, kvarn_k4v4_g128) at N = 8
+# (label, channel rotation, normalization iterations, key bits, value bits, group size); the
+# last rows are the other presets' code widths (kvarn_k2v2_g128, kvarn_k4v4_g128) and group
+# size 64 (kvarn_k4v2_g64, kvarn_k2v2_g64) at N = 8
 VARIANTS = (
-    ("RTN only", False, 0, 4, 2),
-    ("rotation + RTN", True, 0, 4, 2),
-    ("normalization (N=8) + RTN", False, 8, 4, 2),
-    ("KVarN N=1", True, 1, 4, 2),
-    ("KVarN N=2", True, 2, 4, 2),
-    ("KVarN N=4", True, 4, 4, 2),
-    ("KVarN N=8", True, 8, 4, 2),
-    ("KVarN N=8, k2v2", True, 8, 2, 2),
-    ("KVarN N=8, k4v4", True, 8, 4, 4),
+    ("RTN only", False, 0, 4, 2, 128),
+    ("rotation + RTN", True, 0, 4, 2, 128),
+    ("normalization (N=8) + RTN", False, 8, 4, 2, 128),
+    ("KVarN N=1", True, 1, 4, 2, 128),
+    ("KVarN N=2", True, 2, 4, 2, 128),
+    ("KVarN N=4", True, 4, 4, 2, 128),
+    ("KVarN N=8", True, 8, 4, 2, 128),
+    ("KVarN N=8, k2v2", True, 8, 2, 2, 128),
+    ("KVarN N=8, k4v4", True, 8, 4, 4, 128),
+    ("KVarN N=8, g64", True, 8, 4, 2, 64),
+    ("KVarN N=8, k2v2 g64", True, 8, 2, 2, 64),
 )
 
 
 def dequantized(x_tc: np.ndarray, kind: int, rotate: bool, n_iters: int, k_bits: int = 4,
-                v_bits: int = 2) -> np.ndarray:
+                v_bits: int = 2, group: int = 128) -> np.ndarray:
     """x_tc: [T, 128] float16 tokens of one KV head, T a multiple of 128. Returns the oracle's
     quantized-then-dequantized tokens [T, 128], float64."""
     t = x_tc.shape[0]
     tiles = np.asarray(x_tc, np.float16).reshape(t // 128, 128, 128)      # [tile, token, channel]
     x = np.swapaxes(tiles, -1, -2)                                         # channels x tokens
-    d = O.quantize_tiles(x, kind, n_iters, rotate_channels=rotate, k_bits=k_bits, v_bits=v_bits)
+    d = O.quantize_tiles(x, kind, n_iters, rotate_channels=rotate, k_bits=k_bits, v_bits=v_bits,
+                         group=group)
     xh = O.dequantize_tiles(d["codes"], d["r"], d["s"], d["scale"], d["zero"], kind,
-                            rotate_channels=rotate)
+                            rotate_channels=rotate, group=group)
     return np.swapaxes(xh, -1, -2).reshape(t, 128)
 
 
@@ -81,9 +85,9 @@ def frob_rel_err(a: np.ndarray, b: np.ndarray) -> float:
 def caches(k: np.ndarray, v: np.ndarray, variants=VARIANTS) -> dict:
     """Dequantized prompt caches per variant: {label: (k_hat, v_hat)}, each [T, Hkv, 128]."""
     out = {}
-    for label, rot, n, kb, vb in variants:
-        kh = np.stack([dequantized(k[:, g], O.KIND_K, rot, n, kb, vb) for g in range(k.shape[1])], 1)
-        vh = np.stack([dequantized(v[:, g], O.KIND_V, rot, n, kb, vb) for g in range(v.shape[1])], 1)
+    for label, rot, n, kb, vb, gs in variants:
+        kh = np.stack([dequantized(k[:, g], O.KIND_K, rot, n, kb, vb, gs) for g in range(k.shape[1])], 1)
+        vh = np.stack([dequantized(v[:, g], O.KIND_V, rot, n, kb, vb, gs) for g in range(v.shape[1])], 1)
         out[label] = (kh, vh)
     return out
 

@@ -66,16 +66,18 @@ def test_normalization_removes_token_scale_error(results, name):
 
 
 def test_uneven_token_scales_attention(results):
-    """With uneven token scales, plain RTN's attention error is the largest of all variants."""
+    """With uneven token scales, plain RTN's attention error is the largest of all variants
+    with 4-bit keys (the 2-bit-key presets are a coarser code width; their attention error under
+    random queries is dominated by the keys and is erratic, above or below RTN's)."""
     r = results["uneven_tokens"]
-    worst = max(r.values(), key=lambda e: e["attn"])
+    worst = max((e for lab, e in r.items() if "k2v2" not in lab), key=lambda e: e["attn"])
     assert worst is r["RTN only"], r
     assert r["KVarN N=8"]["attn"] < 0.7 * r["RTN only"]["attn"], r
 
 
 def test_toy_loop_is_deterministic_and_starts_at_the_single_step_error():
     k, v, q_sets = _data("t3")
-    cache = A.caches(k, v, [("KVarN N=8", True, 8, 4, 2)])
+    cache = A.caches(k, v, [("KVarN N=8", True, 8, 4, 2, 128)])
     d1 = A.divergence(k, v, q_sets[0], cache, steps=4)
     d2 = A.divergence(k, v, q_sets[0], cache, steps=4)
     assert d1 == d2
@@ -92,7 +94,7 @@ def test_kernels_match_the_oracle_ablation():
         pytest.fail("GPU tests need an MI355X; torch.cuda.is_available() is False")
     for name in ("one_layer", "uneven_tokens"):
         k, v, q_sets = _data(name)
-        cache = A.caches(k, v, [("rotation + RTN", True, 0, 4, 2), ("KVarN N=8", True, 8, 4, 2)])
+        cache = A.caches(k, v, [("rotation + RTN", True, 0, 4, 2, 128), ("KVarN N=8", True, 8, 4, 2, 128)])
         ref = A.single_step(k, v, A.grouped_queries(q_sets), cache)
         kern = A.kernel_attn_errors(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
                                     torch.from_numpy(q_sets).cuda(), n_list=(0, 8))
@@ -111,3 +113,14 @@ def test_code_width_orders_reconstruction(results, name):
     assert r["KVarN N=8, k4v4"]["v"] < 0.3 * r["KVarN N=8"]["v"], r
     assert r["KVarN N=8, k2v2"]["k"] > 3.0 * r["KVarN N=8"]["k"], r
     assert r["KVarN N=8, k4v4"]["k"] == r["KVarN N=8"]["k"], r     # same key path
+
+
+@pytest.mark.parametrize("name", ["one_layer", "long_context", "uneven_tokens", "t3"])
+def test_group_64_lowers_reconstruction_error(results, name):
+    """Group size 64 (two scales and zeros per key channel and per value token instead of one,
+    the same code widths): each half group's range is at most the whole group's, so the keys
+    and values reconstruct at least as well, for both code-width presets."""
+    r = results[name]
+    for base, fine in (("KVarN N=8", "KVarN N=8, g64"), ("KVarN N=8, k2v2", "KVarN N=8, k2v2 g64")):
+        assert r[fine]["k"] < r[base]["k"], (name, base, r[fine]["k"], r[base]["k"])
+        assert r[fine]["v"] < r[base]["v"], (name, base, r[fine]["v"], r[base]["v"])
